@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of int4-KV split-K attention on one MI355X.
+
+Workload: the Llama-3.1-70B-shaped decode layer (batch 1, 64 query heads,
+8 KV heads, head_dim 128, int4 group-64 K/V with fp16 scale and bias,
+softmax scale 1/sqrt(128), split-K chunks of 512 rows) at Skv = 131072 by
+default. One step is one pass of the whole path for one layer: quantise the
+new token's K and V into the cache (n = 1 append at row Skv-1), then the
+split-K partial kernel and the reduce, all on one stream. Steps rotate over a
+pool of distinct layers (>= 640 MB, 2.5x the 256 MB last-level cache) so that
+the cache is read from HBM, not from the Infinity Cache.
+
+Inputs are seeded synthetic fp16 N(0,1) draws made on the GPU and quantised
+by the library itself; they are resident in HBM before timing starts.
+
+Output: one JSON line (rank 0) with value = effective HBM GB/s of the step
+(algorithmic bytes: int4 codes + fp16 scale/bias of K and V, plus the
+appended row), the per-kernel roofline of the partial kernel (HIP events
+around each launch in a second timed pass of the same steps) and the CPU
+oracle timed on the host as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+B, HQ, HKV, D, G = 1, 64, 8, 128, 64
+
+
+def layer_bytes(skv: int) -> int:
+    return HKV * skv * (D // 2 + 4 * (D // G)) * 2  # K and V: codes + fp16 scale + fp16 bias
+
+
+def append_bytes() -> int:
+    return 2 * B * HKV * D * 2 + 2 * B * HKV * (D // 2 + 4 * (D // G))  # fp16 rows in, packed row out
+
+
+def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 1234):
+    n_layers = max(2, math.ceil(pool_bytes / layer_bytes(skv)))
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    pool = []
+    for i in range(n_layers):
+        gen.manual_seed(seed * 1000003 + skv * 131 + i)
+        cache = kvq.Int4KVCache(B, HKV, D, skv, G, device=dev)
+        # fill in slabs so the fp16 staging stays small
+        slab = 16384
+        for t0 in range(0, skv, slab):
+            n = min(slab, skv - t0)
+            k = torch.randn((B, HKV, n, D), generator=gen, device=dev, dtype=torch.float32).half()
+            v = torch.randn((B, HKV, n, D), generator=gen, device=dev, dtype=torch.float32).half()
+            kvq.quantize_kv_append(cache, t0, k, v)
+        q = torch.randn((B, HQ, D), generator=gen, device=dev, dtype=torch.float32).half()
+        k_new = torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.float32).half()
+        v_new = torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.float32).half()
+        ws = kvq.partials_buffers(B, HQ, D, skv, chunk, device=dev)
+        out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+        pool.append(dict(cache=cache, q=q, k_new=k_new, v_new=v_new, ws=ws, out=out))
+    torch.cuda.synchronize()
+    return pool
+
+
+def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None):
+    alpha = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    for i in range(n):
+        L = pool[i % len(pool)]
+        kvq.quantize_kv_append(L["cache"], skv - 1, L["k_new"], L["v_new"], stream=stream)
+        m, l, acc = L["ws"]
+        if events is not None:
+            events[i][0].record(stream)
+        kvq.sdpa_int4_partial(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, kernel=kernel, stream=stream)
+        if events is not None:
+            events[i][1].record(stream)
+        kvq.sdpa_int4_reduce(m, l, acc, L["out"], stream=stream)
+
+
+def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes):
+    pool = make_pool(kvq, torch, skv, pool_bytes, chunk)
+    run_steps(kvq, torch, pool, skv, chunk, kernel, warmup)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    run_steps(kvq, torch, pool, skv, chunk, kernel, steps)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / steps
+    # second pass of the same steps with HIP events around every partial launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    run_steps(kvq, torch, pool, skv, chunk, kernel, steps, events=evs)
+    torch.cuda.synchronize()
+    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    res = dict(skv=skv, ms_per_step=ms_per_step, partial_ms_avg=sum(kern_ms) / len(kern_ms),
+               partial_ms_p10=kern_ms[len(kern_ms) // 10], partial_ms_p90=kern_ms[(9 * len(kern_ms)) // 10],
+               pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv) / 1e6)
+    last = pool[-1]
+    del pool
+    return res, last
+
+
+def cpu_baseline(kvq, torch, entry, skv):
+    """Time the float64 oracle on one full layer-call of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    cache = entry["cache"]
+    oc = oracle.Cache(B, HKV, D, skv, G)
+    oc.k_q[...] = cache.k_q.cpu().numpy().view(np.uint32)
+    oc.v_q[...] = cache.v_q.cpu().numpy().view(np.uint32)
+    oc.k_scale[...] = cache.k_scale.cpu().numpy().view(np.uint16)
+    oc.k_bias[...] = cache.k_bias.cpu().numpy().view(np.uint16)
+    oc.v_scale[...] = cache.v_scale.cpu().numpy().view(np.uint16)
+    oc.v_bias[...] = cache.v_bias.cpu().numpy().view(np.uint16)
+    q = entry["q"].float().cpu().numpy()
+    threads = oracle.default_threads()
+    t = time.perf_counter()
+    ref = oracle.sdpa(oc, skv, q, 1.0 / math.sqrt(D), nthreads=threads)
+    dt = time.perf_counter() - t
+    # the GPU output of this layer must agree with it (a sanity line, not the parity test)
+    alpha = 1.0 / math.sqrt(D)
+    out = kvq.sdpa_int4(cache, skv, entry["q"], alpha)
+    torch.cuda.synchronize()
+    err = float(np.abs(out.cpu().numpy() - ref).max())
+    return dict(value=layer_bytes(skv) / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample="one full layer-call (64 q-heads, Skv=%d) of the float64 oracle, %.2f s wall" % (skv, dt),
+                seconds=dt, max_abs_err_vs_gpu=err)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--skv", type=int, default=131072)
+    ap.add_argument("--chunk", type=int, default=512)
+    ap.add_argument("--pool-mb", type=int, default=int(2.5 * MALL_BYTES / 1e6))
+    ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--sweep", default="1024,16384,65536",
+                    help="extra Skv values timed with fewer steps (empty to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode path would shard "
+              "over KV heads or sequence chunks; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_kv_cache_quantize_amd as kvq
+
+    kvq.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kernel = {"auto": kvq.KERNEL_AUTO, "valu": kvq.KERNEL_VALU, "mfma": kvq.KERNEL_MFMA}[args.kernel]
+    pool_bytes = args.pool_mb * 1000 * 1000
+
+    main_res, last = time_config(kvq, torch, args.skv, args.chunk, kernel, args.steps, args.warmup, pool_bytes)
+    sweep = []
+    for s in [int(x) for x in args.sweep.split(",") if x.strip()]:
+        r, _ = time_config(kvq, torch, s, args.chunk, kernel, max(20, args.steps // 2), args.warmup, pool_bytes)
+        r["us_per_layer"] = r["ms_per_step"] * 1e3
+        r["gbs"] = (layer_bytes(s) + append_bytes()) / (r["ms_per_step"] * 1e-3) / 1e9
+        r["partial_gbs"] = layer_bytes(s) / (r["partial_ms_avg"] * 1e-3) / 1e9
+        sweep.append(r)
+
+    step_bytes = layer_bytes(args.skv) + append_bytes()
+    ms = main_res["ms_per_step"]
+    value = step_bytes / (ms * 1e-3) / 1e9
+    achieved = layer_bytes(args.skv) / (main_res["partial_ms_avg"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(kvq, torch, last, args.skv)
+
+    line = {
+        "metric": "effective HBM GB/s (and us/layer) of int4-KV decode SDPA, Llama-70B layer",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_layer": round(ms * 1e3, 3),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes + fp16 scale/bias, f32 math",
+        "data": "synthetic (seeded fp16 N(0,1) K/V/Q drawn on the GPU, quantised by the library)",
+        "config": {
+            "workload": "Llama-3.1-70B-shaped decode layer: B1 Hq64 Hkv8 D128, int4 G64 fp16 scale+bias, "
+                        "alpha 1/sqrt(128), append 1 row + split-K partial + reduce",
+            "skv": args.skv,
+            "chunk": args.chunk,
+            "kernel": args.kernel,
+            "global_batch": B,
+            "seq_len": args.skv,
+            "parallelism": "single GPU",
+            "pool_layers": main_res["pool_layers"],
+            "pool_mb": round(main_res["pool_mb"], 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "sdpa_partial",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": layer_bytes(args.skv),
+            "avg_launch_us": round(main_res["partial_ms_avg"] * 1e3, 3),
+            "p10_launch_us": round(main_res["partial_ms_p10"] * 1e3, 3),
+            "p90_launch_us": round(main_res["partial_ms_p90"] * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+        "sweep": [{"skv": r["skv"], "us_per_layer": round(r["us_per_layer"], 3), "gbs": round(r["gbs"], 2),
+                   "partial_us": round(r["partial_ms_avg"] * 1e3, 3), "partial_gbs": round(r["partial_gbs"], 2)}
+                  for r in sweep],
+        "context": "pages' Apple-Silicon fused-kernel latency on this shape: 1.6/2.7/5.7/9.9 ms at 1K/16K/64K/128K",
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

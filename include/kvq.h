@@ -1,0 +1,160 @@
+/*
+ * kvq.h - C ABI for decode-time attention on an int4 group-affine KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What the operations are, from the source pages:
+ *  - "Fused int4 Attention for Gemma 4 31B on Apple Silicon", "Background:
+ *    Why TurboQuant Fails on Gemma 4": K/V stored as int4 codes with a scale
+ *    and a bias per group; "What I Built Instead": attention computed as
+ *    sdpa_int4(Q, K_int4, V_int4) -> output, dequantising in registers with
+ *    no float temporaries, nibbles read lowest first.
+ *  - "turboquant-llama3.170B" README: the kernel paragraph (per-element
+ *    dequantisation, Q.K^T, online softmax, no score matrix), the split-K
+ *    paragraph (512-token chunks computed independently, then a second phase
+ *    that reduces the partial softmax results, ordered after the first), the
+ *    decode-step listing (K and V quantised to int4 on append; GQA).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or synchronises, and keeps no global state; it is
+ *    safe to call from several threads.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued asynchronously on it; calls on one stream run in order,
+ *    so the reduce launched after the partial kernel on the same stream sees
+ *    its results without any event or host synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    negative status nothing was written. A fault during execution surfaces
+ *    at the caller's next synchronisation of the stream.
+ *  - Inputs must be finite and within fp16 range (|x| <= 65504); this is not
+ *    checked.
+ *
+ * Cache format (one layer):
+ *  - k_q, v_q: uint32 [B][Hkv][cap][D/8]. Dimension d of a row is code
+ *    (word[d/8] >> (4*(d%8))) & 0xF: eight codes per word, lowest nibble first.
+ *  - k_scale, k_bias, v_scale, v_bias: fp16 bit patterns [B][Hkv][cap][D/G];
+ *    element (t, d) dequantises to code * scale[t][d/G] + bias[t][d/G].
+ *  - Quantiser (per group of G values x): bias = largest fp16 <= min(x);
+ *    scale = smallest fp16 >= fl32(fl32(max(x) - bias) / 15); code =
+ *    clamp(rint(fl32(fl32(x - bias) / scale)), 0, 15), 0 if scale == 0;
+ *    fp32 round-to-nearest-even at every step; -0 metadata stored as +0.
+ *    This rule is this library's reading of "per-group scale + bias"; it is
+ *    bit-exact and keeps every value within scale/2 of its reconstruction.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_E_NULL = -1,        /* a required pointer is NULL */
+    KVQ_E_SHAPE = -2,       /* a size is out of range or inconsistent */
+    KVQ_E_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+    KVQ_E_CAPACITY = -4,    /* rows beyond the cache capacity */
+    KVQ_E_DTYPE = -5,       /* unknown element type */
+    KVQ_E_LAUNCH = -6,      /* the HIP runtime rejected a launch */
+    KVQ_E_UNSUPPORTED = -7  /* valid request that no kernel variant handles */
+} kvq_status;
+
+typedef enum kvq_dtype { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
+
+/* Kernel choice for the partial (split-K) phase. */
+typedef enum kvq_kernel {
+    KVQ_KERNEL_AUTO = 0,  /* fastest variant that supports the shape */
+    KVQ_KERNEL_VALU = 1,  /* vector-ALU kernel: any supported shape */
+    KVQ_KERNEL_MFMA = 2   /* matrix-core kernel: (Hq/Hkv) * (D/G) <= 16 */
+} kvq_kernel;
+
+/* One layer's quantised cache (all device pointers, 16-byte aligned). */
+typedef struct kvq_cache {
+    uint32_t *k_q;
+    uint32_t *v_q;
+    uint16_t *k_scale;
+    uint16_t *k_bias;
+    uint16_t *v_scale;
+    uint16_t *v_bias;
+    int32_t batch;     /* B >= 1 */
+    int32_t kv_heads;  /* Hkv >= 1 */
+    int32_t head_dim;  /* D in {64, 128, 256} */
+    int32_t group;     /* G in {32, 64, 128}, D % G == 0 */
+    int64_t capacity;  /* rows per (batch, KV head), >= 1 */
+} kvq_cache;
+
+/* Library version string, e.g. "kvq 0.1.0 gfx950". */
+const char *kvq_version(void);
+
+/* Human-readable name of a status code (never NULL). */
+const char *kvq_status_str(int status);
+
+/* Number of split-K chunks: ceil(skv / chunk); 0 if skv <= 0 or chunk <= 0. */
+int64_t kvq_num_chunks(int64_t skv, int32_t chunk);
+
+/* Bytes of one layer's cache: codes plus fp16 scale and bias for K and V,
+ * capacity rows per (batch, KV head); 0 for invalid sizes. */
+int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t group, int64_t capacity);
+
+/*
+ * Quantise n_new new rows of K and V and store them at rows
+ * [len, len + n_new) of the cache ("quantize K,V to int4" in the README's
+ * decode-step listing; prefill rows are appended the same way).
+ *
+ *  k_new, v_new: [B][Hkv][n_new][D] row-major, element type `dtype`
+ *                (KVQ_F16 or KVQ_F32), 16-byte aligned.
+ *  len:          rows already in the cache (0 <= len, len + n_new <= cap).
+ *  n_new == 0 is a no-op returning KVQ_OK.
+ * Rows outside [len, len + n_new) are not touched. The caller advances its
+ * own length; the library does not track it.
+ */
+int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new,
+                           int dtype, int64_t n_new, void *stream);
+
+/*
+ * Phase 1 of split-K decode attention ("turboquant-llama3.170B" README,
+ * split-K paragraph): one query row per head over cache rows [0, skv),
+ * cut into C = kvq_num_chunks(skv, chunk) chunks of `chunk` rows (the last
+ * may be shorter). For query head h (KV head h / (Hq / Hkv)) and chunk c,
+ * with scores s_t = softmax_scale * q_h . k^_t over the chunk's rows:
+ *   part_m[b][h][c]      = max_t s_t
+ *   part_l[b][h][c]      = sum_t exp(s_t - part_m)
+ *   part_acc[b][h][c][d] = sum_t exp(s_t - part_m) * v^_t[d]
+ * with k^, v^ dequantised in registers (no float K/V temporaries).
+ *
+ *  q:       [B][Hq][D], element type q_dtype (KVQ_F16 or KVQ_F32), 16-byte aligned.
+ *  Hq:      query heads, a multiple of Hkv.
+ *  chunk:   rows per chunk, >= 1 (512 is the tuned default).
+ *  part_*:  fp32 outputs sized [B][Hq][C] and [B][Hq][C][D], 16-byte aligned.
+ *  kernel:  KVQ_KERNEL_AUTO, or a forced variant (KVQ_E_UNSUPPORTED if it
+ *           cannot run this shape).
+ */
+int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
+                          float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
+                          int kernel, void *stream);
+
+/*
+ * Phase 2: combine the partials of kvq_sdpa_int4_partial (README split-K
+ * paragraph): with M = max_c m_c,
+ *   out[b][h][d] = sum_c e^{m_c - M} acc_c[d] / sum_c e^{m_c - M} l_c.
+ * Launch it on the same stream after the partial call.
+ *  out: fp32 [B][Hq][D], 16-byte aligned. C >= 1.
+ */
+int kvq_sdpa_int4_reduce(const float *part_m, const float *part_l, const float *part_acc, int32_t batch,
+                         int32_t Hq, int32_t head_dim, int64_t num_chunks, float *out, void *stream);
+
+/*
+ * Convenience: both phases back to back on `stream` (the pages' single
+ * sdpa_int4 call). The caller provides the partials workspace, sized as for
+ * kvq_sdpa_int4_partial.
+ */
+int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
+                  float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc, float *out,
+                  int kernel, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

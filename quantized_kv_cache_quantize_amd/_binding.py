@@ -1,0 +1,205 @@
+"""ctypes binding for libkvq.so: names mirror the C ABI in include/kvq.h."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+KVQ_F16, KVQ_F32 = 0, 1
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%d)" % (fn, status_str(status), status))
+        self.status = status
+
+
+class _Cache(C.Structure):
+    _fields_ = [
+        ("k_q", C.c_void_p),
+        ("v_q", C.c_void_p),
+        ("k_scale", C.c_void_p),
+        ("k_bias", C.c_void_p),
+        ("v_scale", C.c_void_p),
+        ("v_bias", C.c_void_p),
+        ("batch", C.c_int32),
+        ("kv_heads", C.c_int32),
+        ("head_dim", C.c_int32),
+        ("group", C.c_int32),
+        ("capacity", C.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libkvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libkvq.so not built: run __graft_entry__.build() or "
+                          "python -m quantized_kv_cache_quantize_amd.build")
+    L = C.CDLL(_LIB_PATH)
+    vp, i32, i64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_float
+    cp = C.POINTER(_Cache)
+    L.kvq_version.restype = C.c_char_p
+    L.kvq_version.argtypes = []
+    L.kvq_status_str.restype = C.c_char_p
+    L.kvq_status_str.argtypes = [C.c_int]
+    L.kvq_num_chunks.restype = i64
+    L.kvq_num_chunks.argtypes = [i64, i32]
+    L.kvq_cache_bytes.restype = i64
+    L.kvq_cache_bytes.argtypes = [i32, i32, i32, i32, i64]
+    L.kvq_quantize_kv_append.restype = C.c_int
+    L.kvq_quantize_kv_append.argtypes = [cp, i64, vp, vp, C.c_int, i64, vp]
+    L.kvq_sdpa_int4_partial.restype = C.c_int
+    L.kvq_sdpa_int4_partial.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, C.c_int, vp]
+    L.kvq_sdpa_int4_reduce.restype = C.c_int
+    L.kvq_sdpa_int4_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    L.kvq_sdpa_int4.restype = C.c_int
+    L.kvq_sdpa_int4.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int, vp]
+    _lib = L
+    return L
+
+
+def version() -> str:
+    return lib().kvq_version().decode()
+
+
+def status_str(status: int) -> str:
+    return lib().kvq_status_str(int(status)).decode()
+
+
+def num_chunks(skv: int, chunk: int) -> int:
+    return int(lib().kvq_num_chunks(int(skv), int(chunk)))
+
+
+def cache_bytes(batch: int, kv_heads: int, head_dim: int, group: int, capacity: int) -> int:
+    return int(lib().kvq_cache_bytes(batch, kv_heads, head_dim, group, capacity))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KvqError(fn, status)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return KVQ_F16
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    return 99  # rejected by the library with KVQ_E_DTYPE
+
+
+class Int4KVCache:
+    """One layer's int4 cache in device memory (allocated by PyTorch).
+
+    k_q, v_q: int32 tensors [B][Hkv][cap][D/8] holding the uint32 words;
+    k_scale, k_bias, v_scale, v_bias: float16 [B][Hkv][cap][D/G]."""
+
+    def __init__(self, batch: int, kv_heads: int, head_dim: int, capacity: int, group: int = 64,
+                 device="cuda", tensors=None):
+        self.batch, self.kv_heads, self.head_dim = batch, kv_heads, head_dim
+        self.capacity, self.group = capacity, group
+        if tensors is not None:
+            self.k_q, self.v_q, self.k_scale, self.k_bias, self.v_scale, self.v_bias = tensors
+        else:
+            wshape = (batch, kv_heads, capacity, head_dim // 8)
+            sshape = (batch, kv_heads, capacity, head_dim // group)
+            self.k_q = torch.zeros(wshape, dtype=torch.int32, device=device)
+            self.v_q = torch.zeros(wshape, dtype=torch.int32, device=device)
+            self.k_scale = torch.zeros(sshape, dtype=torch.float16, device=device)
+            self.k_bias = torch.zeros(sshape, dtype=torch.float16, device=device)
+            self.v_scale = torch.zeros(sshape, dtype=torch.float16, device=device)
+            self.v_bias = torch.zeros(sshape, dtype=torch.float16, device=device)
+
+    def c_struct(self) -> _Cache:
+        return _Cache(_ptr(self.k_q), _ptr(self.v_q), _ptr(self.k_scale), _ptr(self.k_bias), _ptr(self.v_scale),
+                      _ptr(self.v_bias), self.batch, self.kv_heads, self.head_dim, self.group, self.capacity)
+
+    def nbytes(self) -> int:
+        return cache_bytes(self.batch, self.kv_heads, self.head_dim, self.group, self.capacity)
+
+    def tensors(self):
+        return (self.k_q, self.v_q, self.k_scale, self.k_bias, self.v_scale, self.v_bias)
+
+
+def quantize_kv_append(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                       stream=None) -> None:
+    """kvq_quantize_kv_append: quantise k_new, v_new [B][Hkv][n][D] (fp16 or
+    fp32, contiguous) into cache rows [length, length + n)."""
+    assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
+    n = k_new.shape[2] if k_new.dim() == 4 else 0
+    cs = cache.c_struct()
+    _check("kvq_quantize_kv_append",
+           lib().kvq_quantize_kv_append(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                        int(n), _stream(stream)))
+
+
+def partials_buffers(batch: int, hq: int, head_dim: int, skv: int, chunk: int = 512, device="cuda"):
+    """Allocate (part_m, part_l, part_acc) for the split-K workspace."""
+    nc = num_chunks(skv, chunk)
+    m = torch.empty((batch, hq, nc), dtype=torch.float32, device=device)
+    l = torch.empty((batch, hq, nc), dtype=torch.float32, device=device)
+    acc = torch.empty((batch, hq, nc, head_dim), dtype=torch.float32, device=device)
+    return m, l, acc
+
+
+def sdpa_int4_partial(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int,
+                      part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor,
+                      kernel: int = KERNEL_AUTO, stream=None) -> None:
+    """kvq_sdpa_int4_partial: q [B][Hq][D] fp16/fp32 contiguous."""
+    assert q.is_contiguous()
+    cs = cache.c_struct()
+    _check("kvq_sdpa_int4_partial",
+           lib().kvq_sdpa_int4_partial(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), int(q.shape[1]),
+                                       float(softmax_scale), int(chunk), _ptr(part_m), _ptr(part_l),
+                                       _ptr(part_acc), int(kernel), _stream(stream)))
+
+
+def sdpa_int4_reduce(part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor, out: torch.Tensor,
+                     stream=None) -> None:
+    """kvq_sdpa_int4_reduce: out [B][Hq][D] fp32."""
+    b, hq, nc, d = part_acc.shape
+    _check("kvq_sdpa_int4_reduce",
+           lib().kvq_sdpa_int4_reduce(_ptr(part_m), _ptr(part_l), _ptr(part_acc), b, hq, d, nc, _ptr(out),
+                                      _stream(stream)))
+
+
+def sdpa_int4(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int = 512,
+              out: torch.Tensor | None = None, workspace=None, kernel: int = KERNEL_AUTO, stream=None):
+    """kvq_sdpa_int4: both phases on one stream; returns out [B][Hq][D] fp32."""
+    assert q.is_contiguous()
+    b, hq, d = q.shape
+    if workspace is None:
+        workspace = partials_buffers(b, hq, d, skv, chunk, device=q.device)
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+    m, l, acc = workspace
+    cs = cache.c_struct()
+    _check("kvq_sdpa_int4",
+           lib().kvq_sdpa_int4(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), hq, float(softmax_scale),
+                               int(chunk), _ptr(m), _ptr(l), _ptr(acc), _ptr(out), int(kernel), _stream(stream)))
+    return out

@@ -1,0 +1,219 @@
+// C-ABI entry points of libkvq: argument validation on the host, then
+// kernel launches on the caller's stream. Nothing here allocates, frees or
+// synchronises. Every check runs before the first HIP call, so an invalid
+// request returns its status without touching the device (and without
+// needing one).
+#include <math.h>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_cache(const kvq_cache *c)
+{
+    if (!c)
+        return KVQ_E_NULL;
+    if (!c->k_q || !c->v_q || !c->k_scale || !c->k_bias || !c->v_scale || !c->v_bias)
+        return KVQ_E_NULL;
+    if (c->batch < 1 || c->batch > 65535 || c->kv_heads < 1 || c->kv_heads > 65535 || c->capacity < 1)
+        return KVQ_E_SHAPE;
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+        return KVQ_E_SHAPE;
+    if (c->group != 32 && c->group != 64 && c->group != 128)
+        return KVQ_E_SHAPE;
+    if (c->head_dim % c->group != 0)
+        return KVQ_E_SHAPE;
+    // keep every element index far inside int64
+    if (c->capacity > ((int64_t)1 << 40) / ((int64_t)c->batch * c->kv_heads))
+        return KVQ_E_SHAPE;
+    if (!aligned16(c->k_q) || !aligned16(c->v_q) || !aligned16(c->k_scale) || !aligned16(c->k_bias) ||
+        !aligned16(c->v_scale) || !aligned16(c->v_bias))
+        return KVQ_E_ALIGN;
+    return KVQ_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_version(void) { return "kvq 0.1.0 gfx950"; }
+
+const char *kvq_status_str(int status)
+{
+    switch (status) {
+    case KVQ_OK:
+        return "ok";
+    case KVQ_E_NULL:
+        return "null pointer";
+    case KVQ_E_SHAPE:
+        return "invalid size or shape";
+    case KVQ_E_ALIGN:
+        return "pointer not 16-byte aligned";
+    case KVQ_E_CAPACITY:
+        return "rows beyond cache capacity";
+    case KVQ_E_DTYPE:
+        return "unknown element type";
+    case KVQ_E_LAUNCH:
+        return "kernel launch failed";
+    case KVQ_E_UNSUPPORTED:
+        return "shape not supported by the requested kernel";
+    default:
+        return "unknown status";
+    }
+}
+
+int64_t kvq_num_chunks(int64_t skv, int32_t chunk)
+{
+    if (skv <= 0 || chunk <= 0)
+        return 0;
+    return (skv + chunk - 1) / chunk;
+}
+
+int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t group, int64_t capacity)
+{
+    if (batch < 1 || kv_heads < 1 || head_dim < 8 || head_dim % 8 || group < 1 || head_dim % group || capacity < 1)
+        return 0;
+    const int64_t rows = (int64_t)batch * kv_heads * capacity;
+    const int64_t per_row = head_dim / 2 + 2 * 2 * (head_dim / group);  // codes + fp16 scale and bias
+    return 2 * rows * per_row;                                         // K and V
+}
+
+int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int dtype,
+                           int64_t n_new, void *stream)
+{
+    int st = check_cache(cache);
+    if (st)
+        return st;
+    if (dtype != KVQ_F16 && dtype != KVQ_F32)
+        return KVQ_E_DTYPE;
+    if (len < 0 || n_new < 0)
+        return KVQ_E_SHAPE;
+    if (len > cache->capacity || n_new > cache->capacity - len)
+        return KVQ_E_CAPACITY;
+    if (n_new == 0)
+        return KVQ_OK;
+    if (!k_new || !v_new)
+        return KVQ_E_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return KVQ_E_ALIGN;
+    const int64_t rows = (int64_t)cache->batch * cache->kv_heads * n_new;
+    if ((rows * (cache->head_dim / 8) + 255) / 256 > 0x7fffffff)
+        return KVQ_E_SHAPE;
+
+    QuantizeArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_q = cache->k_q;
+    a.v_q = cache->v_q;
+    a.k_scale = cache->k_scale;
+    a.k_bias = cache->k_bias;
+    a.v_scale = cache->v_scale;
+    a.v_bias = cache->v_bias;
+    a.rows = rows;
+    a.n_new = n_new;
+    a.len = len;
+    a.cap = cache->capacity;
+    a.D = cache->head_dim;
+    a.G = cache->group;
+    return launch_status(launch_quantize(a, dtype, (hipStream_t)stream));
+}
+
+int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
+                          float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
+                          int kernel, void *stream)
+{
+    int st = check_cache(cache);
+    if (st)
+        return st;
+    if (!q || !part_m || !part_l || !part_acc)
+        return KVQ_E_NULL;
+    if (q_dtype != KVQ_F16 && q_dtype != KVQ_F32)
+        return KVQ_E_DTYPE;
+    if (skv < 1 || chunk < 1 || Hq < 1 || Hq % cache->kv_heads != 0 || !isfinite(softmax_scale))
+        return KVQ_E_SHAPE;
+    if ((int64_t)cache->batch * Hq > 0x7fffffff)
+        return KVQ_E_SHAPE;
+    if (skv > cache->capacity)
+        return KVQ_E_CAPACITY;
+    if (!aligned16(q) || !aligned16(part_m) || !aligned16(part_l) || !aligned16(part_acc))
+        return KVQ_E_ALIGN;
+    const int64_t C = kvq_num_chunks(skv, chunk);
+    if (C > 0x7fffffff)
+        return KVQ_E_SHAPE;
+    if (kernel != KVQ_KERNEL_AUTO && kernel != KVQ_KERNEL_VALU && kernel != KVQ_KERNEL_MFMA)
+        return KVQ_E_SHAPE;
+    const int n_rep = Hq / cache->kv_heads;
+    const bool mfma_ok = mfma_supports(cache->head_dim, cache->group, n_rep, chunk);
+    if (kernel == KVQ_KERNEL_MFMA && !mfma_ok)
+        return KVQ_E_UNSUPPORTED;
+
+    PartialArgs a;
+    a.k_q = cache->k_q;
+    a.v_q = cache->v_q;
+    a.k_scale = cache->k_scale;
+    a.k_bias = cache->k_bias;
+    a.v_scale = cache->v_scale;
+    a.v_bias = cache->v_bias;
+    a.q = q;
+    a.part_m = part_m;
+    a.part_l = part_l;
+    a.part_acc = part_acc;
+    a.cap = cache->capacity;
+    a.skv = skv;
+    a.num_chunks = C;
+    a.chunk = chunk;
+    a.Hkv = cache->kv_heads;
+    a.Hq = Hq;
+    a.n_rep = n_rep;
+    a.G = cache->group;
+    a.score_scale = softmax_scale * kLog2e;
+    const bool use_mfma = kernel == KVQ_KERNEL_MFMA || (kernel == KVQ_KERNEL_AUTO && mfma_ok);
+    hipError_t e = use_mfma ? launch_partial_mfma(a, cache->head_dim, q_dtype, cache->batch, (hipStream_t)stream)
+                            : launch_partial_valu(a, cache->head_dim, q_dtype, cache->batch, (hipStream_t)stream);
+    return launch_status(e);
+}
+
+int kvq_sdpa_int4_reduce(const float *part_m, const float *part_l, const float *part_acc, int32_t batch, int32_t Hq,
+                         int32_t head_dim, int64_t num_chunks, float *out, void *stream)
+{
+    if (!part_m || !part_l || !part_acc || !out)
+        return KVQ_E_NULL;
+    if (batch < 1 || Hq < 1 || num_chunks < 1 || (int64_t)batch * Hq > 0x7fffffff)
+        return KVQ_E_SHAPE;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return KVQ_E_SHAPE;
+    if (!aligned16(part_m) || !aligned16(part_l) || !aligned16(part_acc) || !aligned16(out))
+        return KVQ_E_ALIGN;
+    ReduceArgs a;
+    a.part_m = part_m;
+    a.part_l = part_l;
+    a.part_acc = part_acc;
+    a.out = out;
+    a.heads = (int64_t)batch * Hq;
+    a.C = num_chunks;
+    a.D = head_dim;
+    return launch_status(launch_reduce(a, (hipStream_t)stream));
+}
+
+int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
+                  int32_t chunk, float *part_m, float *part_l, float *part_acc, float *out, int kernel, void *stream)
+{
+    if (!out)
+        return KVQ_E_NULL;
+    if (!aligned16(out))
+        return KVQ_E_ALIGN;
+    int st = kvq_sdpa_int4_partial(cache, skv, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l, part_acc,
+                                   kernel, stream);
+    if (st)
+        return st;
+    return kvq_sdpa_int4_reduce(part_m, part_l, part_acc, cache->batch, Hq, cache->head_dim,
+                                kvq_num_chunks(skv, chunk), out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal declarations shared by the kvq HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// log2(e) in fp32; scores are kept pre-multiplied by it so that softmax
+// weights come from the hardware exp2.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct QuantizeArgs {
+    const void *k_new;
+    const void *v_new;
+    uint32_t *k_q;
+    uint32_t *v_q;
+    uint16_t *k_scale;
+    uint16_t *k_bias;
+    uint16_t *v_scale;
+    uint16_t *v_bias;
+    int64_t rows;     // B * Hkv * n_new
+    int64_t n_new;
+    int64_t len;
+    int64_t cap;
+    int32_t D;
+    int32_t G;
+};
+
+struct PartialArgs {
+    const uint32_t *k_q;
+    const uint32_t *v_q;
+    const uint16_t *k_scale;
+    const uint16_t *k_bias;
+    const uint16_t *v_scale;
+    const uint16_t *v_bias;
+    const void *q;
+    float *part_m;
+    float *part_l;
+    float *part_acc;
+    int64_t cap;
+    int64_t skv;
+    int64_t num_chunks;
+    int32_t chunk;
+    int32_t Hkv;
+    int32_t Hq;
+    int32_t n_rep;
+    int32_t G;
+    float score_scale;  // softmax_scale * log2(e)
+};
+
+struct ReduceArgs {
+    const float *part_m;
+    const float *part_l;
+    const float *part_acc;
+    float *out;
+    int64_t heads;  // B * Hq
+    int64_t C;
+    int32_t D;
+};
+
+hipError_t launch_quantize(const QuantizeArgs &a, int dtype, hipStream_t s);
+hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s);
+bool mfma_supports(int D, int G, int n_rep, int chunk);
+hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
+
+}  // namespace kvq

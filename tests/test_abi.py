@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/kvq.h declares, rejects invalid requests before any
+launch, and its byte accounting matches the pages' memory table.
+
+Every call below fails validation (or is a no-op), so nothing is ever
+launched with the placeholder pointers used here."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_kv_cache_quantize_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_CAP, E_DTYPE, E_LAUNCH, E_UNSUP = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x100000  # placeholder "device" address, 16-byte aligned; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"kvq_quantize_kv_append", "kvq_sdpa_int4_partial", "kvq_sdpa_int4_reduce"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kvq_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_version_and_status_strings(L):
+    assert "gfx950" in B.version()
+    for s in (OK, E_NULL, E_SHAPE, E_ALIGN, E_CAP, E_DTYPE, E_LAUNCH, E_UNSUP):
+        assert B.status_str(s) and B.status_str(s) != "unknown status"
+    assert B.status_str(12345) == "unknown status"
+
+
+def test_num_chunks(L):
+    assert B.num_chunks(1024, 512) == 2
+    assert B.num_chunks(1025, 512) == 3
+    assert B.num_chunks(1, 512) == 1
+    assert B.num_chunks(131072, 512) == 256
+    assert B.num_chunks(0, 512) == 0 and B.num_chunks(10, 0) == 0
+
+
+def test_cache_bytes_formula(L):
+    # 128 dims: 64 B codes + 2 groups x (2 B scale + 2 B bias) = 72 B per row, x2 for K and V
+    assert B.cache_bytes(1, 8, 128, 64, 1) == 8 * 144
+    assert B.cache_bytes(1, 16, 256, 64, 10) == 16 * 10 * 288
+    assert B.cache_bytes(1, 8, 128, 64, 131072) == 150994944
+    assert B.cache_bytes(0, 8, 128, 64, 1) == 0 and B.cache_bytes(1, 8, 100, 64, 1) == 0
+
+
+def test_memory_table_golden(L):
+    """The README's fp16 column follows from its own formula; its int4 column
+    is 3.2x smaller (5 bits per value); this library's format stores 4.5 bits
+    per value (4-bit codes + fp16 scale and bias per 64 values)."""
+    rows = [l.split() for l in open(os.path.join(ROOT, "tests", "golden", "kv_memory_table.txt"))
+            if l.strip() and not l.startswith("#")]
+    gib = float(1 << 30)
+    for ctx, fp16_gb, int4_gb in rows:
+        ctx, fp16_gb, int4_gb = int(ctx), float(fp16_gb), float(int4_gb)
+        fp16 = 80 * 8 * ctx * 128 * 2 * 2
+        assert round(fp16 / gib, 1) == fp16_gb
+        assert abs(fp16 / 3.2 / gib - int4_gb) <= 0.05 + 1e-9  # printed to one decimal
+        ours = 80 * B.cache_bytes(1, 8, 128, 64, ctx)
+        assert ours * 16 == fp16 * 4.5
+
+
+def _cache(**kw):
+    c = dict(k_q=P, v_q=P, k_scale=P, k_bias=P, v_scale=P, v_bias=P, batch=1, kv_heads=8, head_dim=128,
+             group=64, capacity=1024)
+    c.update(kw)
+    return B._Cache(**c)
+
+
+def _append(L, cache, length=0, k=P, v=P, dtype=0, n=1):
+    return L.kvq_quantize_kv_append(C.byref(cache) if cache is not None else None, length, k, v, dtype, n, None)
+
+
+def _partial(L, cache, skv=100, q=P, qd=0, hq=64, scale=0.1, chunk=512, m=P, l=P, acc=P, kernel=0):
+    return L.kvq_sdpa_int4_partial(C.byref(cache) if cache is not None else None, skv, q, qd, hq, scale, chunk, m,
+                                   l, acc, kernel, None)
+
+
+def test_append_validation(L):
+    assert _append(L, None) == E_NULL
+    assert _append(L, _cache(k_q=None)) == E_NULL
+    assert _append(L, _cache(head_dim=96)) == E_SHAPE
+    assert _append(L, _cache(group=48)) == E_SHAPE
+    assert _append(L, _cache(head_dim=64, group=128)) == E_SHAPE
+    assert _append(L, _cache(batch=0)) == E_SHAPE
+    assert _append(L, _cache(capacity=0)) == E_SHAPE
+    assert _append(L, _cache(v_bias=P + 2)) == E_ALIGN
+    assert _append(L, _cache(), dtype=7) == E_DTYPE
+    assert _append(L, _cache(), length=-1) == E_SHAPE
+    assert _append(L, _cache(), n=-1) == E_SHAPE
+    assert _append(L, _cache(capacity=10), length=8, n=3) == E_CAP
+    assert _append(L, _cache(capacity=10), length=11, n=0) == E_CAP
+    assert _append(L, _cache(), k=None) == E_NULL
+    assert _append(L, _cache(), v=P + 8) == E_ALIGN
+    # zero new rows is a no-op that succeeds without touching the device
+    assert _append(L, _cache(capacity=10), length=10, n=0) == OK
+
+
+def test_partial_validation(L):
+    assert _partial(L, None) == E_NULL
+    assert _partial(L, _cache(), q=None) == E_NULL
+    assert _partial(L, _cache(), acc=None) == E_NULL
+    assert _partial(L, _cache(), qd=3) == E_DTYPE
+    assert _partial(L, _cache(), skv=0) == E_SHAPE
+    assert _partial(L, _cache(), chunk=0) == E_SHAPE
+    assert _partial(L, _cache(), hq=12) == E_SHAPE          # not a multiple of 8 KV heads
+    assert _partial(L, _cache(), scale=float("inf")) == E_SHAPE
+    assert _partial(L, _cache(), scale=float("nan")) == E_SHAPE
+    assert _partial(L, _cache(capacity=64), skv=65) == E_CAP
+    assert _partial(L, _cache(), q=P + 4) == E_ALIGN
+    assert _partial(L, _cache(), m=P + 4) == E_ALIGN
+    assert _partial(L, _cache(), kernel=9) == E_SHAPE
+    # 16 query heads per KV head at D=256, G=32: beyond any matrix-core tile
+    assert _partial(L, _cache(kv_heads=1, head_dim=256, group=32), hq=16, kernel=2) == E_UNSUP
+
+
+def test_reduce_validation(L):
+    f = L.kvq_sdpa_int4_reduce
+    assert f(None, P, P, 1, 64, 128, 4, P, None) == E_NULL
+    assert f(P, P, P, 1, 64, 128, 4, None, None) == E_NULL
+    assert f(P, P, P, 0, 64, 128, 4, P, None) == E_SHAPE
+    assert f(P, P, P, 1, 64, 96, 4, P, None) == E_SHAPE
+    assert f(P, P, P, 1, 64, 128, 0, P, None) == E_SHAPE
+    assert f(P, P, P + 4, 1, 64, 128, 4, P, None) == E_ALIGN
+
+
+def test_fused_validation(L):
+    c = _cache()
+    assert L.kvq_sdpa_int4(C.byref(c), 100, P, 0, 64, 0.1, 512, P, P, P, None, 0, None) == E_NULL
+    assert L.kvq_sdpa_int4(C.byref(c), 0, P, 0, 64, 0.1, 512, P, P, P, P, 0, None) == E_SHAPE
