@@ -14,6 +14,10 @@ pytestmark = pytest.mark.gpu
 
 # Per-head relative L2 gates. The vector-ALU kernel works in fp32 throughout.
 REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: 2e-5, kvq.KERNEL_MFMA: 2e-5}
+# With softmax scale 1 and normalised Q/K the scores reach O(100); their fp32
+# rounding (~sqrt(D) * 2^-24 * sum|q k|) passes undamped into the weights, so
+# the per-head L2 gate there is set one decade wider.
+REL_L2_UNSCALED = 2e-4
 KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_AUTO]
 
 
@@ -88,7 +92,7 @@ def test_gemma_unscaled(kernel, skv):
     q, k, v, alpha = kvq_synth.gemma_layer(skv)
     oc = _oracle_cache(k, v)
     out, *_ = run_sdpa(gpu_cache_from_oracle(oc), skv, q, alpha, kernel=kernel)
-    check_attention(out, oracle.sdpa(oc, skv, q, alpha), REL_L2[kernel], atol=1e-3, rtol=1e-3, label="gemma")
+    check_attention(out, oracle.sdpa(oc, skv, q, alpha), REL_L2_UNSCALED, atol=1e-3, rtol=1e-3, label="gemma")
 
 
 def _llama_gpu_cache(skv):
