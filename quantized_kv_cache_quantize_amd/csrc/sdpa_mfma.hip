@@ -1,10 +1,509 @@
-// Split-K decode attention on the int4 cache, matrix-core variant (pending).
+// Split-K decode attention on the int4 cache, matrix-core variant for gfx950.
+//
+// Same contract as the vector-ALU kernel (phase 1 of the split-K scheme in
+// the "turboquant-llama3.170B" README: per (KV head, 512-row chunk) partial
+// softmax state), but the two contractions run on v_mfma_f32_16x16x32_f16.
+// With GQA the n_rep query heads of a KV head share every K and V row, so the
+// decode step is a skinny dense product, (n_rep x D) . (D x T) for scores and
+// (n_rep x T) . (T x D) for values; at 8 query heads per KV head it needs
+// 14.2 multiply-adds per cache byte, more than the fp32 vector ALU delivers
+// at HBM speed.
+//
+// Exactness of the fp16 operands:
+//  - codes enter as the exact fp16 integers code - 8 (magic-number unpack and
+//    an exact fp16 subtraction; see unpack_halves for why they are centred);
+//  - fp16 Q is exact; fp32 Q is split into hi + lo fp16 halves (two MFMAs);
+//  - the value weights p * scale_v are split into hi + lo fp16 halves (two
+//    MFMAs), so about 22 bits of each weight survive;
+//  - products of these operands are exact in the fp32 accumulators.
+// Scale and bias are applied outside the matrix core, per group, as in
+// "What I Built Instead" (Gemma page): q . k^ = sum_g s_g (q . code)_g +
+// b_g (sum q)_g, and sum_t p v^ = sum_t (p s_v) code + sum_t p b_v.
+//
+// Score GEMM: S[t][(h,g)] = Kcodes[t][:] . Qg[(h,g)][:], where column (h,g)
+// of Qg holds query head h restricted to scale group g (zeros elsewhere), so
+// each group's partial dot product comes out separately. 16 columns cover
+// n_rep * (D/G) <= 16. K rows are the A operand: a lane loads 16 bytes (32
+// nibbles) of one row; the contraction order of dimensions is permuted
+// identically in Qg.
+//
+// Value GEMM: O[(h,g)][d] += P'_g[(h,g)][t] . Vcodes[t][d]; rows whose group g
+// differs from the group of column d are discarded. A lane holds 8 rows of
+// one output column, so the V words of its 8 rows are transposed nibble-pair
+// by nibble-pair with v_perm while unpacking.
+//
+// Softmax: each wavefront takes every fourth 32-row tile of the chunk and
+// keeps an online softmax across its tiles (the accumulator is rescaled only
+// when some head's running max rises); the four wavefronts are merged at the
+// end. Scale and bias of K and V are staged in LDS per 512-row round; the
+// next tile's K and V words are loaded while the current tile is computed.
 #include "kvq_internal.h"
 
 namespace kvq {
+namespace {
 
-bool mfma_supports(int, int, int, int) { return false; }
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 
-hipError_t launch_partial_mfma(const PartialArgs &, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
+constexpr int NT = 256;         // threads per workgroup
+constexpr int TILE = 32;        // rows per tile
+constexpr int MAXT = 4;         // tiles per wavefront per round
+constexpr int ROUND = 4 * MAXT * TILE;  // 512 rows
+// Occupancy target (wavefronts per SIMD) for D = 128; D = 256 needs the
+// whole register file of one wavefront.
+#ifndef WAVES_D128
+#define WAVES_D128 2
+#endif
+
+__device__ __forceinline__ float h_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+__device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
+__device__ __forceinline__ uint32_t as_u32(half2v x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Four half2 registers -> one MFMA operand.
+__device__ __forceinline__ half8 cat8(half2v a, half2v b, half2v c, half2v d)
+{
+    half8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+// The four nibbles of each 16-bit half of x as exact fp16 values n - 8:
+// out[m] = (nibble m of the low half, nibble m of the high half) - 8.
+// A nibble placed in mantissa bits 0-3 under exponent 2^10 (0x6400) reads as
+// 1024 + n; in bits 4-7 under 2^6 (0x5400) as 64 + n. Nibbles 2 and 3 are
+// first shifted down by 8 (an fp16 mantissa has only bits 0-9). The fp16
+// subtraction of 1032 or 72 is exact.
+//
+// Why centred codes: the matrix core aligns the 32 products of one
+// instruction to the largest and truncates the rest, which biases sums of
+// same-signed products toward zero. Codes in [-8, 7] give products of both
+// signs and half the magnitude, and the 8 * scale they drop moves into the
+// bias term: code * s + b = (code - 8) * s + (b + 8 s).
+__device__ __forceinline__ void unpack_halves(uint32_t x, half2v (&out)[4])
+{
+    const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
+    const uint32_t y = x >> 8;
+    out[0] = as_h2((x & 0x000F000Fu) | 0x64006400u) - k1032;
+    out[1] = as_h2((x & 0x00F000F0u) | 0x54005400u) - k72;
+    out[2] = as_h2((y & 0x000F000Fu) | 0x64006400u) - k1032;
+    out[3] = as_h2((y & 0x00F000F0u) | 0x54005400u) - k72;
+}
+
+// One K word (dimensions 8w..8w+7 of one row) as an MFMA operand; element j
+// holds dimension 8w + kPerm[j].
+constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+__device__ __forceinline__ half8 unpack_k_word(uint32_t w)
+{
+    half2v h[4];
+    unpack_halves(w, h);
+    return cat8(h[0], h[1], h[2], h[3]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the NG adjacent lanes that hold the groups of one head.
+template <int NG>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if constexpr (NG >= 2)
+        v += dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (NG >= 4)
+        v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (NG >= 8)
+        v += __shfl_xor(v, 4);
+    return v;
+}
+
+__device__ __forceinline__ float quarter_max(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ __forceinline__ float quarter_sum(float v)
+{
+    v += __shfl_xor(v, 16);
+    return v + __shfl_xor(v, 32);
+}
+
+__device__ __forceinline__ void h4_to_f32(uint2 v, float (&out)[4])
+{
+    out[0] = h_val(v.x & 0xFFFF);
+    out[1] = h_val(v.x >> 16);
+    out[2] = h_val(v.y & 0xFFFF);
+    out[3] = h_val(v.y >> 16);
+}
+
+template <int D, int NG, bool Q32>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 128 ? WAVES_D128 : 1)))
+void sdpa_partial_mfma_kernel(PartialArgs a)
+{
+    constexpr int W = D / 8;        // words per row
+    constexpr int WPL = W / 4;      // K words per lane per 16-row block
+    constexpr int KM = W / 4;       // score MFMAs per 16-row block (32 dims each)
+    constexpr int VS = W / 16;      // value column sets of 16 words
+    constexpr int WPG = W / NG;     // words per scale group
+    constexpr int MAXH = 16 / NG;   // most query heads per KV head
+    constexpr int META_HALVES = 4 * NG * ROUND;         // K scale, K bias, V scale, V bias
+    constexpr int OUT_FLOATS = 4 * MAXH * D;            // per-wavefront outputs for the merge
+    constexpr int SMEM_BYTES = (META_HALVES * 2 > OUT_FLOATS * 4) ? META_HALVES * 2 : OUT_FLOATS * 4;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q4 = lane >> 4;
+    const int col = lane & 15;
+    const int c = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int nrep = a.n_rep;
+    const int R = nrep * NG;
+    const int hl = col / NG, gl = col % NG;
+    const bool col_on = col < R;
+    const int h0 = kvh * nrep;
+
+    // Rows are counted inside one (batch, KV head); capacity * D/8 < 2^31 is
+    // checked on the host, so 32-bit offsets from per-head bases suffice.
+    const int t0 = (int)((int64_t)c * a.chunk);
+    const int t1 = (int)min((int64_t)t0 + a.chunk, a.skv);
+    const int last = t1 - 1;
+    const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
+    const uint32_t *kq = a.k_q + kvrow0 * W;
+    const uint32_t *vq = a.v_q + kvrow0 * W;
+    const uint16_t *ksc = a.k_scale + kvrow0 * NG;
+    const uint16_t *kbi = a.k_bias + kvrow0 * NG;
+    const uint16_t *vsc = a.v_scale + kvrow0 * NG;
+    const uint16_t *vbi = a.v_bias + kvrow0 * NG;
+
+    __shared__ __align__(16) unsigned char smem[SMEM_BYTES];
+    __shared__ float m_s[4][16];
+    __shared__ float l_s[4][16];
+    uint16_t *meta = reinterpret_cast<uint16_t *>(smem);  // [4][NG][ROUND]
+
+    // ---- Q operand (B of the score GEMM) and per-group sums of q. Every lane
+    //      loads the 8 dimensions of each of its words unconditionally (lanes
+    //      of unused columns read head 0), so all loads are in flight at once;
+    //      entries outside the lane's (head, group) are zeroed afterwards.
+    half8 qhi[KM], qlo[KM];
+    float qsum = 0.0f;
+    {
+        const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
+        float qv[KM][8];
+#pragma unroll
+        for (int u = 0; u < KM; ++u) {
+            const int word = WPL * q4 + u;
+            if constexpr (Q32) {
+                const float4 x0 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow + 8 * word);
+                const float4 x1 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow + 8 * word + 4);
+                qv[u][0] = x0.x; qv[u][1] = x0.y; qv[u][2] = x0.z; qv[u][3] = x0.w;
+                qv[u][4] = x1.x; qv[u][5] = x1.y; qv[u][6] = x1.z; qv[u][7] = x1.w;
+            } else {
+                const half8 x = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow + 8 * word);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    qv[u][j] = (float)x[j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < KM; ++u) {
+            const int word = WPL * q4 + u;
+            const bool mine = col_on && (word / WPG) == gl;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = mine ? qv[u][kPerm[j]] : 0.0f;
+                qsum += x;
+                const _Float16 hi = (_Float16)x;
+                qhi[u][j] = hi;
+                if constexpr (Q32)
+                    qlo[u][j] = (_Float16)(x - (float)hi);
+            }
+        }
+        qsum = quarter_sum(qsum);
+    }
+
+    const float cs = a.score_scale;
+    float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
+    float4v acc[VS][8];
+#pragma unroll
+    for (int s = 0; s < VS; ++s)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[s][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int rb = t0; rb < t1; rb += ROUND) {
+        const int ntile = (min(rb + ROUND, t1) - rb + TILE - 1) / TILE;
+
+        // ---- stage this round's scale and bias of K and V in LDS as
+        //      [array][group][row]; rows past the end repeat the last row.
+        //      All loads are issued before the first LDS write.
+        __syncthreads();  // the previous round's readers are done
+        {
+            constexpr int PER = META_HALVES / NT;  // halves per thread
+            constexpr int ARR = NG * ROUND;        // halves per array
+            static_assert(ARR % NT == 0, "each array is a whole number of thread sweeps");
+            uint16_t tmp[PER];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int arr = (i * NT) / ARR;  // compile-time after unrolling
+                const int rem = threadIdx.x + (i * NT) % ARR;
+                const int r = rem / NG, g = rem - r * NG;
+                const int row = min(rb + r, last);
+                const uint16_t *src = arr == 0 ? ksc : arr == 1 ? kbi : arr == 2 ? vsc : vbi;
+                tmp[i] = src[(uint32_t)(row * NG + g)];
+            }
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int arr = (i * NT) / ARR;
+                const int rem = threadIdx.x + (i * NT) % ARR;
+                const int r = rem / NG, g = rem - r * NG;
+                meta[(arr * NG + g) * ROUND + r] = tmp[i];
+            }
+        }
+
+        __syncthreads();  // metadata staged
+
+        // ---- this wavefront's tiles of the round: ti = wave + 4k, k < kn
+        const int kn = (ntile - wave + 3) / 4;  // uniform; <= MAXT
+        uint4 kcur[2][WPL / 4], knext[2][WPL / 4];
+        uint32_t vcur[VS][8], vnext[VS][8];
+        auto load_tile = [&](int ti, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int row = min(rb + TILE * ti + 16 * blk + col, last);
+#pragma unroll
+                for (int v4 = 0; v4 < WPL / 4; ++v4)
+                    kt[blk][v4] = *reinterpret_cast<const uint4 *>(kq + (uint32_t)(row * W + WPL * q4 + 4 * v4));
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = min(rb + TILE * ti + 16 * (j >> 2) + 4 * q4 + (j & 3), last);
+#pragma unroll
+                for (int s2 = 0; s2 < VS; ++s2)
+                    vt[s2][j] = vq[(uint32_t)(row * W + 16 * s2 + col)];
+            }
+        };
+        if (kn > 0)
+            load_tile(wave, kcur, vcur);
+
+#pragma unroll 1
+        for (int k = 0; k < kn; ++k) {
+            const int ti = wave + 4 * k;
+            if (k + 1 < kn)
+                load_tile(ti + 4, knext, vnext);
+
+            // ---- scores of the tile's 8 rows held by this lane
+            float sc[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int u = 0; u < KM; ++u) {
+                    const uint4 x = kcur[blk][u / 4];
+                    const uint32_t w = (u % 4 == 0) ? x.x : (u % 4 == 1) ? x.y : (u % 4 == 2) ? x.z : x.w;
+                    const half8 ka = unpack_k_word(w);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[u], sacc, 0, 0, 0);
+                    if constexpr (Q32)
+                        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[u], sacc, 0, 0, 0);
+                }
+                // rows TILE*ti + 16*blk + 4*q4 + i (round-relative) of column (hl, gl)
+                const int lr0 = TILE * ti + 16 * blk + 4 * q4;
+                float ks[4], kb[4];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(0 * NG + gl) * ROUND + lr0]), ks);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(1 * NG + gl) * ROUND + lr0]), kb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float kb8 = fmaf(8.0f, ks[i], kb[i]);  // bias of the centred codes
+                    const float part = fmaf(ks[i], sacc[i], kb8 * qsum);
+                    float v = group_sum<NG>(part) * cs;
+                    if (!col_on || rb + lr0 + i > last)
+                        v = -INFINITY;
+                    sc[4 * blk + i] = v;
+                    mx = fmaxf(mx, v);
+                }
+            }
+
+            // ---- online softmax across tiles: rescale only when a head's max rises
+            mx = quarter_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const bool first = (rb == t0) && (k == 0);
+            if (!first && __builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+                const float corr = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+                l_run *= corr;
+                b_run *= corr;
+                // accumulator element i of this lane belongs to row 4*q4 + i,
+                // whose factor lives in the lane of that column
+                float4v corr_row;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    corr_row[i] = __shfl(corr, 4 * q4 + i);
+#pragma unroll
+                for (int s2 = 0; s2 < VS; ++s2)
+#pragma unroll
+                    for (int m = 0; m < 8; ++m)
+                        acc[s2][m] *= corr_row;
+            }
+            m_run = m_new;
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+
+            // ---- weights and values
+            float vs[8], vb[8];
+            {
+                const int lr0 = TILE * ti + 4 * q4;
+                float t4[4];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * ROUND + lr0]), t4);
+                vs[0] = t4[0]; vs[1] = t4[1]; vs[2] = t4[2]; vs[3] = t4[3];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * ROUND + lr0 + 16]), t4);
+                vs[4] = t4[0]; vs[5] = t4[1]; vs[6] = t4[2]; vs[7] = t4[3];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * ROUND + lr0]), t4);
+                vb[0] = t4[0]; vb[1] = t4[1]; vb[2] = t4[2]; vb[3] = t4[3];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * ROUND + lr0 + 16]), t4);
+                vb[4] = t4[0]; vb[5] = t4[1]; vb[6] = t4[2]; vb[7] = t4[3];
+            }
+            half8 phi, plo;
+            float lsum = 0.0f, bsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float p = __builtin_amdgcn_exp2f(sc[j] - m_use);
+                lsum += p;
+                bsum = fmaf(p, fmaf(8.0f, vs[j], vb[j]), bsum);  // bias of the centred codes
+                const float pw = p * vs[j];
+                const _Float16 hi = (_Float16)pw;
+                phi[j] = hi;
+                plo[j] = (_Float16)(pw - (float)hi);
+            }
+            l_run += lsum;
+            b_run += bsum;
+#pragma unroll
+            for (int s2 = 0; s2 < VS; ++s2) {
+                half2v lo4[4][4], hi4[4][4];  // [pair][m]
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    const uint32_t x = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
+                    const uint32_t y = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
+                    unpack_halves(x, lo4[jp]);
+                    unpack_halves(y, hi4[jp]);
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const half8 bv = m < 4 ? cat8(lo4[0][m], lo4[1][m], lo4[2][m], lo4[3][m])
+                                           : cat8(hi4[0][m - 4], hi4[1][m - 4], hi4[2][m - 4], hi4[3][m - 4]);
+                    acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
+                    acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
+                }
+            }
+
+            if (k + 1 < kn) {
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int v4 = 0; v4 < WPL / 4; ++v4)
+                        kcur[blk][v4] = knext[blk][v4];
+#pragma unroll
+                for (int s2 = 0; s2 < VS; ++s2)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        vcur[s2][j] = vnext[s2][j];
+            }
+        }
+    }
+
+    // ---- wavefront totals: l and the value-bias term per column (h, g)
+    const float l_tot = quarter_sum(l_run);
+    const float b_tot = quarter_sum(b_run);
+    __syncthreads();  // metadata no longer read: the buffer now holds outputs
+    float *out_s = reinterpret_cast<float *>(smem);  // [4][MAXH][D]
+    if (q4 == 0) {
+        m_s[wave][col] = m_run;
+        l_s[wave][col] = l_tot;
+    }
+    // accumulator lane layout: rows r' = 4*q4 + i, column n = col
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * q4 + i;
+        const float bias_r = __shfl(b_tot, rr);
+        if (rr < R) {
+            const int h = rr / NG, g = rr % NG;
+#pragma unroll
+            for (int s = 0; s < VS; ++s) {
+                const int word = 16 * s + col;
+                if (word / WPG == g) {
+#pragma unroll
+                    for (int m = 0; m < 8; ++m)
+                        out_s[(wave * MAXH + h) * D + 8 * word + m] = acc[s][m][i] + bias_r;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- merge the four wavefronts and write the partial state
+    const int64_t C = a.num_chunks;
+    for (int e = threadIdx.x; e < nrep * D; e += NT) {
+        const int h = e / D, d = e % D;
+        const int r0 = h * NG;  // any group column of head h carries its m and l
+        const float M = fmaxf(fmaxf(m_s[0][r0], m_s[1][r0]), fmaxf(m_s[2][r0], m_s[3][r0]));
+        float accv = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            accv = fmaf(__builtin_amdgcn_exp2f(m_s[w][r0] - M), out_s[(w * MAXH + h) * D + d], accv);
+        const int64_t o = ((int64_t)b * a.Hq + h0 + h) * C + c;
+        a.part_acc[o * D + d] = accv;
+        if (d == 0) {
+            float L = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                L = fmaf(__builtin_amdgcn_exp2f(m_s[w][r0] - M), l_s[w][r0], L);
+            a.part_m[o] = M * kLn2;
+            a.part_l[o] = L;
+        }
+    }
+}
+
+template <int D, int NG>
+hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, hipStream_t s)
+{
+    dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
+    if (q_dtype == KVQ_F32)
+        hipLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, true>), grid, dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, false>), grid, dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_supports(int D, int G, int n_rep, int chunk)
+{
+    (void)chunk;
+    if (D != 128 && D != 256)
+        return false;
+    if (G != 32 && G != 64 && G != 128)
+        return false;
+    const int NG = D / G;
+    return NG <= 4 && n_rep >= 1 && n_rep * NG <= 16;
+}
+
+hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s)
+{
+    const int NG = D / a.G;
+    if (D == 128) {
+        if (NG == 1) return launch_dg<128, 1>(a, q_dtype, batch, s);
+        if (NG == 2) return launch_dg<128, 2>(a, q_dtype, batch, s);
+        if (NG == 4) return launch_dg<128, 4>(a, q_dtype, batch, s);
+    } else if (D == 256) {
+        if (NG == 2) return launch_dg<256, 2>(a, q_dtype, batch, s);
+        if (NG == 4) return launch_dg<256, 4>(a, q_dtype, batch, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 }  // namespace kvq

@@ -13,12 +13,15 @@ from _gpu_common import check_attention, gpu_cache_from_oracle, note, run_sdpa, 
 pytestmark = pytest.mark.gpu
 
 # Per-head relative L2 gates. The vector-ALU kernel works in fp32 throughout.
-REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: 2e-5, kvq.KERNEL_MFMA: 2e-5}
+# The matrix core sums the 32 products of one instruction after aligning them
+# to the largest and truncating the rest (measured: 1 + 0.75 ulp -> 1); with a
+# dominant row in a tile this leaves ~1e-5 relative error, so its gate is 5e-5.
+REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: 5e-5, kvq.KERNEL_MFMA: 5e-5}
 # With softmax scale 1 and normalised Q/K the scores reach O(100); their fp32
 # rounding (~sqrt(D) * 2^-24 * sum|q k|) passes undamped into the weights, so
 # the per-head L2 gate there is set one decade wider.
 REL_L2_UNSCALED = 2e-4
-KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_AUTO]
+KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA, kvq.KERNEL_AUTO]
 
 
 def _oracle_cache(k, v, cap=None, G=64):
@@ -79,7 +82,9 @@ def test_shapes(kernel, B, Hq, Hkv, D, G, qdt):
     try:
         out, *_ = run_sdpa(gpu_cache_from_oracle(oc), S, q, alpha, kernel=kernel)
     except kvq.KvqError as e:
-        pytest.fail(str(e))
+        if kernel == kvq.KERNEL_MFMA and e.status == -7:
+            pytest.skip("shape outside the matrix-core kernel (falls back to the vector kernel)")
+        raise
     check_attention(out, oracle.sdpa(oc, S, q, alpha), REL_L2[kernel], label="shape")
 
 
@@ -167,7 +172,7 @@ def test_one_hot_row_selection():
         v = kvq_synth.normal((1, 1, S, D), [82, tstar]).astype(np.float16)
         q = np.full((1, 4, D), 8.0, dtype=np.float32)
         oc = _oracle_cache(k, v)
-        for kernel in KERNELS:
+        for kernel in (kvq.KERNEL_VALU, kvq.KERNEL_AUTO):
             out, *_ = run_sdpa(gpu_cache_from_oracle(oc), S, q, 1.0, kernel=kernel)
             ref = oracle.sdpa(oc, S, q, 1.0)
             np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-6)
@@ -189,4 +194,4 @@ def test_fused_entry_point():
     gc = gpu_cache_from_oracle(oc)
     out = kvq.sdpa_int4(gc, 1024, to_dev(q), alpha)
     torch.cuda.synchronize()
-    check_attention(out.cpu().numpy(), oracle.sdpa(oc, 1024, q, alpha), 2e-5, label="fused")
+    check_attention(out.cpu().numpy(), oracle.sdpa(oc, 1024, q, alpha), 5e-5, label="fused")
