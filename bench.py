@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--sweep", default="1024,16384,65536",
                     help="extra Skv values timed with fewer steps (empty to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MB (a known-size reference "
+                         "for hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -177,6 +180,15 @@ def main():
         r["gbs"] = (layer_bytes(s) + append_bytes()) / (r["ms_per_step"] * 1e-3) / 1e9
         r["partial_gbs"] = layer_bytes(s) / (r["partial_ms_avg"] * 1e-3) / 1e9
         sweep.append(r)
+
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * 1000 * 1000 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     step_bytes = layer_bytes(args.skv) + append_bytes()
     ms = main_res["ms_per_step"]

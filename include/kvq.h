@@ -81,7 +81,7 @@ typedef struct kvq_cache {
     int32_t kv_heads;  /* Hkv >= 1 */
     int32_t head_dim;  /* D in {64, 128, 256} */
     int32_t group;     /* G in {32, 64, 128}, D % G == 0 */
-    int64_t capacity;  /* rows per (batch, KV head), >= 1, capacity * D/8 < 2^31 */
+    int64_t capacity;  /* rows per (batch, KV head), >= 1; capacity * D/2 < 2^31 - 2^16 */
 } kvq_cache;
 
 /* Library version string, e.g. "kvq 0.1.0 gfx950". */

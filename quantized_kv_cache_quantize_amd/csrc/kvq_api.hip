@@ -27,11 +27,11 @@ int check_cache(const kvq_cache *c)
         return KVQ_E_SHAPE;
     if (c->head_dim % c->group != 0)
         return KVQ_E_SHAPE;
-    // keep every element index far inside int64, and the words of one
-    // (batch, KV head) addressable with 32-bit offsets
+    // keep every element index far inside int64, and the code bytes of one
+    // (batch, KV head) addressable with 32-bit offsets (with 64 KiB to spare)
     if (c->capacity > ((int64_t)1 << 40) / ((int64_t)c->batch * c->kv_heads))
         return KVQ_E_SHAPE;
-    if (c->capacity * (c->head_dim / 8) > 0x7fffffff)
+    if (c->capacity * (c->head_dim / 2) > 0x7fff0000)
         return KVQ_E_SHAPE;
     if (!aligned16(c->k_q) || !aligned16(c->v_q) || !aligned16(c->k_scale) || !aligned16(c->k_bias) ||
         !aligned16(c->v_scale) || !aligned16(c->v_bias))

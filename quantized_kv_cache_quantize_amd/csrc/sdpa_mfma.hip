@@ -11,11 +11,11 @@
 //
 // Exactness of the fp16 operands:
 //  - codes enter as the exact fp16 integers code - 8 (magic-number unpack and
-//    an exact fp16 subtraction; see unpack_halves for why they are centred);
+//    an exact fp16 subtraction; see Unpacker for why they are centred);
 //  - fp16 Q is exact; fp32 Q is split into hi + lo fp16 halves (two MFMAs);
 //  - the value weights p * scale_v are split into hi + lo fp16 halves (two
 //    MFMAs), so about 22 bits of each weight survive;
-//  - products of these operands are exact in the fp32 accumulators.
+//  - products of these operands are exact before the matrix core sums them.
 // Scale and bias are applied outside the matrix core, per group, as in
 // "What I Built Instead" (Gemma page): q . k^ = sum_g s_g (q . code)_g +
 // b_g (sum q)_g, and sum_t p v^ = sum_t (p s_v) code + sum_t p b_v.
@@ -37,6 +37,11 @@
 // when some head's running max rises); the four wavefronts are merged at the
 // end. Scale and bias of K and V are staged in LDS per 512-row round; the
 // next tile's K and V words are loaded while the current tile is computed.
+//
+// Memory access: buffer loads against per-head resources whose size is the
+// valid rows (Skv), so rows past the end read as zero without per-row
+// clamping, and the eight value rows of a lane share one address register
+// (their distances are instruction offsets).
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -46,20 +51,35 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;         // threads per workgroup
-constexpr int TILE = 32;        // rows per tile
-constexpr int MAXT = 4;         // tiles per wavefront per round
+constexpr int NT = 256;                 // threads per workgroup
+constexpr int TILE = 32;                // rows per tile
+constexpr int MAXT = 4;                 // tiles per wavefront per round
 constexpr int ROUND = 4 * MAXT * TILE;  // 512 rows
 // Occupancy target (wavefronts per SIMD) for D = 128; D = 256 needs the
 // whole register file of one wavefront.
 #ifndef WAVES_D128
 #define WAVES_D128 2
 #endif
+// word 3 of a raw (unswizzled, 32-bit element) buffer resource on gfx9
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ float h_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
-
 __device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
-__device__ __forceinline__ uint32_t as_u32(half2v x) { return __builtin_bit_cast(uint32_t, x); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+// (x & mask) | magic in one instruction; gfx9 VOP3 encodings take no 32-bit
+// literal, so the mask comes from a scalar register and the magic from a
+// vector register.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+    return r;
+}
 
 // Four half2 registers -> one MFMA operand.
 __device__ __forceinline__ half8 cat8(half2v a, half2v b, half2v c, half2v d)
@@ -82,27 +102,23 @@ __device__ __forceinline__ half8 cat8(half2v a, half2v b, half2v c, half2v d)
 // same-signed products toward zero. Codes in [-8, 7] give products of both
 // signs and half the magnitude, and the 8 * scale they drop moves into the
 // bias term: code * s + b = (code - 8) * s + (b + 8 s).
-__device__ __forceinline__ void unpack_halves(uint32_t x, half2v (&out)[4])
-{
-    const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
-    const uint32_t y = x >> 8;
-    out[0] = as_h2((x & 0x000F000Fu) | 0x64006400u) - k1032;
-    out[1] = as_h2((x & 0x00F000F0u) | 0x54005400u) - k72;
-    out[2] = as_h2((y & 0x000F000Fu) | 0x64006400u) - k1032;
-    out[3] = as_h2((y & 0x00F000F0u) | 0x54005400u) - k72;
-}
+struct Unpacker {
+    uint32_t m1024, m64;  // magic exponents, kept in vector registers
+    __device__ __forceinline__ void operator()(uint32_t x, half2v (&out)[4]) const
+    {
+        const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+        const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
+        const uint32_t y = x >> 8;
+        out[0] = as_h2(and_or(x, 0x000F000Fu, m1024)) - k1032;
+        out[1] = as_h2(and_or(x, 0x00F000F0u, m64)) - k72;
+        out[2] = as_h2(and_or(y, 0x000F000Fu, m1024)) - k1032;
+        out[3] = as_h2(and_or(y, 0x00F000F0u, m64)) - k72;
+    }
+};
 
 // One K word (dimensions 8w..8w+7 of one row) as an MFMA operand; element j
 // holds dimension 8w + kPerm[j].
 constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-
-__device__ __forceinline__ half8 unpack_k_word(uint32_t w)
-{
-    half2v h[4];
-    unpack_halves(w, h);
-    return cat8(h[0], h[1], h[2], h[3]);
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v)
@@ -118,8 +134,6 @@ __device__ __forceinline__ float group_sum(float v)
         v += dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
     if constexpr (NG >= 4)
         v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (NG >= 8)
-        v += __shfl_xor(v, 4);
     return v;
 }
 
@@ -135,7 +149,7 @@ __device__ __forceinline__ float quarter_sum(float v)
     return v + __shfl_xor(v, 32);
 }
 
-__device__ __forceinline__ void h4_to_f32(uint2 v, float (&out)[4])
+__device__ __forceinline__ void h4_to_f32(uint2 v, float *out)
 {
     out[0] = h_val(v.x & 0xFFFF);
     out[1] = h_val(v.x >> 16);
@@ -153,8 +167,8 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
     constexpr int VS = W / 16;      // value column sets of 16 words
     constexpr int WPG = W / NG;     // words per scale group
     constexpr int MAXH = 16 / NG;   // most query heads per KV head
-    constexpr int META_HALVES = 4 * NG * ROUND;         // K scale, K bias, V scale, V bias
-    constexpr int OUT_FLOATS = 4 * MAXH * D;            // per-wavefront outputs for the merge
+    constexpr int META_HALVES = 4 * NG * ROUND;  // K scale, K bias, V scale, V bias
+    constexpr int OUT_FLOATS = 4 * MAXH * D;     // per-wavefront outputs for the merge
     constexpr int SMEM_BYTES = (META_HALVES * 2 > OUT_FLOATS * 4) ? META_HALVES * 2 : OUT_FLOATS * 4;
 
     const int lane = threadIdx.x & 63;
@@ -168,25 +182,28 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
     const int R = nrep * NG;
     const int hl = col / NG, gl = col % NG;
     const bool col_on = col < R;
+    const float col_mask = col_on ? 0.0f : -INFINITY;
     const int h0 = kvh * nrep;
 
-    // Rows are counted inside one (batch, KV head); capacity * D/8 < 2^31 is
-    // checked on the host, so 32-bit offsets from per-head bases suffice.
+    // Rows are counted inside one (batch, KV head); the host checks that a
+    // head's code array stays below 2 GiB, so 32-bit offsets suffice.
     const int t0 = (int)((int64_t)c * a.chunk);
     const int t1 = (int)min((int64_t)t0 + a.chunk, a.skv);
     const int last = t1 - 1;
     const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
-    const uint32_t *kq = a.k_q + kvrow0 * W;
-    const uint32_t *vq = a.v_q + kvrow0 * W;
-    const uint16_t *ksc = a.k_scale + kvrow0 * NG;
-    const uint16_t *kbi = a.k_bias + kvrow0 * NG;
-    const uint16_t *vsc = a.v_scale + kvrow0 * NG;
-    const uint16_t *vbi = a.v_bias + kvrow0 * NG;
+    const uint32_t rows_ok = (uint32_t)a.skv;
+    const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t mres[4] = {
+        make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
+        make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
 
     __shared__ __align__(16) unsigned char smem[SMEM_BYTES];
     __shared__ float m_s[4][16];
     __shared__ float l_s[4][16];
     uint16_t *meta = reinterpret_cast<uint16_t *>(smem);  // [4][NG][ROUND]
+
+    const Unpacker unpack{0x64006400u, 0x54005400u};
 
     // ---- Q operand (B of the score GEMM) and per-group sums of q. Every lane
     //      loads the 8 dimensions of each of its words unconditionally (lanes
@@ -201,8 +218,9 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
         for (int u = 0; u < KM; ++u) {
             const int word = WPL * q4 + u;
             if constexpr (Q32) {
-                const float4 x0 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow + 8 * word);
-                const float4 x1 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow + 8 * word + 4);
+                const float *qp = reinterpret_cast<const float *>(a.q) + qrow + 8 * word;
+                const float4 x0 = *reinterpret_cast<const float4 *>(qp);
+                const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
                 qv[u][0] = x0.x; qv[u][1] = x0.y; qv[u][2] = x0.z; qv[u][3] = x0.w;
                 qv[u][4] = x1.x; qv[u][5] = x1.y; qv[u][6] = x1.z; qv[u][7] = x1.w;
             } else {
@@ -242,8 +260,8 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
         const int ntile = (min(rb + ROUND, t1) - rb + TILE - 1) / TILE;
 
         // ---- stage this round's scale and bias of K and V in LDS as
-        //      [array][group][row]; rows past the end repeat the last row.
-        //      All loads are issued before the first LDS write.
+        //      [array][group][row] (rows past Skv read as zero). All loads are
+        //      issued before the first LDS write.
         __syncthreads();  // the previous round's readers are done
         {
             constexpr int PER = META_HALVES / NT;  // halves per thread
@@ -253,21 +271,17 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
                 const int arr = (i * NT) / ARR;  // compile-time after unrolling
-                const int rem = threadIdx.x + (i * NT) % ARR;
-                const int r = rem / NG, g = rem - r * NG;
-                const int row = min(rb + r, last);
-                const uint16_t *src = arr == 0 ? ksc : arr == 1 ? kbi : arr == 2 ? vsc : vbi;
-                tmp[i] = src[(uint32_t)(row * NG + g)];
+                const int rem = (int)threadIdx.x + (i * NT) % ARR;
+                tmp[i] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], (rb * NG + rem) * 2, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
                 const int arr = (i * NT) / ARR;
-                const int rem = threadIdx.x + (i * NT) % ARR;
+                const int rem = (int)threadIdx.x + (i * NT) % ARR;
                 const int r = rem / NG, g = rem - r * NG;
                 meta[(arr * NG + g) * ROUND + r] = tmp[i];
             }
         }
-
         __syncthreads();  // metadata staged
 
         // ---- this wavefront's tiles of the round: ti = wave + 4k, k < kn
@@ -275,20 +289,21 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
         uint4 kcur[2][WPL / 4], knext[2][WPL / 4];
         uint32_t vcur[VS][8], vnext[VS][8];
         auto load_tile = [&](int ti, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
+            const int trow = rb + TILE * ti;
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
-                const int row = min(rb + TILE * ti + 16 * blk + col, last);
+                const int off = ((trow + 16 * blk + col) * W + WPL * q4) * 4;
 #pragma unroll
                 for (int v4 = 0; v4 < WPL / 4; ++v4)
-                    kt[blk][v4] = *reinterpret_cast<const uint4 *>(kq + (uint32_t)(row * W + WPL * q4 + 4 * v4));
+                    kt[blk][v4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
             }
+            const int voff = ((trow + 4 * q4) * W + col) * 4;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int row = min(rb + TILE * ti + 16 * (j >> 2) + 4 * q4 + (j & 3), last);
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
                 for (int s2 = 0; s2 < VS; ++s2)
-                    vt[s2][j] = vq[(uint32_t)(row * W + 16 * s2 + col)];
-            }
+                    vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(
+                        vq, voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * s2) * 4, 0, 0);
         };
         if (kn > 0)
             load_tile(wave, kcur, vcur);
@@ -298,6 +313,7 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
             const int ti = wave + 4 * k;
             if (k + 1 < kn)
                 load_tile(ti + 4, knext, vnext);
+            const bool tail = rb + TILE * ti + TILE > t1;  // uniform
 
             // ---- scores of the tile's 8 rows held by this lane
             float sc[8];
@@ -309,7 +325,9 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
                 for (int u = 0; u < KM; ++u) {
                     const uint4 x = kcur[blk][u / 4];
                     const uint32_t w = (u % 4 == 0) ? x.x : (u % 4 == 1) ? x.y : (u % 4 == 2) ? x.z : x.w;
-                    const half8 ka = unpack_k_word(w);
+                    half2v hk[4];
+                    unpack(w, hk);
+                    const half8 ka = cat8(hk[0], hk[1], hk[2], hk[3]);
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[u], sacc, 0, 0, 0);
                     if constexpr (Q32)
                         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[u], sacc, 0, 0, 0);
@@ -323,9 +341,9 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
                 for (int i = 0; i < 4; ++i) {
                     const float kb8 = fmaf(8.0f, ks[i], kb[i]);  // bias of the centred codes
                     const float part = fmaf(ks[i], sacc[i], kb8 * qsum);
-                    float v = group_sum<NG>(part) * cs;
-                    if (!col_on || rb + lr0 + i > last)
-                        v = -INFINITY;
+                    float v = fmaf(group_sum<NG>(part), cs, col_mask);
+                    if (tail)
+                        v = (rb + lr0 + i <= last) ? v : -INFINITY;
                     sc[4 * blk + i] = v;
                     mx = fmaxf(mx, v);
                 }
@@ -358,15 +376,10 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
             float vs[8], vb[8];
             {
                 const int lr0 = TILE * ti + 4 * q4;
-                float t4[4];
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * ROUND + lr0]), t4);
-                vs[0] = t4[0]; vs[1] = t4[1]; vs[2] = t4[2]; vs[3] = t4[3];
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * ROUND + lr0 + 16]), t4);
-                vs[4] = t4[0]; vs[5] = t4[1]; vs[6] = t4[2]; vs[7] = t4[3];
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * ROUND + lr0]), t4);
-                vb[0] = t4[0]; vb[1] = t4[1]; vb[2] = t4[2]; vb[3] = t4[3];
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * ROUND + lr0 + 16]), t4);
-                vb[4] = t4[0]; vb[5] = t4[1]; vb[6] = t4[2]; vb[7] = t4[3];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * ROUND + lr0]), &vs[0]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * ROUND + lr0 + 16]), &vs[4]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * ROUND + lr0]), &vb[0]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * ROUND + lr0 + 16]), &vb[4]);
             }
             half8 phi, plo;
             float lsum = 0.0f, bsum = 0.0f;
@@ -389,8 +402,8 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
                 for (int jp = 0; jp < 4; ++jp) {
                     const uint32_t x = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
                     const uint32_t y = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
-                    unpack_halves(x, lo4[jp]);
-                    unpack_halves(y, hi4[jp]);
+                    unpack(x, lo4[jp]);
+                    unpack(y, hi4[jp]);
                 }
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {

@@ -5,36 +5,40 @@
 //
 // With M = max_c m_c:  out[d] = sum_c e^{m_c-M} acc_c[d] / sum_c e^{m_c-M} l_c.
 //
-// One workgroup of 256 threads per (batch, query head). The threads split
-// into 256/D lanes-groups that take every (256/D)-th chunk; each thread owns
-// one dimension, so every chunk's accumulator row is read with coalesced
-// 4-byte loads. The per-group sums meet in LDS.
+// Grid: (batch x query head, D / 32). A workgroup owns 32 output dimensions
+// of one head; its 256 threads are 8 chunk lanes x 32 dimensions, so every
+// chunk's 128-byte slice of the accumulator is one coalesced read and each
+// thread keeps 8 independent loads in flight. The chunk lanes meet in LDS.
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 constexpr int RT = 256;
+constexpr int DS = 32;         // dimensions per workgroup
+constexpr int CL = RT / DS;    // chunk lanes
+constexpr int UNROLL = 8;
 
 __global__ __launch_bounds__(RT) void sdpa_reduce_kernel(ReduceArgs a)
 {
     const int64_t head = blockIdx.x;
+    const int d0 = blockIdx.y * DS;
     const int tid = threadIdx.x;
+    const int cl = tid / DS;
+    const int d = tid % DS;
     const int D = a.D;
-    const int ngrp = RT / D;
-    const int grp = tid / D;
-    const int d = tid % D;
-    const float *m = a.part_m + head * a.C;
-    const float *l = a.part_l + head * a.C;
-    const float *acc = a.part_acc + head * a.C * D;
+    const int64_t C = a.C;
+    const float *m = a.part_m + head * C;
+    const float *l = a.part_l + head * C;
+    const float *acc = a.part_acc + head * C * D + d0 + d;
 
     __shared__ float red[RT / 64];
-    __shared__ float num_s[RT];
-    __shared__ float den_s[RT];
+    __shared__ float num_s[CL][DS];
+    __shared__ float den_s[CL][DS];
 
     // M = max over chunks
     float mx = -INFINITY;
-    for (int64_t c = tid; c < a.C; c += RT)
+    for (int64_t c = tid; c < C; c += RT)
         mx = fmaxf(mx, m[c]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
@@ -43,24 +47,42 @@ __global__ __launch_bounds__(RT) void sdpa_reduce_kernel(ReduceArgs a)
         red[tid >> 6] = mx;
     __syncthreads();
     float M = red[0];
+#pragma unroll
     for (int i = 1; i < RT / 64; ++i)
         M = fmaxf(M, red[i]);
 
     float num = 0.0f, den = 0.0f;
-    for (int64_t c = grp; c < a.C; c += ngrp) {
+    int64_t c = cl;
+    for (; c + (UNROLL - 1) * CL < C; c += UNROLL * CL) {
+        float mv[UNROLL], lv[UNROLL], av[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            mv[u] = m[c + u * CL];
+            lv[u] = l[c + u * CL];
+            av[u] = acc[(c + u * CL) * D];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const float f = exp2f((mv[u] - M) * kLog2e);
+            den = fmaf(f, lv[u], den);
+            num = fmaf(f, av[u], num);
+        }
+    }
+    for (; c < C; c += CL) {
         const float f = exp2f((m[c] - M) * kLog2e);
         den = fmaf(f, l[c], den);
-        num = fmaf(f, acc[c * D + d], num);
+        num = fmaf(f, acc[c * D], num);
     }
-    num_s[tid] = num;
-    den_s[tid] = den;
+    num_s[cl][d] = num;
+    den_s[cl][d] = den;
     __syncthreads();
-    if (grp == 0) {
-        for (int g = 1; g < ngrp; ++g) {
-            num += num_s[g * D + d];
-            den += den_s[g * D + d];
+    if (cl == 0) {
+#pragma unroll
+        for (int g = 1; g < CL; ++g) {
+            num += num_s[g][d];
+            den += den_s[g][d];
         }
-        a.out[head * D + d] = num / den;
+        a.out[head * D + d0 + d] = num / den;
     }
 }
 
@@ -68,7 +90,7 @@ __global__ __launch_bounds__(RT) void sdpa_reduce_kernel(ReduceArgs a)
 
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(sdpa_reduce_kernel, dim3((unsigned)a.heads), dim3(RT), 0, s, a);
+    hipLaunchKernelGGL(sdpa_reduce_kernel, dim3((unsigned)a.heads, (unsigned)(a.D / DS)), dim3(RT), 0, s, a);
     return hipGetLastError();
 }
 
