@@ -35,8 +35,8 @@
 // Softmax: each wavefront takes every fourth 32-row tile of the chunk and
 // keeps an online softmax across its tiles (the accumulator is rescaled only
 // when some head's running max rises); the four wavefronts are merged at the
-// end. Scale and bias of K and V are staged in LDS per 512-row round; the
-// next tile's K and V words are loaded while the current tile is computed.
+// end. Scale and bias of K and V are staged in LDS per 512-row round, and a
+// wavefront requests the K and V words of all its tiles of the round at once.
 //
 // Memory access: buffer loads against per-head resources whose size is the
 // valid rows (Skv), so rows past the end read as zero without per-row
@@ -205,15 +205,15 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
 
     const Unpacker unpack{0x64006400u, 0x54005400u};
 
-    // ---- Q operand (B of the score GEMM) and per-group sums of q. Every lane
-    //      loads the 8 dimensions of each of its words unconditionally (lanes
-    //      of unused columns read head 0), so all loads are in flight at once;
-    //      entries outside the lane's (head, group) are zeroed afterwards.
-    half8 qhi[KM], qlo[KM];
-    float qsum = 0.0f;
+    // ---- startup: issue the Q loads, the first round's scale/bias loads and
+    //      the first tile's K/V loads back to back, then wait for each group
+    //      only where it is first used.
+    // Q operand (B of the score GEMM): every lane loads the 8 dimensions of
+    // each of its words unconditionally (lanes of unused columns read head
+    // 0); entries outside the lane's (head, group) are zeroed afterwards.
+    float qv[KM][8];
     {
         const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
-        float qv[KM][8];
 #pragma unroll
         for (int u = 0; u < KM; ++u) {
             const int word = WPL * q4 + u;
@@ -230,22 +230,82 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
                     qv[u][j] = (float)x[j];
             }
         }
-#pragma unroll
-        for (int u = 0; u < KM; ++u) {
-            const int word = WPL * q4 + u;
-            const bool mine = col_on && (word / WPG) == gl;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = mine ? qv[u][kPerm[j]] : 0.0f;
-                qsum += x;
-                const _Float16 hi = (_Float16)x;
-                qhi[u][j] = hi;
-                if constexpr (Q32)
-                    qlo[u][j] = (_Float16)(x - (float)hi);
-            }
-        }
-        qsum = quarter_sum(qsum);
     }
+
+    // scale and bias of K and V for one 512-row round, staged in LDS as
+    // [array][group][row] (rows past Skv read as zero)
+    constexpr int PER = META_HALVES / NT;  // halves per thread
+    constexpr int ARR = NG * ROUND;        // halves per array
+    static_assert(ARR % NT == 0, "each array is a whole number of thread sweeps");
+    uint16_t mtmp[PER];
+    auto stage_issue = [&](int rb) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int arr = (i * NT) / ARR;  // compile-time after unrolling
+            const int rem = (int)threadIdx.x + (i * NT) % ARR;
+            mtmp[i] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], (rb * NG + rem) * 2, 0, 0);
+        }
+    };
+    auto stage_write = [&]() {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int arr = (i * NT) / ARR;
+            const int rem = (int)threadIdx.x + (i * NT) % ARR;
+            const int r = rem / NG, g = rem - r * NG;
+            meta[(arr * NG + g) * ROUND + r] = mtmp[i];
+        }
+    };
+
+    // K words (A operand rows) and V words (this lane's 8 rows) of each of
+    // this wavefront's tiles in the current round, all requested at once
+    uint4 kbuf[MAXT][2][WPL / 4];
+    uint32_t vbuf[MAXT][VS][8];
+    auto load_tile = [&](int trow, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int off = ((trow + 16 * blk + col) * W + WPL * q4) * 4;
+#pragma unroll
+            for (int v4 = 0; v4 < WPL / 4; ++v4)
+                kt[blk][v4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
+        }
+        const int voff = ((trow + 4 * q4) * W + col) * 4;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int s2 = 0; s2 < VS; ++s2)
+                vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(
+                    vq, voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * s2) * 4, 0, 0);
+    };
+
+    // every tile of this wavefront in the round starting at rb
+    auto load_round = [&](int rb) {
+        const int ntile = (min(rb + ROUND, t1) - rb + TILE - 1) / TILE;
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k)
+            if (wave + 4 * k < ntile)
+                load_tile(rb + TILE * (wave + 4 * k), kbuf[k], vbuf[k]);
+    };
+
+    stage_issue(t0);
+    load_round(t0);
+
+    half8 qhi[KM], qlo[KM];
+    float qsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < KM; ++u) {
+        const int word = WPL * q4 + u;
+        const bool mine = col_on && (word / WPG) == gl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = mine ? qv[u][kPerm[j]] : 0.0f;
+            qsum += x;
+            const _Float16 hi = (_Float16)x;
+            qhi[u][j] = hi;
+            if constexpr (Q32)
+                qlo[u][j] = (_Float16)(x - (float)hi);
+        }
+    }
+    qsum = quarter_sum(qsum);
 
     const float cs = a.score_scale;
     float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
@@ -258,62 +318,25 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
 
     for (int rb = t0; rb < t1; rb += ROUND) {
         const int ntile = (min(rb + ROUND, t1) - rb + TILE - 1) / TILE;
-
-        // ---- stage this round's scale and bias of K and V in LDS as
-        //      [array][group][row] (rows past Skv read as zero). All loads are
-        //      issued before the first LDS write.
-        __syncthreads();  // the previous round's readers are done
-        {
-            constexpr int PER = META_HALVES / NT;  // halves per thread
-            constexpr int ARR = NG * ROUND;        // halves per array
-            static_assert(ARR % NT == 0, "each array is a whole number of thread sweeps");
-            uint16_t tmp[PER];
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int arr = (i * NT) / ARR;  // compile-time after unrolling
-                const int rem = (int)threadIdx.x + (i * NT) % ARR;
-                tmp[i] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], (rb * NG + rem) * 2, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int arr = (i * NT) / ARR;
-                const int rem = (int)threadIdx.x + (i * NT) % ARR;
-                const int r = rem / NG, g = rem - r * NG;
-                meta[(arr * NG + g) * ROUND + r] = tmp[i];
-            }
+        if (rb != t0) {
+            __syncthreads();  // the previous round's readers are done
+            stage_issue(rb);
+            load_round(rb);
         }
+        stage_write();
         __syncthreads();  // metadata staged
 
         // ---- this wavefront's tiles of the round: ti = wave + 4k, k < kn
         const int kn = (ntile - wave + 3) / 4;  // uniform; <= MAXT
-        uint4 kcur[2][WPL / 4], knext[2][WPL / 4];
-        uint32_t vcur[VS][8], vnext[VS][8];
-        auto load_tile = [&](int ti, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
-            const int trow = rb + TILE * ti;
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int off = ((trow + 16 * blk + col) * W + WPL * q4) * 4;
-#pragma unroll
-                for (int v4 = 0; v4 < WPL / 4; ++v4)
-                    kt[blk][v4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
-            }
-            const int voff = ((trow + 4 * q4) * W + col) * 4;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int s2 = 0; s2 < VS; ++s2)
-                    vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(
-                        vq, voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * s2) * 4, 0, 0);
-        };
-        if (kn > 0)
-            load_tile(wave, kcur, vcur);
 
-#pragma unroll 1
-        for (int k = 0; k < kn; ++k) {
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k) {
+            if (k >= kn)
+                break;
             const int ti = wave + 4 * k;
-            if (k + 1 < kn)
-                load_tile(ti + 4, knext, vnext);
             const bool tail = rb + TILE * ti + TILE > t1;  // uniform
+            const uint4 (&kcur)[2][WPL / 4] = kbuf[k];
+            const uint32_t (&vcur)[VS][8] = vbuf[k];
 
             // ---- scores of the tile's 8 rows held by this lane
             float sc[8];
@@ -414,18 +437,6 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
                 }
             }
 
-            if (k + 1 < kn) {
-#pragma unroll
-                for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                    for (int v4 = 0; v4 < WPL / 4; ++v4)
-                        kcur[blk][v4] = knext[blk][v4];
-#pragma unroll
-                for (int s2 = 0; s2 < VS; ++s2)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        vcur[s2][j] = vnext[s2][j];
-            }
         }
     }
 
