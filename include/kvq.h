@@ -64,9 +64,13 @@ typedef enum kvq_dtype { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
 
 /* Kernel choice for the partial (split-K) phase. */
 typedef enum kvq_kernel {
-    KVQ_KERNEL_AUTO = 0,  /* fastest variant that supports the shape */
-    KVQ_KERNEL_VALU = 1,  /* vector-ALU kernel: any supported shape */
-    KVQ_KERNEL_MFMA = 2   /* matrix-core kernel: (Hq/Hkv) * (D/G) <= 16 */
+    KVQ_KERNEL_AUTO = 0,        /* fastest variant that supports the shape */
+    KVQ_KERNEL_VALU = 1,        /* vector-ALU kernel: any supported shape */
+    KVQ_KERNEL_MFMA = 2,        /* matrix-core kernels, D in {128, 256} and (Hq/Hkv) * (D/G) <= 16;
+                                   the variant below is chosen by grid size */
+    KVQ_KERNEL_MFMA_SPLIT = 3,  /* matrix-core, four wavefronts per chunk (any chunk length) */
+    KVQ_KERNEL_MFMA_WAVE = 4    /* matrix-core, one wavefront per chunk: chunk <= 512 and
+                                   chunk * (D/G) and capacity * (D/G) multiples of 8 */
 } kvq_kernel;
 
 /* One layer's quantised cache (all device pointers, 16-byte aligned). */

@@ -12,6 +12,8 @@ from ._binding import (  # noqa: F401
     KVQ_F32,
     KERNEL_AUTO,
     KERNEL_MFMA,
+    KERNEL_MFMA_SPLIT,
+    KERNEL_MFMA_WAVE,
     KERNEL_VALU,
     Int4KVCache,
     KvqError,

@@ -65,7 +65,8 @@ struct ReduceArgs {
 hipError_t launch_quantize(const QuantizeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s);
 bool mfma_supports(int D, int G, int n_rep, int chunk);
-hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s);
+hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, hipStream_t s);
+bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
 }  // namespace kvq

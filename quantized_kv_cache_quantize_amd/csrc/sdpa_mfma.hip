@@ -492,14 +492,346 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// One-wavefront variant: a 64-thread workgroup owns one (chunk <= 512 rows,
+// KV head, batch). The same tile computation as above, but with no barriers
+// and no cross-wavefront merge: the chunk's scale and bias are staged once in
+// a wavefront-private LDS area, K/V tiles stream through a static ring of PF
+// tiles in flight (slot u is refilled with tile u + PF right after tile u is
+// consumed), and the partial state is written straight from registers. With
+// 512-row chunks every wavefront streams 16 tiles, so its start-up latency is
+// paid once per 73 KB instead of once per 18 KB.
+// ---------------------------------------------------------------------------
+constexpr int CH1 = 512;  // most rows of a chunk in the one-wavefront kernel
+
+template <int D, int NG, bool Q32, int PF>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
+void sdpa_partial_mfma1_kernel(PartialArgs a)
+{
+    constexpr int W = D / 8;
+    constexpr int WPL = W / 4;
+    constexpr int KM = W / 4;
+    constexpr int VS = W / 16;
+    constexpr int WPG = W / NG;
+    constexpr int SEG = 8 / NG;  // rows per 16-byte metadata segment
+
+    const int lane = threadIdx.x;
+    const int q4 = lane >> 4;
+    const int col = lane & 15;
+    const int c = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int nrep = a.n_rep;
+    const int R = nrep * NG;
+    const int hl = col / NG, gl = col % NG;
+    const bool col_on = col < R;
+    const float col_mask = col_on ? 0.0f : -INFINITY;
+    const int h0 = kvh * nrep;
+
+    const int t0 = (int)((int64_t)c * a.chunk);
+    const int t1 = (int)min((int64_t)t0 + a.chunk, a.skv);
+    const int last = t1 - 1;
+    const int ntile = (t1 - t0 + TILE - 1) / TILE;
+    const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
+    const uint32_t rows_ok = (uint32_t)a.skv;
+    const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t mres[4] = {
+        make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
+        make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
+
+    __shared__ __align__(16) uint16_t meta[4 * NG * CH1];  // [array][group][row]
+    const Unpacker unpack{0x64006400u, 0x54005400u};
+
+    // ---- start-up: Q, the chunk's scale/bias and the first PF tiles, all
+    //      requested before the first wait
+    float qv[KM][8];
+    {
+        const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
+#pragma unroll
+        for (int u = 0; u < KM; ++u) {
+            const int word = WPL * q4 + u;
+            if constexpr (Q32) {
+                const float *qp = reinterpret_cast<const float *>(a.q) + qrow + 8 * word;
+                const float4 x0 = *reinterpret_cast<const float4 *>(qp);
+                const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
+                qv[u][0] = x0.x; qv[u][1] = x0.y; qv[u][2] = x0.z; qv[u][3] = x0.w;
+                qv[u][4] = x1.x; qv[u][5] = x1.y; qv[u][6] = x1.z; qv[u][7] = x1.w;
+            } else {
+                const half8 x = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow + 8 * word);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    qv[u][j] = (float)x[j];
+            }
+        }
+    }
+    // metadata: each array holds CH1 * NG halves = CH1 / SEG segments of 16
+    // bytes (SEG rows x NG groups); lane i takes segments i, i + 64, ...
+    constexpr int SEGS = CH1 / SEG;       // per array
+    constexpr int MPL = 4 * SEGS / 64;    // segments per lane
+    uint4 mraw[MPL];
+#pragma unroll
+    for (int i = 0; i < MPL; ++i) {
+        const int sg = lane + 64 * i;
+        const int arr = sg / SEGS;  // uniform per i
+        const int row = (sg % SEGS) * SEG;
+        mraw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mres[arr], (t0 + row) * NG * 2, 0, 0));
+    }
+
+    uint4 kbuf[PF][2][WPL / 4];
+    uint32_t vbuf[PF][VS][8];
+    auto load_tile = [&](int trow, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int off = ((trow + 16 * blk + col) * W + WPL * q4) * 4;
+#pragma unroll
+            for (int v4 = 0; v4 < WPL / 4; ++v4)
+                kt[blk][v4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
+        }
+        const int voff = ((trow + 4 * q4) * W + col) * 4;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int s2 = 0; s2 < VS; ++s2)
+                vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(
+                    vq, voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * s2) * 4, 0, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        if (u < ntile)
+            load_tile(t0 + TILE * u, kbuf[u], vbuf[u]);
+
+    half8 qhi[KM], qlo[KM];
+    float qsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < KM; ++u) {
+        const int word = WPL * q4 + u;
+        const bool mine = col_on && (word / WPG) == gl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = mine ? qv[u][kPerm[j]] : 0.0f;
+            qsum += x;
+            const _Float16 hi = (_Float16)x;
+            qhi[u][j] = hi;
+            if constexpr (Q32)
+                qlo[u][j] = (_Float16)(x - (float)hi);
+        }
+    }
+    qsum = quarter_sum(qsum);
+
+    // transpose the metadata segments into [array][group][row]
+#pragma unroll
+    for (int i = 0; i < MPL; ++i) {
+        const int sg = lane + 64 * i;
+        const int arr = sg / SEGS;
+        const int row = (sg % SEGS) * SEG;
+        const uint32_t w[4] = {mraw[i].x, mraw[i].y, mraw[i].z, mraw[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // half e of the segment: row + e / NG, group e % NG
+            const uint16_t h = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            meta[(arr * NG + (e % NG)) * CH1 + row + e / NG] = h;
+        }
+    }
+    // the wavefront's own LDS writes are seen by its later reads (LDS
+    // instructions of a wavefront execute in order); keep the compiler from
+    // moving reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const float cs = a.score_scale;
+    float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
+    float4v acc[VS][8];
+#pragma unroll
+    for (int s = 0; s < VS; ++s)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[s][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll 1
+    for (int kk = 0; kk < ntile; kk += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int ti = kk + u;
+            if (ti >= ntile)
+                break;
+            const bool tail = t0 + TILE * ti + TILE > t1;  // uniform
+            const uint4 (&kcur)[2][WPL / 4] = kbuf[u];
+            const uint32_t (&vcur)[VS][8] = vbuf[u];
+
+            // ---- scores of the tile's 8 rows held by this lane
+            float sc[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int uu = 0; uu < KM; ++uu) {
+                    const uint4 x = kcur[blk][uu / 4];
+                    const uint32_t w = (uu % 4 == 0) ? x.x : (uu % 4 == 1) ? x.y : (uu % 4 == 2) ? x.z : x.w;
+                    half2v hk[4];
+                    unpack(w, hk);
+                    const half8 ka = cat8(hk[0], hk[1], hk[2], hk[3]);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[uu], sacc, 0, 0, 0);
+                    if constexpr (Q32)
+                        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[uu], sacc, 0, 0, 0);
+                }
+                const int lr0 = TILE * ti + 16 * blk + 4 * q4;  // chunk-relative row
+                float ks[4], kb[4];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(0 * NG + gl) * CH1 + lr0]), ks);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(1 * NG + gl) * CH1 + lr0]), kb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float kb8 = fmaf(8.0f, ks[i], kb[i]);  // bias of the centred codes
+                    const float part = fmaf(ks[i], sacc[i], kb8 * qsum);
+                    float v = fmaf(group_sum<NG>(part), cs, col_mask);
+                    if (tail)
+                        v = (t0 + lr0 + i <= last) ? v : -INFINITY;
+                    sc[4 * blk + i] = v;
+                    mx = fmaxf(mx, v);
+                }
+            }
+
+            // ---- online softmax across tiles: rescale only when a head's max rises
+            mx = quarter_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            if (ti != 0 && __builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+                const float corr = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+                l_run *= corr;
+                b_run *= corr;
+                float4v corr_row;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    corr_row[i] = __shfl(corr, 4 * q4 + i);
+#pragma unroll
+                for (int s2 = 0; s2 < VS; ++s2)
+#pragma unroll
+                    for (int m = 0; m < 8; ++m)
+                        acc[s2][m] *= corr_row;
+            }
+            m_run = m_new;
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+
+            // ---- weights and values
+            float vs[8], vb[8];
+            {
+                const int lr0 = TILE * ti + 4 * q4;
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * CH1 + lr0]), &vs[0]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * CH1 + lr0 + 16]), &vs[4]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * CH1 + lr0]), &vb[0]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * CH1 + lr0 + 16]), &vb[4]);
+            }
+            half8 phi, plo;
+            float lsum = 0.0f, bsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float p = __builtin_amdgcn_exp2f(sc[j] - m_use);
+                lsum += p;
+                bsum = fmaf(p, fmaf(8.0f, vs[j], vb[j]), bsum);  // bias of the centred codes
+                const float pw = p * vs[j];
+                const _Float16 hi = (_Float16)pw;
+                phi[j] = hi;
+                plo[j] = (_Float16)(pw - (float)hi);
+            }
+            l_run += lsum;
+            b_run += bsum;
+#pragma unroll
+            for (int s2 = 0; s2 < VS; ++s2) {
+                half2v lo4[4][4], hi4[4][4];  // [pair][m]
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    const uint32_t x = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
+                    const uint32_t y = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
+                    unpack(x, lo4[jp]);
+                    unpack(y, hi4[jp]);
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const half8 bv = m < 4 ? cat8(lo4[0][m], lo4[1][m], lo4[2][m], lo4[3][m])
+                                           : cat8(hi4[0][m - 4], hi4[1][m - 4], hi4[2][m - 4], hi4[3][m - 4]);
+                    acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
+                    acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
+                }
+            }
+
+            // ---- refill this ring slot
+            if (ti + PF < ntile)
+                load_tile(t0 + TILE * (ti + PF), kbuf[u], vbuf[u]);
+        }
+    }
+
+    // ---- write the partial state of this chunk
+    const float l_tot = quarter_sum(l_run);
+    const float b_tot = quarter_sum(b_run);
+    const int64_t C = a.num_chunks;
+    if (q4 == 0 && col_on && gl == 0) {
+        const int64_t o = ((int64_t)b * a.Hq + h0 + hl) * C + c;
+        a.part_m[o] = m_run * kLn2;
+        a.part_l[o] = l_tot;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * q4 + i;
+        const float bias_r = __shfl(b_tot, rr);
+        if (rr < R) {
+            const int h = rr / NG, g = rr % NG;
+            float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
+#pragma unroll
+            for (int s = 0; s < VS; ++s) {
+                const int word = 16 * s + col;
+                if (word / WPG == g) {
+                    float4 lo = {acc[s][0][i] + bias_r, acc[s][1][i] + bias_r, acc[s][2][i] + bias_r,
+                                 acc[s][3][i] + bias_r};
+                    float4 hi = {acc[s][4][i] + bias_r, acc[s][5][i] + bias_r, acc[s][6][i] + bias_r,
+                                 acc[s][7][i] + bias_r};
+                    *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
+                    *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
+                }
+            }
+        }
+    }
+}
+
+template <int D, int NG, bool Q32>
+void launch_one_wave(const PartialArgs &a, dim3 grid, hipStream_t s)
+{
+    constexpr int PF = D == 128 ? 4 : 2;
+    hipLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF>), grid, dim3(64), 0, s, a);
+}
+
+// The one-wavefront kernel needs chunks of at most 512 rows whose scale/bias
+// segments start on 16-byte boundaries; it pays off once there are enough
+// (chunk, head) items to give every SIMD two wavefronts.
+bool one_wave_fits(const PartialArgs &a, int D, int batch)
+{
+    const int NG = D / a.G;
+    if (a.chunk > CH1)
+        return false;
+    if (((int64_t)a.chunk * NG) % 8 != 0 || (a.cap * NG) % 8 != 0)
+        return false;
+    (void)batch;
+    return true;
+}
+
 template <int D, int NG>
-hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, hipStream_t s)
+hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, hipStream_t s)
 {
     dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
-    if (q_dtype == KVQ_F32)
+    bool one = variant == KVQ_KERNEL_MFMA_WAVE;
+    if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO)
+        one = one_wave_fits(a, D, batch) && (int64_t)a.num_chunks * a.Hkv * batch >= 2048;
+    if (one && !one_wave_fits(a, D, batch))
+        return hipErrorInvalidValue;
+    if (one) {
+        if (q_dtype == KVQ_F32)
+            launch_one_wave<D, NG, true>(a, grid, s);
+        else
+            launch_one_wave<D, NG, false>(a, grid, s);
+    } else if (q_dtype == KVQ_F32) {
         hipLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, true>), grid, dim3(NT), 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, false>), grid, dim3(NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -516,18 +848,20 @@ bool mfma_supports(int D, int G, int n_rep, int chunk)
     return NG <= 4 && n_rep >= 1 && n_rep * NG <= 16;
 }
 
-hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s)
+hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, hipStream_t s)
 {
     const int NG = D / a.G;
     if (D == 128) {
-        if (NG == 1) return launch_dg<128, 1>(a, q_dtype, batch, s);
-        if (NG == 2) return launch_dg<128, 2>(a, q_dtype, batch, s);
-        if (NG == 4) return launch_dg<128, 4>(a, q_dtype, batch, s);
+        if (NG == 1) return launch_dg<128, 1>(a, q_dtype, batch, variant, s);
+        if (NG == 2) return launch_dg<128, 2>(a, q_dtype, batch, variant, s);
+        if (NG == 4) return launch_dg<128, 4>(a, q_dtype, batch, variant, s);
     } else if (D == 256) {
-        if (NG == 2) return launch_dg<256, 2>(a, q_dtype, batch, s);
-        if (NG == 4) return launch_dg<256, 4>(a, q_dtype, batch, s);
+        if (NG == 2) return launch_dg<256, 2>(a, q_dtype, batch, variant, s);
+        if (NG == 4) return launch_dg<256, 4>(a, q_dtype, batch, variant, s);
     }
     return hipErrorInvalidValue;
 }
+
+bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch) { return one_wave_fits(a, D, batch); }
 
 }  // namespace kvq

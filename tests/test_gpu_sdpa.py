@@ -16,12 +16,25 @@ pytestmark = pytest.mark.gpu
 # The matrix core sums the 32 products of one instruction after aligning them
 # to the largest and truncating the rest (measured: 1 + 0.75 ulp -> 1); with a
 # dominant row in a tile this leaves ~1e-5 relative error, so its gate is 5e-5.
-REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: 5e-5, kvq.KERNEL_MFMA: 5e-5}
+REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: 5e-5, kvq.KERNEL_MFMA: 5e-5, kvq.KERNEL_MFMA_SPLIT: 5e-5,
+          kvq.KERNEL_MFMA_WAVE: 5e-5}
 # With softmax scale 1 and normalised Q/K the scores reach O(100); their fp32
 # rounding (~sqrt(D) * 2^-24 * sum|q k|) passes undamped into the weights, so
 # the per-head L2 gate there is set one decade wider.
 REL_L2_UNSCALED = 2e-4
-KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA, kvq.KERNEL_AUTO]
+KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_AUTO]
+MATRIX = (kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE)
+
+
+def _run(gc, skv, q, alpha, kernel, chunk=512):
+    """run_sdpa, skipping the case when an explicitly requested matrix-core
+    variant does not take this shape (AUTO never fails that way)."""
+    try:
+        return run_sdpa(gc, skv, q, alpha, chunk=chunk, kernel=kernel)
+    except kvq.KvqError as e:
+        if kernel in MATRIX and e.status == -7:
+            pytest.skip("shape outside this matrix-core kernel variant")
+        raise
 
 
 def _oracle_cache(k, v, cap=None, G=64):
@@ -36,7 +49,7 @@ def test_tiny(kernel):
     note("sdpa tiny kernel=%d" % kernel)
     q, k, v, alpha = kvq_synth.tiny_decode()
     oc = _oracle_cache(k, v)
-    out, *_ = run_sdpa(gpu_cache_from_oracle(oc), 1024, q, alpha, kernel=kernel)
+    out, *_ = _run(gpu_cache_from_oracle(oc), 1024, q, alpha, kernel)
     check_attention(out, oracle.sdpa(oc, 1024, q, alpha), REL_L2[kernel], label="tiny")
 
 
@@ -62,7 +75,7 @@ def test_ragged(kernel, skv, chunk):
     k = kvq_synth.normal((1, 2, 1536, 128), [80, 1]).astype(np.float16)
     v = kvq_synth.normal((1, 2, 1536, 128), [80, 2]).astype(np.float16)
     oc = _oracle_cache(k, v)
-    out, *_ = run_sdpa(gpu_cache_from_oracle(oc), skv, q, 0.0884, chunk=chunk, kernel=kernel)
+    out, *_ = _run(gpu_cache_from_oracle(oc), skv, q, 0.0884, kernel, chunk=chunk)
     check_attention(out, oracle.sdpa(oc, skv, q, 0.0884), REL_L2[kernel], label="ragged")
 
 
@@ -79,12 +92,7 @@ def test_shapes(kernel, B, Hq, Hkv, D, G, qdt):
     v = kvq_synth.normal((B, Hkv, S, D), [81, Hq, D, G, 2]).astype(np.float16)
     oc = _oracle_cache(k, v, cap=S + 9, G=G)
     alpha = 1 / np.sqrt(D)
-    try:
-        out, *_ = run_sdpa(gpu_cache_from_oracle(oc), S, q, alpha, kernel=kernel)
-    except kvq.KvqError as e:
-        if kernel == kvq.KERNEL_MFMA and e.status == -7:
-            pytest.skip("shape outside the matrix-core kernel (falls back to the vector kernel)")
-        raise
+    out, *_ = _run(gpu_cache_from_oracle(oc), S, q, alpha, kernel)
     check_attention(out, oracle.sdpa(oc, S, q, alpha), REL_L2[kernel], label="shape")
 
 
@@ -96,7 +104,7 @@ def test_gemma_unscaled(kernel, skv):
     note("sdpa gemma skv=%d kernel=%d" % (skv, kernel))
     q, k, v, alpha = kvq_synth.gemma_layer(skv)
     oc = _oracle_cache(k, v)
-    out, *_ = run_sdpa(gpu_cache_from_oracle(oc), skv, q, alpha, kernel=kernel)
+    out, *_ = _run(gpu_cache_from_oracle(oc), skv, q, alpha, kernel)
     check_attention(out, oracle.sdpa(oc, skv, q, alpha), REL_L2_UNSCALED, atol=1e-3, rtol=1e-3, label="gemma")
 
 
@@ -124,7 +132,7 @@ def test_llama_layer(kernel, skv):
     note("sdpa llama skv=%d kernel=%d" % (skv, kernel))
     q, k, v, alpha = kvq_synth.llama_layer(skv)
     gc, _, _ = _llama_gpu_cache(skv)
-    out, *_ = run_sdpa(gc, skv, q, alpha, kernel=kernel)
+    out, *_ = _run(gc, skv, q, alpha, kernel)
     oc = _oracle_cache(k, v)
     check_attention(out, oracle.sdpa(oc, skv, q, alpha), REL_L2[kernel], label="llama")
 
