@@ -69,8 +69,10 @@ typedef enum kvq_kernel {
     KVQ_KERNEL_MFMA = 2,        /* matrix-core kernels, D in {128, 256} and (Hq/Hkv) * (D/G) <= 16;
                                    the variant below is chosen by grid size */
     KVQ_KERNEL_MFMA_SPLIT = 3,  /* matrix-core, four wavefronts per chunk (any chunk length) */
-    KVQ_KERNEL_MFMA_WAVE = 4    /* matrix-core, one wavefront per chunk: chunk <= 512 and
+    KVQ_KERNEL_MFMA_WAVE = 4,   /* matrix-core, one wavefront per chunk: chunk <= 512 and
                                    chunk * (D/G) and capacity * (D/G) multiples of 8 */
+    KVQ_KERNEL_MFMA_PAIR = 5    /* matrix-core, two wavefronts per chunk (half the rows each):
+                                   the MFMA_WAVE rules, D = 128 and fp16 q */
 } kvq_kernel;
 
 /* One layer's quantised cache (all device pointers, 16-byte aligned). */

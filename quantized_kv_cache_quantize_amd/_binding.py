@@ -11,7 +11,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 KVQ_F16, KVQ_F32 = 0, 1
-KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_SPLIT, KERNEL_MFMA_WAVE = 0, 1, 2, 3, 4
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_SPLIT, KERNEL_MFMA_WAVE, KERNEL_MFMA_PAIR = 0, 1, 2, 3, 4, 5
 
 
 class KvqError(RuntimeError):

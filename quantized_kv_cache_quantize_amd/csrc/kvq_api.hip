@@ -149,11 +149,12 @@ int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, in
     const int64_t C = kvq_num_chunks(skv, chunk);
     if (C > 0x7fffffff)
         return KVQ_E_SHAPE;
-    if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA_WAVE)
+    if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA_PAIR)
         return KVQ_E_SHAPE;
     const int n_rep = Hq / cache->kv_heads;
     const bool mfma_ok = mfma_supports(cache->head_dim, cache->group, n_rep, chunk);
-    const bool want_mfma = kernel == KVQ_KERNEL_MFMA || kernel == KVQ_KERNEL_MFMA_SPLIT || kernel == KVQ_KERNEL_MFMA_WAVE;
+    const bool want_mfma = kernel == KVQ_KERNEL_MFMA || kernel == KVQ_KERNEL_MFMA_SPLIT ||
+                           kernel == KVQ_KERNEL_MFMA_WAVE || kernel == KVQ_KERNEL_MFMA_PAIR;
     if (want_mfma && !mfma_ok)
         return KVQ_E_UNSUPPORTED;
 
@@ -178,6 +179,8 @@ int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, in
     a.G = cache->group;
     a.score_scale = softmax_scale * kLog2e;
     if (kernel == KVQ_KERNEL_MFMA_WAVE && !mfma_one_wave_ok(a, cache->head_dim, cache->batch))
+        return KVQ_E_UNSUPPORTED;
+    if (kernel == KVQ_KERNEL_MFMA_PAIR && !mfma_pair_ok(a, cache->head_dim, q_dtype, cache->batch))
         return KVQ_E_UNSUPPORTED;
     const bool use_mfma = want_mfma || (kernel == KVQ_KERNEL_AUTO && mfma_ok);
     hipError_t e = use_mfma ? launch_partial_mfma(a, cache->head_dim, q_dtype, cache->batch, kernel, (hipStream_t)stream)

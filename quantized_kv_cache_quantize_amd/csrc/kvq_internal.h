@@ -67,6 +67,7 @@ hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int bat
 bool mfma_supports(int D, int G, int n_rep, int chunk);
 hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, hipStream_t s);
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch);
+bool mfma_pair_ok(const PartialArgs &a, int D, int q_dtype, int batch);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
 }  // namespace kvq

@@ -114,6 +114,14 @@ struct Unpacker {
         out[2] = as_h2(and_or(y, 0x000F000Fu, m1024)) - k1032;
         out[3] = as_h2(and_or(y, 0x00F000F0u, m64)) - k72;
     }
+    // out[m] of operator() alone (m a compile-time constant)
+    __device__ __forceinline__ half2v one(uint32_t x, int m) const
+    {
+        const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+        const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
+        const uint32_t z = m >= 2 ? x >> 8 : x;
+        return (m & 1) ? as_h2(and_or(z, 0x00F000F0u, m64)) - k72 : as_h2(and_or(z, 0x000F000Fu, m1024)) - k1032;
+    }
 };
 
 // One K word (dimensions 8w..8w+7 of one row) as an MFMA operand; element j
@@ -504,6 +512,76 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
 // ---------------------------------------------------------------------------
 constexpr int CH1 = 512;  // most rows of a chunk in the one-wavefront kernel
 
+// Sum / max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 row
+// swaps: with both operands equal, the two results of a swap hold a lane's
+// own value and its partner's, in some order. (Each element is copied to a
+// scalar before the bit cast: a bit cast of a vector element in place reads
+// element 0.)
+__device__ __forceinline__ void row_swap16(float v, float &x, float &y)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    x = __builtin_bit_cast(float, r0);
+    y = __builtin_bit_cast(float, r1);
+}
+
+__device__ __forceinline__ void row_swap32(float v, float &x, float &y)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    x = __builtin_bit_cast(float, r0);
+    y = __builtin_bit_cast(float, r1);
+}
+
+// max of two values fresh from a lane swap: fmaxf would first canonicalise
+// both (they arrive through an integer bit cast); med3(x, y, +inf) is the
+// same maximum in one compiler-visible instruction
+__device__ __forceinline__ float max_raw(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); }
+
+__device__ __forceinline__ float xrow_max(float v)
+{
+    float x, y;
+    row_swap16(v, x, y);
+    row_swap32(max_raw(x, y), x, y);
+    return max_raw(x, y);
+}
+
+__device__ __forceinline__ float xrow_sum(float v)
+{
+    float x, y;
+    row_swap16(v, x, y);
+    row_swap32(x + y, x, y);
+    return x + y;
+}
+
+// K words as MFMA operands with the nibbles read as 64 + n: all four nibble
+// positions are moved to mantissa bits 4-7 under the exponent 2^6, so no fp16
+// subtraction is needed. The 64 * sum(q) this adds to every group's dot
+// product is removed with the bias, in fp32, outside the matrix core: the
+// products stay within a factor 79/64 of each other, so the truncating sum of
+// one instruction loses at most a few ulps of 79 |q|max.
+//
+// One asm block ending in s_nop 1: the compiler's hazard tracking does not
+// look inside inline asm, and a matrix instruction reading a register that a
+// vector instruction wrote needs two wait states in between.
+__device__ __forceinline__ half8 k_operand64(uint32_t w, uint32_t m64)
+{
+    uint32_t r0, r1, r2, r3;
+    asm("v_lshlrev_b32 %0, 4, %4\n\t"
+        "v_and_or_b32 %0, %0, %5, %6\n\t"
+        "v_and_or_b32 %1, %4, %5, %6\n\t"
+        "v_lshrrev_b32 %2, 4, %4\n\t"
+        "v_and_or_b32 %2, %2, %5, %6\n\t"
+        "v_lshrrev_b32 %3, 8, %4\n\t"
+        "v_and_or_b32 %3, %3, %5, %6\n\t"
+        "s_nop 1"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(w), "s"(0x00F000F0u), "v"(m64));
+    return cat8(as_h2(r0), as_h2(r1), as_h2(r2), as_h2(r3));
+}
+
 template <int D, int NG, bool Q32, int PF>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
 void sdpa_partial_mfma1_kernel(PartialArgs a)
@@ -513,7 +591,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     constexpr int KM = W / 4;
     constexpr int VS = W / 16;
     constexpr int WPG = W / NG;
-    constexpr int SEG = 8 / NG;  // rows per 16-byte metadata segment
+    constexpr int SEG = 8 / NG;  // rows per 16-byte scale/bias segment
 
     const int lane = threadIdx.x;
     const int q4 = lane >> 4;
@@ -524,8 +602,9 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     const int nrep = a.n_rep;
     const int R = nrep * NG;
     const int hl = col / NG, gl = col % NG;
+    // columns >= R (no query head) compute on zero Q and are never written;
+    // every column keeps its own softmax state, so they need no masking
     const bool col_on = col < R;
-    const float col_mask = col_on ? 0.0f : -INFINITY;
     const int h0 = kvh * nrep;
 
     const int t0 = (int)((int64_t)c * a.chunk);
@@ -540,8 +619,15 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
         make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
 
-    __shared__ __align__(16) uint16_t meta[4 * NG * CH1];  // [array][group][row]
+    // The chunk's scale and bias, staged once as the fp32 factors the tile
+    // code uses, [factor][group][row]:
+    //   0: s_k * c            (c = softmax scale * log2 e)
+    //   1: (b_k - 64 s_k) * c (bias of the 64 + n operands)
+    //   2: s_v
+    //   3: b_v + 8 s_v        (bias of the centred value codes)
+    __shared__ __align__(16) float meta[4 * NG * CH1];
     const Unpacker unpack{0x64006400u, 0x54005400u};
+    const float cs = a.score_scale;
 
     // ---- start-up: Q, the chunk's scale/bias and the first PF tiles, all
     //      requested before the first wait
@@ -565,30 +651,39 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             }
         }
     }
-    // metadata: each array holds CH1 * NG halves = CH1 / SEG segments of 16
-    // bytes (SEG rows x NG groups); lane i takes segments i, i + 64, ...
-    constexpr int SEGS = CH1 / SEG;       // per array
-    constexpr int MPL = 4 * SEGS / 64;    // segments per lane
-    uint4 mraw[MPL];
+    // scale/bias: each array holds CH1 * NG halves = CH1 / SEG segments of 16
+    // bytes (SEG rows x NG groups); lane i takes segments i, i + 64, ... of
+    // all four arrays, so it has the matching K (V) scale and bias at hand
+    constexpr int SEGS = CH1 / SEG;  // per array
+    constexpr int SPL = SEGS / 64;   // segments per lane per array
+    uint4 mraw[SPL][4];
 #pragma unroll
-    for (int i = 0; i < MPL; ++i) {
-        const int sg = lane + 64 * i;
-        const int arr = sg / SEGS;  // uniform per i
-        const int row = (sg % SEGS) * SEG;
-        mraw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mres[arr], (t0 + row) * NG * 2, 0, 0));
-    }
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+        for (int arr = 0; arr < 4; ++arr)
+            mraw[i][arr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                mres[arr], (t0 + (lane + 64 * i) * SEG) * NG * 2, 0, 0));
 
+    // Every ring refill is issued, also past the chunk's last tile: such a
+    // request gets a byte base beyond the buffer's records, so it returns
+    // zeros without touching memory. Unconditional requests keep the number
+    // of loads in flight the same on every path, so each wait only covers the
+    // tile about to be used instead of draining the whole ring.
+    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D / 2 < 2^31)
+    auto tile_base = [&](int ti) -> uint32_t {
+        return ti < ntile ? (uint32_t)(t0 + TILE * ti) * (uint32_t)(W * 4) : kNoRows;
+    };
     uint4 kbuf[PF][2][WPL / 4];
     uint32_t vbuf[PF][VS][8];
-    auto load_tile = [&](int trow, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
+    auto load_tile = [&](uint32_t base, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const int off = ((trow + 16 * blk + col) * W + WPL * q4) * 4;
+            const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + WPL * q4) * 4);
 #pragma unroll
             for (int v4 = 0; v4 < WPL / 4; ++v4)
                 kt[blk][v4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
         }
-        const int voff = ((trow + 4 * q4) * W + col) * 4;
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + col) * 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -596,11 +691,19 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(
                     vq, voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * s2) * 4, 0, 0);
     };
+    // Issue the first PF tiles slot by slot, in the order the ring refills
+    // them. The wait counts at the loop head are the smaller of the start-up
+    // and the steady-state ones; a start-up order with all K loads last would
+    // make every pass over the ring wait for nearly all loads in flight.
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-        if (u < ntile)
-            load_tile(t0 + TILE * u, kbuf[u], vbuf[u]);
+    for (int u = 0; u < PF; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(tile_base(u), kbuf[u], vbuf[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
+    // Q restricted to the column's group, in the dimension order of the K
+    // operands; qsum is the group sum of exactly what the matrix core sees
     half8 qhi[KM], qlo[KM];
     float qsum = 0.0f;
 #pragma unroll
@@ -610,26 +713,38 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float x = mine ? qv[u][kPerm[j]] : 0.0f;
-            qsum += x;
             const _Float16 hi = (_Float16)x;
             qhi[u][j] = hi;
-            if constexpr (Q32)
-                qlo[u][j] = (_Float16)(x - (float)hi);
+            if constexpr (Q32) {
+                const _Float16 lo = (_Float16)(x - (float)hi);
+                qlo[u][j] = lo;
+                qsum += (float)hi + (float)lo;
+            } else {
+                qsum += (float)hi;
+            }
         }
     }
-    qsum = quarter_sum(qsum);
+    qsum = xrow_sum(qsum);
 
-    // transpose the metadata segments into [array][group][row]
+    // scale/bias segments -> fp32 factors in LDS
 #pragma unroll
-    for (int i = 0; i < MPL; ++i) {
-        const int sg = lane + 64 * i;
-        const int arr = sg / SEGS;
-        const int row = (sg % SEGS) * SEG;
-        const uint32_t w[4] = {mraw[i].x, mraw[i].y, mraw[i].z, mraw[i].w};
+    for (int i = 0; i < SPL; ++i) {
+        const int row0 = (lane + 64 * i) * SEG;
+        const uint32_t w[4][4] = {{mraw[i][0].x, mraw[i][0].y, mraw[i][0].z, mraw[i][0].w},
+                                  {mraw[i][1].x, mraw[i][1].y, mraw[i][1].z, mraw[i][1].w},
+                                  {mraw[i][2].x, mraw[i][2].y, mraw[i][2].z, mraw[i][2].w},
+                                  {mraw[i][3].x, mraw[i][3].y, mraw[i][3].z, mraw[i][3].w}};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {  // half e of the segment: row + e / NG, group e % NG
-            const uint16_t h = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-            meta[(arr * NG + (e % NG)) * CH1 + row + e / NG] = h;
+        for (int e = 0; e < 8; ++e) {  // half e of a segment: row row0 + e / NG, group e % NG
+            const int g = e % NG, row = row0 + e / NG;
+            const float ks = h_val((uint16_t)(w[0][e >> 1] >> (16 * (e & 1))));
+            const float kb = h_val((uint16_t)(w[1][e >> 1] >> (16 * (e & 1))));
+            const float vs = h_val((uint16_t)(w[2][e >> 1] >> (16 * (e & 1))));
+            const float vb = h_val((uint16_t)(w[3][e >> 1] >> (16 * (e & 1))));
+            meta[(0 * NG + g) * CH1 + row] = ks * cs;
+            meta[(1 * NG + g) * CH1 + row] = fmaf(-64.0f, ks, kb) * cs;
+            meta[(2 * NG + g) * CH1 + row] = vs;
+            meta[(3 * NG + g) * CH1 + row] = fmaf(8.0f, vs, vb);
         }
     }
     // the wavefront's own LDS writes are seen by its later reads (LDS
@@ -639,7 +754,6 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    const float cs = a.score_scale;
     float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
     float4v acc[VS][8];
 #pragma unroll
@@ -652,16 +766,15 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     for (int kk = 0; kk < ntile; kk += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
+            // tiles past the chunk (ntile not a multiple of PF) are run too:
+            // their rows are all masked and their codes read as zeros, so
+            // they add nothing, and the loop has no exit but its own test
             const int ti = kk + u;
-            if (ti >= ntile)
-                break;
-            const bool tail = t0 + TILE * ti + TILE > t1;  // uniform
             const uint4 (&kcur)[2][WPL / 4] = kbuf[u];
             const uint32_t (&vcur)[VS][8] = vbuf[u];
 
-            // ---- scores of the tile's 8 rows held by this lane
+            // ---- scores of the tile's 8 rows held by this lane (log2 units)
             float sc[8];
-            float mx = -INFINITY;
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -669,31 +782,32 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 for (int uu = 0; uu < KM; ++uu) {
                     const uint4 x = kcur[blk][uu / 4];
                     const uint32_t w = (uu % 4 == 0) ? x.x : (uu % 4 == 1) ? x.y : (uu % 4 == 2) ? x.z : x.w;
-                    half2v hk[4];
-                    unpack(w, hk);
-                    const half8 ka = cat8(hk[0], hk[1], hk[2], hk[3]);
+                    const half8 ka = k_operand64(w, unpack.m64);
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[uu], sacc, 0, 0, 0);
                     if constexpr (Q32)
                         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[uu], sacc, 0, 0, 0);
                 }
-                const int lr0 = TILE * ti + 16 * blk + 4 * q4;  // chunk-relative row
-                float ks[4], kb[4];
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(0 * NG + gl) * CH1 + lr0]), ks);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(1 * NG + gl) * CH1 + lr0]), kb);
+                // rows TILE*ti + 16*blk + 4*q4 + i (chunk-relative) of column (hl, gl)
+                const int lr0 = TILE * ti + 16 * blk + 4 * q4;
+                const float4v ksc = *reinterpret_cast<const float4v *>(&meta[(0 * NG + gl) * CH1 + lr0]);
+                const float4v kbc = *reinterpret_cast<const float4v *>(&meta[(1 * NG + gl) * CH1 + lr0]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float kb8 = fmaf(8.0f, ks[i], kb[i]);  // bias of the centred codes
-                    const float part = fmaf(ks[i], sacc[i], kb8 * qsum);
-                    float v = fmaf(group_sum<NG>(part), cs, col_mask);
-                    if (tail)
-                        v = (t0 + lr0 + i <= last) ? v : -INFINITY;
-                    sc[4 * blk + i] = v;
-                    mx = fmaxf(mx, v);
+                for (int i = 0; i < 4; ++i)
+                    sc[4 * blk + i] = group_sum<NG>(fmaf(ksc[i], sacc[i], kbc[i] * qsum));
+            }
+            if (t0 + TILE * ti + TILE > t1) {  // uniform: the chunk's last tiles
+                asm volatile("" ::: "memory");  // keep this a branch
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = t0 + TILE * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
+                    sc[i] = r <= last ? sc[i] : -INFINITY;
                 }
             }
+            float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
 
             // ---- online softmax across tiles: rescale only when a head's max rises
-            mx = quarter_max(mx);
+            mx = xrow_max(mx);
             const float m_new = fmaxf(m_run, mx);
             if (ti != 0 && __builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
                 const float corr = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
@@ -712,57 +826,61 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             m_run = m_new;
             const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
 
-            // ---- weights and values
-            float vs[8], vb[8];
-            {
-                const int lr0 = TILE * ti + 4 * q4;
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * CH1 + lr0]), &vs[0]);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * CH1 + lr0 + 16]), &vs[4]);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * CH1 + lr0]), &vb[0]);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * CH1 + lr0 + 16]), &vb[4]);
-            }
+            // ---- weights p * s_v as hi + lo fp16 halves, and the bias term
+            const int lv0 = TILE * ti + 4 * q4;
+            const float4v vs0 = *reinterpret_cast<const float4v *>(&meta[(2 * NG + gl) * CH1 + lv0]);
+            const float4v vs1 = *reinterpret_cast<const float4v *>(&meta[(2 * NG + gl) * CH1 + lv0 + 16]);
+            const float4v vb0 = *reinterpret_cast<const float4v *>(&meta[(3 * NG + gl) * CH1 + lv0]);
+            const float4v vb1 = *reinterpret_cast<const float4v *>(&meta[(3 * NG + gl) * CH1 + lv0 + 16]);
             half8 phi, plo;
             float lsum = 0.0f, bsum = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = __builtin_amdgcn_exp2f(sc[j] - m_use);
-                lsum += p;
-                bsum = fmaf(p, fmaf(8.0f, vs[j], vb[j]), bsum);  // bias of the centred codes
-                const float pw = p * vs[j];
-                const _Float16 hi = (_Float16)pw;
-                phi[j] = hi;
-                plo[j] = (_Float16)(pw - (float)hi);
+            for (int j = 0; j < 8; j += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(sc[j] - m_use);
+                const float p1 = __builtin_amdgcn_exp2f(sc[j + 1] - m_use);
+                const float s0 = j < 4 ? vs0[j] : vs1[j - 4], s1 = j < 4 ? vs0[j + 1] : vs1[j - 3];
+                const float c0 = j < 4 ? vb0[j] : vb1[j - 4], c1 = j < 4 ? vb0[j + 1] : vb1[j - 3];
+                lsum += p0 + p1;
+                bsum = fmaf(p0, c0, fmaf(p1, c1, bsum));
+                const float w0 = p0 * s0, w1 = p1 * s1;
+                // any rounding of hi works: lo = w - hi is exact in fp32
+                const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0 - (float)h[0], w1 - (float)h[1]));
+                phi[j] = h[0]; phi[j + 1] = h[1];
+                plo[j] = l[0]; plo[j + 1] = l[1];
             }
             l_run += lsum;
             b_run += bsum;
 #pragma unroll
             for (int s2 = 0; s2 < VS; ++s2) {
-                half2v lo4[4][4], hi4[4][4];  // [pair][m]
+                // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
+                // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
+                uint32_t xw[4], yw[4];
 #pragma unroll
                 for (int jp = 0; jp < 4; ++jp) {
-                    const uint32_t x = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
-                    const uint32_t y = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
-                    unpack(x, lo4[jp]);
-                    unpack(y, hi4[jp]);
+                    xw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
+                    yw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
                 }
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    const half8 bv = m < 4 ? cat8(lo4[0][m], lo4[1][m], lo4[2][m], lo4[3][m])
-                                           : cat8(hi4[0][m - 4], hi4[1][m - 4], hi4[2][m - 4], hi4[3][m - 4]);
+                    half2v e[4];
+#pragma unroll
+                    for (int jp = 0; jp < 4; ++jp)
+                        e[jp] = unpack.one(m < 4 ? xw[jp] : yw[jp], m & 3);
+                    const half8 bv = cat8(e[0], e[1], e[2], e[3]);
                     acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
                     acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
                 }
             }
 
             // ---- refill this ring slot
-            if (ti + PF < ntile)
-                load_tile(t0 + TILE * (ti + PF), kbuf[u], vbuf[u]);
+            load_tile(tile_base(ti + PF), kbuf[u], vbuf[u]);
         }
     }
 
     // ---- write the partial state of this chunk
-    const float l_tot = quarter_sum(l_run);
-    const float b_tot = quarter_sum(b_run);
+    const float l_tot = xrow_sum(l_run);
+    const float b_tot = xrow_sum(b_run);
     const int64_t C = a.num_chunks;
     if (q4 == 0 && col_on && gl == 0) {
         const int64_t o = ((int64_t)b * a.Hq + h0 + hl) * C + c;
@@ -792,11 +910,316 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Wavefront-pair variant (D = 128, fp16 Q): a 128-thread workgroup owns one
+// (chunk <= 512 rows, KV head, batch); wavefront w streams the rows
+// [w * RW, (w + 1) * RW) of the chunk with the one-wavefront tile code, and
+// wavefront 1 hands its softmax state to wavefront 0 through LDS at the end.
+// Each wavefront fits in 128 registers (two-tile ring), so a SIMD holds four
+// of them: twice the independent instruction streams of the one-wavefront
+// kernel for the same partial-output traffic.
+// ---------------------------------------------------------------------------
+constexpr int RW2 = CH1 / 2;  // most rows per wavefront in the pair kernel
+
+template <int NG, int PF>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4)))
+void sdpa_partial_mfma_pair_kernel(PartialArgs a)
+{
+    constexpr int D = 128;
+    constexpr int W = D / 8;
+    constexpr int WPL = W / 4;
+    constexpr int KM = W / 4;
+    constexpr int WPG = W / NG;
+    constexpr int SEG = 8 / NG;
+    constexpr int META = 4 * NG * RW2;            // halves per wavefront
+    constexpr int XCH = (3 + 32) * 64;            // floats handed over: m, l, b and acc per lane
+    constexpr int SMEM = (2 * META * 2 > XCH * 4) ? 2 * META * 2 : XCH * 4;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q4 = lane >> 4;
+    const int col = lane & 15;
+    const int c = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int nrep = a.n_rep;
+    const int R = nrep * NG;
+    const int hl = col / NG, gl = col % NG;
+    const bool col_on = col < R;
+    const float col_mask = col_on ? 0.0f : -INFINITY;
+    const int h0 = kvh * nrep;
+
+    const int c0 = (int)((int64_t)c * a.chunk);
+    const int c1 = (int)min((int64_t)c0 + a.chunk, a.skv);
+    // rows per wavefront: half the chunk, rounded up to whole tiles
+    const int rw = ((a.chunk + 1) / 2 + TILE - 1) / TILE * TILE;
+    const int t0 = min(c0 + wave * rw, c1);
+    const int t1 = min(t0 + rw, c1);
+    const int last = t1 - 1;
+    const int ntile = (t1 - t0 + TILE - 1) / TILE;
+    const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
+    const uint32_t rows_ok = (uint32_t)a.skv;
+    const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t mres[4] = {
+        make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
+        make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
+
+    __shared__ __align__(16) float smem_f[SMEM / 4];
+    uint16_t *meta = reinterpret_cast<uint16_t *>(smem_f) + wave * META;  // [array][group][row]
+    const Unpacker unpack{0x64006400u, 0x54005400u};
+
+    // ---- start-up: Q, this wavefront's scale/bias and the first PF tiles
+    half8 qv[KM];
+    {
+        const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
+#pragma unroll
+        for (int u = 0; u < KM; ++u)
+            qv[u] = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow + 8 * (WPL * q4 + u));
+    }
+    constexpr int SEGS = RW2 / SEG;     // 16-byte segments per array
+    constexpr int MPL = 4 * SEGS / 64;  // segments per lane
+    // (a wavefront with no rows reads the chunk's first rows, 16-byte aligned, and ignores them)
+    const int mt0 = ntile > 0 ? t0 : c0;
+    uint4 mraw[MPL];
+#pragma unroll
+    for (int i = 0; i < MPL; ++i) {
+        const int sg = lane + 64 * i;
+        const int arr = sg / SEGS;
+        const int row = (sg % SEGS) * SEG;
+        mraw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mres[arr], (mt0 + row) * NG * 2, 0, 0));
+    }
+
+    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D / 2 < 2^31)
+    auto tile_base = [&](int ti) -> uint32_t {
+        return ti < ntile ? (uint32_t)(t0 + TILE * ti) * (uint32_t)(W * 4) : kNoRows;
+    };
+    uint4 kbuf[PF][2];
+    uint32_t vbuf[PF][8];
+    auto load_tile = [&](uint32_t base, uint4 (&kt)[2], uint32_t (&vt)[8]) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+            kt[blk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                kq, base + (uint32_t)(((16 * blk + col) * W + WPL * q4) * 4), 0, 0));
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + col) * 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + (16 * (j >> 2) + (j & 3)) * W * 4, 0, 0);
+    };
+    // slot by slot, in the order the ring refills them (see the one-wavefront kernel)
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(tile_base(u), kbuf[u], vbuf[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    half8 qhi[KM];
+    float qsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < KM; ++u) {
+        const bool mine = col_on && ((WPL * q4 + u) / WPG) == gl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const _Float16 x = mine ? qv[u][kPerm[j]] : (_Float16)0.0f;
+            qsum += (float)x;
+            qhi[u][j] = x;
+        }
+    }
+    qsum = quarter_sum(qsum);
+
+#pragma unroll
+    for (int i = 0; i < MPL; ++i) {
+        const int sg = lane + 64 * i;
+        const int arr = sg / SEGS;
+        const int row = (sg % SEGS) * SEG;
+        const uint32_t w[4] = {mraw[i].x, mraw[i].y, mraw[i].z, mraw[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            meta[(arr * NG + (e % NG)) * RW2 + row + e / NG] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const float cs = a.score_scale;
+    float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
+    float4v acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        acc[m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll 1
+    for (int kk = 0; kk < ntile; kk += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int ti = kk + u;  // tiles past the end are fully masked (see the one-wavefront kernel)
+            const bool tail = t0 + TILE * ti + TILE > t1;
+            float sc[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+                const uint4 x = kbuf[u][blk];
+#pragma unroll
+                for (int uu = 0; uu < KM; ++uu) {
+                    const uint32_t w = uu == 0 ? x.x : uu == 1 ? x.y : uu == 2 ? x.z : x.w;
+                    half2v hk[4];
+                    unpack(w, hk);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(hk[0], hk[1], hk[2], hk[3]), qhi[uu], sacc, 0, 0, 0);
+                }
+                const int lr0 = TILE * ti + 16 * blk + 4 * q4;  // wavefront-relative row
+                float ks[4], kb[4];
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(0 * NG + gl) * RW2 + lr0]), ks);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(1 * NG + gl) * RW2 + lr0]), kb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float kb8 = fmaf(8.0f, ks[i], kb[i]);
+                    const float part = fmaf(ks[i], sacc[i], kb8 * qsum);
+                    float v = fmaf(group_sum<NG>(part), cs, col_mask);
+                    if (tail)
+                        v = (t0 + lr0 + i <= last) ? v : -INFINITY;
+                    sc[4 * blk + i] = v;
+                    mx = fmaxf(mx, v);
+                }
+            }
+            mx = quarter_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            if (ti != 0 && __builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+                const float corr = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+                l_run *= corr;
+                b_run *= corr;
+                float4v corr_row;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    corr_row[i] = __shfl(corr, 4 * q4 + i);
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    acc[m] *= corr_row;
+            }
+            m_run = m_new;
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+
+            float vs[8], vb[8];
+            {
+                const int lr0 = TILE * ti + 4 * q4;
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * RW2 + lr0]), &vs[0]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * RW2 + lr0 + 16]), &vs[4]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * RW2 + lr0]), &vb[0]);
+                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * RW2 + lr0 + 16]), &vb[4]);
+            }
+            half8 phi, plo;
+            float lsum = 0.0f, bsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float p = __builtin_amdgcn_exp2f(sc[j] - m_use);
+                lsum += p;
+                bsum = fmaf(p, fmaf(8.0f, vs[j], vb[j]), bsum);
+                const float pw = p * vs[j];
+                const _Float16 hi = (_Float16)pw;
+                phi[j] = hi;
+                plo[j] = (_Float16)(pw - (float)hi);
+            }
+            l_run += lsum;
+            b_run += bsum;
+            {
+                // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
+                // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
+                uint32_t xw[4], yw[4];
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    xw[jp] = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x05040100u);
+                    yw[jp] = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x07060302u);
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    half2v e[4];
+#pragma unroll
+                    for (int jp = 0; jp < 4; ++jp)
+                        e[jp] = unpack.one(m < 4 ? xw[jp] : yw[jp], m & 3);
+                    const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[m], 0, 0, 0);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[m], 0, 0, 0);
+                }
+            }
+            load_tile(tile_base(ti + PF), kbuf[u], vbuf[u]);
+        }
+    }
+
+    // ---- wavefront 1 hands (m, l, b, acc) to wavefront 0, which merges
+    __syncthreads();  // both wavefronts are done with their scale/bias rows
+    float *xch = smem_f;
+    if (wave == 1) {
+        xch[0 * 64 + lane] = m_run;
+        xch[1 * 64 + lane] = l_run;
+        xch[2 * 64 + lane] = b_run;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            *reinterpret_cast<float4v *>(&xch[(3 + 4 * m) * 64 + 4 * lane]) = acc[m];
+    }
+    __syncthreads();
+    if (wave == 1)
+        return;
+    {
+        const float m1 = xch[0 * 64 + lane];
+        const float M = fmaxf(m_run, m1);
+        const float Mu = (M == -INFINITY) ? 0.0f : M;
+        const float f0 = __builtin_amdgcn_exp2f(m_run - Mu);  // exp2(-inf) = 0
+        const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
+        l_run = fmaf(l_run, f0, xch[1 * 64 + lane] * f1);
+        b_run = fmaf(b_run, f0, xch[2 * 64 + lane] * f1);
+        m_run = M;
+        float4v f0r, f1r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f0r[i] = __shfl(f0, 4 * q4 + i);
+            f1r[i] = __shfl(f1, 4 * q4 + i);
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float4v o = *reinterpret_cast<const float4v *>(&xch[(3 + 4 * m) * 64 + 4 * lane]);
+            acc[m] = acc[m] * f0r + o * f1r;
+        }
+    }
+
+    // ---- write the partial state of this chunk
+    const float l_tot = quarter_sum(l_run);
+    const float b_tot = quarter_sum(b_run);
+    const int64_t C = a.num_chunks;
+    if (q4 == 0 && col_on && gl == 0) {
+        const int64_t o = ((int64_t)b * a.Hq + h0 + hl) * C + c;
+        a.part_m[o] = m_run * kLn2;
+        a.part_l[o] = l_tot;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * q4 + i;
+        const float bias_r = __shfl(b_tot, rr);
+        if (rr < R) {
+            const int h = rr / NG, g = rr % NG;
+            float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
+            const int word = col;
+            if (word / WPG == g) {
+                float4 lo = {acc[0][i] + bias_r, acc[1][i] + bias_r, acc[2][i] + bias_r, acc[3][i] + bias_r};
+                float4 hi = {acc[4][i] + bias_r, acc[5][i] + bias_r, acc[6][i] + bias_r, acc[7][i] + bias_r};
+                *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
+                *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
+            }
+        }
+    }
+}
+
 template <int D, int NG, bool Q32>
 void launch_one_wave(const PartialArgs &a, dim3 grid, hipStream_t s)
 {
     constexpr int PF = D == 128 ? 4 : 2;
     hipLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF>), grid, dim3(64), 0, s, a);
+}
+
+template <int NG>
+void launch_pair(const PartialArgs &a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((sdpa_partial_mfma_pair_kernel<NG, 2>), grid, dim3(128), 0, s, a);
 }
 
 // The one-wavefront kernel needs chunks of at most 512 rows whose scale/bias
@@ -807,22 +1230,37 @@ bool one_wave_fits(const PartialArgs &a, int D, int batch)
     const int NG = D / a.G;
     if (a.chunk > CH1)
         return false;
+    if (D == 128 && NG > 2)  // fp32 scale/bias staging: 32 KB per wavefront at NG = 4
+        return false;
     if (((int64_t)a.chunk * NG) % 8 != 0 || (a.cap * NG) % 8 != 0)
         return false;
     (void)batch;
     return true;
 }
 
+// The pair kernel: the one-wavefront layout rules, D = 128 and fp16 Q.
+bool pair_fits(const PartialArgs &a, int D, int q_dtype, int batch)
+{
+    return D == 128 && q_dtype == KVQ_F16 && one_wave_fits(a, D, batch);
+}
+
 template <int D, int NG>
 hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, hipStream_t s)
 {
     dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
+    const int64_t items = (int64_t)a.num_chunks * a.Hkv * batch;
+    bool pair = variant == KVQ_KERNEL_MFMA_PAIR;
     bool one = variant == KVQ_KERNEL_MFMA_WAVE;
-    if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO)
-        one = one_wave_fits(a, D, batch) && (int64_t)a.num_chunks * a.Hkv * batch >= 2048;
-    if (one && !one_wave_fits(a, D, batch))
+    if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO) {
+        pair = pair_fits(a, D, q_dtype, batch) && items >= 2048;
+        one = !pair && one_wave_fits(a, D, batch) && items >= 2048;
+    }
+    if ((one && !one_wave_fits(a, D, batch)) || (pair && !pair_fits(a, D, q_dtype, batch)))
         return hipErrorInvalidValue;
-    if (one) {
+    if (pair) {
+        if constexpr (D == 128)
+            launch_pair<NG>(a, grid, s);
+    } else if (one) {
         if (q_dtype == KVQ_F32)
             launch_one_wave<D, NG, true>(a, grid, s);
         else
@@ -863,5 +1301,7 @@ hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int bat
 }
 
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch) { return one_wave_fits(a, D, batch); }
+
+bool mfma_pair_ok(const PartialArgs &a, int D, int q_dtype, int batch) { return pair_fits(a, D, q_dtype, batch); }
 
 }  // namespace kvq

@@ -17,13 +17,13 @@ pytestmark = pytest.mark.gpu
 # to the largest and truncating the rest (measured: 1 + 0.75 ulp -> 1); with a
 # dominant row in a tile this leaves ~1e-5 relative error, so its gate is 5e-5.
 REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: 5e-5, kvq.KERNEL_MFMA: 5e-5, kvq.KERNEL_MFMA_SPLIT: 5e-5,
-          kvq.KERNEL_MFMA_WAVE: 5e-5}
+          kvq.KERNEL_MFMA_WAVE: 5e-5, kvq.KERNEL_MFMA_PAIR: 5e-5}
 # With softmax scale 1 and normalised Q/K the scores reach O(100); their fp32
 # rounding (~sqrt(D) * 2^-24 * sum|q k|) passes undamped into the weights, so
 # the per-head L2 gate there is set one decade wider.
 REL_L2_UNSCALED = 2e-4
-KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_AUTO]
-MATRIX = (kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE)
+KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_MFMA_PAIR, kvq.KERNEL_AUTO]
+MATRIX = (kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_MFMA_PAIR)
 
 
 def _run(gc, skv, q, alpha, kernel, chunk=512):
