@@ -591,7 +591,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     constexpr int KM = W / 4;
     constexpr int VS = W / 16;
     constexpr int WPG = W / NG;
-    constexpr int SEG = 8 / NG;  // rows per 16-byte scale/bias segment
+    constexpr int PAIRS = TILE * NG;        // (row, group) pairs of scale/bias per tile
+    constexpr int MP = (PAIRS + 63) / 64;   // pairs per lane (NG = 1: lanes 32-63 repeat 0-31)
 
     const int lane = threadIdx.x;
     const int q4 = lane >> 4;
@@ -619,18 +620,19 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
         make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
 
-    // The chunk's scale and bias, staged once as the fp32 factors the tile
-    // code uses, [factor][group][row]:
-    //   0: s_k * c            (c = softmax scale * log2 e)
-    //   1: (b_k - 64 s_k) * c (bias of the 64 + n operands)
-    //   2: s_v
-    //   3: b_v + 8 s_v        (bias of the centred value codes)
-    __shared__ __align__(16) float meta[4 * NG * CH1];
+    // Scale and bias travel with the tiles: a lane loads the four fp16 values
+    // of MP (row, group) pairs of a tile; one tile ahead of use they become
+    // the fp32 factors of the tile code, one 16-byte record per pair in a
+    // two-slot LDS buffer [slot][row * NG + group]:
+    //   x: s_k * c            (c = softmax scale * log2 e)
+    //   y: (b_k - 64 s_k) * c (bias of the 64 + n operands)
+    //   z: s_v
+    //   w: b_v + 8 s_v        (bias of the centred value codes)
+    __shared__ __align__(16) float4 mring[2][PAIRS];
     const Unpacker unpack{0x64006400u, 0x54005400u};
     const float cs = a.score_scale;
 
-    // ---- start-up: Q, the chunk's scale/bias and the first PF tiles, all
-    //      requested before the first wait
+    // ---- start-up: Q and the first PF tiles, all requested before the first wait
     float qv[KM][8];
     {
         const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
@@ -651,31 +653,29 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             }
         }
     }
-    // scale/bias: each array holds CH1 * NG halves = CH1 / SEG segments of 16
-    // bytes (SEG rows x NG groups); lane i takes segments i, i + 64, ... of
-    // all four arrays, so it has the matching K (V) scale and bias at hand
-    constexpr int SEGS = CH1 / SEG;  // per array
-    constexpr int SPL = SEGS / 64;   // segments per lane per array
-    uint4 mraw[SPL][4];
-#pragma unroll
-    for (int i = 0; i < SPL; ++i)
-#pragma unroll
-        for (int arr = 0; arr < 4; ++arr)
-            mraw[i][arr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                mres[arr], (t0 + (lane + 64 * i) * SEG) * NG * 2, 0, 0));
 
     // Every ring refill is issued, also past the chunk's last tile: such a
     // request gets a byte base beyond the buffer's records, so it returns
     // zeros without touching memory. Unconditional requests keep the number
     // of loads in flight the same on every path, so each wait only covers the
-    // tile about to be used instead of draining the whole ring.
+    // data about to be used instead of draining the whole ring.
     constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D / 2 < 2^31)
-    auto tile_base = [&](int ti) -> uint32_t {
-        return ti < ntile ? (uint32_t)(t0 + TILE * ti) * (uint32_t)(W * 4) : kNoRows;
-    };
     uint4 kbuf[PF][2][WPL / 4];
     uint32_t vbuf[PF][VS][8];
-    auto load_tile = [&](uint32_t base, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8]) {
+    uint32_t mbuf[PF][MP][4];
+    // scale/bias of a tile first, then its K and V words (a wait for the
+    // scale/bias of the next tile then leaves that tile's words in flight)
+    auto load_tile = [&](int ti, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8], uint32_t (&mt)[MP][4]) {
+        const bool in = ti < ntile;
+#pragma unroll
+        for (int p = 0; p < MP; ++p) {
+            const int pr = (lane + 64 * p) % PAIRS;
+            const uint32_t off = in ? (uint32_t)((t0 + TILE * ti) * NG + pr) * 2u : kNoRows;
+#pragma unroll
+            for (int arr = 0; arr < 4; ++arr)
+                mt[p][arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], off, 0, 0);
+        }
+        const uint32_t base = in ? (uint32_t)(t0 + TILE * ti) * (uint32_t)(W * 4) : kNoRows;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + WPL * q4) * 4);
@@ -691,6 +691,20 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(
                     vq, voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * s2) * 4, 0, 0);
     };
+    auto stage_meta = [&](int slot, const uint32_t (&mt)[MP][4]) {
+#pragma unroll
+        for (int p = 0; p < MP; ++p) {
+            const int pr = (lane + 64 * p) % PAIRS;
+            const float ks = h_val((uint16_t)mt[p][0]);
+            const float kb = h_val((uint16_t)mt[p][1]);
+            const float vs = h_val((uint16_t)mt[p][2]);
+            const float vb = h_val((uint16_t)mt[p][3]);
+            mring[slot][pr] = make_float4(ks * cs, fmaf(-64.0f, ks, kb) * cs, vs, fmaf(8.0f, vs, vb));
+        }
+        // LDS instructions of a wavefront execute in order, so the tile code
+        // sees these records; only the compiler must not move reads above
+        asm volatile("" ::: "memory");
+    };
     // Issue the first PF tiles slot by slot, in the order the ring refills
     // them. The wait counts at the loop head are the smaller of the start-up
     // and the steady-state ones; a start-up order with all K loads last would
@@ -698,7 +712,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(tile_base(u), kbuf[u], vbuf[u]);
+        load_tile(u, kbuf[u], vbuf[u], mbuf[u]);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -725,34 +739,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         }
     }
     qsum = xrow_sum(qsum);
-
-    // scale/bias segments -> fp32 factors in LDS
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-        const int row0 = (lane + 64 * i) * SEG;
-        const uint32_t w[4][4] = {{mraw[i][0].x, mraw[i][0].y, mraw[i][0].z, mraw[i][0].w},
-                                  {mraw[i][1].x, mraw[i][1].y, mraw[i][1].z, mraw[i][1].w},
-                                  {mraw[i][2].x, mraw[i][2].y, mraw[i][2].z, mraw[i][2].w},
-                                  {mraw[i][3].x, mraw[i][3].y, mraw[i][3].z, mraw[i][3].w}};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {  // half e of a segment: row row0 + e / NG, group e % NG
-            const int g = e % NG, row = row0 + e / NG;
-            const float ks = h_val((uint16_t)(w[0][e >> 1] >> (16 * (e & 1))));
-            const float kb = h_val((uint16_t)(w[1][e >> 1] >> (16 * (e & 1))));
-            const float vs = h_val((uint16_t)(w[2][e >> 1] >> (16 * (e & 1))));
-            const float vb = h_val((uint16_t)(w[3][e >> 1] >> (16 * (e & 1))));
-            meta[(0 * NG + g) * CH1 + row] = ks * cs;
-            meta[(1 * NG + g) * CH1 + row] = fmaf(-64.0f, ks, kb) * cs;
-            meta[(2 * NG + g) * CH1 + row] = vs;
-            meta[(3 * NG + g) * CH1 + row] = fmaf(8.0f, vs, vb);
-        }
-    }
-    // the wavefront's own LDS writes are seen by its later reads (LDS
-    // instructions of a wavefront execute in order); keep the compiler from
-    // moving reads above the writes
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    stage_meta(0, mbuf[0]);
 
     float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
     float4v acc[VS][8];
@@ -787,8 +774,16 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             // their rows are all masked and their codes read as zeros, so
             // they add nothing, and the loop has no exit but its own test
             const int ti = kk + u;
+            const int slot = u & 1;  // PF is even, so this is ti & 1
             const uint4 (&kcur)[2][WPL / 4] = kbuf[u];
             const uint32_t (&vcur)[VS][8] = vbuf[u];
+
+            // factors of the tile's 8 rows held by this lane: rows 4*q4 + i
+            // (i < 4) and 16 + 4*q4 + i - 4 (i >= 4), column group gl
+            float4 fac[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                fac[i] = mring[slot][(16 * (i >> 2) + 4 * q4 + (i & 3)) * NG + gl];
 
             // ---- scores of the tile's 8 rows held by this lane (log2 units)
             float sc[8];
@@ -804,13 +799,11 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                     if constexpr (Q32)
                         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[uu], sacc, 0, 0, 0);
                 }
-                // rows TILE*ti + 16*blk + 4*q4 + i (chunk-relative) of column (hl, gl)
-                const int lr0 = TILE * ti + 16 * blk + 4 * q4;
-                const float4v ksc = *reinterpret_cast<const float4v *>(&meta[(0 * NG + gl) * CH1 + lr0]);
-                const float4v kbc = *reinterpret_cast<const float4v *>(&meta[(1 * NG + gl) * CH1 + lr0]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sc[4 * blk + i] = group_sum<NG>(fmaf(ksc[i], sacc[i], kbc[i] * qsum));
+                for (int i = 0; i < 4; ++i) {
+                    const float4 f = fac[4 * blk + i];
+                    sc[4 * blk + i] = group_sum<NG>(fmaf(f.x, sacc[i], f.y * qsum));
+                }
             }
             if (t0 + TILE * ti + TILE > t1) {  // uniform: the chunk's last tiles
                 asm volatile("" ::: "memory");  // keep this a branch
@@ -844,22 +837,15 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
 
             // ---- weights p * s_v as hi + lo fp16 halves, and the bias term
-            const int lv0 = TILE * ti + 4 * q4;
-            const float4v vs0 = *reinterpret_cast<const float4v *>(&meta[(2 * NG + gl) * CH1 + lv0]);
-            const float4v vs1 = *reinterpret_cast<const float4v *>(&meta[(2 * NG + gl) * CH1 + lv0 + 16]);
-            const float4v vb0 = *reinterpret_cast<const float4v *>(&meta[(3 * NG + gl) * CH1 + lv0]);
-            const float4v vb1 = *reinterpret_cast<const float4v *>(&meta[(3 * NG + gl) * CH1 + lv0 + 16]);
             half8 phi, plo;
             float lsum = 0.0f, bsum = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(sc[j] - m_use);
                 const float p1 = __builtin_amdgcn_exp2f(sc[j + 1] - m_use);
-                const float s0 = j < 4 ? vs0[j] : vs1[j - 4], s1 = j < 4 ? vs0[j + 1] : vs1[j - 3];
-                const float c0 = j < 4 ? vb0[j] : vb1[j - 4], c1 = j < 4 ? vb0[j + 1] : vb1[j - 3];
                 lsum += p0 + p1;
-                bsum = fmaf(p0, c0, fmaf(p1, c1, bsum));
-                const float w0 = p0 * s0, w1 = p1 * s1;
+                bsum = fmaf(p0, fac[j].w, fmaf(p1, fac[j + 1].w, bsum));
+                const float w0 = p0 * fac[j].z, w1 = p1 * fac[j + 1].z;
                 // any rounding of hi works: lo = w - hi is exact in fp32
                 const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
                 const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0 - (float)h[0], w1 - (float)h[1]));
@@ -890,8 +876,9 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 }
             }
 
-            // ---- refill this ring slot
-            load_tile(tile_base(ti + PF), kbuf[u], vbuf[u]);
+            // ---- refill this ring slot, then the next tile's factors
+            load_tile(ti + PF, kbuf[u], vbuf[u], mbuf[u]);
+            stage_meta(slot ^ 1, mbuf[(u + 1) % PF]);
         }
     }
 
@@ -1246,8 +1233,6 @@ bool one_wave_fits(const PartialArgs &a, int D, int batch)
 {
     const int NG = D / a.G;
     if (a.chunk > CH1)
-        return false;
-    if (D == 128 && NG > 2)  // fp32 scale/bias staging: 32 KB per wavefront at NG = 4
         return false;
     if (((int64_t)a.chunk * NG) % 8 != 0 || (a.cap * NG) % 8 != 0)
         return false;
