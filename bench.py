@@ -23,6 +23,7 @@ oracle timed on the host as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -35,6 +36,33 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 B, HQ, HKV, D, G = 1, 64, 8, 128, 64
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sdpa_partial_llama_128k_traffic.txt")
+
+
+def measured_traffic(skv: int, chunk: int, kernel: str):
+    """HBM bytes per partial launch from the committed counter summary, or
+    None when this run is not the profiled configuration or the kernel
+    sources changed since the counters were taken (their hash differs)."""
+    if skv != 131072 or chunk != 512 or kernel not in ("auto", "mfma", "mfma-wave"):
+        return None
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        root = os.path.dirname(TRAFFIC_FILE)
+        h = hashlib.sha256()
+        for rel in kv["source_files"].split():
+            with open(os.path.join(root, "..", rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != kv["source_sha256"]:
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def layer_bytes(skv: int) -> int:
@@ -234,7 +262,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.skv, args.chunk, args.kernel),
             "bytes_per_launch": layer_bytes(args.skv),
             "avg_launch_us": round(main_res["partial_ms_avg"] * 1e3, 3),
             "p10_launch_us": round(main_res["partial_ms_p10"] * 1e3, 3),
