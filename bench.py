@@ -98,18 +98,25 @@ def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 123
     return pool
 
 
-def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None):
+def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, bracket=None):
+    """n decode steps. events[i]: (start, stop) recorded in the partial kernel's
+    own dispatch; bracket[i]: (start, stop) recorded on the stream around the
+    partial call (these also hold its dispatch and completion)."""
     alpha = 1.0 / math.sqrt(D)
     stream = torch.cuda.current_stream()
     for i in range(n):
         L = pool[i % len(pool)]
         kvq.quantize_kv_append(L["cache"], skv - 1, L["k_new"], L["v_new"], stream=stream)
         m, l, acc = L["ws"]
+        if bracket is not None:
+            bracket[i][0].record(stream)
         if events is not None:
-            events[i][0].record(stream)
-        kvq.sdpa_int4_partial(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, kernel=kernel, stream=stream)
-        if events is not None:
-            events[i][1].record(stream)
+            kvq.sdpa_int4_partial_timed(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, events[i][0], events[i][1],
+                                        kernel=kernel, stream=stream)
+        else:
+            kvq.sdpa_int4_partial(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, kernel=kernel, stream=stream)
+        if bracket is not None:
+            bracket[i][1].record(stream)
         kvq.sdpa_int4_reduce(m, l, acc, L["out"], stream=stream)
 
 
@@ -124,13 +131,20 @@ def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes):
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / steps
-    # second pass of the same steps with HIP events around every partial launch
+    # second pass of the same steps: HIP events recorded in every partial
+    # kernel's own dispatch (its execution time), and a third with events
+    # recorded on the stream around the call (adds dispatch and completion)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     run_steps(kvq, torch, pool, skv, chunk, kernel, steps, events=evs)
     torch.cuda.synchronize()
     kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    brk = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    run_steps(kvq, torch, pool, skv, chunk, kernel, steps, bracket=brk)
+    torch.cuda.synchronize()
+    brk_ms = [a.elapsed_time(b) for a, b in brk]
     res = dict(skv=skv, ms_per_step=ms_per_step, partial_ms_avg=sum(kern_ms) / len(kern_ms),
                partial_ms_p10=kern_ms[len(kern_ms) // 10], partial_ms_p90=kern_ms[(9 * len(kern_ms)) // 10],
+               partial_bracket_ms_avg=sum(brk_ms) / len(brk_ms),
                pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv) / 1e6)
     last = pool[-1]
     del pool
@@ -265,6 +279,8 @@ def main():
             "traffic": measured_traffic(args.skv, args.chunk, args.kernel),
             "bytes_per_launch": layer_bytes(args.skv),
             "avg_launch_us": round(main_res["partial_ms_avg"] * 1e3, 3),
+            "timing": "HIP events recorded in the kernel's own dispatch (hipExtLaunchKernel), averaged over the steps",
+            "avg_call_bracket_us": round(main_res["partial_bracket_ms_avg"] * 1e3, 3),
             "p10_launch_us": round(main_res["partial_ms_p10"] * 1e3, 3),
             "p90_launch_us": round(main_res["partial_ms_p90"] * 1e3, 3),
         },

@@ -141,6 +141,19 @@ int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, in
                           int kernel, void *stream);
 
 /*
+ * kvq_sdpa_int4_partial with its kernel timed: start_event and stop_event
+ * (hipEvent_t, created by the caller with timing enabled; either may be
+ * NULL) are recorded in the kernel's own dispatch, at the start and the end of
+ * its execution, so their elapsed time is the kernel's duration without the
+ * dispatch and completion latency an event recorded before and after the
+ * call would include. Same arguments, results and errors otherwise; the
+ * events are not touched when the call returns an error.
+ */
+int kvq_sdpa_int4_partial_timed(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
+                                float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
+                                int kernel, void *stream, void *start_event, void *stop_event);
+
+/*
  * Phase 2: combine the partials of kvq_sdpa_int4_partial (README split-K
  * paragraph): with M = max_c m_c,
  *   out[b][h][d] = sum_c e^{m_c - M} acc_c[d] / sum_c e^{m_c - M} l_c.

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     quantize_kv_append,
     sdpa_int4,
     sdpa_int4_partial,
+    sdpa_int4_partial_timed,
     sdpa_int4_reduce,
     status_str,
     version,

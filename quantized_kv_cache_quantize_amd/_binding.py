@@ -66,6 +66,8 @@ def lib():
     L.kvq_quantize_kv_append.argtypes = [cp, i64, vp, vp, C.c_int, i64, vp]
     L.kvq_sdpa_int4_partial.restype = C.c_int
     L.kvq_sdpa_int4_partial.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, C.c_int, vp]
+    L.kvq_sdpa_int4_partial_timed.restype = C.c_int
+    L.kvq_sdpa_int4_partial_timed.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, C.c_int, vp, vp, vp]
     L.kvq_sdpa_int4_reduce.restype = C.c_int
     L.kvq_sdpa_int4_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i64, vp, vp]
     L.kvq_sdpa_int4.restype = C.c_int
@@ -177,6 +179,27 @@ def sdpa_int4_partial(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_sca
            lib().kvq_sdpa_int4_partial(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), int(q.shape[1]),
                                        float(softmax_scale), int(chunk), _ptr(part_m), _ptr(part_l),
                                        _ptr(part_acc), int(kernel), _stream(stream)))
+
+
+def _event_handle(ev) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (created on first record)."""
+    if ev.cuda_event == 0:
+        ev.record()
+    return ev.cuda_event
+
+
+def sdpa_int4_partial_timed(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int,
+                            part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor, start, stop,
+                            kernel: int = KERNEL_AUTO, stream=None) -> None:
+    """kvq_sdpa_int4_partial_timed: as sdpa_int4_partial, with torch.cuda.Event
+    start/stop (enable_timing=True) recorded at the kernel's own start and end."""
+    assert q.is_contiguous()
+    cs = cache.c_struct()
+    _check("kvq_sdpa_int4_partial_timed",
+           lib().kvq_sdpa_int4_partial_timed(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), int(q.shape[1]),
+                                             float(softmax_scale), int(chunk), _ptr(part_m), _ptr(part_l),
+                                             _ptr(part_acc), int(kernel), _stream(stream), _event_handle(start),
+                                             _event_handle(stop)))
 
 
 def sdpa_int4_reduce(part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor, out: torch.Tensor,

@@ -127,9 +127,10 @@ int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_ne
     return launch_status(launch_quantize(a, dtype, (hipStream_t)stream));
 }
 
-int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
-                          float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
-                          int kernel, void *stream)
+namespace {
+
+int partial_impl(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
+                 int32_t chunk, float *part_m, float *part_l, float *part_acc, int kernel, const Launch &l)
 {
     int st = check_cache(cache);
     if (st)
@@ -183,9 +184,27 @@ int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, in
     if (kernel == KVQ_KERNEL_MFMA_PAIR && !mfma_pair_ok(a, cache->head_dim, q_dtype, cache->batch))
         return KVQ_E_UNSUPPORTED;
     const bool use_mfma = want_mfma || (kernel == KVQ_KERNEL_AUTO && mfma_ok);
-    hipError_t e = use_mfma ? launch_partial_mfma(a, cache->head_dim, q_dtype, cache->batch, kernel, (hipStream_t)stream)
-                            : launch_partial_valu(a, cache->head_dim, q_dtype, cache->batch, (hipStream_t)stream);
+    hipError_t e = use_mfma ? launch_partial_mfma(a, cache->head_dim, q_dtype, cache->batch, kernel, l)
+                            : launch_partial_valu(a, cache->head_dim, q_dtype, cache->batch, l);
     return launch_status(e);
+}
+
+}  // namespace
+
+int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
+                          float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
+                          int kernel, void *stream)
+{
+    const Launch l{(hipStream_t)stream, nullptr, nullptr};
+    return partial_impl(cache, skv, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l, part_acc, kernel, l);
+}
+
+int kvq_sdpa_int4_partial_timed(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
+                                float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
+                                int kernel, void *stream, void *start_event, void *stop_event)
+{
+    const Launch l{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return partial_impl(cache, skv, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l, part_acc, kernel, l);
 }
 
 int kvq_sdpa_int4_reduce(const float *part_m, const float *part_l, const float *part_acc, int32_t batch, int32_t Hq,

@@ -1,6 +1,7 @@
 // Internal declarations shared by the kvq HIP sources (not part of the ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,10 +63,18 @@ struct ReduceArgs {
     int32_t D;
 };
 
+// Where a partial-phase launch goes: the stream and, optionally, two events
+// recorded at the kernel's own dispatch start and end (hipExtLaunchKernel).
+struct Launch {
+    hipStream_t s;
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+
 hipError_t launch_quantize(const QuantizeArgs &a, int dtype, hipStream_t s);
-hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s);
+hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l);
 bool mfma_supports(int D, int G, int n_rep, int chunk);
-hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, hipStream_t s);
+hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l);
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch);
 bool mfma_pair_ok(const PartialArgs &a, int D, int q_dtype, int batch);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);

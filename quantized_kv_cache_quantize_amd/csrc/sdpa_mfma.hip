@@ -1214,16 +1214,16 @@ void sdpa_partial_mfma_pair_kernel(PartialArgs a)
 }
 
 template <int D, int NG, bool Q32>
-void launch_one_wave(const PartialArgs &a, dim3 grid, hipStream_t s)
+void launch_one_wave(const PartialArgs &a, dim3 grid, const Launch &l)
 {
     constexpr int PF = D == 128 ? 4 : 2;
-    hipLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF>), grid, dim3(64), 0, s, a);
+    hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF>), grid, dim3(64), 0, l.s, l.start, l.stop, 0, a);
 }
 
 template <int NG>
-void launch_pair(const PartialArgs &a, dim3 grid, hipStream_t s)
+void launch_pair(const PartialArgs &a, dim3 grid, const Launch &l)
 {
-    hipLaunchKernelGGL((sdpa_partial_mfma_pair_kernel<NG, 2>), grid, dim3(128), 0, s, a);
+    hipExtLaunchKernelGGL((sdpa_partial_mfma_pair_kernel<NG, 2>), grid, dim3(128), 0, l.s, l.start, l.stop, 0, a);
 }
 
 // The one-wavefront kernel needs chunks of at most 512 rows whose scale/bias
@@ -1247,7 +1247,7 @@ bool pair_fits(const PartialArgs &a, int D, int q_dtype, int batch)
 }
 
 template <int D, int NG>
-hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, hipStream_t s)
+hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, const Launch &l)
 {
     dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
     const int64_t items = (int64_t)a.num_chunks * a.Hkv * batch;
@@ -1259,16 +1259,16 @@ hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, 
         return hipErrorInvalidValue;
     if (pair) {
         if constexpr (D == 128)
-            launch_pair<NG>(a, grid, s);
+            launch_pair<NG>(a, grid, l);
     } else if (one) {
         if (q_dtype == KVQ_F32)
-            launch_one_wave<D, NG, true>(a, grid, s);
+            launch_one_wave<D, NG, true>(a, grid, l);
         else
-            launch_one_wave<D, NG, false>(a, grid, s);
+            launch_one_wave<D, NG, false>(a, grid, l);
     } else if (q_dtype == KVQ_F32) {
-        hipLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, true>), grid, dim3(NT), 0, s, a);
+        hipExtLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, true>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
     } else {
-        hipLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, false>), grid, dim3(NT), 0, s, a);
+        hipExtLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, false>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
     }
     return hipGetLastError();
 }
@@ -1286,16 +1286,16 @@ bool mfma_supports(int D, int G, int n_rep, int chunk)
     return NG <= 4 && n_rep >= 1 && n_rep * NG <= 16;
 }
 
-hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, hipStream_t s)
+hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l)
 {
     const int NG = D / a.G;
     if (D == 128) {
-        if (NG == 1) return launch_dg<128, 1>(a, q_dtype, batch, variant, s);
-        if (NG == 2) return launch_dg<128, 2>(a, q_dtype, batch, variant, s);
-        if (NG == 4) return launch_dg<128, 4>(a, q_dtype, batch, variant, s);
+        if (NG == 1) return launch_dg<128, 1>(a, q_dtype, batch, variant, l);
+        if (NG == 2) return launch_dg<128, 2>(a, q_dtype, batch, variant, l);
+        if (NG == 4) return launch_dg<128, 4>(a, q_dtype, batch, variant, l);
     } else if (D == 256) {
-        if (NG == 2) return launch_dg<256, 2>(a, q_dtype, batch, variant, s);
-        if (NG == 4) return launch_dg<256, 4>(a, q_dtype, batch, variant, s);
+        if (NG == 2) return launch_dg<256, 2>(a, q_dtype, batch, variant, l);
+        if (NG == 4) return launch_dg<256, 4>(a, q_dtype, batch, variant, l);
     }
     return hipErrorInvalidValue;
 }

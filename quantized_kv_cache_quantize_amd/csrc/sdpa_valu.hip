@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
 }
 
 template <int D, typename QT>
-hipError_t launch_d(const PartialArgs &a, int batch, hipStream_t s)
+hipError_t launch_d(const PartialArgs &a, int batch, const Launch &l)
 {
     int tile = 1;
     for (int t = 8; t >= 1; t >>= 1)
@@ -242,31 +242,31 @@ hipError_t launch_d(const PartialArgs &a, int batch, hipStream_t s)
     dim3 grid((unsigned)a.num_chunks, (unsigned)(a.Hkv * (a.n_rep / tile)), (unsigned)batch);
     switch (tile) {
     case 8:
-        hipLaunchKernelGGL((sdpa_partial_valu_kernel<D, 8, QT>), grid, dim3(NT), 0, s, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 8, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     case 4:
-        hipLaunchKernelGGL((sdpa_partial_valu_kernel<D, 4, QT>), grid, dim3(NT), 0, s, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 4, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     case 2:
-        hipLaunchKernelGGL((sdpa_partial_valu_kernel<D, 2, QT>), grid, dim3(NT), 0, s, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 2, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     default:
-        hipLaunchKernelGGL((sdpa_partial_valu_kernel<D, 1, QT>), grid, dim3(NT), 0, s, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 1, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     }
     return hipGetLastError();
 }
 
 template <typename QT>
-hipError_t launch_q(const PartialArgs &a, int D, int batch, hipStream_t s)
+hipError_t launch_q(const PartialArgs &a, int D, int batch, const Launch &l)
 {
     switch (D) {
     case 64:
-        return launch_d<64, QT>(a, batch, s);
+        return launch_d<64, QT>(a, batch, l);
     case 128:
-        return launch_d<128, QT>(a, batch, s);
+        return launch_d<128, QT>(a, batch, l);
     case 256:
-        return launch_d<256, QT>(a, batch, s);
+        return launch_d<256, QT>(a, batch, l);
     default:
         return hipErrorInvalidValue;
     }
@@ -274,9 +274,9 @@ hipError_t launch_q(const PartialArgs &a, int D, int batch, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, hipStream_t s)
+hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l)
 {
-    return q_dtype == KVQ_F16 ? launch_q<_Float16>(a, D, batch, s) : launch_q<float>(a, D, batch, s);
+    return q_dtype == KVQ_F16 ? launch_q<_Float16>(a, D, batch, l) : launch_q<float>(a, D, batch, l);
 }
 
 }  // namespace kvq

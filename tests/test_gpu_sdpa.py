@@ -203,3 +203,25 @@ def test_fused_entry_point():
     out = kvq.sdpa_int4(gc, 1024, to_dev(q), alpha)
     torch.cuda.synchronize()
     check_attention(out.cpu().numpy(), oracle.sdpa(oc, 1024, q, alpha), 5e-5, label="fused")
+
+
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT])
+def test_timed_partial_matches_untimed(kernel):
+    """kvq_sdpa_int4_partial_timed writes the same partials bit for bit and its
+    dispatch events give a positive duration."""
+    note("sdpa timed partial kernel=%d" % kernel)
+    q, k, v, alpha = kvq_synth.llama_layer(4096)
+    oc = _oracle_cache(k, v)
+    gc = gpu_cache_from_oracle(oc)
+    qd = to_dev(q)
+    B, Hq, D = q.shape
+    a = kvq.partials_buffers(B, Hq, D, 4096, 512, device="cuda")
+    b = kvq.partials_buffers(B, Hq, D, 4096, 512, device="cuda")
+    kvq.sdpa_int4_partial(gc, 4096, qd, alpha, 512, *a, kernel=kernel)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kvq.sdpa_int4_partial_timed(gc, 4096, qd, alpha, 512, *b, e0, e1, kernel=kernel)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 100.0, ms
