@@ -98,53 +98,50 @@ def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 123
     return pool
 
 
-def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, bracket=None):
-    """n decode steps. events[i]: (start, stop) recorded in the partial kernel's
-    own dispatch; bracket[i]: (start, stop) recorded on the stream around the
-    partial call (these also hold its dispatch and completion)."""
+def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"):
+    """n decode steps, each on a different layer of the pool: the current
+    token's K/V row is quantised into row skv-1 and attention runs over skv
+    rows. step "fused": kvq_decode_step (append inside the attention kernel,
+    then the reduce); "unfused": append, partial and reduce as three calls.
+    events[i]: (start, stop) recorded in the attention kernel's own dispatch."""
     alpha = 1.0 / math.sqrt(D)
     stream = torch.cuda.current_stream()
     for i in range(n):
         L = pool[i % len(pool)]
+        ev = events[i] if events is not None else None
+        if step == "fused":
+            kvq.decode_step(L["cache"], skv - 1, L["k_new"], L["v_new"], L["q"], alpha, chunk, out=L["out"],
+                            workspace=L["ws"], kernel=kernel, stream=stream, events=ev)
+            continue
         kvq.quantize_kv_append(L["cache"], skv - 1, L["k_new"], L["v_new"], stream=stream)
         m, l, acc = L["ws"]
-        if bracket is not None:
-            bracket[i][0].record(stream)
-        if events is not None:
-            kvq.sdpa_int4_partial_timed(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, events[i][0], events[i][1],
+        if ev is not None:
+            kvq.sdpa_int4_partial_timed(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, ev[0], ev[1],
                                         kernel=kernel, stream=stream)
         else:
             kvq.sdpa_int4_partial(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, kernel=kernel, stream=stream)
-        if bracket is not None:
-            bracket[i][1].record(stream)
         kvq.sdpa_int4_reduce(m, l, acc, L["out"], stream=stream)
 
 
-def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes):
+def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused"):
     pool = make_pool(kvq, torch, skv, pool_bytes, chunk)
-    run_steps(kvq, torch, pool, skv, chunk, kernel, warmup)
+    run_steps(kvq, torch, pool, skv, chunk, kernel, warmup, step=step)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    run_steps(kvq, torch, pool, skv, chunk, kernel, steps)
+    run_steps(kvq, torch, pool, skv, chunk, kernel, steps, step=step)
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / steps
-    # second pass of the same steps: HIP events recorded in every partial
-    # kernel's own dispatch (its execution time), and a third with events
-    # recorded on the stream around the call (adds dispatch and completion)
+    # second pass of the same steps with HIP events recorded in every
+    # attention kernel's own dispatch: that kernel's execution time
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    run_steps(kvq, torch, pool, skv, chunk, kernel, steps, events=evs)
+    run_steps(kvq, torch, pool, skv, chunk, kernel, steps, events=evs, step=step)
     torch.cuda.synchronize()
     kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    brk = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    run_steps(kvq, torch, pool, skv, chunk, kernel, steps, bracket=brk)
-    torch.cuda.synchronize()
-    brk_ms = [a.elapsed_time(b) for a, b in brk]
     res = dict(skv=skv, ms_per_step=ms_per_step, partial_ms_avg=sum(kern_ms) / len(kern_ms),
                partial_ms_p10=kern_ms[len(kern_ms) // 10], partial_ms_p90=kern_ms[(9 * len(kern_ms)) // 10],
-               partial_bracket_ms_avg=sum(brk_ms) / len(brk_ms),
                pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv) / 1e6)
     last = pool[-1]
     del pool
@@ -192,6 +189,9 @@ def main():
     ap.add_argument("--sweep", default="1024,16384,65536",
                     help="extra Skv values timed with fewer steps (empty to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step", choices=["fused", "unfused"], default="fused",
+                    help="fused: kvq_decode_step (append inside the attention kernel, then the reduce); "
+                         "unfused: append, partial and reduce as three calls")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MB (a known-size reference "
                          "for hardware byte counters)")
@@ -216,10 +216,12 @@ def main():
               "mfma-pair": kvq.KERNEL_MFMA_PAIR}[args.kernel]
     pool_bytes = args.pool_mb * 1000 * 1000
 
-    main_res, last = time_config(kvq, torch, args.skv, args.chunk, kernel, args.steps, args.warmup, pool_bytes)
+    main_res, last = time_config(kvq, torch, args.skv, args.chunk, kernel, args.steps, args.warmup, pool_bytes,
+                                 step=args.step)
     sweep = []
     for s in [int(x) for x in args.sweep.split(",") if x.strip()]:
-        r, _ = time_config(kvq, torch, s, args.chunk, kernel, max(20, args.steps // 2), args.warmup, pool_bytes)
+        r, _ = time_config(kvq, torch, s, args.chunk, kernel, max(20, args.steps // 2), args.warmup, pool_bytes,
+                           step=args.step)
         r["us_per_layer"] = r["ms_per_step"] * 1e3
         r["gbs"] = (layer_bytes(s) + append_bytes()) / (r["ms_per_step"] * 1e-3) / 1e9
         r["partial_gbs"] = layer_bytes(s) / (r["partial_ms_avg"] * 1e-3) / 1e9
@@ -259,7 +261,9 @@ def main():
         "data": "synthetic (seeded fp16 N(0,1) K/V/Q drawn on the GPU, quantised by the library)",
         "config": {
             "workload": "Llama-3.1-70B-shaped decode layer: B1 Hq64 Hkv8 D128, int4 G64 fp16 scale+bias, "
-                        "alpha 1/sqrt(128), append 1 row + split-K partial + reduce",
+                        "alpha 1/sqrt(128); one decode step = quantise the token's K/V row into the cache + "
+                        "split-K attention over 512-row chunks + reduce",
+            "step": args.step,
             "skv": args.skv,
             "chunk": args.chunk,
             "kernel": args.kernel,
@@ -271,7 +275,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "sdpa_partial",
+            "kernel": "sdpa_partial (attention kernel of the step; in the fused step it also appends the row)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -280,7 +284,6 @@ def main():
             "bytes_per_launch": layer_bytes(args.skv),
             "avg_launch_us": round(main_res["partial_ms_avg"] * 1e3, 3),
             "timing": "HIP events recorded in the kernel's own dispatch (hipExtLaunchKernel), averaged over the steps",
-            "avg_call_bracket_us": round(main_res["partial_bracket_ms_avg"] * 1e3, 3),
             "p10_launch_us": round(main_res["partial_ms_p10"] * 1e3, 3),
             "p90_launch_us": round(main_res["partial_ms_p90"] * 1e3, 3),
         },

@@ -172,6 +172,36 @@ int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtyp
                   float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc, float *out,
                   int kernel, void *stream);
 
+/*
+ * One decode step (the README's decode-step listing: quantise the current
+ * token's K and V into the cache, then the fused int4 attention with GQA):
+ * writes k_new / v_new ([B][Hkv][D], kv_dtype, one row per (batch, KV head))
+ * into cache row `len` with the rule of kvq_quantize_kv_append, then
+ * computes out over the len + 1 rows 0..len exactly as kvq_sdpa_int4 would.
+ * When the one-wavefront matrix-core kernel is the one that runs (kernel
+ * MFMA_WAVE, or AUTO / MFMA with at least 1024 (chunk, KV head, batch) items),
+ * the append runs inside the attention kernel, in the wavefront that owns the
+ * last chunk, so the step is two launches (attention, reduce) instead of
+ * three; otherwise it is the three calls in order. Results are the same either way (cache bit for bit, out as
+ * kvq_sdpa_int4 with that kernel). All arguments are validated before anything
+ * is enqueued: len + 1 <= capacity (else KVQ_E_CAPACITY), k_new, v_new and out
+ * 16-byte aligned, the partials workspace sized for C = ceil((len+1)/chunk).
+ */
+int kvq_decode_step(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                    const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,
+                    float *part_l, float *part_acc, float *out, int kernel, void *stream);
+
+/*
+ * kvq_decode_step with its attention kernel timed: start_event / stop_event
+ * (hipEvent_t with timing, either may be NULL) are recorded in that kernel's
+ * own dispatch, as in kvq_sdpa_int4_partial_timed (in the fused step this is
+ * the kernel that also appends the row). Otherwise identical.
+ */
+int kvq_decode_step_timed(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                          const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,
+                          float *part_l, float *part_acc, float *out, int kernel, void *stream, void *start_event,
+                          void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

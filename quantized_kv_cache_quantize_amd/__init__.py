@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     Int4KVCache,
     KvqError,
     cache_bytes,
+    decode_step,
     lib,
     lib_path,
     num_chunks,

@@ -70,6 +70,11 @@ def lib():
     L.kvq_sdpa_int4_partial_timed.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, C.c_int, vp, vp, vp]
     L.kvq_sdpa_int4_reduce.restype = C.c_int
     L.kvq_sdpa_int4_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    L.kvq_decode_step.restype = C.c_int
+    L.kvq_decode_step.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int, vp]
+    L.kvq_decode_step_timed.restype = C.c_int
+    L.kvq_decode_step_timed.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int,
+                                        vp, vp, vp]
     L.kvq_sdpa_int4.restype = C.c_int
     L.kvq_sdpa_int4.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int, vp]
     _lib = L
@@ -225,4 +230,29 @@ def sdpa_int4(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: floa
     _check("kvq_sdpa_int4",
            lib().kvq_sdpa_int4(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), hq, float(softmax_scale),
                                int(chunk), _ptr(m), _ptr(l), _ptr(acc), _ptr(out), int(kernel), _stream(stream)))
+    return out
+
+
+def decode_step(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                softmax_scale: float, chunk: int = 512, out: torch.Tensor | None = None, workspace=None,
+                kernel: int = KERNEL_AUTO, stream=None, events=None):
+    """kvq_decode_step: append k_new, v_new ([B][Hkv][D] or [B][Hkv][1][D]) at
+    row `length`, then attention over length + 1 rows; returns out [B][Hq][D].
+    events: optional (start, stop) torch.cuda.Event recorded in the attention
+    kernel's own dispatch (kvq_decode_step_timed)."""
+    assert q.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
+    b, hq, d = q.shape
+    if workspace is None:
+        workspace = partials_buffers(b, hq, d, length + 1, chunk, device=q.device)
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+    m, l, acc = workspace
+    cs = cache.c_struct()
+    args = (C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q), _dtype_code(q), hq,
+            float(softmax_scale), int(chunk), _ptr(m), _ptr(l), _ptr(acc), _ptr(out), int(kernel), _stream(stream))
+    if events is None:
+        _check("kvq_decode_step", lib().kvq_decode_step(*args))
+    else:
+        _check("kvq_decode_step_timed",
+               lib().kvq_decode_step_timed(*args, _event_handle(events[0]), _event_handle(events[1])))
     return out

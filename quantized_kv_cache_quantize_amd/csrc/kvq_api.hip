@@ -129,8 +129,15 @@ int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_ne
 
 namespace {
 
-int partial_impl(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
-                 int32_t chunk, float *part_m, float *part_l, float *part_acc, int kernel, const Launch &l)
+// A validated partial-phase request: its kernel arguments and whether it runs
+// on the matrix cores.
+struct PartialPlan {
+    PartialArgs a;
+    bool use_mfma;
+};
+
+int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
+                    int32_t chunk, float *part_m, float *part_l, float *part_acc, int kernel, PartialPlan &p)
 {
     int st = check_cache(cache);
     if (st)
@@ -159,7 +166,7 @@ int partial_impl(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype
     if (want_mfma && !mfma_ok)
         return KVQ_E_UNSUPPORTED;
 
-    PartialArgs a;
+    PartialArgs &a = p.a;
     a.k_q = cache->k_q;
     a.v_q = cache->v_q;
     a.k_scale = cache->k_scale;
@@ -179,14 +186,32 @@ int partial_impl(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype
     a.n_rep = n_rep;
     a.G = cache->group;
     a.score_scale = softmax_scale * kLog2e;
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.append_row = -1;
+    a.append_dtype = KVQ_F16;
     if (kernel == KVQ_KERNEL_MFMA_WAVE && !mfma_one_wave_ok(a, cache->head_dim, cache->batch))
         return KVQ_E_UNSUPPORTED;
     if (kernel == KVQ_KERNEL_MFMA_PAIR && !mfma_pair_ok(a, cache->head_dim, q_dtype, cache->batch))
         return KVQ_E_UNSUPPORTED;
-    const bool use_mfma = want_mfma || (kernel == KVQ_KERNEL_AUTO && mfma_ok);
-    hipError_t e = use_mfma ? launch_partial_mfma(a, cache->head_dim, q_dtype, cache->batch, kernel, l)
-                            : launch_partial_valu(a, cache->head_dim, q_dtype, cache->batch, l);
+    p.use_mfma = want_mfma || (kernel == KVQ_KERNEL_AUTO && mfma_ok);
+    return KVQ_OK;
+}
+
+int launch_plan(const PartialPlan &p, const kvq_cache *cache, int q_dtype, int kernel, const Launch &l)
+{
+    hipError_t e = p.use_mfma ? launch_partial_mfma(p.a, cache->head_dim, q_dtype, cache->batch, kernel, l)
+                              : launch_partial_valu(p.a, cache->head_dim, q_dtype, cache->batch, l);
     return launch_status(e);
+}
+
+int partial_impl(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
+                 int32_t chunk, float *part_m, float *part_l, float *part_acc, int kernel, const Launch &l)
+{
+    PartialPlan p;
+    const int st = prepare_partial(cache, skv, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l, part_acc,
+                                   kernel, p);
+    return st ? st : launch_plan(p, cache, q_dtype, kernel, l);
 }
 
 }  // namespace
@@ -242,6 +267,79 @@ int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtyp
         return st;
     return kvq_sdpa_int4_reduce(part_m, part_l, part_acc, cache->batch, Hq, cache->head_dim,
                                 kvq_num_chunks(skv, chunk), out, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                     const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,
+                     float *part_l, float *part_acc, float *out, int kernel, const Launch &l)
+{
+    void *stream = (void *)l.s;
+    int st = check_cache(cache);
+    if (st)
+        return st;
+    if (kv_dtype != KVQ_F16 && kv_dtype != KVQ_F32)
+        return KVQ_E_DTYPE;
+    if (len < 0)
+        return KVQ_E_SHAPE;
+    if (len >= cache->capacity)
+        return KVQ_E_CAPACITY;
+    if (!k_new || !v_new || !out)
+        return KVQ_E_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+        return KVQ_E_ALIGN;
+    PartialPlan p;
+    st = prepare_partial(cache, len + 1, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l, part_acc, kernel, p);
+    if (st)
+        return st;
+    // fused when the one-wavefront kernel is the one that runs: forced, or
+    // AUTO / MFMA at one (chunk, KV head) item or more per SIMD (below that
+    // the four-wavefront kernel plus a separate append is faster)
+    const int64_t items = p.a.num_chunks * cache->kv_heads * cache->batch;
+    const bool fused = p.use_mfma && mfma_one_wave_ok(p.a, cache->head_dim, cache->batch) &&
+                       (kernel == KVQ_KERNEL_MFMA_WAVE ||
+                        ((kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) && items >= kOneWaveItems));
+    if (fused) {
+        p.a.k_new = k_new;
+        p.a.v_new = v_new;
+        p.a.append_row = len;
+        p.a.append_dtype = kv_dtype;
+        st = launch_status(launch_decode_fused(p.a, cache->head_dim, q_dtype, cache->batch, l));
+    } else {
+        st = kvq_quantize_kv_append(cache, len, k_new, v_new, kv_dtype, 1, stream);
+        if (!st)
+            st = launch_plan(p, cache, q_dtype, kernel, l);
+    }
+    if (st)
+        return st;
+    return kvq_sdpa_int4_reduce(part_m, part_l, part_acc, cache->batch, Hq, cache->head_dim, p.a.num_chunks, out,
+                                stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_decode_step(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                    const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,
+                    float *part_l, float *part_acc, float *out, int kernel, void *stream)
+{
+    const Launch l{(hipStream_t)stream, nullptr, nullptr};
+    return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l,
+                            part_acc, out, kernel, l);
+}
+
+int kvq_decode_step_timed(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                          const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,
+                          float *part_l, float *part_acc, float *out, int kernel, void *stream, void *start_event,
+                          void *stop_event)
+{
+    const Launch l{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l,
+                            part_acc, out, kernel, l);
 }
 
 }  // extern "C"

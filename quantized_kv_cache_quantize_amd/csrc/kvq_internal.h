@@ -14,6 +14,10 @@ namespace kvq {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// AUTO picks the one-wavefront matrix-core kernel from this many (chunk, KV
+// head, batch) items on: one wavefront per SIMD of the 256-CU chip.
+constexpr int64_t kOneWaveItems = 1024;
+
 struct QuantizeArgs {
     const void *k_new;
     const void *v_new;
@@ -51,6 +55,13 @@ struct PartialArgs {
     int32_t n_rep;
     int32_t G;
     float score_scale;  // softmax_scale * log2(e)
+    // Fused decode step (one-wavefront kernel only): when append_row >= 0,
+    // the wavefront whose chunk holds that row first quantises k_new / v_new
+    // ([B][Hkv][D], append_dtype) into it. -1: no append.
+    const void *k_new;
+    const void *v_new;
+    int64_t append_row;
+    int32_t append_dtype;
 };
 
 struct ReduceArgs {
@@ -77,6 +88,8 @@ bool mfma_supports(int D, int G, int n_rep, int chunk);
 hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l);
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch);
 bool mfma_pair_ok(const PartialArgs &a, int D, int q_dtype, int batch);
+// the fused decode step: append (a.append_row) + partial with the one-wavefront kernel
+hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
 }  // namespace kvq

@@ -43,6 +43,7 @@
 // clamping, and the eight value rows of a lane share one address register
 // (their distances are instruction offsets).
 #include "kvq_internal.h"
+#include "quant_rule.h"
 
 namespace kvq {
 namespace {
@@ -582,6 +583,49 @@ __device__ __forceinline__ half8 k_operand64(uint32_t w, uint32_t m64)
     return cat8(as_h2(r0), as_h2(r1), as_h2(r2), as_h2(r3));
 }
 
+// Fused decode step: quantise this (batch, KV head)'s new K and V rows into
+// cache row a.append_row (the rule of quant_rule.h; lanes 0..D/8-1 take the
+// K words, the next D/8 lanes the V words, idle lanes only join the swaps of
+// their group), then wait until the stores are done, so that the wavefront's
+// later loads of that row, all issued after this, see the new values.
+template <int D, int NG>
+__device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvrow0)
+{
+    constexpr int W = D / 8;
+    constexpr int LPG = W / NG;  // lanes per scale group
+    const int lane = threadIdx.x;
+    const bool active = lane < 2 * W;
+    const int which = lane / W;  // 0: K, 1: V
+    const int w = lane % W;
+    const int64_t src = ((int64_t)b * a.Hkv + kvh) * D + 8 * w;
+    float x[8];
+    if (!active) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = 0.0f;
+    } else if (a.append_dtype == KVQ_F32) {
+        quant::load8<float>(reinterpret_cast<const float *>(which ? a.v_new : a.k_new) + src, x);
+    } else {
+        quant::load8<_Float16>(reinterpret_cast<const _Float16 *>(which ? a.v_new : a.k_new) + src, x);
+    }
+    uint16_t sb, bb;
+    const uint32_t word = quant::quantize_word<LPG>(x, sb, bb);
+    if (active) {
+        const int64_t row = kvrow0 + a.append_row;
+        uint32_t *dq = const_cast<uint32_t *>(which ? a.v_q : a.k_q);
+        dq[row * W + w] = word;
+        if (w % LPG == 0) {
+            uint16_t *ds = const_cast<uint16_t *>(which ? a.v_scale : a.k_scale);
+            uint16_t *db = const_cast<uint16_t *>(which ? a.v_bias : a.k_bias);
+            ds[row * NG + w / LPG] = sb;
+            db[row * NG + w / LPG] = bb;
+        }
+    }
+    // every store of this wavefront has completed before any later load issues
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
+
 template <int D, int NG, bool Q32, int PF>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
 void sdpa_partial_mfma1_kernel(PartialArgs a)
@@ -613,6 +657,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     const int last = t1 - 1;
     const int ntile = (t1 - t0 + TILE - 1) / TILE;
     const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
+    if (a.append_row >= t0 && a.append_row < t1)  // uniform: the fused decode step's new row is in this chunk
+        append_new_row<D, NG>(a, b, kvh, kvrow0);
     const uint32_t rows_ok = (uint32_t)a.skv;
     const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
     const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
@@ -1254,7 +1300,7 @@ hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, 
     bool pair = variant == KVQ_KERNEL_MFMA_PAIR;
     bool one = variant == KVQ_KERNEL_MFMA_WAVE;
     if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO)
-        one = one_wave_fits(a, D, batch) && items >= 1024;  // a wavefront per SIMD
+        one = one_wave_fits(a, D, batch) && items >= kOneWaveItems;
     if ((one && !one_wave_fits(a, D, batch)) || (pair && !pair_fits(a, D, q_dtype, batch)))
         return hipErrorInvalidValue;
     if (pair) {
@@ -1303,5 +1349,12 @@ hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int bat
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch) { return one_wave_fits(a, D, batch); }
 
 bool mfma_pair_ok(const PartialArgs &a, int D, int q_dtype, int batch) { return pair_fits(a, D, q_dtype, batch); }
+
+hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l)
+{
+    if (!one_wave_fits(a, D, batch) || a.append_row < 0)
+        return hipErrorInvalidValue;
+    return launch_partial_mfma(a, D, q_dtype, batch, KVQ_KERNEL_MFMA_WAVE, l);
+}
 
 }  // namespace kvq

@@ -5,84 +5,109 @@
 //
 // With M = max_c m_c:  out[d] = sum_c e^{m_c-M} acc_c[d] / sum_c e^{m_c-M} l_c.
 //
-// Grid: (batch x query head, D / 32). A workgroup owns 32 output dimensions
-// of one head; its 256 threads are 8 chunk lanes x 32 dimensions, so every
-// chunk's 128-byte slice of the accumulator is one coalesced read and each
-// thread keeps 8 independent loads in flight. The chunk lanes meet in LDS.
+// Grid: (batch x query head, D / 32). A workgroup owns 32 output dimensions of
+// one head; its 256 threads are 32 chunk lanes x 8 groups of 4 dimensions.
+// A thread takes every 32nd chunk, reading its (m, l) and a 16-byte slice of
+// its accumulator; all of a thread's loads are issued before the first use
+// (one memory round trip up to 256 chunks) and combined with a running
+// maximum; the 32 chunk lanes then meet in a butterfly and one LDS step.
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 constexpr int RT = 256;
-constexpr int DS = 32;         // dimensions per workgroup
-constexpr int CL = RT / DS;    // chunk lanes
-constexpr int UNROLL = 8;
+constexpr int DS = 32;          // dimensions per workgroup
+constexpr int DQ = DS / 4;      // float4 groups per workgroup
+constexpr int CL = RT / DQ;     // chunk lanes (32)
+constexpr int UNROLL = 8;       // chunks per thread per round
 
 __global__ __launch_bounds__(RT) void sdpa_reduce_kernel(ReduceArgs a)
 {
     const int64_t head = blockIdx.x;
     const int d0 = blockIdx.y * DS;
     const int tid = threadIdx.x;
-    const int cl = tid / DS;
-    const int d = tid % DS;
+    const int cl = tid / DQ;
+    const int dq = tid % DQ;
     const int D = a.D;
     const int64_t C = a.C;
     const float *m = a.part_m + head * C;
     const float *l = a.part_l + head * C;
-    const float *acc = a.part_acc + head * C * D + d0 + d;
+    const float *acc = a.part_acc + head * C * D + d0 + 4 * dq;
 
-    __shared__ float red[RT / 64];
-    __shared__ float num_s[CL][DS];
-    __shared__ float den_s[CL][DS];
-
-    // M = max over chunks
-    float mx = -INFINITY;
-    for (int64_t c = tid; c < C; c += RT)
-        mx = fmaxf(mx, m[c]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((tid & 63) == 0)
-        red[tid >> 6] = mx;
-    __syncthreads();
-    float M = red[0];
-#pragma unroll
-    for (int i = 1; i < RT / 64; ++i)
-        M = fmaxf(M, red[i]);
-
-    float num = 0.0f, den = 0.0f;
-    int64_t c = cl;
-    for (; c + (UNROLL - 1) * CL < C; c += UNROLL * CL) {
-        float mv[UNROLL], lv[UNROLL], av[UNROLL];
+    // running state of this thread's chunks (natural-log maxima)
+    float M = -INFINITY, den = 0.0f;
+    float4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t c0 = cl; c0 < C; c0 += UNROLL * CL) {
+        float mv[UNROLL], lv[UNROLL];
+        float4 av[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            mv[u] = m[c + u * CL];
-            lv[u] = l[c + u * CL];
-            av[u] = acc[(c + u * CL) * D];
+            const int64_t c = c0 + u * CL;
+            const bool in = c < C;
+            mv[u] = in ? m[c] : -INFINITY;
+            lv[u] = in ? l[c] : 0.0f;
+            av[u] = in ? *reinterpret_cast<const float4 *>(acc + c * D) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
+        float Mn = M;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const float f = exp2f((mv[u] - M) * kLog2e);
-            den = fmaf(f, lv[u], den);
-            num = fmaf(f, av[u], num);
+        for (int u = 0; u < UNROLL; ++u)
+            Mn = fmaxf(Mn, mv[u]);
+        if (Mn != -INFINITY) {
+            const float r = exp2f((M - Mn) * kLog2e);  // 0 while M is -inf
+            den *= r;
+            num.x *= r; num.y *= r; num.z *= r; num.w *= r;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const float f = exp2f((mv[u] - Mn) * kLog2e);
+                den = fmaf(f, lv[u], den);
+                num.x = fmaf(f, av[u].x, num.x);
+                num.y = fmaf(f, av[u].y, num.y);
+                num.z = fmaf(f, av[u].z, num.z);
+                num.w = fmaf(f, av[u].w, num.w);
+            }
+            M = Mn;
         }
     }
-    for (; c < C; c += CL) {
-        const float f = exp2f((m[c] - M) * kLog2e);
-        den = fmaf(f, l[c], den);
-        num = fmaf(f, acc[c * D], num);
+
+    // combine the chunk lanes: a butterfly over the 8 lanes of a wavefront
+    // that share dq (lane offsets 8, 16, 32), then the 4 wavefronts in LDS
+    auto merge = [](float &Ma, float &da, float4 &na, float Mb, float db, float4 nb) {
+        const float Mn = fmaxf(Ma, Mb);
+        if (Mn == -INFINITY)
+            return;  // neither side has chunks
+        const float fa = exp2f((Ma - Mn) * kLog2e), fb = exp2f((Mb - Mn) * kLog2e);
+        da = fmaf(da, fa, db * fb);
+        na.x = fmaf(na.x, fa, nb.x * fb);
+        na.y = fmaf(na.y, fa, nb.y * fb);
+        na.z = fmaf(na.z, fa, nb.z * fb);
+        na.w = fmaf(na.w, fa, nb.w * fb);
+        Ma = Mn;
+    };
+#pragma unroll
+    for (int off = DQ; off < 64; off <<= 1) {
+        const float Mb = __shfl_xor(M, off), db = __shfl_xor(den, off);
+        const float4 nb = make_float4(__shfl_xor(num.x, off), __shfl_xor(num.y, off), __shfl_xor(num.z, off),
+                                      __shfl_xor(num.w, off));
+        merge(M, den, num, Mb, db, nb);
     }
-    num_s[cl][d] = num;
-    den_s[cl][d] = den;
+    constexpr int NW = RT / 64;
+    __shared__ float m_s[NW][DQ];
+    __shared__ float den_s[NW][DQ];
+    __shared__ float4 num_s[NW][DQ];
+    const int w = tid >> 6;
+    if ((tid & 63) < DQ) {
+        m_s[w][dq] = M;
+        den_s[w][dq] = den;
+        num_s[w][dq] = num;
+    }
     __syncthreads();
-    if (cl == 0) {
+    if (tid < DQ) {
 #pragma unroll
-        for (int g = 1; g < CL; ++g) {
-            num += num_s[g][d];
-            den += den_s[g][d];
-        }
-        a.out[head * D + d0 + d] = num / den;
+        for (int g = 1; g < NW; ++g)
+            merge(M, den, num, m_s[g][dq], den_s[g][dq], num_s[g][dq]);
+        *reinterpret_cast<float4 *>(a.out + head * D + d0 + 4 * dq) =
+            make_float4(num.x / den, num.y / den, num.z / den, num.w / den);
     }
 }
 

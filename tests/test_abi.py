@@ -149,3 +149,26 @@ def test_fused_validation(L):
     c = _cache()
     assert L.kvq_sdpa_int4(C.byref(c), 100, P, 0, 64, 0.1, 512, P, P, P, None, 0, None) == E_NULL
     assert L.kvq_sdpa_int4(C.byref(c), 0, P, 0, 64, 0.1, 512, P, P, P, P, 0, None) == E_SHAPE
+
+
+def _step(L, cache, length=100, k=P, v=P, kvd=0, q=P, qd=0, hq=64, scale=0.1, chunk=512, m=P, l=P, acc=P, out=P,
+          kernel=0):
+    return L.kvq_decode_step(C.byref(cache) if cache is not None else None, length, k, v, kvd, q, qd, hq, scale,
+                             chunk, m, l, acc, out, kernel, None)
+
+
+def test_decode_step_validation(L):
+    c = _cache()
+    assert _step(L, None) == E_NULL
+    for kw in (dict(k=None), dict(v=None), dict(out=None), dict(q=None), dict(m=None), dict(acc=None)):
+        assert _step(L, c, **kw) == E_NULL, kw
+    assert _step(L, c, kvd=7) == E_DTYPE
+    assert _step(L, c, qd=7) == E_DTYPE
+    assert _step(L, c, length=-1) == E_SHAPE
+    assert _step(L, c, length=1024) == E_CAP  # row 1024 does not exist (capacity 1024)
+    assert _step(L, c, k=P + 8) == E_ALIGN
+    assert _step(L, c, out=P + 4) == E_ALIGN
+    assert _step(L, c, hq=12) == E_SHAPE  # not a multiple of the KV heads
+    assert _step(L, c, chunk=0) == E_SHAPE
+    assert _step(L, c, kernel=9) == E_SHAPE
+    assert _step(L, c, kernel=4, chunk=1024) == E_UNSUP  # one-wavefront kernel: chunk <= 512

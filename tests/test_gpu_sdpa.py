@@ -14,10 +14,13 @@ pytestmark = pytest.mark.gpu
 
 # Per-head relative L2 gates. The vector-ALU kernel works in fp32 throughout.
 # The matrix core sums the 32 products of one instruction after aligning them
-# to the largest and truncating the rest (measured: 1 + 0.75 ulp -> 1); with a
-# dominant row in a tile this leaves ~1e-5 relative error, so its gate is 5e-5.
-REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: 5e-5, kvq.KERNEL_MFMA: 5e-5, kvq.KERNEL_MFMA_SPLIT: 5e-5,
-          kvq.KERNEL_MFMA_WAVE: 5e-5, kvq.KERNEL_MFMA_PAIR: 5e-5}
+# to the largest and truncating the rest (measured: 1 + 0.75 ulp -> 1); over a
+# chunk's value accumulation this leaves 1e-5 to 6e-5 relative error, so the
+# matrix-core gate is the 1e-4 diagnostic gate (a dropped chunk at 128K is
+# about 4e-3).
+MFMA_REL_L2 = 1e-4
+REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: MFMA_REL_L2, kvq.KERNEL_MFMA: MFMA_REL_L2,
+          kvq.KERNEL_MFMA_SPLIT: MFMA_REL_L2, kvq.KERNEL_MFMA_WAVE: MFMA_REL_L2, kvq.KERNEL_MFMA_PAIR: MFMA_REL_L2}
 # With softmax scale 1 and normalised Q/K the scores reach O(100); their fp32
 # rounding (~sqrt(D) * 2^-24 * sum|q k|) passes undamped into the weights, so
 # the per-head L2 gate there is set one decade wider.
@@ -202,7 +205,7 @@ def test_fused_entry_point():
     gc = gpu_cache_from_oracle(oc)
     out = kvq.sdpa_int4(gc, 1024, to_dev(q), alpha)
     torch.cuda.synchronize()
-    check_attention(out.cpu().numpy(), oracle.sdpa(oc, 1024, q, alpha), 5e-5, label="fused")
+    check_attention(out.cpu().numpy(), oracle.sdpa(oc, 1024, q, alpha), MFMA_REL_L2, label="fused")
 
 
 @pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT])
