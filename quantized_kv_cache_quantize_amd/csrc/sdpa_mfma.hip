@@ -72,14 +72,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferFlags);
 }
 
-// (x & mask) | magic in one instruction; gfx9 VOP3 encodings take no 32-bit
-// literal, so the mask comes from a scalar register and the magic from a
-// vector register.
+// (x & mask) | magic, meant for one v_and_or_b32. A gfx9 VOP3 encoding takes
+// no 32-bit literal, so with constant operands the compiler would split it
+// into an AND and an OR that each carry a literal; the Unpacker therefore
+// holds mask and magic as opaque register values (mask in a scalar register,
+// magic in a vector register). Plain code, not inline asm, so that the
+// compiler's hazard tracking sees every write next to the matrix instructions.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
 {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
-    return r;
+    return (x & mask) | magic;
+}
+
+// x as a value the compiler cannot see through, in a scalar or a vector
+// register (an empty asm statement; no instruction is emitted)
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 // Four half2 registers -> one MFMA operand.
@@ -104,16 +118,21 @@ __device__ __forceinline__ half8 cat8(half2v a, half2v b, half2v c, half2v d)
 // signs and half the magnitude, and the 8 * scale they drop moves into the
 // bias term: code * s + b = (code - 8) * s + (b + 8 s).
 struct Unpacker {
-    uint32_t m1024, m64;  // magic exponents, kept in vector registers
+    uint32_t m1024, m64;  // magic exponents 0x6400 / 0x5400 (vector registers)
+    uint32_t lo4, hi4;    // nibble masks 0x000F000F / 0x00F000F0 (scalar registers)
+    __device__ static Unpacker make()
+    {
+        return Unpacker{opaque_v(0x64006400u), opaque_v(0x54005400u), opaque_s(0x000F000Fu), opaque_s(0x00F000F0u)};
+    }
     __device__ __forceinline__ void operator()(uint32_t x, half2v (&out)[4]) const
     {
         const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
         const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
         const uint32_t y = x >> 8;
-        out[0] = as_h2(and_or(x, 0x000F000Fu, m1024)) - k1032;
-        out[1] = as_h2(and_or(x, 0x00F000F0u, m64)) - k72;
-        out[2] = as_h2(and_or(y, 0x000F000Fu, m1024)) - k1032;
-        out[3] = as_h2(and_or(y, 0x00F000F0u, m64)) - k72;
+        out[0] = as_h2(and_or(x, lo4, m1024)) - k1032;
+        out[1] = as_h2(and_or(x, hi4, m64)) - k72;
+        out[2] = as_h2(and_or(y, lo4, m1024)) - k1032;
+        out[3] = as_h2(and_or(y, hi4, m64)) - k72;
     }
     // out[m] of operator() alone (m a compile-time constant)
     __device__ __forceinline__ half2v one(uint32_t x, int m) const
@@ -121,7 +140,7 @@ struct Unpacker {
         const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
         const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
         const uint32_t z = m >= 2 ? x >> 8 : x;
-        return (m & 1) ? as_h2(and_or(z, 0x00F000F0u, m64)) - k72 : as_h2(and_or(z, 0x000F000Fu, m1024)) - k1032;
+        return (m & 1) ? as_h2(and_or(z, hi4, m64)) - k72 : as_h2(and_or(z, lo4, m1024)) - k1032;
     }
 };
 
@@ -212,7 +231,7 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
     __shared__ float l_s[4][16];
     uint16_t *meta = reinterpret_cast<uint16_t *>(smem);  // [4][NG][ROUND]
 
-    const Unpacker unpack{0x64006400u, 0x54005400u};
+    const Unpacker unpack = Unpacker::make();
 
     // ---- startup: issue the Q loads, the first round's scale/bias loads and
     //      the first tile's K/V loads back to back, then wait for each group
@@ -512,6 +531,16 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
 // paid once per 73 KB instead of once per 18 KB.
 // ---------------------------------------------------------------------------
 constexpr int CH1 = 512;  // most rows of a chunk in the one-wavefront kernel
+// Headroom (log2 units) above a head's running maximum when its softmax
+// reference is raised: weights are at most 2^-kHeadroom of their largest
+// possible value, which costs nothing in fp32 and about 2 bits at the fp16
+// subnormal floor of the value weights' lo halves.
+constexpr float kHeadroom = 2.0f;
+// With the hi and lo halves of the value weights in separate operand rows,
+// the lo halves are stored scaled by 2^11: lo is at most half an fp16 ulp of
+// hi, so lo * 2^11 stays within hi's magnitude (no overflow) and, for any
+// weight above 2^-13, in the normal fp16 range instead of the subnormals.
+constexpr float kLoScale = 2048.0f;
 
 // Sum / max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 row
 // swaps: with both operands equal, the two results of a swap hold a lane's
@@ -536,17 +565,52 @@ __device__ __forceinline__ void row_swap32(float v, float &x, float &y)
     y = __builtin_bit_cast(float, r1);
 }
 
-// max of two values fresh from a lane swap: fmaxf would first canonicalise
-// both (they arrive through an integer bit cast); med3(x, y, +inf) is the
-// same maximum in one compiler-visible instruction
-__device__ __forceinline__ float max_raw(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); }
+// Maxima of values the compiler cannot prove canonical (results of lane
+// swaps and DPP sums, or joined across the tail branch): fmaxf would first
+// canonicalise every operand with an extra v_max. The NaN-propagating
+// maximum needs no canonical operands and maps to gfx950's v_maximum3_f32;
+// scores are finite or -inf, never NaN, so it is the same maximum.
+__device__ __forceinline__ float max_raw(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 
-__device__ __forceinline__ float xrow_max(float v)
+__device__ __forceinline__ float max3_raw(float x, float y, float z) { return max_raw(max_raw(x, y), z); }
+
+// max(m, maximum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float xrow_max(float v, float m)
 {
     float x, y;
     row_swap16(v, x, y);
     row_swap32(max_raw(x, y), x, y);
-    return max_raw(x, y);
+    return max3_raw(m, x, y);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Multiply an accumulator tile in place. Tied asm operands keep the products
+// in the accumulator's own registers: as plain code the compiler writes them
+// to new registers and, on the far more common path that skips the rescale,
+// copies every accumulator across (one move per accumulator element and tile).
+// The compiler's hazard tracking does not see into inline asm, so a rescale
+// starts with mfma_result_wait(): more wait states than any matrix
+// instruction here needs before a vector instruction may read its result.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"); }
+
+__device__ __forceinline__ void scale_in_place(float4v &v, const float4v &c)
+{
+    float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+    asm volatile("v_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %5\n\tv_mul_f32 %2, %2, %6\n\tv_mul_f32 %3, %3, %7"
+                 : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+                 : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
+    v = (float4v){x0, x1, x2, x3};
+}
+
+
+// One DPP move inside each row of 16 lanes: lanes in the banks of BANKS
+// (bank b = lanes 4b..4b+3 of a row) take src from lane l ^ 8 (row_ror:8);
+// the other lanes keep old.
+template <int BANKS>
+__device__ __forceinline__ uint32_t take_half_row(uint32_t old, uint32_t src)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x128, 0xF, BANKS, false);
 }
 
 __device__ __forceinline__ float xrow_sum(float v)
@@ -557,31 +621,25 @@ __device__ __forceinline__ float xrow_sum(float v)
     return x + y;
 }
 
-// K words as MFMA operands with the nibbles read as 64 + n: all four nibble
-// positions are moved to mantissa bits 4-7 under the exponent 2^6, so no fp16
-// subtraction is needed. The 64 * sum(q) this adds to every group's dot
-// product is removed with the bias, in fp32, outside the matrix core: the
-// products stay within a factor 79/64 of each other, so the truncating sum of
-// one instruction loses at most a few ulps of 79 |q|max.
-//
-// One asm block ending in s_nop 1: the compiler's hazard tracking does not
-// look inside inline asm, and a matrix instruction reading a register that a
-// vector instruction wrote needs two wait states in between.
-__device__ __forceinline__ half8 k_operand64(uint32_t w, uint32_t m64)
+// K words as MFMA operands with the nibbles read as fp16 subnormals: a
+// nibble masked into bits 0-3 of a half whose exponent field is zero is the
+// exact value n * 2^-24, one masked into bits 4-7 is n * 2^-20 (the matrix
+// core takes subnormal fp16 inputs exactly). Element j of the operand holds
+// dimension kPerm[j]; elements 2, 3, 6 and 7 are of the second kind, and the
+// query elements they meet are stored divided by 16, so that every product
+// is n q 2^-24 and the score factor carries the 2^24. The codes enter with
+// no offset, so the products are at most 15 |q| and the truncating sum of
+// one instruction loses at most a few ulps of that. Dividing by 16 is exact
+// in fp16 unless |q| < 2^-10, where it rounds to the subnormal grid (an
+// absolute error below 2^-21 |q| units in that element).
+__device__ __forceinline__ half8 k_operand_sub(uint32_t w, const Unpacker &u)
 {
-    uint32_t r0, r1, r2, r3;
-    asm("v_lshlrev_b32 %0, 4, %4\n\t"
-        "v_and_or_b32 %0, %0, %5, %6\n\t"
-        "v_and_or_b32 %1, %4, %5, %6\n\t"
-        "v_lshrrev_b32 %2, 4, %4\n\t"
-        "v_and_or_b32 %2, %2, %5, %6\n\t"
-        "v_lshrrev_b32 %3, 8, %4\n\t"
-        "v_and_or_b32 %3, %3, %5, %6\n\t"
-        "s_nop 1"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(w), "s"(0x00F000F0u), "v"(m64));
-    return cat8(as_h2(r0), as_h2(r1), as_h2(r2), as_h2(r3));
+    const uint32_t y = w >> 8;
+    return cat8(as_h2(w & u.lo4), as_h2(w & u.hi4), as_h2(y & u.lo4), as_h2(y & u.hi4));
 }
+
+// elements of a K operand that read n * 2^-20 (their query elements are / 16)
+__device__ __forceinline__ constexpr bool k_elem_fine(int j) { return (j & 2) != 0; }
 
 // Fused decode step: quantise this (batch, KV head)'s new K and V rows into
 // cache row a.append_row (the rule of quant_rule.h; lanes 0..D/8-1 take the
@@ -637,6 +695,10 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     constexpr int WPG = W / NG;
     constexpr int PAIRS = TILE * NG;        // (row, group) pairs of scale/bias per tile
     constexpr int MP = (PAIRS + 63) / 64;   // pairs per lane (NG = 1: lanes 32-63 repeat 0-31)
+    // D = 128 with two scale groups: value products group by group, with the
+    // hi and lo weight halves as operand rows (half the matrix instructions)
+    constexpr bool GV = D == 128 && NG == 2;
+    constexpr float LS = GV ? kLoScale : 1.0f;  // scale of the lo weight halves
 
     const int lane = threadIdx.x;
     const int q4 = lane >> 4;
@@ -646,11 +708,15 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     const int b = blockIdx.z;
     const int nrep = a.n_rep;
     const int R = nrep * NG;
-    const int hl = col / NG, gl = col % NG;
-    // columns >= R (no query head) compute on zero Q and are never written;
+    // score column col = (head hl, scale group gl): hl * NG + gl, or with GV
+    // hl + 8 gl, so that a lane and its partner of the other group are
+    // lanes l and l ^ 8, which a bank-masked DPP move can pair
+    const int hl = GV ? (col & 7) : col / NG, gl = GV ? (col >> 3) : col % NG;
+    // columns without a query head compute on zero Q and are never written;
     // every column keeps its own softmax state, so they need no masking
-    const bool col_on = col < R;
+    const bool col_on = hl < nrep;
     const int h0 = kvh * nrep;
+    const bool low8 = (lane & 8) == 0;  // GV: this lane's V word is in group 0
 
     const int t0 = (int)((int64_t)c * a.chunk);
     const int t1 = (int)min((int64_t)t0 + a.chunk, a.skv);
@@ -670,13 +736,15 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // of MP (row, group) pairs of a tile; one tile ahead of use they become
     // the fp32 factors of the tile code, one 16-byte record per pair in a
     // two-slot LDS buffer [slot][row * NG + group]:
-    //   x: s_k * c            (c = softmax scale * log2 e)
-    //   y: (b_k - 64 s_k) * c (bias of the 64 + n operands)
+    //   x: s_k * c * 2^24     (c = softmax scale * log2 e; 2^24 undoes the
+    //                          subnormal scale of the K operands)
+    //   y: b_k * c
     //   z: s_v
     //   w: b_v + 8 s_v        (bias of the centred value codes)
     __shared__ __align__(16) float4 mring[2][PAIRS];
-    const Unpacker unpack{0x64006400u, 0x54005400u};
+    const Unpacker unpack = Unpacker::make();
     const float cs = a.score_scale;
+    const float cs24 = cs * 16777216.0f;  // c * 2^24
 
     // ---- start-up: Q and the first PF tiles, all requested before the first wait
     float qv[KM][8];
@@ -745,7 +813,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             const float kb = h_val((uint16_t)mt[p][1]);
             const float vs = h_val((uint16_t)mt[p][2]);
             const float vb = h_val((uint16_t)mt[p][3]);
-            mring[slot][pr] = make_float4(ks * cs, fmaf(-64.0f, ks, kb) * cs, vs, fmaf(8.0f, vs, vb));
+            mring[slot][pr] = make_float4(ks * cs24, kb * cs, vs, fmaf(8.0f, vs, vb));
         }
         // LDS instructions of a wavefront execute in order, so the tile code
         // sees these records; only the compiler must not move reads above
@@ -763,7 +831,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     __builtin_amdgcn_sched_barrier(0);
 
     // Q restricted to the column's group, in the dimension order of the K
-    // operands; qsum is the group sum of exactly what the matrix core sees
+    // operands, divided by 16 where the K operand reads n * 2^-20; qsum is
+    // the group sum of exactly what the matrix core sees, in query units
     half8 qhi[KM], qlo[KM];
     float qsum = 0.0f;
 #pragma unroll
@@ -772,22 +841,26 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         const bool mine = col_on && (word / WPG) == gl;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float x = mine ? qv[u][kPerm[j]] : 0.0f;
+            const float unit = k_elem_fine(j) ? 16.0f : 1.0f;
+            const float x = mine ? qv[u][kPerm[j]] * (1.0f / unit) : 0.0f;
             const _Float16 hi = (_Float16)x;
             qhi[u][j] = hi;
             if constexpr (Q32) {
                 const _Float16 lo = (_Float16)(x - (float)hi);
                 qlo[u][j] = lo;
-                qsum += (float)hi + (float)lo;
+                qsum = fmaf(unit, (float)hi + (float)lo, qsum);
             } else {
-                qsum += (float)hi;
+                qsum = fmaf(unit, (float)hi, qsum);
             }
         }
     }
     qsum = xrow_sum(qsum);
     stage_meta(0, mbuf[0]);
 
-    float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
+    // m_run: the softmax reference of this lane's head (log2 units); scores
+    // are computed relative to it, each of the NG group columns of a head
+    // subtracting m_part = m_run / NG before their sum
+    float m_run = 0.0f, m_part = 0.0f, l_run = 0.0f, b_run = 0.0f;
     float4v acc[VS][8];
 #pragma unroll
     for (int s = 0; s < VS; ++s)
@@ -840,7 +913,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 for (int uu = 0; uu < KM; ++uu) {
                     const uint4 x = kcur[blk][uu / 4];
                     const uint32_t w = (uu % 4 == 0) ? x.x : (uu % 4 == 1) ? x.y : (uu % 4 == 2) ? x.z : x.w;
-                    const half8 ka = k_operand64(w, unpack.m64);
+                    const half8 ka = k_operand_sub(w, unpack);
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[uu], sacc, 0, 0, 0);
                     if constexpr (Q32)
                         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[uu], sacc, 0, 0, 0);
@@ -848,7 +921,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float4 f = fac[4 * blk + i];
-                    sc[4 * blk + i] = group_sum<NG>(fmaf(f.x, sacc[i], f.y * qsum));
+                    const float sg = fmaf(f.x, sacc[i], fmaf(f.y, qsum, -m_part));
+                    sc[4 * blk + i] = GV ? sg + dpp_f<0x128>(sg) : group_sum<NG>(sg);  // row_ror:8
                 }
             }
             if (t0 + TILE * ti + TILE > t1) {  // uniform: the chunk's last tiles
@@ -859,66 +933,124 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                     sc[i] = r <= last ? sc[i] : -INFINITY;
                 }
             }
-            float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            const float mx = max3_raw(max3_raw(sc[0], sc[1], sc[2]), max3_raw(sc[3], sc[4], sc[5]),
+                                      max_raw(sc[6], sc[7]));
 
-            // ---- online softmax across tiles: rescale only when a head's max rises
-            mx = xrow_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            if (ti != 0 && __builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-                const float corr = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
-                l_run *= corr;
-                b_run *= corr;
-                float4v corr_row;
+            // ---- online softmax across tiles. The scores are relative to the
+            // head's reference m_run, which is raised only when a score
+            // exceeds it, and then to that maximum plus kHeadroom: every
+            // weight exp2(s - m_run) stays <= 1, the small rises of the
+            // running maximum over most later tiles cost nothing, and only
+            // the first tile and the rare raise take this branch (the first
+            // sets the reference from its own maximum).
+            if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > 0.0f) != 0) {
+                const float full = xrow_max(mx, -INFINITY);  // the head's tile maximum
+                const bool raise = full > 0.0f || (ti == 0 && full > -INFINITY);
+                const float delta = raise ? full + kHeadroom : 0.0f;
+                m_run += delta;
+                m_part = m_run * (1.0f / NG);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    corr_row[i] = __shfl(corr, 4 * q4 + i);
+                for (int i = 0; i < 8; ++i)
+                    sc[i] -= delta;
+                if (ti != 0) {
+                    const float corr = __builtin_amdgcn_exp2f(-delta);
+                    l_run *= corr;
+                    b_run *= corr;
+                    float4v corr_row;
 #pragma unroll
-                for (int s2 = 0; s2 < VS; ++s2)
+                    for (int i = 0; i < 4; ++i)
+                        corr_row[i] = __shfl(corr, 4 * q4 + i);
+                    mfma_result_wait();
 #pragma unroll
-                    for (int m = 0; m < 8; ++m)
-                        acc[s2][m] *= corr_row;
+                    for (int s2 = 0; s2 < VS; ++s2)
+#pragma unroll
+                        for (int m = 0; m < 8; ++m)
+                            scale_in_place(acc[s2][m], corr_row);
+                }
             }
-            m_run = m_new;
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
 
             // ---- weights p * s_v as hi + lo fp16 halves, and the bias term
             half8 phi, plo;
             float lsum = 0.0f, bsum = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(sc[j] - m_use);
-                const float p1 = __builtin_amdgcn_exp2f(sc[j + 1] - m_use);
+                const float p0 = __builtin_amdgcn_exp2f(sc[j]);
+                const float p1 = __builtin_amdgcn_exp2f(sc[j + 1]);
                 lsum += p0 + p1;
                 bsum = fmaf(p0, fac[j].w, fmaf(p1, fac[j + 1].w, bsum));
                 const float w0 = p0 * fac[j].z, w1 = p1 * fac[j + 1].z;
-                // any rounding of hi works: lo = w - hi is exact in fp32
+                // any rounding of hi works: lo = w - hi is exact in fp32; with
+                // GV the lo halves have rows of their own and are kept as
+                // lo * kLoScale, above the fp16 subnormal range
                 const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-                const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0 - (float)h[0], w1 - (float)h[1]));
+                const half2v l = __builtin_bit_cast(
+                    half2v, __builtin_amdgcn_cvt_pkrtz((w0 - (float)h[0]) * LS, (w1 - (float)h[1]) * LS));
                 phi[j] = h[0]; phi[j + 1] = h[1];
                 plo[j] = l[0]; plo[j + 1] = l[1];
             }
             l_run += lsum;
             b_run += bsum;
+            if constexpr (GV) {
+                // Group-aligned value products: row h + 8 e of group g's
+                // value operand is the hi (e = 0) or lo (e = 1) half of head
+                // h's weights for group g. The lane of column h + 8 g holds
+                // both halves for group g, so group 0's operand takes the lo
+                // half into lanes 8-15 of each row and group 1's the hi half
+                // into lanes 0-7, each with one DPP move per register.
+                const u32x4 H = __builtin_bit_cast(u32x4, phi), L = __builtin_bit_cast(u32x4, plo);
+                u32x4 A0, A1;
 #pragma unroll
-            for (int s2 = 0; s2 < VS; ++s2) {
-                // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
-                // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
-                uint32_t xw[4], yw[4];
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t h = H[r], lo = L[r];
+                    A0[r] = take_half_row<0xC>(h, lo);
+                    A1[r] = take_half_row<0x3>(lo, h);
+                }
+                const half8 a0 = __builtin_bit_cast(half8, A0), a1 = __builtin_bit_cast(half8, A1);
+                // A lane of column col < 8 holds a group-0 V word, col >= 8 a
+                // group-1 word; in group g's products a lane whose word is in
+                // g gives its dimensions 0..3, the others dimensions 4..7 of
+                // the word of lane l ^ 8 (see the store)
+                uint32_t bx[2][4];
 #pragma unroll
                 for (int jp = 0; jp < 4; ++jp) {
-                    xw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
-                    yw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
+                    const uint32_t xw = __builtin_amdgcn_perm(vcur[0][2 * jp + 1], vcur[0][2 * jp], 0x05040100u);
+                    const uint32_t yw = __builtin_amdgcn_perm(vcur[0][2 * jp + 1], vcur[0][2 * jp], 0x07060302u);
+                    bx[0][jp] = take_half_row<0xC>(xw, yw);
+                    bx[1][jp] = take_half_row<0x3>(xw, yw);
                 }
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    half2v e[4];
+                for (int g = 0; g < 2; ++g)
 #pragma unroll
-                    for (int jp = 0; jp < 4; ++jp)
-                        e[jp] = unpack.one(m < 4 ? xw[jp] : yw[jp], m & 3);
-                    const half8 bv = cat8(e[0], e[1], e[2], e[3]);
-                    acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
-                    acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
+                    for (int mm = 0; mm < 4; ++mm) {
+                        half2v e[4];
+#pragma unroll
+                        for (int jp = 0; jp < 4; ++jp)
+                            e[jp] = unpack.one(bx[g][jp], mm);
+                        const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                        acc[0][4 * g + mm] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(g ? a1 : a0, bv, acc[0][4 * g + mm], 0, 0, 0);
+                    }
+            } else {
+#pragma unroll
+                for (int s2 = 0; s2 < VS; ++s2) {
+                    // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
+                    // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
+                    uint32_t xw[4], yw[4];
+#pragma unroll
+                    for (int jp = 0; jp < 4; ++jp) {
+                        xw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
+                        yw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
+                    }
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        half2v e[4];
+#pragma unroll
+                        for (int jp = 0; jp < 4; ++jp)
+                            e[jp] = unpack.one(m < 4 ? xw[jp] : yw[jp], m & 3);
+                        const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                        acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
+                        acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
+                    }
                 }
             }
 
@@ -936,6 +1068,46 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         const int64_t o = ((int64_t)b * a.Hq + h0 + hl) * C + c;
         a.part_m[o] = m_run * kLn2;
         a.part_l[o] = l_tot;
+    }
+    if constexpr (GV) {
+        // Row i = h + 8 e of the value products sits in lanes of q4 = i / 4:
+        // lanes l < 32 hold the hi rows, lanes l ^ 32 the lo rows (scaled by
+        // kLoScale) of the same heads 4 (q4 & 1) + r. One swap of lanes 32-63
+        // of group 0's value with lanes 0-31 of group 1's leaves (hi, lo) of
+        // group 0 in lanes 0-31 and of group 1 in lanes 32-63, so that
+        // hi + lo / kLoScale is group g = q4 / 2.
+        // Group g's products of this lane are dimensions 8 col + 0..3 when
+        // its own V word is in group g, else 8 (col ^ 8) + 4..7.
+        const int g = q4 >> 1;
+        const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
+        float o[4][4];  // [r][mm]
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // (elements go through scalars: a bit cast of a vector
+                // element in place reads element 0)
+                const float e0 = acc[0][mm][r], e1 = acc[0][4 + mm][r];
+                const uint32_t a0 = __builtin_bit_cast(uint32_t, e0);
+                const uint32_t a1 = __builtin_bit_cast(uint32_t, e1);
+                // the swap leaves lanes 0-31 of both operands (the hi rows)
+                // in the first result and lanes 32-63 (the lo rows) in the
+                // second
+                const auto sw = __builtin_amdgcn_permlane32_swap(a0, a1, false, false);
+                const uint32_t x = sw[0], y = sw[1];
+                o[r][mm] = fmaf(__builtin_bit_cast(float, y), 1.0f / kLoScale, __builtin_bit_cast(float, x));
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * (q4 & 1) + r;
+            const float bias = __shfl(b_tot, h + 8 * g);
+            if (h < nrep) {
+                float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
+                *reinterpret_cast<float4 *>(dst + d0) =
+                    make_float4(o[r][0] + bias, o[r][1] + bias, o[r][2] + bias, o[r][3] + bias);
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1017,7 +1189,7 @@ void sdpa_partial_mfma_pair_kernel(PartialArgs a)
 
     __shared__ __align__(16) float smem_f[SMEM / 4];
     uint16_t *meta = reinterpret_cast<uint16_t *>(smem_f) + wave * META;  // [array][group][row]
-    const Unpacker unpack{0x64006400u, 0x54005400u};
+    const Unpacker unpack = Unpacker::make();
 
     // ---- start-up: Q, this wavefront's scale/bias and the first PF tiles
     half8 qv[KM];

@@ -1,11 +1,17 @@
 """Checks on the gfx950 assembly of the matrix-core kernels (CPU only).
 
-The compiler inserts the wait states that gfx9 matrix instructions need after
-a vector instruction writes one of their A/B source registers, but it cannot
-see inside inline asm. Every kernel is compiled to assembly and each
-v_mfma's A/B sources are traced back to the last instruction that wrote them:
-if that was a vector instruction (in or out of inline asm), at least two
-wait states (instructions or s_nop slots) must separate the two.
+The compiler inserts the wait states that gfx9 matrix instructions need
+around vector instructions, but it cannot see inside inline asm. Every kernel
+is compiled to assembly and checked two ways:
+ - each v_mfma's A, B and C sources are traced back to the last instruction
+   that wrote them: if that was a vector instruction (in or out of inline
+   asm), at least two wait states (instructions or s_nop slots) must separate
+   the two;
+ - each vector instruction inside inline asm that reads a register a v_mfma
+   wrote, or writes a register a v_mfma read as its accumulator, must come at
+   least MFMA_TO_ASM wait states after that v_mfma (more than the 16x16x32
+   and 32x32x16 instructions need), scanning back in layout order across
+   block boundaries.
 """
 
 import os
@@ -18,6 +24,7 @@ import pytest
 from quantized_kv_cache_quantize_amd import build as B
 
 MIN_WAIT = 2
+MFMA_TO_ASM = 18
 
 
 def _regs(text):
@@ -29,12 +36,53 @@ def _regs(text):
     return out
 
 
-def _kernels(asm):
+def _kernels(asm, keep_asm_marks=False):
     for m in re.finditer(r"^(_Z\S*_kernel\S*):", asm, re.M):
         name = m.group(1)
         end = asm.index(".Lfunc_end", m.end())
-        lines = [ln.split(";")[0].strip() for ln in asm[m.end():end].split("\n")]
-        yield name, [ln for ln in lines if ln and not ln.startswith(".")]
+        out = []
+        for ln in asm[m.end():end].split("\n"):
+            t = ln.strip()
+            if keep_asm_marks and t.startswith((";;#ASMSTART", ";;#ASMEND")):
+                out.append(t)
+                continue
+            t = t.split(";")[0].strip()
+            if t and not t.startswith("."):
+                out.append(t)
+        yield name, out
+
+
+def _asm_after_mfma(lines):
+    """Smallest count of wait states between a v_mfma and a later vector
+    instruction inside inline asm that reads one of its results or writes
+    one of its accumulator sources."""
+    worst = None
+    inside = False
+    for i, ln in enumerate(lines):
+        if ln.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if ln.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if not inside or not ln.startswith("v_") or ln.startswith("v_mfma"):
+            continue
+        ops = ln.split(None, 1)[1].split(",")
+        reads, writes = _regs(",".join(ops[1:])), _regs(ops[0])
+        waits = 0
+        for j in range(i - 1, -1, -1):
+            prev = lines[j]
+            if prev.startswith(";;#") or prev.endswith(":"):
+                continue
+            if waits >= MFMA_TO_ASM:
+                break
+            if prev.startswith("v_mfma"):
+                mops = prev.split(None, 1)[1].split(",")
+                if _regs(mops[0]) & reads or _regs(mops[3]) & writes:
+                    worst = waits if worst is None else min(worst, waits)
+                    break
+            waits += int(prev.split()[1]) + 1 if prev.startswith("s_nop") else 1
+    return worst
 
 
 def _min_wait(lines):
@@ -45,7 +93,7 @@ def _min_wait(lines):
         if not ln.startswith("v_mfma"):
             continue
         ops = ln.split(None, 1)[1].split(",")
-        srcs = _regs(ops[1]) | _regs(ops[2])
+        srcs = _regs(ops[1]) | _regs(ops[2]) | _regs(ops[3])
         waits = 0
         for j in range(i - 1, max(-1, i - 16), -1):
             prev = lines[j]
@@ -84,9 +132,31 @@ def test_vector_write_to_mfma_read_wait_states(mfma_asm):
             assert w >= MIN_WAIT, "%s: MFMA reads a vector result after %d wait states" % (name, w)
 
 
+def test_mfma_result_to_inline_asm_wait_states(mfma_asm):
+    for name, lines in _kernels(mfma_asm, keep_asm_marks=True):
+        w = _asm_after_mfma(lines)
+        if w is not None:
+            assert w >= MFMA_TO_ASM, "%s: inline asm reads a matrix result after %d wait states" % (name, w)
+
+
+def test_checker_flags_asm_after_mfma():
+    lines = ["v_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[20:23], v[0:3]", ";;#ASMSTART",
+             "v_mul_f32 v1, v1, v40", ";;#ASMEND"]
+    assert _asm_after_mfma(lines) == 0
+    lines = ["v_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[20:23], v[0:3]", ";;#ASMSTART", "s_nop 7", "s_nop 7",
+             "s_nop 3", ";;#ASMEND", ".LBB0_1:", ";;#ASMSTART", "v_mul_f32 v1, v1, v40", ";;#ASMEND"]
+    assert _asm_after_mfma(lines) is None  # 20 wait states: the scan stops before the MFMA
+    # an asm write into the accumulator source of a v_mfma just issued
+    lines = ["v_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[20:23], v[4:7]", "s_nop 0", ";;#ASMSTART",
+             "v_lshlrev_b32 v5, 4, v40", ";;#ASMEND"]
+    assert _asm_after_mfma(lines) == 1
+
+
 def test_checker_flags_a_close_write():
     # the checker itself: a vector write right before the MFMA that reads it
     lines = ["v_and_or_b32 v10, v1, s2, v3", "v_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[20:23], 0"]
     assert _min_wait(lines) == 0
     lines = ["v_and_or_b32 v10, v1, s2, v3", "s_nop 1", "v_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[20:23], 0"]
     assert _min_wait(lines) == 2
+    lines = ["v_mul_f32 v2, v2, v9", "v_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[20:23], v[0:3]"]
+    assert _min_wait(lines) == 0  # an accumulator source counts too
