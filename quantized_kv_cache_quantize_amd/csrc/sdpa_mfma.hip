@@ -870,23 +870,6 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 
 #pragma unroll 1
     for (int kk = 0; kk < ntile; kk += PF) {
-        // Issue priority falls as the chunk progresses. The SIMD favours its
-        // older wavefront, which would otherwise run ahead while the other
-        // one is starved and finishes alone; with priorities that drop in
-        // steps, the wavefront that is behind gets issue slots first, the
-        // two stay within one ring pass of each other and keep their loads
-        // in flight together.
-        {
-            const int lvl = __builtin_amdgcn_readfirstlane((ntile - kk) * 4 / (ntile + 1));
-            if (lvl >= 3)
-                __builtin_amdgcn_s_setprio(3);
-            else if (lvl == 2)
-                __builtin_amdgcn_s_setprio(2);
-            else if (lvl == 1)
-                __builtin_amdgcn_s_setprio(1);
-            else
-                __builtin_amdgcn_s_setprio(0);
-        }
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             // tiles past the chunk (ntile not a multiple of PF) are run too:
