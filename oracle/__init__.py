@@ -61,6 +61,8 @@ def _load():
     lib.oracle_sdpa.argtypes = cache_args + [f64p, C.c_int]
     lib.oracle_sdpa_partials.restype = C.c_int
     lib.oracle_sdpa_partials.argtypes = cache_args + [C.c_int64, f64p, f64p, f64p, C.c_int]
+    lib.oracle_hadamard_rows.restype = C.c_int
+    lib.oracle_hadamard_rows.argtypes = [f64p, C.c_int64, C.c_int, f64p]
     lib.oracle_combine_partials.restype = None
     lib.oracle_combine_partials.argtypes = [f64p, f64p, f64p, C.c_int64, C.c_int64, C.c_int, f64p]
     _lib = lib
@@ -198,6 +200,17 @@ class Cache:
             sc[:, :, length:length + n] = s
             bi[:, :, length:length + n] = b
 
+    def append_rotated(self, k: np.ndarray, v: np.ndarray, length: int):
+        """Hadamard-rotated append (TurboQuant explainer blog, "TurboQuant"
+        section and step "1. Vector Rotation"): each fp16 row x is rotated to
+        fl32(hadamard(x)) and that fp32 row is quantised into rows
+        [length, length + n). fp16 inputs only: their rotation sums are exact,
+        so the fp32 values, and with them the codes, are fixed."""
+        k, v = np.asarray(k), np.asarray(v)
+        if k.dtype != np.float16 or v.dtype != np.float16:
+            raise TypeError("append_rotated takes fp16 rows")
+        self.append(hadamard(k).astype(np.float32), hadamard(v).astype(np.float32), length)
+
     def _args(self):
         return (_p(self.k_q, C.c_uint32), _p(self.v_q, C.c_uint32), _p(self.k_scale, C.c_uint16),
                 _p(self.k_bias, C.c_uint16), _p(self.v_scale, C.c_uint16), _p(self.v_bias, C.c_uint16),
@@ -237,6 +250,28 @@ def sdpa_partials(cache: Cache, skv: int, q: np.ndarray, alpha: float, chunk: in
     if rc != 0:
         raise ValueError("oracle_sdpa_partials failed (%d)" % rc)
     return m, l, acc
+
+
+def hadamard(x: np.ndarray) -> np.ndarray:
+    """Normalised Hadamard rotation of the last axis (a power of two), in
+    float64: y = H_n x / sqrt(n) with H_n in Sylvester order (the TurboQuant
+    explainer blog's worked example). Its own inverse."""
+    lib = _load()
+    x64 = np.ascontiguousarray(x, dtype=np.float64)
+    n = x64.shape[-1]
+    out = np.zeros_like(x64)
+    if lib.oracle_hadamard_rows(_p(x64, C.c_double), x64.size // n, n, _p(out, C.c_double)) != 0:
+        raise ValueError("hadamard: length %d is not a power of two" % n)
+    return out
+
+
+def sdpa_rotated(cache: Cache, skv: int, q: np.ndarray, alpha: float, nthreads: int | None = None) -> np.ndarray:
+    """Attention over a Hadamard-rotated cache (rows appended with
+    Cache.append_rotated): the query is rotated the same way, so its scores
+    against rotated keys equal those against the original keys, and the
+    output, a combination of rotated value rows, is rotated back (the
+    rotation is its own inverse). float64 throughout."""
+    return hadamard(sdpa(cache, skv, hadamard(q), alpha, nthreads))
 
 
 def combine_partials(m: np.ndarray, l: np.ndarray, acc: np.ndarray) -> np.ndarray:

@@ -20,6 +20,10 @@
  *    step (K and V quantised to int4 on append; GQA) and the lesson that
  *    asymmetric int4 quantisation is the practical choice.
  *
+ *  - The blog on running Gemma 4 with TurboQuant (devengoratela.com), section
+ *    "TurboQuant" with its Hadamard worked example: the normalised Hadamard
+ *    rotation applied to K (and here also V and Q) before quantisation.
+ *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - Quantiser: per group of G consecutive head-dim values, bias = the group
  *    minimum rounded DOWN to fp16, scale = fl32(fl32(max - bias) / 15)
@@ -413,6 +417,49 @@ void oracle_combine_partials(const double *part_m, const double *part_l, const d
         for (int d = 0; d < D; ++d)
             out[i * D + d] /= den;
     }
+}
+
+/* ----------------------------------------------------- Hadamard rotation */
+/* The normalised Hadamard transform of the TurboQuant explainer blog on
+ * running Gemma 4 with TurboQuant (devengoratela.com; its "TurboQuant"
+ * section, the worked example under it and "Transform Results", and step
+ * "1. Vector Rotation"): a row x of length n (a power of two) becomes
+ * y = H_n x / sqrt(n), where H_n is the Hadamard matrix in Sylvester order
+ * (the matrix of the example: H_2n = [[H_n, H_n], [H_n, -H_n]]), whose entry
+ * (i, j) is (-1)^(number of bits set in i & j). The normalised matrix is
+ * orthogonal and its own inverse, which is how the blog recovers the vector.
+ *
+ * Written from the definition: the sum over j is a plain loop in float64,
+ * then one multiplication by c = 1.0 / sqrt(n) (correctly rounded sqrt and
+ * division). For fp16 inputs every term and partial sum is a multiple of
+ * 2^-24 below 2^23 in magnitude, so the sum is exact in float64 whatever the
+ * order, and y = fl64(S * c) is a single rounding of the exact value. */
+static int parity_of(unsigned v)
+{
+    int p = 0;
+    while (v) {
+        p ^= 1;
+        v &= v - 1;
+    }
+    return p;
+}
+
+int oracle_hadamard_rows(const double *x, int64_t rows, int n, double *out)
+{
+    if (n < 1 || (n & (n - 1)) != 0)
+        return -1;
+    const double c = 1.0 / sqrt((double)n);
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * n;
+        double *yr = out + r * n;
+        for (int i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int j = 0; j < n; ++j)
+                s += parity_of((unsigned)(i & j)) ? -xr[j] : xr[j];
+            yr[i] = s * c;
+        }
+    }
+    return 0;
 }
 
 /* ------------------------------------------------- array forms for tests */
