@@ -93,7 +93,8 @@ def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 123
         v_new = torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.float32).half()
         ws = kvq.partials_buffers(B, HQ, D, skv, chunk, device=dev)
         out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
-        pool.append(dict(cache=cache, q=q, k_new=k_new, v_new=v_new, ws=ws, out=out))
+        qr = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+        pool.append(dict(cache=cache, q=q, k_new=k_new, v_new=v_new, ws=ws, out=out, qr=qr))
     torch.cuda.synchronize()
     return pool
 
@@ -102,7 +103,9 @@ def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"
     """n decode steps, each on a different layer of the pool: the current
     token's K/V row is quantised into row skv-1 and attention runs over skv
     rows. step "fused": kvq_decode_step (append inside the attention kernel,
-    then the reduce); "unfused": append, partial and reduce as three calls.
+    then the reduce); "unfused": append, partial and reduce as three calls;
+    "rotated": the Hadamard-rotated cache, i.e. rotate q, rotated append,
+    partial (fp32 q), reduce, rotate the output back.
     events[i]: (start, stop) recorded in the attention kernel's own dispatch."""
     alpha = 1.0 / math.sqrt(D)
     stream = torch.cuda.current_stream()
@@ -113,14 +116,21 @@ def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"
             kvq.decode_step(L["cache"], skv - 1, L["k_new"], L["v_new"], L["q"], alpha, chunk, out=L["out"],
                             workspace=L["ws"], kernel=kernel, stream=stream, events=ev)
             continue
-        kvq.quantize_kv_append(L["cache"], skv - 1, L["k_new"], L["v_new"], stream=stream)
+        q = L["q"]
+        if step == "rotated":
+            q = kvq.hadamard_rotate(L["q"], out=L["qr"], stream=stream)
+            kvq.quantize_kv_append_rotated(L["cache"], skv - 1, L["k_new"], L["v_new"], stream=stream)
+        else:
+            kvq.quantize_kv_append(L["cache"], skv - 1, L["k_new"], L["v_new"], stream=stream)
         m, l, acc = L["ws"]
         if ev is not None:
-            kvq.sdpa_int4_partial_timed(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, ev[0], ev[1],
+            kvq.sdpa_int4_partial_timed(L["cache"], skv, q, alpha, chunk, m, l, acc, ev[0], ev[1],
                                         kernel=kernel, stream=stream)
         else:
-            kvq.sdpa_int4_partial(L["cache"], skv, L["q"], alpha, chunk, m, l, acc, kernel=kernel, stream=stream)
+            kvq.sdpa_int4_partial(L["cache"], skv, q, alpha, chunk, m, l, acc, kernel=kernel, stream=stream)
         kvq.sdpa_int4_reduce(m, l, acc, L["out"], stream=stream)
+        if step == "rotated":
+            kvq.hadamard_rotate(L["out"], out=L["out"], stream=stream)
 
 
 def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused"):
@@ -146,6 +156,42 @@ def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step=
     last = pool[-1]
     del pool
     return res, last
+
+
+APPEND_ROWS, APPEND_LEN, APPEND_CAP = 4096, 61440, 65536  # the outlier workload's bulk append
+
+
+def time_bulk_append(kvq, torch, rotated: bool, reps: int = 40, n_inputs: int = 20):
+    """Bulk append of the outlier workload's shape (4096 fp16 rows per KV head
+    at row 61440 of a 65536-row cache), plain or Hadamard-rotated, over
+    n_inputs distinct input sets (336 MB, more than the Infinity Cache).
+    Returns the median time of one append call in ms (events around the call)."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(777)
+    inputs = [(torch.randn((B, HKV, APPEND_ROWS, D), generator=gen, device=dev).half(),
+               torch.randn((B, HKV, APPEND_ROWS, D), generator=gen, device=dev).half()) for _ in range(n_inputs)]
+    cache = kvq.Int4KVCache(B, HKV, D, APPEND_CAP, G, device=dev)
+    fn = kvq.quantize_kv_append_rotated if rotated else kvq.quantize_kv_append
+    for i in range(5):
+        fn(cache, APPEND_LEN, *inputs[i % n_inputs])
+    torch.cuda.synchronize()
+    times = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(cache, APPEND_LEN, *inputs[i % n_inputs])
+        e1.record()
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+    del inputs, cache
+    return ms[len(ms) // 2]
+
+
+def bulk_append_bytes() -> int:
+    rows = B * HKV * APPEND_ROWS
+    return 2 * rows * D * 2 + 2 * rows * (D // 2 + 4 * (D // G))  # fp16 K and V in, packed rows out
 
 
 def cpu_baseline(kvq, torch, entry, skv):
@@ -189,7 +235,9 @@ def main():
     ap.add_argument("--sweep", default="1024,16384,65536",
                     help="extra Skv values timed with fewer steps (empty to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--step", choices=["fused", "unfused"], default="fused",
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the measurements of the rows beyond the headline path (Hadamard-rotated cache)")
+    ap.add_argument("--step", choices=["fused", "unfused", "rotated"], default="fused",
                     help="fused: kvq_decode_step (append inside the attention kernel, then the reduce); "
                          "unfused: append, partial and reduce as three calls")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -235,6 +283,29 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    next_rows = None
+    if not args.no_next_rows:
+        plain_ms = time_bulk_append(kvq, torch, False)
+        rot_ms = time_bulk_append(kvq, torch, True)
+        nb = bulk_append_bytes()
+        s64 = 65536
+        rot_res, _ = time_config(kvq, torch, s64, args.chunk, kernel, max(20, args.steps // 2), args.warmup,
+                                 pool_bytes, step="rotated")
+        next_rows = {"hadamard": {
+            "workload": "outlier-workload shape: append 4096 fp16 rows per KV head (B1 Hkv8 D128 G64) at row "
+                        "61440; rotated decode step at Skv 65536",
+            "append_bytes": nb,
+            "append_us": round(plain_ms * 1e3, 3),
+            "append_rotated_us": round(rot_ms * 1e3, 3),
+            "append_rotated_gbs": round(nb / (rot_ms * 1e-3) / 1e9, 2),
+            "append_rotated_frac": round(nb / (rot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_rotated_us_64k": round(rot_res["ms_per_step"] * 1e3, 3),
+            "step_rotated_gbs_64k": round((layer_bytes(s64) + append_bytes()) / (rot_res["ms_per_step"] * 1e-3) / 1e9, 2),
+            "attention_rotated_us_64k": round(rot_res["partial_ms_avg"] * 1e3, 3),
+            "timing": "append: median of 40 calls between stream events; step: as the headline step "
+                      "(rotate q, rotated append, partial with fp32 q, reduce, rotate the output back)",
+        }}
 
     step_bytes = layer_bytes(args.skv) + append_bytes()
     ms = main_res["ms_per_step"]
@@ -291,6 +362,7 @@ def main():
         "sweep": [{"skv": r["skv"], "us_per_layer": round(r["us_per_layer"], 3), "gbs": round(r["gbs"], 2),
                    "partial_us": round(r["partial_ms_avg"] * 1e3, 3), "partial_gbs": round(r["partial_gbs"], 2)}
                   for r in sweep],
+        "next_rows": next_rows,
         "context": "pages' Apple-Silicon fused-kernel latency on this shape: 1.6/2.7/5.7/9.9 ms at 1K/16K/64K/128K",
     }
     print(json.dumps(line), flush=True)

@@ -119,6 +119,36 @@ int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_ne
                            int dtype, int64_t n_new, void *stream);
 
 /*
+ * Hadamard-rotated append: the rotation of the blog on running Gemma 4 with
+ * TurboQuant (devengoratela.com; its "TurboQuant" section with the worked
+ * example and step "1. Vector Rotation"), which spreads outlier channels
+ * before quantisation. Each K and V row x is replaced by
+ *   r = fp32( fp64(H_D x) * fp64(1 / sqrt(D)) ),
+ * H_D the Sylvester-ordered Hadamard matrix (entry (i, j) = (-1)^popcount(i & j));
+ * the sum is exact for fp16 rows, then one rounding to float64 and one to
+ * fp32, and r is quantised exactly as kvq_quantize_kv_append quantises its
+ * rows. Arguments, layout and errors as kvq_quantize_kv_append, but the rows
+ * must be fp16 (KVQ_E_DTYPE otherwise) and the rotated values within
+ * +-65504 (not checked). A rotated cache is read with a rotated query and
+ * gives a rotated output: rotate q with kvq_hadamard_rotate, run the
+ * attention calls unchanged, rotate the output back (the rotation is its own
+ * inverse).
+ */
+int kvq_quantize_kv_append_rotated(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new,
+                                   int dtype, int64_t n_new, void *stream);
+
+/*
+ * out[r][:] = H_D x[r][:] / sqrt(D) in fp32, for rows r < rows (the rotation
+ * above, computed in float64 and rounded once to fp32; for fp16 rows the
+ * result equals the values kvq_quantize_kv_append_rotated quantises).
+ *  x:   [rows][D], KVQ_F16 or KVQ_F32; out: fp32 [rows][D]; both 16-byte
+ *       aligned. out may be x itself when x is fp32 (in place); any other
+ *       overlap returns KVQ_E_SHAPE.
+ *  D:   64, 128 or 256. rows == 0 is a no-op returning KVQ_OK.
+ */
+int kvq_hadamard_rotate(const void *x, int dtype, int64_t rows, int32_t head_dim, float *out, void *stream);
+
+/*
  * Phase 1 of split-K decode attention ("turboquant-llama3.170B" README,
  * split-K paragraph): one query row per head over cache rows [0, skv),
  * cut into C = kvq_num_chunks(skv, chunk) chunks of `chunk` rows (the last

@@ -20,11 +20,13 @@ from ._binding import (  # noqa: F401
     KvqError,
     cache_bytes,
     decode_step,
+    hadamard_rotate,
     lib,
     lib_path,
     num_chunks,
     partials_buffers,
     quantize_kv_append,
+    quantize_kv_append_rotated,
     sdpa_int4,
     sdpa_int4_partial,
     sdpa_int4_partial_timed,

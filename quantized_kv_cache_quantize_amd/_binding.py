@@ -64,6 +64,10 @@ def lib():
     L.kvq_cache_bytes.argtypes = [i32, i32, i32, i32, i64]
     L.kvq_quantize_kv_append.restype = C.c_int
     L.kvq_quantize_kv_append.argtypes = [cp, i64, vp, vp, C.c_int, i64, vp]
+    L.kvq_quantize_kv_append_rotated.restype = C.c_int
+    L.kvq_quantize_kv_append_rotated.argtypes = [cp, i64, vp, vp, C.c_int, i64, vp]
+    L.kvq_hadamard_rotate.restype = C.c_int
+    L.kvq_hadamard_rotate.argtypes = [vp, C.c_int, i64, i32, vp, vp]
     L.kvq_sdpa_int4_partial.restype = C.c_int
     L.kvq_sdpa_int4_partial.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, C.c_int, vp]
     L.kvq_sdpa_int4_partial_timed.restype = C.c_int
@@ -163,6 +167,34 @@ def quantize_kv_append(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_n
     _check("kvq_quantize_kv_append",
            lib().kvq_quantize_kv_append(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
                                         int(n), _stream(stream)))
+
+
+def quantize_kv_append_rotated(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                               stream=None) -> None:
+    """kvq_quantize_kv_append_rotated: Hadamard-rotate, then quantise, fp16
+    rows k_new, v_new [B][Hkv][n][D] (contiguous) into cache rows
+    [length, length + n)."""
+    assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
+    n = k_new.shape[2] if k_new.dim() == 4 else 0
+    cs = cache.c_struct()
+    _check("kvq_quantize_kv_append_rotated",
+           lib().kvq_quantize_kv_append_rotated(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new),
+                                                _dtype_code(k_new), int(n), _stream(stream)))
+
+
+def hadamard_rotate(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_hadamard_rotate: rotate every row of x [..., D] (fp16 or fp32,
+    contiguous) by H_D / sqrt(D); returns fp32 `out` (new, or the one given,
+    which may be x itself when x is fp32)."""
+    assert x.is_contiguous()
+    d = x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    assert out.is_contiguous() and out.dtype == torch.float32 and out.shape == x.shape
+    _check("kvq_hadamard_rotate",
+           lib().kvq_hadamard_rotate(_ptr(x), _dtype_code(x), int(x.numel() // d), int(d), _ptr(out),
+                                     _stream(stream)))
+    return out
 
 
 def partials_buffers(batch: int, hq: int, head_dim: int, skv: int, chunk: int = 512, device="cuda"):

@@ -87,13 +87,17 @@ int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32
     return 2 * rows * per_row;                                         // K and V
 }
 
-int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int dtype,
-                           int64_t n_new, void *stream)
+}  // extern "C"
+
+namespace {
+
+int append_impl(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int dtype, int64_t n_new,
+                void *stream, bool rotate)
 {
     int st = check_cache(cache);
     if (st)
         return st;
-    if (dtype != KVQ_F16 && dtype != KVQ_F32)
+    if (dtype != KVQ_F16 && (dtype != KVQ_F32 || rotate))
         return KVQ_E_DTYPE;
     if (len < 0 || n_new < 0)
         return KVQ_E_SHAPE;
@@ -124,7 +128,57 @@ int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_ne
     a.cap = cache->capacity;
     a.D = cache->head_dim;
     a.G = cache->group;
+    a.rot_scale = rotate ? 1.0 / sqrt((double)cache->head_dim) : 0.0;
     return launch_status(launch_quantize(a, dtype, (hipStream_t)stream));
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_quantize_kv_append(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int dtype,
+                           int64_t n_new, void *stream)
+{
+    return append_impl(cache, len, k_new, v_new, dtype, n_new, stream, false);
+}
+
+int kvq_quantize_kv_append_rotated(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new,
+                                   int dtype, int64_t n_new, void *stream)
+{
+    return append_impl(cache, len, k_new, v_new, dtype, n_new, stream, true);
+}
+
+int kvq_hadamard_rotate(const void *x, int dtype, int64_t rows, int32_t head_dim, float *out, void *stream)
+{
+    if (dtype != KVQ_F16 && dtype != KVQ_F32)
+        return KVQ_E_DTYPE;
+    if (rows < 0 || (head_dim != 64 && head_dim != 128 && head_dim != 256))
+        return KVQ_E_SHAPE;
+    if (rows == 0)
+        return KVQ_OK;
+    if (!x || !out)
+        return KVQ_E_NULL;
+    if (!aligned16(x) || !aligned16(out))
+        return KVQ_E_ALIGN;
+    if (rows > ((int64_t)1 << 40) / head_dim || (rows * (head_dim / 8) + 255) / 256 > 0x7fffffff)
+        return KVQ_E_SHAPE;
+    const int64_t n = rows * head_dim;
+    // in place only as fp32 -> fp32 on the same rows
+    if (overlaps(x, n * (dtype == KVQ_F16 ? 2 : 4), out, n * 4) && !(dtype == KVQ_F32 && (const void *)out == x))
+        return KVQ_E_SHAPE;
+    RotateArgs a;
+    a.x = x;
+    a.out = out;
+    a.rows = rows;
+    a.D = head_dim;
+    a.scale = 1.0 / sqrt((double)head_dim);
+    return launch_status(launch_rotate(a, dtype, (hipStream_t)stream));
 }
 
 namespace {

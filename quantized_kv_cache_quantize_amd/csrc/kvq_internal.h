@@ -33,7 +33,17 @@ struct QuantizeArgs {
     int64_t cap;
     int32_t D;
     int32_t G;
+    double rot_scale;  // nonzero: rotate each row by H_D * rot_scale (1 / sqrt(D)) before quantising
 };
+
+struct RotateArgs {
+    const void *x;
+    float *out;
+    int64_t rows;
+    int32_t D;
+    double scale;  // 1 / sqrt(D)
+};
+hipError_t launch_rotate(const RotateArgs &a, int dtype, hipStream_t s);
 
 struct PartialArgs {
     const uint32_t *k_q;

@@ -10,13 +10,18 @@
 // and stores it; the first lane of the group stores the fp16 scale and bias.
 // Loads are 16-byte (fp16) or 2x16-byte (fp32) per lane and consecutive lanes
 // touch consecutive addresses, so both loads and stores coalesce.
+//
+// The rotated variant (fp16 rows) first applies the normalised Hadamard
+// rotation of hadamard_row.h to the row, whose D/8 lanes are consecutive in
+// one wavefront, and quantises the fp32 rounding of the rotated values.
+#include "hadamard_row.h"
 #include "kvq_internal.h"
 #include "quant_rule.h"
 
 namespace kvq {
 namespace {
 
-template <typename T, int LPG>  // LPG = lanes per group = G / 8
+template <typename T, int LPG, bool ROT>  // LPG = lanes per group = G / 8
 __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
 {
     const int which = blockIdx.y;  // 0: K, 1: V
@@ -42,6 +47,17 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
         for (int j = 0; j < 8; ++j)
             x[j] = 0.0f;
     }
+    if constexpr (ROT) {
+        // every lane of the row, past-the-end ones included, joins the shuffles
+        double xd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            xd[j] = (double)x[j];
+        hadamard_row(xd, w, W, a.rot_scale);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = (float)xd[j];
+    }
     // lanes past the end still take part in their group's swaps
     uint16_t sb, bb;
     const uint32_t word = quant::quantize_word<LPG>(x, sb, bb);
@@ -59,7 +75,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
     }
 }
 
-template <typename T>
+template <typename T, bool ROT>
 hipError_t launch_t(const QuantizeArgs &a, hipStream_t s)
 {
     const int64_t total = a.rows * (a.D / 8);
@@ -67,13 +83,13 @@ hipError_t launch_t(const QuantizeArgs &a, hipStream_t s)
     dim3 grid((unsigned)blocks, 2, 1);
     switch (a.G) {
     case 32:
-        hipLaunchKernelGGL((quantize_append_kernel<T, 4>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((quantize_append_kernel<T, 4, ROT>), grid, dim3(256), 0, s, a);
         break;
     case 64:
-        hipLaunchKernelGGL((quantize_append_kernel<T, 8>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((quantize_append_kernel<T, 8, ROT>), grid, dim3(256), 0, s, a);
         break;
     case 128:
-        hipLaunchKernelGGL((quantize_append_kernel<T, 16>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((quantize_append_kernel<T, 16, ROT>), grid, dim3(256), 0, s, a);
         break;
     default:
         return hipErrorInvalidValue;
@@ -81,11 +97,54 @@ hipError_t launch_t(const QuantizeArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// One lane per 8 values of a row: the rotation of hadamard_row.h in float64,
+// rounded once to fp32. A row's lanes read all their values before any lane
+// stores, so out may be x itself when x is fp32.
+template <typename T>
+__global__ __launch_bounds__(256) void hadamard_rotate_kernel(RotateArgs a)
+{
+    const int W = a.D >> 3;
+    const int64_t lane_id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool active = lane_id < a.rows * W;
+    const int64_t row = active ? lane_id / W : 0;
+    const int w = (int)(lane_id % W);
+    float x[8];
+    if (active) {
+        quant::load8<T>(reinterpret_cast<const T *>(a.x) + row * a.D + 8 * w, x);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = 0.0f;
+    }
+    double xd[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        xd[j] = (double)x[j];
+    hadamard_row(xd, w, W, a.scale);
+    if (!active)
+        return;
+    float *o = a.out + row * a.D + 8 * w;
+    *reinterpret_cast<float4 *>(o) = make_float4((float)xd[0], (float)xd[1], (float)xd[2], (float)xd[3]);
+    *reinterpret_cast<float4 *>(o + 4) = make_float4((float)xd[4], (float)xd[5], (float)xd[6], (float)xd[7]);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const QuantizeArgs &a, int dtype, hipStream_t s)
 {
-    return dtype == KVQ_F16 ? launch_t<_Float16>(a, s) : launch_t<float>(a, s);
+    if (a.rot_scale != 0.0)
+        return dtype == KVQ_F16 ? launch_t<_Float16, true>(a, s) : hipErrorInvalidValue;
+    return dtype == KVQ_F16 ? launch_t<_Float16, false>(a, s) : launch_t<float, false>(a, s);
+}
+
+hipError_t launch_rotate(const RotateArgs &a, int dtype, hipStream_t s)
+{
+    const int64_t blocks = (a.rows * (a.D / 8) + 255) / 256;
+    if (dtype == KVQ_F16)
+        hipLaunchKernelGGL((hadamard_rotate_kernel<_Float16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((hadamard_rotate_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace kvq

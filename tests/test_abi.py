@@ -117,6 +117,42 @@ def test_append_validation(L):
     assert _append(L, _cache(capacity=10), length=10, n=0) == OK
 
 
+def _append_rot(L, cache, length=0, k=P, v=P, dtype=0, n=1):
+    return L.kvq_quantize_kv_append_rotated(C.byref(cache) if cache is not None else None, length, k, v, dtype, n,
+                                            None)
+
+
+def test_rotated_append_validation(L):
+    assert _append_rot(L, None) == E_NULL
+    assert _append_rot(L, _cache(head_dim=96)) == E_SHAPE
+    assert _append_rot(L, _cache(v_bias=P + 2)) == E_ALIGN
+    # fp16 rows only: their rotation sums are exact
+    assert _append_rot(L, _cache(), dtype=1) == E_DTYPE
+    assert _append_rot(L, _cache(), dtype=7) == E_DTYPE
+    assert _append_rot(L, _cache(), length=-1) == E_SHAPE
+    assert _append_rot(L, _cache(capacity=10), length=8, n=3) == E_CAP
+    assert _append_rot(L, _cache(), k=None) == E_NULL
+    assert _append_rot(L, _cache(), v=P + 8) == E_ALIGN
+    assert _append_rot(L, _cache(capacity=10), length=10, n=0) == OK
+
+
+def test_rotate_validation(L):
+    rot = L.kvq_hadamard_rotate
+    assert rot(P, 2, 4, 128, P + 4096, None) == E_DTYPE
+    assert rot(P, 0, -1, 128, P + 4096, None) == E_SHAPE
+    assert rot(P, 0, 4, 96, P + 4096, None) == E_SHAPE
+    assert rot(P, 0, 4, 32, P + 4096, None) == E_SHAPE
+    assert rot(P, 0, 0, 128, None, None) == OK  # no rows: no-op
+    assert rot(None, 0, 4, 128, P + 4096, None) == E_NULL
+    assert rot(P, 0, 4, 128, None, None) == E_NULL
+    assert rot(P + 8, 0, 4, 128, P + 4096, None) == E_ALIGN
+    assert rot(P, 1, 4, 128, P + 8, None) == E_ALIGN
+    # overlapping rows: only fp32 in place is allowed
+    assert rot(P, 0, 4, 128, P, None) == E_SHAPE          # fp16 in, fp32 out on the same bytes
+    assert rot(P, 1, 4, 128, P + 512, None) == E_SHAPE    # fp32 partly overlapping
+    assert rot(P, 1, 1 << 40, 128, P + 4096, None) == E_SHAPE
+
+
 def test_partial_validation(L):
     assert _partial(L, None) == E_NULL
     assert _partial(L, _cache(), q=None) == E_NULL

@@ -1,0 +1,156 @@
+"""GPU parity of the Hadamard-rotated cache (the rotation of the blog on
+running Gemma 4 with TurboQuant, its "TurboQuant" section): the rotated
+append must write the cache the oracle writes bit for bit (fp16 rows: the
+rotation sums are exact, so both sides quantise the same fp32 values), the
+rotation kernel must give the oracle's rotation (bit for bit for fp16 rows),
+and attention over a rotated cache with a rotated query, rotated back, must
+match the oracle within the matrix-core tolerance."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+import oracle
+import quantized_kv_cache_quantize_amd as kvq
+from _gpu_common import (META_CANARY, WORD_CANARY, assert_cache_equal, canary_cache, check_attention, host_arrays,
+                         note, run_sdpa, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-4  # the matrix-core gate of test_gpu_sdpa.py
+
+
+def _rot_append_and_check(k, v, length, cap, G=64):
+    B, Hkv, n, D = k.shape
+    gc = canary_cache(B, Hkv, D, cap, G)
+    kvq.quantize_kv_append_rotated(gc, length, to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    oc = oracle.Cache(B, Hkv, D, cap, G)
+    oc.append_rotated(k, v, length)
+    rows = slice(length, length + n)
+    assert_cache_equal(gc, oc, rows)
+    outside = np.ones(cap, dtype=bool)
+    outside[rows] = False
+    for i, a in enumerate(host_arrays(gc)):
+        canary = WORD_CANARY.view(np.uint32) if i < 2 else META_CANARY
+        assert np.all(a[:, :, outside] == canary), "rows outside the append range were written"
+    return gc, oc
+
+
+@pytest.mark.parametrize("B,Hkv,D,G,n,length", [(1, 8, 128, 64, 300, 5), (2, 3, 64, 32, 77, 0),
+                                                 (1, 2, 256, 64, 129, 3), (1, 4, 128, 128, 64, 1),
+                                                 (1, 1, 256, 128, 1, 9)])
+def test_rotated_append_bit_exact(B, Hkv, D, G, n, length):
+    note("rotated append B%d Hkv%d D%d G%d n%d len%d" % (B, Hkv, D, G, n, length))
+    k = kvq_synth.to_f16(kvq_synth.normal((B, Hkv, n, D), [110, B, Hkv, D, G, n, 0]))
+    v = kvq_synth.to_f16(kvq_synth.normal((B, Hkv, n, D), [110, B, Hkv, D, G, n, 1]))
+    _rot_append_and_check(k, v, length, length + n + 3, G)
+
+
+def test_rotated_append_special_rows():
+    note("rotated append special rows")
+    D = 128
+    rows = [np.zeros(D), np.full(D, 3.5), np.full(D, -1e-7), np.linspace(-5000, 5000, D),
+            np.where(np.arange(D) % 9 == 0, 2000.0, 6e-8), (np.arange(D) % 2) * 2.0 ** -20,
+            np.eye(D)[0] * 40000.0, np.eye(D)[D - 1] * -40000.0]
+    k = np.stack(rows).astype(np.float16)[None, None]
+    v = np.stack(rows[::-1]).astype(np.float16)[None, None]
+    _rot_append_and_check(k, v, 2, 12)
+
+
+def test_rotated_decode_appends():
+    note("rotated single-row appends")
+    k = kvq_synth.to_f16(kvq_synth.normal((1, 8, 6, 128), [111, 0]))
+    v = kvq_synth.to_f16(kvq_synth.normal((1, 8, 6, 128), [111, 1]))
+    gc = kvq.Int4KVCache(1, 8, 128, 8, 64, device=torch.device("cuda"))
+    oc = oracle.Cache(1, 8, 128, 8, 64)
+    for t in range(6):
+        kt, vt = np.ascontiguousarray(k[:, :, t:t + 1]), np.ascontiguousarray(v[:, :, t:t + 1])
+        kvq.quantize_kv_append_rotated(gc, t, to_dev(kt), to_dev(vt))
+        oc.append_rotated(kt, vt, t)
+    torch.cuda.synchronize()
+    assert_cache_equal(gc, oc, slice(0, 6))
+
+
+def test_outlier_rotated_append():
+    """The outlier workload's 4096-row append (Student-t keys with boosted
+    channels), rotated, at row 61440 of a 65536-row cache."""
+    note("rotated outlier append 4096 at 61440")
+    _, k, v, _ = kvq_synth.outlier_kv()
+    kn = np.ascontiguousarray(k[:, :, 61440:])
+    vn = np.ascontiguousarray(v[:, :, 61440:])
+    _rot_append_and_check(kn, vn, 61440, 65536)
+
+
+def test_rotated_append_rejects_fp32():
+    note("rotated append fp32 rejected")
+    gc = kvq.Int4KVCache(1, 1, 128, 4, 64, device=torch.device("cuda"))
+    x = torch.zeros((1, 1, 1, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(kvq.KvqError):
+        kvq.quantize_kv_append_rotated(gc, 0, x, x)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("rows", [1, 7, 1000])
+def test_rotate_fp16_bit_exact(D, rows):
+    note("rotate fp16 D%d rows%d" % (D, rows))
+    x = kvq_synth.to_f16(kvq_synth.normal((rows, D), [112, D, rows]) * 30.0)
+    got = kvq.hadamard_rotate(to_dev(x)).cpu().numpy()
+    want = oracle.hadamard(x).astype(np.float32)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rotate_fp32_and_in_place(D):
+    note("rotate fp32 D%d" % D)
+    x = kvq_synth.normal((33, D), [113, D])
+    want = oracle.hadamard(x)
+    xd = to_dev(x)
+    got = kvq.hadamard_rotate(xd).cpu().numpy()
+    assert np.allclose(got, want, rtol=2e-7, atol=1e-7)
+    kvq.hadamard_rotate(xd, out=xd)  # in place
+    assert np.array_equal(xd.cpu().numpy(), got)
+    back = kvq.hadamard_rotate(xd).cpu().numpy()  # its own inverse
+    assert np.allclose(back, x, rtol=1e-6, atol=1e-6)
+
+
+def _rotated_attention(q, k, v, alpha, cap=None, chunk=512, kernel=kvq.KERNEL_AUTO, label=""):
+    B, Hkv, S, D = k.shape
+    gc = kvq.Int4KVCache(B, Hkv, D, cap or S, 64, device=torch.device("cuda"))
+    kvq.quantize_kv_append_rotated(gc, 0, to_dev(k), to_dev(v))
+    qr = kvq.hadamard_rotate(to_dev(q)).cpu().numpy()
+    out, _, _, _ = run_sdpa(gc, S, qr, alpha, chunk=chunk, kernel=kernel)
+    got = kvq.hadamard_rotate(torch.from_numpy(out).cuda()).cpu().numpy()
+    oc = oracle.Cache(B, Hkv, D, cap or S, 64)
+    oc.append_rotated(k, v, 0)
+    assert_cache_equal(gc, oc, slice(0, S))
+    return check_attention(got, oracle.sdpa_rotated(oc, S, q, alpha), REL_L2, label=label)
+
+
+@pytest.mark.parametrize("skv", [1, 700, 4096])
+def test_rotated_attention_llama(skv):
+    note("rotated attention llama skv=%d" % skv)
+    q, k, v, alpha = kvq_synth.llama_layer(skv)
+    _rotated_attention(q, k, v, alpha, label="rotated llama %d" % skv)
+
+
+def test_rotated_attention_outlier():
+    note("rotated attention outlier 8192")
+    q, k, v, alpha = kvq_synth.outlier_kv(total=8192)
+    _rotated_attention(q, k, v, alpha, label="rotated outlier")
+
+
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_WAVE])
+def test_rotated_attention_kernels(kernel):
+    note("rotated attention kernel %d" % kernel)
+    q, k, v, alpha = kvq_synth.llama_layer(1500)
+    _rotated_attention(q, k, v, alpha, kernel=kernel, label="rotated kernel %d" % kernel)
+
+
+def test_rotated_attention_gemma():
+    note("rotated attention gemma D=256")
+    q, k, v, alpha = kvq_synth.gemma_layer(786)
+    _rotated_attention(q, k, v, alpha, label="rotated gemma")
