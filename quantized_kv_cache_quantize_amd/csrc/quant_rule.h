@@ -7,9 +7,10 @@
 // fp16, codes rint((x - bias)/scale) clamped to [0, 15], 0 when scale is 0,
 // -0 stored as +0) is spelled out in include/kvq.h.
 //
-// Bit-exactness: no contraction (a*b+c stays two roundings), division is the
-// correctly rounded IEEE one, rint is round-half-even, and the fp16
-// conversions are the hardware round-to-nearest-even plus a one-ulp step.
+// Bit-exactness: no contraction (a*b+c stays two roundings), every quotient
+// that can change a code is the correctly rounded IEEE one (see
+// quantize_word), rint is round-half-even, and the fp16 conversions are the
+// hardware round-to-nearest-even plus a one-ulp step.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,25 +71,53 @@ __device__ __forceinline__ void load8<float>(const float *p, float (&x)[8])
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// One DPP exchange inside rows of 16 lanes (a bound-checked source lane is
+// always a lane of the same row for the controls used here).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Minimum and maximum over the LPG aligned lanes of a group (LPG in {4, 8,
+// 16}): quad exchanges (lane ^ 1, lane ^ 2), then the mirror inside 8 lanes
+// and inside 16 lanes, each pairing lanes of different halves. The
+// NaN-propagating minimum/maximum need no canonical operands (inputs are
+// finite; a zero's sign is dropped later with the bias and scale).
+template <int LPG>
+__device__ __forceinline__ void group_min_max(float &lo, float &hi)
+{
+    lo = __builtin_elementwise_minimum(lo, dpp_f<0xB1>(lo));  // quad_perm [1,0,3,2]
+    hi = __builtin_elementwise_maximum(hi, dpp_f<0xB1>(hi));
+    lo = __builtin_elementwise_minimum(lo, dpp_f<0x4E>(lo));  // quad_perm [2,3,0,1]
+    hi = __builtin_elementwise_maximum(hi, dpp_f<0x4E>(hi));
+    if constexpr (LPG >= 8) {
+        lo = __builtin_elementwise_minimum(lo, dpp_f<0x141>(lo));  // row_half_mirror
+        hi = __builtin_elementwise_maximum(hi, dpp_f<0x141>(hi));
+    }
+    if constexpr (LPG >= 16) {
+        lo = __builtin_elementwise_minimum(lo, dpp_f<0x140>(lo));  // row_mirror
+        hi = __builtin_elementwise_maximum(hi, dpp_f<0x140>(hi));
+    }
+}
+
 // Quantise one word of a group whose G values are held by LPG = G/8
-// consecutive lanes (every lane of the group must call this together: the
-// group's min and max meet through lane swaps). Returns the packed codes and
-// the group's fp16 scale and bias bit patterns (the same on every lane).
+// consecutive, aligned lanes (every lane of the group must call this
+// together: the group's min and max meet through lane exchanges). Returns the
+// packed codes and the group's fp16 scale and bias bit patterns (the same on
+// every lane).
 template <int LPG>
 __device__ __forceinline__ uint32_t quantize_word(const float (&x)[8], uint16_t &scale_bits, uint16_t &bias_bits)
 {
 #pragma clang fp contract(off)
+    static_assert(LPG == 4 || LPG == 8 || LPG == 16, "groups of 32, 64 or 128 values");
     float lo = x[0], hi = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
-        lo = fminf(lo, x[j]);
-        hi = fmaxf(hi, x[j]);
+        lo = __builtin_elementwise_minimum(lo, x[j]);
+        hi = __builtin_elementwise_maximum(hi, x[j]);
     }
-#pragma unroll
-    for (int off = 1; off < LPG; off <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, off));
-        hi = fmaxf(hi, __shfl_xor(hi, off));
-    }
+    group_min_max<LPG>(lo, hi);
     uint16_t bb = f16_round_down(lo);
     if (bb == 0x8000)
         bb = 0;
@@ -100,17 +129,32 @@ __device__ __forceinline__ uint32_t quantize_word(const float (&x)[8], uint16_t 
         sb = 0;
     const float sf = h_value(sb);
 
-    uint32_t word = 0;
-    if (sf != 0.0f) {
+    // The code is rint of the correctly rounded quotient u = (x - bias) /
+    // scale, which lies in [0, 16). The product (x - bias) * rcp(scale)
+    // (v_rcp_f32, 1 ulp) is within 16 * 1.5 * 2^-23 of the exact quotient and
+    // u within 16 * 2^-24 of it, so both round to the same integer unless the
+    // product lies within 3.8e-6 of a half-integer. When some lane of the
+    // wavefront has a product that close (margin 2^-16), the wavefront
+    // recomputes its codes from correctly rounded quotients.
+    float r[8];
+    const float rs = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+    bool near = false;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float diff = x[j] - bf;
-            const float u = diff / sf;
-            float r = rintf(u);
-            r = fminf(fmaxf(r, 0.0f), 15.0f);
-            word |= (uint32_t)r << (4 * j);
-        }
+    for (int j = 0; j < 8; ++j) {
+        const float u = (x[j] - bf) * rs;
+        r[j] = rintf(u);
+        near |= fabsf(u - r[j]) > 0.5f - 0x1p-16f;
     }
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        asm volatile("" ::: "memory");  // a real branch: the divisions run only here
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            r[j] = sf != 0.0f ? rintf((x[j] - bf) / sf) : 0.0f;
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        word |= (uint32_t)__builtin_amdgcn_fmed3f(r[j], 0.0f, 15.0f) << (4 * j);
     scale_bits = sb;
     bias_bits = bb;
     return word;

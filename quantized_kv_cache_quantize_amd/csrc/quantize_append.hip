@@ -30,14 +30,15 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
     uint16_t *dscale = which ? a.v_scale : a.k_scale;
     uint16_t *dbias = which ? a.v_bias : a.k_bias;
 
-    const int W = a.D >> 3;  // words per row
+    const int W = a.D >> 3;            // words per row, a power of two
+    const int lw = __builtin_ctz(W);   // (shifts, not 64-bit divisions)
     const int64_t lane_id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = a.rows * W;
     // Lanes past the end still take part in the swaps of their (partial)
     // group; groups never straddle the end because W is a multiple of LPG.
     const bool active = lane_id < total;
-    const int64_t row = active ? lane_id / W : 0;
-    const int w = active ? (int)(lane_id - row * W) : 0;
+    const int64_t row = active ? lane_id >> lw : 0;
+    const int w = (int)(lane_id & (W - 1));
 
     float x[8];
     if (active) {
@@ -63,12 +64,21 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
     const uint32_t word = quant::quantize_word<LPG>(x, sb, bb);
     if (!active)
         return;
-    const int64_t bh = row / a.n_new;
-    const int64_t t = row - bh * a.n_new;
+    // (batch * KV head, new row) of this row: a 32-bit division whenever the
+    // row count fits (a 64-bit one costs several times as many instructions)
+    int64_t bh, t;
+    if (a.rows <= (int64_t)0xffffffff) {
+        const uint32_t r = (uint32_t)row, n = (uint32_t)a.n_new, qt = r / n;
+        bh = qt;
+        t = r - qt * n;
+    } else {
+        bh = row / a.n_new;
+        t = row - bh * a.n_new;
+    }
     const int64_t crow = bh * a.cap + a.len + t;
-    dq[crow * W + w] = word;
+    dq[(crow << lw) + w] = word;
     if ((w & (LPG - 1)) == 0) {
-        const int NG = a.D / a.G;
+        const int NG = W / LPG;
         const int g = w / LPG;
         dscale[crow * NG + g] = sb;
         dbias[crow * NG + g] = bb;
@@ -104,10 +114,11 @@ template <typename T>
 __global__ __launch_bounds__(256) void hadamard_rotate_kernel(RotateArgs a)
 {
     const int W = a.D >> 3;
+    const int lw = __builtin_ctz(W);
     const int64_t lane_id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool active = lane_id < a.rows * W;
-    const int64_t row = active ? lane_id / W : 0;
-    const int w = (int)(lane_id % W);
+    const int64_t row = active ? lane_id >> lw : 0;
+    const int w = (int)(lane_id & (W - 1));
     float x[8];
     if (active) {
         quant::load8<T>(reinterpret_cast<const T *>(a.x) + row * a.D + 8 * w, x);

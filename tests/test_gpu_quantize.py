@@ -77,6 +77,35 @@ def test_special_values(dt):
     _append_and_check(k, v, 0, x.shape[0])
 
 
+def _boundary_rows(D=128, G=64):
+    """Groups whose quotients (x - bias) / scale sit on and right next to the
+    half-integers where rint changes the code: each group holds its bias b
+    and b + 15 s (so the scale is s) and values b + (k + 1/2 + delta) s for
+    delta in {0, +-2^-22 .. +-2^-12}, in fp32; several scales, some of them
+    not powers of two."""
+    rows = []
+    deltas = [0.0] + [sgn * 2.0 ** -e for e in (22, 20, 18, 16, 14, 12) for sgn in (1, -1)]
+    for si, s in enumerate([0.1, 0.3, 1.7, 3e-3, 7.0, 1.0, 0.0625]):
+        s = float(np.float16(s))
+        b = float(np.float16(-0.37 * (si + 1)))
+        row = np.empty(D, dtype=np.float64)
+        for g in range(D // G):
+            vals = [b, b + 15 * s]
+            k = 0
+            while len(vals) < G:
+                vals.append(b + (k % 15 + 0.5 + deltas[k % len(deltas)]) * s)
+                k += 1
+            row[g * G:(g + 1) * G] = vals
+        rows.append(row)
+    return np.array(rows, dtype=np.float32)
+
+
+def test_rounding_boundaries():
+    note("quantize rounding boundaries fp32")
+    x = _boundary_rows()
+    _append_and_check(x[None, None], x[None, None, ::-1].copy(), 1, x.shape[0] + 2)
+
+
 def test_decode_appends_one_row_at_a_time():
     note("quantize single-row appends")
     k = kvq_synth.to_f16(kvq_synth.normal((1, 8, 6, 128), [71, 1]))
