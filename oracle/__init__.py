@@ -1,4 +1,5 @@
-"""CPU oracle for int4 group-affine KV quantisation and decode attention.
+"""CPU oracle for int4 (and int8) group-affine KV quantisation and decode
+attention.
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product library and its Python
@@ -49,14 +50,16 @@ def _load():
     lib.oracle_f16_round_n.argtypes = [f32p, C.c_int64, C.c_int, u16p]
     lib.oracle_quantize_group.restype = None
     lib.oracle_quantize_group.argtypes = [f32p, C.c_int, u16p, u16p, u8p]
-    lib.oracle_pack_row.argtypes = [u8p, C.c_int, u32p]
-    lib.oracle_unpack_row.argtypes = [u32p, C.c_int, u8p]
+    lib.oracle_quantize_group_bits.restype = None
+    lib.oracle_quantize_group_bits.argtypes = [f32p, C.c_int, C.c_int, u16p, u16p, u8p]
+    lib.oracle_pack_row_bits.argtypes = [u8p, C.c_int, C.c_int, u32p]
+    lib.oracle_unpack_row_bits.argtypes = [u32p, C.c_int, C.c_int, u8p]
     lib.oracle_quantize_rows.restype = C.c_int
-    lib.oracle_quantize_rows.argtypes = [f32p, C.c_int64, C.c_int, C.c_int, u32p, u16p, u16p]
+    lib.oracle_quantize_rows.argtypes = [f32p, C.c_int64, C.c_int, C.c_int, C.c_int, u32p, u16p, u16p]
     lib.oracle_dequantize_rows.restype = None
-    lib.oracle_dequantize_rows.argtypes = [u32p, u16p, u16p, C.c_int64, C.c_int, C.c_int, f64p]
-    cache_args = [u32p, u32p, u16p, u16p, u16p, u16p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
-                  f64p, C.c_int, C.c_double]
+    lib.oracle_dequantize_rows.argtypes = [u32p, u16p, u16p, C.c_int64, C.c_int, C.c_int, C.c_int, f64p]
+    cache_args = [u32p, u32p, u16p, u16p, u16p, u16p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64,
+                  C.c_int64, f64p, C.c_int, C.c_double]
     lib.oracle_sdpa.restype = C.c_int
     lib.oracle_sdpa.argtypes = cache_args + [f64p, C.c_int]
     lib.oracle_sdpa_partials.restype = C.c_int
@@ -114,76 +117,97 @@ def f16_ru(x):
 
 # -------------------------------------------------------------- quantiser
 
-def quantize_group(x: np.ndarray):
-    """One group -> (codes uint8[G], scale bits, bias bits). Group-affine int4
-    with a scale and a bias per group ("Background: Why TurboQuant Fails on
-    Gemma 4"; the README's lesson on asymmetric int4)."""
+BITS = (4, 8)
+
+
+def _check_bits(bits):
+    if bits not in BITS:
+        raise ValueError("bits must be 4 or 8, got %r" % (bits,))
+    return 32 // bits  # codes per word
+
+
+def quantize_group(x: np.ndarray, bits: int = 4):
+    """One group -> (codes uint8[G], scale bits, bias bits). Group-affine
+    quantisation with a scale and a bias per group ("Background: Why
+    TurboQuant Fails on Gemma 4"; the README's lesson on asymmetric int4):
+    codes 0..15 for bits=4, 0..255 for the 8-bit variant (the Gemma page's
+    "What I Tried" table lists int8 KV; the blog's driver takes 4 or 8 KV
+    bits)."""
     lib = _load()
+    _check_bits(bits)
     x = np.ascontiguousarray(x, dtype=np.float32).ravel()
     codes = np.zeros(x.size, dtype=np.uint8)
     s = C.c_uint16()
     b = C.c_uint16()
-    lib.oracle_quantize_group(_p(x, C.c_float), x.size, C.byref(s), C.byref(b), _p(codes, C.c_uint8))
+    lib.oracle_quantize_group_bits(_p(x, C.c_float), x.size, bits, C.byref(s), C.byref(b), _p(codes, C.c_uint8))
     return codes, int(s.value), int(b.value)
 
 
-def pack_row(codes: np.ndarray) -> np.ndarray:
-    """Codes of one row -> uint32 words, eight per word, lowest nibble first
-    ("What I Built Instead": masks 0xF, 0xF0, 0xF00, 0xF000)."""
+def pack_row(codes: np.ndarray, bits: int = 4) -> np.ndarray:
+    """Codes of one row -> uint32 words, 32/bits per word, lowest field first
+    ("What I Built Instead": masks 0xF, 0xF0, 0xF00, 0xF000; bytes for the
+    8-bit variant)."""
     lib = _load()
+    P = _check_bits(bits)
     c = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
-    w = np.zeros(c.size // 8, dtype=np.uint32)
-    lib.oracle_pack_row(_p(c, C.c_uint8), c.size, _p(w, C.c_uint32))
+    w = np.zeros(c.size // P, dtype=np.uint32)
+    lib.oracle_pack_row_bits(_p(c, C.c_uint8), c.size, bits, _p(w, C.c_uint32))
     return w
 
 
-def unpack_row(words: np.ndarray) -> np.ndarray:
+def unpack_row(words: np.ndarray, bits: int = 4) -> np.ndarray:
     lib = _load()
+    P = _check_bits(bits)
     w = np.ascontiguousarray(words, dtype=np.uint32).ravel()
-    c = np.zeros(w.size * 8, dtype=np.uint8)
-    lib.oracle_unpack_row(_p(w, C.c_uint32), c.size, _p(c, C.c_uint8))
+    c = np.zeros(w.size * P, dtype=np.uint8)
+    lib.oracle_unpack_row_bits(_p(w, C.c_uint32), c.size, bits, _p(c, C.c_uint8))
     return c
 
 
-def quantize_rows(x: np.ndarray, group: int = 64):
+def quantize_rows(x: np.ndarray, group: int = 64, bits: int = 4):
     """x[..., D] (fp16 or fp32; widened exactly to fp32) -> (words uint32[...,
-    D/8], scale uint16[..., D/G], bias uint16[..., D/G])."""
+    D*bits/32], scale uint16[..., D/G], bias uint16[..., D/G])."""
     lib = _load()
+    P = _check_bits(bits)
     x32 = np.ascontiguousarray(x, dtype=np.float32)
     D = x32.shape[-1]
     rows = x32.size // D
     lead = x32.shape[:-1]
-    words = np.zeros(lead + (D // 8,), dtype=np.uint32)
+    words = np.zeros(lead + (D // P,), dtype=np.uint32)
     scale = np.zeros(lead + (D // group,), dtype=np.uint16)
     bias = np.zeros(lead + (D // group,), dtype=np.uint16)
-    rc = lib.oracle_quantize_rows(_p(x32, C.c_float), rows, D, group, _p(words, C.c_uint32),
+    rc = lib.oracle_quantize_rows(_p(x32, C.c_float), rows, D, group, bits, _p(words, C.c_uint32),
                                   _p(scale, C.c_uint16), _p(bias, C.c_uint16))
     if rc != 0:
         raise ValueError("oracle_quantize_rows: bad shape D=%d G=%d" % (D, group))
     return words, scale, bias
 
 
-def dequantize_rows(words: np.ndarray, scale: np.ndarray, bias: np.ndarray, group: int = 64) -> np.ndarray:
+def dequantize_rows(words: np.ndarray, scale: np.ndarray, bias: np.ndarray, group: int = 64,
+                    bits: int = 4) -> np.ndarray:
     """Packed rows -> float64 values code * scale + bias (exact in float64)."""
     lib = _load()
+    P = _check_bits(bits)
     w = np.ascontiguousarray(words, dtype=np.uint32)
     s = np.ascontiguousarray(scale, dtype=np.uint16)
     b = np.ascontiguousarray(bias, dtype=np.uint16)
-    D = w.shape[-1] * 8
+    D = w.shape[-1] * P
     rows = w.size // w.shape[-1]
     out = np.zeros(w.shape[:-1] + (D,), dtype=np.float64)
-    lib.oracle_dequantize_rows(_p(w, C.c_uint32), _p(s, C.c_uint16), _p(b, C.c_uint16), rows, D, group,
+    lib.oracle_dequantize_rows(_p(w, C.c_uint32), _p(s, C.c_uint16), _p(b, C.c_uint16), rows, D, group, bits,
                                _p(out, C.c_double))
     return out
 
 
 class Cache:
     """Host copy of one layer's quantised cache in the oracle's layout:
-    words [B][Hkv][cap][D/8]; scale/bias [B][Hkv][cap][D/G] (fp16 bits)."""
+    words [B][Hkv][cap][D*bits/32]; scale/bias [B][Hkv][cap][D/G] (fp16
+    bits)."""
 
-    def __init__(self, B, Hkv, D, cap, group=64):
-        self.B, self.Hkv, self.D, self.cap, self.G = B, Hkv, D, cap, group
-        self.k_q = np.zeros((B, Hkv, cap, D // 8), dtype=np.uint32)
+    def __init__(self, B, Hkv, D, cap, group=64, bits=4):
+        P = _check_bits(bits)
+        self.B, self.Hkv, self.D, self.cap, self.G, self.bits = B, Hkv, D, cap, group, bits
+        self.k_q = np.zeros((B, Hkv, cap, D // P), dtype=np.uint32)
         self.v_q = np.zeros_like(self.k_q)
         self.k_scale = np.zeros((B, Hkv, cap, D // group), dtype=np.uint16)
         self.k_bias = np.zeros_like(self.k_scale)
@@ -195,7 +219,7 @@ class Cache:
         n = k.shape[2]
         assert length + n <= self.cap
         for src, wq, sc, bi in ((k, self.k_q, self.k_scale, self.k_bias), (v, self.v_q, self.v_scale, self.v_bias)):
-            w, s, b = quantize_rows(src, self.G)
+            w, s, b = quantize_rows(src, self.G, self.bits)
             wq[:, :, length:length + n] = w
             sc[:, :, length:length + n] = s
             bi[:, :, length:length + n] = b
@@ -214,7 +238,7 @@ class Cache:
     def _args(self):
         return (_p(self.k_q, C.c_uint32), _p(self.v_q, C.c_uint32), _p(self.k_scale, C.c_uint16),
                 _p(self.k_bias, C.c_uint16), _p(self.v_scale, C.c_uint16), _p(self.v_bias, C.c_uint16),
-                self.B, self.Hkv, self.D, self.G, self.cap)
+                self.B, self.Hkv, self.D, self.G, self.bits, self.cap)
 
 
 def sdpa(cache: Cache, skv: int, q: np.ndarray, alpha: float, nthreads: int | None = None) -> np.ndarray:

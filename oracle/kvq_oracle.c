@@ -33,7 +33,11 @@
  *    representable range [bias, bias + 15 * scale].
  *  - Packing: dimension d of a row goes to word d / 8, bits 4 * (d % 8).
  *  - Cache layout: words [B][Hkv][cap][D/8], scale and bias [B][Hkv][cap][D/G]
- *    (fp16 bit patterns), one row per token.
+ *    (fp16 bits), one row per token.
+ *  - 8-bit variant (the Gemma page's "What I Tried" table lists an int8 KV
+ *    cache; the blog's decode driver takes 4 or 8 KV bits): the same rule
+ *    with 255 in place of 15, codes 0..255, four per word, dimension d at
+ *    word d / 4, bits 8 * (d % 4); words [B][Hkv][cap][D/4].
  *  - GQA: query head h reads KV head h / (Hq / Hkv).
  *  - Attention: o = sum_t softmax_t(alpha * q . k^_t) v^_t over all Skv rows,
  *    with k^ = code * scale + bias, evaluated in float64 with an exact
@@ -136,9 +140,13 @@ uint16_t oracle_f16_ru(float x)
 
 /* ------------------------------------------------------------- quantiser */
 
-/* One group of G values -> G codes in 0..15 plus fp16 scale and bias. */
-void oracle_quantize_group(const float *x, int G, uint16_t *scale_out, uint16_t *bias_out, uint8_t *codes)
+/* One group of G values -> G codes in 0..L plus fp16 scale and bias, with
+ * L = 2^bits - 1: 15 for the int4 cache, 255 for the int8 variant (the same
+ * affine rule with 255 steps; reading for the pages' 8-bit KV option). */
+void oracle_quantize_group_bits(const float *x, int G, int bits, uint16_t *scale_out, uint16_t *bias_out,
+                                uint8_t *codes)
 {
+    const float levels = (float)((1 << bits) - 1);
     float lo = x[0], hi = x[0];
     for (int j = 1; j < G; ++j) {
         if (x[j] < lo)
@@ -151,7 +159,7 @@ void oracle_quantize_group(const float *x, int G, uint16_t *scale_out, uint16_t 
         b = 0x0000;
     float bf = (float)oracle_f16_to_f64(b);
     float range = hi - bf;      /* fp32, round to nearest */
-    float s32 = range / 15.0f;  /* fp32, correctly rounded */
+    float s32 = range / levels; /* fp32, correctly rounded */
     uint16_t s = oracle_f16_ru(s32);
     if (s == 0x8000) /* hi - bias is -0 only when every value is -0 */
         s = 0x0000;
@@ -164,8 +172,8 @@ void oracle_quantize_group(const float *x, int G, uint16_t *scale_out, uint16_t 
             float r = rintf(u);
             if (r < 0.0f)
                 r = 0.0f;
-            if (r > 15.0f)
-                r = 15.0f;
+            if (r > levels)
+                r = levels;
             q = (int)r;
         }
         codes[j] = (uint8_t)q;
@@ -174,30 +182,46 @@ void oracle_quantize_group(const float *x, int G, uint16_t *scale_out, uint16_t 
     *bias_out = b;
 }
 
-/* codes[D] (0..15) -> words[D/8]; dimension d at word d/8, bits 4*(d%8) */
-void oracle_pack_row(const uint8_t *codes, int D, uint32_t *words)
+void oracle_quantize_group(const float *x, int G, uint16_t *scale_out, uint16_t *bias_out, uint8_t *codes)
 {
-    for (int w = 0; w < D / 8; ++w) {
+    oracle_quantize_group_bits(x, G, 4, scale_out, bias_out, codes);
+}
+
+/* codes[D] -> words[D*bits/32]: P = 32/bits codes per word, dimension d at
+ * word d/P, bits bits*(d%P) (lowest field first, as the nibble masks of the
+ * int4 kernel read; the int8 variant packs bytes the same way) */
+void oracle_pack_row_bits(const uint8_t *codes, int D, int bits, uint32_t *words)
+{
+    const int P = 32 / bits;
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int w = 0; w < D / P; ++w) {
         uint32_t word = 0;
-        for (int j = 0; j < 8; ++j)
-            word |= (uint32_t)(codes[8 * w + j] & 0xF) << (4 * j);
+        for (int j = 0; j < P; ++j)
+            word |= ((uint32_t)codes[P * w + j] & mask) << (bits * j);
         words[w] = word;
     }
 }
 
-void oracle_unpack_row(const uint32_t *words, int D, uint8_t *codes)
+void oracle_unpack_row_bits(const uint32_t *words, int D, int bits, uint8_t *codes)
 {
+    const int P = 32 / bits;
+    const uint32_t mask = (1u << bits) - 1u;
     for (int d = 0; d < D; ++d)
-        codes[d] = (uint8_t)((words[d / 8] >> (4 * (d % 8))) & 0xF);
+        codes[d] = (uint8_t)((words[d / P] >> (bits * (d % P))) & mask);
 }
 
+void oracle_pack_row(const uint8_t *codes, int D, uint32_t *words) { oracle_pack_row_bits(codes, D, 4, words); }
+
+void oracle_unpack_row(const uint32_t *words, int D, uint8_t *codes) { oracle_unpack_row_bits(words, D, 4, codes); }
+
 /* Quantise `rows` rows of D fp32 values (row-major) into packed words
- * [rows][D/8] and fp16 scale/bias [rows][D/G]. */
-int oracle_quantize_rows(const float *x, int64_t rows, int D, int G, uint32_t *words, uint16_t *scale,
+ * [rows][D*bits/32] and fp16 scale/bias [rows][D/G]. */
+int oracle_quantize_rows(const float *x, int64_t rows, int D, int G, int bits, uint32_t *words, uint16_t *scale,
                          uint16_t *bias)
 {
-    if (D <= 0 || G <= 0 || D % G != 0 || D % 8 != 0 || G > 1024)
+    if (D <= 0 || G <= 0 || D % G != 0 || D % 8 != 0 || G > 1024 || (bits != 4 && bits != 8))
         return -1;
+    const int WR = D * bits / 32;
     uint8_t codes[1024];
     uint8_t rowc[4096];
     if (D > 4096)
@@ -205,21 +229,23 @@ int oracle_quantize_rows(const float *x, int64_t rows, int D, int G, uint32_t *w
     for (int64_t r = 0; r < rows; ++r) {
         const float *xr = x + r * D;
         for (int g = 0; g < D / G; ++g) {
-            oracle_quantize_group(xr + g * G, G, &scale[r * (D / G) + g], &bias[r * (D / G) + g], codes);
+            oracle_quantize_group_bits(xr + g * G, G, bits, &scale[r * (D / G) + g], &bias[r * (D / G) + g],
+                                       codes);
             memcpy(rowc + g * G, codes, (size_t)G);
         }
-        oracle_pack_row(rowc, D, words + r * (D / 8));
+        oracle_pack_row_bits(rowc, D, bits, words + r * WR);
     }
     return 0;
 }
 
 /* words/scale/bias of `rows` rows -> float64 values code*scale + bias */
 void oracle_dequantize_rows(const uint32_t *words, const uint16_t *scale, const uint16_t *bias, int64_t rows,
-                            int D, int G, double *out)
+                            int D, int G, int bits, double *out)
 {
     uint8_t rowc[4096];
+    const int WR = D * bits / 32;
     for (int64_t r = 0; r < rows; ++r) {
-        oracle_unpack_row(words + r * (D / 8), D, rowc);
+        oracle_unpack_row_bits(words + r * WR, D, bits, rowc);
         for (int d = 0; d < D; ++d) {
             double s = oracle_f16_to_f64(scale[r * (D / G) + d / G]);
             double b = oracle_f16_to_f64(bias[r * (D / G) + d / G]);
@@ -233,7 +259,7 @@ void oracle_dequantize_rows(const uint32_t *words, const uint16_t *scale, const 
 typedef struct {
     const uint32_t *k_q, *v_q;
     const uint16_t *k_scale, *k_bias, *v_scale, *v_bias;
-    int B, Hkv, Hq, D, G;
+    int B, Hkv, Hq, D, G, bits;
     int64_t cap, skv;
     const double *q; /* [B][Hq][D] */
     double alpha;
@@ -247,13 +273,13 @@ typedef struct {
 /* Dequantised row t of KV head (b, kvh) of one of the two caches. */
 static void deq_row(const attn_job *J, int which_v, int b, int kvh, int64_t t, double *row)
 {
-    int D = J->D, G = J->G;
+    int D = J->D, G = J->G, bits = J->bits, P = 32 / bits;
     int64_t base = ((int64_t)b * J->Hkv + kvh) * J->cap + t;
-    const uint32_t *w = (which_v ? J->v_q : J->k_q) + base * (D / 8);
+    const uint32_t *w = (which_v ? J->v_q : J->k_q) + base * (D / P);
     const uint16_t *sc = (which_v ? J->v_scale : J->k_scale) + base * (D / G);
     const uint16_t *bi = (which_v ? J->v_bias : J->k_bias) + base * (D / G);
     for (int d = 0; d < D; ++d) {
-        unsigned code = (w[d / 8] >> (4 * (d % 8))) & 0xF;
+        unsigned code = (w[d / P] >> (bits * (d % P))) & ((1u << bits) - 1u);
         row[d] = (double)code * oracle_f16_to_f64(sc[d / G]) + oracle_f16_to_f64(bi[d / G]);
     }
 }
@@ -368,13 +394,15 @@ static int run_attention(attn_job *J, int nthreads)
 
 /* Exact decode attention: out[B][Hq][D] (float64). */
 int oracle_sdpa(const uint32_t *k_q, const uint32_t *v_q, const uint16_t *k_scale, const uint16_t *k_bias,
-                const uint16_t *v_scale, const uint16_t *v_bias, int B, int Hkv, int D, int G, int64_t cap,
+                const uint16_t *v_scale, const uint16_t *v_bias, int B, int Hkv, int D, int G, int bits, int64_t cap,
                 int64_t skv, const double *q, int Hq, double alpha, double *out, int nthreads)
 {
+    if (bits != 4 && bits != 8)
+        return -1;
     attn_job J;
     memset(&J, 0, sizeof J);
     J.k_q = k_q; J.v_q = v_q; J.k_scale = k_scale; J.k_bias = k_bias; J.v_scale = v_scale; J.v_bias = v_bias;
-    J.B = B; J.Hkv = Hkv; J.Hq = Hq; J.D = D; J.G = G; J.cap = cap; J.skv = skv;
+    J.B = B; J.Hkv = Hkv; J.Hq = Hq; J.D = D; J.G = G; J.bits = bits; J.cap = cap; J.skv = skv;
     J.q = q; J.alpha = alpha; J.chunk = 0; J.out = out;
     return run_attention(&J, nthreads);
 }
@@ -382,15 +410,15 @@ int oracle_sdpa(const uint32_t *k_q, const uint32_t *v_q, const uint16_t *k_scal
 /* Split-K partials per chunk of `chunk` rows (the last chunk is shorter). */
 int oracle_sdpa_partials(const uint32_t *k_q, const uint32_t *v_q, const uint16_t *k_scale,
                          const uint16_t *k_bias, const uint16_t *v_scale, const uint16_t *v_bias, int B, int Hkv,
-                         int D, int G, int64_t cap, int64_t skv, const double *q, int Hq, double alpha,
+                         int D, int G, int bits, int64_t cap, int64_t skv, const double *q, int Hq, double alpha,
                          int64_t chunk, double *part_m, double *part_l, double *part_acc, int nthreads)
 {
-    if (chunk <= 0)
+    if (chunk <= 0 || (bits != 4 && bits != 8))
         return -1;
     attn_job J;
     memset(&J, 0, sizeof J);
     J.k_q = k_q; J.v_q = v_q; J.k_scale = k_scale; J.k_bias = k_bias; J.v_scale = v_scale; J.v_bias = v_bias;
-    J.B = B; J.Hkv = Hkv; J.Hq = Hq; J.D = D; J.G = G; J.cap = cap; J.skv = skv;
+    J.B = B; J.Hkv = Hkv; J.Hq = Hq; J.D = D; J.G = G; J.bits = bits; J.cap = cap; J.skv = skv;
     J.q = q; J.alpha = alpha; J.chunk = chunk;
     J.part_m = part_m; J.part_l = part_l; J.part_acc = part_acc;
     return run_attention(&J, nthreads);
