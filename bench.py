@@ -65,22 +65,22 @@ def measured_traffic(skv: int, chunk: int, kernel: str):
         return None
 
 
-def layer_bytes(skv: int) -> int:
-    return HKV * skv * (D // 2 + 4 * (D // G)) * 2  # K and V: codes + fp16 scale + fp16 bias
+def layer_bytes(skv: int, bits: int = 4) -> int:
+    return HKV * skv * (D * bits // 8 + 4 * (D // G)) * 2  # K and V: codes + fp16 scale + fp16 bias
 
 
-def append_bytes() -> int:
-    return 2 * B * HKV * D * 2 + 2 * B * HKV * (D // 2 + 4 * (D // G))  # fp16 rows in, packed row out
+def append_bytes(bits: int = 4) -> int:
+    return 2 * B * HKV * D * 2 + 2 * B * HKV * (D * bits // 8 + 4 * (D // G))  # fp16 rows in, packed row out
 
 
-def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 1234):
-    n_layers = max(2, math.ceil(pool_bytes / layer_bytes(skv)))
+def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 1234, bits: int = 4):
+    n_layers = max(2, math.ceil(pool_bytes / layer_bytes(skv, bits)))
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     pool = []
     for i in range(n_layers):
         gen.manual_seed(seed * 1000003 + skv * 131 + i)
-        cache = kvq.Int4KVCache(B, HKV, D, skv, G, device=dev)
+        cache = kvq.QuantKVCache(B, HKV, D, skv, G, device=dev, bits=bits)
         # fill in slabs so the fp16 staging stays small
         slab = 16384
         for t0 in range(0, skv, slab):
@@ -133,8 +133,8 @@ def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"
             kvq.hadamard_rotate(L["out"], out=L["out"], stream=stream)
 
 
-def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused"):
-    pool = make_pool(kvq, torch, skv, pool_bytes, chunk)
+def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused", bits=4):
+    pool = make_pool(kvq, torch, skv, pool_bytes, chunk, bits=bits)
     run_steps(kvq, torch, pool, skv, chunk, kernel, warmup, step=step)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -152,7 +152,7 @@ def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step=
     kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
     res = dict(skv=skv, ms_per_step=ms_per_step, partial_ms_avg=sum(kern_ms) / len(kern_ms),
                partial_ms_p10=kern_ms[len(kern_ms) // 10], partial_ms_p90=kern_ms[(9 * len(kern_ms)) // 10],
-               pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv) / 1e6)
+               pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv, bits) / 1e6)
     last = pool[-1]
     del pool
     return res, last
@@ -161,7 +161,7 @@ def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step=
 APPEND_ROWS, APPEND_LEN, APPEND_CAP = 4096, 61440, 65536  # the outlier workload's bulk append
 
 
-def time_bulk_append(kvq, torch, rotated: bool, reps: int = 40, n_inputs: int = 20):
+def time_bulk_append(kvq, torch, rotated: bool, reps: int = 40, n_inputs: int = 20, bits: int = 4):
     """Bulk append of the outlier workload's shape (4096 fp16 rows per KV head
     at row 61440 of a 65536-row cache), plain or Hadamard-rotated, over
     n_inputs distinct input sets (336 MB, more than the Infinity Cache).
@@ -171,7 +171,7 @@ def time_bulk_append(kvq, torch, rotated: bool, reps: int = 40, n_inputs: int = 
     gen.manual_seed(777)
     inputs = [(torch.randn((B, HKV, APPEND_ROWS, D), generator=gen, device=dev).half(),
                torch.randn((B, HKV, APPEND_ROWS, D), generator=gen, device=dev).half()) for _ in range(n_inputs)]
-    cache = kvq.Int4KVCache(B, HKV, D, APPEND_CAP, G, device=dev)
+    cache = kvq.QuantKVCache(B, HKV, D, APPEND_CAP, G, device=dev, bits=bits)
     fn = kvq.quantize_kv_append_rotated if rotated else kvq.quantize_kv_append
     for i in range(5):
         fn(cache, APPEND_LEN, *inputs[i % n_inputs])
@@ -200,9 +200,9 @@ def time_bulk_append(kvq, torch, rotated: bool, reps: int = 40, n_inputs: int = 
     return sorted(per)[len(per) // 2]
 
 
-def bulk_append_bytes() -> int:
+def bulk_append_bytes(bits: int = 4) -> int:
     rows = B * HKV * APPEND_ROWS
-    return 2 * rows * D * 2 + 2 * rows * (D // 2 + 4 * (D // G))  # fp16 K and V in, packed rows out
+    return 2 * rows * D * 2 + 2 * rows * (D * bits // 8 + 4 * (D // G))  # fp16 K and V in, packed rows out
 
 
 def cpu_baseline(kvq, torch, entry, skv):
@@ -212,7 +212,7 @@ def cpu_baseline(kvq, torch, entry, skv):
     import oracle
 
     cache = entry["cache"]
-    oc = oracle.Cache(B, HKV, D, skv, G)
+    oc = oracle.Cache(B, HKV, D, skv, G, bits=cache.bits)
     oc.k_q[...] = cache.k_q.cpu().numpy().view(np.uint32)
     oc.v_q[...] = cache.v_q.cpu().numpy().view(np.uint32)
     oc.k_scale[...] = cache.k_scale.cpu().numpy().view(np.uint16)
@@ -229,7 +229,7 @@ def cpu_baseline(kvq, torch, entry, skv):
     out = kvq.sdpa_int4(cache, skv, entry["q"], alpha)
     torch.cuda.synchronize()
     err = float(np.abs(out.cpu().numpy() - ref).max())
-    return dict(value=layer_bytes(skv) / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+    return dict(value=layer_bytes(skv, cache.bits) / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
                 sample="one full layer-call (64 q-heads, Skv=%d) of the float64 oracle, %.2f s wall" % (skv, dt),
                 seconds=dt, max_abs_err_vs_gpu=err)
 
@@ -251,6 +251,8 @@ def main():
     ap.add_argument("--step", choices=["fused", "unfused", "rotated"], default="fused",
                     help="fused: kvq_decode_step (append inside the attention kernel, then the reduce); "
                          "unfused: append, partial and reduce as three calls")
+    ap.add_argument("--bits", type=int, choices=[4, 8], default=4,
+                    help="bits per cached code of the headline run (8: the int8 cache, vector-ALU attention)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MB (a known-size reference "
                          "for hardware byte counters)")
@@ -275,15 +277,16 @@ def main():
               "mfma-pair": kvq.KERNEL_MFMA_PAIR}[args.kernel]
     pool_bytes = args.pool_mb * 1000 * 1000
 
+    bits = args.bits
     main_res, last = time_config(kvq, torch, args.skv, args.chunk, kernel, args.steps, args.warmup, pool_bytes,
-                                 step=args.step)
+                                 step=args.step, bits=bits)
     sweep = []
     for s in [int(x) for x in args.sweep.split(",") if x.strip()]:
         r, _ = time_config(kvq, torch, s, args.chunk, kernel, max(20, args.steps // 2), args.warmup, pool_bytes,
-                           step=args.step)
+                           step=args.step, bits=bits)
         r["us_per_layer"] = r["ms_per_step"] * 1e3
-        r["gbs"] = (layer_bytes(s) + append_bytes()) / (r["ms_per_step"] * 1e-3) / 1e9
-        r["partial_gbs"] = layer_bytes(s) / (r["partial_ms_avg"] * 1e-3) / 1e9
+        r["gbs"] = (layer_bytes(s, bits) + append_bytes(bits)) / (r["ms_per_step"] * 1e-3) / 1e9
+        r["partial_gbs"] = layer_bytes(s, bits) / (r["partial_ms_avg"] * 1e-3) / 1e9
         sweep.append(r)
 
     if args.calib_copy_mb > 0:
@@ -318,11 +321,30 @@ def main():
                       "step: as the headline step (rotate q, rotated append, partial with fp32 q, reduce, "
                       "rotate the output back)",
         }}
+        s8 = args.skv
+        i8, _ = time_config(kvq, torch, s8, args.chunk, kvq.KERNEL_AUTO, max(20, args.steps // 2), args.warmup,
+                            pool_bytes, step="fused", bits=8)
+        i8_ms = time_bulk_append(kvq, torch, False, bits=8)
+        nb8 = bulk_append_bytes(8)
+        att8 = layer_bytes(s8, 8) / (i8["partial_ms_avg"] * 1e-3) / 1e9
+        next_rows["int8"] = {
+            "workload": "the headline layer (B1 Hq64 Hkv8 D128 G64, Skv %d) with 8-bit codes: decode step "
+                        "(append, vector-ALU partial, reduce); bulk append of the outlier-workload shape" % s8,
+            "layer_bytes": layer_bytes(s8, 8),
+            "step_us": round(i8["ms_per_step"] * 1e3, 3),
+            "step_gbs": round((layer_bytes(s8, 8) + append_bytes(8)) / (i8["ms_per_step"] * 1e-3) / 1e9, 2),
+            "attention_us": round(i8["partial_ms_avg"] * 1e3, 3),
+            "attention_gbs": round(att8, 2),
+            "attention_frac": round(att8 / HBM_PEAK_GBS, 4),
+            "append_us": round(i8_ms * 1e3, 3),
+            "append_gbs": round(nb8 / (i8_ms * 1e-3) / 1e9, 2),
+            "timing": "step and attention as the headline; append as the hadamard row's",
+        }
 
-    step_bytes = layer_bytes(args.skv) + append_bytes()
+    step_bytes = layer_bytes(args.skv, bits) + append_bytes(bits)
     ms = main_res["ms_per_step"]
     value = step_bytes / (ms * 1e-3) / 1e9
-    achieved = layer_bytes(args.skv) / (main_res["partial_ms_avg"] * 1e-3) / 1e9
+    achieved = layer_bytes(args.skv, bits) / (main_res["partial_ms_avg"] * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(kvq, torch, last, args.skv)
@@ -340,12 +362,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes + fp16 scale/bias, f32 math",
+        "dtype": "int%d codes + fp16 scale/bias, f32 math" % bits,
         "data": "synthetic (seeded fp16 N(0,1) K/V/Q drawn on the GPU, quantised by the library)",
         "config": {
-            "workload": "Llama-3.1-70B-shaped decode layer: B1 Hq64 Hkv8 D128, int4 G64 fp16 scale+bias, "
-                        "alpha 1/sqrt(128); one decode step = quantise the token's K/V row into the cache + "
-                        "split-K attention over 512-row chunks + reduce",
+            "workload": ("Llama-3.1-70B-shaped decode layer: B1 Hq64 Hkv8 D128, int%d G64 fp16 scale+bias, "
+                         "alpha 1/sqrt(128); one decode step = quantise the token's K/V row into the cache + "
+                         "split-K attention over 512-row chunks + reduce" % bits),
             "step": args.step,
             "skv": args.skv,
             "chunk": args.chunk,
@@ -363,8 +385,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.skv, args.chunk, args.kernel),
-            "bytes_per_launch": layer_bytes(args.skv),
+            "traffic": measured_traffic(args.skv, args.chunk, args.kernel) if bits == 4 else None,
+            "bytes_per_launch": layer_bytes(args.skv, bits),
             "avg_launch_us": round(main_res["partial_ms_avg"] * 1e3, 3),
             "timing": "HIP events recorded in the kernel's own dispatch (hipExtLaunchKernel), averaged over the steps",
             "p10_launch_us": round(main_res["partial_ms_p10"] * 1e3, 3),

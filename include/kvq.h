@@ -39,6 +39,13 @@
  *    fp32 round-to-nearest-even at every step; -0 metadata stored as +0.
  *    This rule is this library's reading of "per-group scale + bias"; it is
  *    bit-exact and keeps every value within scale/2 of its reconstruction.
+ *  - 8-bit variant (kvq_cache.bits == 8; the Gemma page's "What I Tried"
+ *    table lists an int8 KV cache and the blog's decode driver takes 4 or 8
+ *    KV bits): the same rule with 255 in place of 15, codes 0..255, k_q and
+ *    v_q uint32 [B][Hkv][cap][D/4] with dimension d at
+ *    (word[d/4] >> (8*(d%4))) & 0xFF. Every entry point that takes a cache
+ *    reads and writes this format; the matrix-core kernels read int4 codes
+ *    only (KVQ_KERNEL_AUTO picks the vector-ALU kernel for 8-bit caches).
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -87,7 +94,8 @@ typedef struct kvq_cache {
     int32_t kv_heads;  /* Hkv >= 1 */
     int32_t head_dim;  /* D in {64, 128, 256} */
     int32_t group;     /* G in {32, 64, 128}, D % G == 0 */
-    int64_t capacity;  /* rows per (batch, KV head), >= 1; capacity * D/2 < 2^31 - 2^16 */
+    int64_t capacity;  /* rows per (batch, KV head), >= 1; capacity * D * bits/8 < 2^31 - 2^16 */
+    int32_t bits;      /* bits per code: 4 (0 means 4) or 8 */
 } kvq_cache;
 
 /* Library version string, e.g. "kvq 0.1.0 gfx950". */
@@ -100,8 +108,10 @@ const char *kvq_status_str(int status);
 int64_t kvq_num_chunks(int64_t skv, int32_t chunk);
 
 /* Bytes of one layer's cache: codes plus fp16 scale and bias for K and V,
- * capacity rows per (batch, KV head); 0 for invalid sizes. */
-int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t group, int64_t capacity);
+ * capacity rows per (batch, KV head), bits per code 4 (or 0) or 8; 0 for
+ * invalid sizes. */
+int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t group, int64_t capacity,
+                        int32_t bits);
 
 /*
  * Quantise n_new new rows of K and V and store them at rows
@@ -164,7 +174,8 @@ int kvq_hadamard_rotate(const void *x, int dtype, int64_t rows, int32_t head_dim
  *  chunk:   rows per chunk, >= 1 (512 is the tuned default).
  *  part_*:  fp32 outputs sized [B][Hq][C] and [B][Hq][C][D], 16-byte aligned.
  *  kernel:  KVQ_KERNEL_AUTO, or a forced variant (KVQ_E_UNSUPPORTED if it
- *           cannot run this shape).
+ *           cannot run this shape, or an 8-bit cache on a matrix-core
+ *           variant).
  */
 int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
                           float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
@@ -212,7 +223,8 @@ int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtyp
  * MFMA_WAVE, or AUTO / MFMA with at least 1024 (chunk, KV head, batch) items),
  * the append runs inside the attention kernel, in the wavefront that owns the
  * last chunk, so the step is two launches (attention, reduce) instead of
- * three; otherwise it is the three calls in order. Results are the same either way (cache bit for bit, out as
+ * three; otherwise (and always for 8-bit caches) it is the three calls in
+ * order. Results are the same either way (cache bit for bit, out as
  * kvq_sdpa_int4 with that kernel). All arguments are validated before anything
  * is enqueued: len + 1 <= capacity (else KVQ_E_CAPACITY), k_new, v_new and out
  * 16-byte aligned, the partials workspace sized for C = ceil((len+1)/chunk).

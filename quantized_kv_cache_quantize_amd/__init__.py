@@ -1,4 +1,5 @@
-"""Decode-time attention on an int4 group-affine KV cache for MI355X (gfx950).
+"""Decode-time attention on an int4 (or int8) group-affine KV cache for MI355X
+(gfx950).
 
 Thin Python binding over ``libkvq.so`` (the C ABI declared in
 ``include/kvq.h``). It only marshals arguments: PyTorch provides device memory
@@ -18,6 +19,7 @@ from ._binding import (  # noqa: F401
     KERNEL_VALU,
     Int4KVCache,
     KvqError,
+    QuantKVCache,
     cache_bytes,
     decode_step,
     hadamard_rotate,

@@ -33,6 +33,7 @@ class _Cache(C.Structure):
         ("head_dim", C.c_int32),
         ("group", C.c_int32),
         ("capacity", C.c_int64),
+        ("bits", C.c_int32),
     ]
 
 
@@ -61,7 +62,7 @@ def lib():
     L.kvq_num_chunks.restype = i64
     L.kvq_num_chunks.argtypes = [i64, i32]
     L.kvq_cache_bytes.restype = i64
-    L.kvq_cache_bytes.argtypes = [i32, i32, i32, i32, i64]
+    L.kvq_cache_bytes.argtypes = [i32, i32, i32, i32, i64, i32]
     L.kvq_quantize_kv_append.restype = C.c_int
     L.kvq_quantize_kv_append.argtypes = [cp, i64, vp, vp, C.c_int, i64, vp]
     L.kvq_quantize_kv_append_rotated.restype = C.c_int
@@ -97,8 +98,8 @@ def num_chunks(skv: int, chunk: int) -> int:
     return int(lib().kvq_num_chunks(int(skv), int(chunk)))
 
 
-def cache_bytes(batch: int, kv_heads: int, head_dim: int, group: int, capacity: int) -> int:
-    return int(lib().kvq_cache_bytes(batch, kv_heads, head_dim, group, capacity))
+def cache_bytes(batch: int, kv_heads: int, head_dim: int, group: int, capacity: int, bits: int = 4) -> int:
+    return int(lib().kvq_cache_bytes(batch, kv_heads, head_dim, group, capacity, bits))
 
 
 def _check(fn: str, status: int):
@@ -124,20 +125,21 @@ def _dtype_code(t: torch.Tensor) -> int:
     return 99  # rejected by the library with KVQ_E_DTYPE
 
 
-class Int4KVCache:
-    """One layer's int4 cache in device memory (allocated by PyTorch).
+class QuantKVCache:
+    """One layer's quantised cache in device memory (allocated by PyTorch).
 
-    k_q, v_q: int32 tensors [B][Hkv][cap][D/8] holding the uint32 words;
+    k_q, v_q: int32 tensors [B][Hkv][cap][D*bits/32] holding the uint32 words
+    (bits = 4: eight nibbles per word; bits = 8: four bytes per word);
     k_scale, k_bias, v_scale, v_bias: float16 [B][Hkv][cap][D/G]."""
 
     def __init__(self, batch: int, kv_heads: int, head_dim: int, capacity: int, group: int = 64,
-                 device="cuda", tensors=None):
+                 device="cuda", tensors=None, bits: int = 4):
         self.batch, self.kv_heads, self.head_dim = batch, kv_heads, head_dim
-        self.capacity, self.group = capacity, group
+        self.capacity, self.group, self.bits = capacity, group, bits
         if tensors is not None:
             self.k_q, self.v_q, self.k_scale, self.k_bias, self.v_scale, self.v_bias = tensors
         else:
-            wshape = (batch, kv_heads, capacity, head_dim // 8)
+            wshape = (batch, kv_heads, capacity, head_dim * bits // 32)
             sshape = (batch, kv_heads, capacity, head_dim // group)
             self.k_q = torch.zeros(wshape, dtype=torch.int32, device=device)
             self.v_q = torch.zeros(wshape, dtype=torch.int32, device=device)
@@ -148,16 +150,20 @@ class Int4KVCache:
 
     def c_struct(self) -> _Cache:
         return _Cache(_ptr(self.k_q), _ptr(self.v_q), _ptr(self.k_scale), _ptr(self.k_bias), _ptr(self.v_scale),
-                      _ptr(self.v_bias), self.batch, self.kv_heads, self.head_dim, self.group, self.capacity)
+                      _ptr(self.v_bias), self.batch, self.kv_heads, self.head_dim, self.group, self.capacity,
+                      self.bits)
 
     def nbytes(self) -> int:
-        return cache_bytes(self.batch, self.kv_heads, self.head_dim, self.group, self.capacity)
+        return cache_bytes(self.batch, self.kv_heads, self.head_dim, self.group, self.capacity, self.bits)
 
     def tensors(self):
         return (self.k_q, self.v_q, self.k_scale, self.k_bias, self.v_scale, self.v_bias)
 
 
-def quantize_kv_append(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
+Int4KVCache = QuantKVCache  # the int4 cache of the pages (bits=4, the default)
+
+
+def quantize_kv_append(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
                        stream=None) -> None:
     """kvq_quantize_kv_append: quantise k_new, v_new [B][Hkv][n][D] (fp16 or
     fp32, contiguous) into cache rows [length, length + n)."""
@@ -169,7 +175,7 @@ def quantize_kv_append(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_n
                                         int(n), _stream(stream)))
 
 
-def quantize_kv_append_rotated(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
+def quantize_kv_append_rotated(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
                                stream=None) -> None:
     """kvq_quantize_kv_append_rotated: Hadamard-rotate, then quantise, fp16
     rows k_new, v_new [B][Hkv][n][D] (contiguous) into cache rows
@@ -206,7 +212,7 @@ def partials_buffers(batch: int, hq: int, head_dim: int, skv: int, chunk: int = 
     return m, l, acc
 
 
-def sdpa_int4_partial(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int,
+def sdpa_int4_partial(cache: QuantKVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int,
                       part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor,
                       kernel: int = KERNEL_AUTO, stream=None) -> None:
     """kvq_sdpa_int4_partial: q [B][Hq][D] fp16/fp32 contiguous."""
@@ -225,7 +231,7 @@ def _event_handle(ev) -> int:
     return ev.cuda_event
 
 
-def sdpa_int4_partial_timed(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int,
+def sdpa_int4_partial_timed(cache: QuantKVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int,
                             part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor, start, stop,
                             kernel: int = KERNEL_AUTO, stream=None) -> None:
     """kvq_sdpa_int4_partial_timed: as sdpa_int4_partial, with torch.cuda.Event
@@ -248,7 +254,7 @@ def sdpa_int4_reduce(part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch
                                       _stream(stream)))
 
 
-def sdpa_int4(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int = 512,
+def sdpa_int4(cache: QuantKVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int = 512,
               out: torch.Tensor | None = None, workspace=None, kernel: int = KERNEL_AUTO, stream=None):
     """kvq_sdpa_int4: both phases on one stream; returns out [B][Hq][D] fp32."""
     assert q.is_contiguous()
@@ -265,7 +271,7 @@ def sdpa_int4(cache: Int4KVCache, skv: int, q: torch.Tensor, softmax_scale: floa
     return out
 
 
-def decode_step(cache: Int4KVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+def decode_step(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
                 softmax_scale: float, chunk: int = 512, out: torch.Tensor | None = None, workspace=None,
                 kernel: int = KERNEL_AUTO, stream=None, events=None):
     """kvq_decode_step: append k_new, v_new ([B][Hkv][D] or [B][Hkv][1][D]) at

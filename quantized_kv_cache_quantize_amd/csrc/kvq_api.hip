@@ -13,6 +13,10 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// bits per code of a cache: 4 (also the zero of a cache set up before the
+// field existed) or 8; 0 for anything else
+int cache_bits(const kvq_cache *c) { return c->bits == 0 || c->bits == 4 ? 4 : c->bits == 8 ? 8 : 0; }
+
 int check_cache(const kvq_cache *c)
 {
     if (!c)
@@ -27,11 +31,14 @@ int check_cache(const kvq_cache *c)
         return KVQ_E_SHAPE;
     if (c->head_dim % c->group != 0)
         return KVQ_E_SHAPE;
+    const int bits = cache_bits(c);
+    if (!bits)
+        return KVQ_E_SHAPE;
     // keep every element index far inside int64, and the code bytes of one
     // (batch, KV head) addressable with 32-bit offsets (with 64 KiB to spare)
     if (c->capacity > ((int64_t)1 << 40) / ((int64_t)c->batch * c->kv_heads))
         return KVQ_E_SHAPE;
-    if (c->capacity * (c->head_dim / 2) > 0x7fff0000)
+    if (c->capacity * (c->head_dim * bits / 8) > 0x7fff0000)
         return KVQ_E_SHAPE;
     if (!aligned16(c->k_q) || !aligned16(c->v_q) || !aligned16(c->k_scale) || !aligned16(c->k_bias) ||
         !aligned16(c->v_scale) || !aligned16(c->v_bias))
@@ -78,12 +85,17 @@ int64_t kvq_num_chunks(int64_t skv, int32_t chunk)
     return (skv + chunk - 1) / chunk;
 }
 
-int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t group, int64_t capacity)
+int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t group, int64_t capacity,
+                        int32_t bits)
 {
     if (batch < 1 || kv_heads < 1 || head_dim < 8 || head_dim % 8 || group < 1 || head_dim % group || capacity < 1)
         return 0;
+    if (bits == 0)
+        bits = 4;
+    if (bits != 4 && bits != 8)
+        return 0;
     const int64_t rows = (int64_t)batch * kv_heads * capacity;
-    const int64_t per_row = head_dim / 2 + 2 * 2 * (head_dim / group);  // codes + fp16 scale and bias
+    const int64_t per_row = head_dim * bits / 8 + 2 * 2 * (head_dim / group);  // codes + fp16 scale and bias
     return 2 * rows * per_row;                                         // K and V
 }
 
@@ -128,6 +140,7 @@ int append_impl(const kvq_cache *cache, int64_t len, const void *k_new, const vo
     a.cap = cache->capacity;
     a.D = cache->head_dim;
     a.G = cache->group;
+    a.bits = cache_bits(cache);
     a.rot_scale = rotate ? 1.0 / sqrt((double)cache->head_dim) : 0.0;
     return launch_status(launch_quantize(a, dtype, (hipStream_t)stream));
 }
@@ -214,7 +227,7 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA_PAIR)
         return KVQ_E_SHAPE;
     const int n_rep = Hq / cache->kv_heads;
-    const bool mfma_ok = mfma_supports(cache->head_dim, cache->group, n_rep, chunk);
+    const bool mfma_ok = cache_bits(cache) == 4 && mfma_supports(cache->head_dim, cache->group, n_rep, chunk);
     const bool want_mfma = kernel == KVQ_KERNEL_MFMA || kernel == KVQ_KERNEL_MFMA_SPLIT ||
                            kernel == KVQ_KERNEL_MFMA_WAVE || kernel == KVQ_KERNEL_MFMA_PAIR;
     if (want_mfma && !mfma_ok)
@@ -239,6 +252,7 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     a.Hq = Hq;
     a.n_rep = n_rep;
     a.G = cache->group;
+    a.bits = cache_bits(cache);
     a.score_scale = softmax_scale * kLog2e;
     a.k_new = nullptr;
     a.v_new = nullptr;

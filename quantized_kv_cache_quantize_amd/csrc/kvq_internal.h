@@ -33,6 +33,7 @@ struct QuantizeArgs {
     int64_t cap;
     int32_t D;
     int32_t G;
+    int32_t bits;      // 4 or 8 bits per code
     double rot_scale;  // nonzero: rotate each row by H_D * rot_scale (1 / sqrt(D)) before quantising
 };
 
@@ -64,6 +65,7 @@ struct PartialArgs {
     int32_t Hq;
     int32_t n_rep;
     int32_t G;
+    int32_t bits;       // 4 or 8 bits per code (the matrix-core kernels take 4 only)
     float score_scale;  // softmax_scale * log2(e)
     // Fused decode step (one-wavefront kernel only): when append_row >= 0,
     // the wavefront whose chunk holds that row first quantises k_new / v_new

@@ -1,15 +1,16 @@
-// The int4 group-affine quantiser of one packed word, for any kernel that
+// The group-affine quantiser of eight values of a row, for any kernel that
 // writes cache rows (the append kernel and the fused decode step).
 //
 // "Background: Why TurboQuant Fails on Gemma 4" (Gemma page) fixes the
 // format: int4 codes with an fp16 scale and bias per group; the exact rule
-// (bias = min rounded down to fp16, scale = (max - bias)/15 rounded up to
-// fp16, codes rint((x - bias)/scale) clamped to [0, 15], 0 when scale is 0,
-// -0 stored as +0) is spelled out in include/kvq.h.
+// (bias = min rounded down to fp16, scale = (max - bias)/L rounded up to
+// fp16, codes rint((x - bias)/scale) clamped to [0, L], 0 when scale is 0,
+// -0 stored as +0; L = 15 for int4 codes, 255 for the 8-bit cache of the
+// Gemma page's "What I Tried" table) is spelled out in include/kvq.h.
 //
 // Bit-exactness: no contraction (a*b+c stays two roundings), every quotient
 // that can change a code is the correctly rounded IEEE one (see
-// quantize_word), rint is round-half-even, and the fp16 conversions are the
+// quantize_codes), rint is round-half-even, and the fp16 conversions are the
 // hardware round-to-nearest-even plus a one-ulp step.
 #pragma once
 
@@ -48,7 +49,8 @@ __device__ __forceinline__ uint16_t f16_round_up(float x)
     return b;
 }
 
-// Eight consecutive values of a row (element j -> nibble j of the word).
+// Eight consecutive values of a row (element j -> code j of the lane's
+// word, or of its two words for 8-bit codes).
 template <typename T>
 __device__ __forceinline__ void load8(const T *p, float (&x)[8]);
 
@@ -101,16 +103,20 @@ __device__ __forceinline__ void group_min_max(float &lo, float &hi)
     }
 }
 
-// Quantise one word of a group whose G values are held by LPG = G/8
+// Quantise eight values of a group whose G values are held by LPG = G/8
 // consecutive, aligned lanes (every lane of the group must call this
-// together: the group's min and max meet through lane exchanges). Returns the
-// packed codes and the group's fp16 scale and bias bit patterns (the same on
-// every lane).
-template <int LPG>
-__device__ __forceinline__ uint32_t quantize_word(const float (&x)[8], uint16_t &scale_bits, uint16_t &bias_bits)
+// together: the group's min and max meet through lane exchanges). Stores the
+// packed codes, BITS/4 words (int4: one word of eight nibbles; int8: two
+// words of four bytes, lowest first), and returns the group's fp16 scale and
+// bias bit patterns (the same on every lane).
+template <int LPG, int BITS>
+__device__ __forceinline__ void quantize_codes(const float (&x)[8], uint32_t (&words)[BITS / 4], uint16_t &scale_bits,
+                                               uint16_t &bias_bits)
 {
 #pragma clang fp contract(off)
     static_assert(LPG == 4 || LPG == 8 || LPG == 16, "groups of 32, 64 or 128 values");
+    static_assert(BITS == 4 || BITS == 8, "int4 or int8 codes");
+    constexpr float L = (float)((1 << BITS) - 1);
     float lo = x[0], hi = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
@@ -123,19 +129,22 @@ __device__ __forceinline__ uint32_t quantize_word(const float (&x)[8], uint16_t 
         bb = 0;
     const float bf = h_value(bb);
     const float range = hi - bf;
-    const float s32 = range / 15.0f;
+    const float s32 = range / L;
     uint16_t sb = f16_round_up(s32);
     if (sb == 0x8000)
         sb = 0;
     const float sf = h_value(sb);
 
     // The code is rint of the correctly rounded quotient u = (x - bias) /
-    // scale, which lies in [0, 16). The product (x - bias) * rcp(scale)
-    // (v_rcp_f32, 1 ulp) is within 16 * 1.5 * 2^-23 of the exact quotient and
-    // u within 16 * 2^-24 of it, so both round to the same integer unless the
-    // product lies within 3.8e-6 of a half-integer. When some lane of the
-    // wavefront has a product that close (margin 2^-16), the wavefront
-    // recomputes its codes from correctly rounded quotients.
+    // scale, which lies in [0, L + 1). The product (x - bias) * rcp(scale)
+    // (v_rcp_f32, 1 ulp) is within (L + 1) * 1.5 * 2^-23 of the exact
+    // quotient and u within (L + 1) * 2^-24 of it, so both round to the same
+    // integer unless the product lies within (L + 1) * 2^-22 of a
+    // half-integer (3.8e-6 for int4, 6.1e-5 for int8). When some lane of the
+    // wavefront has a product closer than the margin (twice that or more:
+    // 2^-16 for int4, 2^-13 for int8), the wavefront recomputes its codes
+    // from correctly rounded quotients.
+    constexpr float margin = BITS == 4 ? 0x1p-16f : 0x1p-13f;
     float r[8];
     const float rs = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
     bool near = false;
@@ -143,7 +152,7 @@ __device__ __forceinline__ uint32_t quantize_word(const float (&x)[8], uint16_t 
     for (int j = 0; j < 8; ++j) {
         const float u = (x[j] - bf) * rs;
         r[j] = rintf(u);
-        near |= fabsf(u - r[j]) > 0.5f - 0x1p-16f;
+        near |= fabsf(u - r[j]) > 0.5f - margin;
     }
     if (__builtin_amdgcn_ballot_w64(near) != 0) {
         asm volatile("" ::: "memory");  // a real branch: the divisions run only here
@@ -151,13 +160,26 @@ __device__ __forceinline__ uint32_t quantize_word(const float (&x)[8], uint16_t 
         for (int j = 0; j < 8; ++j)
             r[j] = sf != 0.0f ? rintf((x[j] - bf) / sf) : 0.0f;
     }
-    uint32_t word = 0;
+    constexpr int P = 32 / BITS;  // codes per word
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        word |= (uint32_t)__builtin_amdgcn_fmed3f(r[j], 0.0f, 15.0f) << (4 * j);
+    for (int i = 0; i < BITS / 4; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            word |= (uint32_t)__builtin_amdgcn_fmed3f(r[P * i + j], 0.0f, L) << (BITS * j);
+        words[i] = word;
+    }
     scale_bits = sb;
     bias_bits = bb;
-    return word;
+}
+
+// The int4 word of eight values (see quantize_codes).
+template <int LPG>
+__device__ __forceinline__ uint32_t quantize_word(const float (&x)[8], uint16_t &scale_bits, uint16_t &bias_bits)
+{
+    uint32_t w[1];
+    quantize_codes<LPG, 4>(x, w, scale_bits, bias_bits);
+    return w[0];
 }
 
 }  // namespace quant

@@ -1,15 +1,16 @@
-// Quantise new K/V rows into the int4 group-affine cache.
+// Quantise new K/V rows into the group-affine cache (int4 codes, or int8).
 //
 // The decode-step listing of the "turboquant-llama3.170B" README quantises K
 // and V to int4 before the fused attention; the rule itself is in
 // quant_rule.h.
 //
-// Mapping: one lane per packed word. A group of G values is G/8 consecutive
-// lanes of one wavefront; they reduce min/max with cross-lane swaps, every
-// lane derives the same bias and scale, packs its eight codes into one word
-// and stores it; the first lane of the group stores the fp16 scale and bias.
-// Loads are 16-byte (fp16) or 2x16-byte (fp32) per lane and consecutive lanes
-// touch consecutive addresses, so both loads and stores coalesce.
+// Mapping: one lane per eight values of a row. A group of G values is G/8
+// consecutive lanes of one wavefront; they reduce min/max with cross-lane
+// swaps, every lane derives the same bias and scale, packs its eight codes
+// (one word of nibbles, or two words of bytes) and stores them; the first
+// lane of the group stores the fp16 scale and bias. Loads are 16-byte (fp16)
+// or 2x16-byte (fp32) per lane and consecutive lanes touch consecutive
+// addresses, so both loads and stores coalesce.
 //
 // The rotated variant (fp16 rows) first applies the normalised Hadamard
 // rotation of hadamard_row.h to the row, whose D/8 lanes are consecutive in
@@ -21,7 +22,7 @@
 namespace kvq {
 namespace {
 
-template <typename T, int LPG, bool ROT>  // LPG = lanes per group = G / 8
+template <typename T, int LPG, bool ROT, int BITS>  // LPG = lanes per group = G / 8
 __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
 {
     const int which = blockIdx.y;  // 0: K, 1: V
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
     uint16_t *dscale = which ? a.v_scale : a.k_scale;
     uint16_t *dbias = which ? a.v_bias : a.k_bias;
 
-    const int W = a.D >> 3;            // words per row, a power of two
+    const int W = a.D >> 3;            // lanes per row, a power of two
     const int lw = __builtin_ctz(W);   // (shifts, not 64-bit divisions)
     const int64_t lane_id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = a.rows * W;
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
     }
     // lanes past the end still take part in their group's swaps
     uint16_t sb, bb;
-    const uint32_t word = quant::quantize_word<LPG>(x, sb, bb);
+    uint32_t words[BITS / 4];
+    quant::quantize_codes<LPG, BITS>(x, words, sb, bb);
     if (!active)
         return;
     // (batch * KV head, new row) of this row: a 32-bit division whenever the
@@ -76,7 +78,10 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
         t = row - bh * a.n_new;
     }
     const int64_t crow = bh * a.cap + a.len + t;
-    dq[(crow << lw) + w] = word;
+    if constexpr (BITS == 4)
+        dq[(crow << lw) + w] = words[0];
+    else
+        *reinterpret_cast<uint2 *>(dq + (crow << (lw + 1)) + 2 * w) = make_uint2(words[0], words[1]);
     if ((w & (LPG - 1)) == 0) {
         const int NG = W / LPG;
         const int g = w / LPG;
@@ -85,26 +90,34 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantizeArgs a)
     }
 }
 
-template <typename T, bool ROT>
-hipError_t launch_t(const QuantizeArgs &a, hipStream_t s)
+template <typename T, bool ROT, int BITS>
+hipError_t launch_tb(const QuantizeArgs &a, hipStream_t s)
 {
     const int64_t total = a.rows * (a.D / 8);
     const int64_t blocks = (total + 255) / 256;
     dim3 grid((unsigned)blocks, 2, 1);
     switch (a.G) {
     case 32:
-        hipLaunchKernelGGL((quantize_append_kernel<T, 4, ROT>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((quantize_append_kernel<T, 4, ROT, BITS>), grid, dim3(256), 0, s, a);
         break;
     case 64:
-        hipLaunchKernelGGL((quantize_append_kernel<T, 8, ROT>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((quantize_append_kernel<T, 8, ROT, BITS>), grid, dim3(256), 0, s, a);
         break;
     case 128:
-        hipLaunchKernelGGL((quantize_append_kernel<T, 16, ROT>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((quantize_append_kernel<T, 16, ROT, BITS>), grid, dim3(256), 0, s, a);
         break;
     default:
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename T, bool ROT>
+hipError_t launch_t(const QuantizeArgs &a, hipStream_t s)
+{
+    if (a.bits == 8)
+        return launch_tb<T, ROT, 8>(a, s);
+    return a.bits == 4 ? launch_tb<T, ROT, 4>(a, s) : hipErrorInvalidValue;
 }
 
 // One lane per 8 values of a row: the rotation of hadamard_row.h in float64,

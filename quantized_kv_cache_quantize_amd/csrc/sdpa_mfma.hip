@@ -1489,6 +1489,8 @@ bool mfma_supports(int D, int G, int n_rep, int chunk)
 
 hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l)
 {
+    if (a.bits != 4)  // these kernels read int4 codes only
+        return hipErrorInvalidValue;
     const int NG = D / a.G;
     if (D == 128) {
         if (NG == 1) return launch_dg<128, 1>(a, q_dtype, batch, variant, l);

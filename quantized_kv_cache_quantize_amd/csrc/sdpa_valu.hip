@@ -1,4 +1,5 @@
-// Split-K decode attention on the int4 cache, vector-ALU variant.
+// Split-K decode attention on the quantised cache (int4 codes, or the 8-bit
+// variant), vector-ALU kernel.
 //
 // Phase 1 of the split-K scheme of the "turboquant-llama3.170B" README: each
 // workgroup owns one (batch, KV head, head tile, chunk) and emits the partial
@@ -8,14 +9,15 @@
 // weights and the running softmax live in registers and LDS only.
 //
 // This variant handles every supported shape (any GQA ratio, D in
-// {64,128,256}, G in {32,64,128}, any chunk length) and is the fallback for
-// shapes the matrix-core kernel does not cover. Within a chunk the rows are
-// walked in tiles of 256 with an online softmax across tiles.
+// {64,128,256}, G in {32,64,128}, any chunk length, 4- or 8-bit codes) and
+// is the fallback for what the matrix-core kernels do not cover. Within a
+// chunk the rows are walked in tiles of 256 with an online softmax across
+// tiles.
 //
 // Layout per tile (256 threads, 4 wavefronts):
 //   K pass: thread i scores row tile+i for all NREP heads (q broadcast from LDS).
 //   V pass: thread (word w, slot r) accumulates words w of rows r, r+NT/W, ...
-//           so each wavefront load instruction reads whole 16..128-byte rows.
+//           so each wavefront load instruction reads whole 32..256-byte rows.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -48,10 +50,12 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-template <int D, int NREP, typename QT>
+template <int D, int NREP, typename QT, int BITS>
 __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
 {
-    constexpr int W = D / 8;      // words per row
+    constexpr int P = 32 / BITS;  // codes per word
+    constexpr uint32_t MASK = (1u << BITS) - 1u;
+    constexpr int W = D / P;      // words per row
     constexpr int NS = NT / W;    // V-pass row slots
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -80,16 +84,16 @@ __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
 
     const int w = tid % W;
     const int slot = tid / W;
-    const int gw = (8 * w) / G;  // group of this thread's V word
+    const int gw = (P * w) / G;  // group of this thread's V word
 
-    float acc[NREP][8];
+    float acc[NREP][P];
     float m_run[NREP], l_part[NREP];
 #pragma unroll
     for (int h = 0; h < NREP; ++h) {
         m_run[h] = -INFINITY;
         l_part[h] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < P; ++j)
             acc[h][j] = 0.0f;
     }
 
@@ -110,26 +114,24 @@ __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
                 const uint32_t wv[4] = {words.x, words.y, words.z, words.w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int g = (8 * (w4 + u)) / G;
+                    const int g = (P * (w4 + u)) / G;
                     const float sc = h_val(ksr[g]);
                     const float bi = h_val(kbr[g]);
-                    float kv[8];
+                    float kv[P];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        kv[j] = fmaf((float)((wv[u] >> (4 * j)) & 0xF), sc, bi);
+                    for (int j = 0; j < P; ++j)
+                        kv[j] = fmaf((float)((wv[u] >> (BITS * j)) & MASK), sc, bi);
 #pragma unroll
                     for (int h = 0; h < NREP; ++h) {
-                        const float4 qa = *reinterpret_cast<const float4 *>(&q_s[h][8 * (w4 + u)]);
-                        const float4 qb = *reinterpret_cast<const float4 *>(&q_s[h][8 * (w4 + u) + 4]);
                         float acc_s0 = s[h];
-                        acc_s0 = fmaf(qa.x, kv[0], acc_s0);
-                        acc_s0 = fmaf(qa.y, kv[1], acc_s0);
-                        acc_s0 = fmaf(qa.z, kv[2], acc_s0);
-                        acc_s0 = fmaf(qa.w, kv[3], acc_s0);
-                        acc_s0 = fmaf(qb.x, kv[4], acc_s0);
-                        acc_s0 = fmaf(qb.y, kv[5], acc_s0);
-                        acc_s0 = fmaf(qb.z, kv[6], acc_s0);
-                        acc_s0 = fmaf(qb.w, kv[7], acc_s0);
+#pragma unroll
+                        for (int j4 = 0; j4 < P; j4 += 4) {
+                            const float4 qa = *reinterpret_cast<const float4 *>(&q_s[h][P * (w4 + u) + j4]);
+                            acc_s0 = fmaf(qa.x, kv[j4 + 0], acc_s0);
+                            acc_s0 = fmaf(qa.y, kv[j4 + 1], acc_s0);
+                            acc_s0 = fmaf(qa.z, kv[j4 + 2], acc_s0);
+                            acc_s0 = fmaf(qa.w, kv[j4 + 3], acc_s0);
+                        }
                         s[h] = acc_s0;
                     }
                 }
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
 #pragma unroll
         for (int h = 0; h < NREP; ++h)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < P; ++j)
                 acc[h][j] *= corr[h];
         const int nrows = (int)min((int64_t)NT, t1 - tb);
         for (int r = slot; r < nrows; r += NS) {
@@ -176,15 +178,15 @@ __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
             const uint32_t word = a.v_q[vrow * W + w];
             const float sc = h_val(a.v_scale[vrow * NG + gw]);
             const float bi = h_val(a.v_bias[vrow * NG + gw]);
-            float vv[8];
+            float vv[P];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vv[j] = fmaf((float)((word >> (4 * j)) & 0xF), sc, bi);
+            for (int j = 0; j < P; ++j)
+                vv[j] = fmaf((float)((word >> (BITS * j)) & MASK), sc, bi);
 #pragma unroll
             for (int h = 0; h < NREP; ++h) {
                 const float p = p_s[h][r];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < P; ++j)
                     acc[h][j] = fmaf(p, vv[j], acc[h][j]);
             }
         }
@@ -197,15 +199,15 @@ __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
 #pragma unroll
         for (int h = 0; h < NREP; ++h)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < P; ++j)
                 acc[h][j] += __shfl_xor(acc[h][j], off);
     // ... then across the four wavefronts through LDS
     if (lane < W) {
 #pragma unroll
         for (int h = 0; h < NREP; ++h)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc_s[wave][h][8 * w + j] = acc[h][j];
+            for (int j = 0; j < P; ++j)
+                acc_s[wave][h][P * w + j] = acc[h][j];
     }
     // l: sum of every thread's running partial (all scaled to the same m)
 #pragma unroll
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(NT) void sdpa_partial_valu_kernel(PartialArgs a)
     }
 }
 
-template <int D, typename QT>
+template <int D, typename QT, int BITS>
 hipError_t launch_d(const PartialArgs &a, int batch, const Launch &l)
 {
     int tile = 1;
@@ -242,41 +244,49 @@ hipError_t launch_d(const PartialArgs &a, int batch, const Launch &l)
     dim3 grid((unsigned)a.num_chunks, (unsigned)(a.Hkv * (a.n_rep / tile)), (unsigned)batch);
     switch (tile) {
     case 8:
-        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 8, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 8, QT, BITS>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     case 4:
-        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 4, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 4, QT, BITS>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     case 2:
-        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 2, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 2, QT, BITS>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     default:
-        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 1, QT>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
+        hipExtLaunchKernelGGL((sdpa_partial_valu_kernel<D, 1, QT, BITS>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
         break;
     }
     return hipGetLastError();
 }
 
-template <typename QT>
+template <typename QT, int BITS>
 hipError_t launch_q(const PartialArgs &a, int D, int batch, const Launch &l)
 {
     switch (D) {
     case 64:
-        return launch_d<64, QT>(a, batch, l);
+        return launch_d<64, QT, BITS>(a, batch, l);
     case 128:
-        return launch_d<128, QT>(a, batch, l);
+        return launch_d<128, QT, BITS>(a, batch, l);
     case 256:
-        return launch_d<256, QT>(a, batch, l);
+        return launch_d<256, QT, BITS>(a, batch, l);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+template <int BITS>
+hipError_t launch_b(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l)
+{
+    return q_dtype == KVQ_F16 ? launch_q<_Float16, BITS>(a, D, batch, l) : launch_q<float, BITS>(a, D, batch, l);
 }
 
 }  // namespace
 
 hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l)
 {
-    return q_dtype == KVQ_F16 ? launch_q<_Float16>(a, D, batch, l) : launch_q<float>(a, D, batch, l);
+    if (a.bits == 8)
+        return launch_b<8>(a, D, q_dtype, batch, l);
+    return a.bits == 4 ? launch_b<4>(a, D, q_dtype, batch, l) : hipErrorInvalidValue;
 }
 
 }  // namespace kvq

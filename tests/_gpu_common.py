@@ -46,8 +46,8 @@ def to_host_bits(t: torch.Tensor) -> np.ndarray:
     return a
 
 
-def canary_cache(B, Hkv, D, cap, G=64) -> kvq.Int4KVCache:
-    c = kvq.Int4KVCache(B, Hkv, D, cap, G, device=dev())
+def canary_cache(B, Hkv, D, cap, G=64, bits=4) -> kvq.QuantKVCache:
+    c = kvq.QuantKVCache(B, Hkv, D, cap, G, device=dev(), bits=bits)
     c.k_q.fill_(int(WORD_CANARY))
     c.v_q.fill_(int(WORD_CANARY))
     for t in (c.k_scale, c.k_bias, c.v_scale, c.v_bias):
@@ -55,17 +55,17 @@ def canary_cache(B, Hkv, D, cap, G=64) -> kvq.Int4KVCache:
     return c
 
 
-def gpu_cache_from_oracle(oc: oracle.Cache) -> kvq.Int4KVCache:
+def gpu_cache_from_oracle(oc: oracle.Cache) -> kvq.QuantKVCache:
     """Device copy of a cache the oracle quantised on the host."""
     tensors = tuple(to_dev(a) for a in (oc.k_q, oc.v_q, oc.k_scale, oc.k_bias, oc.v_scale, oc.v_bias))
-    return kvq.Int4KVCache(oc.B, oc.Hkv, oc.D, oc.cap, oc.G, tensors=tensors)
+    return kvq.QuantKVCache(oc.B, oc.Hkv, oc.D, oc.cap, oc.G, tensors=tensors, bits=oc.bits)
 
 
-def host_arrays(c: kvq.Int4KVCache):
+def host_arrays(c: kvq.QuantKVCache):
     return tuple(to_host_bits(t) for t in c.tensors())
 
 
-def assert_cache_equal(gc: kvq.Int4KVCache, oc: oracle.Cache, rows=None):
+def assert_cache_equal(gc: kvq.QuantKVCache, oc: oracle.Cache, rows=None):
     names = ("k_q", "v_q", "k_scale", "k_bias", "v_scale", "v_bias")
     got = host_arrays(gc)
     for n, g in zip(names, got):
@@ -77,7 +77,7 @@ def assert_cache_equal(gc: kvq.Int4KVCache, oc: oracle.Cache, rows=None):
             n, len(bad), tuple(bad[0]), int(g[tuple(bad[0])]), int(r[tuple(bad[0])]))
 
 
-def run_sdpa(gc: kvq.Int4KVCache, skv: int, q: np.ndarray, alpha: float, chunk=512, kernel=kvq.KERNEL_AUTO,
+def run_sdpa(gc: kvq.QuantKVCache, skv: int, q: np.ndarray, alpha: float, chunk=512, kernel=kvq.KERNEL_AUTO,
              guard=64):
     """Partial + reduce through the C ABI with NaN-filled guard zones around
     every output; returns (out, m, l, acc) as numpy and checks the guards."""

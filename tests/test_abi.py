@@ -63,6 +63,18 @@ def test_cache_bytes_formula(L):
     assert B.cache_bytes(1, 16, 256, 64, 10) == 16 * 10 * 288
     assert B.cache_bytes(1, 8, 128, 64, 131072) == 150994944
     assert B.cache_bytes(0, 8, 128, 64, 1) == 0 and B.cache_bytes(1, 8, 100, 64, 1) == 0
+    # bits 0 means 4; 8-bit codes: 128 B codes + 8 B metadata = 136 B per row
+    assert B.cache_bytes(1, 8, 128, 64, 1, bits=0) == 8 * 144
+    assert B.cache_bytes(1, 8, 128, 64, 1, bits=8) == 8 * 272
+    assert B.cache_bytes(1, 8, 128, 64, 131072, bits=8) == 285212672
+    assert B.cache_bytes(1, 8, 128, 64, 1, bits=2) == 0 and B.cache_bytes(1, 8, 128, 64, 1, bits=16) == 0
+
+
+def test_cache_struct_layout(L):
+    """bits sits after capacity, so a cache set up without it (zeroed) reads
+    as int4."""
+    assert B._Cache.bits.offset == B._Cache.capacity.offset + 8
+    assert C.sizeof(B._Cache) == 6 * 8 + 4 * 4 + 8 + 8
 
 
 def test_memory_table_golden(L):
@@ -83,7 +95,7 @@ def test_memory_table_golden(L):
 
 def _cache(**kw):
     c = dict(k_q=P, v_q=P, k_scale=P, k_bias=P, v_scale=P, v_bias=P, batch=1, kv_heads=8, head_dim=128,
-             group=64, capacity=1024)
+             group=64, capacity=1024, bits=4)
     c.update(kw)
     return B._Cache(**c)
 
@@ -115,6 +127,24 @@ def test_append_validation(L):
     assert _append(L, _cache(), v=P + 8) == E_ALIGN
     # zero new rows is a no-op that succeeds without touching the device
     assert _append(L, _cache(capacity=10), length=10, n=0) == OK
+
+
+def test_bits_validation(L):
+    for bad in (1, 2, 3, 5, 16, -4):
+        assert _append(L, _cache(bits=bad)) == E_SHAPE, bad
+        assert _partial(L, _cache(bits=bad)) == E_SHAPE, bad
+        assert _append_rot(L, _cache(bits=bad)) == E_SHAPE, bad
+    for ok in (0, 4, 8):
+        assert _append(L, _cache(capacity=10, bits=ok), length=10, n=0) == OK
+    # 8-bit codes double the code bytes of one (batch, KV head): capacity * D
+    # must stay below 2^31 - 2^16
+    assert _append(L, _cache(capacity=(0x7fff0000 // 64) + 1, bits=4), length=0, n=0) == E_SHAPE
+    assert _append(L, _cache(capacity=0x7fff0000 // 128, bits=8), length=0, n=0) == OK
+    assert _append(L, _cache(capacity=(0x7fff0000 // 128) + 1, bits=8), length=0, n=0) == E_SHAPE
+    # the matrix-core kernels read int4 codes only
+    for k in (2, 3, 4, 5):
+        assert _partial(L, _cache(bits=8), kernel=k) == E_UNSUP, k
+        assert _step(L, _cache(bits=8), kernel=k) == E_UNSUP, k
 
 
 def _append_rot(L, cache, length=0, k=P, v=P, dtype=0, n=1):

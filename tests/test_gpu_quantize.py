@@ -14,15 +14,15 @@ from _gpu_common import (META_CANARY, WORD_CANARY, assert_cache_equal, canary_ca
 pytestmark = pytest.mark.gpu
 
 
-def _append_and_check(k, v, length, cap, G=64):
+def _append_and_check(k, v, length, cap, G=64, bits=4):
     """Append k, v [B][Hkv][n][D] at row `length` of a canary-filled cache of
     `cap` rows; compare the written rows with the oracle and the rest with
     the canary."""
     B, Hkv, n, D = k.shape
-    gc = canary_cache(B, Hkv, D, cap, G)
+    gc = canary_cache(B, Hkv, D, cap, G, bits=bits)
     kvq.quantize_kv_append(gc, length, to_dev(k), to_dev(v))
     torch.cuda.synchronize()
-    oc = oracle.Cache(B, Hkv, D, cap, G)
+    oc = oracle.Cache(B, Hkv, D, cap, G, bits=bits)
     oc.append(k, v, length)
     rows = slice(length, length + n)
     assert_cache_equal(gc, oc, rows)
@@ -77,23 +77,23 @@ def test_special_values(dt):
     _append_and_check(k, v, 0, x.shape[0])
 
 
-def _boundary_rows(D=128, G=64):
+def _boundary_rows(D=128, G=64, L=15):
     """Groups whose quotients (x - bias) / scale sit on and right next to the
     half-integers where rint changes the code: each group holds its bias b
-    and b + 15 s (so the scale is s) and values b + (k + 1/2 + delta) s for
-    delta in {0, +-2^-22 .. +-2^-12}, in fp32; several scales, some of them
-    not powers of two."""
+    and b + L s (so the scale is s) and values b + (k + 1/2 + delta) s for
+    delta in {0, +-2^-22 .. +-2^-10}, in fp32; several scales, some of them
+    not powers of two. L = 15 for int4 codes, 255 for int8."""
     rows = []
-    deltas = [0.0] + [sgn * 2.0 ** -e for e in (22, 20, 18, 16, 14, 12) for sgn in (1, -1)]
+    deltas = [0.0] + [sgn * 2.0 ** -e for e in (22, 20, 18, 16, 14, 13, 12, 10) for sgn in (1, -1)]
     for si, s in enumerate([0.1, 0.3, 1.7, 3e-3, 7.0, 1.0, 0.0625]):
         s = float(np.float16(s))
         b = float(np.float16(-0.37 * (si + 1)))
         row = np.empty(D, dtype=np.float64)
         for g in range(D // G):
-            vals = [b, b + 15 * s]
+            vals = [b, b + L * s]
             k = 0
             while len(vals) < G:
-                vals.append(b + (k % 15 + 0.5 + deltas[k % len(deltas)]) * s)
+                vals.append(b + ((k * 7) % L + 0.5 + deltas[k % len(deltas)]) * s)
                 k += 1
             row[g * G:(g + 1) * G] = vals
         rows.append(row)
