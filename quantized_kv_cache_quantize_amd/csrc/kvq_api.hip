@@ -227,10 +227,11 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA_PAIR)
         return KVQ_E_SHAPE;
     const int n_rep = Hq / cache->kv_heads;
-    const bool mfma_ok = cache_bits(cache) == 4 && mfma_supports(cache->head_dim, cache->group, n_rep, chunk);
+    const int bits = cache_bits(cache);
     const bool want_mfma = kernel == KVQ_KERNEL_MFMA || kernel == KVQ_KERNEL_MFMA_SPLIT ||
                            kernel == KVQ_KERNEL_MFMA_WAVE || kernel == KVQ_KERNEL_MFMA_PAIR;
-    if (want_mfma && !mfma_ok)
+    // 8-bit caches have the one-wavefront matrix-core kernel only
+    if (bits == 8 && (kernel == KVQ_KERNEL_MFMA_SPLIT || kernel == KVQ_KERNEL_MFMA_PAIR))
         return KVQ_E_UNSUPPORTED;
 
     PartialArgs &a = p.a;
@@ -252,12 +253,16 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     a.Hq = Hq;
     a.n_rep = n_rep;
     a.G = cache->group;
-    a.bits = cache_bits(cache);
+    a.bits = bits;
     a.score_scale = softmax_scale * kLog2e;
     a.k_new = nullptr;
     a.v_new = nullptr;
     a.append_row = -1;
     a.append_dtype = KVQ_F16;
+    const bool mfma_ok = mfma_supports(cache->head_dim, cache->group, n_rep, chunk) &&
+                         (bits == 4 || mfma_one_wave_ok(a, cache->head_dim, cache->batch));
+    if (want_mfma && !mfma_ok)
+        return KVQ_E_UNSUPPORTED;
     if (kernel == KVQ_KERNEL_MFMA_WAVE && !mfma_one_wave_ok(a, cache->head_dim, cache->batch))
         return KVQ_E_UNSUPPORTED;
     if (kernel == KVQ_KERNEL_MFMA_PAIR && !mfma_pair_ok(a, cache->head_dim, q_dtype, cache->batch))
@@ -367,8 +372,10 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
     // AUTO / MFMA at one (chunk, KV head) item or more per SIMD (below that
     // the four-wavefront kernel plus a separate append is faster)
     const int64_t items = p.a.num_chunks * cache->kv_heads * cache->batch;
+    // (8-bit caches: always, the one-wavefront kernel being their only
+    // matrix-core kernel)
     const bool fused = p.use_mfma && mfma_one_wave_ok(p.a, cache->head_dim, cache->batch) &&
-                       (kernel == KVQ_KERNEL_MFMA_WAVE ||
+                       (kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 ||
                         ((kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) && items >= kOneWaveItems));
     if (fused) {
         p.a.k_new = k_new;

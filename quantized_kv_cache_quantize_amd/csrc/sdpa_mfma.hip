@@ -95,6 +95,15 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t x)
     asm volatile("" : "+v"(x));
     return x;
 }
+// opaque_s where ON, else x as a plain constant (no asm statement at all)
+template <bool ON>
+__device__ __forceinline__ uint32_t opaque_s_if(uint32_t x)
+{
+    if constexpr (ON)
+        return opaque_s(x);
+    else
+        return x;
+}
 
 // Four half2 registers -> one MFMA operand.
 __device__ __forceinline__ half8 cat8(half2v a, half2v b, half2v c, half2v d)
@@ -641,15 +650,41 @@ __device__ __forceinline__ half8 k_operand_sub(uint32_t w, const Unpacker &u)
 // elements of a K operand that read n * 2^-20 (their query elements are / 16)
 __device__ __forceinline__ constexpr bool k_elem_fine(int j) { return (j & 2) != 0; }
 
+// 8-bit codes. Two K words (dimensions 8o..8o+7 of one row, four bytes each)
+// as an MFMA operand: a byte moved into bits 0-7 of a half whose upper byte
+// is zero is the exact fp16 subnormal n * 2^-24 (at most 255 * 2^-24), so
+// one AND and one byte permute give two operand halves each. Element j holds
+// dimension kPerm8[j]; the score factor carries the 2^24 as for int4 codes.
+constexpr int kPerm8[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+
+__device__ __forceinline__ half8 k_operand8(uint32_t w0, uint32_t w1, uint32_t m_even, uint32_t sel_odd)
+{
+    return cat8(as_h2(w0 & m_even), as_h2(__builtin_amdgcn_perm(0u, w0, sel_odd)), as_h2(w1 & m_even),
+                as_h2(__builtin_amdgcn_perm(0u, w1, sel_odd)));
+}
+
+// Byte m of the value words of two rows (r0 in the low half, r1 in the high
+// half) as exact fp16 values (n - 128) * 2^-24: a byte permute places each
+// code as a subnormal n * 2^-24 and one packed subtraction of 128 * 2^-24
+// centres it (exact: every operand and result is a multiple of 2^-24 below
+// 2^-14 in magnitude). Centred codes, as for int4: the matrix core truncates
+// the aligned products of one instruction, which biases sums of same-signed
+// products toward zero.
+__device__ __forceinline__ half2v v_pair8(uint32_t r0, uint32_t r1, uint32_t sel)
+{
+    const half2v c128 = {(_Float16)0x1p-17f, (_Float16)0x1p-17f};
+    return as_h2(__builtin_amdgcn_perm(r1, r0, sel)) - c128;
+}
+
 // Fused decode step: quantise this (batch, KV head)'s new K and V rows into
 // cache row a.append_row (the rule of quant_rule.h; lanes 0..D/8-1 take the
 // K words, the next D/8 lanes the V words, idle lanes only join the swaps of
 // their group), then wait until the stores are done, so that the wavefront's
 // later loads of that row, all issued after this, see the new values.
-template <int D, int NG>
+template <int D, int NG, int BITS>
 __device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvrow0)
 {
-    constexpr int W = D / 8;
+    constexpr int W = D / 8;     // lanes per row (eight values each)
     constexpr int LPG = W / NG;  // lanes per scale group
     const int lane = threadIdx.x;
     const bool active = lane < 2 * W;
@@ -667,11 +702,15 @@ __device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvr
         quant::load8<_Float16>(reinterpret_cast<const _Float16 *>(which ? a.v_new : a.k_new) + src, x);
     }
     uint16_t sb, bb;
-    const uint32_t word = quant::quantize_word<LPG>(x, sb, bb);
+    uint32_t words[BITS / 4];
+    quant::quantize_codes<LPG, BITS>(x, words, sb, bb);
     if (active) {
         const int64_t row = kvrow0 + a.append_row;
         uint32_t *dq = const_cast<uint32_t *>(which ? a.v_q : a.k_q);
-        dq[row * W + w] = word;
+        if constexpr (BITS == 4)
+            dq[row * W + w] = words[0];
+        else
+            *reinterpret_cast<uint2 *>(dq + row * (2 * W) + 2 * w) = make_uint2(words[0], words[1]);
         if (w % LPG == 0) {
             uint16_t *ds = const_cast<uint16_t *>(which ? a.v_scale : a.k_scale);
             uint16_t *db = const_cast<uint16_t *>(which ? a.v_bias : a.k_bias);
@@ -684,15 +723,28 @@ __device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvr
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
-template <int D, int NG, bool Q32, int PF>
+template <int D, int NG, bool Q32, int PF, int BITS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
 void sdpa_partial_mfma1_kernel(PartialArgs a)
 {
-    constexpr int W = D / 8;
-    constexpr int WPL = W / 4;
-    constexpr int KM = W / 4;
-    constexpr int VS = W / 16;
-    constexpr int WPG = W / NG;
+    // BITS = 8: byte codes, two words per eight dimensions. K operands and
+    // value codes are fp16 subnormals (n * 2^-24, values centred by 128). The
+    // value weights p * s_v are carried times WS = 2^6: byte scales are 17
+    // times finer than int4 ones, and the factor keeps the weights' fp16
+    // halves as far above the subnormal range as with int4 codes, while
+    // p * s_v * 2^6 <= 514 * 64 stays below the fp16 maximum for any fp16
+    // input range. The value products are multiplied by VU = 2^24 / WS when
+    // the partial state is written.
+    constexpr bool B8 = BITS == 8;
+    constexpr int W = D * BITS / 32;  // words per row
+    constexpr int WPL = W / 4;        // K words per lane: a quarter row
+    constexpr int KM = D / 32;        // score products per 16-row block
+    constexpr int VS = D / 128;       // sets of 16 value columns (eight dimensions each)
+    constexpr int VW = BITS / 4;      // value words per row and column
+    constexpr int WPG = D / 8 / NG;   // eight-dimension columns per scale group
+    constexpr float VC = B8 ? 128.0f : 8.0f;     // centre of the value codes
+    constexpr float WS = B8 ? 64.0f : 1.0f;      // scale of the value weights
+    constexpr float VU = B8 ? 262144.0f : 1.0f;  // unit of the value products: 2^24 / WS
     constexpr int PAIRS = TILE * NG;        // (row, group) pairs of scale/bias per tile
     constexpr int MP = (PAIRS + 63) / 64;   // pairs per lane (NG = 1: lanes 32-63 repeat 0-31)
     // D = 128 with two scale groups: value products group by group, with the
@@ -724,7 +776,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     const int ntile = (t1 - t0 + TILE - 1) / TILE;
     const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
     if (a.append_row >= t0 && a.append_row < t1)  // uniform: the fused decode step's new row is in this chunk
-        append_new_row<D, NG>(a, b, kvh, kvrow0);
+        append_new_row<D, NG, BITS>(a, b, kvh, kvrow0);
     const uint32_t rows_ok = (uint32_t)a.skv;
     const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
     const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
@@ -739,10 +791,15 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     //   x: s_k * c * 2^24     (c = softmax scale * log2 e; 2^24 undoes the
     //                          subnormal scale of the K operands)
     //   y: b_k * c
-    //   z: s_v
-    //   w: b_v + 8 s_v        (bias of the centred value codes)
+    //   z: s_v * WS
+    //   w: b_v + VC s_v       (bias of the value codes centred by VC)
     __shared__ __align__(16) float4 mring[2][PAIRS];
     const Unpacker unpack = Unpacker::make();
+    const uint32_t m_even = opaque_s_if<B8>(0x00FF00FFu), sel_odd = opaque_s_if<B8>(0x0C030C01u);  // 8-bit K
+    // 8-bit value pairs: byte m of the low source word into bits 0-7, byte m
+    // of the high one into bits 16-23, zeros elsewhere
+    const uint32_t sel_b[4] = {opaque_s_if<B8>(0x0C040C00u), opaque_s_if<B8>(0x0C050C01u),
+                               opaque_s_if<B8>(0x0C060C02u), opaque_s_if<B8>(0x0C070C03u)};
     const float cs = a.score_scale;
     const float cs24 = cs * 16777216.0f;  // c * 2^24
 
@@ -752,7 +809,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
 #pragma unroll
         for (int u = 0; u < KM; ++u) {
-            const int word = WPL * q4 + u;
+            const int word = KM * q4 + u;  // dimensions 8 word .. 8 word + 7
             if constexpr (Q32) {
                 const float *qp = reinterpret_cast<const float *>(a.q) + qrow + 8 * word;
                 const float4 x0 = *reinterpret_cast<const float4 *>(qp);
@@ -773,13 +830,13 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // zeros without touching memory. Unconditional requests keep the number
     // of loads in flight the same on every path, so each wait only covers the
     // data about to be used instead of draining the whole ring.
-    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D / 2 < 2^31)
+    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D * BITS / 8 < 2^31)
     uint4 kbuf[PF][2][WPL / 4];
-    uint32_t vbuf[PF][VS][8];
+    uint32_t vbuf[PF][VS][8 * VW];
     uint32_t mbuf[PF][MP][4];
     // scale/bias of a tile first, then its K and V words (a wait for the
     // scale/bias of the next tile then leaves that tile's words in flight)
-    auto load_tile = [&](int ti, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8], uint32_t (&mt)[MP][4]) {
+    auto load_tile = [&](int ti, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8 * VW], uint32_t (&mt)[MP][4]) {
         const bool in = ti < ntile;
 #pragma unroll
         for (int p = 0; p < MP; ++p) {
@@ -797,13 +854,20 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             for (int v4 = 0; v4 < WPL / 4; ++v4)
                 kt[blk][v4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
         }
-        const uint32_t voff = base + (uint32_t)((4 * q4 * W + col) * 4);
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + VW * col) * 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int s2 = 0; s2 < VS; ++s2)
-                vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(
-                    vq, voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * s2) * 4, 0, 0);
+            for (int s2 = 0; s2 < VS; ++s2) {
+                const uint32_t o = voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * VW * s2) * 4;
+                if constexpr (B8) {
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
+                    vt[s2][2 * j] = x[0];
+                    vt[s2][2 * j + 1] = x[1];
+                } else {
+                    vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, o, 0, 0);
+                }
+            }
     };
     auto stage_meta = [&](int slot, const uint32_t (&mt)[MP][4]) {
 #pragma unroll
@@ -813,7 +877,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             const float kb = h_val((uint16_t)mt[p][1]);
             const float vs = h_val((uint16_t)mt[p][2]);
             const float vb = h_val((uint16_t)mt[p][3]);
-            mring[slot][pr] = make_float4(ks * cs24, kb * cs, vs, fmaf(8.0f, vs, vb));
+            mring[slot][pr] = make_float4(ks * cs24, kb * cs, vs * WS, fmaf(VC, vs, vb));
         }
         // LDS instructions of a wavefront execute in order, so the tile code
         // sees these records; only the compiler must not move reads above
@@ -837,12 +901,12 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     float qsum = 0.0f;
 #pragma unroll
     for (int u = 0; u < KM; ++u) {
-        const int word = WPL * q4 + u;
+        const int word = KM * q4 + u;
         const bool mine = col_on && (word / WPG) == gl;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float unit = k_elem_fine(j) ? 16.0f : 1.0f;
-            const float x = mine ? qv[u][kPerm[j]] * (1.0f / unit) : 0.0f;
+            const float unit = (!B8 && k_elem_fine(j)) ? 16.0f : 1.0f;
+            const float x = mine ? qv[u][B8 ? kPerm8[j] : kPerm[j]] * (1.0f / unit) : 0.0f;
             const _Float16 hi = (_Float16)x;
             qhi[u][j] = hi;
             if constexpr (Q32) {
@@ -878,7 +942,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             const int ti = kk + u;
             const int slot = u & 1;  // PF is even, so this is ti & 1
             const uint4 (&kcur)[2][WPL / 4] = kbuf[u];
-            const uint32_t (&vcur)[VS][8] = vbuf[u];
+            const uint32_t (&vcur)[VS][8 * VW] = vbuf[u];
 
             // factors of the tile's 8 rows held by this lane: rows 4*q4 + i
             // (i < 4) and 16 + 4*q4 + i - 4 (i >= 4), column group gl
@@ -894,9 +958,16 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int uu = 0; uu < KM; ++uu) {
-                    const uint4 x = kcur[blk][uu / 4];
-                    const uint32_t w = (uu % 4 == 0) ? x.x : (uu % 4 == 1) ? x.y : (uu % 4 == 2) ? x.z : x.w;
-                    const half8 ka = k_operand_sub(w, unpack);
+                    half8 ka;
+                    if constexpr (B8) {
+                        const uint4 x = kcur[blk][uu / 2];
+                        ka = (uu % 2 == 0) ? k_operand8(x.x, x.y, m_even, sel_odd)
+                                           : k_operand8(x.z, x.w, m_even, sel_odd);
+                    } else {
+                        const uint4 x = kcur[blk][uu / 4];
+                        const uint32_t w = (uu % 4 == 0) ? x.x : (uu % 4 == 1) ? x.y : (uu % 4 == 2) ? x.z : x.w;
+                        ka = k_operand_sub(w, unpack);
+                    }
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[uu], sacc, 0, 0, 0);
                     if constexpr (Q32)
                         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[uu], sacc, 0, 0, 0);
@@ -993,29 +1064,69 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 // group-1 word; in group g's products a lane whose word is in
                 // g gives its dimensions 0..3, the others dimensions 4..7 of
                 // the word of lane l ^ 8 (see the store)
-                uint32_t bx[2][4];
+                if constexpr (B8) {
+                    // the same exchange on whole words: row r's words hold
+                    // dimensions 0..3 and 4..7 of the lane's eight; rows
+                    // (2jp, 2jp + 1) meet byte by byte in each operand pair
+                    uint32_t bx[2][8];
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    const uint32_t xw = __builtin_amdgcn_perm(vcur[0][2 * jp + 1], vcur[0][2 * jp], 0x05040100u);
-                    const uint32_t yw = __builtin_amdgcn_perm(vcur[0][2 * jp + 1], vcur[0][2 * jp], 0x07060302u);
-                    bx[0][jp] = take_half_row<0xC>(xw, yw);
-                    bx[1][jp] = take_half_row<0x3>(xw, yw);
-                }
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-#pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) {
-                        half2v e[4];
-#pragma unroll
-                        for (int jp = 0; jp < 4; ++jp)
-                            e[jp] = unpack.one(bx[g][jp], mm);
-                        const half8 bv = cat8(e[0], e[1], e[2], e[3]);
-                        acc[0][4 * g + mm] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(g ? a1 : a0, bv, acc[0][4 * g + mm], 0, 0, 0);
+                    for (int r = 0; r < 8; ++r) {
+                        bx[0][r] = take_half_row<0xC>(vcur[0][2 * r], vcur[0][2 * r + 1]);
+                        bx[1][r] = take_half_row<0x3>(vcur[0][2 * r], vcur[0][2 * r + 1]);
                     }
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+#pragma unroll
+                        for (int mm = 0; mm < 4; ++mm) {
+                            half2v e[4];
+#pragma unroll
+                            for (int jp = 0; jp < 4; ++jp)
+                                e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm]);
+                            const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                            acc[0][4 * g + mm] =
+                                __builtin_amdgcn_mfma_f32_16x16x32_f16(g ? a1 : a0, bv, acc[0][4 * g + mm], 0, 0, 0);
+                        }
+                } else {
+                    uint32_t bx[2][4];
+#pragma unroll
+                    for (int jp = 0; jp < 4; ++jp) {
+                        const uint32_t xw = __builtin_amdgcn_perm(vcur[0][2 * jp + 1], vcur[0][2 * jp], 0x05040100u);
+                        const uint32_t yw = __builtin_amdgcn_perm(vcur[0][2 * jp + 1], vcur[0][2 * jp], 0x07060302u);
+                        bx[0][jp] = take_half_row<0xC>(xw, yw);
+                        bx[1][jp] = take_half_row<0x3>(xw, yw);
+                    }
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+#pragma unroll
+                        for (int mm = 0; mm < 4; ++mm) {
+                            half2v e[4];
+#pragma unroll
+                            for (int jp = 0; jp < 4; ++jp)
+                                e[jp] = unpack.one(bx[g][jp], mm);
+                            const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                            acc[0][4 * g + mm] =
+                                __builtin_amdgcn_mfma_f32_16x16x32_f16(g ? a1 : a0, bv, acc[0][4 * g + mm], 0, 0, 0);
+                        }
+                }
             } else {
 #pragma unroll
                 for (int s2 = 0; s2 < VS; ++s2) {
+                    if constexpr (B8) {
+                        // column dimension m of rows (2jp, 2jp + 1): byte m & 3
+                        // of their first (m < 4) or second word
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            half2v e[4];
+#pragma unroll
+                            for (int jp = 0; jp < 4; ++jp)
+                                e[jp] = v_pair8(vcur[s2][4 * jp + (m >> 2)], vcur[s2][4 * jp + 2 + (m >> 2)],
+                                                sel_b[m & 3]);
+                            const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                            acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
+                            acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
+                        }
+                        continue;
+                    }
                     // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
                     // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
                     uint32_t xw[4], yw[4];
@@ -1078,7 +1189,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 // second
                 const auto sw = __builtin_amdgcn_permlane32_swap(a0, a1, false, false);
                 const uint32_t x = sw[0], y = sw[1];
-                o[r][mm] = fmaf(__builtin_bit_cast(float, y), 1.0f / kLoScale, __builtin_bit_cast(float, x));
+                o[r][mm] = fmaf(__builtin_bit_cast(float, y), VU / kLoScale, __builtin_bit_cast(float, x) * VU);
             }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1103,10 +1214,10 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             for (int s = 0; s < VS; ++s) {
                 const int word = 16 * s + col;
                 if (word / WPG == g) {
-                    float4 lo = {acc[s][0][i] + bias_r, acc[s][1][i] + bias_r, acc[s][2][i] + bias_r,
-                                 acc[s][3][i] + bias_r};
-                    float4 hi = {acc[s][4][i] + bias_r, acc[s][5][i] + bias_r, acc[s][6][i] + bias_r,
-                                 acc[s][7][i] + bias_r};
+                    float4 lo = {acc[s][0][i] * VU + bias_r, acc[s][1][i] * VU + bias_r, acc[s][2][i] * VU + bias_r,
+                                 acc[s][3][i] * VU + bias_r};
+                    float4 hi = {acc[s][4][i] * VU + bias_r, acc[s][5][i] * VU + bias_r, acc[s][6][i] * VU + bias_r,
+                                 acc[s][7][i] * VU + bias_r};
                     *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
                     *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
                 }
@@ -1414,11 +1525,14 @@ void sdpa_partial_mfma_pair_kernel(PartialArgs a)
     }
 }
 
-template <int D, int NG, bool Q32>
+template <int D, int NG, bool Q32, int BITS>
 void launch_one_wave(const PartialArgs &a, dim3 grid, const Launch &l)
 {
-    constexpr int PF = D == 128 ? 4 : 2;
-    hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF>), grid, dim3(64), 0, l.s, l.start, l.stop, 0, a);
+    // tiles in flight: 8-bit tiles are twice as large, so two of them carry
+    // as many bytes as four int4 tiles
+    constexpr int PF = (D == 128 && BITS == 4) ? 4 : 2;
+    hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF, BITS>), grid, dim3(64), 0, l.s, l.start, l.stop,
+                          0, a);
 }
 
 template <int NG>
@@ -1447,9 +1561,26 @@ bool pair_fits(const PartialArgs &a, int D, int q_dtype, int batch)
     return D == 128 && q_dtype == KVQ_F16 && one_wave_fits(a, D, batch);
 }
 
+// 8-bit caches: the one-wavefront kernel only
+template <int D, int NG>
+hipError_t launch_dg8(const PartialArgs &a, int q_dtype, int batch, int variant, const Launch &l)
+{
+    dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
+    if ((variant != KVQ_KERNEL_AUTO && variant != KVQ_KERNEL_MFMA && variant != KVQ_KERNEL_MFMA_WAVE) ||
+        !one_wave_fits(a, D, batch))
+        return hipErrorInvalidValue;
+    if (q_dtype == KVQ_F32)
+        launch_one_wave<D, NG, true, 8>(a, grid, l);
+    else
+        launch_one_wave<D, NG, false, 8>(a, grid, l);
+    return hipGetLastError();
+}
+
 template <int D, int NG>
 hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, const Launch &l)
 {
+    if (a.bits == 8)
+        return launch_dg8<D, NG>(a, q_dtype, batch, variant, l);
     dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
     const int64_t items = (int64_t)a.num_chunks * a.Hkv * batch;
     bool pair = variant == KVQ_KERNEL_MFMA_PAIR;
@@ -1463,9 +1594,9 @@ hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, 
             launch_pair<NG>(a, grid, l);
     } else if (one) {
         if (q_dtype == KVQ_F32)
-            launch_one_wave<D, NG, true>(a, grid, l);
+            launch_one_wave<D, NG, true, 4>(a, grid, l);
         else
-            launch_one_wave<D, NG, false>(a, grid, l);
+            launch_one_wave<D, NG, false, 4>(a, grid, l);
     } else if (q_dtype == KVQ_F32) {
         hipExtLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, true>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
     } else {
@@ -1489,7 +1620,7 @@ bool mfma_supports(int D, int G, int n_rep, int chunk)
 
 hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l)
 {
-    if (a.bits != 4)  // these kernels read int4 codes only
+    if (a.bits != 4 && a.bits != 8)
         return hipErrorInvalidValue;
     const int NG = D / a.G;
     if (D == 128) {

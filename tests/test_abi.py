@@ -141,10 +141,16 @@ def test_bits_validation(L):
     assert _append(L, _cache(capacity=(0x7fff0000 // 64) + 1, bits=4), length=0, n=0) == E_SHAPE
     assert _append(L, _cache(capacity=0x7fff0000 // 128, bits=8), length=0, n=0) == OK
     assert _append(L, _cache(capacity=(0x7fff0000 // 128) + 1, bits=8), length=0, n=0) == E_SHAPE
-    # the matrix-core kernels read int4 codes only
-    for k in (2, 3, 4, 5):
+    # 8-bit caches have one matrix-core kernel, the one-wavefront one: the
+    # four-wavefront and pair variants refuse them (the accepted variants are
+    # exercised by the GPU tests; a call here that passed validation would
+    # launch on placeholder pointers)
+    for k in (3, 5):
         assert _partial(L, _cache(bits=8), kernel=k) == E_UNSUP, k
         assert _step(L, _cache(bits=8), kernel=k) == E_UNSUP, k
+    # ... and it needs chunks of at most 512 rows
+    assert _partial(L, _cache(bits=8), kernel=4, chunk=1024) == E_UNSUP
+    assert _partial(L, _cache(bits=8), kernel=2, chunk=1024) == E_UNSUP
 
 
 def _append_rot(L, cache, length=0, k=P, v=P, dtype=0, n=1):

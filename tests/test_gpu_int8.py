@@ -1,8 +1,9 @@
 """GPU parity of the 8-bit cache (the Gemma page's "What I Tried" table lists
 an int8 KV cache; the blog's decode driver takes 4 or 8 KV bits): the append
-kernel must write the oracle's bytes bit for bit, the vector-ALU attention
-must match the float64 oracle on the 8-bit cache within the fp32 gates of the
-int4 tests, and the matrix-core variants must refuse the format."""
+kernel must write the oracle's bytes bit for bit; the vector-ALU and the
+one-wavefront matrix-core attention must match the float64 oracle on the
+8-bit cache within the gates of the int4 tests; the other matrix-core
+variants must refuse the format."""
 
 import numpy as np
 import pytest
@@ -18,7 +19,21 @@ from test_gpu_quantize import _append_and_check, _boundary_rows, _special_rows
 pytestmark = pytest.mark.gpu
 
 REL_L2 = 2e-5            # the vector-ALU gate of the int4 tests (fp32 throughout)
+MFMA_REL_L2 = 1e-4       # the matrix-core gate of the int4 tests
 REL_L2_UNSCALED = 2e-4   # softmax scale 1: score rounding passes undamped into the weights
+KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_AUTO]
+GATE = {kvq.KERNEL_VALU: REL_L2, kvq.KERNEL_MFMA_WAVE: MFMA_REL_L2, kvq.KERNEL_AUTO: MFMA_REL_L2}
+
+
+def _run(gc, skv, q, alpha, kernel, chunk=512):
+    """run_sdpa, skipping a forced one-wavefront run on a chunk it does not
+    take (AUTO falls back to the vector-ALU kernel there)."""
+    try:
+        return run_sdpa(gc, skv, q, alpha, chunk=chunk, kernel=kernel)
+    except kvq.KvqError as e:
+        if kernel == kvq.KERNEL_MFMA_WAVE and e.status == -7:
+            pytest.skip("chunk outside the one-wavefront kernel")
+        raise
 
 
 def _oracle_cache(k, v, cap=None, G=64):
@@ -84,33 +99,39 @@ def test_append_llama_full_length():
 
 # --------------------------------------------------------------- attention
 
-@pytest.mark.parametrize("kernel", [kvq.KERNEL_VALU, kvq.KERNEL_AUTO])
-@pytest.mark.parametrize("skv,chunk", [(1, 512), (33, 512), (512, 512), (513, 512), (1000, 100), (1000, 3),
-                                       (1500, 256), (1000, 2048)])
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("skv,chunk", [(1, 512), (33, 512), (512, 512), (513, 512), (1000, 8), (1000, 64),
+                                       (1000, 100), (1000, 3), (1500, 256), (1000, 2048)])
 def test_ragged(kernel, skv, chunk):
     note("int8 sdpa ragged skv=%d chunk=%d kernel=%d" % (skv, chunk, kernel))
     q = kvq_synth.normal((1, 8, 128), [180, skv, 0]).astype(np.float16)
     k = kvq_synth.normal((1, 2, 1536, 128), [180, 1]).astype(np.float16)
     v = kvq_synth.normal((1, 2, 1536, 128), [180, 2]).astype(np.float16)
     oc = _oracle_cache(k, v)
-    out, *_ = run_sdpa(gpu_cache_from_oracle(oc), skv, q, 0.0884, chunk=chunk, kernel=kernel)
-    check_attention(out, oracle.sdpa(oc, skv, q, 0.0884), REL_L2, label="int8 ragged")
+    out, *_ = _run(gpu_cache_from_oracle(oc), skv, q, 0.0884, kernel, chunk=chunk)
+    check_attention(out, oracle.sdpa(oc, skv, q, 0.0884), GATE[kernel], label="int8 ragged")
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,D,G,qdt", [(2, 4, 4, 64, 32, np.float32), (1, 6, 2, 128, 64, np.float16),
                                               (1, 16, 1, 128, 64, np.float16), (1, 8, 1, 256, 128, np.float32),
                                               (1, 2, 2, 256, 64, np.float16), (2, 8, 2, 128, 32, np.float32),
                                               (1, 4, 1, 64, 64, np.float16)])
-def test_shapes(B, Hq, Hkv, D, G, qdt):
-    note("int8 sdpa shape B%d Hq%d Hkv%d D%d G%d" % (B, Hq, Hkv, D, G))
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_shapes(kernel, B, Hq, Hkv, D, G, qdt):
+    note("int8 sdpa shape B%d Hq%d Hkv%d D%d G%d kernel=%d" % (B, Hq, Hkv, D, G, kernel))
     S = 700
     q = kvq_synth.normal((B, Hq, D), [181, Hq, D, G, 0]).astype(qdt)
     k = kvq_synth.normal((B, Hkv, S, D), [181, Hq, D, G, 1]).astype(np.float16)
     v = kvq_synth.normal((B, Hkv, S, D), [181, Hq, D, G, 2]).astype(np.float16)
-    oc = _oracle_cache(k, v, cap=S + 9, G=G)
+    oc = _oracle_cache(k, v, cap=S + 12, G=G)  # (capacity * D/G a multiple of 8: one-wavefront layout)
     alpha = 1 / np.sqrt(D)
-    out, *_ = run_sdpa(gpu_cache_from_oracle(oc), S, q, alpha)
-    check_attention(out, oracle.sdpa(oc, S, q, alpha), REL_L2, label="int8 shape")
+    try:
+        out, *_ = run_sdpa(gpu_cache_from_oracle(oc), S, q, alpha, kernel=kernel)
+    except kvq.KvqError as e:
+        if kernel == kvq.KERNEL_MFMA_WAVE and e.status == -7:
+            pytest.skip("shape outside the matrix-core kernels")  # D = 64, or more than 16 (head, group) columns
+        raise
+    check_attention(out, oracle.sdpa(oc, S, q, alpha), GATE[kernel], label="int8 shape")
 
 
 def test_partials_match_oracle():
@@ -124,12 +145,13 @@ def test_partials_match_oracle():
     np.testing.assert_allclose(acc / l[..., None], racc / rl[..., None], rtol=1e-3, atol=1e-4)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("skv", [423, 4096])
-def test_gemma_unscaled(skv):
-    note("int8 sdpa gemma skv=%d" % skv)
+def test_gemma_unscaled(kernel, skv):
+    note("int8 sdpa gemma skv=%d kernel=%d" % (skv, kernel))
     q, k, v, alpha = kvq_synth.gemma_layer(skv)
-    oc = _oracle_cache(k, v)
-    out, *_ = run_sdpa(gpu_cache_from_oracle(oc), skv, q, alpha)
+    oc = _oracle_cache(k, v, cap=(skv + 7) // 8 * 8)
+    out, *_ = _run(gpu_cache_from_oracle(oc), skv, q, alpha, kernel)
     check_attention(out, oracle.sdpa(oc, skv, q, alpha), REL_L2_UNSCALED, atol=1e-3, rtol=1e-3, label="int8 gemma")
 
 
@@ -149,7 +171,10 @@ def test_llama_layer(skv):
         oc = _oracle_cache(np.ascontiguousarray(k[:, h:h + 1]), np.ascontiguousarray(v[:, h:h + 1]))
         refs.append(oracle.sdpa(oc, skv, np.ascontiguousarray(q[:, 8 * h:8 * h + 8]), alpha))
     got = np.concatenate([out[:, 8 * h:8 * h + 8] for h in heads], axis=1)
-    check_attention(got, np.concatenate(refs, axis=1), REL_L2, label="int8 llama")
+    check_attention(got, np.concatenate(refs, axis=1), MFMA_REL_L2, label="int8 llama")
+    if skv <= 16384:  # the vector-ALU kernel on the same cache
+        out_v, *_ = run_sdpa(gc, skv, q, alpha, kernel=kvq.KERNEL_VALU)
+        check_attention(out_v, np.concatenate(refs, axis=1), REL_L2, label="int8 llama valu")
 
 
 def test_closer_to_float_attention_than_int4():
@@ -174,12 +199,14 @@ def test_closer_to_float_attention_than_int4():
 
 # ------------------------------------------------------------- decode step
 
-@pytest.mark.parametrize("length", [0, 511, 1000])
-def test_decode_step(length):
-    """Append + attention in one call on the 8-bit cache (three launches:
-    append, vector-ALU partial, reduce): cache bit for bit as the append
-    alone, output bit for bit as the separate calls, and near the oracle."""
-    note("int8 decode step len=%d" % length)
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("length", [0, 511, 512, 1000])
+def test_decode_step(kernel, length):
+    """Append + attention in one call on the 8-bit cache (the append inside
+    the one-wavefront kernel, or append, vector-ALU partial and reduce):
+    cache bit for bit as the append alone, output bit for bit as the
+    separate calls with the same kernel, and near the oracle."""
+    note("int8 decode step len=%d kernel=%d" % (length, kernel))
     q, k, v, alpha = kvq_synth.llama_layer(length + 1)
     cap = 1024 + 8
     oc = oracle.Cache(1, 8, 128, cap, 64, bits=8)
@@ -189,19 +216,36 @@ def test_decode_step(length):
     vn = np.ascontiguousarray(v[:, :, length:length + 1])
     g1, g2 = gpu_cache_from_oracle(oc), gpu_cache_from_oracle(oc)
     qd, knd, vnd = to_dev(q), to_dev(kn), to_dev(vn)
-    out1 = kvq.decode_step(g1, length, knd, vnd, qd, alpha)
+    out1 = kvq.decode_step(g1, length, knd, vnd, qd, alpha, kernel=kernel)
     kvq.quantize_kv_append(g2, length, knd, vnd)
-    out2 = kvq.sdpa_int4(g2, length + 1, qd, alpha)
+    out2 = kvq.sdpa_int4(g2, length + 1, qd, alpha, kernel=kernel)
     torch.cuda.synchronize()
     oc.append(kn, vn, length)
     assert_cache_equal(g1, oc)
     got = out1.cpu().numpy()
     assert np.array_equal(got, out2.cpu().numpy())
-    check_attention(got, oracle.sdpa(oc, length + 1, q, alpha), REL_L2, label="int8 step")
+    check_attention(got, oracle.sdpa(oc, length + 1, q, alpha), GATE[kernel], label="int8 step")
 
 
-@pytest.mark.parametrize("kernel", [kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE,
-                                    kvq.KERNEL_MFMA_PAIR])
+@pytest.mark.parametrize("length", [511, 1023])
+def test_decode_step_fp32_inputs(length):
+    """fp32 K/V rows and fp32 q (the split-query matrix-core path)."""
+    note("int8 decode step fp32 len=%d" % length)
+    q, k, v, alpha = kvq_synth.tiny_decode(skv=length + 1)
+    B, Hkv, _, D = k.shape
+    oc = oracle.Cache(B, Hkv, D, length + 1, 64, bits=8)
+    oc.append(np.ascontiguousarray(k[:, :, :length]), np.ascontiguousarray(v[:, :, :length]), 0)
+    kn = np.ascontiguousarray(k[:, :, length:])
+    vn = np.ascontiguousarray(v[:, :, length:])
+    g = gpu_cache_from_oracle(oc)
+    out = kvq.decode_step(g, length, to_dev(kn), to_dev(vn), to_dev(q), alpha, kernel=kvq.KERNEL_MFMA_WAVE)
+    torch.cuda.synchronize()
+    oc.append(kn, vn, length)
+    assert_cache_equal(g, oc)
+    check_attention(out.cpu().numpy(), oracle.sdpa(oc, length + 1, q, alpha), MFMA_REL_L2, label="int8 step fp32")
+
+
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_PAIR])
 def test_matrix_core_variants_refuse_int8(kernel):
     note("int8 refused by kernel=%d" % kernel)
     gc = kvq.QuantKVCache(1, 8, 128, 1024, 64, device="cuda", bits=8)
