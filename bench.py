@@ -38,22 +38,26 @@ MALL_BYTES = 256 << 20
 B, HQ, HKV, D, G = 1, 64, 8, 128, 64
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sdpa_partial_llama_128k_traffic.txt")
+TRAFFIC_FILES = {
+    4: os.path.join(ROOT, "profiles", "sdpa_partial_llama_128k_traffic.txt"),
+    8: os.path.join(ROOT, "profiles", "sdpa_partial_int8_llama_128k_traffic.txt"),
+}
 
 
-def measured_traffic(skv: int, chunk: int, kernel: str):
+def measured_traffic(skv: int, chunk: int, kernel: str, bits: int = 4):
     """HBM bytes per partial launch from the committed counter summary, or
     None when this run is not the profiled configuration or the kernel
     sources changed since the counters were taken (their hash differs)."""
     if skv != 131072 or chunk != 512 or kernel not in ("auto", "mfma", "mfma-wave"):
         return None
+    path = TRAFFIC_FILES[bits]
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        root = os.path.dirname(TRAFFIC_FILE)
+        root = os.path.dirname(path)
         h = hashlib.sha256()
         for rel in kv["source_files"].split():
             with open(os.path.join(root, "..", rel), "rb") as f:
@@ -329,13 +333,15 @@ def main():
         att8 = layer_bytes(s8, 8) / (i8["partial_ms_avg"] * 1e-3) / 1e9
         next_rows["int8"] = {
             "workload": "the headline layer (B1 Hq64 Hkv8 D128 G64, Skv %d) with 8-bit codes: decode step "
-                        "(append, vector-ALU partial, reduce); bulk append of the outlier-workload shape" % s8,
+                        "(append inside the one-wavefront matrix-core attention kernel, then the reduce); bulk "
+                        "append of the outlier-workload shape" % s8,
             "layer_bytes": layer_bytes(s8, 8),
             "step_us": round(i8["ms_per_step"] * 1e3, 3),
             "step_gbs": round((layer_bytes(s8, 8) + append_bytes(8)) / (i8["ms_per_step"] * 1e-3) / 1e9, 2),
             "attention_us": round(i8["partial_ms_avg"] * 1e3, 3),
             "attention_gbs": round(att8, 2),
             "attention_frac": round(att8 / HBM_PEAK_GBS, 4),
+            "attention_traffic": measured_traffic(s8, args.chunk, "auto", 8),
             "append_us": round(i8_ms * 1e3, 3),
             "append_gbs": round(nb8 / (i8_ms * 1e-3) / 1e9, 2),
             "timing": "step and attention as the headline; append as the hadamard row's",
@@ -385,7 +391,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.skv, args.chunk, args.kernel) if bits == 4 else None,
+            "traffic": measured_traffic(args.skv, args.chunk, args.kernel, bits),
             "bytes_per_launch": layer_bytes(args.skv, bits),
             "avg_launch_us": round(main_res["partial_ms_avg"] * 1e3, 3),
             "timing": "HIP events recorded in the kernel's own dispatch (hipExtLaunchKernel), averaged over the steps",
