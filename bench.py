@@ -69,35 +69,39 @@ def measured_traffic(skv: int, chunk: int, kernel: str, bits: int = 4):
         return None
 
 
-def layer_bytes(skv: int, bits: int = 4) -> int:
-    return HKV * skv * (D * bits // 8 + 4 * (D // G)) * 2  # K and V: codes + fp16 scale + fp16 bias
+def layer_bytes(skv: int, bits: int = 4, hkv: int = HKV) -> int:
+    return hkv * skv * (D * bits // 8 + 4 * (D // G)) * 2  # K and V: codes + fp16 scale + fp16 bias
 
 
-def append_bytes(bits: int = 4) -> int:
-    return 2 * B * HKV * D * 2 + 2 * B * HKV * (D * bits // 8 + 4 * (D // G))  # fp16 rows in, packed row out
+def append_bytes(bits: int = 4, hkv: int = HKV) -> int:
+    return 2 * B * hkv * D * 2 + 2 * B * hkv * (D * bits // 8 + 4 * (D // G))  # fp16 rows in, packed row out
 
 
-def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 1234, bits: int = 4):
-    n_layers = max(2, math.ceil(pool_bytes / layer_bytes(skv, bits)))
+def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 1234, bits: int = 4, hkv: int = HKV):
+    """Distinct layers of the Llama-shaped cache (hkv KV heads, 8 query heads
+    each) totalling at least pool_bytes, filled with seeded fp16 N(0,1) rows
+    quantised by the library."""
+    hq = 8 * hkv
+    n_layers = max(2, math.ceil(pool_bytes / layer_bytes(skv, bits, hkv)))
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     pool = []
     for i in range(n_layers):
         gen.manual_seed(seed * 1000003 + skv * 131 + i)
-        cache = kvq.QuantKVCache(B, HKV, D, skv, G, device=dev, bits=bits)
+        cache = kvq.QuantKVCache(B, hkv, D, skv, G, device=dev, bits=bits)
         # fill in slabs so the fp16 staging stays small
         slab = 16384
         for t0 in range(0, skv, slab):
             n = min(slab, skv - t0)
-            k = torch.randn((B, HKV, n, D), generator=gen, device=dev, dtype=torch.float32).half()
-            v = torch.randn((B, HKV, n, D), generator=gen, device=dev, dtype=torch.float32).half()
+            k = torch.randn((B, hkv, n, D), generator=gen, device=dev, dtype=torch.float32).half()
+            v = torch.randn((B, hkv, n, D), generator=gen, device=dev, dtype=torch.float32).half()
             kvq.quantize_kv_append(cache, t0, k, v)
-        q = torch.randn((B, HQ, D), generator=gen, device=dev, dtype=torch.float32).half()
-        k_new = torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.float32).half()
-        v_new = torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.float32).half()
-        ws = kvq.partials_buffers(B, HQ, D, skv, chunk, device=dev)
-        out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
-        qr = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+        q = torch.randn((B, hq, D), generator=gen, device=dev, dtype=torch.float32).half()
+        k_new = torch.randn((B, hkv, 1, D), generator=gen, device=dev, dtype=torch.float32).half()
+        v_new = torch.randn((B, hkv, 1, D), generator=gen, device=dev, dtype=torch.float32).half()
+        ws = kvq.partials_buffers(B, hq, D, skv, chunk, device=dev)
+        out = torch.empty((B, hq, D), dtype=torch.float32, device=dev)
+        qr = torch.empty((B, hq, D), dtype=torch.float32, device=dev)
         pool.append(dict(cache=cache, q=q, k_new=k_new, v_new=v_new, ws=ws, out=out, qr=qr))
     torch.cuda.synchronize()
     return pool
@@ -137,8 +141,8 @@ def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"
             kvq.hadamard_rotate(L["out"], out=L["out"], stream=stream)
 
 
-def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused", bits=4):
-    pool = make_pool(kvq, torch, skv, pool_bytes, chunk, bits=bits)
+def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused", bits=4, hkv=HKV):
+    pool = make_pool(kvq, torch, skv, pool_bytes, chunk, bits=bits, hkv=hkv)
     run_steps(kvq, torch, pool, skv, chunk, kernel, warmup, step=step)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -156,10 +160,35 @@ def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step=
     kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
     res = dict(skv=skv, ms_per_step=ms_per_step, partial_ms_avg=sum(kern_ms) / len(kern_ms),
                partial_ms_p10=kern_ms[len(kern_ms) // 10], partial_ms_p90=kern_ms[(9 * len(kern_ms)) // 10],
-               pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv, bits) / 1e6)
+               pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv, bits, hkv) / 1e6)
     last = pool[-1]
     del pool
     return res, last
+
+
+def time_layer_loop(kvq, torch, layers, skv, chunk, kernel, steps, warmup):
+    """The full-depth decode step: one decode step (fused append + attention
+    + reduce) on each of `layers` distinct caches of the Llama layer, in
+    order, on one stream; the caches stay resident in HBM. Returns ms per
+    step (all layers) and the cache bytes."""
+    pool = make_pool(kvq, torch, skv, layers * layer_bytes(skv), chunk, seed=4321)
+    assert len(pool) == layers
+    run_steps(kvq, torch, pool, skv, chunk, kernel, warmup * layers)
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(steps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        run_steps(kvq, torch, pool, skv, chunk, kernel, layers)
+        t1.record()
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1))
+    cache_bytes = sum(L["cache"].nbytes() for L in pool)
+    del pool
+    per.sort()
+    return dict(ms_median=per[len(per) // 2], ms_p10=per[len(per) // 10], ms_p90=per[(9 * len(per)) // 10],
+                ms_min=per[0], cache_bytes=cache_bytes)
 
 
 APPEND_ROWS, APPEND_LEN, APPEND_CAP = 4096, 61440, 65536  # the outlier workload's bulk append
@@ -255,6 +284,8 @@ def main():
     ap.add_argument("--step", choices=["fused", "unfused", "rotated"], default="fused",
                     help="fused: kvq_decode_step (append inside the attention kernel, then the reduce); "
                          "unfused: append, partial and reduce as three calls")
+    ap.add_argument("--layers", type=int, default=80,
+                    help="layers of the full-depth decode step timed after the headline (0 skips it)")
     ap.add_argument("--bits", type=int, choices=[4, 8], default=4,
                     help="bits per cached code of the headline run (8: the int8 cache, vector-ALU attention)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -292,6 +323,36 @@ def main():
         r["gbs"] = (layer_bytes(s, bits) + append_bytes(bits)) / (r["ms_per_step"] * 1e-3) / 1e9
         r["partial_gbs"] = layer_bytes(s, bits) / (r["partial_ms_avg"] * 1e-3) / 1e9
         sweep.append(r)
+
+    depth = None
+    if args.layers > 0:
+        lp = time_layer_loop(kvq, torch, args.layers, args.skv, args.chunk, kernel, steps=10, warmup=2)
+        step_b = args.layers * (layer_bytes(args.skv) + append_bytes())
+        depth = {
+            "workload": "%d distinct Llama-shaped layers at Skv %d resident in HBM (%.2f GB of int4 cache); one "
+                        "decode step = kvq_decode_step on every layer in order, one stream" % (
+                            args.layers, args.skv, lp["cache_bytes"] / 1e9),
+            "layers": args.layers,
+            "ms_per_step": round(lp["ms_median"], 4),
+            "ms_p10": round(lp["ms_p10"], 4),
+            "ms_p90": round(lp["ms_p90"], 4),
+            "us_per_layer": round(lp["ms_median"] * 1e3 / args.layers, 3),
+            "gbs": round(step_b / (lp["ms_median"] * 1e-3) / 1e9, 2),
+            "frac_of_hbm_peak": round(step_b / (lp["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "median of 10 steps, events around each step's %d x 2 launches" % args.layers,
+        }
+        # the one-GPU share of head sharding over 8 GPUs: one KV head and its 8 query heads
+        sh, _ = time_config(kvq, torch, args.skv, args.chunk, kernel, max(20, args.steps // 2), args.warmup,
+                            pool_bytes, step=args.step, hkv=1)
+        sb = layer_bytes(args.skv, 4, 1)
+        depth["shard_share"] = {
+            "workload": "one GPU's share of the Llama layer split over 8 GPUs by KV head: Hkv 1, Hq 8, Skv %d "
+                        "(%d bytes)" % (args.skv, sb),
+            "us_per_layer": round(sh["ms_per_step"] * 1e3, 3),
+            "gbs": round((sb + append_bytes(4, 1)) / (sh["ms_per_step"] * 1e-3) / 1e9, 2),
+            "attention_us": round(sh["partial_ms_avg"] * 1e3, 3),
+            "attention_gbs": round(sb / (sh["partial_ms_avg"] * 1e-3) / 1e9, 2),
+        }
 
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb * 1000 * 1000 // 4
@@ -402,6 +463,7 @@ def main():
         "sweep": [{"skv": r["skv"], "us_per_layer": round(r["us_per_layer"], 3), "gbs": round(r["gbs"], 2),
                    "partial_us": round(r["partial_ms_avg"] * 1e3, 3), "partial_gbs": round(r["partial_gbs"], 2)}
                   for r in sweep],
+        "full_depth": depth,
         "next_rows": next_rows,
         "context": "pages' Apple-Silicon fused-kernel latency on this shape: 1.6/2.7/5.7/9.9 ms at 1K/16K/64K/128K",
     }
