@@ -276,6 +276,22 @@ def sdpa_partials(cache: Cache, skv: int, q: np.ndarray, alpha: float, chunk: in
     return m, l, acc
 
 
+def sdpa_prefill(cache: Cache, q_start: int, q: np.ndarray, alpha: float, nthreads: int | None = None) -> np.ndarray:
+    """Prefill-side attention over the quantised cache, float64 (the README's
+    hybrid paragraph routes Sq > 1 to a separate attention; here it reads the
+    same quantised cache): q[B][Hq][Sq][D] holds the queries of positions
+    q_start .. q_start + Sq - 1, whose K/V rows are already cache rows
+    [q_start, q_start + Sq); query i attends to rows [0, q_start + i]
+    (causal). Each position is the decode attention (sdpa) over its own
+    prefix, taken one position at a time."""
+    q64 = np.asarray(q, dtype=np.float64)
+    B, Hq, Sq, D = q64.shape
+    out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    for i in range(Sq):
+        out[:, :, i] = sdpa(cache, q_start + i + 1, np.ascontiguousarray(q64[:, :, i]), alpha, nthreads)
+    return out
+
+
 def hadamard(x: np.ndarray) -> np.ndarray:
     """Normalised Hadamard rotation of the last axis (a power of two), in
     float64: y = H_n x / sqrt(n) with H_n in Sylvester order (the TurboQuant
