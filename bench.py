@@ -233,6 +233,48 @@ def time_bulk_append(kvq, torch, rotated: bool, reps: int = 40, n_inputs: int = 
     return sorted(per)[len(per) // 2]
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak
+
+
+def prefill_flops(q_start: int, sq: int, hq: int = HQ) -> int:
+    """Algorithmic flops of causal prefill attention: per query head and
+    position i, q.k and p.v over its q_start + i + 1 rows, 2 * D flops each."""
+    rows = sq * q_start + sq * (sq + 1) // 2
+    return 2 * 2 * hq * D * rows
+
+
+def time_prefill(kvq, torch, q_start: int, sq: int, reps: int = 5):
+    """Prefill attention on the Llama layer: a cache of q_start + sq rows
+    (seeded fp16 N(0,1), quantised by the library), then kvq_sdpa_int4_prefill
+    for the sq positions after q_start. Returns the median kernel time in ms
+    (events around each call; one call runs for milliseconds)."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+    S = q_start + sq
+    cache = kvq.QuantKVCache(B, HKV, D, S, G, device=dev)
+    for t0 in range(0, S, 16384):
+        n = min(16384, S - t0)
+        k = torch.randn((B, HKV, n, D), generator=gen, device=dev).half()
+        v = torch.randn((B, HKV, n, D), generator=gen, device=dev).half()
+        kvq.quantize_kv_append(cache, t0, k, v)
+    q = torch.randn((B, HQ, sq, D), generator=gen, device=dev).half()
+    out = torch.empty((B, HQ, sq, D), dtype=torch.float32, device=dev)
+    alpha = 1.0 / math.sqrt(D)
+    kvq.sdpa_int4_prefill(cache, q_start, q, alpha, out=out)
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.sdpa_int4_prefill(cache, q_start, q, alpha, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    del cache, q, out
+    return sorted(per)[len(per) // 2]
+
+
 def bulk_append_bytes(bits: int = 4) -> int:
     rows = B * HKV * APPEND_ROWS
     return 2 * rows * D * 2 + 2 * rows * (D * bits // 8 + 4 * (D // G))  # fp16 K and V in, packed rows out
@@ -407,6 +449,21 @@ def main():
             "append_gbs": round(nb8 / (i8_ms * 1e-3) / 1e9, 2),
             "timing": "step and attention as the headline; append as the hadamard row's",
         }
+        pf = {}
+        for name, qs, sq in (("chunk4096_at_61440", APPEND_LEN, APPEND_ROWS), ("prompt4096", 0, 4096)):
+            ms = time_prefill(kvq, torch, qs, sq)
+            fl = prefill_flops(qs, sq)
+            pf[name] = {
+                "q_start": qs, "sq": sq, "ms": round(ms, 4),
+                "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                "cache_gbs": round(layer_bytes(qs + sq) / (ms * 1e-3) / 1e9, 1),
+            }
+        next_rows["prefill"] = dict(
+            workload="prefill-side attention on the Llama layer's int4 cache (Hq 64, Hkv 8, D 128, fp16 q, "
+                     "causal): the outlier workload's 4096-row chunk at row 61440, and a 4096-token prompt",
+            roofline="mfma: algorithmic flops 4 * Hq * D * (rows each position sees), dense fp16 peak 2500 TFLOP/s",
+            timing="median of 5 calls, events around each (one kernel of milliseconds)", **pf)
 
     step_bytes = layer_bytes(args.skv, bits) + append_bytes(bits)
     ms = main_res["ms_per_step"]

@@ -214,6 +214,23 @@ int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtyp
                   int kernel, void *stream);
 
 /*
+ * Prefill-side attention on the quantised cache (the README's hybrid
+ * paragraph sends Sq > 1 to a separate fp16 attention before quantising;
+ * here the block's queries read the packed cache itself): the queries of
+ * positions q_start .. q_start + sq - 1, whose K/V rows must already be cache
+ * rows [q_start, q_start + sq) (append them first), with query i attending
+ * to rows [0, q_start + i] (causal):
+ *   out[b][h][i][:] = sum_{t <= q_start + i} softmax_t(softmax_scale * q_hi . k^_t) v^_t
+ *  q:    [B][Hq][sq][D] fp16, 16-byte aligned; Hq a multiple of Hkv.
+ *  out:  [B][Hq][sq][D] fp32, normalised, 16-byte aligned.
+ * One launch, no workspace. Supported: D = 128, G = 64, int4 codes, fp16
+ * queries, Hq / Hkv <= 16 (KVQ_E_UNSUPPORTED otherwise). q_start + sq beyond
+ * the capacity returns KVQ_E_CAPACITY.
+ */
+int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, const void *q, int q_dtype,
+                          int32_t Hq, float softmax_scale, float *out, void *stream);
+
+/*
  * One decode step (the README's decode-step listing: quantise the current
  * token's K and V into the cache, then the fused int4 attention with GQA):
  * writes k_new / v_new ([B][Hkv][D], kv_dtype, one row per (batch, KV head))

@@ -32,6 +32,7 @@ from ._binding import (  # noqa: F401
     sdpa_int4,
     sdpa_int4_partial,
     sdpa_int4_partial_timed,
+    sdpa_int4_prefill,
     sdpa_int4_reduce,
     status_str,
     version,

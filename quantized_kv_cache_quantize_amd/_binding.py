@@ -80,6 +80,8 @@ def lib():
     L.kvq_decode_step_timed.restype = C.c_int
     L.kvq_decode_step_timed.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int,
                                         vp, vp, vp]
+    L.kvq_sdpa_int4_prefill.restype = C.c_int
+    L.kvq_sdpa_int4_prefill.argtypes = [cp, i64, i32, vp, C.c_int, i32, f32, vp, vp]
     L.kvq_sdpa_int4.restype = C.c_int
     L.kvq_sdpa_int4.argtypes = [cp, i64, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int, vp]
     _lib = L
@@ -293,4 +295,20 @@ def decode_step(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: to
     else:
         _check("kvq_decode_step_timed",
                lib().kvq_decode_step_timed(*args, _event_handle(events[0]), _event_handle(events[1])))
+    return out
+
+
+def sdpa_int4_prefill(cache: QuantKVCache, q_start: int, q: torch.Tensor, softmax_scale: float,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_sdpa_int4_prefill: q [B][Hq][Sq][D] fp16 contiguous, the queries of
+    positions q_start .. q_start + Sq - 1 (their K/V rows already appended);
+    returns out [B][Hq][Sq][D] fp32."""
+    assert q.is_contiguous() and q.dim() == 4
+    b, hq, sq, d = q.shape
+    if out is None:
+        out = torch.empty((b, hq, sq, d), dtype=torch.float32, device=q.device)
+    cs = cache.c_struct()
+    _check("kvq_sdpa_int4_prefill",
+           lib().kvq_sdpa_int4_prefill(C.byref(cs), int(q_start), int(sq), _ptr(q), _dtype_code(q), hq,
+                                       float(softmax_scale), _ptr(out), _stream(stream)))
     return out

@@ -342,6 +342,48 @@ int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtyp
                                 kvq_num_chunks(skv, chunk), out, stream);
 }
 
+int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, const void *q, int q_dtype, int32_t Hq,
+                          float softmax_scale, float *out, void *stream)
+{
+    int st = check_cache(cache);
+    if (st)
+        return st;
+    if (q_dtype != KVQ_F16 && q_dtype != KVQ_F32)
+        return KVQ_E_DTYPE;
+    if (q_start < 0 || sq < 1 || Hq < 1 || Hq % cache->kv_heads != 0 || !isfinite(softmax_scale))
+        return KVQ_E_SHAPE;
+    if (q_start > cache->capacity || sq > cache->capacity - q_start)
+        return KVQ_E_CAPACITY;
+    if (!q || !out)
+        return KVQ_E_NULL;
+    if (!aligned16(q) || !aligned16(out))
+        return KVQ_E_ALIGN;
+    const int n_rep = Hq / cache->kv_heads;
+    if (!prefill_supports(cache->head_dim, cache->group, n_rep, q_dtype, cache_bits(cache)))
+        return KVQ_E_UNSUPPORTED;
+    const int pb = prefill_positions_per_block(n_rep);
+    if ((int64_t)cache->batch * Hq * sq > ((int64_t)1 << 40) / cache->head_dim || (sq + pb - 1) / pb > 0x7fffffff)
+        return KVQ_E_SHAPE;
+    PrefillArgs a;
+    a.k_q = cache->k_q;
+    a.v_q = cache->v_q;
+    a.k_scale = cache->k_scale;
+    a.k_bias = cache->k_bias;
+    a.v_scale = cache->v_scale;
+    a.v_bias = cache->v_bias;
+    a.q = q;
+    a.out = out;
+    a.cap = cache->capacity;
+    a.q_start = q_start;
+    a.sq = sq;
+    a.Hkv = cache->kv_heads;
+    a.Hq = Hq;
+    a.n_rep = n_rep;
+    a.pb = pb;
+    a.score_scale = softmax_scale * kLog2e;
+    return launch_status(launch_prefill(a, cache->batch, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

@@ -86,6 +86,31 @@ struct ReduceArgs {
     int32_t D;
 };
 
+// Prefill-side attention: queries of positions q_start .. q_start + sq - 1
+// (q [B][Hq][sq][D] fp16), each over cache rows [0, q_start + i]; out fp32
+// [B][Hq][sq][D], normalised.
+struct PrefillArgs {
+    const uint32_t *k_q;
+    const uint32_t *v_q;
+    const uint16_t *k_scale;
+    const uint16_t *k_bias;
+    const uint16_t *v_scale;
+    const uint16_t *v_bias;
+    const void *q;
+    float *out;
+    int64_t cap;
+    int64_t q_start;
+    int32_t sq;
+    int32_t Hkv;
+    int32_t Hq;
+    int32_t n_rep;
+    int32_t pb;         // positions per wavefront (64 / n_rep)
+    float score_scale;  // softmax_scale * log2(e)
+};
+bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits);
+int prefill_positions_per_block(int n_rep);
+hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
+
 // Where a partial-phase launch goes: the stream and, optionally, two events
 // recorded at the kernel's own dispatch start and end (hipExtLaunchKernel).
 struct Launch {

@@ -43,14 +43,12 @@
 // clamping, and the eight value rows of a lane share one address register
 // (their distances are instruction offsets).
 #include "kvq_internal.h"
+#include "mfma_common.h"
 #include "quant_rule.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;                 // threads per workgroup
 constexpr int TILE = 32;                // rows per tile
@@ -61,118 +59,6 @@ constexpr int ROUND = 4 * MAXT * TILE;  // 512 rows
 #ifndef WAVES_D128
 #define WAVES_D128 2
 #endif
-// word 3 of a raw (unswizzled, 32-bit element) buffer resource on gfx9
-constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ float h_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
-__device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferFlags);
-}
-
-// (x & mask) | magic, meant for one v_and_or_b32. A gfx9 VOP3 encoding takes
-// no 32-bit literal, so with constant operands the compiler would split it
-// into an AND and an OR that each carry a literal; the Unpacker therefore
-// holds mask and magic as opaque register values (mask in a scalar register,
-// magic in a vector register). Plain code, not inline asm, so that the
-// compiler's hazard tracking sees every write next to the matrix instructions.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
-{
-    return (x & mask) | magic;
-}
-
-// x as a value the compiler cannot see through, in a scalar or a vector
-// register (an empty asm statement; no instruction is emitted)
-__device__ __forceinline__ uint32_t opaque_s(uint32_t x)
-{
-    asm volatile("" : "+s"(x));
-    return x;
-}
-__device__ __forceinline__ uint32_t opaque_v(uint32_t x)
-{
-    asm volatile("" : "+v"(x));
-    return x;
-}
-// opaque_s where ON, else x as a plain constant (no asm statement at all)
-template <bool ON>
-__device__ __forceinline__ uint32_t opaque_s_if(uint32_t x)
-{
-    if constexpr (ON)
-        return opaque_s(x);
-    else
-        return x;
-}
-
-// Four half2 registers -> one MFMA operand.
-__device__ __forceinline__ half8 cat8(half2v a, half2v b, half2v c, half2v d)
-{
-    half8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-    return r;
-}
-
-// The four nibbles of each 16-bit half of x as exact fp16 values n - 8:
-// out[m] = (nibble m of the low half, nibble m of the high half) - 8.
-// A nibble placed in mantissa bits 0-3 under exponent 2^10 (0x6400) reads as
-// 1024 + n; in bits 4-7 under 2^6 (0x5400) as 64 + n. Nibbles 2 and 3 are
-// first shifted down by 8 (an fp16 mantissa has only bits 0-9). The fp16
-// subtraction of 1032 or 72 is exact.
-//
-// Why centred codes: the matrix core aligns the 32 products of one
-// instruction to the largest and truncates the rest, which biases sums of
-// same-signed products toward zero. Codes in [-8, 7] give products of both
-// signs and half the magnitude, and the 8 * scale they drop moves into the
-// bias term: code * s + b = (code - 8) * s + (b + 8 s).
-struct Unpacker {
-    uint32_t m1024, m64;  // magic exponents 0x6400 / 0x5400 (vector registers)
-    uint32_t lo4, hi4;    // nibble masks 0x000F000F / 0x00F000F0 (scalar registers)
-    __device__ static Unpacker make()
-    {
-        return Unpacker{opaque_v(0x64006400u), opaque_v(0x54005400u), opaque_s(0x000F000Fu), opaque_s(0x00F000F0u)};
-    }
-    __device__ __forceinline__ void operator()(uint32_t x, half2v (&out)[4]) const
-    {
-        const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
-        const uint32_t y = x >> 8;
-        out[0] = as_h2(and_or(x, lo4, m1024)) - k1032;
-        out[1] = as_h2(and_or(x, hi4, m64)) - k72;
-        out[2] = as_h2(and_or(y, lo4, m1024)) - k1032;
-        out[3] = as_h2(and_or(y, hi4, m64)) - k72;
-    }
-    // out[m] of operator() alone (m a compile-time constant)
-    __device__ __forceinline__ half2v one(uint32_t x, int m) const
-    {
-        const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
-        const uint32_t z = m >= 2 ? x >> 8 : x;
-        return (m & 1) ? as_h2(and_or(z, hi4, m64)) - k72 : as_h2(and_or(z, lo4, m1024)) - k1032;
-    }
-};
-
-// One K word (dimensions 8w..8w+7 of one row) as an MFMA operand; element j
-// holds dimension 8w + kPerm[j].
-constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over the NG adjacent lanes that hold the groups of one head.
-template <int NG>
-__device__ __forceinline__ float group_sum(float v)
-{
-    if constexpr (NG >= 2)
-        v += dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
-    if constexpr (NG >= 4)
-        v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
-    return v;
-}
 
 __device__ __forceinline__ float quarter_max(float v)
 {
@@ -540,141 +426,6 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
 // paid once per 73 KB instead of once per 18 KB.
 // ---------------------------------------------------------------------------
 constexpr int CH1 = 512;  // most rows of a chunk in the one-wavefront kernel
-// Headroom (log2 units) above a head's running maximum when its softmax
-// reference is raised: weights are at most 2^-kHeadroom of their largest
-// possible value, which costs nothing in fp32 and about 2 bits at the fp16
-// subnormal floor of the value weights' lo halves.
-constexpr float kHeadroom = 2.0f;
-// With the hi and lo halves of the value weights in separate operand rows,
-// the lo halves are stored scaled by 2^11: lo is at most half an fp16 ulp of
-// hi, so lo * 2^11 stays within hi's magnitude (no overflow) and, for any
-// weight above 2^-13, in the normal fp16 range instead of the subnormals.
-constexpr float kLoScale = 2048.0f;
-
-// Sum / max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 row
-// swaps: with both operands equal, the two results of a swap hold a lane's
-// own value and its partner's, in some order. (Each element is copied to a
-// scalar before the bit cast: a bit cast of a vector element in place reads
-// element 0.)
-__device__ __forceinline__ void row_swap16(float v, float &x, float &y)
-{
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const uint32_t r0 = r[0], r1 = r[1];
-    x = __builtin_bit_cast(float, r0);
-    y = __builtin_bit_cast(float, r1);
-}
-
-__device__ __forceinline__ void row_swap32(float v, float &x, float &y)
-{
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const uint32_t r0 = r[0], r1 = r[1];
-    x = __builtin_bit_cast(float, r0);
-    y = __builtin_bit_cast(float, r1);
-}
-
-// Maxima of values the compiler cannot prove canonical (results of lane
-// swaps and DPP sums, or joined across the tail branch): fmaxf would first
-// canonicalise every operand with an extra v_max. The NaN-propagating
-// maximum needs no canonical operands and maps to gfx950's v_maximum3_f32;
-// scores are finite or -inf, never NaN, so it is the same maximum.
-__device__ __forceinline__ float max_raw(float x, float y) { return __builtin_elementwise_maximum(x, y); }
-
-__device__ __forceinline__ float max3_raw(float x, float y, float z) { return max_raw(max_raw(x, y), z); }
-
-// max(m, maximum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float xrow_max(float v, float m)
-{
-    float x, y;
-    row_swap16(v, x, y);
-    row_swap32(max_raw(x, y), x, y);
-    return max3_raw(m, x, y);
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Multiply an accumulator tile in place. Tied asm operands keep the products
-// in the accumulator's own registers: as plain code the compiler writes them
-// to new registers and, on the far more common path that skips the rescale,
-// copies every accumulator across (one move per accumulator element and tile).
-// The compiler's hazard tracking does not see into inline asm, so a rescale
-// starts with mfma_result_wait(): more wait states than any matrix
-// instruction here needs before a vector instruction may read its result.
-__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"); }
-
-__device__ __forceinline__ void scale_in_place(float4v &v, const float4v &c)
-{
-    float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-    asm volatile("v_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %5\n\tv_mul_f32 %2, %2, %6\n\tv_mul_f32 %3, %3, %7"
-                 : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
-                 : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
-    v = (float4v){x0, x1, x2, x3};
-}
-
-
-// One DPP move inside each row of 16 lanes: lanes in the banks of BANKS
-// (bank b = lanes 4b..4b+3 of a row) take src from lane l ^ 8 (row_ror:8);
-// the other lanes keep old.
-template <int BANKS>
-__device__ __forceinline__ uint32_t take_half_row(uint32_t old, uint32_t src)
-{
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x128, 0xF, BANKS, false);
-}
-
-__device__ __forceinline__ float xrow_sum(float v)
-{
-    float x, y;
-    row_swap16(v, x, y);
-    row_swap32(x + y, x, y);
-    return x + y;
-}
-
-// K words as MFMA operands with the nibbles read as fp16 subnormals: a
-// nibble masked into bits 0-3 of a half whose exponent field is zero is the
-// exact value n * 2^-24, one masked into bits 4-7 is n * 2^-20 (the matrix
-// core takes subnormal fp16 inputs exactly). Element j of the operand holds
-// dimension kPerm[j]; elements 2, 3, 6 and 7 are of the second kind, and the
-// query elements they meet are stored divided by 16, so that every product
-// is n q 2^-24 and the score factor carries the 2^24. The codes enter with
-// no offset, so the products are at most 15 |q| and the truncating sum of
-// one instruction loses at most a few ulps of that. Dividing by 16 is exact
-// in fp16 unless |q| < 2^-10, where it rounds to the subnormal grid (an
-// absolute error below 2^-21 |q| units in that element).
-__device__ __forceinline__ half8 k_operand_sub(uint32_t w, const Unpacker &u)
-{
-    const uint32_t y = w >> 8;
-    return cat8(as_h2(w & u.lo4), as_h2(w & u.hi4), as_h2(y & u.lo4), as_h2(y & u.hi4));
-}
-
-// elements of a K operand that read n * 2^-20 (their query elements are / 16)
-__device__ __forceinline__ constexpr bool k_elem_fine(int j) { return (j & 2) != 0; }
-
-// 8-bit codes. Two K words (dimensions 8o..8o+7 of one row, four bytes each)
-// as an MFMA operand: a byte moved into bits 0-7 of a half whose upper byte
-// is zero is the exact fp16 subnormal n * 2^-24 (at most 255 * 2^-24), so
-// one AND and one byte permute give two operand halves each. Element j holds
-// dimension kPerm8[j]; the score factor carries the 2^24 as for int4 codes.
-constexpr int kPerm8[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-
-__device__ __forceinline__ half8 k_operand8(uint32_t w0, uint32_t w1, uint32_t m_even, uint32_t sel_odd)
-{
-    return cat8(as_h2(w0 & m_even), as_h2(__builtin_amdgcn_perm(0u, w0, sel_odd)), as_h2(w1 & m_even),
-                as_h2(__builtin_amdgcn_perm(0u, w1, sel_odd)));
-}
-
-// Byte m of the value words of two rows (r0 in the low half, r1 in the high
-// half) as exact fp16 values (n - 128) * 2^-24: a byte permute places each
-// code as a subnormal n * 2^-24 and one packed subtraction of 128 * 2^-24
-// centres it (exact: every operand and result is a multiple of 2^-24 below
-// 2^-14 in magnitude). Centred codes, as for int4: the matrix core truncates
-// the aligned products of one instruction, which biases sums of same-signed
-// products toward zero.
-__device__ __forceinline__ half2v v_pair8(uint32_t r0, uint32_t r1, uint32_t sel)
-{
-    const half2v c128 = {(_Float16)0x1p-17f, (_Float16)0x1p-17f};
-    return as_h2(__builtin_amdgcn_perm(r1, r0, sel)) - c128;
-}
 
 // Fused decode step: quantise this (batch, KV head)'s new K and V rows into
 // cache row a.append_row (the rule of quant_rule.h; lanes 0..D/8-1 take the
@@ -727,14 +478,14 @@ template <int D, int NG, bool Q32, int PF, int BITS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
 void sdpa_partial_mfma1_kernel(PartialArgs a)
 {
-    // BITS = 8: byte codes, two words per eight dimensions. K operands and
-    // value codes are fp16 subnormals (n * 2^-24, values centred by 128). The
-    // value weights p * s_v are carried times WS = 2^6: byte scales are 17
-    // times finer than int4 ones, and the factor keeps the weights' fp16
-    // halves as far above the subnormal range as with int4 codes, while
+    // BITS = 8: byte codes, two words per eight dimensions, both K and V
+    // codes entering as the exact centred integers n - 128. The value
+    // weights p * s_v are carried times WS = 2^6: byte scales are 17 times
+    // finer than int4 ones, and the factor keeps the weights' fp16 halves as
+    // far above the subnormal range as with int4 codes, while
     // p * s_v * 2^6 <= 514 * 64 stays below the fp16 maximum for any fp16
-    // input range. The value products are multiplied by VU = 2^24 / WS when
-    // the partial state is written.
+    // input range. The value products are multiplied by VU = 1 / WS when the
+    // partial state is written.
     constexpr bool B8 = BITS == 8;
     constexpr int W = D * BITS / 32;  // words per row
     constexpr int WPL = W / 4;        // K words per lane: a quarter row
@@ -744,7 +495,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     constexpr int WPG = D / 8 / NG;   // eight-dimension columns per scale group
     constexpr float VC = B8 ? 128.0f : 8.0f;     // centre of the value codes
     constexpr float WS = B8 ? 64.0f : 1.0f;      // scale of the value weights
-    constexpr float VU = B8 ? 262144.0f : 1.0f;  // unit of the value products: 2^24 / WS
+    constexpr float VU = B8 ? 1.0f / 64.0f : 1.0f;  // unit of the value products: 1 / WS
     constexpr int PAIRS = TILE * NG;        // (row, group) pairs of scale/bias per tile
     constexpr int MP = (PAIRS + 63) / 64;   // pairs per lane (NG = 1: lanes 32-63 repeat 0-31)
     // D = 128 with two scale groups: value products group by group, with the
@@ -788,20 +539,25 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // of MP (row, group) pairs of a tile; one tile ahead of use they become
     // the fp32 factors of the tile code, one 16-byte record per pair in a
     // two-slot LDS buffer [slot][row * NG + group]:
-    //   x: s_k * c * 2^24     (c = softmax scale * log2 e; 2^24 undoes the
-    //                          subnormal scale of the K operands)
-    //   y: b_k * c
+    //   x: s_k * c * 2^20     (c = softmax scale * log2 e; 2^20 undoes the
+    //                          subnormal scale of the int4 K operands), or
+    //      s_k * c            (8-bit codes)
+    //   y: b_k * c, or (b_k + 128 s_k) * c (the bias of centred 8-bit codes)
     //   z: s_v * WS
     //   w: b_v + VC s_v       (bias of the value codes centred by VC)
     __shared__ __align__(16) float4 mring[2][PAIRS];
     const Unpacker unpack = Unpacker::make();
-    const uint32_t m_even = opaque_s_if<B8>(0x00FF00FFu), sel_odd = opaque_s_if<B8>(0x0C030C01u);  // 8-bit K
+    const uint32_t m_fine = opaque_s_if<!B8>(0x00F000F0u);  // int4 K operands
+    // 8-bit K operands: the magic exponent bytes (src0 bytes 4-7 of a permute)
+    // and the selectors of bytes (0, 2) and (1, 3) under them
+    const uint32_t magic8 = opaque_s_if<B8>(kMagic1024x4), magic16 = opaque_s_if<B8>(0x64006400u);
+    const uint32_t sel_even = opaque_s_if<B8>(0x04020400u), sel_odd = opaque_s_if<B8>(0x04030401u);
     // 8-bit value pairs: byte m of the low source word into bits 0-7, byte m
     // of the high one into bits 16-23, zeros elsewhere
     const uint32_t sel_b[4] = {opaque_s_if<B8>(0x0C040C00u), opaque_s_if<B8>(0x0C050C01u),
                                opaque_s_if<B8>(0x0C060C02u), opaque_s_if<B8>(0x0C070C03u)};
     const float cs = a.score_scale;
-    const float cs24 = cs * 16777216.0f;  // c * 2^24
+    const float csk = B8 ? cs : cs * 1048576.0f;  // c, times 2^20 for the int4 K operands
 
     // ---- start-up: Q and the first PF tiles, all requested before the first wait
     float qv[KM][8];
@@ -877,7 +633,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             const float kb = h_val((uint16_t)mt[p][1]);
             const float vs = h_val((uint16_t)mt[p][2]);
             const float vb = h_val((uint16_t)mt[p][3]);
-            mring[slot][pr] = make_float4(ks * cs24, kb * cs, vs * WS, fmaf(VC, vs, vb));
+            mring[slot][pr] = make_float4(ks * csk, (B8 ? fmaf(128.0f, ks, kb) : kb) * cs, vs * WS, fmaf(VC, vs, vb));
         }
         // LDS instructions of a wavefront execute in order, so the tile code
         // sees these records; only the compiler must not move reads above
@@ -895,8 +651,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     __builtin_amdgcn_sched_barrier(0);
 
     // Q restricted to the column's group, in the dimension order of the K
-    // operands, divided by 16 where the K operand reads n * 2^-20; qsum is
-    // the group sum of exactly what the matrix core sees, in query units
+    // operands; qsum is the group sum of exactly what the matrix core sees
     half8 qhi[KM], qlo[KM];
     float qsum = 0.0f;
 #pragma unroll
@@ -905,16 +660,15 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         const bool mine = col_on && (word / WPG) == gl;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float unit = (!B8 && k_elem_fine(j)) ? 16.0f : 1.0f;
-            const float x = mine ? qv[u][B8 ? kPerm8[j] : kPerm[j]] * (1.0f / unit) : 0.0f;
+            const float x = mine ? qv[u][B8 ? kPerm8[j] : kPerm[j]] : 0.0f;
             const _Float16 hi = (_Float16)x;
             qhi[u][j] = hi;
             if constexpr (Q32) {
                 const _Float16 lo = (_Float16)(x - (float)hi);
                 qlo[u][j] = lo;
-                qsum = fmaf(unit, (float)hi + (float)lo, qsum);
+                qsum += (float)hi + (float)lo;
             } else {
-                qsum = fmaf(unit, (float)hi, qsum);
+                qsum += (float)hi;
             }
         }
     }
@@ -961,12 +715,12 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                     half8 ka;
                     if constexpr (B8) {
                         const uint4 x = kcur[blk][uu / 2];
-                        ka = (uu % 2 == 0) ? k_operand8(x.x, x.y, m_even, sel_odd)
-                                           : k_operand8(x.z, x.w, m_even, sel_odd);
+                        ka = (uu % 2 == 0) ? k_operand8(x.x, x.y, magic8, sel_even, sel_odd)
+                                           : k_operand8(x.z, x.w, magic8, sel_even, sel_odd);
                     } else {
                         const uint4 x = kcur[blk][uu / 4];
                         const uint32_t w = (uu % 4 == 0) ? x.x : (uu % 4 == 1) ? x.y : (uu % 4 == 2) ? x.z : x.w;
-                        ka = k_operand_sub(w, unpack);
+                        ka = k_operand_sub(w, m_fine);
                     }
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[uu], sacc, 0, 0, 0);
                     if constexpr (Q32)
@@ -1081,7 +835,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                             half2v e[4];
 #pragma unroll
                             for (int jp = 0; jp < 4; ++jp)
-                                e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm]);
+                                e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm], magic16);
                             const half8 bv = cat8(e[0], e[1], e[2], e[3]);
                             acc[0][4 * g + mm] =
                                 __builtin_amdgcn_mfma_f32_16x16x32_f16(g ? a1 : a0, bv, acc[0][4 * g + mm], 0, 0, 0);
@@ -1120,7 +874,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 #pragma unroll
                             for (int jp = 0; jp < 4; ++jp)
                                 e[jp] = v_pair8(vcur[s2][4 * jp + (m >> 2)], vcur[s2][4 * jp + 2 + (m >> 2)],
-                                                sel_b[m & 3]);
+                                                sel_b[m & 3], magic16);
                             const half8 bv = cat8(e[0], e[1], e[2], e[3]);
                             acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
                             acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);

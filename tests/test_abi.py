@@ -244,3 +244,31 @@ def test_decode_step_validation(L):
     assert _step(L, c, chunk=0) == E_SHAPE
     assert _step(L, c, kernel=9) == E_SHAPE
     assert _step(L, c, kernel=4, chunk=1024) == E_UNSUP  # one-wavefront kernel: chunk <= 512
+
+
+def _prefill(L, cache, q_start=100, sq=16, q=P, qd=0, hq=64, scale=0.1, out=P):
+    return L.kvq_sdpa_int4_prefill(C.byref(cache) if cache is not None else None, q_start, sq, q, qd, hq, scale, out,
+                                   None)
+
+
+def test_prefill_validation(L):
+    assert _prefill(L, None) == E_NULL
+    assert _prefill(L, _cache(k_q=None)) == E_NULL
+    assert _prefill(L, _cache(), q=None) == E_NULL
+    assert _prefill(L, _cache(), out=None) == E_NULL
+    assert _prefill(L, _cache(), qd=5) == E_DTYPE
+    assert _prefill(L, _cache(), q_start=-1) == E_SHAPE
+    assert _prefill(L, _cache(), sq=0) == E_SHAPE
+    assert _prefill(L, _cache(), hq=12) == E_SHAPE
+    assert _prefill(L, _cache(), scale=float("inf")) == E_SHAPE
+    assert _prefill(L, _cache(capacity=1024), q_start=1000, sq=25) == E_CAP
+    assert _prefill(L, _cache(capacity=1024), q_start=1025, sq=1) == E_CAP
+    assert _prefill(L, _cache(), q=P + 4) == E_ALIGN
+    assert _prefill(L, _cache(), out=P + 8) == E_ALIGN
+    # outside the prefill kernel: other head sizes and groups, 8-bit codes,
+    # fp32 queries, more than 16 query heads per KV head
+    assert _prefill(L, _cache(head_dim=256)) == E_UNSUP
+    assert _prefill(L, _cache(group=32)) == E_UNSUP
+    assert _prefill(L, _cache(bits=8)) == E_UNSUP
+    assert _prefill(L, _cache(), qd=1) == E_UNSUP
+    assert _prefill(L, _cache(kv_heads=2), hq=64) == E_UNSUP

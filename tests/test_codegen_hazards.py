@@ -110,17 +110,31 @@ def _min_wait(lines):
     return worst
 
 
+MFMA_SOURCES = ("sdpa_mfma.hip", "sdpa_prefill.hip")  # every source with matrix instructions
+
+
 @pytest.fixture(scope="module")
 def mfma_asm(tmp_path_factory):
     hipcc = B.hipcc()
     if shutil.which(hipcc) is None and not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "sdpa_mfma.s"
+    d = tmp_path_factory.mktemp("asm")
     flags = [f for f in B.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
-    cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", B.INCLUDE, "-I", B.CSRC,
-           os.path.join(B.CSRC, "sdpa_mfma.hip"), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True)
-    return out.read_text()
+    texts = []
+    for src in MFMA_SOURCES:
+        out = d / (src + ".s")
+        cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", B.INCLUDE, "-I", B.CSRC,
+               os.path.join(B.CSRC, src), "-o", str(out)]
+        subprocess.run(cmd, check=True, capture_output=True)
+        texts.append(out.read_text())
+    return "\n".join(texts)
+
+
+def test_every_matrix_source_is_checked():
+    """A source added later with matrix instructions must join the list."""
+    for src in B.sources():
+        if os.path.basename(src) not in MFMA_SOURCES:
+            assert "__builtin_amdgcn_mfma" not in open(src).read(), "%s uses matrix instructions but is not checked" % src
 
 
 def test_vector_write_to_mfma_read_wait_states(mfma_asm):

@@ -1,0 +1,113 @@
+"""GPU parity of prefill-side attention over the int4 cache
+(kvq_sdpa_int4_prefill: Sq > 1 query positions, causal, against the float64
+oracle's sdpa_prefill on the same packed cache)."""
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+import oracle
+import quantized_kv_cache_quantize_amd as kvq
+from _gpu_common import check_attention, gpu_cache_from_oracle, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-4  # the matrix-core gate of the decode tests
+
+
+def _case(B, hq, hkv, q_start, sq, seed, alpha=None, cap=None):
+    S = q_start + sq
+    q = kvq_synth.normal((B, hq, sq, 128), [90, seed, 0]).astype(np.float16)
+    k = kvq_synth.normal((B, hkv, S, 128), [90, seed, 1]).astype(np.float16)
+    v = kvq_synth.normal((B, hkv, S, 128), [90, seed, 2]).astype(np.float16)
+    oc = oracle.Cache(B, hkv, 128, cap or S, 64)
+    oc.append(k, v, 0)
+    return q, oc, (1 / np.sqrt(128) if alpha is None else alpha)
+
+
+def _run(oc, q_start, q, alpha):
+    gc = gpu_cache_from_oracle(oc)
+    out = kvq.sdpa_int4_prefill(gc, q_start, to_dev(q), alpha)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("q_start,sq", [(0, 1), (0, 2), (0, 7), (0, 33), (5, 64), (511, 100), (1000, 17),
+                                        (31, 1), (32, 32), (4000, 96)])
+def test_gqa4(q_start, sq):
+    note("prefill gqa4 q_start=%d sq=%d" % (q_start, sq))
+    q, oc, alpha = _case(1, 8, 2, q_start, sq, seed=q_start * 1000 + sq)
+    got = _run(oc, q_start, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, q_start, q, alpha), REL_L2, label="prefill")
+
+
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (16, 16), (16, 1), (6, 2), (12, 4)])
+def test_head_layouts(hq, hkv):
+    """GQA 8 (the Llama layer), MHA, 16 heads per KV head, and ratios that do
+    not divide the 16 query columns of a wavefront (3)."""
+    note("prefill heads hq=%d hkv=%d" % (hq, hkv))
+    q, oc, alpha = _case(1, hq, hkv, 300, 45, seed=hq * 100 + hkv)
+    got = _run(oc, 300, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, 300, q, alpha), REL_L2, label="prefill heads")
+
+
+def test_batch_two_and_spare_capacity():
+    note("prefill batch 2")
+    q, oc, alpha = _case(2, 8, 2, 200, 40, seed=7, cap=400)
+    got = _run(oc, 200, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, 200, q, alpha), REL_L2, label="prefill batch")
+
+
+def test_unscaled_scores():
+    """Softmax scale 1 on N(0,1) rows: scores of O(10), weights far from flat."""
+    note("prefill alpha 1")
+    q, oc, alpha = _case(1, 8, 2, 700, 20, seed=11, alpha=1.0)
+    got = _run(oc, 700, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, 700, q, alpha), 2e-4, atol=1e-3, rtol=1e-3, label="prefill a1")
+
+
+def test_first_position_is_row_zero():
+    note("prefill first row")
+    q, oc, alpha = _case(1, 8, 2, 0, 3, seed=12)
+    got = _run(oc, 0, q, alpha)
+    vd = oracle.dequantize_rows(oc.v_q[:, :, :1], oc.v_scale[:, :, :1], oc.v_bias[:, :, :1], 64)
+    for h in range(8):
+        np.testing.assert_allclose(got[0, h, 0], vd[0, h // 4, 0], rtol=1e-5, atol=1e-6)
+
+
+def test_outlier_chunked_prefill_sampled():
+    """The outlier workload's append: 4096 new rows per KV head at row 61440
+    (quantised by the GPU append), then prefill attention for those 4096
+    positions; sampled positions (first, second, middle, last) checked against
+    the oracle on all heads."""
+    note("prefill outlier 4096 at 61440")
+    total, prefix = 65536, 61440
+    _, k, v, _ = kvq_synth.outlier_kv(total)
+    q = kvq_synth.normal((1, 64, total - prefix, 128), [91, 0]).astype(np.float16)
+    alpha = 1 / np.sqrt(128)
+    oc = oracle.Cache(1, 8, 128, total, 64)
+    oc.append(k[:, :, :prefix], v[:, :, :prefix], 0)
+    gc = gpu_cache_from_oracle(oc)
+    kvq.quantize_kv_append(gc, prefix, to_dev(np.ascontiguousarray(k[:, :, prefix:])),
+                           to_dev(np.ascontiguousarray(v[:, :, prefix:])))
+    out = kvq.sdpa_int4_prefill(gc, prefix, to_dev(q), alpha)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    oc.append(k[:, :, prefix:], v[:, :, prefix:], prefix)
+    for i in (0, 1, 2047, 4095):
+        ref = oracle.sdpa(oc, prefix + i + 1, np.ascontiguousarray(q[:, :, i]), alpha)
+        check_attention(got[:, :, i], ref, REL_L2, label="prefill outlier pos %d" % i)
+
+
+@pytest.mark.parametrize("what", ["d256", "g32", "int8", "fp32q"])
+def test_unsupported_shapes_refused(what):
+    note("prefill refuses %s" % what)
+    D = 256 if what == "d256" else 128
+    G = 32 if what == "g32" else 64
+    bits = 8 if what == "int8" else 4
+    gc = kvq.QuantKVCache(1, 2, D, 64, G, device="cuda", bits=bits)
+    q = torch.zeros((1, 8, 4, D), dtype=torch.float32 if what == "fp32q" else torch.float16, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.sdpa_int4_prefill(gc, 10, q, 0.1)
+    assert e.value.status == -7
