@@ -24,7 +24,10 @@
 //
 // Values: O[c][d] += P'_g[c][t] . Vcodes[t][d] per scale group g, with the
 // weights p * s_v of group g as hi and lo fp16 halves (lo scaled by 2^11) in
-// separate accumulators, and the value codes centred by 8. A lane's value
+// separate accumulators, and the value codes centred by 8 (one accumulator
+// per output across all the rows: with normal centred operands its error on
+// the outlier workload's 65536 rows matches that of fp32 flushes every 512
+// rows, measured). A lane's value
 // word holds eight dimensions of one group; the operand of group g takes the
 // four dimensions it lacks from lane l ^ 8 with a bank-masked DPP move (the
 // layout of the decode kernel's two-group path).
@@ -32,12 +35,7 @@
 // Softmax: per query column, relative to a reference raised (with headroom)
 // only when a score exceeds it, as in the decode kernel; the output is
 // normalised in the kernel (no split over rows, so no partial state).
-//
-// Accumulation: the matrix core truncates each instruction's sum toward
-// zero, so a value accumulator carried across tens of thousands of rows
-// drifts low (measured: 1.1e-4 relative at 65K rows). Every 16 tiles (512
-// rows, the decode chunk) the matrix accumulators are added into fp32 totals
-// with round-to-nearest vector adds and restart from zero.
+
 #include "kvq_internal.h"
 #include "mfma_common.h"
 
@@ -45,22 +43,23 @@ namespace kvq {
 namespace {
 
 constexpr int PT = 32;  // rows per tile
-constexpr int FLUSH = 16;  // tiles between flushes of the matrix accumulators
-#ifndef PB_BLOCKS
-#define PB_BLOCKS 1  // blocks of 16 query columns per wavefront (two spill registers)
-#endif
 
-// D = 128, two scale groups of 64, fp16 queries, int4 codes; NB blocks of 16
-// query columns per wavefront; PF tiles in flight.
-template <int NB, int PF>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+// D = 128, two scale groups of 64, fp16 queries, int4 codes; 16 query
+// columns per wavefront; PF tiles in flight. Operands are unpacked right
+// before the instruction that reads them and the scale/bias factors read
+// from LDS where they are used, which keeps a wavefront within 256
+// registers (two per SIMD, no accumulation registers: beyond 256 the
+// compiler moved the accumulators between register files around every
+// matrix instruction).
+template <int PF>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void sdpa_prefill_mfma_kernel(PrefillArgs a)
 {
     constexpr int D = 128;
     constexpr int NG = 2;
-    constexpr int W = D / 8;     // words per row
-    constexpr int KM = D / 32;   // score products per 16-row block
-    constexpr int KPG = KM / NG; // of them per scale group
+    constexpr int W = D / 8;      // words per row
+    constexpr int KM = D / 32;    // score products per 16-row block
+    constexpr int KPG = KM / NG;  // of them per scale group
     constexpr int PAIRS = PT * NG;
     static_assert(PAIRS == 64, "one (row, group) pair per lane");
 
@@ -70,25 +69,18 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
     const int nrep = a.n_rep;
-    const int p0 = blockIdx.x * a.pb;                 // first position of the block
-    const int npos = min(a.pb, a.sq - p0);            // positions in this block
-    const int t_end = (int)a.q_start + p0 + npos;     // rows [0, t_end) are read
-    const int t_all = (int)a.q_start + p0;            // rows <= t_all are seen by every column
+    const int p0 = blockIdx.x * a.pb;              // first position of the block
+    const int npos = min(a.pb, a.sq - p0);         // positions in this block
+    const int t_end = (int)a.q_start + p0 + npos;  // rows [0, t_end) are read
+    const int t_all = (int)a.q_start + p0;         // rows <= t_all are seen by every column
     const int ntile = (t_end + PT - 1) / PT;
     const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
-    const bool low8 = (lane & 8) == 0;                // this lane's V word is in group 0
+    const bool low8 = (lane & 8) == 0;             // this lane's V word is in group 0
 
-    // column c = 16 bb + col: position c / nrep, head c % nrep (inactive
-    // columns compute on zero queries and are never stored)
-    int cpos[NB], chead[NB];
-    bool con[NB];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-        const int c = 16 * bb + col;
-        cpos[bb] = c / nrep;
-        chead[bb] = c % nrep;
-        con[bb] = c < a.pb * nrep && cpos[bb] < npos;
-    }
+    // column col: position col / nrep, head col % nrep (inactive columns
+    // compute on zero queries and are never stored)
+    const int cpos = col / nrep, chead = col % nrep;
+    const bool con = col < a.pb * nrep && cpos < npos;
 
     const uint32_t rows_ok = (uint32_t)t_end;
     const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
@@ -138,6 +130,13 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
         mring[slot][lane] = make_float4(ks * cs20, kb * cs, vs, fmaf(8.0f, vs, vb));
         asm volatile("" ::: "memory");
     };
+    // factors (x, y) or (z, w) of row r, group g
+    auto fac_xy = [&](int slot, int r, int g) {
+        return *reinterpret_cast<const float2 *>(&mring[slot][r * NG + g]);
+    };
+    auto fac_zw = [&](int slot, int r, int g) {
+        return *(reinterpret_cast<const float2 *>(&mring[slot][r * NG + g]) + 1);
+    };
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
         __builtin_amdgcn_sched_barrier(0);
@@ -145,15 +144,13 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // queries as B operands: column block bb, score product uu, dimensions
+    // the column's query as B operands: score product uu holds dimensions
     // 32 uu + 8 q4 + kPerm[j]; qsum: group sums of exactly what the matrix
     // core sees
-    half8 qop[NB][KM];
-    float qsum[NB][NG];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-        const int64_t qrow =
-            (((int64_t)b * a.Hq + kvh * nrep + (con[bb] ? chead[bb] : 0)) * a.sq + p0 + (con[bb] ? cpos[bb] : 0)) * D;
+    half8 qop[KM];
+    float qsum[NG];
+    {
+        const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con ? chead : 0)) * a.sq + p0 + (con ? cpos : 0)) * D;
         const _Float16 *qp = reinterpret_cast<const _Float16 *>(a.q) + qrow;
         float gs[NG] = {};
 #pragma unroll
@@ -161,34 +158,23 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const half8 x = *reinterpret_cast<const half8 *>(qp + 32 * uu + 8 * q4);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const _Float16 h = con[bb] ? x[kPerm[j]] : (_Float16)0.0f;
-                qop[bb][uu][j] = h;
+                const _Float16 h = con ? x[kPerm[j]] : (_Float16)0.0f;
+                qop[uu][j] = h;
                 gs[uu / KPG] += (float)h;
             }
         }
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-            qsum[bb][g] = xrow_sum(gs[g]);
+            qsum[g] = xrow_sum(gs[g]);
     }
     stage_meta(0, mbuf[0]);
 
-    float m_run[NB], l_run[NB], b_run[NB][NG];
-    float4v acc[NB][8], accl[NB][8];  // [block][4 g + mm]: hi and lo (x kLoScale) weight halves
-    float4v tot[NB][8], totl[NB][8];  // fp32 totals of the flushed accumulators
+    float m_run = 0.0f, l_run = 0.0f, b_run[NG] = {0.0f, 0.0f};
+    float4v acc[8], accl[8];  // [4 g + mm]: hi and lo (x kLoScale) weight halves
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-        m_run[bb] = 0.0f;
-        l_run[bb] = 0.0f;
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-            b_run[bb][g] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            acc[bb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-            accl[bb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-            tot[bb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-            totl[bb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-        }
+    for (int m = 0; m < 8; ++m) {
+        acc[m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+        accl[m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
     }
 
 #pragma unroll 1
@@ -198,196 +184,147 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const int ti = kk + u;
             const int slot = u & 1;
 
-            // factors of the lane's 8 rows (4 q4 + i, 16 + 4 q4 + i - 4) for both groups
-            float4 fac[8][NG];
+            // ---- scores of the lane's 8 rows (4 q4 + i, 16 + 4 q4 + i - 4), log2 units
+            float sc[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-                    fac[i][g] = mring[slot][(16 * (i >> 2) + 4 * q4 + (i & 3)) * NG + g];
-
-            // K operands of the tile (shared by every column block)
-            half8 ka[2][KM];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int uu = 0; uu < KM; ++uu)
-                    ka[blk][uu] = k_operand_sub(kbuf[u][blk][uu], m_fine);
-
-            // value operands per group: the lane's word gives dimensions 0..3
-            // in its own group's products and lends 4..7 to lane l ^ 8
-            half8 bv[NG][4];
-            {
-                uint32_t bx[2][4];
-#pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    const uint32_t xw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x05040100u);
-                    const uint32_t yw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x07060302u);
-                    bx[0][jp] = take_half_row<0xC>(xw, yw);
-                    bx[1][jp] = take_half_row<0x3>(xw, yw);
-                }
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-#pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) {
-                        half2v e[4];
-#pragma unroll
-                        for (int jp = 0; jp < 4; ++jp)
-                            e[jp] = unpack.one(bx[g][jp], mm);
-                        bv[g][mm] = cat8(e[0], e[1], e[2], e[3]);
-                    }
-            }
-
-            const bool edge = PT * ti + PT - 1 > t_all;  // uniform: some row is past some column's position
-
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-                // ---- scores of the lane's 8 rows for column 16 bb + col (log2 units)
-                float sc[8];
-#pragma unroll
-                for (int blk = 0; blk < 2; ++blk) {
-                    float s[4] = {-m_run[bb], -m_run[bb], -m_run[bb], -m_run[bb]};
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) {
-                        float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                        for (int k = 0; k < KPG; ++k)
-                            sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[blk][g * KPG + k], qop[bb][g * KPG + k],
-                                                                         sacc, 0, 0, 0);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float4 f = fac[4 * blk + i][g];
-                            s[i] = fmaf(f.x, sacc[i], fmaf(f.y, qsum[bb][g], s[i]));
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sc[4 * blk + i] = s[i];
-                }
-                if (edge) {
-                    asm volatile("" ::: "memory");  // keep this a branch
-                    const int lim = t_all + cpos[bb];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int r = PT * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
-                        sc[i] = r <= lim ? sc[i] : -INFINITY;
-                    }
-                }
-                const float mx = max3_raw(max3_raw(sc[0], sc[1], sc[2]), max3_raw(sc[3], sc[4], sc[5]),
-                                          max_raw(sc[6], sc[7]));
-                // ---- reference raised only when a score exceeds it (the first tile sets it)
-                if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > 0.0f) != 0) {
-                    const float full = xrow_max(mx, -INFINITY);
-                    const bool raise = full > 0.0f || (ti == 0 && full > -INFINITY);
-                    const float delta = raise ? full + kHeadroom : 0.0f;
-                    m_run[bb] += delta;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        sc[i] -= delta;
-                    if (ti != 0) {
-                        const float corr = __builtin_amdgcn_exp2f(-delta);
-                        l_run[bb] *= corr;
-#pragma unroll
-                        for (int g = 0; g < NG; ++g)
-                            b_run[bb][g] *= corr;
-                        float4v corr_row;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            corr_row[i] = __shfl(corr, 4 * q4 + i);
-                        mfma_result_wait();
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            scale_in_place(acc[bb][m], corr_row);
-                            scale_in_place(accl[bb][m], corr_row);
-                            tot[bb][m] *= corr_row;
-                            totl[bb][m] *= corr_row;
-                        }
-                    }
-                }
-
-                // ---- weights and value products, group by group
-                float p[8];
-                float lsum = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(sc[i]);
-                    lsum += p[i];
-                }
-                l_run[bb] += lsum;
+            for (int blk = 0; blk < 2; ++blk) {
+                float s[4] = {-m_run, -m_run, -m_run, -m_run};
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
-                    half8 phi, plo;
-                    float bsum = 0.0f;
+                    float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int j = 0; j < 8; j += 2) {
-                        bsum = fmaf(p[j], fac[j][g].w, fmaf(p[j + 1], fac[j + 1][g].w, bsum));
-                        const float w0 = p[j] * fac[j][g].z, w1 = p[j + 1] * fac[j + 1][g].z;
-                        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-                        const half2v l = __builtin_bit_cast(
-                            half2v, __builtin_amdgcn_cvt_pkrtz((w0 - (float)h[0]) * kLoScale,
-                                                               (w1 - (float)h[1]) * kLoScale));
-                        phi[j] = h[0]; phi[j + 1] = h[1];
-                        plo[j] = l[0]; plo[j + 1] = l[1];
-                    }
-                    b_run[bb][g] += bsum;
+                    for (int k = 0; k < KPG; ++k)
+                        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand_sub(kbuf[u][blk][g * KPG + k], m_fine),
+                                                                     qop[g * KPG + k], sacc, 0, 0, 0);
 #pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) {
-                        acc[bb][4 * g + mm] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv[g][mm], acc[bb][4 * g + mm], 0, 0, 0);
-                        accl[bb][4 * g + mm] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv[g][mm], accl[bb][4 * g + mm], 0, 0, 0);
+                    for (int i = 0; i < 4; ++i) {
+                        const float2 f = fac_xy(slot, 16 * blk + 4 * q4 + i, g);
+                        s[i] = fmaf(f.x, sacc[i], fmaf(f.y, qsum[g], s[i]));
                     }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sc[4 * blk + i] = s[i];
+            }
+            if (PT * ti + PT - 1 > t_all) {  // uniform: some row is past some column's position
+                asm volatile("" ::: "memory");  // keep this a branch
+                const int lim = t_all + cpos;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = PT * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
+                    sc[i] = r <= lim ? sc[i] : -INFINITY;
+                }
+            }
+            const float mx = max3_raw(max3_raw(sc[0], sc[1], sc[2]), max3_raw(sc[3], sc[4], sc[5]),
+                                      max_raw(sc[6], sc[7]));
+            // ---- reference raised only when a score exceeds it (the first tile sets it)
+            if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > 0.0f) != 0) {
+                const float full = xrow_max(mx, -INFINITY);
+                const bool raise = full > 0.0f || (ti == 0 && full > -INFINITY);
+                const float delta = raise ? full + kHeadroom : 0.0f;
+                m_run += delta;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    sc[i] -= delta;
+                if (ti != 0) {
+                    const float corr = __builtin_amdgcn_exp2f(-delta);
+                    l_run *= corr;
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        b_run[g] *= corr;
+                    float4v corr_row;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        corr_row[i] = __shfl(corr, 4 * q4 + i);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        acc[m] *= corr_row;
+                        accl[m] *= corr_row;
+                    }
+                }
+            }
+
+            // ---- weights and value products, group by group
+            float p[8];
+            float lsum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(sc[i]);
+                lsum += p[i];
+            }
+            l_run += lsum;
+            // the lane's word gives dimensions 0..3 in its own group's
+            // products and lends 4..7 to lane l ^ 8
+            uint32_t bx[NG][4];
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp) {
+                const uint32_t xw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x05040100u);
+                const uint32_t yw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x07060302u);
+                bx[0][jp] = take_half_row<0xC>(xw, yw);
+                bx[1][jp] = take_half_row<0x3>(xw, yw);
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                half8 phi, plo;
+                float bsum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const float2 f0 = fac_zw(slot, 16 * (j >> 2) + 4 * q4 + (j & 3), g);
+                    const float2 f1 = fac_zw(slot, 16 * ((j + 1) >> 2) + 4 * q4 + ((j + 1) & 3), g);
+                    bsum = fmaf(p[j], f0.y, fmaf(p[j + 1], f1.y, bsum));
+                    const float w0 = p[j] * f0.x, w1 = p[j + 1] * f1.x;
+                    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                    const half2v l = __builtin_bit_cast(
+                        half2v, __builtin_amdgcn_cvt_pkrtz((w0 - (float)h[0]) * kLoScale, (w1 - (float)h[1]) * kLoScale));
+                    phi[j] = h[0]; phi[j + 1] = h[1];
+                    plo[j] = l[0]; plo[j + 1] = l[1];
+                }
+                b_run[g] += bsum;
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    half2v e[4];
+#pragma unroll
+                    for (int jp = 0; jp < 4; ++jp)
+                        e[jp] = unpack.one(bx[g][jp], mm);
+                    const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                    acc[4 * g + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[4 * g + mm], 0, 0, 0);
+                    accl[4 * g + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, accl[4 * g + mm], 0, 0, 0);
                 }
             }
 
             load_tile(ti + PF, kbuf[u], vbuf[u], mbuf[u]);
             stage_meta(slot ^ 1, mbuf[(u + 1) % PF]);
-            if (ti % FLUSH == FLUSH - 1) {  // uniform
-#pragma unroll
-                for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        tot[bb][m] += acc[bb][m];
-                        totl[bb][m] += accl[bb][m];
-                        acc[bb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-                        accl[bb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-                    }
-            }
         }
     }
 
-    // ---- normalised outputs: row r = 4 q4 + i of block bb is column 16 bb + r
+    // ---- normalised outputs: row r = 4 q4 + i is column r
+    const float l_tot = xrow_sum(l_run);
+    float b_tot[NG];
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-        const float l_tot = xrow_sum(l_run[bb]);
-        float b_tot[NG];
+    for (int g = 0; g < NG; ++g)
+        b_tot[g] = xrow_sum(b_run[g]);
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
-            b_tot[g] = xrow_sum(b_run[bb][g]);
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * q4 + i;
+        const float inv_l = 1.0f / __shfl(l_tot, r);
+        const int rpos = r / nrep, rhead = r % nrep;
+        const bool on = r < a.pb * nrep && rpos < npos;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * q4 + i;
-            const int c = 16 * bb + r;
-            const float inv_l = 1.0f / __shfl(l_tot, r);
-            const int rpos = c / nrep, rhead = c % nrep;
-            const bool on = c < a.pb * nrep && rpos < npos;
+        for (int g = 0; g < NG; ++g) {
+            const float bias = __shfl(b_tot[g], r);
+            // group g's products of this lane: dimensions 8 col + 0..3 when
+            // its own word is in g, else 8 (col ^ 8) + 4..7
+            const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
+            float o[4];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const float bias = __shfl(b_tot[g], r);
-                // group g's products of this lane: dimensions 8 col + 0..3 when
-                // its own word is in g, else 8 (col ^ 8) + 4..7
-                const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
-                float o[4];
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const float hi = tot[bb][4 * g + mm][i] + acc[bb][4 * g + mm][i];
-                    const float lo = totl[bb][4 * g + mm][i] + accl[bb][4 * g + mm][i];
-                    o[mm] = (fmaf(lo, 1.0f / kLoScale, hi) + bias) * inv_l;
-                }
-                if (on) {
-                    float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
-                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-                }
+            for (int mm = 0; mm < 4; ++mm) {
+                const float hi = acc[4 * g + mm][i];
+                const float lo = accl[4 * g + mm][i];
+                o[mm] = (fmaf(lo, 1.0f / kLoScale, hi) + bias) * inv_l;
+            }
+            if (on) {
+                float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
+                *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
             }
         }
     }
@@ -397,18 +334,18 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
 {
-    return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 * PB_BLOCKS && q_dtype == KVQ_F16 && bits == 4;
+    return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 && q_dtype == KVQ_F16 && bits == 4;
 }
 
-int prefill_positions_per_block(int n_rep) { return 16 * PB_BLOCKS / n_rep; }
+int prefill_positions_per_block(int n_rep) { return 16 / n_rep; }
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
 {
-    if (a.pb < 1 || a.pb * a.n_rep > 16 * PB_BLOCKS)
+    if (a.pb < 1 || a.pb * a.n_rep > 16)
         return hipErrorInvalidValue;
     const int64_t blocks = (a.sq + a.pb - 1) / a.pb;
     dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
-    hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<PB_BLOCKS, 2>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
