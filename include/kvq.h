@@ -251,6 +251,25 @@ int kvq_decode_step(const kvq_cache *cache, int64_t len, const void *k_new, cons
                     float *part_l, float *part_acc, float *out, int kernel, void *stream);
 
 /*
+ * One decode step on a Hadamard-rotated cache (the rotation of
+ * kvq_quantize_kv_append_rotated; blog on running Gemma 4 with TurboQuant,
+ * "TurboQuant" section): the token's fp16 K/V rows are rotated and
+ * quantised into row `len`, the query is rotated, attention runs over rows
+ * 0..len, and the output is rotated back, so `out` is the attention output
+ * in the original coordinates. Arguments as kvq_decode_step, but k_new and
+ * v_new must be fp16 (KVQ_E_DTYPE otherwise), and `out` must not overlap q
+ * unless q is fp32 and out == q (KVQ_E_SHAPE).
+ * With the one-wavefront kernel and D = 128 the step is two launches: the
+ * attention kernel rotates the query in float64 in its prologue and the
+ * appended rows in its fused append, and the reduce rotates each head's
+ * output before storing it. Otherwise the query is first rotated into
+ * `out` (four launches).
+ */
+int kvq_decode_step_rotated(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                            const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk,
+                            float *part_m, float *part_l, float *part_acc, float *out, int kernel, void *stream);
+
+/*
  * kvq_decode_step with its attention kernel timed: start_event / stop_event
  * (hipEvent_t with timing, either may be NULL) are recorded in that kernel's
  * own dispatch, as in kvq_sdpa_int4_partial_timed (in the fused step this is

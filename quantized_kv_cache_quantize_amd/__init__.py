@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     QuantKVCache,
     cache_bytes,
     decode_step,
+    decode_step_rotated,
     hadamard_rotate,
     lib,
     lib_path,

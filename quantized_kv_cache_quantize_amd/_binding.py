@@ -77,6 +77,9 @@ def lib():
     L.kvq_sdpa_int4_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i64, vp, vp]
     L.kvq_decode_step.restype = C.c_int
     L.kvq_decode_step.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int, vp]
+    L.kvq_decode_step_rotated.restype = C.c_int
+    L.kvq_decode_step_rotated.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int,
+                                          vp]
     L.kvq_decode_step_timed.restype = C.c_int
     L.kvq_decode_step_timed.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int,
                                         vp, vp, vp]
@@ -311,4 +314,25 @@ def sdpa_int4_prefill(cache: QuantKVCache, q_start: int, q: torch.Tensor, softma
     _check("kvq_sdpa_int4_prefill",
            lib().kvq_sdpa_int4_prefill(C.byref(cs), int(q_start), int(sq), _ptr(q), _dtype_code(q), hq,
                                        float(softmax_scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_step_rotated(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                        softmax_scale: float, chunk: int = 512, out: torch.Tensor | None = None, workspace=None,
+                        kernel: int = KERNEL_AUTO, stream=None):
+    """kvq_decode_step_rotated: the decode step on a Hadamard-rotated cache
+    (fp16 k_new, v_new; q and out in the original coordinates); returns out
+    [B][Hq][D] fp32."""
+    assert q.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
+    b, hq, d = q.shape
+    if workspace is None:
+        workspace = partials_buffers(b, hq, d, length + 1, chunk, device=q.device)
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+    m, l, acc = workspace
+    cs = cache.c_struct()
+    _check("kvq_decode_step_rotated",
+           lib().kvq_decode_step_rotated(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                         _ptr(q), _dtype_code(q), hq, float(softmax_scale), int(chunk), _ptr(m),
+                                         _ptr(l), _ptr(acc), _ptr(out), int(kernel), _stream(stream)))
     return out

@@ -259,6 +259,9 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     a.v_new = nullptr;
     a.append_row = -1;
     a.append_dtype = KVQ_F16;
+    a.rotate = 0;
+    a.q_f16 = 0;
+    a.rot_scale = 0.0;
     const bool mfma_ok = mfma_supports(cache->head_dim, cache->group, n_rep, chunk) &&
                          (bits == 4 || mfma_one_wave_ok(a, cache->head_dim, cache->batch));
     if (want_mfma && !mfma_ok)
@@ -324,6 +327,7 @@ int kvq_sdpa_int4_reduce(const float *part_m, const float *part_l, const float *
     a.heads = (int64_t)batch * Hq;
     a.C = num_chunks;
     a.D = head_dim;
+    a.rot_scale = 0.0;
     return launch_status(launch_reduce(a, (hipStream_t)stream));
 }
 
@@ -388,15 +392,32 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
 
 namespace {
 
+// rows_b[i] = H_D rows_a[i] / sqrt(D) for the query (fp32 out) and the output
+// reduce of a rotated decode step
+int reduce_rotated(const float *part_m, const float *part_l, const float *part_acc, const kvq_cache *cache, int32_t Hq,
+                   int64_t num_chunks, float *out, hipStream_t s)
+{
+    ReduceArgs ra;
+    ra.part_m = part_m;
+    ra.part_l = part_l;
+    ra.part_acc = part_acc;
+    ra.out = out;
+    ra.heads = (int64_t)cache->batch * Hq;
+    ra.C = num_chunks;
+    ra.D = cache->head_dim;
+    ra.rot_scale = 1.0 / sqrt((double)cache->head_dim);
+    return launch_status(launch_reduce(ra, s));
+}
+
 int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
                      const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,
-                     float *part_l, float *part_acc, float *out, int kernel, const Launch &l)
+                     float *part_l, float *part_acc, float *out, int kernel, const Launch &l, bool rotate)
 {
     void *stream = (void *)l.s;
     int st = check_cache(cache);
     if (st)
         return st;
-    if (kv_dtype != KVQ_F16 && kv_dtype != KVQ_F32)
+    if (kv_dtype != KVQ_F16 && (kv_dtype != KVQ_F32 || rotate))
         return KVQ_E_DTYPE;
     if (len < 0)
         return KVQ_E_SHAPE;
@@ -406,10 +427,30 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
         return KVQ_E_NULL;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
         return KVQ_E_ALIGN;
+    if (rotate && (q_dtype != KVQ_F16 && q_dtype != KVQ_F32))
+        return KVQ_E_DTYPE;
+    if (rotate && (!q || !aligned16(q)))
+        return !q ? KVQ_E_NULL : KVQ_E_ALIGN;
+    if (rotate) {  // out may hold the rotated query: it must not overlap q, except fp32 q in place
+        const int64_t n = (int64_t)cache->batch * Hq * cache->head_dim;
+        if (overlaps(q, n * (q_dtype == KVQ_F16 ? 2 : 4), out, n * 4) && !(q_dtype == KVQ_F32 && (const void *)out == q))
+            return KVQ_E_SHAPE;
+    }
+    // a rotated step that cannot rotate the query inside the attention kernel
+    // first rotates it into `out` (fp32, the query's size) and attends with that
     PartialPlan p;
     st = prepare_partial(cache, len + 1, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l, part_acc, kernel, p);
     if (st)
         return st;
+    const bool rot_inside = rotate && p.use_mfma && cache->head_dim == 128 &&
+                            mfma_one_wave_ok(p.a, cache->head_dim, cache->batch) &&
+                            (kernel != KVQ_KERNEL_MFMA_SPLIT && kernel != KVQ_KERNEL_MFMA_PAIR);
+    if (rotate && !rot_inside) {
+        st = prepare_partial(cache, len + 1, out, KVQ_F32, Hq, softmax_scale, chunk, part_m, part_l, part_acc, kernel,
+                             p);
+        if (st)
+            return st;
+    }
     // fused when the one-wavefront kernel is the one that runs: forced, or
     // AUTO / MFMA at one (chunk, KV head) item or more per SIMD (below that
     // the four-wavefront kernel plus a separate append is faster)
@@ -417,21 +458,49 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
     // (8-bit caches: always, the one-wavefront kernel being their only
     // matrix-core kernel)
     const bool fused = p.use_mfma && mfma_one_wave_ok(p.a, cache->head_dim, cache->batch) &&
-                       (kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 ||
+                       (kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 || rot_inside ||
                         ((kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) && items >= kOneWaveItems));
     if (fused) {
         p.a.k_new = k_new;
         p.a.v_new = v_new;
         p.a.append_row = len;
         p.a.append_dtype = kv_dtype;
-        st = launch_status(launch_decode_fused(p.a, cache->head_dim, q_dtype, cache->batch, l));
+        int launch_q_dtype = q_dtype;
+        if (rotate) {
+            p.a.rot_scale = 1.0 / sqrt((double)cache->head_dim);
+            launch_q_dtype = KVQ_F32;  // the split-query kernel variant
+            if (rot_inside) {          // rotate the appended rows and the query (read as given)
+                p.a.rotate = kRotateRows | kRotateQuery;
+                p.a.q_f16 = q_dtype == KVQ_F16;
+            } else {                   // query rotated beforehand (into out); rotate only the rows
+                p.a.rotate = kRotateRows;
+                p.a.q_f16 = 0;
+            }
+        }
+        if (rotate && !rot_inside) {
+            RotateArgs ra{q, out, (int64_t)cache->batch * Hq, cache->head_dim, 1.0 / sqrt((double)cache->head_dim)};
+            st = launch_status(launch_rotate(ra, q_dtype, l.s));
+            if (st)
+                return st;
+            p.a.q = out;
+        }
+        st = launch_status(launch_decode_fused(p.a, cache->head_dim, launch_q_dtype, cache->batch, l));
     } else {
-        st = kvq_quantize_kv_append(cache, len, k_new, v_new, kv_dtype, 1, stream);
+        if (rotate) {
+            RotateArgs ra{q, out, (int64_t)cache->batch * Hq, cache->head_dim, 1.0 / sqrt((double)cache->head_dim)};
+            st = launch_status(launch_rotate(ra, q_dtype, l.s));
+            if (!st)
+                st = kvq_quantize_kv_append_rotated(cache, len, k_new, v_new, kv_dtype, 1, stream);
+        } else {
+            st = kvq_quantize_kv_append(cache, len, k_new, v_new, kv_dtype, 1, stream);
+        }
         if (!st)
-            st = launch_plan(p, cache, q_dtype, kernel, l);
+            st = launch_plan(p, cache, rotate ? KVQ_F32 : q_dtype, kernel, l);
     }
     if (st)
         return st;
+    if (rotate)
+        return reduce_rotated(part_m, part_l, part_acc, cache, Hq, p.a.num_chunks, out, l.s);
     return kvq_sdpa_int4_reduce(part_m, part_l, part_acc, cache->batch, Hq, cache->head_dim, p.a.num_chunks, out,
                                 stream);
 }
@@ -446,7 +515,16 @@ int kvq_decode_step(const kvq_cache *cache, int64_t len, const void *k_new, cons
 {
     const Launch l{(hipStream_t)stream, nullptr, nullptr};
     return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l,
-                            part_acc, out, kernel, l);
+                            part_acc, out, kernel, l, false);
+}
+
+int kvq_decode_step_rotated(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                            const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,
+                            float *part_l, float *part_acc, float *out, int kernel, void *stream)
+{
+    const Launch l{(hipStream_t)stream, nullptr, nullptr};
+    return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l,
+                            part_acc, out, kernel, l, true);
 }
 
 int kvq_decode_step_timed(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
@@ -456,7 +534,7 @@ int kvq_decode_step_timed(const kvq_cache *cache, int64_t len, const void *k_new
 {
     const Launch l{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
     return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l,
-                            part_acc, out, kernel, l);
+                            part_acc, out, kernel, l, false);
 }
 
 }  // extern "C"

@@ -74,7 +74,16 @@ struct PartialArgs {
     const void *v_new;
     int64_t append_row;
     int32_t append_dtype;
+    // Hadamard-rotated cache (one-wavefront kernel): kRotateRows rotates the
+    // appended rows, kRotateQuery (D = 128, split-query variant) the query
+    // (read as fp16 when q_f16, else fp32), each by H_D * rot_scale in
+    // float64 before use; 0: no rotation.
+    int32_t rotate;
+    int32_t q_f16;
+    double rot_scale;
 };
+
+constexpr int32_t kRotateRows = 1, kRotateQuery = 2;
 
 struct ReduceArgs {
     const float *part_m;
@@ -84,6 +93,7 @@ struct ReduceArgs {
     int64_t heads;  // B * Hq
     int64_t C;
     int32_t D;
+    double rot_scale;  // nonzero: store H_D * out * rot_scale (the output of a rotated cache, rotated back)
 };
 
 // Prefill-side attention: queries of positions q_start .. q_start + sq - 1

@@ -42,6 +42,7 @@
 // valid rows (Skv), so rows past the end read as zero without per-row
 // clamping, and the eight value rows of a lane share one address register
 // (their distances are instruction offsets).
+#include "hadamard_row.h"
 #include "kvq_internal.h"
 #include "mfma_common.h"
 #include "quant_rule.h"
@@ -452,6 +453,16 @@ __device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvr
     } else {
         quant::load8<_Float16>(reinterpret_cast<const _Float16 *>(which ? a.v_new : a.k_new) + src, x);
     }
+    if (a.rotate & kRotateRows) {  // uniform: the rows of a Hadamard-rotated cache (fp16 rows, W lanes each)
+        double xd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            xd[j] = (double)x[j];
+        hadamard_row(xd, w, W, a.rot_scale);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = (float)xd[j];
+    }
     uint16_t sb, bb;
     uint32_t words[BITS / 4];
     quant::quantize_codes<LPG, BITS>(x, words, sb, bb);
@@ -561,7 +572,22 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 
     // ---- start-up: Q and the first PF tiles, all requested before the first wait
     float qv[KM][8];
-    {
+    bool q_done = false;
+    if constexpr (Q32 && D == 128) {
+        if (a.rotate & kRotateQuery) {  // uniform: the query of a Hadamard-rotated cache
+            // this lane's 32 dimensions 32 q4 + 8 u + j (exact in fp32), to be
+            // rotated once the first tiles are requested
+            const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D + 32 * q4;
+#pragma unroll
+            for (int u = 0; u < KM; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    qv[u][j] = a.q_f16 ? (float)reinterpret_cast<const _Float16 *>(a.q)[qrow + 8 * u + j]
+                                       : reinterpret_cast<const float *>(a.q)[qrow + 8 * u + j];
+            q_done = true;
+        }
+    }
+    if (!q_done) {
         const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
 #pragma unroll
         for (int u = 0; u < KM; ++u) {
@@ -649,6 +675,41 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         load_tile(u, kbuf[u], vbuf[u], mbuf[u]);
     }
     __builtin_amdgcn_sched_barrier(0);
+
+    if constexpr (Q32 && D == 128) {
+        if (a.rotate & kRotateQuery) {
+            // the query rotated in fp32 (its exact fp16 or fp32 values, seven
+            // butterfly stages: a relative error of a few 2^-24, far below
+            // the scores' own): dimension bits 0-4 inside the lane, bits 5
+            // and 6 between the lanes l ^ 16 and l ^ 32 that hold the rest of
+            // the head, each stage x' = partner + sign * x
+#pragma unroll
+            for (int sb = 1; sb < KM * 8; sb <<= 1)
+#pragma unroll
+                for (int j = 0; j < KM * 8; ++j)
+                    if (!(j & sb)) {
+                        float &x0 = qv[j / 8][j % 8], &x1 = qv[(j | sb) / 8][(j | sb) % 8];
+                        const float p = x0, r = x1;
+                        x0 = p + r;
+                        x1 = p - r;
+                    }
+#pragma unroll
+            for (int mb = 16; mb < 64; mb <<= 1) {
+                const float sign = (lane & mb) ? -1.0f : 1.0f;
+#pragma unroll
+                for (int u = 0; u < KM; ++u)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        qv[u][j] = fmaf(sign, qv[u][j], __shfl_xor(qv[u][j], mb));
+            }
+            const float rs = (float)a.rot_scale;
+#pragma unroll
+            for (int u = 0; u < KM; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    qv[u][j] *= rs;
+        }
+    }
 
     // Q restricted to the column's group, in the dimension order of the K
     // operands; qsum is the group sum of exactly what the matrix core sees

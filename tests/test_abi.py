@@ -272,3 +272,25 @@ def test_prefill_validation(L):
     assert _prefill(L, _cache(bits=8)) == E_UNSUP
     assert _prefill(L, _cache(), qd=1) == E_UNSUP
     assert _prefill(L, _cache(kv_heads=2), hq=64) == E_UNSUP
+
+
+def _step_rot(L, cache, length=100, k=P, v=P, kvd=0, q=P, qd=0, hq=64, scale=0.1, chunk=512, m=P, l=P, acc=P,
+              out=P + 0x100000, kernel=0):
+    return L.kvq_decode_step_rotated(C.byref(cache) if cache is not None else None, length, k, v, kvd, q, qd, hq,
+                                     scale, chunk, m, l, acc, out, kernel, None)
+
+
+def test_rotated_decode_step_validation(L):
+    c = _cache()
+    assert _step_rot(L, None) == E_NULL
+    assert _step_rot(L, c, kvd=1) == E_DTYPE          # rotated rows must be fp16
+    assert _step_rot(L, c, qd=7) == E_DTYPE
+    assert _step_rot(L, c, q=None) == E_NULL
+    assert _step_rot(L, c, out=None) == E_NULL
+    assert _step_rot(L, c, q=P + 8) == E_ALIGN
+    assert _step_rot(L, c, length=1024) == E_CAP
+    assert _step_rot(L, c, hq=12) == E_SHAPE
+    # out holds the rotated query in some paths: no overlap with q but fp32 in place
+    assert _step_rot(L, c, q=P, out=P + 256) == E_SHAPE
+    assert _step_rot(L, c, qd=0, q=P, out=P) == E_SHAPE
+    assert _step_rot(L, c, kernel=4, chunk=1024) == E_UNSUP

@@ -154,3 +154,90 @@ def test_rotated_attention_gemma():
     note("rotated attention gemma D=256")
     q, k, v, alpha = kvq_synth.gemma_layer(786)
     _rotated_attention(q, k, v, alpha, label="rotated gemma")
+
+
+# ------------------------------------------------------- rotated decode step
+
+def _rot_step_case(q, k, v, alpha, length, cap, kernel, q_dev=None, out=None):
+    """Rows [0, length) rotated into the cache by the oracle; the step rotates
+    and appends row `length` and attends over rows 0..length. Returns the GPU
+    output and the oracle cache after the same append."""
+    B, Hkv, _, D = k.shape
+    oc = oracle.Cache(B, Hkv, D, cap, 64)
+    if length:
+        oc.append_rotated(np.ascontiguousarray(k[:, :, :length]), np.ascontiguousarray(v[:, :, :length]), 0)
+    kn = np.ascontiguousarray(k[:, :, length:length + 1])
+    vn = np.ascontiguousarray(v[:, :, length:length + 1])
+    from _gpu_common import gpu_cache_from_oracle
+    g = gpu_cache_from_oracle(oc)
+    got = kvq.decode_step_rotated(g, length, to_dev(kn), to_dev(vn), to_dev(q) if q_dev is None else q_dev, alpha,
+                                  kernel=kernel, out=out)
+    torch.cuda.synchronize()
+    oc.append_rotated(kn, vn, length)
+    assert_cache_equal(g, oc)
+    return got.cpu().numpy(), oc
+
+
+GATES = {kvq.KERNEL_VALU: 2e-5}
+
+
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_VALU])
+@pytest.mark.parametrize("length", [0, 700, 4095])
+def test_rotated_decode_step_llama(kernel, length):
+    """The fused path (one-wavefront kernel: query rotated in its prologue,
+    rows in its append, output in the reduce) and the fallbacks agree with
+    the oracle's attention over the rotated cache, rotated back."""
+    note("rotated step llama len=%d kernel=%d" % (length, kernel))
+    q, k, v, alpha = kvq_synth.llama_layer(length + 1)
+    got, oc = _rot_step_case(q, k, v, alpha, length, 4096 + 8, kernel)
+    check_attention(got, oracle.sdpa_rotated(oc, length + 1, q, alpha), GATES.get(kernel, 1e-4),
+                    label="rotated step")
+
+
+def test_rotated_decode_step_matches_separate_calls():
+    """The fused step against the four separate calls it replaces (rotate q,
+    rotated append, attention with the fp32 rotated query, reduce, rotate the
+    output): the same numbers up to the reduce's summation order."""
+    note("rotated step vs separate calls")
+    length = 2047
+    q, k, v, alpha = kvq_synth.llama_layer(length + 1)
+    got, oc = _rot_step_case(q, k, v, alpha, length, 2048, kvq.KERNEL_MFMA_WAVE)
+    from _gpu_common import gpu_cache_from_oracle
+    g = gpu_cache_from_oracle(oc)  # already holds the rotated row `length`
+    qr = kvq.hadamard_rotate(to_dev(q))
+    sep = kvq.sdpa_int4(g, length + 1, qr, alpha, kernel=kvq.KERNEL_MFMA_WAVE)
+    kvq.hadamard_rotate(sep, out=sep)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(got, sep.cpu().numpy(), rtol=1e-5, atol=1e-7)
+
+
+def test_rotated_decode_step_fp32_query_in_place():
+    note("rotated step fp32 q in place")
+    length = 1000
+    q, k, v, alpha = kvq_synth.llama_layer(length + 1)
+    qd = to_dev(q.astype(np.float32))
+    for kernel in (kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_MFMA_SPLIT):
+        buf = qd.clone()
+        got, oc = _rot_step_case(q, k, v, alpha, length, 1024, kernel, q_dev=buf, out=buf)
+        check_attention(got, oracle.sdpa_rotated(oc, length + 1, q.astype(np.float32), alpha), 1e-4,
+                        label="rotated step fp32 in place kernel=%d" % kernel)
+
+
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE])
+def test_rotated_decode_step_gemma(kernel):
+    """D = 256: the query is rotated before the attention kernel, the rows
+    inside its append."""
+    note("rotated step gemma kernel=%d" % kernel)
+    q, k, v, alpha = kvq_synth.gemma_layer(787)
+    got, oc = _rot_step_case(q, k.astype(np.float16), v.astype(np.float16), alpha, 786, 800, kernel)
+    check_attention(got, oracle.sdpa_rotated(oc, 787, q, alpha), 2e-4, atol=1e-3, rtol=1e-3, label="rotated gemma")
+
+
+def test_rotated_decode_step_rejects_fp32_rows():
+    note("rotated step fp32 rows")
+    g = kvq.QuantKVCache(1, 8, 128, 16, 64, device="cuda")
+    q = torch.zeros((1, 64, 128), dtype=torch.float16, device="cuda")
+    kn = torch.zeros((1, 8, 1, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_step_rotated(g, 3, kn, kn, q, 0.1)
+    assert e.value.status == -5
