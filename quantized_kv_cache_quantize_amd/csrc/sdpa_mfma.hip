@@ -1343,9 +1343,11 @@ void sdpa_partial_mfma_pair_kernel(PartialArgs a)
 template <int D, int NG, bool Q32, int BITS>
 void launch_one_wave(const PartialArgs &a, dim3 grid, const Launch &l)
 {
-    // tiles in flight: 8-bit tiles are twice as large, so two of them carry
-    // as many bytes as four int4 tiles
-    constexpr int PF = (D == 128 && BITS == 4) ? 4 : 2;
+    // two tiles in flight per wavefront: with 2048 wavefronts at 128K that is
+    // 19 MB of int4 tiles requested at the start. Four int4 tiles (38 MB)
+    // measured 6% slower at 128K and 10% at 64K (presumably because each
+    // wavefront's first tile then queues behind more of the others' requests).
+    constexpr int PF = 2;
     hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF, BITS>), grid, dim3(64), 0, l.s, l.start, l.stop,
                           0, a);
 }
