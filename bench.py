@@ -148,7 +148,8 @@ def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"
             kvq.hadamard_rotate(L["out"], out=L["out"], stream=stream)
 
 
-def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused", bits=4, hkv=HKV):
+def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused", bits=4, hkv=HKV,
+                repeats=0):
     pool = make_pool(kvq, torch, skv, pool_bytes, chunk, bits=bits, hkv=hkv)
     run_steps(kvq, torch, pool, skv, chunk, kernel, warmup, step=step)
     torch.cuda.synchronize()
@@ -172,9 +173,52 @@ def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step=
     res = dict(skv=skv, ms_per_step=ms_per_step, partial_ms_avg=sum(kern_ms) / len(kern_ms),  # nan: not timed
                partial_ms_p10=kern_ms[len(kern_ms) // 10], partial_ms_p90=kern_ms[(9 * len(kern_ms)) // 10],
                pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv, bits, hkv) / 1e6)
+    if repeats:
+        # the step time's spread: `repeats` runs of steps // repeats steps,
+        # events around each run, per-step time of each run
+        per_run = max(1, steps // repeats)
+        runs = []
+        for _ in range(repeats):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            run_steps(kvq, torch, pool, skv, chunk, kernel, per_run, step=step)
+            b.record()
+            torch.cuda.synchronize()
+            runs.append(a.elapsed_time(b) / per_run)
+        runs.sort()
+        res.update(step_ms_median=runs[len(runs) // 2], step_ms_p10=runs[len(runs) // 10],
+                   step_ms_p90=runs[(9 * len(runs)) // 10], step_repeats=repeats, step_per_repeat=per_run)
     last = pool[-1]
     del pool
     return res, last
+
+
+def hbm_read_calibration(kvq, torch, gib: int = 1, reps: int = 20):
+    """Achievable HBM read bandwidth on this GPU, the context of the spec
+    fraction: the library's plain grid-stride read kernel (kvq_hbm_read)
+    over `gib` GiB, which no cache level holds; median over `reps` calls,
+    events around each."""
+    x = torch.ones((gib << 28,), dtype=torch.int32, device="cuda")
+    sink = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        kvq.hbm_read(x, sink)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        kvq.hbm_read(x, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    nbytes = x.numel() * 4
+    del x
+    ms = ts[len(ts) // 2]
+    return dict(kind="kvq_hbm_read (grid-stride 16-byte loads, 2048 x 256 threads) over %d GiB, median of %d calls"
+                % (gib, reps), bytes=nbytes, ms=round(ms, 4), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1))
 
 
 def time_layer_loop(kvq, torch, layers, skv, chunk, kernel, steps, warmup):
@@ -341,6 +385,11 @@ def main():
                     help="layers of the full-depth decode step timed after the headline (0 skips it)")
     ap.add_argument("--bits", type=int, choices=[4, 8], default=4,
                     help="bits per cached code of the headline run (8: the int8 cache, vector-ALU attention)")
+    ap.add_argument("--repeats", type=int, default=10,
+                    help="after the timed steps, time the same steps again as this many separate runs "
+                         "(median / p10 / p90 of the per-step time; 0 skips)")
+    ap.add_argument("--no-hbm-calibration", action="store_true",
+                    help="skip the plain read of 1 GiB that gives the achievable HBM bandwidth")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MB (a known-size reference "
                          "for hardware byte counters)")
@@ -348,8 +397,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the decode path would shard "
-              "over KV heads or sequence chunks; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path here (the decode path would shard "
+              "over KV heads or over sequence chunks). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -367,7 +416,7 @@ def main():
 
     bits = args.bits
     main_res, last = time_config(kvq, torch, args.skv, args.chunk, kernel, args.steps, args.warmup, pool_bytes,
-                                 step=args.step, bits=bits)
+                                 step=args.step, bits=bits, repeats=args.repeats)
     sweep = []
     for s in [int(x) for x in args.sweep.split(",") if x.strip()]:
         r, _ = time_config(kvq, torch, s, args.chunk, kernel, max(20, args.steps // 2), args.warmup, pool_bytes,
@@ -483,6 +532,7 @@ def main():
     ms = main_res["ms_per_step"]
     value = step_bytes / (ms * 1e-3) / 1e9
     achieved = layer_bytes(args.skv, bits) / (main_res["partial_ms_avg"] * 1e-3) / 1e9
+    calib = None if args.no_hbm_calibration else hbm_read_calibration(kvq, torch)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(kvq, torch, last, args.skv)
@@ -497,6 +547,11 @@ def main():
         "ms_per_step": round(ms, 6),
         "us_per_layer": round(ms * 1e3, 3),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "step_spread": None if "step_ms_median" not in main_res else {
+            "us_median": round(main_res["step_ms_median"] * 1e3, 3),
+            "us_p10": round(main_res["step_ms_p10"] * 1e3, 3),
+            "us_p90": round(main_res["step_ms_p90"] * 1e3, 3),
+            "runs": main_res["step_repeats"], "steps_per_run": main_res["step_per_repeat"]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -529,6 +584,9 @@ def main():
             "timing": "HIP events recorded in the kernel's own dispatch (hipExtLaunchKernel), averaged over the steps",
             "p10_launch_us": round(main_res["partial_ms_p10"] * 1e3, 3),
             "p90_launch_us": round(main_res["partial_ms_p90"] * 1e3, 3),
+            "achievable": None if calib is None else dict(
+                calib, frac=round(achieved / calib["gbs"], 4),
+                note="the attention kernel's achieved bandwidth as a fraction of this GPU's plain read rate"),
         },
         "cpu_baseline": cpu,
         "sweep": [{"skv": r["skv"], "us_per_layer": round(r["us_per_layer"], 3), "gbs": round(r["gbs"], 2),

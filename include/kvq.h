@@ -114,6 +114,22 @@ int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32
                         int32_t bits);
 
 /*
+ * Measurement helper, not a step of the method: read `bytes` bytes of device
+ * memory once with a plain grid-stride kernel (16-byte loads, 2048
+ * workgroups of 256 threads) and discard them. Timing it over a buffer no
+ * cache holds (>= 1 GB) gives the HBM read rate this GPU reaches, beside
+ * which the attention kernel's algorithmic bytes per second are judged.
+ *  buf:  device memory, 16-byte aligned; bytes: a multiple of 16, >= 0
+ *        (0: no-op returning KVQ_OK).
+ *  sink: one device uint32, 4-byte aligned; written only when a thread's XOR
+ *        of its words equals `key` (a caller-chosen value, so no load can be
+ *        dropped); the caller owns both buffers.
+ * KVQ_E_NULL / KVQ_E_SHAPE / KVQ_E_ALIGN before anything is enqueued;
+ * KVQ_E_LAUNCH if the launch fails. Asynchronous on `stream`.
+ */
+int kvq_hbm_read(const void *buf, int64_t bytes, uint32_t key, uint32_t *sink, void *stream);
+
+/*
  * Quantise n_new new rows of K and V and store them at rows
  * [len, len + n_new) of the cache ("quantize K,V to int4" in the README's
  * decode-step listing; prefill rows are appended the same way).
@@ -260,10 +276,11 @@ int kvq_decode_step(const kvq_cache *cache, int64_t len, const void *k_new, cons
  * v_new must be fp16 (KVQ_E_DTYPE otherwise), and `out` must not overlap q
  * unless q is fp32 and out == q (KVQ_E_SHAPE).
  * With the one-wavefront kernel and D = 128 the step is two launches: the
- * attention kernel rotates the query in float64 in its prologue and the
- * appended rows in its fused append, and the reduce rotates each head's
- * output before storing it. Otherwise the query is first rotated into
- * `out` (four launches).
+ * attention kernel rotates the query (fp32 butterflies, a relative error of
+ * a few 2^-24) in its prologue and the appended rows (float64, exact for
+ * fp16 rows) in its fused append, and the reduce rotates each head's output
+ * (fp32) before storing it. Otherwise the query is first rotated into `out`
+ * (four launches).
  */
 int kvq_decode_step_rotated(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
                             const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk,

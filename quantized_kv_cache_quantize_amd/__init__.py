@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     decode_step,
     decode_step_rotated,
     hadamard_rotate,
+    hbm_read,
     lib,
     lib_path,
     num_chunks,

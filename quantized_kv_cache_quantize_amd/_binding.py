@@ -63,6 +63,8 @@ def lib():
     L.kvq_num_chunks.argtypes = [i64, i32]
     L.kvq_cache_bytes.restype = i64
     L.kvq_cache_bytes.argtypes = [i32, i32, i32, i32, i64, i32]
+    L.kvq_hbm_read.restype = C.c_int
+    L.kvq_hbm_read.argtypes = [vp, i64, C.c_uint32, vp, vp]
     L.kvq_quantize_kv_append.restype = C.c_int
     L.kvq_quantize_kv_append.argtypes = [cp, i64, vp, vp, C.c_int, i64, vp]
     L.kvq_quantize_kv_append_rotated.restype = C.c_int
@@ -206,6 +208,15 @@ def hadamard_rotate(x: torch.Tensor, out: torch.Tensor | None = None, stream=Non
            lib().kvq_hadamard_rotate(_ptr(x), _dtype_code(x), int(x.numel() // d), int(d), _ptr(out),
                                      _stream(stream)))
     return out
+
+
+def hbm_read(buf: torch.Tensor, sink: torch.Tensor, key: int = 0xFFFFFFFF, stream=None) -> None:
+    """kvq_hbm_read: read every byte of the contiguous device tensor `buf`
+    once (a measurement helper); `sink` is a device int32 tensor of at least
+    one element, written only when a thread's XOR of its words equals key."""
+    assert buf.is_contiguous() and sink.dtype == torch.int32 and sink.numel() >= 1
+    _check("kvq_hbm_read", lib().kvq_hbm_read(_ptr(buf), int(buf.numel() * buf.element_size()), int(key) & 0xFFFFFFFF,
+                                              _ptr(sink), _stream(stream)))
 
 
 def partials_buffers(batch: int, hq: int, head_dim: int, skv: int, chunk: int = 512, device="cuda"):

@@ -294,3 +294,14 @@ def test_rotated_decode_step_validation(L):
     assert _step_rot(L, c, q=P, out=P + 256) == E_SHAPE
     assert _step_rot(L, c, qd=0, q=P, out=P) == E_SHAPE
     assert _step_rot(L, c, kernel=4, chunk=1024) == E_UNSUP
+
+
+def test_hbm_read_validation(L):
+    rd = L.kvq_hbm_read
+    assert rd(P, 0, 0, None, None) == OK          # nothing to read: no-op
+    assert rd(None, 1024, 0, P + 4096, None) == E_NULL
+    assert rd(P, 1024, 0, None, None) == E_NULL
+    assert rd(P, 1000, 0, P + 4096, None) == E_SHAPE  # not a multiple of 16
+    assert rd(P, -16, 0, P + 4096, None) == E_SHAPE
+    assert rd(P + 8, 1024, 0, P + 4096, None) == E_ALIGN
+    assert rd(P, 1024, 0, P + 4098, None) == E_ALIGN
