@@ -94,7 +94,7 @@ typedef struct kvq_cache {
     int32_t kv_heads;  /* Hkv >= 1 */
     int32_t head_dim;  /* D in {64, 128, 256} */
     int32_t group;     /* G in {32, 64, 128}, D % G == 0 */
-    int64_t capacity;  /* rows per (batch, KV head), >= 1; capacity * D * bits/8 < 2^31 - 2^16 */
+    int64_t capacity;  /* rows per (batch, KV head), >= 1; capacity * D * bits/8 <= 2^31 - 2^16 */
     int32_t bits;      /* bits per code: 4 (0 means 4) or 8 */
 } kvq_cache;
 
