@@ -7,11 +7,12 @@
 // q_start + i; its K/V row is cache row q_start + i (appended before the
 // call), and it attends to rows [0, q_start + i] (causal).
 //
-// Work split: one wavefront per (16 / n_rep query positions x the n_rep heads
+// Work split: one wavefront per (32 / n_rep query positions x the n_rep heads
 // of a KV head, batch), streaming the rows its positions can see in 32-row
 // tiles. With GQA the n_rep heads of a KV head and the block's positions all
-// read the same rows, so every K/V tile is fetched and unpacked once for 16
-// query columns.
+// read the same rows, so every K/V tile is fetched and unpacked once for 32
+// query columns (two blocks of 16, each the N side of its own matrix
+// instructions).
 //
 // Scores (per tile): S^T[t][c] = Kcodes[t][:] . Q[c][:] on
 // v_mfma_f32_16x16x32_f16, A = K codes (16 rows, 32 dimensions), B = the
@@ -44,15 +45,19 @@ namespace {
 
 constexpr int PT = 32;  // rows per tile
 
-// D = 128, two scale groups of 64, fp16 queries, int4 codes; 16 query
-// columns per wavefront; PF tiles in flight. Operands are unpacked right
+// D = 128, two scale groups of 64, fp16 queries, int4 codes; NB blocks of
+// 16 query columns per wavefront (every unpacked K and V operand feeds NB
+// matrix instructions); PF tiles in flight. Operands are unpacked right
 // before the instruction that reads them and the scale/bias factors read
-// from LDS where they are used, which keeps a wavefront within 256
-// registers (two per SIMD, no accumulation registers: beyond 256 the
-// compiler moved the accumulators between register files around every
-// matrix instruction).
-template <int PF>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+// from LDS where they are used. NB = 1 fits a wavefront in 256 registers
+// (two per SIMD). NB = 2 runs one wavefront per SIMD; its query operands
+// wait in LDS (read back every tile) to ease the register pressure, yet the
+// compiler still keeps part of the state in accumulation registers and
+// copies it around the matrix instructions. Measured on the Llama layer's
+// 4096-position chunk at row 61440: NB = 1 30.4 ms, NB = 2 with the queries
+// in registers 26.9 ms, NB = 2 with them in LDS 25.5 ms.
+template <int PF, int NB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
 void sdpa_prefill_mfma_kernel(PrefillArgs a)
 {
     constexpr int D = 128;
@@ -77,10 +82,18 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
     const bool low8 = (lane & 8) == 0;             // this lane's V word is in group 0
 
-    // column col: position col / nrep, head col % nrep (inactive columns
-    // compute on zero queries and are never stored)
-    const int cpos = col / nrep, chead = col % nrep;
-    const bool con = col < a.pb * nrep && cpos < npos;
+    // column 16 nb + col of the wavefront: position (16 nb + col) / nrep,
+    // head (16 nb + col) % nrep (inactive columns compute on zero queries and
+    // are never stored)
+    int cpos[NB], chead[NB];
+    bool con[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int cc = 16 * nb + col;
+        cpos[nb] = cc / nrep;
+        chead[nb] = cc % nrep;
+        con[nb] = cc < a.pb * nrep && cpos[nb] < npos;
+    }
 
     const uint32_t rows_ok = (uint32_t)t_end;
     const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
@@ -144,13 +157,18 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // the column's query as B operands: score product uu holds dimensions
-    // 32 uu + 8 q4 + kPerm[j]; qsum: group sums of exactly what the matrix
-    // core sees
-    half8 qop[KM];
-    float qsum[NG];
-    {
-        const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con ? chead : 0)) * a.sq + p0 + (con ? cpos : 0)) * D;
+    // each block's column query as B operands: score product uu holds
+    // dimensions 32 uu + 8 q4 + kPerm[j]; qsum: group sums of exactly what
+    // the matrix core sees
+    half8 qop[NB][KM];
+    float qsum[NB][NG];
+    // NB > 1: the operands wait in LDS and are read back tile by tile, which
+    // keeps the wavefront within 256 registers (see the kernel comment)
+    __shared__ __align__(16) half8 q_lds[NB > 1 ? NB : 1][KM][64];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con[nb] ? chead[nb] : 0)) * a.sq + p0 +
+                              (con[nb] ? cpos[nb] : 0)) * D;
         const _Float16 *qp = reinterpret_cast<const _Float16 *>(a.q) + qrow;
         float gs[NG] = {};
 #pragma unroll
@@ -158,23 +176,36 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const half8 x = *reinterpret_cast<const half8 *>(qp + 32 * uu + 8 * q4);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const _Float16 h = con ? x[kPerm[j]] : (_Float16)0.0f;
-                qop[uu][j] = h;
+                const _Float16 h = con[nb] ? x[kPerm[j]] : (_Float16)0.0f;
+                qop[nb][uu][j] = h;
                 gs[uu / KPG] += (float)h;
             }
         }
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-            qsum[g] = xrow_sum(gs[g]);
+            qsum[nb][g] = xrow_sum(gs[g]);
+        if constexpr (NB > 1) {
+#pragma unroll
+            for (int uu = 0; uu < KM; ++uu)
+                q_lds[nb][uu][lane] = qop[nb][uu];
+        }
     }
     stage_meta(0, mbuf[0]);
 
-    float m_run = 0.0f, l_run = 0.0f, b_run[NG] = {0.0f, 0.0f};
-    float4v acc[8], accl[8];  // [4 g + mm]: hi and lo (x kLoScale) weight halves
+    float m_run[NB], l_run[NB], b_run[NB][NG];
+    float4v acc[NB][8], accl[NB][8];  // [nb][4 g + mm]: hi and lo (x kLoScale) weight halves
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        acc[m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-        accl[m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = 0.0f;
+        l_run[nb] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            b_run[nb][g] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+            accl[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+        }
     }
 
 #pragma unroll 1
@@ -184,77 +215,102 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const int ti = kk + u;
             const int slot = u & 1;
 
-            // ---- scores of the lane's 8 rows (4 q4 + i, 16 + 4 q4 + i - 4), log2 units
-            float sc[8];
+            // ---- scores of the lane's 8 rows (4 q4 + i, 16 + 4 q4 + i - 4), log2 units,
+            // for each block's column; every K operand serves all NB blocks
+            float sc[NB][8];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
-                float s[4] = {-m_run, -m_run, -m_run, -m_run};
+                float s[NB][4];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[nb][i] = -m_run[nb];
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
-                    float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+                    float4v sacc[NB];
 #pragma unroll
-                    for (int k = 0; k < KPG; ++k)
-                        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand_sub(kbuf[u][blk][g * KPG + k], m_fine),
-                                                                     qop[g * KPG + k], sacc, 0, 0, 0);
+                    for (int nb = 0; nb < NB; ++nb)
+                        sacc[nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KPG; ++k) {
+                        const half8 ka = k_operand_sub(kbuf[u][blk][g * KPG + k], m_fine);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const half8 qb = NB > 1 ? q_lds[nb][g * KPG + k][lane] : qop[nb][g * KPG + k];
+                            sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, sacc[nb], 0, 0, 0);
+                        }
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float2 f = fac_xy(slot, 16 * blk + 4 * q4 + i, g);
-                        s[i] = fmaf(f.x, sacc[i], fmaf(f.y, qsum[g], s[i]));
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            s[nb][i] = fmaf(f.x, sacc[nb][i], fmaf(f.y, qsum[nb][g], s[nb][i]));
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sc[4 * blk + i] = s[i];
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sc[nb][4 * blk + i] = s[nb][i];
             }
             if (PT * ti + PT - 1 > t_all) {  // uniform: some row is past some column's position
                 asm volatile("" ::: "memory");  // keep this a branch
-                const int lim = t_all + cpos;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = PT * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
-                    sc[i] = r <= lim ? sc[i] : -INFINITY;
-                }
-            }
-            const float mx = max3_raw(max3_raw(sc[0], sc[1], sc[2]), max3_raw(sc[3], sc[4], sc[5]),
-                                      max_raw(sc[6], sc[7]));
-            // ---- reference raised only when a score exceeds it (the first tile sets it)
-            if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > 0.0f) != 0) {
-                const float full = xrow_max(mx, -INFINITY);
-                const bool raise = full > 0.0f || (ti == 0 && full > -INFINITY);
-                const float delta = raise ? full + kHeadroom : 0.0f;
-                m_run += delta;
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int lim = t_all + cpos[nb];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    sc[i] -= delta;
-                if (ti != 0) {
-                    const float corr = __builtin_amdgcn_exp2f(-delta);
-                    l_run *= corr;
-#pragma unroll
-                    for (int g = 0; g < NG; ++g)
-                        b_run[g] *= corr;
-                    float4v corr_row;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        corr_row[i] = __shfl(corr, 4 * q4 + i);
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        acc[m] *= corr_row;
-                        accl[m] *= corr_row;
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = PT * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
+                        sc[nb][i] = r <= lim ? sc[nb][i] : -INFINITY;
                     }
                 }
             }
-
-            // ---- weights and value products, group by group
-            float p[8];
-            float lsum = 0.0f;
+            float p[NB][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(sc[i]);
-                lsum += p[i];
+            for (int nb = 0; nb < NB; ++nb) {
+                const float mx = max3_raw(max3_raw(sc[nb][0], sc[nb][1], sc[nb][2]),
+                                          max3_raw(sc[nb][3], sc[nb][4], sc[nb][5]), max_raw(sc[nb][6], sc[nb][7]));
+                // ---- reference raised only when a score exceeds it (the first tile sets it)
+                if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > 0.0f) != 0) {
+                    const float full = xrow_max(mx, -INFINITY);
+                    const bool raise = full > 0.0f || (ti == 0 && full > -INFINITY);
+                    const float delta = raise ? full + kHeadroom : 0.0f;
+                    m_run[nb] += delta;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        sc[nb][i] -= delta;
+                    if (ti != 0) {
+                        const float corr = __builtin_amdgcn_exp2f(-delta);
+                        l_run[nb] *= corr;
+#pragma unroll
+                        for (int g = 0; g < NG; ++g)
+                            b_run[nb][g] *= corr;
+                        float4v corr_row;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            corr_row[i] = __shfl(corr, 4 * q4 + i);
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            acc[nb][m] *= corr_row;
+                            accl[nb][m] *= corr_row;
+                        }
+                    }
+                }
+                // ---- weights
+                float lsum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    p[nb][i] = __builtin_amdgcn_exp2f(sc[nb][i]);
+                    lsum += p[nb][i];
+                }
+                l_run[nb] += lsum;
             }
-            l_run += lsum;
-            // the lane's word gives dimensions 0..3 in its own group's
-            // products and lends 4..7 to lane l ^ 8
+
+            // ---- value products, group by group; the lane's word gives
+            // dimensions 0..3 in its own group's products and lends 4..7 to
+            // lane l ^ 8, and every unpacked operand serves all NB blocks
             uint32_t bx[NG][4];
 #pragma unroll
             for (int jp = 0; jp < 4; ++jp) {
@@ -265,21 +321,25 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             }
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                half8 phi, plo;
-                float bsum = 0.0f;
+                half8 phi[NB], plo[NB];
 #pragma unroll
-                for (int j = 0; j < 8; j += 2) {
-                    const float2 f0 = fac_zw(slot, 16 * (j >> 2) + 4 * q4 + (j & 3), g);
-                    const float2 f1 = fac_zw(slot, 16 * ((j + 1) >> 2) + 4 * q4 + ((j + 1) & 3), g);
-                    bsum = fmaf(p[j], f0.y, fmaf(p[j + 1], f1.y, bsum));
-                    const float w0 = p[j] * f0.x, w1 = p[j + 1] * f1.x;
-                    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-                    const half2v l = __builtin_bit_cast(
-                        half2v, __builtin_amdgcn_cvt_pkrtz((w0 - (float)h[0]) * kLoScale, (w1 - (float)h[1]) * kLoScale));
-                    phi[j] = h[0]; phi[j + 1] = h[1];
-                    plo[j] = l[0]; plo[j + 1] = l[1];
+                for (int nb = 0; nb < NB; ++nb) {
+                    float bsum = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2) {
+                        const float2 f0 = fac_zw(slot, 16 * (j >> 2) + 4 * q4 + (j & 3), g);
+                        const float2 f1 = fac_zw(slot, 16 * ((j + 1) >> 2) + 4 * q4 + ((j + 1) & 3), g);
+                        bsum = fmaf(p[nb][j], f0.y, fmaf(p[nb][j + 1], f1.y, bsum));
+                        const float w0 = p[nb][j] * f0.x, w1 = p[nb][j + 1] * f1.x;
+                        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                        const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(
+                                                                        (w0 - (float)h[0]) * kLoScale,
+                                                                        (w1 - (float)h[1]) * kLoScale));
+                        phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
+                        plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
+                    }
+                    b_run[nb][g] += bsum;
                 }
-                b_run[g] += bsum;
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm) {
                     half2v e[4];
@@ -287,8 +347,13 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                     for (int jp = 0; jp < 4; ++jp)
                         e[jp] = unpack.one(bx[g][jp], mm);
                     const half8 bv = cat8(e[0], e[1], e[2], e[3]);
-                    acc[4 * g + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[4 * g + mm], 0, 0, 0);
-                    accl[4 * g + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, accl[4 * g + mm], 0, 0, 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        acc[nb][4 * g + mm] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], bv, acc[nb][4 * g + mm], 0, 0, 0);
+                        accl[nb][4 * g + mm] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, accl[nb][4 * g + mm], 0, 0, 0);
+                    }
                 }
             }
 
@@ -297,34 +362,38 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
         }
     }
 
-    // ---- normalised outputs: row r = 4 q4 + i is column r
-    const float l_tot = xrow_sum(l_run);
-    float b_tot[NG];
+    // ---- normalised outputs: row r = 4 q4 + i is column 16 nb + r
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-        b_tot[g] = xrow_sum(b_run[g]);
+    for (int nb = 0; nb < NB; ++nb) {
+        const float l_tot = xrow_sum(l_run[nb]);
+        float b_tot[NG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * q4 + i;
-        const float inv_l = 1.0f / __shfl(l_tot, r);
-        const int rpos = r / nrep, rhead = r % nrep;
-        const bool on = r < a.pb * nrep && rpos < npos;
+        for (int g = 0; g < NG; ++g)
+            b_tot[g] = xrow_sum(b_run[nb][g]);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const float bias = __shfl(b_tot[g], r);
-            // group g's products of this lane: dimensions 8 col + 0..3 when
-            // its own word is in g, else 8 (col ^ 8) + 4..7
-            const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
-            float o[4];
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q4 + i;
+            const int cc = 16 * nb + r;
+            const float inv_l = 1.0f / __shfl(l_tot, r);
+            const int rpos = cc / nrep, rhead = cc % nrep;
+            const bool on = cc < a.pb * nrep && rpos < npos;
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm) {
-                const float hi = acc[4 * g + mm][i];
-                const float lo = accl[4 * g + mm][i];
-                o[mm] = (fmaf(lo, 1.0f / kLoScale, hi) + bias) * inv_l;
-            }
-            if (on) {
-                float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
-                *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            for (int g = 0; g < NG; ++g) {
+                const float bias = __shfl(b_tot[g], r);
+                // group g's products of this lane: dimensions 8 col + 0..3 when
+                // its own word is in g, else 8 (col ^ 8) + 4..7
+                const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
+                float o[4];
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const float hi = acc[nb][4 * g + mm][i];
+                    const float lo = accl[nb][4 * g + mm][i];
+                    o[mm] = (fmaf(lo, 1.0f / kLoScale, hi) + bias) * inv_l;
+                }
+                if (on) {
+                    float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                }
             }
         }
     }
@@ -337,15 +406,18 @@ bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
     return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 && q_dtype == KVQ_F16 && bits == 4;
 }
 
-int prefill_positions_per_block(int n_rep) { return 16 / n_rep; }
+// query columns per wavefront: kPrefillNB blocks of 16
+constexpr int kPrefillNB = 2;
+
+int prefill_positions_per_block(int n_rep) { return 16 * kPrefillNB / n_rep; }
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
 {
-    if (a.pb < 1 || a.pb * a.n_rep > 16)
+    if (a.pb < 1 || a.pb * a.n_rep > 16 * kPrefillNB)
         return hipErrorInvalidValue;
     const int64_t blocks = (a.sq + a.pb - 1) / a.pb;
     dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
-    hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

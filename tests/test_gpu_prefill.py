@@ -45,7 +45,8 @@ def test_gqa4(q_start, sq):
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (16, 16), (16, 1), (6, 2), (12, 4)])
 def test_head_layouts(hq, hkv):
     """GQA 8 (the Llama layer), MHA, 16 heads per KV head, and ratios that do
-    not divide the 16 query columns of a wavefront (3)."""
+    not divide the 32 query columns of a wavefront (3, with a position split
+    between the wavefront's two 16-column blocks)."""
     note("prefill heads hq=%d hkv=%d" % (hq, hkv))
     q, oc, alpha = _case(1, hq, hkv, 300, 45, seed=hq * 100 + hkv)
     got = _run(oc, 300, q, alpha)
