@@ -367,8 +367,8 @@ def cpu_baseline(kvq, torch, entry, skv):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--skv", type=int, default=131072)
     ap.add_argument("--chunk", type=int, default=512)
     ap.add_argument("--pool-mb", type=int, default=int(2.5 * MALL_BYTES / 1e6))
