@@ -298,16 +298,17 @@ def prefill_flops(q_start: int, sq: int, hq: int = HQ) -> int:
     return 2 * 2 * hq * D * rows
 
 
-def time_prefill(kvq, torch, q_start: int, sq: int, reps: int = 5):
+def time_prefill(kvq, torch, q_start: int, sq: int, reps: int = 5, bits: int = 4):
     """Prefill attention on the Llama layer: a cache of q_start + sq rows
-    (seeded fp16 N(0,1), quantised by the library), then kvq_sdpa_int4_prefill
-    for the sq positions after q_start. Returns the median kernel time in ms
-    (events around each call; one call runs for milliseconds)."""
+    (seeded fp16 N(0,1), quantised by the library with `bits` per code), then
+    kvq_sdpa_int4_prefill for the sq positions after q_start. Returns the
+    median kernel time in ms (events around each call; one call runs for
+    milliseconds)."""
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(99)
     S = q_start + sq
-    cache = kvq.QuantKVCache(B, HKV, D, S, G, device=dev)
+    cache = kvq.QuantKVCache(B, HKV, D, S, G, device=dev, bits=bits)
     for t0 in range(0, S, 16384):
         n = min(16384, S - t0)
         k = torch.randn((B, HKV, n, D), generator=gen, device=dev).half()
@@ -513,18 +514,20 @@ def main():
             "timing": "step and attention as the headline; append as the hadamard row's",
         }
         pf = {}
-        for name, qs, sq in (("chunk4096_at_61440", APPEND_LEN, APPEND_ROWS), ("prompt4096", 0, 4096)):
-            ms = time_prefill(kvq, torch, qs, sq)
+        for name, qs, sq, pbits in (("chunk4096_at_61440", APPEND_LEN, APPEND_ROWS, 4), ("prompt4096", 0, 4096, 4),
+                                    ("chunk4096_at_61440_int8", APPEND_LEN, APPEND_ROWS, 8)):
+            ms = time_prefill(kvq, torch, qs, sq, bits=pbits)
             fl = prefill_flops(qs, sq)
             pf[name] = {
-                "q_start": qs, "sq": sq, "ms": round(ms, 4),
+                "q_start": qs, "sq": sq, "bits": pbits, "ms": round(ms, 4),
                 "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                 "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-                "cache_gbs": round(layer_bytes(qs + sq) / (ms * 1e-3) / 1e9, 1),
+                "cache_gbs": round(layer_bytes(qs + sq, pbits) / (ms * 1e-3) / 1e9, 1),
             }
         next_rows["prefill"] = dict(
-            workload="prefill-side attention on the Llama layer's int4 cache (Hq 64, Hkv 8, D 128, fp16 q, "
-                     "causal): the outlier workload's 4096-row chunk at row 61440, and a 4096-token prompt",
+            workload="prefill-side attention on the Llama layer's quantised cache (Hq 64, Hkv 8, D 128, fp16 q, "
+                     "causal): the outlier workload's 4096-row chunk at row 61440 (int4 and 8-bit codes), and a "
+                     "4096-token prompt (int4)",
             roofline="mfma: algorithmic flops 4 * Hq * D * (rows each position sees), dense fp16 peak 2500 TFLOP/s",
             timing="median of 5 calls, events around each (one kernel of milliseconds)", **pf)
 

@@ -114,11 +114,12 @@ struct PrefillArgs {
     int32_t Hkv;
     int32_t Hq;
     int32_t n_rep;
-    int32_t pb;         // positions per wavefront (64 / n_rep)
+    int32_t pb;         // positions per wavefront (prefill_positions_per_block)
+    int32_t bits;       // 4 or 8
     float score_scale;  // softmax_scale * log2(e)
 };
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits);
-int prefill_positions_per_block(int n_rep);
+int prefill_positions_per_block(int n_rep, int bits);
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
 
 // Where a partial-phase launch goes: the stream and, optionally, two events

@@ -56,15 +56,26 @@ constexpr int PT = 32;  // rows per tile
 // copies it around the matrix instructions. Measured on the Llama layer's
 // 4096-position chunk at row 61440: NB = 1 30.4 ms, NB = 2 with the queries
 // in registers 26.9 ms, NB = 2 with them in LDS 25.5 ms.
-template <int PF, int NB>
+//
+// BITS = 8 (byte codes, four per word): the K and V codes enter as the exact
+// centred integers n - 128 through the byte permutes of the decode kernel
+// (k_operand8, v_pair8), the value weights are carried times WS = 2^6 (as
+// there, to keep their fp16 halves clear of the subnormal range) and the
+// value products are multiplied by VU = 1 / WS at the end.
+template <int PF, int NB, int BITS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
 void sdpa_prefill_mfma_kernel(PrefillArgs a)
 {
+    constexpr bool B8 = BITS == 8;
     constexpr int D = 128;
     constexpr int NG = 2;
-    constexpr int W = D / 8;      // words per row
-    constexpr int KM = D / 32;    // score products per 16-row block
-    constexpr int KPG = KM / NG;  // of them per scale group
+    constexpr int W = D * BITS / 32;  // words per row
+    constexpr int KW = BITS / 4;      // words per eight dimensions
+    constexpr int KM = D / 32;        // score products per 16-row block
+    constexpr int KPG = KM / NG;      // of them per scale group
+    constexpr float VC = B8 ? 128.0f : 8.0f;        // centre of the value codes
+    constexpr float WS = B8 ? 64.0f : 1.0f;         // scale of the value weights
+    constexpr float VU = B8 ? 1.0f / 64.0f : 1.0f;  // unit of the value products
     constexpr int PAIRS = PT * NG;
     static_assert(PAIRS == 64, "one (row, group) pair per lane");
 
@@ -102,45 +113,70 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
         make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
         make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
 
-    // fp32 factors per (row, group) of a tile, two-slot LDS ring:
-    // x = s_k c 2^20, y = b_k c, z = s_v, w = b_v + 8 s_v (c = softmax scale * log2 e)
+    // fp32 factors per (row, group) of a tile, two-slot LDS ring
+    // (c = softmax scale * log2 e):
+    //   x = s_k c 2^20 (int4: the subnormal scale of the K operands) or s_k c
+    //   y = b_k c, or (b_k + 128 s_k) c (the bias of centred 8-bit codes)
+    //   z = s_v WS, w = b_v + VC s_v
     __shared__ __align__(16) float4 mring[2][PAIRS];
     const Unpacker unpack = Unpacker::make();
     const float cs = a.score_scale;
-    const float cs20 = cs * 1048576.0f;  // c * 2^20 (the subnormal scale of the K operands)
-    const uint32_t m_fine = opaque_s(0x00F000F0u);
+    const float csk = B8 ? cs : cs * 1048576.0f;
+    const uint32_t m_fine = opaque_s_if<!B8>(0x00F000F0u);
+    // 8-bit operands: the magic exponent bytes and the byte selectors of
+    // k_operand8 and v_pair8
+    const uint32_t magic8 = opaque_s_if<B8>(kMagic1024x4), magic16 = opaque_s_if<B8>(0x64006400u);
+    const uint32_t sel_even = opaque_s_if<B8>(0x04020400u), sel_odd = opaque_s_if<B8>(0x04030401u);
+    const uint32_t sel_b[4] = {opaque_s_if<B8>(0x0C040C00u), opaque_s_if<B8>(0x0C050C01u),
+                               opaque_s_if<B8>(0x0C060C02u), opaque_s_if<B8>(0x0C070C03u)};
 
-    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D / 2 < 2^31)
-    uint32_t kbuf[PF][2][KM];
-    uint32_t vbuf[PF][8];
+    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D * BITS / 8 < 2^31)
+    uint32_t kbuf[PF][2][KM][KW];
+    uint32_t vbuf[PF][8 * KW];
     uint32_t mbuf[PF][4];
-    auto load_tile = [&](int ti, uint32_t (&kt)[2][KM], uint32_t (&vt)[8], uint32_t (&mt)[4]) {
+    auto load_tile = [&](int ti, uint32_t (&kt)[2][KM][KW], uint32_t (&vt)[8 * KW], uint32_t (&mt)[4]) {
         const bool in = ti < ntile;
         const uint32_t moff = in ? (uint32_t)((PT * ti) * NG + lane) * 2u : kNoRows;
 #pragma unroll
         for (int arr = 0; arr < 4; ++arr)
             mt[arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
         const uint32_t base = in ? (uint32_t)(PT * ti) * (uint32_t)(W * 4) : kNoRows;
-        // K: row 16 blk + col, words 4 uu + q4 (dimensions 32 uu + 8 q4 .. + 7)
+        // K: row 16 blk + col, dimensions 32 uu + 8 q4 .. + 7 (the KW words
+        // from word KW (4 uu + q4))
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + q4) * 4);
+            const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + KW * q4) * 4);
 #pragma unroll
-            for (int uu = 0; uu < KM; ++uu)
-                kt[blk][uu] = __builtin_amdgcn_raw_buffer_load_b32(kq, off + 16 * uu, 0, 0);
+            for (int uu = 0; uu < KM; ++uu) {
+                if constexpr (B8) {
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(kq, off + 16 * KW * uu, 0, 0);
+                    kt[blk][uu][0] = x[0];
+                    kt[blk][uu][1] = x[1];
+                } else {
+                    kt[blk][uu][0] = __builtin_amdgcn_raw_buffer_load_b32(kq, off + 16 * uu, 0, 0);
+                }
+            }
         }
-        // V: word col of rows 16 (j >> 2) + 4 q4 + (j & 3)
-        const uint32_t voff = base + (uint32_t)((4 * q4 * W + col) * 4);
+        // V: dimensions 8 col .. 8 col + 7 (KW words) of rows 16 (j >> 2) + 4 q4 + (j & 3)
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + KW * col) * 4);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t o = voff + ((16 * (j >> 2) + (j & 3)) * W) * 4;
+            if constexpr (B8) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
+                vt[2 * j] = x[0];
+                vt[2 * j + 1] = x[1];
+            } else {
+                vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, o, 0, 0);
+            }
+        }
     };
     auto stage_meta = [&](int slot, const uint32_t (&mt)[4]) {
         const float ks = h_val((uint16_t)mt[0]);
         const float kb = h_val((uint16_t)mt[1]);
         const float vs = h_val((uint16_t)mt[2]);
         const float vb = h_val((uint16_t)mt[3]);
-        mring[slot][lane] = make_float4(ks * cs20, kb * cs, vs, fmaf(8.0f, vs, vb));
+        mring[slot][lane] = make_float4(ks * csk, (B8 ? fmaf(128.0f, ks, kb) : kb) * cs, vs * WS, fmaf(VC, vs, vb));
         asm volatile("" ::: "memory");
     };
     // factors (x, y) or (z, w) of row r, group g
@@ -158,8 +194,8 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     __builtin_amdgcn_sched_barrier(0);
 
     // each block's column query as B operands: score product uu holds
-    // dimensions 32 uu + 8 q4 + kPerm[j]; qsum: group sums of exactly what
-    // the matrix core sees
+    // dimensions 32 uu + 8 q4 + kPerm[j] (kPerm8 for 8-bit codes); qsum:
+    // group sums of exactly what the matrix core sees
     half8 qop[NB][KM];
     float qsum[NB][NG];
     // NB > 1: the operands wait in LDS and are read back tile by tile, which
@@ -176,7 +212,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const half8 x = *reinterpret_cast<const half8 *>(qp + 32 * uu + 8 * q4);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const _Float16 h = con[nb] ? x[kPerm[j]] : (_Float16)0.0f;
+                const _Float16 h = con[nb] ? x[B8 ? kPerm8[j] : kPerm[j]] : (_Float16)0.0f;
                 qop[nb][uu][j] = h;
                 gs[uu / KPG] += (float)h;
             }
@@ -234,7 +270,12 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                         sacc[nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int k = 0; k < KPG; ++k) {
-                        const half8 ka = k_operand_sub(kbuf[u][blk][g * KPG + k], m_fine);
+                        const uint32_t(&kw)[KW] = kbuf[u][blk][g * KPG + k];
+                        half8 ka;
+                        if constexpr (B8)
+                            ka = k_operand8(kw[0], kw[KW - 1], magic8, sel_even, sel_odd);
+                        else
+                            ka = k_operand_sub(kw[0], m_fine);
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb) {
                             const half8 qb = NB > 1 ? q_lds[nb][g * KPG + k][lane] : qop[nb][g * KPG + k];
@@ -308,16 +349,27 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                 l_run[nb] += lsum;
             }
 
-            // ---- value products, group by group; the lane's word gives
-            // dimensions 0..3 in its own group's products and lends 4..7 to
-            // lane l ^ 8, and every unpacked operand serves all NB blocks
-            uint32_t bx[NG][4];
+            // ---- value products, group by group; the lane's eight dimensions
+            // give 0..3 in its own group's products and lend 4..7 to lane
+            // l ^ 8, and every unpacked operand serves all NB blocks. int4:
+            // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair;
+            // 8-bit: the same exchange on whole words (row r's two words hold
+            // dimensions 0..3 and 4..7)
+            uint32_t bx[NG][4 * KW];
+            if constexpr (B8) {
 #pragma unroll
-            for (int jp = 0; jp < 4; ++jp) {
-                const uint32_t xw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x05040100u);
-                const uint32_t yw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x07060302u);
-                bx[0][jp] = take_half_row<0xC>(xw, yw);
-                bx[1][jp] = take_half_row<0x3>(xw, yw);
+                for (int r = 0; r < 8; ++r) {
+                    bx[0][r] = take_half_row<0xC>(vbuf[u][2 * r], vbuf[u][2 * r + 1]);
+                    bx[1][r] = take_half_row<0x3>(vbuf[u][2 * r], vbuf[u][2 * r + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    const uint32_t xw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x05040100u);
+                    const uint32_t yw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x07060302u);
+                    bx[0][jp] = take_half_row<0xC>(xw, yw);
+                    bx[1][jp] = take_half_row<0x3>(xw, yw);
+                }
             }
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
@@ -344,8 +396,12 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                 for (int mm = 0; mm < 4; ++mm) {
                     half2v e[4];
 #pragma unroll
-                    for (int jp = 0; jp < 4; ++jp)
-                        e[jp] = unpack.one(bx[g][jp], mm);
+                    for (int jp = 0; jp < 4; ++jp) {
+                        if constexpr (B8)
+                            e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm], magic16);
+                        else
+                            e[jp] = unpack.one(bx[g][jp], mm);
+                    }
                     const half8 bv = cat8(e[0], e[1], e[2], e[3]);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
@@ -388,7 +444,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                 for (int mm = 0; mm < 4; ++mm) {
                     const float hi = acc[nb][4 * g + mm][i];
                     const float lo = accl[nb][4 * g + mm][i];
-                    o[mm] = (fmaf(lo, 1.0f / kLoScale, hi) + bias) * inv_l;
+                    o[mm] = (fmaf(lo, VU / kLoScale, hi * VU) + bias) * inv_l;
                 }
                 if (on) {
                     float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
@@ -403,21 +459,29 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
 {
-    return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 && q_dtype == KVQ_F16 && bits == 4;
+    return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 && q_dtype == KVQ_F16 && (bits == 4 || bits == 8);
 }
 
-// query columns per wavefront: kPrefillNB blocks of 16
+// blocks of 16 query columns per wavefront, both code widths (8-bit codes
+// with one block: 35.8 ms against 28.8 ms on the 4096-position chunk)
 constexpr int kPrefillNB = 2;
 
-int prefill_positions_per_block(int n_rep) { return 16 * kPrefillNB / n_rep; }
+int prefill_positions_per_block(int n_rep, int bits)
+{
+    (void)bits;
+    return 16 * kPrefillNB / n_rep;
+}
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
 {
-    if (a.pb < 1 || a.pb * a.n_rep > 16 * kPrefillNB)
+    if (a.pb < 1 || a.pb * a.n_rep > 16 * kPrefillNB || (a.bits != 4 && a.bits != 8))
         return hipErrorInvalidValue;
     const int64_t blocks = (a.sq + a.pb - 1) / a.pb;
     dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
-    hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB>), grid, dim3(64), 0, s, a);
+    if (a.bits == 8)
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 8>), grid, dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 4>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

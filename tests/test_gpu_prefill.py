@@ -1,6 +1,6 @@
-"""GPU parity of prefill-side attention over the int4 cache
-(kvq_sdpa_int4_prefill: Sq > 1 query positions, causal, against the float64
-oracle's sdpa_prefill on the same packed cache)."""
+"""GPU parity of prefill-side attention over the quantised cache, int4 and
+8-bit codes (kvq_sdpa_int4_prefill: Sq > 1 query positions, causal, against
+the float64 oracle's sdpa_prefill on the same packed cache)."""
 
 import numpy as np
 import pytest
@@ -16,12 +16,12 @@ pytestmark = pytest.mark.gpu
 REL_L2 = 1e-4  # the matrix-core gate of the decode tests
 
 
-def _case(B, hq, hkv, q_start, sq, seed, alpha=None, cap=None):
+def _case(B, hq, hkv, q_start, sq, seed, alpha=None, cap=None, bits=4):
     S = q_start + sq
     q = kvq_synth.normal((B, hq, sq, 128), [90, seed, 0]).astype(np.float16)
     k = kvq_synth.normal((B, hkv, S, 128), [90, seed, 1]).astype(np.float16)
     v = kvq_synth.normal((B, hkv, S, 128), [90, seed, 2]).astype(np.float16)
-    oc = oracle.Cache(B, hkv, 128, cap or S, 64)
+    oc = oracle.Cache(B, hkv, 128, cap or S, 64, bits=bits)
     oc.append(k, v, 0)
     return q, oc, (1 / np.sqrt(128) if alpha is None else alpha)
 
@@ -101,12 +101,58 @@ def test_outlier_chunked_prefill_sampled():
         check_attention(got[:, :, i], ref, REL_L2, label="prefill outlier pos %d" % i)
 
 
-@pytest.mark.parametrize("what", ["d256", "g32", "int8", "fp32q"])
+@pytest.mark.parametrize("q_start,sq", [(0, 1), (0, 33), (5, 64), (511, 100), (4000, 96)])
+def test_int8_gqa4(q_start, sq):
+    """8-bit codes: the same positions and prefixes as the int4 cases."""
+    note("prefill int8 gqa4 q_start=%d sq=%d" % (q_start, sq))
+    q, oc, alpha = _case(1, 8, 2, q_start, sq, seed=7000 + q_start * 1000 + sq, bits=8)
+    got = _run(oc, q_start, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, q_start, q, alpha), REL_L2, label="prefill int8")
+
+
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (16, 16), (16, 1), (6, 2)])
+def test_int8_head_layouts(hq, hkv):
+    note("prefill int8 heads hq=%d hkv=%d" % (hq, hkv))
+    q, oc, alpha = _case(1, hq, hkv, 300, 45, seed=8000 + hq * 100 + hkv, bits=8)
+    got = _run(oc, 300, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, 300, q, alpha), REL_L2, label="prefill int8 heads")
+
+
+def test_int8_unscaled_scores():
+    note("prefill int8 alpha 1")
+    q, oc, alpha = _case(1, 8, 2, 700, 20, seed=8011, alpha=1.0, bits=8)
+    got = _run(oc, 700, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, 700, q, alpha), 2e-4, atol=1e-3, rtol=1e-3, label="prefill int8 a1")
+
+
+def test_int8_outlier_chunked_prefill_sampled():
+    """The outlier workload's 4096-row append into an 8-bit cache (GPU append),
+    then prefill attention for those positions, sampled on all heads."""
+    note("prefill int8 outlier 4096 at 61440")
+    total, prefix = 65536, 61440
+    _, k, v, _ = kvq_synth.outlier_kv(total)
+    q = kvq_synth.normal((1, 64, total - prefix, 128), [91, 1]).astype(np.float16)
+    alpha = 1 / np.sqrt(128)
+    oc = oracle.Cache(1, 8, 128, total, 64, bits=8)
+    oc.append(k[:, :, :prefix], v[:, :, :prefix], 0)
+    gc = gpu_cache_from_oracle(oc)
+    kvq.quantize_kv_append(gc, prefix, to_dev(np.ascontiguousarray(k[:, :, prefix:])),
+                           to_dev(np.ascontiguousarray(v[:, :, prefix:])))
+    out = kvq.sdpa_int4_prefill(gc, prefix, to_dev(q), alpha)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    oc.append(k[:, :, prefix:], v[:, :, prefix:], prefix)
+    for i in (0, 1, 2047, 4095):
+        ref = oracle.sdpa(oc, prefix + i + 1, np.ascontiguousarray(q[:, :, i]), alpha)
+        check_attention(got[:, :, i], ref, REL_L2, label="prefill int8 outlier pos %d" % i)
+
+
+@pytest.mark.parametrize("what", ["d256", "g32", "fp32q"])
 def test_unsupported_shapes_refused(what):
     note("prefill refuses %s" % what)
     D = 256 if what == "d256" else 128
     G = 32 if what == "g32" else 64
-    bits = 8 if what == "int8" else 4
+    bits = 4
     gc = kvq.QuantKVCache(1, 2, D, 64, G, device="cuda", bits=bits)
     q = torch.zeros((1, 8, 4, D), dtype=torch.float32 if what == "fp32q" else torch.float16, device="cuda")
     with pytest.raises(kvq.KvqError) as e:
