@@ -148,8 +148,37 @@ def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"
             kvq.hadamard_rotate(L["out"], out=L["out"], stream=stream)
 
 
+def graph_step_ms(kvq, torch, pool, skv, chunk, kernel, step, reps=5):
+    """Per-step time with the host out of the loop: one pass over the pool
+    (every layer once, so the cache still streams from HBM) captured in a HIP
+    graph, replayed `reps` times with events around each replay; median."""
+    n = len(pool)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_steps(kvq, torch, pool, skv, chunk, kernel, n, step=step)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_steps(kvq, torch, pool, skv, chunk, kernel, n, step=step)
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / n)
+    del g
+    return sorted(per)[len(per) // 2]
+
+
 def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step="fused", bits=4, hkv=HKV,
-                repeats=0):
+                repeats=0, graph=False):
     pool = make_pool(kvq, torch, skv, pool_bytes, chunk, bits=bits, hkv=hkv)
     run_steps(kvq, torch, pool, skv, chunk, kernel, warmup, step=step)
     torch.cuda.synchronize()
@@ -173,6 +202,8 @@ def time_config(kvq, torch, skv, chunk, kernel, steps, warmup, pool_bytes, step=
     res = dict(skv=skv, ms_per_step=ms_per_step, partial_ms_avg=sum(kern_ms) / len(kern_ms),  # nan: not timed
                partial_ms_p10=kern_ms[len(kern_ms) // 10], partial_ms_p90=kern_ms[(9 * len(kern_ms)) // 10],
                pool_layers=len(pool), pool_mb=len(pool) * layer_bytes(skv, bits, hkv) / 1e6)
+    if graph:
+        res.update(graph_ms_per_step=graph_step_ms(kvq, torch, pool, skv, chunk, kernel, step))
     if repeats:
         # the step time's spread: `repeats` runs of steps // repeats steps,
         # events around each run, per-step time of each run
@@ -421,7 +452,7 @@ def main():
     sweep = []
     for s in [int(x) for x in args.sweep.split(",") if x.strip()]:
         r, _ = time_config(kvq, torch, s, args.chunk, kernel, max(20, args.steps // 2), args.warmup, pool_bytes,
-                           step=args.step, bits=bits)
+                           step=args.step, bits=bits, graph=True)
         r["us_per_layer"] = r["ms_per_step"] * 1e3
         r["gbs"] = (layer_bytes(s, bits) + append_bytes(bits)) / (r["ms_per_step"] * 1e-3) / 1e9
         r["partial_gbs"] = layer_bytes(s, bits) / (r["partial_ms_avg"] * 1e-3) / 1e9
@@ -593,8 +624,11 @@ def main():
         },
         "cpu_baseline": cpu,
         "sweep": [{"skv": r["skv"], "us_per_layer": round(r["us_per_layer"], 3), "gbs": round(r["gbs"], 2),
+                   "us_per_layer_graph": round(r["graph_ms_per_step"] * 1e3, 3),
                    "partial_us": round(r["partial_ms_avg"] * 1e3, 3), "partial_gbs": round(r["partial_gbs"], 2)}
                   for r in sweep],
+        "sweep_note": ("us_per_layer: steps issued one by one from Python; us_per_layer_graph: one pass over "
+                       "the same pool captured in a HIP graph and replayed (the host out of the loop)"),
         "full_depth": depth,
         "next_rows": next_rows,
         "context": "pages' Apple-Silicon fused-kernel latency on this shape: 1.6/2.7/5.7/9.9 ms at 1K/16K/64K/128K",
