@@ -23,12 +23,12 @@ pytestmark = pytest.mark.gpu
 REL_L2 = 1e-4  # the matrix-core gate of test_gpu_sdpa.py
 
 
-def _rot_append_and_check(k, v, length, cap, G=64):
+def _rot_append_and_check(k, v, length, cap, G=64, bits=4):
     B, Hkv, n, D = k.shape
-    gc = canary_cache(B, Hkv, D, cap, G)
+    gc = canary_cache(B, Hkv, D, cap, G, bits=bits)
     kvq.quantize_kv_append_rotated(gc, length, to_dev(k), to_dev(v))
     torch.cuda.synchronize()
-    oc = oracle.Cache(B, Hkv, D, cap, G)
+    oc = oracle.Cache(B, Hkv, D, cap, G, bits=bits)
     oc.append_rotated(k, v, length)
     rows = slice(length, length + n)
     assert_cache_equal(gc, oc, rows)
@@ -158,12 +158,12 @@ def test_rotated_attention_gemma():
 
 # ------------------------------------------------------- rotated decode step
 
-def _rot_step_case(q, k, v, alpha, length, cap, kernel, q_dev=None, out=None):
+def _rot_step_case(q, k, v, alpha, length, cap, kernel, q_dev=None, out=None, bits=4):
     """Rows [0, length) rotated into the cache by the oracle; the step rotates
     and appends row `length` and attends over rows 0..length. Returns the GPU
     output and the oracle cache after the same append."""
     B, Hkv, _, D = k.shape
-    oc = oracle.Cache(B, Hkv, D, cap, 64)
+    oc = oracle.Cache(B, Hkv, D, cap, 64, bits=bits)
     if length:
         oc.append_rotated(np.ascontiguousarray(k[:, :, :length]), np.ascontiguousarray(v[:, :, :length]), 0)
     kn = np.ascontiguousarray(k[:, :, length:length + 1])
@@ -192,6 +192,28 @@ def test_rotated_decode_step_llama(kernel, length):
     got, oc = _rot_step_case(q, k, v, alpha, length, 4096 + 8, kernel)
     check_attention(got, oracle.sdpa_rotated(oc, length + 1, q, alpha), GATES.get(kernel, 1e-4),
                     label="rotated step")
+
+
+@pytest.mark.parametrize("B,Hkv,D,G,n,length", [(1, 8, 128, 64, 300, 5), (1, 2, 256, 64, 129, 3),
+                                                 (1, 4, 128, 128, 64, 1)])
+def test_rotated_append_int8_bit_exact(B, Hkv, D, G, n, length):
+    """The rotated append into an 8-bit cache (bytes instead of nibbles)."""
+    note("rotated append int8 B%d Hkv%d D%d G%d n%d len%d" % (B, Hkv, D, G, n, length))
+    k = kvq_synth.to_f16(kvq_synth.normal((B, Hkv, n, D), [111, B, Hkv, D, G, n, 0]))
+    v = kvq_synth.to_f16(kvq_synth.normal((B, Hkv, n, D), [111, B, Hkv, D, G, n, 1]))
+    _rot_append_and_check(k, v, length, length + n + 3, G, bits=8)
+
+
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_VALU])
+@pytest.mark.parametrize("length", [0, 700, 4095])
+def test_rotated_decode_step_int8(kernel, length):
+    """The rotated step on an 8-bit cache: the fused one-wavefront path with
+    byte operands and the vector-ALU fallback, against the oracle."""
+    note("rotated step int8 len=%d kernel=%d" % (length, kernel))
+    q, k, v, alpha = kvq_synth.llama_layer(length + 1)
+    got, oc = _rot_step_case(q, k, v, alpha, length, 4096 + 8, kernel, bits=8)
+    check_attention(got, oracle.sdpa_rotated(oc, length + 1, q, alpha), GATES.get(kernel, 1e-4),
+                    label="rotated step int8")
 
 
 def test_rotated_decode_step_matches_separate_calls():
