@@ -237,11 +237,14 @@ int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtyp
  * rows [q_start, q_start + sq) (append them first), with query i attending
  * to rows [0, q_start + i] (causal):
  *   out[b][h][i][:] = sum_{t <= q_start + i} softmax_t(softmax_scale * q_hi . k^_t) v^_t
- *  q:    [B][Hq][sq][D] fp16, 16-byte aligned; Hq a multiple of Hkv.
+ *  q:    [B][Hq][sq][D], q_dtype KVQ_F16 or KVQ_F32 (fp32: split into fp16
+ *        hi and lo halves, e.g. a query rotated for a Hadamard-rotated
+ *        cache), 16-byte aligned; Hq a multiple of Hkv.
  *  out:  [B][Hq][sq][D] fp32, normalised, 16-byte aligned.
  * One launch, no workspace. Supported: D = 128, G = 64, 4- or 8-bit codes,
- * fp16 queries, Hq / Hkv <= 16 (KVQ_E_UNSUPPORTED otherwise). q_start + sq
- * beyond the capacity returns KVQ_E_CAPACITY.
+ * Hq / Hkv <= 16 (KVQ_E_UNSUPPORTED otherwise). q_start + sq beyond the
+ * capacity returns KVQ_E_CAPACITY. On a Hadamard-rotated cache: rotate q with
+ * kvq_hadamard_rotate (fp32 out), call this with KVQ_F32, rotate out back.
  */
 int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, const void *q, int q_dtype,
                           int32_t Hq, float softmax_scale, float *out, void *stream);

@@ -314,7 +314,7 @@ def decode_step(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: to
 
 def sdpa_int4_prefill(cache: QuantKVCache, q_start: int, q: torch.Tensor, softmax_scale: float,
                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """kvq_sdpa_int4_prefill: q [B][Hq][Sq][D] fp16 contiguous, the queries of
+    """kvq_sdpa_int4_prefill: q [B][Hq][Sq][D] fp16 or fp32 contiguous, the queries of
     positions q_start .. q_start + Sq - 1 (their K/V rows already appended);
     returns out [B][Hq][Sq][D] fp32."""
     assert q.is_contiguous() and q.dim() == 4

@@ -385,6 +385,7 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
     a.n_rep = n_rep;
     a.pb = pb;
     a.bits = cache_bits(cache);
+    a.q_f32 = q_dtype == KVQ_F32;
     a.score_scale = softmax_scale * kLog2e;
     return launch_status(launch_prefill(a, cache->batch, (hipStream_t)stream));
 }

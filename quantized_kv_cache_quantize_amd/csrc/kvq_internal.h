@@ -116,6 +116,7 @@ struct PrefillArgs {
     int32_t n_rep;
     int32_t pb;         // positions per wavefront (prefill_positions_per_block)
     int32_t bits;       // 4 or 8
+    int32_t q_f32;      // queries fp32 (else fp16)
     float score_scale;  // softmax_scale * log2(e)
 };
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits);

@@ -62,7 +62,11 @@ constexpr int PT = 32;  // rows per tile
 // (k_operand8, v_pair8), the value weights are carried times WS = 2^6 (as
 // there, to keep their fp16 halves clear of the subnormal range) and the
 // value products are multiplied by VU = 1 / WS at the end.
-template <int PF, int NB, int BITS>
+//
+// Q32 (fp32 queries, e.g. a query rotated for a Hadamard-rotated cache): the
+// query is split into fp16 hi and lo halves, hi + lo exact to 22 bits, each
+// the B operand of its own score product (as in the decode kernel).
+template <int PF, int NB, int BITS, bool Q32>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
 void sdpa_prefill_mfma_kernel(PrefillArgs a)
 {
@@ -196,25 +200,45 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     // each block's column query as B operands: score product uu holds
     // dimensions 32 uu + 8 q4 + kPerm[j] (kPerm8 for 8-bit codes); qsum:
     // group sums of exactly what the matrix core sees
-    half8 qop[NB][KM];
+    constexpr int QH = Q32 ? 2 : 1;  // query halves: hi (and lo)
+    half8 qop[NB][QH][KM];
     float qsum[NB][NG];
     // NB > 1: the operands wait in LDS and are read back tile by tile, which
     // keeps the wavefront within 256 registers (see the kernel comment)
-    __shared__ __align__(16) half8 q_lds[NB > 1 ? NB : 1][KM][64];
+    __shared__ __align__(16) half8 q_lds[NB > 1 ? NB : 1][QH][KM][64];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con[nb] ? chead[nb] : 0)) * a.sq + p0 +
                               (con[nb] ? cpos[nb] : 0)) * D;
-        const _Float16 *qp = reinterpret_cast<const _Float16 *>(a.q) + qrow;
         float gs[NG] = {};
 #pragma unroll
         for (int uu = 0; uu < KM; ++uu) {
-            const half8 x = *reinterpret_cast<const half8 *>(qp + 32 * uu + 8 * q4);
+            float x[8];
+            if constexpr (Q32) {
+                const float *qp = reinterpret_cast<const float *>(a.q) + qrow + 32 * uu + 8 * q4;
+                const float4 x0 = *reinterpret_cast<const float4 *>(qp);
+                const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
+                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+                x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            } else {
+                const half8 h8 = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow +
+                                                                  32 * uu + 8 * q4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[j] = (float)h8[j];
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const _Float16 h = con[nb] ? x[B8 ? kPerm8[j] : kPerm[j]] : (_Float16)0.0f;
-                qop[nb][uu][j] = h;
-                gs[uu / KPG] += (float)h;
+                const float xv = con[nb] ? x[B8 ? kPerm8[j] : kPerm[j]] : 0.0f;
+                const _Float16 hi = (_Float16)xv;
+                qop[nb][0][uu][j] = hi;
+                if constexpr (Q32) {
+                    const _Float16 lo = (_Float16)(xv - (float)hi);
+                    qop[nb][QH - 1][uu][j] = lo;
+                    gs[uu / KPG] += (float)hi + (float)lo;
+                } else {
+                    gs[uu / KPG] += (float)hi;
+                }
             }
         }
 #pragma unroll
@@ -222,8 +246,10 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             qsum[nb][g] = xrow_sum(gs[g]);
         if constexpr (NB > 1) {
 #pragma unroll
-            for (int uu = 0; uu < KM; ++uu)
-                q_lds[nb][uu][lane] = qop[nb][uu];
+            for (int hl = 0; hl < QH; ++hl)
+#pragma unroll
+                for (int uu = 0; uu < KM; ++uu)
+                    q_lds[nb][hl][uu][lane] = qop[nb][hl][uu];
         }
     }
     stage_meta(0, mbuf[0]);
@@ -277,10 +303,12 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                         else
                             ka = k_operand_sub(kw[0], m_fine);
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            const half8 qb = NB > 1 ? q_lds[nb][g * KPG + k][lane] : qop[nb][g * KPG + k];
-                            sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, sacc[nb], 0, 0, 0);
-                        }
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int hl = 0; hl < QH; ++hl) {
+                                const half8 qb = NB > 1 ? q_lds[nb][hl][g * KPG + k][lane] : qop[nb][hl][g * KPG + k];
+                                sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, sacc[nb], 0, 0, 0);
+                            }
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -459,7 +487,8 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
 {
-    return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 && q_dtype == KVQ_F16 && (bits == 4 || bits == 8);
+    return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 && (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) &&
+           (bits == 4 || bits == 8);
 }
 
 // blocks of 16 query columns per wavefront, both code widths (8-bit codes
@@ -478,10 +507,14 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
         return hipErrorInvalidValue;
     const int64_t blocks = (a.sq + a.pb - 1) / a.pb;
     dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
-    if (a.bits == 8)
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 8>), grid, dim3(64), 0, s, a);
+    if (a.bits == 8 && a.q_f32)
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 8, true>), grid, dim3(64), 0, s, a);
+    else if (a.bits == 8)
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 8, false>), grid, dim3(64), 0, s, a);
+    else if (a.q_f32)
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 4, true>), grid, dim3(64), 0, s, a);
     else
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 4>), grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 4, false>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

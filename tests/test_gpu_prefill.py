@@ -147,14 +147,52 @@ def test_int8_outlier_chunked_prefill_sampled():
         check_attention(got[:, :, i], ref, REL_L2, label="prefill int8 outlier pos %d" % i)
 
 
-@pytest.mark.parametrize("what", ["d256", "g32", "fp32q"])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("q_start,sq", [(0, 33), (511, 100)])
+def test_fp32_queries(bits, q_start, sq):
+    """fp32 queries (hi + lo fp16 halves) against the oracle on the same fp32 values."""
+    note("prefill fp32 q bits=%d q_start=%d sq=%d" % (bits, q_start, sq))
+    q16, oc, alpha = _case(1, 8, 2, q_start, sq, seed=9000 + bits * 100 + sq, bits=bits)
+    q = (q16.astype(np.float32) * np.float32(1.0 + 2.0 ** -13)).astype(np.float32)  # not fp16-exact
+    gc = gpu_cache_from_oracle(oc)
+    got = kvq.sdpa_int4_prefill(gc, q_start, to_dev(q), alpha)
+    torch.cuda.synchronize()
+    check_attention(got.cpu().numpy(), oracle.sdpa_prefill(oc, q_start, q, alpha), REL_L2, label="prefill fp32 q")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_rotated_cache_prefill(bits):
+    """Prefill over a Hadamard-rotated cache from the entry points: rotate q
+    (fp32), prefill with fp32 queries, rotate the output back; against the
+    oracle's rotated attention, position by position."""
+    note("prefill on a rotated cache bits=%d" % bits)
+    q_start, sq, hq, hkv = 700, 24, 8, 2
+    S = q_start + sq
+    q = kvq_synth.normal((1, hq, sq, 128), [92, bits, 0]).astype(np.float16)
+    k = kvq_synth.normal((1, hkv, S, 128), [92, bits, 1]).astype(np.float16)
+    v = kvq_synth.normal((1, hkv, S, 128), [92, bits, 2]).astype(np.float16)
+    alpha = 1 / np.sqrt(128)
+    oc = oracle.Cache(1, hkv, 128, S, 64, bits=bits)
+    oc.append_rotated(k, v, 0)
+    gc = gpu_cache_from_oracle(oc)
+    qr = kvq.hadamard_rotate(to_dev(q))
+    out = kvq.sdpa_int4_prefill(gc, q_start, qr, alpha)
+    kvq.hadamard_rotate(out, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i in range(sq):
+        ref = oracle.sdpa_rotated(oc, q_start + i + 1, np.ascontiguousarray(q[:, :, i]), alpha)
+        check_attention(got[:, :, i], ref, REL_L2, label="rotated prefill pos %d" % i)
+
+
+@pytest.mark.parametrize("what", ["d256", "g32"])
 def test_unsupported_shapes_refused(what):
     note("prefill refuses %s" % what)
     D = 256 if what == "d256" else 128
     G = 32 if what == "g32" else 64
     bits = 4
     gc = kvq.QuantKVCache(1, 2, D, 64, G, device="cuda", bits=bits)
-    q = torch.zeros((1, 8, 4, D), dtype=torch.float32 if what == "fp32q" else torch.float16, device="cuda")
+    q = torch.zeros((1, 8, 4, D), dtype=torch.float16, device="cuda")
     with pytest.raises(kvq.KvqError) as e:
         kvq.sdpa_int4_prefill(gc, 10, q, 0.1)
     assert e.value.status == -7
