@@ -365,7 +365,7 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
     const int n_rep = Hq / cache->kv_heads;
     if (!prefill_supports(cache->head_dim, cache->group, n_rep, q_dtype, cache_bits(cache)))
         return KVQ_E_UNSUPPORTED;
-    const int pb = prefill_positions_per_block(n_rep, cache_bits(cache));
+    const int pb = prefill_positions_per_block(n_rep, cache->head_dim);
     if ((int64_t)cache->batch * Hq * sq > ((int64_t)1 << 40) / cache->head_dim || (sq + pb - 1) / pb > 0x7fffffff)
         return KVQ_E_SHAPE;
     PrefillArgs a;
@@ -386,6 +386,7 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
     a.pb = pb;
     a.bits = cache_bits(cache);
     a.q_f32 = q_dtype == KVQ_F32;
+    a.D = cache->head_dim;
     a.score_scale = softmax_scale * kLog2e;
     return launch_status(launch_prefill(a, cache->batch, (hipStream_t)stream));
 }

@@ -117,10 +117,11 @@ struct PrefillArgs {
     int32_t pb;         // positions per wavefront (prefill_positions_per_block)
     int32_t bits;       // 4 or 8
     int32_t q_f32;      // queries fp32 (else fp16)
+    int32_t D;          // head dimension: 128 or 256
     float score_scale;  // softmax_scale * log2(e)
 };
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits);
-int prefill_positions_per_block(int n_rep, int bits);
+int prefill_positions_per_block(int n_rep, int D);
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
 
 // Where a partial-phase launch goes: the stream and, optionally, two events

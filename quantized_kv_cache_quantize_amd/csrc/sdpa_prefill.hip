@@ -66,13 +66,18 @@ constexpr int PT = 32;  // rows per tile
 // Q32 (fp32 queries, e.g. a query rotated for a Hadamard-rotated cache): the
 // query is split into fp16 hi and lo halves, hi + lo exact to 22 bits, each
 // the B operand of its own score product (as in the decode kernel).
-template <int PF, int NB, int BITS, bool Q32>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
+//
+// D = 256 (four scale groups): the value words of a row come in VS = D / 128
+// sets of 16 words, each set two scale groups handled as the D = 128 layout
+// handles its two; NB = 1 there (the accumulators of one block already take
+// what two blocks take at D = 128).
+template <int PF, int NB, int BITS, bool Q32, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 1 && D == 128 ? 2 : 1)))
 void sdpa_prefill_mfma_kernel(PrefillArgs a)
 {
     constexpr bool B8 = BITS == 8;
-    constexpr int D = 128;
-    constexpr int NG = 2;
+    constexpr int NG = D / 64;   // scale groups of 64
+    constexpr int VS = D / 128;  // sets of 16 value words (two groups each)
     constexpr int W = D * BITS / 32;  // words per row
     constexpr int KW = BITS / 4;      // words per eight dimensions
     constexpr int KM = D / 32;        // score products per 16-row block
@@ -81,7 +86,9 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     constexpr float WS = B8 ? 64.0f : 1.0f;         // scale of the value weights
     constexpr float VU = B8 ? 1.0f / 64.0f : 1.0f;  // unit of the value products
     constexpr int PAIRS = PT * NG;
-    static_assert(PAIRS == 64, "one (row, group) pair per lane");
+    constexpr int MP = PAIRS / 64;  // (row, group) pairs per lane
+    static_assert(PAIRS % 64 == 0, "whole pairs per lane");
+    constexpr bool QLDS = NB > 1 || D > 128;  // query operands in LDS
 
     const int lane = threadIdx.x;
     const int q4 = lane >> 4;
@@ -136,14 +143,17 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 
     constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D * BITS / 8 < 2^31)
     uint32_t kbuf[PF][2][KM][KW];
-    uint32_t vbuf[PF][8 * KW];
-    uint32_t mbuf[PF][4];
-    auto load_tile = [&](int ti, uint32_t (&kt)[2][KM][KW], uint32_t (&vt)[8 * KW], uint32_t (&mt)[4]) {
+    uint32_t vbuf[PF][VS][8 * KW];
+    uint32_t mbuf[PF][MP][4];
+    auto load_tile = [&](int ti, uint32_t (&kt)[2][KM][KW], uint32_t (&vt)[VS][8 * KW], uint32_t (&mt)[MP][4]) {
         const bool in = ti < ntile;
-        const uint32_t moff = in ? (uint32_t)((PT * ti) * NG + lane) * 2u : kNoRows;
 #pragma unroll
-        for (int arr = 0; arr < 4; ++arr)
-            mt[arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
+        for (int pp = 0; pp < MP; ++pp) {
+            const uint32_t moff = in ? (uint32_t)((PT * ti) * NG + lane + 64 * pp) * 2u : kNoRows;
+#pragma unroll
+            for (int arr = 0; arr < 4; ++arr)
+                mt[pp][arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
+        }
         const uint32_t base = in ? (uint32_t)(PT * ti) * (uint32_t)(W * 4) : kNoRows;
         // K: row 16 blk + col, dimensions 32 uu + 8 q4 .. + 7 (the KW words
         // from word KW (4 uu + q4))
@@ -161,26 +171,33 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                 }
             }
         }
-        // V: dimensions 8 col .. 8 col + 7 (KW words) of rows 16 (j >> 2) + 4 q4 + (j & 3)
-        const uint32_t voff = base + (uint32_t)((4 * q4 * W + KW * col) * 4);
+        // V: dimensions 128 s2 + 8 col .. + 7 (KW words) of rows 16 (j >> 2) + 4 q4 + (j & 3)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t o = voff + ((16 * (j >> 2) + (j & 3)) * W) * 4;
-            if constexpr (B8) {
-                const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
-                vt[2 * j] = x[0];
-                vt[2 * j + 1] = x[1];
-            } else {
-                vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, o, 0, 0);
+        for (int s2 = 0; s2 < VS; ++s2) {
+            const uint32_t voff = base + (uint32_t)((4 * q4 * W + KW * (16 * s2 + col)) * 4);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t o = voff + ((16 * (j >> 2) + (j & 3)) * W) * 4;
+                if constexpr (B8) {
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
+                    vt[s2][2 * j] = x[0];
+                    vt[s2][2 * j + 1] = x[1];
+                } else {
+                    vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, o, 0, 0);
+                }
             }
         }
     };
-    auto stage_meta = [&](int slot, const uint32_t (&mt)[4]) {
-        const float ks = h_val((uint16_t)mt[0]);
-        const float kb = h_val((uint16_t)mt[1]);
-        const float vs = h_val((uint16_t)mt[2]);
-        const float vb = h_val((uint16_t)mt[3]);
-        mring[slot][lane] = make_float4(ks * csk, (B8 ? fmaf(128.0f, ks, kb) : kb) * cs, vs * WS, fmaf(VC, vs, vb));
+    auto stage_meta = [&](int slot, const uint32_t (&mt)[MP][4]) {
+#pragma unroll
+        for (int pp = 0; pp < MP; ++pp) {
+            const float ks = h_val((uint16_t)mt[pp][0]);
+            const float kb = h_val((uint16_t)mt[pp][1]);
+            const float vs = h_val((uint16_t)mt[pp][2]);
+            const float vb = h_val((uint16_t)mt[pp][3]);
+            mring[slot][lane + 64 * pp] =
+                make_float4(ks * csk, (B8 ? fmaf(128.0f, ks, kb) : kb) * cs, vs * WS, fmaf(VC, vs, vb));
+        }
         asm volatile("" ::: "memory");
     };
     // factors (x, y) or (z, w) of row r, group g
@@ -205,7 +222,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     float qsum[NB][NG];
     // NB > 1: the operands wait in LDS and are read back tile by tile, which
     // keeps the wavefront within 256 registers (see the kernel comment)
-    __shared__ __align__(16) half8 q_lds[NB > 1 ? NB : 1][QH][KM][64];
+    __shared__ __align__(16) half8 q_lds[QLDS ? NB : 1][QH][KM][64];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con[nb] ? chead[nb] : 0)) * a.sq + p0 +
@@ -244,7 +261,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 #pragma unroll
         for (int g = 0; g < NG; ++g)
             qsum[nb][g] = xrow_sum(gs[g]);
-        if constexpr (NB > 1) {
+        if constexpr (QLDS) {
 #pragma unroll
             for (int hl = 0; hl < QH; ++hl)
 #pragma unroll
@@ -255,7 +272,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     stage_meta(0, mbuf[0]);
 
     float m_run[NB], l_run[NB], b_run[NB][NG];
-    float4v acc[NB][8], accl[NB][8];  // [nb][4 g + mm]: hi and lo (x kLoScale) weight halves
+    float4v acc[NB][8 * VS], accl[NB][8 * VS];  // [nb][8 s2 + 4 g + mm]: hi and lo (x kLoScale) weight halves
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         m_run[nb] = 0.0f;
@@ -264,7 +281,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
         for (int g = 0; g < NG; ++g)
             b_run[nb][g] = 0.0f;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < 8 * VS; ++m) {
             acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
             accl[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
         }
@@ -306,7 +323,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                             for (int hl = 0; hl < QH; ++hl) {
-                                const half8 qb = NB > 1 ? q_lds[nb][hl][g * KPG + k][lane] : qop[nb][hl][g * KPG + k];
+                                const half8 qb = QLDS ? q_lds[nb][hl][g * KPG + k][lane] : qop[nb][hl][g * KPG + k];
                                 sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, sacc[nb], 0, 0, 0);
                             }
                     }
@@ -361,7 +378,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                         for (int i = 0; i < 4; ++i)
                             corr_row[i] = __shfl(corr, 4 * q4 + i);
 #pragma unroll
-                        for (int m = 0; m < 8; ++m) {
+                        for (int m = 0; m < 8 * VS; ++m) {
                             acc[nb][m] *= corr_row;
                             accl[nb][m] *= corr_row;
                         }
@@ -383,60 +400,64 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair;
             // 8-bit: the same exchange on whole words (row r's two words hold
             // dimensions 0..3 and 4..7)
-            uint32_t bx[NG][4 * KW];
-            if constexpr (B8) {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    bx[0][r] = take_half_row<0xC>(vbuf[u][2 * r], vbuf[u][2 * r + 1]);
-                    bx[1][r] = take_half_row<0x3>(vbuf[u][2 * r], vbuf[u][2 * r + 1]);
-                }
-            } else {
+            for (int s2 = 0; s2 < VS; ++s2) {
+                const uint32_t(&vw)[8 * KW] = vbuf[u][s2];
+                uint32_t bx[2][4 * KW];
+                if constexpr (B8) {
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    const uint32_t xw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x05040100u);
-                    const uint32_t yw = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x07060302u);
-                    bx[0][jp] = take_half_row<0xC>(xw, yw);
-                    bx[1][jp] = take_half_row<0x3>(xw, yw);
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                half8 phi[NB], plo[NB];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    float bsum = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < 8; j += 2) {
-                        const float2 f0 = fac_zw(slot, 16 * (j >> 2) + 4 * q4 + (j & 3), g);
-                        const float2 f1 = fac_zw(slot, 16 * ((j + 1) >> 2) + 4 * q4 + ((j + 1) & 3), g);
-                        bsum = fmaf(p[nb][j], f0.y, fmaf(p[nb][j + 1], f1.y, bsum));
-                        const float w0 = p[nb][j] * f0.x, w1 = p[nb][j + 1] * f1.x;
-                        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-                        const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(
-                                                                        (w0 - (float)h[0]) * kLoScale,
-                                                                        (w1 - (float)h[1]) * kLoScale));
-                        phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
-                        plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
+                    for (int r = 0; r < 8; ++r) {
+                        bx[0][r] = take_half_row<0xC>(vw[2 * r], vw[2 * r + 1]);
+                        bx[1][r] = take_half_row<0x3>(vw[2 * r], vw[2 * r + 1]);
                     }
-                    b_run[nb][g] += bsum;
-                }
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    half2v e[4];
+                } else {
 #pragma unroll
                     for (int jp = 0; jp < 4; ++jp) {
-                        if constexpr (B8)
-                            e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm], magic16);
-                        else
-                            e[jp] = unpack.one(bx[g][jp], mm);
+                        const uint32_t xw = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], 0x05040100u);
+                        const uint32_t yw = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], 0x07060302u);
+                        bx[0][jp] = take_half_row<0xC>(xw, yw);
+                        bx[1][jp] = take_half_row<0x3>(xw, yw);
                     }
-                    const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                }
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int gg = 2 * s2 + g;  // scale group of the head
+                    half8 phi[NB], plo[NB];
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        acc[nb][4 * g + mm] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], bv, acc[nb][4 * g + mm], 0, 0, 0);
-                        accl[nb][4 * g + mm] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, accl[nb][4 * g + mm], 0, 0, 0);
+                        float bsum = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < 8; j += 2) {
+                            const float2 f0 = fac_zw(slot, 16 * (j >> 2) + 4 * q4 + (j & 3), gg);
+                            const float2 f1 = fac_zw(slot, 16 * ((j + 1) >> 2) + 4 * q4 + ((j + 1) & 3), gg);
+                            bsum = fmaf(p[nb][j], f0.y, fmaf(p[nb][j + 1], f1.y, bsum));
+                            const float w0 = p[nb][j] * f0.x, w1 = p[nb][j + 1] * f1.x;
+                            const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                            const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(
+                                                                            (w0 - (float)h[0]) * kLoScale,
+                                                                            (w1 - (float)h[1]) * kLoScale));
+                            phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
+                            plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
+                        }
+                        b_run[nb][gg] += bsum;
+                    }
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) {
+                        half2v e[4];
+#pragma unroll
+                        for (int jp = 0; jp < 4; ++jp) {
+                            if constexpr (B8)
+                                e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm], magic16);
+                            else
+                                e[jp] = unpack.one(bx[g][jp], mm);
+                        }
+                        const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const int m = 8 * s2 + 4 * g + mm;
+                            acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], bv, acc[nb][m], 0, 0, 0);
+                            accl[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, accl[nb][m], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -462,16 +483,18 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const int rpos = cc / nrep, rhead = cc % nrep;
             const bool on = cc < a.pb * nrep && rpos < npos;
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const float bias = __shfl(b_tot[g], r);
-                // group g's products of this lane: dimensions 8 col + 0..3 when
-                // its own word is in g, else 8 (col ^ 8) + 4..7
-                const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
+            for (int gg = 0; gg < NG; ++gg) {
+                const int s2 = gg >> 1, g = gg & 1;
+                const float bias = __shfl(b_tot[gg], r);
+                // group gg's products of this lane: dimensions 128 s2 + 8 col +
+                // 0..3 when its own word is in the set's group g, else
+                // 128 s2 + 8 (col ^ 8) + 4..7
+                const int d0 = 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
                 float o[4];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm) {
-                    const float hi = acc[nb][4 * g + mm][i];
-                    const float lo = accl[nb][4 * g + mm][i];
+                    const float hi = acc[nb][8 * s2 + 4 * g + mm][i];
+                    const float lo = accl[nb][8 * s2 + 4 * g + mm][i];
                     o[mm] = (fmaf(lo, VU / kLoScale, hi * VU) + bias) * inv_l;
                 }
                 if (on) {
@@ -487,34 +510,42 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
 {
-    return D == 128 && G == 64 && n_rep >= 1 && n_rep <= 16 && (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) &&
-           (bits == 4 || bits == 8);
+    return (D == 128 || D == 256) && G == 64 && n_rep >= 1 && n_rep <= 16 &&
+           (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) && (bits == 4 || bits == 8);
 }
 
-// blocks of 16 query columns per wavefront, both code widths (8-bit codes
-// with one block: 35.8 ms against 28.8 ms on the 4096-position chunk)
-constexpr int kPrefillNB = 2;
+// blocks of 16 query columns per wavefront: two at D = 128 (8-bit codes with
+// one block: 35.8 ms against 28.8 ms on the 4096-position chunk), one at
+// D = 256
+constexpr int prefill_nb(int D) { return D == 256 ? 1 : 2; }
 
-int prefill_positions_per_block(int n_rep, int bits)
+int prefill_positions_per_block(int n_rep, int D) { return 16 * prefill_nb(D) / n_rep; }
+
+template <int D>
+void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
 {
-    (void)bits;
-    return 16 * kPrefillNB / n_rep;
+    constexpr int NB = prefill_nb(D);
+    if (a.bits == 8 && a.q_f32)
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 8, true, D>), grid, dim3(64), 0, s, a);
+    else if (a.bits == 8)
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 8, false, D>), grid, dim3(64), 0, s, a);
+    else if (a.q_f32)
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 4, true, D>), grid, dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 4, false, D>), grid, dim3(64), 0, s, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
 {
-    if (a.pb < 1 || a.pb * a.n_rep > 16 * kPrefillNB || (a.bits != 4 && a.bits != 8))
+    if ((a.D != 128 && a.D != 256) || a.pb < 1 || a.pb * a.n_rep > 16 * prefill_nb(a.D) ||
+        (a.bits != 4 && a.bits != 8))
         return hipErrorInvalidValue;
     const int64_t blocks = (a.sq + a.pb - 1) / a.pb;
     dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
-    if (a.bits == 8 && a.q_f32)
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 8, true>), grid, dim3(64), 0, s, a);
-    else if (a.bits == 8)
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 8, false>), grid, dim3(64), 0, s, a);
-    else if (a.q_f32)
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 4, true>), grid, dim3(64), 0, s, a);
+    if (a.D == 256)
+        launch_prefill_d<256>(a, grid, s);
     else
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, kPrefillNB, 4, false>), grid, dim3(64), 0, s, a);
+        launch_prefill_d<128>(a, grid, s);
     return hipGetLastError();
 }
 

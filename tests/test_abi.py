@@ -265,12 +265,12 @@ def test_prefill_validation(L):
     assert _prefill(L, _cache(capacity=1024), q_start=1025, sq=1) == E_CAP
     assert _prefill(L, _cache(), q=P + 4) == E_ALIGN
     assert _prefill(L, _cache(), out=P + 8) == E_ALIGN
-    # outside the prefill kernel: other head sizes and groups, more than 16
-    # query heads per KV head (4- and 8-bit codes, fp16 and fp32 queries are
-    # inside)
-    assert _prefill(L, _cache(head_dim=256)) == E_UNSUP
+    # outside the prefill kernel: head sizes other than 128 and 256, other
+    # groups, more than 16 query heads per KV head (4- and 8-bit codes, fp16
+    # and fp32 queries are inside)
+    assert _prefill(L, _cache(head_dim=64)) == E_UNSUP
     assert _prefill(L, _cache(group=32)) == E_UNSUP
-    assert _prefill(L, _cache(head_dim=256), qd=1) == E_UNSUP
+    assert _prefill(L, _cache(head_dim=64), qd=1) == E_UNSUP
     assert _prefill(L, _cache(bits=3)) == E_SHAPE
     assert _prefill(L, _cache(kv_heads=2), hq=64) == E_UNSUP
 

@@ -16,14 +16,14 @@ pytestmark = pytest.mark.gpu
 REL_L2 = 1e-4  # the matrix-core gate of the decode tests
 
 
-def _case(B, hq, hkv, q_start, sq, seed, alpha=None, cap=None, bits=4):
+def _case(B, hq, hkv, q_start, sq, seed, alpha=None, cap=None, bits=4, D=128):
     S = q_start + sq
-    q = kvq_synth.normal((B, hq, sq, 128), [90, seed, 0]).astype(np.float16)
-    k = kvq_synth.normal((B, hkv, S, 128), [90, seed, 1]).astype(np.float16)
-    v = kvq_synth.normal((B, hkv, S, 128), [90, seed, 2]).astype(np.float16)
-    oc = oracle.Cache(B, hkv, 128, cap or S, 64, bits=bits)
+    q = kvq_synth.normal((B, hq, sq, D), [90, seed, 0]).astype(np.float16)
+    k = kvq_synth.normal((B, hkv, S, D), [90, seed, 1]).astype(np.float16)
+    v = kvq_synth.normal((B, hkv, S, D), [90, seed, 2]).astype(np.float16)
+    oc = oracle.Cache(B, hkv, D, cap or S, 64, bits=bits)
     oc.append(k, v, 0)
-    return q, oc, (1 / np.sqrt(128) if alpha is None else alpha)
+    return q, oc, (1 / np.sqrt(D) if alpha is None else alpha)
 
 
 def _run(oc, q_start, q, alpha):
@@ -185,10 +185,33 @@ def test_rotated_cache_prefill(bits):
         check_attention(got[:, :, i], ref, REL_L2, label="rotated prefill pos %d" % i)
 
 
-@pytest.mark.parametrize("what", ["d256", "g32"])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("q_start,sq", [(0, 1), (0, 33), (423, 40), (1000, 17)])
+def test_head_dim_256(bits, q_start, sq):
+    """D = 256 (four scale groups, two sets of value words): the Gemma-style
+    layer of the decode tests, 32 query heads on 16 KV heads, alpha 1."""
+    note("prefill D256 bits=%d q_start=%d sq=%d" % (bits, q_start, sq))
+    q, oc, _ = _case(1, 32, 16, q_start, sq, seed=9500 + bits * 100 + sq, bits=bits, D=256)
+    q = (q.astype(np.float32) * np.float32(0.25)).astype(np.float16)  # O(10) scores at alpha 1
+    got = _run(oc, q_start, q, 1.0)
+    check_attention(got, oracle.sdpa_prefill(oc, q_start, q, 1.0), 2e-4, atol=1e-3, rtol=1e-3,
+                    label="prefill D256")
+
+
+def test_head_dim_256_fp32_queries_and_gqa8():
+    note("prefill D256 fp32 q, 8 heads per KV head")
+    q16, oc, alpha = _case(1, 16, 2, 300, 45, seed=9600, D=256)
+    q = (q16.astype(np.float32) * np.float32(1.0 + 2.0 ** -13)).astype(np.float32)
+    gc = gpu_cache_from_oracle(oc)
+    got = kvq.sdpa_int4_prefill(gc, 300, to_dev(q), alpha)
+    torch.cuda.synchronize()
+    check_attention(got.cpu().numpy(), oracle.sdpa_prefill(oc, 300, q, alpha), REL_L2, label="prefill D256 fp32")
+
+
+@pytest.mark.parametrize("what", ["d64", "g32"])
 def test_unsupported_shapes_refused(what):
     note("prefill refuses %s" % what)
-    D = 256 if what == "d256" else 128
+    D = 64 if what == "d64" else 128
     G = 32 if what == "g32" else 64
     bits = 4
     gc = kvq.QuantKVCache(1, 2, D, 64, G, device="cuda", bits=bits)
