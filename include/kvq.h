@@ -44,8 +44,10 @@
  *    KV bits): the same rule with 255 in place of 15, codes 0..255, k_q and
  *    v_q uint32 [B][Hkv][cap][D/4] with dimension d at
  *    (word[d/4] >> (8*(d%4))) & 0xFF. Every entry point that takes a cache
- *    reads and writes this format; the matrix-core kernels read int4 codes
- *    only (KVQ_KERNEL_AUTO picks the vector-ALU kernel for 8-bit caches).
+ *    reads and writes this format. Of the split-K kernels, the vector-ALU
+ *    and the one-wavefront matrix-core kernel (KVQ_KERNEL_MFMA_WAVE) read
+ *    8-bit codes; AUTO and MFMA run 8-bit caches on the latter when the chunk
+ *    layout fits it, else on the vector-ALU kernel.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -190,8 +192,8 @@ int kvq_hadamard_rotate(const void *x, int dtype, int64_t rows, int32_t head_dim
  *  chunk:   rows per chunk, >= 1 (512 is the tuned default).
  *  part_*:  fp32 outputs sized [B][Hq][C] and [B][Hq][C][D], 16-byte aligned.
  *  kernel:  KVQ_KERNEL_AUTO, or a forced variant (KVQ_E_UNSUPPORTED if it
- *           cannot run this shape, or an 8-bit cache on a matrix-core
- *           variant).
+ *           cannot run this shape; MFMA_SPLIT and MFMA_PAIR refuse 8-bit
+ *           caches).
  */
 int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
                           float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,
@@ -259,8 +261,8 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
  * MFMA_WAVE, or AUTO / MFMA with at least 1024 (chunk, KV head, batch) items),
  * the append runs inside the attention kernel, in the wavefront that owns the
  * last chunk, so the step is two launches (attention, reduce) instead of
- * three; otherwise (and always for 8-bit caches) it is the three calls in
- * order. Results are the same either way (cache bit for bit, out as
+ * three (8-bit caches: whenever that kernel takes the chunk layout);
+ * otherwise it is the three calls in order. Results are the same either way (cache bit for bit, out as
  * kvq_sdpa_int4 with that kernel). All arguments are validated before anything
  * is enqueued: len + 1 <= capacity (else KVQ_E_CAPACITY), k_new, v_new and out
  * 16-byte aligned, the partials workspace sized for C = ceil((len+1)/chunk).
