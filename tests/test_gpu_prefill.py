@@ -53,9 +53,10 @@ def test_head_layouts(hq, hkv):
     check_attention(got, oracle.sdpa_prefill(oc, 300, q, alpha), REL_L2, label="prefill heads")
 
 
-def test_batch_two_and_spare_capacity():
-    note("prefill batch 2")
-    q, oc, alpha = _case(2, 8, 2, 200, 40, seed=7, cap=400)
+@pytest.mark.parametrize("bits,D", [(4, 128), (8, 128), (4, 256), (8, 256)])
+def test_batch_two_and_spare_capacity(bits, D):
+    note("prefill batch 2 bits=%d D=%d" % (bits, D))
+    q, oc, alpha = _case(2, 8, 2, 200, 40, seed=7 + bits + D, cap=400, bits=bits, D=D)
     got = _run(oc, 200, q, alpha)
     check_attention(got, oracle.sdpa_prefill(oc, 200, q, alpha), REL_L2, label="prefill batch")
 
