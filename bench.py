@@ -396,7 +396,7 @@ def cpu_baseline(kvq, torch, entry, skv):
                 seconds=dt, max_abs_err_vs_gpu=err)
 
 
-def main():
+def build_parser():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
@@ -409,14 +409,15 @@ def main():
                     help="extra Skv values timed with fewer steps (empty to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
-                    help="skip the measurements of the rows beyond the headline path (Hadamard-rotated cache)")
+                    help="skip the measurements of the rows beyond the headline path (Hadamard-rotated cache, "
+                         "8-bit cache, prefill)")
     ap.add_argument("--step", choices=["fused", "unfused", "rotated", "rotated-unfused"], default="fused",
                     help="fused: kvq_decode_step (append inside the attention kernel, then the reduce); "
                          "unfused: append, partial and reduce as three calls")
     ap.add_argument("--layers", type=int, default=80,
                     help="layers of the full-depth decode step timed after the headline (0 skips it)")
     ap.add_argument("--bits", type=int, choices=[4, 8], default=4,
-                    help="bits per cached code of the headline run (8: the int8 cache, vector-ALU attention)")
+                    help="bits per cached code of the headline run (8: the 8-bit cache)")
     ap.add_argument("--repeats", type=int, default=10,
                     help="after the timed steps, time the same steps again as this many separate runs "
                          "(median / p10 / p90 of the per-step time; 0 skips)")
@@ -425,7 +426,11 @@ def main():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MB (a known-size reference "
                          "for hardware byte counters)")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = build_parser().parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
