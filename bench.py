@@ -392,7 +392,8 @@ def cpu_baseline(kvq, torch, entry, skv):
     torch.cuda.synchronize()
     err = float(np.abs(out.cpu().numpy() - ref).max())
     return dict(value=layer_bytes(skv, cache.bits) / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                sample="one full layer-call (64 q-heads, Skv=%d) of the float64 oracle, %.2f s wall" % (skv, dt),
+                sample="one full layer-call (64 q-heads, Skv=%d) of the float64 oracle, %.2f s wall on %d threads "
+                       "(at most %.0f thread-seconds of CPU work)" % (skv, dt, threads, dt * threads),
                 seconds=dt, max_abs_err_vs_gpu=err)
 
 
