@@ -136,3 +136,33 @@ def test_rows_layout_groups(oracle_mod):
             c, s, b = oracle_mod.quantize_group(x[r, g * 64:(g + 1) * 64])
             assert np.array_equal(codes[g * 64:(g + 1) * 64], c)
             assert (sc[r, g], bi[r, g]) == (s, b)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bias,step", [(0.0, 1.0), (-4.0, 0.5), (3.0, 0.25)])
+def test_exact_ties_round_to_even(oracle_mod, bits, bias, step):
+    """Reading R3 of the code rounding (the pages name no rule): a quotient
+    (x - bias) / scale that lies exactly halfway between two codes takes the
+    even one. The group holds its own minimum (bias, fp16-exact, so the bias
+    is that value) and maximum bias + levels * step (scale exactly step, a
+    power of two, so every quotient below is exact in fp32), and every
+    half-integer quotient k + 1/2 in between. Rounding half away from zero
+    would give k + 1 for every even k and fails here."""
+    levels = (1 << bits) - 1
+    half = np.arange(levels, dtype=np.float64) + 0.5  # 0.5, 1.5, ..., levels - 0.5
+    G = 64 if bits == 4 else 256
+    members = np.concatenate([[0.0, float(levels)], half])
+    members = np.resize(members, G)  # both ends first, ties fill the rest
+    x = bias + members * step
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    codes, sbits, bbits = oracle_mod.quantize_group(x.astype(np.float32), bits)
+    s = oracle_mod.f16_to_f64(np.array([sbits], dtype=np.uint16))[0]
+    b = oracle_mod.f16_to_f64(np.array([bbits], dtype=np.uint16))[0]
+    assert (s, b) == (step, bias)
+    # k + 1/2 -> k when k is even, k + 1 when k is odd
+    k = np.floor(members)
+    expect = np.where(members == k, k, np.where(k % 2 == 0, k, k + 1))
+    assert np.array_equal(codes.astype(np.float64), expect)
+    # spot values named in the rule: 0.5 -> 0, 2.5 -> 2, 14.5 -> 14 (and 1.5 -> 2)
+    by_member = {float(m): int(c) for m, c in zip(members, codes)}
+    assert by_member[0.5] == 0 and by_member[1.5] == 2 and by_member[2.5] == 2 and by_member[14.5] == 14
