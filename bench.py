@@ -405,7 +405,7 @@ def build_parser():
     ap.add_argument("--skv", type=int, default=131072)
     ap.add_argument("--chunk", type=int, default=512)
     ap.add_argument("--pool-mb", type=int, default=int(2.5 * MALL_BYTES / 1e6))
-    ap.add_argument("--kernel", choices=["auto", "valu", "mfma", "mfma-split", "mfma-wave", "mfma-pair"], default="auto")
+    ap.add_argument("--kernel", choices=["auto", "valu", "mfma", "mfma-split", "mfma-wave"], default="auto")
     ap.add_argument("--sweep", default="1024,16384,65536",
                     help="extra Skv values timed with fewer steps (empty to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -448,8 +448,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     kernel = {"auto": kvq.KERNEL_AUTO, "valu": kvq.KERNEL_VALU, "mfma": kvq.KERNEL_MFMA,
-              "mfma-split": kvq.KERNEL_MFMA_SPLIT, "mfma-wave": kvq.KERNEL_MFMA_WAVE,
-              "mfma-pair": kvq.KERNEL_MFMA_PAIR}[args.kernel]
+              "mfma-split": kvq.KERNEL_MFMA_SPLIT, "mfma-wave": kvq.KERNEL_MFMA_WAVE}[args.kernel]
     pool_bytes = args.pool_mb * 1000 * 1000
 
     bits = args.bits

@@ -10,8 +10,8 @@
  *    no float temporaries, nibbles read lowest first.
  *  - "turboquant-llama3.170B" README: the kernel paragraph (per-element
  *    dequantisation, Q.K^T, online softmax, no score matrix), the split-K
- *    paragraph (512-token chunks computed independently, then a second phase
- *    that reduces the partial softmax results, ordered after the first), the
+ *    paragraph (512-token chunks computed independently, then a second phase,
+ *    run after the first, that merges the per-chunk softmax states), the
  *    decode-step listing (K and V quantised to int4 on append; GQA).
  *
  * Conventions for every entry point:
@@ -78,10 +78,9 @@ typedef enum kvq_kernel {
     KVQ_KERNEL_MFMA = 2,        /* matrix-core kernels, D in {128, 256} and (Hq/Hkv) * (D/G) <= 16;
                                    the variant below is chosen by grid size */
     KVQ_KERNEL_MFMA_SPLIT = 3,  /* matrix-core, four wavefronts per chunk (any chunk length) */
-    KVQ_KERNEL_MFMA_WAVE = 4,   /* matrix-core, one wavefront per chunk: chunk <= 512 and
+    KVQ_KERNEL_MFMA_WAVE = 4    /* matrix-core, one wavefront per chunk: chunk <= 512 and
                                    chunk * (D/G) and capacity * (D/G) multiples of 8 */
-    KVQ_KERNEL_MFMA_PAIR = 5    /* matrix-core, two wavefronts per chunk (half the rows each):
-                                   the MFMA_WAVE rules, D = 128 and fp16 q */
+    /* any other value returns KVQ_E_SHAPE (5 named a two-wavefront variant, since removed) */
 } kvq_kernel;
 
 /* One layer's quantised cache (all device pointers, 16-byte aligned). */
@@ -192,8 +191,7 @@ int kvq_hadamard_rotate(const void *x, int dtype, int64_t rows, int32_t head_dim
  *  chunk:   rows per chunk, >= 1 (512 is the tuned default).
  *  part_*:  fp32 outputs sized [B][Hq][C] and [B][Hq][C][D], 16-byte aligned.
  *  kernel:  KVQ_KERNEL_AUTO, or a forced variant (KVQ_E_UNSUPPORTED if it
- *           cannot run this shape; MFMA_SPLIT and MFMA_PAIR refuse 8-bit
- *           caches).
+ *           cannot run this shape; MFMA_SPLIT refuses 8-bit caches).
  */
 int kvq_sdpa_int4_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dtype, int32_t Hq,
                           float softmax_scale, int32_t chunk, float *part_m, float *part_l, float *part_acc,

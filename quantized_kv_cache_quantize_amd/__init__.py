@@ -13,7 +13,6 @@ from ._binding import (  # noqa: F401
     KVQ_F32,
     KERNEL_AUTO,
     KERNEL_MFMA,
-    KERNEL_MFMA_PAIR,
     KERNEL_MFMA_SPLIT,
     KERNEL_MFMA_WAVE,
     KERNEL_VALU,

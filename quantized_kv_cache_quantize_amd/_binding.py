@@ -11,7 +11,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 KVQ_F16, KVQ_F32 = 0, 1
-KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_SPLIT, KERNEL_MFMA_WAVE, KERNEL_MFMA_PAIR = 0, 1, 2, 3, 4, 5
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_SPLIT, KERNEL_MFMA_WAVE = 0, 1, 2, 3, 4
 
 
 class KvqError(RuntimeError):
@@ -132,6 +132,90 @@ def _dtype_code(t: torch.Tensor) -> int:
     return 99  # rejected by the library with KVQ_E_DTYPE
 
 
+# ---- argument checks. The C ABI takes bare device pointers and cannot see
+# sizes, so every tensor is checked here before anything is enqueued: shapes,
+# dtypes and sizes of all arguments first (so that they are checked without a
+# GPU too), then that each is a contiguous tensor on the cache's CUDA device.
+# A failed check raises ValueError and nothing is launched.
+
+def _fail(fn: str, msg: str):
+    raise ValueError("%s: %s" % (fn, msg))
+
+
+class _Args:
+    """Checks of one call's tensors: need() checks a tensor's layout at once
+    and keeps it; devices() then checks where all of them live."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.seen = []
+
+    def need(self, name: str, t, shape=None, dtypes=None, min_numel=None):
+        fn = self.fn
+        if not isinstance(t, torch.Tensor):
+            _fail(fn, "%s must be a torch.Tensor" % name)
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            _fail(fn, "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        if dtypes is not None and t.dtype not in dtypes:
+            _fail(fn, "%s has dtype %s, expected one of %s" % (name, t.dtype, [str(d) for d in dtypes]))
+        if min_numel is not None and t.numel() < min_numel:
+            _fail(fn, "%s holds %d elements, needs at least %d" % (name, t.numel(), min_numel))
+        if not t.is_contiguous():
+            _fail(fn, "%s must be contiguous" % name)
+        self.seen.append((name, t))
+        return t
+
+    def devices(self, device=None):
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                _fail(self.fn, "%s must be a CUDA (HIP) device tensor, got %s" % (name, t.device))
+            if device is not None and t.device != device:
+                _fail(self.fn, "%s is on %s, the cache is on %s" % (name, t.device, device))
+
+
+_FP = (torch.float16, torch.float32)
+_F32 = (torch.float32,)
+
+
+def _rows_arg(A: _Args, name: str, t, cache, allow_3d: bool):
+    """k_new / v_new: [B][Hkv][n][D] (or [B][Hkv][D] for one row where
+    allow_3d); returns n."""
+    B, H, D = cache.batch, cache.kv_heads, cache.head_dim
+    if not isinstance(t, torch.Tensor):
+        _fail(A.fn, "%s must be a torch.Tensor" % name)
+    if t.dim() == 3 and allow_3d:
+        A.need(name, t, (B, H, D), _FP)
+        return 1
+    if t.dim() != 4 or tuple(t.shape[:2]) != (B, H) or t.shape[3] != D or (allow_3d and t.shape[2] != 1):
+        want = "[%d, %d, %s, %d]" % (B, H, "1" if allow_3d else "n", D)
+        if allow_3d:
+            want += " or [%d, %d, %d]" % (B, H, D)
+        _fail(A.fn, "%s has shape %s, expected %s" % (name, tuple(t.shape), want))
+    A.need(name, t, None, _FP)
+    return int(t.shape[2])
+
+
+def _query_arg(A: _Args, q, cache, dims: int = 3):
+    if not isinstance(q, torch.Tensor) or q.dim() != dims:
+        _fail(A.fn, "q must be a %d-D tensor" % dims)
+    B, Hq, D = q.shape[0], q.shape[1], q.shape[-1]
+    if B != cache.batch or D != cache.head_dim or Hq < 1 or Hq % cache.kv_heads:
+        _fail(A.fn, "q has shape %s: batch %d, head_dim %d and a multiple of %d query heads expected" % (
+            tuple(q.shape), cache.batch, cache.head_dim, cache.kv_heads))
+    A.need("q", q, None, _FP)
+    return B, Hq, D
+
+
+def _workspace_arg(A: _Args, ws, B, Hq, D, C):
+    if ws is None or len(ws) != 3:
+        _fail(A.fn, "workspace must be (part_m, part_l, part_acc)")
+    m, l, acc = ws
+    A.need("part_m", m, None, _F32, B * Hq * C)
+    A.need("part_l", l, None, _F32, B * Hq * C)
+    A.need("part_acc", acc, None, _F32, B * Hq * C * D)
+    return m, l, acc
+
+
 class QuantKVCache:
     """One layer's quantised cache in device memory (allocated by PyTorch).
 
@@ -143,17 +227,29 @@ class QuantKVCache:
                  device="cuda", tensors=None, bits: int = 4):
         self.batch, self.kv_heads, self.head_dim = batch, kv_heads, head_dim
         self.capacity, self.group, self.bits = capacity, group, bits
+        if bits not in (4, 8) or head_dim % 8 or group < 1 or head_dim % group:
+            _fail("QuantKVCache", "unsupported layout (head_dim %d, group %d, bits %d)" % (head_dim, group, bits))
+        wshape = (batch, kv_heads, capacity, head_dim * bits // 32)
+        sshape = (batch, kv_heads, capacity, head_dim // group)
         if tensors is not None:
             self.k_q, self.v_q, self.k_scale, self.k_bias, self.v_scale, self.v_bias = tensors
+            A = _Args("QuantKVCache")
+            for name in ("k_q", "v_q"):
+                A.need(name, getattr(self, name), wshape, (torch.int32,))
+            for name in ("k_scale", "k_bias", "v_scale", "v_bias"):
+                A.need(name, getattr(self, name), sshape, (torch.float16,))
+            A.devices(self.k_q.device)
         else:
-            wshape = (batch, kv_heads, capacity, head_dim * bits // 32)
-            sshape = (batch, kv_heads, capacity, head_dim // group)
             self.k_q = torch.zeros(wshape, dtype=torch.int32, device=device)
             self.v_q = torch.zeros(wshape, dtype=torch.int32, device=device)
             self.k_scale = torch.zeros(sshape, dtype=torch.float16, device=device)
             self.k_bias = torch.zeros(sshape, dtype=torch.float16, device=device)
             self.v_scale = torch.zeros(sshape, dtype=torch.float16, device=device)
             self.v_bias = torch.zeros(sshape, dtype=torch.float16, device=device)
+
+    @property
+    def device(self):
+        return self.k_q.device
 
     def c_struct(self) -> _Cache:
         return _Cache(_ptr(self.k_q), _ptr(self.v_q), _ptr(self.k_scale), _ptr(self.k_bias), _ptr(self.v_scale),
@@ -170,12 +266,20 @@ class QuantKVCache:
 Int4KVCache = QuantKVCache  # the int4 cache of the pages (bits=4, the default)
 
 
+def _append_rows(fn, cache, k_new, v_new):
+    A = _Args(fn)
+    n = _rows_arg(A, "k_new", k_new, cache, allow_3d=False)
+    if _rows_arg(A, "v_new", v_new, cache, allow_3d=False) != n or v_new.dtype != k_new.dtype:
+        _fail(fn, "k_new and v_new must have the same shape and dtype")
+    A.devices(cache.device)
+    return n
+
+
 def quantize_kv_append(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
                        stream=None) -> None:
     """kvq_quantize_kv_append: quantise k_new, v_new [B][Hkv][n][D] (fp16 or
     fp32, contiguous) into cache rows [length, length + n)."""
-    assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
-    n = k_new.shape[2] if k_new.dim() == 4 else 0
+    n = _append_rows("quantize_kv_append", cache, k_new, v_new)
     cs = cache.c_struct()
     _check("kvq_quantize_kv_append",
            lib().kvq_quantize_kv_append(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
@@ -187,8 +291,7 @@ def quantize_kv_append_rotated(cache: QuantKVCache, length: int, k_new: torch.Te
     """kvq_quantize_kv_append_rotated: Hadamard-rotate, then quantise, fp16
     rows k_new, v_new [B][Hkv][n][D] (contiguous) into cache rows
     [length, length + n)."""
-    assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
-    n = k_new.shape[2] if k_new.dim() == 4 else 0
+    n = _append_rows("quantize_kv_append_rotated", cache, k_new, v_new)
     cs = cache.c_struct()
     _check("kvq_quantize_kv_append_rotated",
            lib().kvq_quantize_kv_append_rotated(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new),
@@ -199,11 +302,15 @@ def hadamard_rotate(x: torch.Tensor, out: torch.Tensor | None = None, stream=Non
     """kvq_hadamard_rotate: rotate every row of x [..., D] (fp16 or fp32,
     contiguous) by H_D / sqrt(D); returns fp32 `out` (new, or the one given,
     which may be x itself when x is fp32)."""
-    assert x.is_contiguous()
+    A = _Args("hadamard_rotate")
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        _fail(A.fn, "x must be a tensor [..., D]")
+    A.need("x", x, None, _FP)
     d = x.shape[-1]
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    assert out.is_contiguous() and out.dtype == torch.float32 and out.shape == x.shape
+    A.need("out", out, x.shape, _F32)
+    A.devices(x.device)
     _check("kvq_hadamard_rotate",
            lib().kvq_hadamard_rotate(_ptr(x), _dtype_code(x), int(x.numel() // d), int(d), _ptr(out),
                                      _stream(stream)))
@@ -214,7 +321,10 @@ def hbm_read(buf: torch.Tensor, sink: torch.Tensor, key: int = 0xFFFFFFFF, strea
     """kvq_hbm_read: read every byte of the contiguous device tensor `buf`
     once (a measurement helper); `sink` is a device int32 tensor of at least
     one element, written only when a thread's XOR of its words equals key."""
-    assert buf.is_contiguous() and sink.dtype == torch.int32 and sink.numel() >= 1
+    A = _Args("hbm_read")
+    A.need("buf", buf)
+    A.need("sink", sink, None, (torch.int32,), 1)
+    A.devices(buf.device)
     _check("kvq_hbm_read", lib().kvq_hbm_read(_ptr(buf), int(buf.numel() * buf.element_size()), int(key) & 0xFFFFFFFF,
                                               _ptr(sink), _stream(stream)))
 
@@ -228,16 +338,24 @@ def partials_buffers(batch: int, hq: int, head_dim: int, skv: int, chunk: int = 
     return m, l, acc
 
 
+def _partial_args(fn, cache, skv, q, chunk, ws):
+    A = _Args(fn)
+    B, Hq, D = _query_arg(A, q, cache)
+    ws = _workspace_arg(A, ws, B, Hq, D, num_chunks(skv, chunk))
+    A.devices(cache.device)
+    return (Hq,) + ws
+
+
 def sdpa_int4_partial(cache: QuantKVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int,
                       part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor,
                       kernel: int = KERNEL_AUTO, stream=None) -> None:
     """kvq_sdpa_int4_partial: q [B][Hq][D] fp16/fp32 contiguous."""
-    assert q.is_contiguous()
+    hq, m, l, acc = _partial_args("sdpa_int4_partial", cache, skv, q, chunk, (part_m, part_l, part_acc))
     cs = cache.c_struct()
     _check("kvq_sdpa_int4_partial",
-           lib().kvq_sdpa_int4_partial(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), int(q.shape[1]),
-                                       float(softmax_scale), int(chunk), _ptr(part_m), _ptr(part_l),
-                                       _ptr(part_acc), int(kernel), _stream(stream)))
+           lib().kvq_sdpa_int4_partial(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), hq,
+                                       float(softmax_scale), int(chunk), _ptr(m), _ptr(l),
+                                       _ptr(acc), int(kernel), _stream(stream)))
 
 
 def _event_handle(ev) -> int:
@@ -252,39 +370,69 @@ def sdpa_int4_partial_timed(cache: QuantKVCache, skv: int, q: torch.Tensor, soft
                             kernel: int = KERNEL_AUTO, stream=None) -> None:
     """kvq_sdpa_int4_partial_timed: as sdpa_int4_partial, with torch.cuda.Event
     start/stop (enable_timing=True) recorded at the kernel's own start and end."""
-    assert q.is_contiguous()
+    hq, m, l, acc = _partial_args("sdpa_int4_partial_timed", cache, skv, q, chunk, (part_m, part_l, part_acc))
     cs = cache.c_struct()
     _check("kvq_sdpa_int4_partial_timed",
-           lib().kvq_sdpa_int4_partial_timed(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), int(q.shape[1]),
-                                             float(softmax_scale), int(chunk), _ptr(part_m), _ptr(part_l),
-                                             _ptr(part_acc), int(kernel), _stream(stream), _event_handle(start),
+           lib().kvq_sdpa_int4_partial_timed(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), hq,
+                                             float(softmax_scale), int(chunk), _ptr(m), _ptr(l),
+                                             _ptr(acc), int(kernel), _stream(stream), _event_handle(start),
                                              _event_handle(stop)))
 
 
 def sdpa_int4_reduce(part_m: torch.Tensor, part_l: torch.Tensor, part_acc: torch.Tensor, out: torch.Tensor,
                      stream=None) -> None:
-    """kvq_sdpa_int4_reduce: out [B][Hq][D] fp32."""
+    """kvq_sdpa_int4_reduce: part_acc [B][Hq][C][D], part_m and part_l
+    [B][Hq][C], out [B][Hq][D] fp32."""
+    A = _Args("sdpa_int4_reduce")
+    if not isinstance(part_acc, torch.Tensor) or part_acc.dim() != 4:
+        _fail(A.fn, "part_acc must be a 4-D tensor [B][Hq][C][D]")
     b, hq, nc, d = part_acc.shape
+    A.need("part_acc", part_acc, None, _F32)
+    A.need("part_m", part_m, (b, hq, nc), _F32)
+    A.need("part_l", part_l, (b, hq, nc), _F32)
+    A.need("out", out, (b, hq, d), _F32)
+    A.devices(part_acc.device)
     _check("kvq_sdpa_int4_reduce",
            lib().kvq_sdpa_int4_reduce(_ptr(part_m), _ptr(part_l), _ptr(part_acc), b, hq, d, nc, _ptr(out),
                                       _stream(stream)))
 
 
+def _out_arg(A: _Args, out, B, Hq, D, device):
+    if out is None:
+        return torch.empty((B, Hq, D), dtype=torch.float32, device=device)
+    return A.need("out", out, (B, Hq, D), _F32)
+
+
 def sdpa_int4(cache: QuantKVCache, skv: int, q: torch.Tensor, softmax_scale: float, chunk: int = 512,
               out: torch.Tensor | None = None, workspace=None, kernel: int = KERNEL_AUTO, stream=None):
     """kvq_sdpa_int4: both phases on one stream; returns out [B][Hq][D] fp32."""
-    assert q.is_contiguous()
-    b, hq, d = q.shape
+    A = _Args("sdpa_int4")
+    b, hq, d = _query_arg(A, q, cache)
     if workspace is None:
         workspace = partials_buffers(b, hq, d, skv, chunk, device=q.device)
-    if out is None:
-        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
-    m, l, acc = workspace
+    m, l, acc = _workspace_arg(A, workspace, b, hq, d, num_chunks(skv, chunk))
+    out = _out_arg(A, out, b, hq, d, q.device)
+    A.devices(cache.device)
     cs = cache.c_struct()
     _check("kvq_sdpa_int4",
            lib().kvq_sdpa_int4(C.byref(cs), int(skv), _ptr(q), _dtype_code(q), hq, float(softmax_scale),
                                int(chunk), _ptr(m), _ptr(l), _ptr(acc), _ptr(out), int(kernel), _stream(stream)))
     return out
+
+
+def _step_args(fn, cache, length, k_new, v_new, q, chunk, out, workspace):
+    A = _Args(fn)
+    _rows_arg(A, "k_new", k_new, cache, allow_3d=True)
+    _rows_arg(A, "v_new", v_new, cache, allow_3d=True)
+    if v_new.dtype != k_new.dtype:
+        _fail(fn, "k_new and v_new must have the same dtype")
+    b, hq, d = _query_arg(A, q, cache)
+    if workspace is None:
+        workspace = partials_buffers(b, hq, d, length + 1, chunk, device=q.device)
+    ws = _workspace_arg(A, workspace, b, hq, d, num_chunks(length + 1, chunk))
+    out = _out_arg(A, out, b, hq, d, q.device)
+    A.devices(cache.device)
+    return hq, ws, out
 
 
 def decode_step(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
@@ -294,13 +442,7 @@ def decode_step(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: to
     row `length`, then attention over length + 1 rows; returns out [B][Hq][D].
     events: optional (start, stop) torch.cuda.Event recorded in the attention
     kernel's own dispatch (kvq_decode_step_timed)."""
-    assert q.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
-    b, hq, d = q.shape
-    if workspace is None:
-        workspace = partials_buffers(b, hq, d, length + 1, chunk, device=q.device)
-    if out is None:
-        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
-    m, l, acc = workspace
+    hq, (m, l, acc), out = _step_args("decode_step", cache, length, k_new, v_new, q, chunk, out, workspace)
     cs = cache.c_struct()
     args = (C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q), _dtype_code(q), hq,
             float(softmax_scale), int(chunk), _ptr(m), _ptr(l), _ptr(acc), _ptr(out), int(kernel), _stream(stream))
@@ -317,10 +459,13 @@ def sdpa_int4_prefill(cache: QuantKVCache, q_start: int, q: torch.Tensor, softma
     """kvq_sdpa_int4_prefill: q [B][Hq][Sq][D] fp16 or fp32 contiguous, the queries of
     positions q_start .. q_start + Sq - 1 (their K/V rows already appended);
     returns out [B][Hq][Sq][D] fp32."""
-    assert q.is_contiguous() and q.dim() == 4
+    A = _Args("sdpa_int4_prefill")
+    _query_arg(A, q, cache, dims=4)
     b, hq, sq, d = q.shape
     if out is None:
         out = torch.empty((b, hq, sq, d), dtype=torch.float32, device=q.device)
+    A.need("out", out, (b, hq, sq, d), _F32)
+    A.devices(cache.device)
     cs = cache.c_struct()
     _check("kvq_sdpa_int4_prefill",
            lib().kvq_sdpa_int4_prefill(C.byref(cs), int(q_start), int(sq), _ptr(q), _dtype_code(q), hq,
@@ -334,13 +479,7 @@ def decode_step_rotated(cache: QuantKVCache, length: int, k_new: torch.Tensor, v
     """kvq_decode_step_rotated: the decode step on a Hadamard-rotated cache
     (fp16 k_new, v_new; q and out in the original coordinates); returns out
     [B][Hq][D] fp32."""
-    assert q.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype
-    b, hq, d = q.shape
-    if workspace is None:
-        workspace = partials_buffers(b, hq, d, length + 1, chunk, device=q.device)
-    if out is None:
-        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
-    m, l, acc = workspace
+    hq, (m, l, acc), out = _step_args("decode_step_rotated", cache, length, k_new, v_new, q, chunk, out, workspace)
     cs = cache.c_struct()
     _check("kvq_decode_step_rotated",
            lib().kvq_decode_step_rotated(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),

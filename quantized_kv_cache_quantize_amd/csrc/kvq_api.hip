@@ -224,14 +224,14 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     const int64_t C = kvq_num_chunks(skv, chunk);
     if (C > 0x7fffffff)
         return KVQ_E_SHAPE;
-    if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA_PAIR)
+    if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA_WAVE)
         return KVQ_E_SHAPE;
     const int n_rep = Hq / cache->kv_heads;
     const int bits = cache_bits(cache);
     const bool want_mfma = kernel == KVQ_KERNEL_MFMA || kernel == KVQ_KERNEL_MFMA_SPLIT ||
-                           kernel == KVQ_KERNEL_MFMA_WAVE || kernel == KVQ_KERNEL_MFMA_PAIR;
+                           kernel == KVQ_KERNEL_MFMA_WAVE;
     // 8-bit caches have the one-wavefront matrix-core kernel only
-    if (bits == 8 && (kernel == KVQ_KERNEL_MFMA_SPLIT || kernel == KVQ_KERNEL_MFMA_PAIR))
+    if (bits == 8 && kernel == KVQ_KERNEL_MFMA_SPLIT)
         return KVQ_E_UNSUPPORTED;
 
     PartialArgs &a = p.a;
@@ -267,8 +267,6 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     if (want_mfma && !mfma_ok)
         return KVQ_E_UNSUPPORTED;
     if (kernel == KVQ_KERNEL_MFMA_WAVE && !mfma_one_wave_ok(a, cache->head_dim, cache->batch))
-        return KVQ_E_UNSUPPORTED;
-    if (kernel == KVQ_KERNEL_MFMA_PAIR && !mfma_pair_ok(a, cache->head_dim, q_dtype, cache->batch))
         return KVQ_E_UNSUPPORTED;
     p.use_mfma = want_mfma || (kernel == KVQ_KERNEL_AUTO && mfma_ok);
     return KVQ_OK;
@@ -447,7 +445,7 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
         return st;
     const bool rot_inside = rotate && p.use_mfma && cache->head_dim == 128 &&
                             mfma_one_wave_ok(p.a, cache->head_dim, cache->batch) &&
-                            (kernel != KVQ_KERNEL_MFMA_SPLIT && kernel != KVQ_KERNEL_MFMA_PAIR);
+                            kernel != KVQ_KERNEL_MFMA_SPLIT;
     if (rotate && !rot_inside) {
         st = prepare_partial(cache, len + 1, out, KVQ_F32, Hq, softmax_scale, chunk, part_m, part_l, part_acc, kernel,
                              p);

@@ -137,7 +137,6 @@ hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int bat
 bool mfma_supports(int D, int G, int n_rep, int chunk);
 hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l);
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch);
-bool mfma_pair_ok(const PartialArgs &a, int D, int q_dtype, int batch);
 // the fused decode step: append (a.append_row) + partial with the one-wavefront kernel
 hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);

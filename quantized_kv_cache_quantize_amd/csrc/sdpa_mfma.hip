@@ -738,8 +738,10 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 
     // m_run: the softmax reference of this lane's head (log2 units); scores
     // are computed relative to it, each of the NG group columns of a head
-    // subtracting m_part = m_run / NG before their sum
-    float m_run = 0.0f, m_part = 0.0f, l_run = 0.0f, b_run = 0.0f;
+    // subtracting m_part = m_run / NG before their sum. m_top: this lane's
+    // largest score so far, relative to m_run (the partial state is written
+    // against the true maximum, which lies in [m_run - kHeadroom, m_run]).
+    float m_run = 0.0f, m_part = 0.0f, l_run = 0.0f, b_run = 0.0f, m_top = -INFINITY;
     float4v acc[VS][8];
 #pragma unroll
     for (int s = 0; s < VS; ++s)
@@ -804,6 +806,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             }
             const float mx = max3_raw(max3_raw(sc[0], sc[1], sc[2]), max3_raw(sc[3], sc[4], sc[5]),
                                       max_raw(sc[6], sc[7]));
+            m_top = max_raw(m_top, mx);
 
             // ---- online softmax across tiles. The scores are relative to the
             // head's reference m_run, which is raised only when a score
@@ -818,6 +821,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 const float delta = raise ? full + kHeadroom : 0.0f;
                 m_run += delta;
                 m_part = m_run * (1.0f / NG);
+                m_top -= delta;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     sc[i] -= delta;
@@ -969,13 +973,19 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         }
     }
 
-    // ---- write the partial state of this chunk
-    const float l_tot = xrow_sum(l_run);
-    const float b_tot = xrow_sum(b_run);
+    // ---- write the partial state of this chunk, against the head's true
+    // maximum: the weights so far are relative to m_run, and the largest of
+    // them is exp2(top) with top in [-kHeadroom, 0], so l and the products
+    // are multiplied by exp2(-top) (a factor in [1, 2^kHeadroom]) and
+    // m = m_run + top
+    const float top = xrow_max(m_top, -INFINITY);
+    const float renorm = __builtin_amdgcn_exp2f(-top);
+    const float l_tot = xrow_sum(l_run) * renorm;
+    const float b_tot = xrow_sum(b_run) * renorm;
     const int64_t C = a.num_chunks;
     if (q4 == 0 && col_on && gl == 0) {
         const int64_t o = ((int64_t)b * a.Hq + h0 + hl) * C + c;
-        a.part_m[o] = m_run * kLn2;
+        a.part_m[o] = (m_run + top) * kLn2;
         a.part_l[o] = l_tot;
     }
     if constexpr (GV) {
@@ -1010,10 +1020,11 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         for (int r = 0; r < 4; ++r) {
             const int h = 4 * (q4 & 1) + r;
             const float bias = __shfl(b_tot, h + 8 * g);
+            const float f = __shfl(renorm, h + 8 * g);
             if (h < nrep) {
                 float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
-                *reinterpret_cast<float4 *>(dst + d0) =
-                    make_float4(o[r][0] + bias, o[r][1] + bias, o[r][2] + bias, o[r][3] + bias);
+                *reinterpret_cast<float4 *>(dst + d0) = make_float4(fmaf(o[r][0], f, bias), fmaf(o[r][1], f, bias),
+                                                                    fmaf(o[r][2], f, bias), fmaf(o[r][3], f, bias));
             }
         }
         return;
@@ -1022,6 +1033,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     for (int i = 0; i < 4; ++i) {
         const int rr = 4 * q4 + i;
         const float bias_r = __shfl(b_tot, rr);
+        const float f = __shfl(renorm, rr);
         if (rr < R) {
             const int h = rr / NG, g = rr % NG;
             float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
@@ -1029,312 +1041,14 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             for (int s = 0; s < VS; ++s) {
                 const int word = 16 * s + col;
                 if (word / WPG == g) {
-                    float4 lo = {acc[s][0][i] * VU + bias_r, acc[s][1][i] * VU + bias_r, acc[s][2][i] * VU + bias_r,
-                                 acc[s][3][i] * VU + bias_r};
-                    float4 hi = {acc[s][4][i] * VU + bias_r, acc[s][5][i] * VU + bias_r, acc[s][6][i] * VU + bias_r,
-                                 acc[s][7][i] * VU + bias_r};
+                    const float fu = f * VU;
+                    float4 lo = {fmaf(acc[s][0][i], fu, bias_r), fmaf(acc[s][1][i], fu, bias_r),
+                                 fmaf(acc[s][2][i], fu, bias_r), fmaf(acc[s][3][i], fu, bias_r)};
+                    float4 hi = {fmaf(acc[s][4][i], fu, bias_r), fmaf(acc[s][5][i], fu, bias_r),
+                                 fmaf(acc[s][6][i], fu, bias_r), fmaf(acc[s][7][i], fu, bias_r)};
                     *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
                     *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
                 }
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Wavefront-pair variant (D = 128, fp16 Q): a 128-thread workgroup owns one
-// (chunk <= 512 rows, KV head, batch); wavefront w streams the rows
-// [w * RW, (w + 1) * RW) of the chunk with the one-wavefront tile code, and
-// wavefront 1 hands its softmax state to wavefront 0 through LDS at the end.
-// Each wavefront fits in 128 registers (two-tile ring), so a SIMD holds four
-// of them: twice the independent instruction streams of the one-wavefront
-// kernel for the same partial-output traffic.
-// ---------------------------------------------------------------------------
-constexpr int RW2 = CH1 / 2;  // most rows per wavefront in the pair kernel
-
-template <int NG, int PF>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4)))
-void sdpa_partial_mfma_pair_kernel(PartialArgs a)
-{
-    constexpr int D = 128;
-    constexpr int W = D / 8;
-    constexpr int WPL = W / 4;
-    constexpr int KM = W / 4;
-    constexpr int WPG = W / NG;
-    constexpr int SEG = 8 / NG;
-    constexpr int META = 4 * NG * RW2;            // halves per wavefront
-    constexpr int XCH = (3 + 32) * 64;            // floats handed over: m, l, b and acc per lane
-    constexpr int SMEM = (2 * META * 2 > XCH * 4) ? 2 * META * 2 : XCH * 4;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int q4 = lane >> 4;
-    const int col = lane & 15;
-    const int c = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
-    const int nrep = a.n_rep;
-    const int R = nrep * NG;
-    const int hl = col / NG, gl = col % NG;
-    const bool col_on = col < R;
-    const float col_mask = col_on ? 0.0f : -INFINITY;
-    const int h0 = kvh * nrep;
-
-    const int c0 = (int)((int64_t)c * a.chunk);
-    const int c1 = (int)min((int64_t)c0 + a.chunk, a.skv);
-    // rows per wavefront: half the chunk, rounded up to whole tiles
-    const int rw = ((a.chunk + 1) / 2 + TILE - 1) / TILE * TILE;
-    const int t0 = min(c0 + wave * rw, c1);
-    const int t1 = min(t0 + rw, c1);
-    const int last = t1 - 1;
-    const int ntile = (t1 - t0 + TILE - 1) / TILE;
-    const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
-    const uint32_t rows_ok = (uint32_t)a.skv;
-    const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
-    const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
-    const __amdgpu_buffer_rsrc_t mres[4] = {
-        make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
-        make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
-
-    __shared__ __align__(16) float smem_f[SMEM / 4];
-    uint16_t *meta = reinterpret_cast<uint16_t *>(smem_f) + wave * META;  // [array][group][row]
-    const Unpacker unpack = Unpacker::make();
-
-    // ---- start-up: Q, this wavefront's scale/bias and the first PF tiles
-    half8 qv[KM];
-    {
-        const int64_t qrow = ((int64_t)b * a.Hq + h0 + (col_on ? hl : 0)) * D;
-#pragma unroll
-        for (int u = 0; u < KM; ++u)
-            qv[u] = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow + 8 * (WPL * q4 + u));
-    }
-    constexpr int SEGS = RW2 / SEG;     // 16-byte segments per array
-    constexpr int MPL = 4 * SEGS / 64;  // segments per lane
-    // (a wavefront with no rows reads the chunk's first rows, 16-byte aligned, and ignores them)
-    const int mt0 = ntile > 0 ? t0 : c0;
-    uint4 mraw[MPL];
-#pragma unroll
-    for (int i = 0; i < MPL; ++i) {
-        const int sg = lane + 64 * i;
-        const int arr = sg / SEGS;
-        const int row = (sg % SEGS) * SEG;
-        mraw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mres[arr], (mt0 + row) * NG * 2, 0, 0));
-    }
-
-    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D / 2 < 2^31)
-    auto tile_base = [&](int ti) -> uint32_t {
-        return ti < ntile ? (uint32_t)(t0 + TILE * ti) * (uint32_t)(W * 4) : kNoRows;
-    };
-    uint4 kbuf[PF][2];
-    uint32_t vbuf[PF][8];
-    auto load_tile = [&](uint32_t base, uint4 (&kt)[2], uint32_t (&vt)[8]) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-            kt[blk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                kq, base + (uint32_t)(((16 * blk + col) * W + WPL * q4) * 4), 0, 0));
-        const uint32_t voff = base + (uint32_t)((4 * q4 * W + col) * 4);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + (16 * (j >> 2) + (j & 3)) * W * 4, 0, 0);
-    };
-    // slot by slot, in the order the ring refills them (see the one-wavefront kernel)
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-        __builtin_amdgcn_sched_barrier(0);
-        load_tile(tile_base(u), kbuf[u], vbuf[u]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    half8 qhi[KM];
-    float qsum = 0.0f;
-#pragma unroll
-    for (int u = 0; u < KM; ++u) {
-        const bool mine = col_on && ((WPL * q4 + u) / WPG) == gl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const _Float16 x = mine ? qv[u][kPerm[j]] : (_Float16)0.0f;
-            qsum += (float)x;
-            qhi[u][j] = x;
-        }
-    }
-    qsum = quarter_sum(qsum);
-
-#pragma unroll
-    for (int i = 0; i < MPL; ++i) {
-        const int sg = lane + 64 * i;
-        const int arr = sg / SEGS;
-        const int row = (sg % SEGS) * SEG;
-        const uint32_t w[4] = {mraw[i].x, mraw[i].y, mraw[i].z, mraw[i].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            meta[(arr * NG + (e % NG)) * RW2 + row + e / NG] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    const float cs = a.score_scale;
-    float m_run = -INFINITY, l_run = 0.0f, b_run = 0.0f;
-    float4v acc[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-        acc[m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-
-#pragma unroll 1
-    for (int kk = 0; kk < ntile; kk += PF) {
-#pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int ti = kk + u;  // tiles past the end are fully masked (see the one-wavefront kernel)
-            const bool tail = t0 + TILE * ti + TILE > t1;
-            float sc[8];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                float4v sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-                const uint4 x = kbuf[u][blk];
-#pragma unroll
-                for (int uu = 0; uu < KM; ++uu) {
-                    const uint32_t w = uu == 0 ? x.x : uu == 1 ? x.y : uu == 2 ? x.z : x.w;
-                    half2v hk[4];
-                    unpack(w, hk);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(hk[0], hk[1], hk[2], hk[3]), qhi[uu], sacc, 0, 0, 0);
-                }
-                const int lr0 = TILE * ti + 16 * blk + 4 * q4;  // wavefront-relative row
-                float ks[4], kb[4];
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(0 * NG + gl) * RW2 + lr0]), ks);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(1 * NG + gl) * RW2 + lr0]), kb);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float kb8 = fmaf(8.0f, ks[i], kb[i]);
-                    const float part = fmaf(ks[i], sacc[i], kb8 * qsum);
-                    float v = fmaf(group_sum<NG>(part), cs, col_mask);
-                    if (tail)
-                        v = (t0 + lr0 + i <= last) ? v : -INFINITY;
-                    sc[4 * blk + i] = v;
-                    mx = fmaxf(mx, v);
-                }
-            }
-            mx = quarter_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            if (ti != 0 && __builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-                const float corr = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
-                l_run *= corr;
-                b_run *= corr;
-                float4v corr_row;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    corr_row[i] = __shfl(corr, 4 * q4 + i);
-#pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    acc[m] *= corr_row;
-            }
-            m_run = m_new;
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-
-            float vs[8], vb[8];
-            {
-                const int lr0 = TILE * ti + 4 * q4;
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * RW2 + lr0]), &vs[0]);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(2 * NG + gl) * RW2 + lr0 + 16]), &vs[4]);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * RW2 + lr0]), &vb[0]);
-                h4_to_f32(*reinterpret_cast<const uint2 *>(&meta[(3 * NG + gl) * RW2 + lr0 + 16]), &vb[4]);
-            }
-            half8 phi, plo;
-            float lsum = 0.0f, bsum = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = __builtin_amdgcn_exp2f(sc[j] - m_use);
-                lsum += p;
-                bsum = fmaf(p, fmaf(8.0f, vs[j], vb[j]), bsum);
-                const float pw = p * vs[j];
-                const _Float16 hi = (_Float16)pw;
-                phi[j] = hi;
-                plo[j] = (_Float16)(pw - (float)hi);
-            }
-            l_run += lsum;
-            b_run += bsum;
-            {
-                // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
-                // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
-                uint32_t xw[4], yw[4];
-#pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    xw[jp] = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x05040100u);
-                    yw[jp] = __builtin_amdgcn_perm(vbuf[u][2 * jp + 1], vbuf[u][2 * jp], 0x07060302u);
-                }
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    half2v e[4];
-#pragma unroll
-                    for (int jp = 0; jp < 4; ++jp)
-                        e[jp] = unpack.one(m < 4 ? xw[jp] : yw[jp], m & 3);
-                    const half8 bv = cat8(e[0], e[1], e[2], e[3]);
-                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[m], 0, 0, 0);
-                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[m], 0, 0, 0);
-                }
-            }
-            load_tile(tile_base(ti + PF), kbuf[u], vbuf[u]);
-        }
-    }
-
-    // ---- wavefront 1 hands (m, l, b, acc) to wavefront 0, which merges
-    __syncthreads();  // both wavefronts are done with their scale/bias rows
-    float *xch = smem_f;
-    if (wave == 1) {
-        xch[0 * 64 + lane] = m_run;
-        xch[1 * 64 + lane] = l_run;
-        xch[2 * 64 + lane] = b_run;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            *reinterpret_cast<float4v *>(&xch[(3 + 4 * m) * 64 + 4 * lane]) = acc[m];
-    }
-    __syncthreads();
-    if (wave == 1)
-        return;
-    {
-        const float m1 = xch[0 * 64 + lane];
-        const float M = fmaxf(m_run, m1);
-        const float Mu = (M == -INFINITY) ? 0.0f : M;
-        const float f0 = __builtin_amdgcn_exp2f(m_run - Mu);  // exp2(-inf) = 0
-        const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
-        l_run = fmaf(l_run, f0, xch[1 * 64 + lane] * f1);
-        b_run = fmaf(b_run, f0, xch[2 * 64 + lane] * f1);
-        m_run = M;
-        float4v f0r, f1r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f0r[i] = __shfl(f0, 4 * q4 + i);
-            f1r[i] = __shfl(f1, 4 * q4 + i);
-        }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float4v o = *reinterpret_cast<const float4v *>(&xch[(3 + 4 * m) * 64 + 4 * lane]);
-            acc[m] = acc[m] * f0r + o * f1r;
-        }
-    }
-
-    // ---- write the partial state of this chunk
-    const float l_tot = quarter_sum(l_run);
-    const float b_tot = quarter_sum(b_run);
-    const int64_t C = a.num_chunks;
-    if (q4 == 0 && col_on && gl == 0) {
-        const int64_t o = ((int64_t)b * a.Hq + h0 + hl) * C + c;
-        a.part_m[o] = m_run * kLn2;
-        a.part_l[o] = l_tot;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * q4 + i;
-        const float bias_r = __shfl(b_tot, rr);
-        if (rr < R) {
-            const int h = rr / NG, g = rr % NG;
-            float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
-            const int word = col;
-            if (word / WPG == g) {
-                float4 lo = {acc[0][i] + bias_r, acc[1][i] + bias_r, acc[2][i] + bias_r, acc[3][i] + bias_r};
-                float4 hi = {acc[4][i] + bias_r, acc[5][i] + bias_r, acc[6][i] + bias_r, acc[7][i] + bias_r};
-                *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
-                *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
             }
         }
     }
@@ -1352,12 +1066,6 @@ void launch_one_wave(const PartialArgs &a, dim3 grid, const Launch &l)
                           0, a);
 }
 
-template <int NG>
-void launch_pair(const PartialArgs &a, dim3 grid, const Launch &l)
-{
-    hipExtLaunchKernelGGL((sdpa_partial_mfma_pair_kernel<NG, 2>), grid, dim3(128), 0, l.s, l.start, l.stop, 0, a);
-}
-
 // The one-wavefront kernel needs chunks of at most 512 rows whose scale/bias
 // segments start on 16-byte boundaries; it pays off once there are enough
 // (chunk, head) items to give every SIMD two wavefronts.
@@ -1370,12 +1078,6 @@ bool one_wave_fits(const PartialArgs &a, int D, int batch)
         return false;
     (void)batch;
     return true;
-}
-
-// The pair kernel: the one-wavefront layout rules, D = 128 and fp16 Q.
-bool pair_fits(const PartialArgs &a, int D, int q_dtype, int batch)
-{
-    return D == 128 && q_dtype == KVQ_F16 && one_wave_fits(a, D, batch);
 }
 
 // 8-bit caches: the one-wavefront kernel only
@@ -1400,16 +1102,12 @@ hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, 
         return launch_dg8<D, NG>(a, q_dtype, batch, variant, l);
     dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
     const int64_t items = (int64_t)a.num_chunks * a.Hkv * batch;
-    bool pair = variant == KVQ_KERNEL_MFMA_PAIR;
     bool one = variant == KVQ_KERNEL_MFMA_WAVE;
     if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO)
         one = one_wave_fits(a, D, batch) && items >= kOneWaveItems;
-    if ((one && !one_wave_fits(a, D, batch)) || (pair && !pair_fits(a, D, q_dtype, batch)))
+    if (one && !one_wave_fits(a, D, batch))
         return hipErrorInvalidValue;
-    if (pair) {
-        if constexpr (D == 128)
-            launch_pair<NG>(a, grid, l);
-    } else if (one) {
+    if (one) {
         if (q_dtype == KVQ_F32)
             launch_one_wave<D, NG, true, 4>(a, grid, l);
         else
@@ -1453,7 +1151,6 @@ hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int bat
 
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch) { return one_wave_fits(a, D, batch); }
 
-bool mfma_pair_ok(const PartialArgs &a, int D, int q_dtype, int batch) { return pair_fits(a, D, q_dtype, batch); }
 
 hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l)
 {

@@ -1,6 +1,6 @@
 // Phase 2 of split-K decode attention: combine per-chunk partial softmax
 // states into the output (split-K paragraph of the "turboquant-llama3.170B"
-// README: a second phase reduces the partial softmax results and must run
+// README: a second phase merges the per-chunk softmax states and has to run
 // after the first; here both are launched on one stream, which orders them).
 //
 // With M = max_c m_c:  out[d] = sum_c e^{m_c-M} acc_c[d] / sum_c e^{m_c-M} l_c.

@@ -142,12 +142,15 @@ def test_bits_validation(L):
     assert _append(L, _cache(capacity=0x7fff0000 // 128, bits=8), length=0, n=0) == OK
     assert _append(L, _cache(capacity=(0x7fff0000 // 128) + 1, bits=8), length=0, n=0) == E_SHAPE
     # 8-bit caches have one matrix-core kernel, the one-wavefront one: the
-    # four-wavefront and pair variants refuse them (the accepted variants are
+    # four-wavefront variant refuses them (the accepted variants are
     # exercised by the GPU tests; a call here that passed validation would
     # launch on placeholder pointers)
-    for k in (3, 5):
-        assert _partial(L, _cache(bits=8), kernel=k) == E_UNSUP, k
-        assert _step(L, _cache(bits=8), kernel=k) == E_UNSUP, k
+    assert _partial(L, _cache(bits=8), kernel=3) == E_UNSUP
+    assert _step(L, _cache(bits=8), kernel=3) == E_UNSUP
+    # kernel selectors outside the enum (5 named a removed variant) are invalid
+    for k in (5, 6, -1):
+        assert _partial(L, _cache(bits=8), kernel=k) == E_SHAPE, k
+        assert _partial(L, _cache(), kernel=k) == E_SHAPE, k
     # ... and it needs chunks of at most 512 rows
     assert _partial(L, _cache(bits=8), kernel=4, chunk=1024) == E_UNSUP
     assert _partial(L, _cache(bits=8), kernel=2, chunk=1024) == E_UNSUP

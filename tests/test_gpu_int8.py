@@ -245,7 +245,7 @@ def test_decode_step_fp32_inputs(length):
     check_attention(out.cpu().numpy(), oracle.sdpa(oc, length + 1, q, alpha), MFMA_REL_L2, label="int8 step fp32")
 
 
-@pytest.mark.parametrize("kernel", [kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_PAIR])
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_MFMA_SPLIT])
 def test_matrix_core_variants_refuse_int8(kernel):
     note("int8 refused by kernel=%d" % kernel)
     gc = kvq.QuantKVCache(1, 8, 128, 1024, 64, device="cuda", bits=8)

@@ -20,13 +20,13 @@ pytestmark = pytest.mark.gpu
 # about 4e-3).
 MFMA_REL_L2 = 1e-4
 REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: MFMA_REL_L2, kvq.KERNEL_MFMA: MFMA_REL_L2,
-          kvq.KERNEL_MFMA_SPLIT: MFMA_REL_L2, kvq.KERNEL_MFMA_WAVE: MFMA_REL_L2, kvq.KERNEL_MFMA_PAIR: MFMA_REL_L2}
+          kvq.KERNEL_MFMA_SPLIT: MFMA_REL_L2, kvq.KERNEL_MFMA_WAVE: MFMA_REL_L2}
 # With softmax scale 1 and normalised Q/K the scores reach O(100); their fp32
 # rounding (~sqrt(D) * 2^-24 * sum|q k|) passes undamped into the weights, so
 # the per-head L2 gate there is set one decade wider.
 REL_L2_UNSCALED = 2e-4
-KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_MFMA_PAIR, kvq.KERNEL_AUTO]
-MATRIX = (kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_MFMA_PAIR)
+KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_AUTO]
+MATRIX = (kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE)
 
 
 def _run(gc, skv, q, alpha, kernel, chunk=512):
@@ -56,16 +56,49 @@ def test_tiny(kernel):
     check_attention(out, oracle.sdpa(oc, 1024, q, alpha), REL_L2[kernel], label="tiny")
 
 
-@pytest.mark.parametrize("chunk", [512, 100])
-def test_partials_match_oracle(chunk):
-    note("sdpa partials tiny chunk=%d" % chunk)
+def _check_partials(m, l, acc, oc, skv, q, alpha, chunk, rel_l2, label):
+    """The partial state of include/kvq.h for every (head, chunk): m the
+    chunk's largest score, l the sum of exp(s - m) (so l >= 1), acc the
+    weighted value sum; compared with the oracle's float64 partials."""
+    rm, rl, racc = oracle.sdpa_partials(oc, skv, q, alpha, chunk)
+    assert np.all(np.isfinite(m)) and np.all(np.isfinite(l)) and np.all(np.isfinite(acc)), label
+    np.testing.assert_allclose(m, rm, rtol=1e-5, atol=1e-4, err_msg=label + ": chunk maximum")
+    np.testing.assert_allclose(l, rl, rtol=1e-4, err_msg=label + ": l")
+    assert np.all(l >= 1.0 - 1e-5), label + ": l below 1 (m is not the chunk maximum)"
+    check_attention(acc / l[..., None], racc / rl[..., None], rel_l2, label=label + " acc/l")
+    # the reference-free log mass m + ln l
+    np.testing.assert_allclose(m + np.log(l), rm + np.log(rl), rtol=1e-5, atol=1e-4, err_msg=label + ": m + ln l")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("skv,chunk", [(1024, 512), (1024, 100), (4096, 512), (4001, 512)])
+def test_partials_match_oracle(kernel, skv, chunk):
+    """Every kernel variant writes the partial state the header defines."""
+    note("sdpa partials llama skv=%d chunk=%d kernel=%d" % (skv, chunk, kernel))
+    q, k, v, alpha = kvq_synth.llama_layer(4096)
+    oc = _oracle_cache(k, v)
+    _, m, l, acc = _run(gpu_cache_from_oracle(oc), skv, q, alpha, kernel, chunk=chunk)
+    _check_partials(m, l, acc, oc, skv, q, alpha, chunk, REL_L2[kernel], "partials kernel=%d" % kernel)
+
+
+def test_partials_match_oracle_tiny():
+    note("sdpa partials tiny")
     q, k, v, alpha = kvq_synth.tiny_decode()
     oc = _oracle_cache(k, v)
-    _, m, l, acc = run_sdpa(gpu_cache_from_oracle(oc), 1024, q, alpha, chunk=chunk, kernel=kvq.KERNEL_VALU)
-    rm, rl, racc = oracle.sdpa_partials(oc, 1024, q, alpha, chunk)
-    np.testing.assert_allclose(m, rm, rtol=1e-5, atol=1e-5)
-    np.testing.assert_allclose(l, rl, rtol=1e-4)
-    np.testing.assert_allclose(acc / l[..., None], racc / rl[..., None], rtol=1e-3, atol=1e-4)
+    for kernel in KERNELS:
+        _, m, l, acc = _run(gpu_cache_from_oracle(oc), 1024, q, alpha, kernel, chunk=512)
+        _check_partials(m, l, acc, oc, 1024, q, alpha, 512, REL_L2[kernel], "tiny partials kernel=%d" % kernel)
+
+
+def test_partials_match_oracle_long_auto():
+    """At 65536 rows AUTO runs the one-wavefront kernel (1024 chunk items):
+    its partials for every head and chunk against the oracle's."""
+    note("sdpa partials llama 65536 auto")
+    skv = 65536
+    q, k, v, alpha = kvq_synth.llama_layer(skv)
+    gc, _, _ = _llama_gpu_cache(skv)
+    _, m, l, acc = run_sdpa(gc, skv, q, alpha)
+    _check_partials(m, l, acc, _oracle_cache(k, v), skv, q, alpha, 512, MFMA_REL_L2, "partials 64K auto")
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -141,18 +174,16 @@ def test_llama_layer(kernel, skv):
 
 
 @pytest.mark.parametrize("skv", [65536, 131072])
-def test_llama_layer_long_sampled(skv):
+def test_llama_layer_long(skv):
     """Full-size layer in the benchmark's launch configuration (chunk 512,
-    automatic kernel choice); outputs of two KV heads' query heads are
-    checked against the oracle."""
+    automatic kernel choice), the cache quantised on the GPU: every query
+    head against the oracle."""
     note("sdpa llama long skv=%d" % skv)
     q, k, v, alpha = kvq_synth.llama_layer(skv)
     gc, _, _ = _llama_gpu_cache(skv)
     out, *_ = run_sdpa(gc, skv, q, alpha)
-    heads = [0, 5]
-    ref = _sampled_oracle(k, v, q, alpha, skv, heads)
-    got = np.concatenate([out[:, h * 8:(h + 1) * 8] for h in heads], axis=1)
-    check_attention(got, ref, REL_L2[kvq.KERNEL_AUTO], label="llama-long")
+    check_attention(out, oracle.sdpa(_oracle_cache(k, v), skv, q, alpha), REL_L2[kvq.KERNEL_AUTO],
+                    label="llama-long")
 
 
 def test_outlier_decode():
