@@ -102,7 +102,8 @@ def make_pool(kvq, torch, skv: int, pool_bytes: int, chunk: int, seed: int = 123
         ws = kvq.partials_buffers(B, hq, D, skv, chunk, device=dev)
         out = torch.empty((B, hq, D), dtype=torch.float32, device=dev)
         qr = torch.empty((B, hq, D), dtype=torch.float32, device=dev)
-        pool.append(dict(cache=cache, q=q, k_new=k_new, v_new=v_new, ws=ws, out=out, qr=qr))
+        ws1 = kvq.decode_workspace(cache, hq, skv)
+        pool.append(dict(cache=cache, q=q, k_new=k_new, v_new=v_new, ws=ws, ws1=ws1, out=out, qr=qr))
     torch.cuda.synchronize()
     return pool
 
@@ -123,6 +124,10 @@ def run_steps(kvq, torch, pool, skv, chunk, kernel, n, events=None, step="fused"
     for i in range(n):
         L = pool[i % len(pool)]
         ev = events[i] if events is not None else None
+        if step == "single":
+            kvq.decode_step_single_launch(L["cache"], skv - 1, L["k_new"], L["v_new"], L["q"], alpha,
+                                          workspace=L["ws1"], out=L["out"], stream=stream, events=ev)
+            continue
         if step == "fused":
             kvq.decode_step(L["cache"], skv - 1, L["k_new"], L["v_new"], L["q"], alpha, chunk, out=L["out"],
                             workspace=L["ws"], kernel=kernel, stream=stream, events=ev)
@@ -412,7 +417,7 @@ def build_parser():
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the measurements of the rows beyond the headline path (Hadamard-rotated cache, "
                          "8-bit cache, prefill)")
-    ap.add_argument("--step", choices=["fused", "unfused", "rotated", "rotated-unfused"], default="fused",
+    ap.add_argument("--step", choices=["single", "fused", "unfused", "rotated", "rotated-unfused"], default="fused",
                     help="fused: kvq_decode_step (append inside the attention kernel, then the reduce); "
                          "unfused: append, partial and reduce as three calls")
     ap.add_argument("--layers", type=int, default=80,

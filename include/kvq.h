@@ -290,6 +290,52 @@ int kvq_decode_step_rotated(const kvq_cache *cache, int64_t len, const void *k_n
                             float *part_m, float *part_l, float *part_acc, float *out, int kernel, void *stream);
 
 /*
+ * Bytes of workspace that kvq_decode_step_single_launch needs for steps over
+ * at most max_rows cache rows (len + 1 <= max_rows) with Hq query heads; 0
+ * for an invalid cache or sizes. Grows with max_rows: a workspace sized for
+ * the longest context serves every shorter one.
+ */
+int64_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t Hq, int64_t max_rows);
+
+/*
+ * One decode step in a single kernel launch: the step of kvq_decode_step
+ * (the README's decode-step listing: quantise the token's K and V into cache
+ * row len, then attention with GQA over rows 0..len), with the split-K merge
+ * (README split-K paragraph: per-chunk softmax states, then a merge that
+ * must follow them) inside the same launch. Each workgroup streams a few
+ * consecutive chunks of one (batch, KV head), one wavefront per chunk,
+ * merges its wavefronts' states in LDS and stores one partial state in the
+ * workspace; the last workgroup of each (batch, KV head) to finish (an
+ * arrival counter in the workspace) merges those partials into out.
+ *  k_new, v_new: [B][Hkv][D], kv_dtype KVQ_F16 or KVQ_F32, 16-byte aligned.
+ *  q:            [B][Hq][D], q_dtype KVQ_F16 or KVQ_F32; out: [B][Hq][D] fp32
+ *                normalised, 16-byte aligned.
+ *  workspace:    device memory owned by the caller, 16-byte aligned, at least
+ *                kvq_decode_workspace_bytes(cache, Hq, len + 1) bytes
+ *                (KVQ_E_SHAPE otherwise). Its first 4 * B * Hkv bytes are
+ *                the arrival counters (uint32, one per (batch, KV head)):
+ *                zero them once before the first call (e.g. hipMemset);
+ *                every call leaves them at zero again. Calls that use one
+ *                workspace must not overlap in time (one stream, or ordered
+ *                by events); after a call that did not complete (a fault),
+ *                zero them again.
+ *  start_event, stop_event: optional hipEvent_t (timing enabled, either may
+ *                be NULL), recorded in the kernel's own dispatch as in
+ *                kvq_sdpa_int4_partial_timed.
+ * The matrix-core shapes of the one-wavefront kernel run in one launch
+ * (D 128 or 256, (Hq/Hkv) * (D/G) <= 16, capacity * (D/G) a multiple of 8,
+ * 4- or 8-bit codes); other shapes run as kvq_decode_step with 512-row
+ * chunks (append, partial and reduce), inside the same workspace. The cache
+ * row written is the one kvq_quantize_kv_append writes, bit for bit; out
+ * matches kvq_sdpa_int4 within the attention tolerance (the merge order
+ * differs). Validated before anything is enqueued, as kvq_decode_step.
+ */
+int kvq_decode_step_single_launch(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new,
+                                  int kv_dtype, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
+                                  void *workspace, int64_t workspace_bytes, float *out, void *stream,
+                                  void *start_event, void *stop_event);
+
+/*
  * kvq_decode_step with its attention kernel timed: start_event / stop_event
  * (hipEvent_t with timing, either may be NULL) are recorded in that kernel's
  * own dispatch, as in kvq_sdpa_int4_partial_timed (in the fused step this is

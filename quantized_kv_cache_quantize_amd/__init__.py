@@ -21,6 +21,9 @@ from ._binding import (  # noqa: F401
     QuantKVCache,
     cache_bytes,
     decode_step,
+    decode_step_single_launch,
+    decode_workspace,
+    decode_workspace_bytes,
     decode_step_rotated,
     hadamard_rotate,
     hbm_read,

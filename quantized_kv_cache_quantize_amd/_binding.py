@@ -85,6 +85,11 @@ def lib():
     L.kvq_decode_step_timed.restype = C.c_int
     L.kvq_decode_step_timed.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int,
                                         vp, vp, vp]
+    L.kvq_decode_workspace_bytes.restype = i64
+    L.kvq_decode_workspace_bytes.argtypes = [cp, i32, i64]
+    L.kvq_decode_step_single_launch.restype = C.c_int
+    L.kvq_decode_step_single_launch.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, vp, i64, vp, vp,
+                                                vp, vp]
     L.kvq_sdpa_int4_prefill.restype = C.c_int
     L.kvq_sdpa_int4_prefill.argtypes = [cp, i64, i32, vp, C.c_int, i32, f32, vp, vp]
     L.kvq_sdpa_int4.restype = C.c_int
@@ -485,4 +490,52 @@ def decode_step_rotated(cache: QuantKVCache, length: int, k_new: torch.Tensor, v
            lib().kvq_decode_step_rotated(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
                                          _ptr(q), _dtype_code(q), hq, float(softmax_scale), int(chunk), _ptr(m),
                                          _ptr(l), _ptr(acc), _ptr(out), int(kernel), _stream(stream)))
+    return out
+
+
+def decode_workspace_bytes(cache: QuantKVCache, hq: int, max_rows: int) -> int:
+    """kvq_decode_workspace_bytes: workspace bytes of decode_step_single_launch
+    for steps over at most max_rows rows."""
+    cs = cache.c_struct()
+    n = int(lib().kvq_decode_workspace_bytes(C.byref(cs), int(hq), int(max_rows)))
+    if n <= 0:
+        _fail("decode_workspace_bytes", "invalid cache or sizes (Hq %d, max_rows %d)" % (hq, max_rows))
+    return n
+
+
+def decode_workspace(cache: QuantKVCache, hq: int, max_rows: int) -> torch.Tensor:
+    """A zeroed workspace (uint8 device tensor) for decode_step_single_launch
+    over at most max_rows rows; every call leaves its counters zero again."""
+    n = decode_workspace_bytes(cache, hq, max_rows)
+    return torch.zeros((n + 15) // 16 * 16, dtype=torch.uint8, device=cache.device)
+
+
+def decode_step_single_launch(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                              q: torch.Tensor, softmax_scale: float, workspace: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None, stream=None, events=None):
+    """kvq_decode_step_single_launch: append k_new, v_new ([B][Hkv][D] or
+    [B][Hkv][1][D]) at row `length`, then attention over length + 1 rows with
+    the split-K merge inside the same launch; returns out [B][Hq][D] fp32.
+    workspace: a uint8 device tensor from decode_workspace() (zeroed once,
+    reused across calls on one stream). events: optional (start, stop)
+    torch.cuda.Event recorded in the kernel's own dispatch."""
+    fn = "decode_step_single_launch"
+    A = _Args(fn)
+    _rows_arg(A, "k_new", k_new, cache, allow_3d=True)
+    _rows_arg(A, "v_new", v_new, cache, allow_3d=True)
+    if v_new.dtype != k_new.dtype:
+        _fail(fn, "k_new and v_new must have the same dtype")
+    b, hq, d = _query_arg(A, q, cache)
+    if workspace is None:
+        workspace = decode_workspace(cache, hq, length + 1)
+    need = decode_workspace_bytes(cache, hq, length + 1)
+    A.need("workspace", workspace, None, (torch.uint8,), need)
+    out = _out_arg(A, out, b, hq, d, q.device)
+    A.devices(cache.device)
+    ev = (None, None) if events is None else (_event_handle(events[0]), _event_handle(events[1]))
+    cs = cache.c_struct()
+    _check("kvq_decode_step_single_launch",
+           lib().kvq_decode_step_single_launch(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                               _ptr(q), _dtype_code(q), hq, float(softmax_scale), _ptr(workspace),
+                                               int(workspace.numel()), _ptr(out), _stream(stream), ev[0], ev[1]))
     return out

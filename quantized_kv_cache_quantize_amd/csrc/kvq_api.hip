@@ -262,6 +262,10 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     a.rotate = 0;
     a.q_f16 = 0;
     a.rot_scale = 0.0;
+    a.merge_ws = nullptr;
+    a.counters = nullptr;
+    a.out = nullptr;
+    a.nwg = 0;
     const bool mfma_ok = mfma_supports(cache->head_dim, cache->group, n_rep, chunk) &&
                          (bits == 4 || mfma_one_wave_ok(a, cache->head_dim, cache->batch));
     if (want_mfma && !mfma_ok)
@@ -506,6 +510,83 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
                                 stream);
 }
 
+// Workspace of the single-launch decode step, for steps over at most
+// max_rows rows: per (batch, KV head) an arrival counter (padded to 256
+// bytes), then room for one merged partial per 512 rows and (batch, KV head)
+// (kMergeHeader + n_rep * D floats), which also holds the split-K partials
+// (m, l, acc, fp32) of the paths with a separate reduce.
+int64_t counter_region(const kvq_cache *c) { return ((int64_t)c->batch * c->kv_heads * 4 + 255) / 256 * 256; }
+
+int64_t workspace_bytes(const kvq_cache *c, int32_t Hq, int64_t max_rows)
+{
+    const int64_t n_rep = Hq / c->kv_heads, D = c->head_dim;
+    const int64_t blocks = (max_rows + 511) / 512;
+    const int64_t merged = kMergeHeader + n_rep * D, split = n_rep * (D + 2);
+    return counter_region(c) + (int64_t)c->batch * c->kv_heads * blocks * (merged > split ? merged : split) * 4 +
+           64;
+}
+
+// the single-launch step's workgroups write split-K partials for a separate
+// reduce launch (true) or merge them inside the launch (false)
+constexpr bool kSplitMerge = false;
+
+int single_launch_impl(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                       const void *q, int q_dtype, int32_t Hq, float softmax_scale, void *workspace, int64_t ws_bytes,
+                       float *out, const Launch &l)
+{
+    int st = check_cache(cache);
+    if (st)
+        return st;
+    if (kv_dtype != KVQ_F16 && kv_dtype != KVQ_F32)
+        return KVQ_E_DTYPE;
+    if (len < 0 || Hq < 1 || Hq % cache->kv_heads != 0)
+        return KVQ_E_SHAPE;
+    if (len >= cache->capacity)
+        return KVQ_E_CAPACITY;
+    if (!workspace || !out || !k_new || !v_new || !q)
+        return KVQ_E_NULL;
+    if (!aligned16(workspace) || !aligned16(out) || !aligned16(k_new) || !aligned16(v_new))
+        return KVQ_E_ALIGN;
+    const int64_t skv = len + 1;
+    if (ws_bytes < workspace_bytes(cache, Hq, skv))
+        return KVQ_E_SHAPE;
+    // the split-K workspace of the three-launch path, inside the same bytes
+    char *base = (char *)workspace + counter_region(cache);
+    const int64_t C = kvq_num_chunks(skv, 512);
+    const int64_t nm = ((int64_t)cache->batch * Hq * C + 3) / 4 * 4;
+    float *part_m = (float *)base, *part_l = part_m + nm, *part_acc = part_l + nm;
+    PartialPlan p;
+    st = prepare_partial(cache, skv, q, q_dtype, Hq, softmax_scale, 512, part_m, part_l, part_acc, KVQ_KERNEL_AUTO,
+                         p);
+    if (st)
+        return st;
+    int32_t rows = 0, nwg = 0;
+    const int64_t heads = (int64_t)cache->batch * cache->kv_heads;
+    if (p.use_mfma && decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, cache_bits(cache),
+                                         cache->capacity, skv, heads, rows, nwg)) {
+        p.a.chunk = rows;
+        p.a.num_chunks = (int64_t)nwg * (cache->head_dim == 128 ? 8 : 4);
+        p.a.k_new = k_new;
+        p.a.v_new = v_new;
+        p.a.append_row = len;
+        p.a.append_dtype = kv_dtype;
+        p.a.merge_ws = (float *)base;
+        p.a.counters = (uint32_t *)workspace;
+        p.a.out = out;
+        p.a.nwg = nwg;
+        if (!kSplitMerge) {  // the merge inside the launch
+            p.a.part_m = p.a.part_l = p.a.part_acc = nullptr;
+            return launch_status(launch_decode_single(p.a, cache->head_dim, q_dtype, cache->batch, l));
+        }
+        // workgroup partials as split-K partials (nwg per head), then the reduce
+        st = launch_status(launch_decode_single(p.a, cache->head_dim, q_dtype, cache->batch, l));
+        return st ? st : kvq_sdpa_int4_reduce(part_m, part_l, part_acc, cache->batch, Hq, cache->head_dim, nwg, out,
+                                              (void *)l.s);
+    }
+    return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, 512, part_m, part_l,
+                            part_acc, out, KVQ_KERNEL_AUTO, l, false);
+}
+
 }  // namespace
 
 extern "C" {
@@ -526,6 +607,23 @@ int kvq_decode_step_rotated(const kvq_cache *cache, int64_t len, const void *k_n
     const Launch l{(hipStream_t)stream, nullptr, nullptr};
     return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, chunk, part_m, part_l,
                             part_acc, out, kernel, l, true);
+}
+
+int64_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t Hq, int64_t max_rows)
+{
+    if (check_cache(cache) || Hq < 1 || Hq % cache->kv_heads != 0 || max_rows < 1)
+        return 0;
+    return workspace_bytes(cache, Hq, max_rows);
+}
+
+int kvq_decode_step_single_launch(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new,
+                                  int kv_dtype, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
+                                  void *workspace, int64_t workspace_bytes, float *out, void *stream,
+                                  void *start_event, void *stop_event)
+{
+    const Launch l{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return single_launch_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, workspace,
+                              workspace_bytes, out, l);
 }
 
 int kvq_decode_step_timed(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,

@@ -81,9 +81,26 @@ struct PartialArgs {
     int32_t rotate;
     int32_t q_f16;
     double rot_scale;
+    // Single-launch decode step (workgroups of several wavefronts, each
+    // streaming `chunk` rows): each workgroup merges its wavefronts' states
+    // and stores them as partial wg of its (batch, KV head) in merge_ws
+    // (kMergeHeader + n_rep * D tagged 64-bit words: (m, l) pairs in log2
+    // units, then the value sums) and takes a ticket from
+    // counters[2 (b Hkv + kvh)]; the workgroup with the last ticket merges
+    // all nwg partials into out, sets the counter back to zero and advances
+    // the epoch in counters[2 (b Hkv + kvh) + 1].
+    float *merge_ws;
+    uint32_t *counters;
+    float *out;
+    int32_t nwg;
 };
 
 constexpr int32_t kRotateRows = 1, kRotateQuery = 2;
+// words before the value sums in a merged partial: (m, l) of up to 16 heads
+constexpr int kMergeHeader = 32;
+// most workgroups per (batch, KV head) in the single-launch step (longer
+// contexts take the three-launch step)
+constexpr int kMaxMergeGroups = 256;
 
 struct ReduceArgs {
     const float *part_m;
@@ -139,6 +156,12 @@ hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int bat
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch);
 // the fused decode step: append (a.append_row) + partial with the one-wavefront kernel
 hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l);
+// the single-launch decode step: rows per wavefront and workgroups per
+// (batch, KV head) for a step over skv rows, or false if the shape does not
+// take it
+bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t skv, int64_t heads, int32_t &rows,
+                        int32_t &nwg);
+hipError_t launch_decode_single(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
 }  // namespace kvq

@@ -438,7 +438,7 @@ __device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvr
 {
     constexpr int W = D / 8;     // lanes per row (eight values each)
     constexpr int LPG = W / NG;  // lanes per scale group
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const bool active = lane < 2 * W;
     const int which = lane / W;  // 0: K, 1: V
     const int w = lane % W;
@@ -485,8 +485,185 @@ __device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvr
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
-template <int D, int NG, bool Q32, int PF, int BITS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
+// Merges of the decode step's multi-wavefront workgroups, run by all
+// 64 * WG threads of a workgroup after each wavefront has put its state (m
+// in log2 units, l, and the D value sums of each of its nrep query heads)
+// into LDS, heads MAXH apart. 1) The workgroup merges its wavefronts' states
+// into one partial state. Then either
+//  - (a.part_acc set) it stores that state as split-K partial blockIdx.x
+//    of a.nwg, for the reduce kernel launched after it; or
+//  - the split-K merge of the README's split-K paragraph happens inside the
+//    same launch: 2) the workgroup stores its partial in a.merge_ws, waits
+//    until the stores are complete and takes a ticket from its (batch, KV
+//    head) arrival counter; all but the last of the a.nwg workgroups are
+//    then done; 3) the last one reads the other partials, merges them with
+//    its own (kept in registers) into the normalised output and sets the
+//    counter back to zero. The partials cross workgroups, and the chip's
+//    separate L2 caches, as device-scope atomic stores and loads (coherent
+//    at the device's memory side); a store is complete before its
+//    workgroup's ticket is taken, and every load of the last workgroup is
+//    issued after its own ticket came back, after every other ticket.
+// Elements are handled in pairs of adjacent dimensions (one 64-bit access).
+template <int D, int NG, int WG>
+__device__ __forceinline__ void merge_epilogue(const PartialArgs &a, int b, int kvh, int nrep, const float *ml_s,
+                                               const float *acc_s)
+{
+    constexpr int NT1 = 64 * WG;
+    constexpr int MAXH = 16 / NG;
+    constexpr int EP = (MAXH * D / 2 + NT1 - 1) / NT1;  // dimension pairs per thread, at most
+    constexpr int PB = 32 / EP;                         // partials per batch of loads (128 registers)
+    const int tid = threadIdx.x;
+    const int64_t bh = (int64_t)b * a.Hkv + kvh;
+    const int nwg = a.nwg;
+    const int npair = nrep * D / 2;
+    __syncthreads();  // every wavefront's state is in LDS
+
+    // 1) this workgroup's partial: per head the largest m, then every
+    //    wavefront's state weighted by exp2(m_w - M) (0 for one without rows)
+    float2 own[EP];
+    float own_m[EP], own_l[EP];  // of each pair's head
+#pragma unroll
+    for (int k = 0; k < EP; ++k) {
+        const int pr = tid + k * NT1;
+        own[k] = make_float2(0.0f, 0.0f);
+        own_m[k] = -INFINITY;
+        own_l[k] = 0.0f;
+        if (pr < npair) {
+            const int h = 2 * pr / D, d = 2 * pr % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < WG; ++w)
+                M = fmaxf(M, ml_s[(w * MAXH + h) * 2]);
+            float2 sum = make_float2(0.0f, 0.0f);
+            float L = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WG; ++w) {
+                const float f = __builtin_amdgcn_exp2f(ml_s[(w * MAXH + h) * 2] - M);
+                const float2 v = *reinterpret_cast<const float2 *>(acc_s + (w * MAXH + h) * D + d);
+                sum.x = fmaf(f, v.x, sum.x);
+                sum.y = fmaf(f, v.y, sum.y);
+                L = fmaf(f, ml_s[(w * MAXH + h) * 2 + 1], L);
+            }
+            own[k] = sum;
+            own_m[k] = M;
+            own_l[k] = L;
+        }
+    }
+
+    if (a.part_acc) {  // split-K partial blockIdx.x of nwg, m in natural-log units
+        const int64_t C = nwg;
+        const int64_t o = ((int64_t)b * a.Hq + (int64_t)kvh * nrep) * C + blockIdx.x;
+#pragma unroll
+        for (int k = 0; k < EP; ++k) {
+            const int pr = tid + k * NT1;
+            if (pr < npair) {
+                const int h = 2 * pr / D, d = 2 * pr % D;
+                *reinterpret_cast<float2 *>(a.part_acc + (o + h * C) * D + d) = own[k];
+                if (d == 0) {
+                    a.part_m[o + h * C] = own_m[k] * kLn2;
+                    a.part_l[o + h * C] = own_l[k];
+                }
+            }
+        }
+        return;
+    }
+
+    // 2) the partial into the workspace: [nwg][kMergeHeader + nrep D] words,
+    //    (m, l) pairs of the heads first, then the value sums
+    const int stride = kMergeHeader + nrep * D;
+    uint64_t *ws = reinterpret_cast<uint64_t *>(a.merge_ws + bh * nwg * (int64_t)stride);  // 8-byte words
+    uint64_t *mine = ws + (int64_t)blockIdx.x * (stride / 2);
+#pragma unroll
+    for (int k = 0; k < EP; ++k) {
+        const int pr = tid + k * NT1;
+        if (pr < npair) {
+            __hip_atomic_store(mine + kMergeHeader / 2 + pr, __builtin_bit_cast(uint64_t, own[k]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (2 * pr % D == 0)
+                __hip_atomic_store(mine + 2 * pr / D, __builtin_bit_cast(uint64_t, make_float2(own_m[k], own_l[k])),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the stores are complete
+    __shared__ uint32_t ticket;
+    __syncthreads();
+    if (tid == 0)
+        ticket = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket != (uint32_t)nwg - 1)
+        return;
+
+    // 3) the last workgroup: out = sum_p exp2(m_p - M) acc_p / sum_p exp2(m_p - M) l_p,
+    //    the partials taken in index order (so the result does not depend on
+    //    which workgroup came last), PB at a time with every load of a batch
+    //    issued before the first is used
+    float M[EP], L[EP];
+    float2 acc[EP];
+#pragma unroll
+    for (int k = 0; k < EP; ++k) {
+        M[k] = -INFINITY;
+        L[k] = 0.0f;
+        acc[k] = make_float2(0.0f, 0.0f);
+    }
+    const int me = blockIdx.x;
+    for (int p0 = 0; p0 < nwg; p0 += PB) {
+        float2 ml[PB][EP], av[PB][EP];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const uint64_t *src = ws + (int64_t)min(p0 + u, nwg - 1) * (stride / 2);
+#pragma unroll
+            for (int k = 0; k < EP; ++k) {
+                const int pr = min(tid + k * NT1, npair - 1);
+                ml[u][k] = __builtin_bit_cast(
+                    float2, __hip_atomic_load(src + 2 * pr / D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                av[u][k] = __builtin_bit_cast(
+                    float2, __hip_atomic_load(src + kMergeHeader / 2 + pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < EP; ++k) {
+            float Mn = M[k];
+#pragma unroll
+            for (int u = 0; u < PB; ++u)
+                if (p0 + u < nwg)
+                    Mn = fmaxf(Mn, p0 + u == me ? own_m[k] : ml[u][k].x);
+            const float r = __builtin_amdgcn_exp2f(M[k] - Mn);  // 0 while M is -inf (Mn is finite)
+            L[k] *= r;
+            acc[k].x *= r;
+            acc[k].y *= r;
+#pragma unroll
+            for (int u = 0; u < PB; ++u)
+                if (p0 + u < nwg) {
+                    const bool self = p0 + u == me;
+                    const float f = __builtin_amdgcn_exp2f((self ? own_m[k] : ml[u][k].x) - Mn);
+                    const float2 v = self ? own[k] : av[u][k];
+                    L[k] = fmaf(f, self ? own_l[k] : ml[u][k].y, L[k]);
+                    acc[k].x = fmaf(f, v.x, acc[k].x);
+                    acc[k].y = fmaf(f, v.y, acc[k].y);
+                }
+            M[k] = Mn;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < EP; ++k) {
+        const int pr = tid + k * NT1;
+        if (pr < npair) {
+            const int h = 2 * pr / D, d = 2 * pr % D;
+            *reinterpret_cast<float2 *>(a.out + ((int64_t)b * a.Hq + (int64_t)kvh * nrep + h) * D + d) =
+                make_float2(acc[k].x / L[k], acc[k].y / L[k]);
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// WG wavefronts per workgroup. WG = 1: the split-K partial kernel, one
+// (chunk, KV head, batch) per workgroup, its state written as that chunk's
+// partial. WG > 1: the single-launch decode step, WG consecutive chunks of
+// one (KV head, batch) per workgroup, merged in LDS, then across workgroups
+// by the last one to arrive (merge_epilogue).
+template <int D, int NG, bool Q32, int PF, int BITS, int WG = 1>
+__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
 void sdpa_partial_mfma1_kernel(PartialArgs a)
 {
     // BITS = 8: byte codes, two words per eight dimensions, both K and V
@@ -514,10 +691,11 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     constexpr bool GV = D == 128 && NG == 2;
     constexpr float LS = GV ? kLoScale : 1.0f;  // scale of the lo weight halves
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = WG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
     const int q4 = lane >> 4;
     const int col = lane & 15;
-    const int c = blockIdx.x;
+    const int c = blockIdx.x * WG + wave;  // this wavefront's chunk of rows
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
     const int nrep = a.n_rep;
@@ -556,7 +734,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     //   y: b_k * c, or (b_k + 128 s_k) * c (the bias of centred 8-bit codes)
     //   z: s_v * WS
     //   w: b_v + VC s_v       (bias of the value codes centred by VC)
-    __shared__ __align__(16) float4 mring[2][PAIRS];
+    __shared__ __align__(16) float4 mring_all[WG][2][PAIRS];
+    float4 (&mring)[2][PAIRS] = mring_all[wave];
     const Unpacker unpack = Unpacker::make();
     const uint32_t m_fine = opaque_s_if<!B8>(0x00F000F0u);  // int4 K operands
     // 8-bit K operands: the magic exponent bytes (src0 bytes 4-7 of a permute)
@@ -973,84 +1152,110 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         }
     }
 
-    // ---- write the partial state of this chunk, against the head's true
-    // maximum: the weights so far are relative to m_run, and the largest of
-    // them is exp2(top) with top in [-kHeadroom, 0], so l and the products
-    // are multiplied by exp2(-top) (a factor in [1, 2^kHeadroom]) and
-    // m = m_run + top
+    // ---- this wavefront's state against the head's true maximum: the
+    // weights so far are relative to m_run, and the largest of them is
+    // exp2(top) with top in [-kHeadroom, 0], so l and the products are
+    // multiplied by exp2(-top) (a factor in [1, 2^kHeadroom]) and the state's
+    // maximum is m = m_run + top. emit() stores it through m_at(h) (m in
+    // units of m_unit per log2 unit, then l) and acc_at(h) (the D value sums)
+    // for the query heads h of this KV head.
     const float top = xrow_max(m_top, -INFINITY);
     const float renorm = __builtin_amdgcn_exp2f(-top);
     const float l_tot = xrow_sum(l_run) * renorm;
     const float b_tot = xrow_sum(b_run) * renorm;
-    const int64_t C = a.num_chunks;
-    if (q4 == 0 && col_on && gl == 0) {
-        const int64_t o = ((int64_t)b * a.Hq + h0 + hl) * C + c;
-        a.part_m[o] = (m_run + top) * kLn2;
-        a.part_l[o] = l_tot;
-    }
-    if constexpr (GV) {
-        // Row i = h + 8 e of the value products sits in lanes of q4 = i / 4:
-        // lanes l < 32 hold the hi rows, lanes l ^ 32 the lo rows (scaled by
-        // kLoScale) of the same heads 4 (q4 & 1) + r. One swap of lanes 32-63
-        // of group 0's value with lanes 0-31 of group 1's leaves (hi, lo) of
-        // group 0 in lanes 0-31 and of group 1 in lanes 32-63, so that
-        // hi + lo / kLoScale is group g = q4 / 2.
-        // Group g's products of this lane are dimensions 8 col + 0..3 when
-        // its own V word is in group g, else 8 (col ^ 8) + 4..7.
-        const int g = q4 >> 1;
-        const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
-        float o[4][4];  // [r][mm]
+    auto emit = [&](auto m_at, auto l_at, auto acc_at, float m_unit) {
+        if (q4 == 0 && col_on && gl == 0) {
+            *m_at(hl) = (m_run + top) * m_unit;
+            *l_at(hl) = l_tot;
+        }
+        if constexpr (GV) {
+            // Row i = h + 8 e of the value products sits in lanes of q4 =
+            // i / 4: lanes l < 32 hold the hi rows, lanes l ^ 32 the lo rows
+            // (scaled by kLoScale) of the same heads 4 (q4 & 1) + r. One swap
+            // of lanes 32-63 of group 0's value with lanes 0-31 of group 1's
+            // leaves (hi, lo) of group 0 in lanes 0-31 and of group 1 in
+            // lanes 32-63, so that hi + lo / kLoScale is group g = q4 / 2.
+            // Group g's products of this lane are dimensions 8 col + 0..3
+            // when its own V word is in group g, else 8 (col ^ 8) + 4..7.
+            const int g = q4 >> 1;
+            const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
+            float o[4][4];  // [r][mm]
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
+            for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // (elements go through scalars: a bit cast of a vector
+                    // element in place reads element 0)
+                    const float e0 = acc[0][mm][r], e1 = acc[0][4 + mm][r];
+                    const uint32_t a0 = __builtin_bit_cast(uint32_t, e0);
+                    const uint32_t a1 = __builtin_bit_cast(uint32_t, e1);
+                    // the swap leaves lanes 0-31 of both operands (the hi
+                    // rows) in the first result and lanes 32-63 (the lo rows)
+                    // in the second
+                    const auto sw = __builtin_amdgcn_permlane32_swap(a0, a1, false, false);
+                    const uint32_t x = sw[0], y = sw[1];
+                    o[r][mm] = fmaf(__builtin_bit_cast(float, y), VU / kLoScale, __builtin_bit_cast(float, x) * VU);
+                }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                // (elements go through scalars: a bit cast of a vector
-                // element in place reads element 0)
-                const float e0 = acc[0][mm][r], e1 = acc[0][4 + mm][r];
-                const uint32_t a0 = __builtin_bit_cast(uint32_t, e0);
-                const uint32_t a1 = __builtin_bit_cast(uint32_t, e1);
-                // the swap leaves lanes 0-31 of both operands (the hi rows)
-                // in the first result and lanes 32-63 (the lo rows) in the
-                // second
-                const auto sw = __builtin_amdgcn_permlane32_swap(a0, a1, false, false);
-                const uint32_t x = sw[0], y = sw[1];
-                o[r][mm] = fmaf(__builtin_bit_cast(float, y), VU / kLoScale, __builtin_bit_cast(float, x) * VU);
+                const int h = 4 * (q4 & 1) + r;
+                const float bias = __shfl(b_tot, h + 8 * g);
+                const float f = __shfl(renorm, h + 8 * g);
+                if (h < nrep)
+                    *reinterpret_cast<float4 *>(acc_at(h) + d0) =
+                        make_float4(fmaf(o[r][0], f, bias), fmaf(o[r][1], f, bias), fmaf(o[r][2], f, bias),
+                                    fmaf(o[r][3], f, bias));
             }
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = 4 * (q4 & 1) + r;
-            const float bias = __shfl(b_tot, h + 8 * g);
-            const float f = __shfl(renorm, h + 8 * g);
-            if (h < nrep) {
-                float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
-                *reinterpret_cast<float4 *>(dst + d0) = make_float4(fmaf(o[r][0], f, bias), fmaf(o[r][1], f, bias),
-                                                                    fmaf(o[r][2], f, bias), fmaf(o[r][3], f, bias));
-            }
-        }
-        return;
-    }
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 4 * q4 + i;
+                const float bias_r = __shfl(b_tot, rr);
+                const float f = __shfl(renorm, rr);
+                if (rr < R) {
+                    const int h = rr / NG, g = rr % NG;
+                    float *dst = acc_at(h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * q4 + i;
-        const float bias_r = __shfl(b_tot, rr);
-        const float f = __shfl(renorm, rr);
-        if (rr < R) {
-            const int h = rr / NG, g = rr % NG;
-            float *dst = a.part_acc + (((int64_t)b * a.Hq + h0 + h) * C + c) * D;
-#pragma unroll
-            for (int s = 0; s < VS; ++s) {
-                const int word = 16 * s + col;
-                if (word / WPG == g) {
-                    const float fu = f * VU;
-                    float4 lo = {fmaf(acc[s][0][i], fu, bias_r), fmaf(acc[s][1][i], fu, bias_r),
-                                 fmaf(acc[s][2][i], fu, bias_r), fmaf(acc[s][3][i], fu, bias_r)};
-                    float4 hi = {fmaf(acc[s][4][i], fu, bias_r), fmaf(acc[s][5][i], fu, bias_r),
-                                 fmaf(acc[s][6][i], fu, bias_r), fmaf(acc[s][7][i], fu, bias_r)};
-                    *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
-                    *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
+                    for (int s = 0; s < VS; ++s) {
+                        const int word = 16 * s + col;
+                        if (word / WPG == g) {
+                            const float fu = f * VU;
+                            float4 lo = {fmaf(acc[s][0][i], fu, bias_r), fmaf(acc[s][1][i], fu, bias_r),
+                                         fmaf(acc[s][2][i], fu, bias_r), fmaf(acc[s][3][i], fu, bias_r)};
+                            float4 hi = {fmaf(acc[s][4][i], fu, bias_r), fmaf(acc[s][5][i], fu, bias_r),
+                                         fmaf(acc[s][6][i], fu, bias_r), fmaf(acc[s][7][i], fu, bias_r)};
+                            *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
+                            *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
+                        }
+                    }
                 }
             }
         }
+    };
+
+    if constexpr (WG == 1) {
+        // the split-K partial state of chunk c (m in natural-log units)
+        const int64_t C = a.num_chunks;
+        const int64_t o = ((int64_t)b * a.Hq + h0) * C + c;
+        emit([&](int h) { return a.part_m + o + h * C; }, [&](int h) { return a.part_l + o + h * C; },
+             [&](int h) { return a.part_acc + (o + h * C) * D; }, kLn2);
+    } else {
+        // the wavefront's state into LDS (m in log2 units), then the merges
+        constexpr int MAXH = 16 / NG;
+        __shared__ __align__(16) float mg_ml[WG][MAXH][2];
+        __shared__ __align__(16) float mg_acc[WG][MAXH][D];
+        if (t0 >= a.skv) {  // uniform: a wavefront past the last row holds no state
+            for (int e = lane; e < nrep * D; e += 64)
+                mg_acc[wave][e / D][e % D] = 0.0f;
+            if (lane < nrep) {
+                mg_ml[wave][lane][0] = -INFINITY;
+                mg_ml[wave][lane][1] = 0.0f;
+            }
+        } else {
+            emit([&](int h) { return &mg_ml[wave][h][0]; }, [&](int h) { return &mg_ml[wave][h][1]; },
+                 [&](int h) { return &mg_acc[wave][h][0]; }, 1.0f);
+        }
+        merge_epilogue<D, NG, WG>(a, b, kvh, nrep, &mg_ml[0][0][0], &mg_acc[0][0][0]);
     }
 }
 
@@ -1157,6 +1362,78 @@ hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int bat
     if (!one_wave_fits(a, D, batch) || a.append_row < 0)
         return hipErrorInvalidValue;
     return launch_partial_mfma(a, D, q_dtype, batch, KVQ_KERNEL_MFMA_WAVE, l);
+}
+
+// Single-launch decode step. Workgroups of WG wavefronts (two per SIMD of
+// one CU at D = 128, one at D = 256), each wavefront streaming `rows` rows;
+// rows is the largest of 512, 256, 128 that still gives at least two
+// wavefronts per SIMD of the 256-CU chip (at 64K rows of the Llama layer:
+// 256), so short contexts trade longer streams for more of them.
+constexpr int64_t kSingleWaves = 2048;
+
+template <int D>
+constexpr int single_wg() { return D == 128 ? 8 : 4; }
+
+bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t skv, int64_t heads, int32_t &rows,
+                        int32_t &nwg)
+{
+    if (!mfma_supports(D, G, n_rep, 512) || (bits != 4 && bits != 8) || skv < 1 || heads < 1)
+        return false;
+    const int NG = D / G;
+    if ((cap * NG) % 8 != 0)
+        return false;
+    int r = 512;
+    while (r > 128 && heads * ((skv + r - 1) / r) < kSingleWaves)
+        r /= 2;
+    const int wg = D == 128 ? single_wg<128>() : single_wg<256>();
+    const int64_t n = (skv + (int64_t)wg * r - 1) / ((int64_t)wg * r);
+    if (n > kMaxMergeGroups || (r * NG) % 8 != 0)
+        return false;
+    rows = r;
+    nwg = (int32_t)n;
+    return true;
+}
+
+template <int D, int NG, bool Q32, int BITS>
+void launch_single(const PartialArgs &a, dim3 grid, const Launch &l)
+{
+    constexpr int WG = single_wg<D>();
+    hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, 2, BITS, WG>), grid, dim3(64 * WG), 0, l.s, l.start,
+                          l.stop, 0, a);
+}
+
+template <int D, int NG>
+hipError_t launch_single_dg(const PartialArgs &a, int q_dtype, int batch, const Launch &l)
+{
+    const dim3 grid((unsigned)a.nwg, (unsigned)a.Hkv, (unsigned)batch);
+    if (a.bits == 8) {
+        if (q_dtype == KVQ_F32)
+            launch_single<D, NG, true, 8>(a, grid, l);
+        else
+            launch_single<D, NG, false, 8>(a, grid, l);
+    } else {
+        if (q_dtype == KVQ_F32)
+            launch_single<D, NG, true, 4>(a, grid, l);
+        else
+            launch_single<D, NG, false, 4>(a, grid, l);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_single(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l)
+{
+    if (!a.merge_ws || !a.counters || !a.out || a.nwg < 1 || a.chunk > CH1)
+        return hipErrorInvalidValue;
+    const int NG = D / a.G;
+    if (D == 128) {
+        if (NG == 1) return launch_single_dg<128, 1>(a, q_dtype, batch, l);
+        if (NG == 2) return launch_single_dg<128, 2>(a, q_dtype, batch, l);
+        if (NG == 4) return launch_single_dg<128, 4>(a, q_dtype, batch, l);
+    } else if (D == 256) {
+        if (NG == 2) return launch_single_dg<256, 2>(a, q_dtype, batch, l);
+        if (NG == 4) return launch_single_dg<256, 4>(a, q_dtype, batch, l);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kvq

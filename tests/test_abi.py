@@ -309,3 +309,33 @@ def test_hbm_read_validation(L):
     assert rd(P, -16, 0, P + 4096, None) == E_SHAPE
     assert rd(P + 8, 1024, 0, P + 4096, None) == E_ALIGN
     assert rd(P, 1024, 0, P + 4098, None) == E_ALIGN
+
+
+def _single(L, cache, length=100, k=P, v=P, kvd=0, q=P, qd=0, hq=64, scale=0.1, ws=P, ws_bytes=1 << 30, out=P):
+    return L.kvq_decode_step_single_launch(C.byref(cache) if cache is not None else None, length, k, v, kvd, q, qd,
+                                           hq, scale, ws, ws_bytes, out, None, None, None)
+
+
+def test_single_launch_step_validation(L):
+    ws = lambda c, hq, rows: L.kvq_decode_workspace_bytes(C.byref(c), hq, rows)  # noqa: E731
+    c = _cache(capacity=131072)
+    # grows with the rows it serves; holds one merged partial per 512 rows and head
+    assert ws(c, 64, 1) > 256 and ws(c, 64, 512) == ws(c, 64, 1)
+    assert ws(c, 64, 513) > ws(c, 64, 512)
+    assert ws(c, 64, 131072) >= 256 + 8 * 256 * (32 + 8 * 128) * 4
+    assert ws(c, 63, 100) == 0 and ws(c, 0, 100) == 0 and ws(c, 64, 0) == 0
+    assert ws(_cache(head_dim=96), 64, 100) == 0
+    assert _single(L, None) == E_NULL
+    assert _single(L, c, ws=None) == E_NULL
+    assert _single(L, c, out=None) == E_NULL
+    assert _single(L, c, q=None) == E_NULL
+    assert _single(L, c, ws=P + 8) == E_ALIGN
+    assert _single(L, c, k=P + 4) == E_ALIGN
+    assert _single(L, c, kvd=3) == E_DTYPE
+    assert _single(L, c, qd=3) == E_DTYPE
+    assert _single(L, c, hq=60) == E_SHAPE
+    assert _single(L, c, length=-1) == E_SHAPE
+    assert _single(L, c, length=131072) == E_CAP
+    # a workspace one byte short of what the step over length + 1 rows needs
+    assert _single(L, c, length=4095, ws_bytes=ws(c, 64, 4096) - 1) == E_SHAPE
+    assert _single(L, c, scale=float("inf")) == E_SHAPE
