@@ -254,16 +254,25 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
  * token's K and V into the cache, then the fused int4 attention with GQA):
  * writes k_new / v_new ([B][Hkv][D], kv_dtype, one row per (batch, KV head))
  * into cache row `len` with the rule of kvq_quantize_kv_append, then
- * computes out over the len + 1 rows 0..len exactly as kvq_sdpa_int4 would.
- * When the one-wavefront matrix-core kernel is the one that runs (kernel
- * MFMA_WAVE, or AUTO / MFMA with at least 1024 (chunk, KV head, batch) items),
- * the append runs inside the attention kernel, in the wavefront that owns the
- * last chunk, so the step is two launches (attention, reduce) instead of
- * three (8-bit caches: whenever that kernel takes the chunk layout);
- * otherwise it is the three calls in order. Results are the same either way (cache bit for bit, out as
- * kvq_sdpa_int4 with that kernel). All arguments are validated before anything
- * is enqueued: len + 1 <= capacity (else KVQ_E_CAPACITY), k_new, v_new and out
- * 16-byte aligned, the partials workspace sized for C = ceil((len+1)/chunk).
+ * computes out over the len + 1 rows 0..len as kvq_sdpa_int4 would.
+ * When the one-wavefront matrix-core kernel takes the shape, the append runs
+ * inside the attention kernel, in the wavefront that owns the new row, so the
+ * step is two launches (attention, reduce) instead of three:
+ *  - AUTO / MFMA: workgroups of eight wavefronts (four at D = 256), each
+ *    wavefront streaming every eighth 32-row tile of the workgroup's rows
+ *    (512 / 256 / 128 rows per wavefront, the most that still gives two
+ *    wavefronts per SIMD), merged in LDS into one partial per workgroup, so
+ *    the reduce reads at most as many partials as there are chunks; out
+ *    matches kvq_sdpa_int4 within the attention tolerance (a different
+ *    split of the rows);
+ *  - MFMA_WAVE (or AUTO / MFMA where the partials would outnumber the
+ *    chunks): one wavefront per chunk; out is kvq_sdpa_int4's with that
+ *    kernel, bit for bit (also for 8-bit caches).
+ * Otherwise it is the three calls in order. The cache row is bit for bit
+ * the append's either way. All arguments are validated before anything is
+ * enqueued: len + 1 <= capacity (else KVQ_E_CAPACITY), k_new, v_new and out
+ * 16-byte aligned, the partials workspace sized for C = ceil((len+1)/chunk)
+ * (its contents after the call are the step's own partials).
  */
 int kvq_decode_step(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
                     const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *part_m,

@@ -489,7 +489,23 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
                 return st;
             p.a.q = out;
         }
-        st = launch_status(launch_decode_fused(p.a, cache->head_dim, launch_q_dtype, cache->batch, l));
+        // AUTO / MFMA: the multi-wavefront workgroups of the single-launch
+        // step, each writing one split-K partial for its rows (fewer partials
+        // for the reduce: at most the caller's chunk count)
+        int32_t rows = 0, nwg = 0;
+        const bool wide = (kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) &&
+                          decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, p.a.bits,
+                                             cache->capacity, len + 1, (int64_t)cache->batch * cache->kv_heads, rows,
+                                             nwg) &&
+                          nwg <= p.a.num_chunks;
+        if (wide) {
+            p.a.chunk = rows;
+            p.a.nwg = nwg;
+            p.a.num_chunks = nwg;
+            st = launch_status(launch_decode_single(p.a, cache->head_dim, launch_q_dtype, cache->batch, l));
+        } else {
+            st = launch_status(launch_decode_fused(p.a, cache->head_dim, launch_q_dtype, cache->batch, l));
+        }
     } else {
         if (rotate) {
             RotateArgs ra{q, out, (int64_t)cache->batch * Hq, cache->head_dim, 1.0 / sqrt((double)cache->head_dim)};
@@ -525,10 +541,6 @@ int64_t workspace_bytes(const kvq_cache *c, int32_t Hq, int64_t max_rows)
     return counter_region(c) + (int64_t)c->batch * c->kv_heads * blocks * (merged > split ? merged : split) * 4 +
            64;
 }
-
-// the single-launch step's workgroups write split-K partials for a separate
-// reduce launch (true) or merge them inside the launch (false)
-constexpr bool kSplitMerge = false;
 
 int single_launch_impl(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
                        const void *q, int q_dtype, int32_t Hq, float softmax_scale, void *workspace, int64_t ws_bytes,
@@ -574,14 +586,8 @@ int single_launch_impl(const kvq_cache *cache, int64_t len, const void *k_new, c
         p.a.counters = (uint32_t *)workspace;
         p.a.out = out;
         p.a.nwg = nwg;
-        if (!kSplitMerge) {  // the merge inside the launch
-            p.a.part_m = p.a.part_l = p.a.part_acc = nullptr;
-            return launch_status(launch_decode_single(p.a, cache->head_dim, q_dtype, cache->batch, l));
-        }
-        // workgroup partials as split-K partials (nwg per head), then the reduce
-        st = launch_status(launch_decode_single(p.a, cache->head_dim, q_dtype, cache->batch, l));
-        return st ? st : kvq_sdpa_int4_reduce(part_m, part_l, part_acc, cache->batch, Hq, cache->head_dim, nwg, out,
-                                              (void *)l.s);
+        p.a.part_m = p.a.part_l = p.a.part_acc = nullptr;  // the merge inside the launch
+        return launch_status(launch_decode_single(p.a, cache->head_dim, q_dtype, cache->batch, l));
     }
     return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, 512, part_m, part_l,
                             part_acc, out, KVQ_KERNEL_AUTO, l, false);

@@ -710,12 +710,21 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     const int h0 = kvh * nrep;
     const bool low8 = (lane & 8) == 0;  // GV: this lane's V word is in group 0
 
-    const int t0 = (int)((int64_t)c * a.chunk);
-    const int t1 = (int)min((int64_t)t0 + a.chunk, a.skv);
+    // Rows of this wavefront: tiles of TILE rows from t0, TS * TILE apart,
+    // below t1. WG = 1: the chunk [c * chunk, (c + 1) * chunk). WG > 1: the
+    // workgroup's WG * chunk rows, its wavefronts taking every WG-th tile
+    // (at any time the workgroup streams one region of each array instead of
+    // WG of them).
+    constexpr int TS = WG;
+    const int t0 = WG == 1 ? (int)((int64_t)c * a.chunk)
+                           : (int)((int64_t)blockIdx.x * WG * a.chunk) + TILE * wave;
+    const int t1 = WG == 1 ? (int)min((int64_t)t0 + a.chunk, a.skv)
+                           : (int)min((int64_t)(blockIdx.x + 1) * WG * a.chunk, a.skv);
     const int last = t1 - 1;
-    const int ntile = (t1 - t0 + TILE - 1) / TILE;
+    const int ntile = t1 > t0 ? (t1 - t0 + TS * TILE - 1) / (TS * TILE) : 0;
     const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
-    if (a.append_row >= t0 && a.append_row < t1)  // uniform: the fused decode step's new row is in this chunk
+    // uniform: the fused decode step's new row is in one of this wavefront's tiles
+    if (a.append_row >= t0 && a.append_row < t1 && ((a.append_row - t0) / TILE) % TS == 0)
         append_new_row<D, NG, BITS>(a, b, kvh, kvrow0);
     const uint32_t rows_ok = (uint32_t)a.skv;
     const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
@@ -802,12 +811,12 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 #pragma unroll
         for (int p = 0; p < MP; ++p) {
             const int pr = (lane + 64 * p) % PAIRS;
-            const uint32_t off = in ? (uint32_t)((t0 + TILE * ti) * NG + pr) * 2u : kNoRows;
+            const uint32_t off = in ? (uint32_t)((t0 + TS * TILE * ti) * NG + pr) * 2u : kNoRows;
 #pragma unroll
             for (int arr = 0; arr < 4; ++arr)
                 mt[p][arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], off, 0, 0);
         }
-        const uint32_t base = in ? (uint32_t)(t0 + TILE * ti) * (uint32_t)(W * 4) : kNoRows;
+        const uint32_t base = in ? (uint32_t)(t0 + TS * TILE * ti) * (uint32_t)(W * 4) : kNoRows;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + WPL * q4) * 4);
@@ -975,11 +984,11 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                     sc[4 * blk + i] = GV ? sg + dpp_f<0x128>(sg) : group_sum<NG>(sg);  // row_ror:8
                 }
             }
-            if (t0 + TILE * ti + TILE > t1) {  // uniform: the chunk's last tiles
+            if (t0 + TS * TILE * ti + TILE > t1) {  // uniform: the chunk's last tiles
                 asm volatile("" ::: "memory");  // keep this a branch
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int r = t0 + TILE * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
+                    const int r = t0 + TS * TILE * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
                     sc[i] = r <= last ? sc[i] : -INFINITY;
                 }
             }
@@ -1244,7 +1253,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
         constexpr int MAXH = 16 / NG;
         __shared__ __align__(16) float mg_ml[WG][MAXH][2];
         __shared__ __align__(16) float mg_acc[WG][MAXH][D];
-        if (t0 >= a.skv) {  // uniform: a wavefront past the last row holds no state
+        if (ntile <= 0) {  // uniform: a wavefront past the last row holds no state
             for (int e = lane; e < nrep * D; e += 64)
                 mg_acc[wave][e / D][e % D] = 0.0f;
             if (lane < nrep) {
@@ -1422,7 +1431,9 @@ hipError_t launch_single_dg(const PartialArgs &a, int q_dtype, int batch, const 
 
 hipError_t launch_decode_single(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l)
 {
-    if (!a.merge_ws || !a.counters || !a.out || a.nwg < 1 || a.chunk > CH1)
+    // the merge inside the launch needs its workspace and the output; split-K
+    // partials (part_acc set) go to the reduce launched after this kernel
+    if (a.nwg < 1 || a.chunk > CH1 || (!a.part_acc && (!a.merge_ws || !a.counters || !a.out)))
         return hipErrorInvalidValue;
     const int NG = D / a.G;
     if (D == 128) {

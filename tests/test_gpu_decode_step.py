@@ -1,10 +1,12 @@
 """GPU parity of the decode step (kvq_decode_step): append the current
 token's K/V row, then attention over the rows up to and including it.
 
-The fused path (append inside the one-wavefront attention kernel) must leave
-the cache bit for bit as kvq_quantize_kv_append does and give the same output,
-bit for bit, as the separate calls with the same kernel; both are also checked
-against the float64 oracle."""
+The fused path (append inside the attention kernel) must leave the cache bit
+for bit as kvq_quantize_kv_append does. With a forced one-wavefront kernel its
+output equals the separate calls with the same kernel bit for bit; with AUTO
+(the eight-wavefront workgroups, another split of the rows) it matches them
+within the attention tolerance. Both are also checked against the float64
+oracle."""
 
 import numpy as np
 import pytest
@@ -47,7 +49,10 @@ def _step_and_compare(q, k, v, alpha, length, cap, kernel=kvq.KERNEL_AUTO, G=64)
     oc.append(kn, vn, length)
     assert_cache_equal(g1, oc)
     got = out1.cpu().numpy()
-    assert np.array_equal(got, out2.cpu().numpy()), "decode step differs from the separate calls"
+    if kernel in (kvq.KERNEL_AUTO, kvq.KERNEL_MFMA):
+        check_attention(got, out2.cpu().numpy(), REL_L2, label="decode step vs separate calls len=%d" % length)
+    else:
+        assert np.array_equal(got, out2.cpu().numpy()), "decode step differs from the separate calls"
     check_attention(got, oracle.sdpa(oc, length + 1, q, alpha), REL_L2, label="decode step len=%d" % length)
 
 

@@ -203,9 +203,10 @@ def test_closer_to_float_attention_than_int4():
 @pytest.mark.parametrize("length", [0, 511, 512, 1000])
 def test_decode_step(kernel, length):
     """Append + attention in one call on the 8-bit cache (the append inside
-    the one-wavefront kernel, or append, vector-ALU partial and reduce):
-    cache bit for bit as the append alone, output bit for bit as the
-    separate calls with the same kernel, and near the oracle."""
+    the matrix-core kernel, or append, vector-ALU partial and reduce): cache
+    bit for bit as the append alone, output bit for bit as the separate calls
+    with a forced kernel (within the tolerance with AUTO), and near the
+    oracle."""
     note("int8 decode step len=%d kernel=%d" % (length, kernel))
     q, k, v, alpha = kvq_synth.llama_layer(length + 1)
     cap = 1024 + 8
@@ -223,7 +224,10 @@ def test_decode_step(kernel, length):
     oc.append(kn, vn, length)
     assert_cache_equal(g1, oc)
     got = out1.cpu().numpy()
-    assert np.array_equal(got, out2.cpu().numpy())
+    if kernel in (kvq.KERNEL_AUTO, kvq.KERNEL_MFMA):  # another split of the rows
+        check_attention(got, out2.cpu().numpy(), GATE[kernel], label="int8 step vs separate calls")
+    else:
+        assert np.array_equal(got, out2.cpu().numpy())
     check_attention(got, oracle.sdpa(oc, length + 1, q, alpha), GATE[kernel], label="int8 step")
 
 
