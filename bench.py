@@ -367,6 +367,131 @@ def time_prefill(kvq, torch, q_start: int, sq: int, reps: int = 5, bits: int = 4
     return sorted(per)[len(per) // 2]
 
 
+GEMMA_SKVS = (33, 423, 786, 950, 8192)  # the Gemma page's decode contexts and the 8K case
+GEMMA_HQ, GEMMA_HKV, GEMMA_D = 32, 16, 256
+
+
+def gemma_bytes(skv: int) -> int:
+    return GEMMA_HKV * skv * (GEMMA_D // 2 + 4 * (GEMMA_D // G)) * 2  # int4 codes + fp16 scale/bias, K and V
+
+
+def time_gemma_decode(kvq, torch, skv: int, steps: int, warmup: int, pool_bytes: int, max_layers: int = 64):
+    """Decode steps (kvq_decode_step, AUTO) on the Gemma-style layer: batch 1,
+    32 query heads on 16 KV heads, head_dim 256, softmax scale 1, Q and K
+    rows at unit RMS times a per-channel gain ~U(0.5, 2) (one gain vector
+    each), V ~N(0,1), all drawn on the GPU from a seed and quantised by the
+    library; over a pool of distinct layers (>= pool_bytes, at most
+    max_layers). Returns (us per step, pool layers)."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31 * skv + 7)
+    gq = torch.rand((GEMMA_D,), generator=gen, device=dev) * 1.5 + 0.5
+    gk = torch.rand((GEMMA_D,), generator=gen, device=dev) * 1.5 + 0.5
+
+    def rms_gain(x, gain):
+        return x / x.pow(2).mean(dim=-1, keepdim=True).sqrt() * gain
+
+    n_layers = max(2, min(max_layers, math.ceil(pool_bytes / gemma_bytes(skv))))
+    pool = []
+    for _ in range(n_layers):
+        cache = kvq.QuantKVCache(B, GEMMA_HKV, GEMMA_D, skv, G, device=dev)
+        k = rms_gain(torch.randn((B, GEMMA_HKV, skv, GEMMA_D), generator=gen, device=dev), gk).half()
+        v = torch.randn((B, GEMMA_HKV, skv, GEMMA_D), generator=gen, device=dev).half()
+        kvq.quantize_kv_append(cache, 0, k[:, :, :skv - 1].contiguous(), v[:, :, :skv - 1].contiguous())
+        q = rms_gain(torch.randn((B, GEMMA_HQ, GEMMA_D), generator=gen, device=dev), gq).contiguous()
+        kn, vn = k[:, :, skv - 1].contiguous(), v[:, :, skv - 1].contiguous()
+        ws = kvq.partials_buffers(B, GEMMA_HQ, GEMMA_D, skv, 512, device=dev)
+        out = torch.empty((B, GEMMA_HQ, GEMMA_D), dtype=torch.float32, device=dev)
+        pool.append((cache, q, kn, vn, ws, out))
+        del k, v
+    stream = torch.cuda.current_stream()
+
+    def run(n):
+        for i in range(n):
+            cache, q, kn, vn, ws, out = pool[i % len(pool)]
+            kvq.decode_step(cache, skv - 1, kn, vn, q, 1.0, 512, out=out, workspace=ws, stream=stream)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del pool
+    return us, n_layers
+
+
+def time_outlier_append_decode(kvq, torch, steps: int, warmup: int, reps: int = 40):
+    """The append + decode workload: 4096 new fp16 rows per KV head with
+    outlier-heavy K (Student-t with 3 degrees of freedom, as Z / sqrt(chi2_3 / 3),
+    and 4 channels per KV head scaled by 20, the same channels for every row;
+    V ~N(0,1)) appended at row 61440 of a 65536-row Llama-layout cache, then
+    decode steps over all 65536 rows. Returns (append us, decode us)."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4096)
+
+    def student_t(shape):
+        z = torch.randn(shape, generator=gen, device=dev)
+        chi2 = torch.randn((3,) + tuple(shape), generator=gen, device=dev).pow(2).sum(0)
+        return z / (chi2 / 3).sqrt()
+
+    chans = torch.stack([torch.randperm(D, generator=gen, device=dev)[:4] for _ in range(HKV)])
+    boost = torch.ones((HKV, D), device=dev)
+    boost[torch.arange(HKV, device=dev)[:, None], chans] = 20.0
+    n_inputs = 8
+    inputs = []
+    for _ in range(n_inputs):
+        k = (student_t((B, HKV, APPEND_ROWS, D)) * boost[None, :, None, :]).clamp(-60000, 60000).half()
+        v = torch.randn((B, HKV, APPEND_ROWS, D), generator=gen, device=dev).half()
+        inputs.append((k, v))
+    cache = kvq.QuantKVCache(B, HKV, D, APPEND_CAP, G, device=dev)
+    for t0 in range(0, APPEND_LEN, APPEND_ROWS):
+        k, v = inputs[(t0 // APPEND_ROWS) % n_inputs]
+        kvq.quantize_kv_append(cache, t0, k, v)
+    torch.cuda.synchronize()
+    # the append, captured in a graph (one kernel per call) and replayed
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(reps):
+                kvq.quantize_kv_append(cache, APPEND_LEN, *inputs[i % n_inputs])
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps)
+    append_us = sorted(per)[len(per) // 2] * 1e3
+    del graph
+    # decode steps over the 65536 rows (the last row rewritten by each step)
+    q = torch.randn((B, HQ, D), generator=gen, device=dev).half()
+    kn, vn = inputs[0][0][:, :, 0].contiguous(), inputs[0][1][:, :, 0].contiguous()
+    ws = kvq.partials_buffers(B, HQ, D, APPEND_CAP, 512, device=dev)
+    out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+    alpha = 1.0 / math.sqrt(D)
+    for _ in range(warmup):
+        kvq.decode_step(cache, APPEND_CAP - 1, kn, vn, q, alpha, 512, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        kvq.decode_step(cache, APPEND_CAP - 1, kn, vn, q, alpha, 512, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    decode_us = e0.elapsed_time(e1) * 1e3 / steps
+    del inputs, cache
+    return append_us, decode_us
+
+
 def bulk_append_bytes(bits: int = 4) -> int:
     rows = B * HKV * APPEND_ROWS
     return 2 * rows * D * 2 + 2 * rows * (D * bits // 8 + 4 * (D // G))  # fp16 K and V in, packed rows out
@@ -427,6 +552,9 @@ def build_parser():
     ap.add_argument("--repeats", type=int, default=10,
                     help="after the timed steps, time the same steps again as this many separate runs "
                          "(median / p10 / p90 of the per-step time; 0 skips)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' timings (Gemma-style decode at 33..8192 rows, the outlier "
+                         "append + 64K decode pair, the single-launch step)")
     ap.add_argument("--no-hbm-calibration", action="store_true",
                     help="skip the plain read of 1 GiB that gives the achievable HBM bandwidth")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -572,6 +700,51 @@ def main():
             roofline="mfma: algorithmic flops 4 * Hq * D * (rows each position sees), dense fp16 peak 2500 TFLOP/s",
             timing="median of 5 calls, events around each (one kernel of milliseconds)", **pf)
 
+    workloads = None
+    if not args.no_workloads:
+        gem = []
+        for gs in GEMMA_SKVS:
+            us, nl = time_gemma_decode(kvq, torch, gs, max(20, args.steps // 2), args.warmup, pool_bytes)
+            gb = gemma_bytes(gs)
+            gem.append({"skv": gs, "us_per_step": round(us, 3), "gbs": round(gb / (us * 1e-6) / 1e9, 2),
+                        "frac_of_hbm_peak": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "pool_layers": nl})
+        app_us, dec_us = time_outlier_append_decode(kvq, torch, max(20, args.steps // 2), args.warmup)
+        ab = bulk_append_bytes()
+        db = layer_bytes(APPEND_CAP)
+        single_res, _ = time_config(kvq, torch, args.skv, args.chunk, kernel, max(20, args.steps // 2), args.warmup,
+                                    pool_bytes, step="single", bits=bits)
+        sb = layer_bytes(args.skv, bits) + append_bytes(bits)
+        workloads = {
+            "gemma_decode": {
+                "workload": "Gemma-style unscaled decode layer: B1 Hq32 Hkv16 D256, softmax scale 1, Q/K rows at "
+                            "unit RMS x per-channel gain U(0.5,2), V N(0,1); kvq_decode_step (AUTO) at each "
+                            "context; bytes = int4 K+V codes + fp16 scale/bias (4608 B per row)",
+                "timing": "events around max(20, steps/2) steps over a pool of distinct layers (<= 64; the "
+                          "short contexts then sit in the 256 MB last-level cache: latency-bound)",
+                "points": gem},
+            "outlier_append_decode": {
+                "workload": "append of 4096 fp16 rows per KV head (Llama layout B1 Hkv8 D128 G64; K Student-t(3) "
+                            "with 4 channels per KV head x20, V N(0,1)) at row 61440 of a 65536-row int4 cache, "
+                            "then kvq_decode_step (AUTO, Hq 64) over all 65536 rows",
+                "append_us": round(app_us, 3),
+                "append_bytes": ab,
+                "append_gbs": round(ab / (app_us * 1e-6) / 1e9, 2),
+                "append_frac_of_hbm_peak": round(ab / (app_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "decode_us": round(dec_us, 3),
+                "decode_gbs": round(db / (dec_us * 1e-6) / 1e9, 2),
+                "decode_frac_of_hbm_peak": round(db / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "pair_us": round(app_us + dec_us, 3),
+                "timing": "append: 40 calls on 8 input sets captured in a HIP graph, median of 5 replays; "
+                          "decode: events around max(20, steps/2) steps on the one cache"},
+            "single_launch_step": {
+                "workload": "the headline layer and step through kvq_decode_step_single_launch (the split-K "
+                            "merge inside the attention launch)",
+                "us_per_layer": round(single_res["ms_per_step"] * 1e3, 3),
+                "gbs": round(sb / (single_res["ms_per_step"] * 1e-3) / 1e9, 2),
+                "frac_of_hbm_peak": round(sb / (single_res["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernel_us": round(single_res["partial_ms_avg"] * 1e3, 3)},
+        }
+
     step_bytes = layer_bytes(args.skv, bits) + append_bytes(bits)
     ms = main_res["ms_per_step"]
     value = step_bytes / (ms * 1e-3) / 1e9
@@ -640,6 +813,7 @@ def main():
         "sweep_note": ("us_per_layer: steps issued one by one from Python; us_per_layer_graph: one pass over "
                        "the same pool captured in a HIP graph and replayed (the host out of the loop)"),
         "full_depth": depth,
+        "workloads": workloads,
         "next_rows": next_rows,
         "context": "pages' Apple-Silicon fused-kernel latency on this shape: 1.6/2.7/5.7/9.9 ms at 1K/16K/64K/128K",
     }
