@@ -16,8 +16,10 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library
- *    never allocates, frees or synchronises, and keeps no global state; it is
- *    safe to call from several threads.
+ *    never allocates, frees or synchronises, and keeps no global state, with
+ *    one exception: kvq_decode_step_noalloc's static device scratch and the
+ *    address it looks up once per GPU. It is safe to call from several
+ *    threads.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued asynchronously on it; calls on one stream run in order,
  *    so the reduce launched after the partial kernel on the same stream sees
@@ -66,8 +68,12 @@ typedef enum kvq_status {
     KVQ_E_CAPACITY = -4,    /* rows beyond the cache capacity */
     KVQ_E_DTYPE = -5,       /* unknown element type */
     KVQ_E_LAUNCH = -6,      /* the HIP runtime rejected a launch */
-    KVQ_E_UNSUPPORTED = -7  /* valid request that no kernel variant handles */
+    KVQ_E_UNSUPPORTED = -7, /* valid request that no kernel variant handles */
+    KVQ_E_SCRATCH = -8      /* kvq_decode_step_noalloc: partials beyond its static scratch */
 } kvq_status;
+
+/* Bytes of the static device scratch that kvq_decode_step_noalloc uses. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
 
 typedef enum kvq_dtype { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
 
@@ -343,6 +349,26 @@ int kvq_decode_step_single_launch(const kvq_cache *cache, int64_t len, const voi
                                   int kv_dtype, const void *q, int q_dtype, int32_t Hq, float softmax_scale,
                                   void *workspace, int64_t workspace_bytes, float *out, void *stream,
                                   void *start_event, void *stop_event);
+
+/*
+ * kvq_decode_step for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step, arguments and results, but its split-K partials live in a static
+ * device array of KVQ_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds
+ * on each GPU it runs on until the process ends, so the caller passes no
+ * workspace. The request must fit it: B * Hq * C * (D + 2) floats, C =
+ * ceil((len + 1) / chunk), with m and l each rounded up to 64 floats (the
+ * Llama layer, B 1, Hq 64, D 128, chunk 512: up to 258,048 rows); larger ones
+ * return KVQ_E_SCRATCH before anything is enqueued. Nothing is allocated:
+ * on its first call on a device, with that device current, the call looks
+ * up the array's device address once and keeps it. Every call on one GPU
+ * shares the array (it holds the last call's partials, all written before
+ * they are read within a call), so calls that overlap in time on one GPU
+ * race: issue them on one stream or order them.
+ */
+int kvq_decode_step_noalloc(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                            const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *out,
+                            int kernel, void *stream);
 
 /*
  * kvq_decode_step with its attention kernel timed: start_event / stop_event

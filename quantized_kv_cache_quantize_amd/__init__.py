@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     QuantKVCache,
     cache_bytes,
     decode_step,
+    decode_step_noalloc,
     decode_step_single_launch,
     decode_workspace,
     decode_workspace_bytes,

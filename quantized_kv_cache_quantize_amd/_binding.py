@@ -85,6 +85,8 @@ def lib():
     L.kvq_decode_step_timed.restype = C.c_int
     L.kvq_decode_step_timed.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, vp, vp, vp, C.c_int,
                                         vp, vp, vp]
+    L.kvq_decode_step_noalloc.restype = C.c_int
+    L.kvq_decode_step_noalloc.argtypes = [cp, i64, vp, vp, C.c_int, vp, C.c_int, i32, f32, i32, vp, C.c_int, vp]
     L.kvq_decode_workspace_bytes.restype = i64
     L.kvq_decode_workspace_bytes.argtypes = [cp, i32, i64]
     L.kvq_decode_step_single_launch.restype = C.c_int
@@ -538,4 +540,28 @@ def decode_step_single_launch(cache: QuantKVCache, length: int, k_new: torch.Ten
            lib().kvq_decode_step_single_launch(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
                                                _ptr(q), _dtype_code(q), hq, float(softmax_scale), _ptr(workspace),
                                                int(workspace.numel()), _ptr(out), _stream(stream), ev[0], ev[1]))
+    return out
+
+
+def decode_step_noalloc(cache: QuantKVCache, length: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                        softmax_scale: float, chunk: int = 512, out: torch.Tensor | None = None,
+                        kernel: int = KERNEL_AUTO, stream=None):
+    """kvq_decode_step_noalloc: kvq_decode_step with its partials in the
+    library's static device scratch (no workspace; the library allocates
+    nothing). Pass `out` to allocate nothing here either; returns out
+    [B][Hq][D] fp32."""
+    fn = "decode_step_noalloc"
+    A = _Args(fn)
+    _rows_arg(A, "k_new", k_new, cache, allow_3d=True)
+    _rows_arg(A, "v_new", v_new, cache, allow_3d=True)
+    if v_new.dtype != k_new.dtype:
+        _fail(fn, "k_new and v_new must have the same dtype")
+    b, hq, d = _query_arg(A, q, cache)
+    out = _out_arg(A, out, b, hq, d, q.device)
+    A.devices(cache.device)
+    cs = cache.c_struct()
+    _check("kvq_decode_step_noalloc",
+           lib().kvq_decode_step_noalloc(C.byref(cs), int(length), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                         _ptr(q), _dtype_code(q), hq, float(softmax_scale), int(chunk), _ptr(out),
+                                         int(kernel), _stream(stream)))
     return out

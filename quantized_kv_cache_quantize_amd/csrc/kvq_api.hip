@@ -5,6 +5,8 @@
 // needing one).
 #include <math.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -73,6 +75,8 @@ const char *kvq_status_str(int status)
         return "kernel launch failed";
     case KVQ_E_UNSUPPORTED:
         return "shape not supported by the requested kernel";
+    case KVQ_E_SCRATCH:
+        return "request needs more than the library's static scratch";
     default:
         return "unknown status";
     }
@@ -593,6 +597,33 @@ int single_launch_impl(const kvq_cache *cache, int64_t len, const void *k_new, c
                             part_acc, out, KVQ_KERNEL_AUTO, l, false);
 }
 
+// Scratch of kvq_decode_step_noalloc: a file-scope device array (each GPU
+// that loads the library holds its own copy until the process ends). Host
+// code never uses the array's name as an address: on first use on a device,
+// with that device current, its device address is looked up once and kept
+// per device (g_scratch), and kernels receive that pointer.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxDevices] = {};
+
+int noalloc_scratch(float **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return KVQ_E_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return KVQ_E_LAUNCH;
+        g_scratch[dev] = static_cast<float *>(ptr);
+    }
+    *out = g_scratch[dev];
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -630,6 +661,32 @@ int kvq_decode_step_single_launch(const kvq_cache *cache, int64_t len, const voi
     const Launch l{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
     return single_launch_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, workspace,
                               workspace_bytes, out, l);
+}
+
+int kvq_decode_step_noalloc(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
+                            const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk, float *out,
+                            int kernel, void *stream)
+{
+    int st = check_cache(cache);
+    if (st)
+        return st;
+    if (len < 0 || chunk < 1 || Hq < 1 || Hq % cache->kv_heads != 0)
+        return KVQ_E_SHAPE;
+    if (len >= cache->capacity)
+        return KVQ_E_CAPACITY;
+    // the split-K partials of kvq_decode_step, laid out in the scratch array
+    const int64_t C = kvq_num_chunks(len + 1, chunk);
+    const int64_t nm = ((int64_t)cache->batch * Hq * C + 63) / 64 * 64;  // floats of m (and of l), 256-byte multiple
+    const int64_t nacc = (int64_t)cache->batch * Hq * C * cache->head_dim;
+    if ((2 * nm + nacc) * 4 > KVQ_NOALLOC_SCRATCH_BYTES)
+        return KVQ_E_SCRATCH;
+    float *base = nullptr;
+    st = noalloc_scratch(&base);
+    if (st)
+        return st;
+    const Launch l{(hipStream_t)stream, nullptr, nullptr};
+    return decode_step_impl(cache, len, k_new, v_new, kv_dtype, q, q_dtype, Hq, softmax_scale, chunk, base, base + nm,
+                            base + 2 * nm, out, kernel, l, false);
 }
 
 int kvq_decode_step_timed(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,

@@ -17,7 +17,7 @@ from quantized_kv_cache_quantize_amd import _binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
 
-OK, E_NULL, E_SHAPE, E_ALIGN, E_CAP, E_DTYPE, E_LAUNCH, E_UNSUP = 0, -1, -2, -3, -4, -5, -6, -7
+OK, E_NULL, E_SHAPE, E_ALIGN, E_CAP, E_DTYPE, E_LAUNCH, E_UNSUP, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 P = 0x100000  # placeholder "device" address, 16-byte aligned; never dereferenced
 
 
@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert "gfx950" in B.version()
-    for s in (OK, E_NULL, E_SHAPE, E_ALIGN, E_CAP, E_DTYPE, E_LAUNCH, E_UNSUP):
+    for s in (OK, E_NULL, E_SHAPE, E_ALIGN, E_CAP, E_DTYPE, E_LAUNCH, E_UNSUP, E_SCRATCH):
         assert B.status_str(s) and B.status_str(s) != "unknown status"
     assert B.status_str(12345) == "unknown status"
 
@@ -339,3 +339,24 @@ def test_single_launch_step_validation(L):
     # a workspace one byte short of what the step over length + 1 rows needs
     assert _single(L, c, length=4095, ws_bytes=ws(c, 64, 4096) - 1) == E_SHAPE
     assert _single(L, c, scale=float("inf")) == E_SHAPE
+
+
+def _noalloc(L, cache, length=100, hq=64, chunk=512):
+    return L.kvq_decode_step_noalloc(C.byref(cache) if cache is not None else None, length, P, P, 0, P, 0, hq, 0.1,
+                                     chunk, P, 0, None)
+
+
+def test_noalloc_step_validation(L):
+    """Requests beyond the 16 MiB static scratch are refused before anything
+    touches the device (these calls never reach a launch)."""
+    c = _cache(capacity=1 << 20)
+    assert _noalloc(L, None) == E_NULL
+    assert _noalloc(L, c, length=-1) == E_SHAPE
+    assert _noalloc(L, c, chunk=0) == E_SHAPE
+    assert _noalloc(L, c, hq=60) == E_SHAPE
+    assert _noalloc(L, c, length=1 << 20) == E_CAP
+    # Llama layer, chunk 512: 258048 rows fit, one more chunk does not
+    assert _noalloc(L, c, length=258048) == E_SCRATCH
+    assert _noalloc(L, c, length=300000) == E_SCRATCH
+    # smaller chunks need more partials for the same rows
+    assert _noalloc(L, c, length=100000, chunk=64) == E_SCRATCH

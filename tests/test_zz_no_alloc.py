@@ -1,0 +1,62 @@
+"""kvq_decode_step_noalloc, the decode step for callers that cannot allocate
+(its partials in the library's static device scratch), through the C ABI:
+two calls in a row, the second over fewer rows, each against the existing
+kvq_decode_step with a workspace on its own copy of the cache (the same
+kernels: the cache row and the output bit for bit), and against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+import oracle
+import quantized_kv_cache_quantize_amd as kvq
+from _gpu_common import assert_cache_equal, check_attention, gpu_cache_from_oracle, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(skv, bits):
+    q, k, v, alpha = kvq_synth.llama_layer(skv)
+    length = skv - 1
+    oc = oracle.Cache(1, 8, 128, skv, 64, bits=bits)
+    oc.append(np.ascontiguousarray(k[:, :, :length]), np.ascontiguousarray(v[:, :, :length]), 0)
+    kn = np.ascontiguousarray(k[:, :, length:length + 1])
+    vn = np.ascontiguousarray(v[:, :, length:length + 1])
+    return q, alpha, oc, kn, vn, length
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_noalloc_matches_decode_step(bits):
+    # the second call is the smaller one; both run on the one scratch array
+    for skv in (131072, 20000):
+        note("noalloc decode step skv=%d bits=%d" % (skv, bits))
+        q, alpha, oc, kn, vn, length = _case(skv, bits)
+        g1, g2 = gpu_cache_from_oracle(oc), gpu_cache_from_oracle(oc)
+        qd, knd, vnd = to_dev(q), to_dev(kn), to_dev(vn)
+        out1 = torch.full((1, 64, 128), float("nan"), device="cuda")
+        kvq.decode_step_noalloc(g1, length, knd, vnd, qd, alpha, out=out1)
+        out2 = kvq.decode_step(g2, length, knd, vnd, qd, alpha)
+        torch.cuda.synchronize()
+        oc.append(kn, vn, length)
+        assert_cache_equal(g1, oc)
+        assert_cache_equal(g2, oc)
+        assert torch.equal(out1, out2), "no-alloc step differs from kvq_decode_step (skv %d)" % skv
+        check_attention(out1.cpu().numpy(), oracle.sdpa(oc, skv, q, alpha), 1e-4, label="noalloc skv=%d" % skv)
+
+
+def test_noalloc_refuses_beyond_scratch():
+    """A request whose partials exceed the static scratch returns
+    KVQ_E_SCRATCH before anything is enqueued (the cache is left as it was)."""
+    note("noalloc refuses an oversized request")
+    rows = 258048 + 512
+    g = kvq.QuantKVCache(1, 8, 128, rows, 64, device="cuda")
+    x = torch.zeros((1, 8, 128), dtype=torch.float16, device="cuda")
+    q = torch.zeros((1, 64, 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_step_noalloc(g, rows - 1, x, x, q, 0.1)
+    assert e.value.status == -8
+    # the largest request that fits is accepted
+    out = kvq.decode_step_noalloc(g, 258047, x, x, q, 0.1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
