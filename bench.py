@@ -40,15 +40,17 @@ B, HQ, HKV, D, G = 1, 64, 8, 128, 64
 
 TRAFFIC_FILES = {
     4: os.path.join(ROOT, "profiles", "sdpa_partial_llama_128k_traffic.txt"),
-    8: os.path.join(ROOT, "profiles", "sdpa_partial_int8_llama_128k_traffic.txt"),
+    8: os.path.join(ROOT, "profiles", "sdpa_partial_int8_llama_128k_traffic.txt"),  # absent until profiled
 }
 
 
-def measured_traffic(skv: int, chunk: int, kernel: str, bits: int = 4):
-    """HBM bytes per partial launch from the committed counter summary, or
-    None when this run is not the profiled configuration or the kernel
-    sources changed since the counters were taken (their hash differs)."""
-    if skv != 131072 or chunk != 512 or kernel not in ("auto", "mfma", "mfma-wave"):
+def measured_traffic(skv: int, chunk: int, kernel: str, bits: int = 4, step: str = "fused"):
+    """HBM bytes per attention launch of the decode step from the committed
+    counter summary, or None when this run is not the profiled configuration
+    (the Llama layer at 131072 rows, chunk 512, kvq_decode_step with AUTO or
+    MFMA) or the kernel sources changed since the counters were taken (their
+    hash differs)."""
+    if skv != 131072 or chunk != 512 or kernel not in ("auto", "mfma") or step != "fused":
         return None
     path = TRAFFIC_FILES[bits]
     try:
@@ -790,12 +792,15 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "sdpa_partial (attention kernel of the step; in the fused step it also appends the row)",
+            "kernel": ("sdpa_partial_mfma1_kernel<128, 2, false, 2, 4, 8> (the decode step's attention launch: "
+                       "eight-wavefront workgroups, appends the row, one merged partial per workgroup)"
+                       if args.step == "fused" and args.kernel in ("auto", "mfma") else
+                       "the attention launch of the step (also appends the row in the fused steps)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.skv, args.chunk, args.kernel, bits),
+            "traffic": measured_traffic(args.skv, args.chunk, args.kernel, bits, args.step),
             "bytes_per_launch": layer_bytes(args.skv, bits),
             "avg_launch_us": round(main_res["partial_ms_avg"] * 1e3, 3),
             "timing": "HIP events recorded in the kernel's own dispatch (hipExtLaunchKernel), averaged over the steps",

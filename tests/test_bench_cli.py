@@ -49,8 +49,7 @@ def test_profile_commands_parse():
         sys.path.remove(ROOT)
     cmds = _profile_bench_commands()
     names = {name for name, _ in cmds}
-    assert {"sdpa_partial_mfma_wave_llama_128k.md", "sdpa_partial_int8_mfma_wave_llama_128k.md",
-            "sdpa_prefill_llama_int4.md", "sdpa_partial_valu_llama_128k.md"} <= names
+    assert {"sdpa_decode_wg8_llama_128k.md", "sdpa_prefill_llama_int4.md", "sdpa_partial_valu_llama_128k.md"} <= names
     for name, args in cmds:
         try:
             bench.build_parser().parse_args(args)
