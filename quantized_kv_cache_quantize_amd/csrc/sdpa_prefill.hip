@@ -7,35 +7,30 @@
 // q_start + i; its K/V row is cache row q_start + i (appended before the
 // call), and it attends to rows [0, q_start + i] (causal).
 //
-// Work split: one wavefront per (32 / n_rep query positions x the n_rep heads
-// of a KV head, batch), streaming the rows its positions can see in 32-row
-// tiles. With GQA the n_rep heads of a KV head and the block's positions all
-// read the same rows, so every K/V tile is fetched and unpacked once for 32
-// query columns (two blocks of 16, each the N side of its own matrix
-// instructions).
+// Work split: a wavefront takes 32 / n_rep query positions x the n_rep heads
+// of a KV head (32 query columns: two blocks of 16, each the N side of its
+// own matrix instructions) and streams the rows its positions can see in
+// 32-row tiles. With GQA the n_rep heads of a KV head and the block's
+// positions all read the same rows, so every K/V tile is fetched and
+// unpacked once for all the columns of a wavefront (and, in the int4 D = 128
+// kernel, once for the four wavefronts of a workgroup).
 //
 // Scores (per tile): S^T[t][c] = Kcodes[t][:] . Q[c][:] on
 // v_mfma_f32_16x16x32_f16, A = K codes (16 rows, 32 dimensions), B = the
 // queries of a 16-column block. A lane loads the K words of its row strided
 // by 4 words, so each instruction's 32 dimensions lie in one scale group and
-// the group's scale and bias apply in fp32 afterwards (the factored form of
-// the Gemma page's "What I Built Instead"): s = sum_g s_g (q . code)_g +
-// b_g (sum q)_g. K codes enter as the fp16 subnormals n * 2^-20, as in the
-// decode kernel.
-//
-// Values: O[c][d] += P'_g[c][t] . Vcodes[t][d] per scale group g, with the
-// weights p * s_v of group g as hi and lo fp16 halves (lo scaled by 2^11) in
-// separate accumulators, and the value codes centred by 8 (one accumulator
-// per output across all the rows: with normal centred operands its error on
-// the outlier workload's 65536 rows matches that of fp32 flushes every 512
-// rows, measured). A lane's value
-// word holds eight dimensions of one group; the operand of group g takes the
-// four dimensions it lacks from lane l ^ 8 with a bank-masked DPP move (the
-// layout of the decode kernel's two-group path).
+// the group's scale applies in fp32 afterwards (the factored form of the
+// Gemma page's "What I Built Instead"): s = sum_g s_g (q . code)_g +
+// b_g (sum q)_g.
 //
 // Softmax: per query column, relative to a reference raised (with headroom)
 // only when a score exceeds it, as in the decode kernel; the output is
 // normalised in the kernel (no split over rows, so no partial state).
+//
+// Three kernels: 8-bit codes (sdpa_prefill_b8_kernel: per-group value
+// weights, the layout the int4 kernels started from), int4 at D = 256
+// (sdpa_prefill_i4_kernel) and int4 at D = 128 (sdpa_prefill_i4_wg_kernel,
+// the same arithmetic with the tile's operands shared by a workgroup).
 
 #include "kvq_internal.h"
 #include "mfma_common.h"
@@ -45,46 +40,42 @@ namespace {
 
 constexpr int PT = 32;  // rows per tile
 
-// D = 128, two scale groups of 64, fp16 queries, int4 codes; NB blocks of
-// 16 query columns per wavefront (every unpacked K and V operand feeds NB
-// matrix instructions); PF tiles in flight. Operands are unpacked right
-// before the instruction that reads them and the scale/bias factors read
-// from LDS where they are used. NB = 1 fits a wavefront in 256 registers
-// (two per SIMD). NB = 2 runs one wavefront per SIMD; its query operands
-// wait in LDS (read back every tile) to ease the register pressure, yet the
-// compiler still keeps part of the state in accumulation registers and
-// copies it around the matrix instructions. Measured on the Llama layer's
-// 4096-position chunk at row 61440: NB = 1 30.4 ms, NB = 2 with the queries
-// in registers 26.9 ms, NB = 2 with them in LDS 25.5 ms.
+// 8-bit codes (four per word). NB blocks of 16 query columns per wavefront
+// (every unpacked K and V operand feeds NB matrix instructions), PF tiles in
+// flight; operands are unpacked right before the instruction that reads them
+// and the scale/bias factors read from LDS where they are used. NB = 2 runs
+// one wavefront per SIMD with its query operands in LDS (read back every
+// tile) to ease the register pressure (one block: 35.8 ms against 28.8 ms on
+// the Llama layer's 4096-position chunk at row 61440).
 //
-// BITS = 8 (byte codes, four per word): the K and V codes enter as the exact
-// centred integers n - 128 through the byte permutes of the decode kernel
-// (k_operand8, v_pair8), the value weights are carried times WS = 2^6 (as
-// there, to keep their fp16 halves clear of the subnormal range) and the
-// value products are multiplied by VU = 1 / WS at the end.
+// The K and V codes enter as the exact centred integers n - 128 through the
+// byte permutes of the decode kernel (k_operand8, v_pair8); the value
+// weights p * s_v of each scale group are hi and lo fp16 halves (lo scaled
+// by 2^11) in separate accumulators, carried times WS = 2^6 (as in the
+// decode kernel, to keep their fp16 halves clear of the subnormal range),
+// and the value products are multiplied by VU = 1 / WS at the end.
 //
 // Q32 (fp32 queries, e.g. a query rotated for a Hadamard-rotated cache): the
 // query is split into fp16 hi and lo halves, hi + lo exact to 22 bits, each
 // the B operand of its own score product (as in the decode kernel).
 //
 // D = 256 (four scale groups): the value words of a row come in VS = D / 128
-// sets of 16 words, each set two scale groups handled as the D = 128 layout
+// sets of 32 words, each set two scale groups handled as the D = 128 layout
 // handles its two; NB = 1 there (the accumulators of one block already take
 // what two blocks take at D = 128).
-template <int PF, int NB, int BITS, bool Q32, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 1 && D == 128 ? 2 : 1)))
-void sdpa_prefill_mfma_kernel(PrefillArgs a)
+template <int PF, int NB, bool Q32, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+void sdpa_prefill_b8_kernel(PrefillArgs a)
 {
-    constexpr bool B8 = BITS == 8;
     constexpr int NG = D / 64;   // scale groups of 64
     constexpr int VS = D / 128;  // sets of 16 value words (two groups each)
-    constexpr int W = D * BITS / 32;  // words per row
-    constexpr int KW = BITS / 4;      // words per eight dimensions
+    constexpr int W = D / 4;    // words per row
+    constexpr int KW = 2;       // words per eight dimensions
     constexpr int KM = D / 32;        // score products per 16-row block
     constexpr int KPG = KM / NG;      // of them per scale group
-    constexpr float VC = B8 ? 128.0f : 8.0f;        // centre of the value codes
-    constexpr float WS = B8 ? 64.0f : 1.0f;         // scale of the value weights
-    constexpr float VU = B8 ? 1.0f / 64.0f : 1.0f;  // unit of the value products
+    constexpr float VC = 128.0f;       // centre of the value codes
+    constexpr float WS = 64.0f;        // scale of the value weights
+    constexpr float VU = 1.0f / 64.0f;  // unit of the value products
     constexpr int PAIRS = PT * NG;
     constexpr int MP = PAIRS / 64;  // (row, group) pairs per lane
     static_assert(PAIRS % 64 == 0, "whole pairs per lane");
@@ -130,18 +121,15 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     //   y = b_k c, or (b_k + 128 s_k) c (the bias of centred 8-bit codes)
     //   z = s_v WS, w = b_v + VC s_v
     __shared__ __align__(16) float4 mring[2][PAIRS];
-    const Unpacker unpack = Unpacker::make();
     const float cs = a.score_scale;
-    const float csk = B8 ? cs : cs * 1048576.0f;
-    const uint32_t m_fine = opaque_s_if<!B8>(0x00F000F0u);
-    // 8-bit operands: the magic exponent bytes and the byte selectors of
-    // k_operand8 and v_pair8
-    const uint32_t magic8 = opaque_s_if<B8>(kMagic1024x4), magic16 = opaque_s_if<B8>(0x64006400u);
-    const uint32_t sel_even = opaque_s_if<B8>(0x04020400u), sel_odd = opaque_s_if<B8>(0x04030401u);
-    const uint32_t sel_b[4] = {opaque_s_if<B8>(0x0C040C00u), opaque_s_if<B8>(0x0C050C01u),
-                               opaque_s_if<B8>(0x0C060C02u), opaque_s_if<B8>(0x0C070C03u)};
+    const float csk = cs;
+    // the magic exponent bytes and the byte selectors of k_operand8 and v_pair8
+    const uint32_t magic8 = opaque_s(kMagic1024x4), magic16 = opaque_s(0x64006400u);
+    const uint32_t sel_even = opaque_s(0x04020400u), sel_odd = opaque_s(0x04030401u);
+    const uint32_t sel_b[4] = {opaque_s(0x0C040C00u), opaque_s(0x0C050C01u), opaque_s(0x0C060C02u),
+                               opaque_s(0x0C070C03u)};
 
-    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D * BITS / 8 < 2^31)
+    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D < 2^31 bytes)
     uint32_t kbuf[PF][2][KM][KW];
     uint32_t vbuf[PF][VS][8 * KW];
     uint32_t mbuf[PF][MP][4];
@@ -162,13 +150,9 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + KW * q4) * 4);
 #pragma unroll
             for (int uu = 0; uu < KM; ++uu) {
-                if constexpr (B8) {
-                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(kq, off + 16 * KW * uu, 0, 0);
-                    kt[blk][uu][0] = x[0];
-                    kt[blk][uu][1] = x[1];
-                } else {
-                    kt[blk][uu][0] = __builtin_amdgcn_raw_buffer_load_b32(kq, off + 16 * uu, 0, 0);
-                }
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(kq, off + 16 * KW * uu, 0, 0);
+                kt[blk][uu][0] = x[0];
+                kt[blk][uu][1] = x[1];
             }
         }
         // V: dimensions 128 s2 + 8 col .. + 7 (KW words) of rows 16 (j >> 2) + 4 q4 + (j & 3)
@@ -178,13 +162,9 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t o = voff + ((16 * (j >> 2) + (j & 3)) * W) * 4;
-                if constexpr (B8) {
-                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
-                    vt[s2][2 * j] = x[0];
-                    vt[s2][2 * j + 1] = x[1];
-                } else {
-                    vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, o, 0, 0);
-                }
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
+                vt[s2][2 * j] = x[0];
+                vt[s2][2 * j + 1] = x[1];
             }
         }
     };
@@ -196,7 +176,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             const float vs = h_val((uint16_t)mt[pp][2]);
             const float vb = h_val((uint16_t)mt[pp][3]);
             mring[slot][lane + 64 * pp] =
-                make_float4(ks * csk, (B8 ? fmaf(128.0f, ks, kb) : kb) * cs, vs * WS, fmaf(VC, vs, vb));
+                make_float4(ks * csk, fmaf(128.0f, ks, kb) * cs, vs * WS, fmaf(VC, vs, vb));
         }
         asm volatile("" ::: "memory");
     };
@@ -246,7 +226,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float xv = con[nb] ? x[B8 ? kPerm8[j] : kPerm[j]] : 0.0f;
+                const float xv = con[nb] ? x[kPerm8[j]] : 0.0f;
                 const _Float16 hi = (_Float16)xv;
                 qop[nb][0][uu][j] = hi;
                 if constexpr (Q32) {
@@ -314,11 +294,7 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 #pragma unroll
                     for (int k = 0; k < KPG; ++k) {
                         const uint32_t(&kw)[KW] = kbuf[u][blk][g * KPG + k];
-                        half8 ka;
-                        if constexpr (B8)
-                            ka = k_operand8(kw[0], kw[KW - 1], magic8, sel_even, sel_odd);
-                        else
-                            ka = k_operand_sub(kw[0], m_fine);
+                        const half8 ka = k_operand8(kw[0], kw[KW - 1], magic8, sel_even, sel_odd);
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -396,28 +372,16 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
 
             // ---- value products, group by group; the lane's eight dimensions
             // give 0..3 in its own group's products and lend 4..7 to lane
-            // l ^ 8, and every unpacked operand serves all NB blocks. int4:
-            // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair;
-            // 8-bit: the same exchange on whole words (row r's two words hold
-            // dimensions 0..3 and 4..7)
+            // l ^ 8 (row r's two words hold dimensions 0..3 and 4..7), and
+            // every unpacked operand serves all NB blocks
 #pragma unroll
             for (int s2 = 0; s2 < VS; ++s2) {
                 const uint32_t(&vw)[8 * KW] = vbuf[u][s2];
                 uint32_t bx[2][4 * KW];
-                if constexpr (B8) {
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        bx[0][r] = take_half_row<0xC>(vw[2 * r], vw[2 * r + 1]);
-                        bx[1][r] = take_half_row<0x3>(vw[2 * r], vw[2 * r + 1]);
-                    }
-                } else {
-#pragma unroll
-                    for (int jp = 0; jp < 4; ++jp) {
-                        const uint32_t xw = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], 0x05040100u);
-                        const uint32_t yw = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], 0x07060302u);
-                        bx[0][jp] = take_half_row<0xC>(xw, yw);
-                        bx[1][jp] = take_half_row<0x3>(xw, yw);
-                    }
+                for (int r = 0; r < 8; ++r) {
+                    bx[0][r] = take_half_row<0xC>(vw[2 * r], vw[2 * r + 1]);
+                    bx[1][r] = take_half_row<0x3>(vw[2 * r], vw[2 * r + 1]);
                 }
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
@@ -445,12 +409,8 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
                     for (int mm = 0; mm < 4; ++mm) {
                         half2v e[4];
 #pragma unroll
-                        for (int jp = 0; jp < 4; ++jp) {
-                            if constexpr (B8)
-                                e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm], magic16);
-                            else
-                                e[jp] = unpack.one(bx[g][jp], mm);
-                        }
+                        for (int jp = 0; jp < 4; ++jp)
+                            e[jp] = v_pair8(bx[g][2 * jp], bx[g][2 * jp + 1], sel_b[mm], magic16);
                         const half8 bv = cat8(e[0], e[1], e[2], e[3]);
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb) {
@@ -506,6 +466,932 @@ void sdpa_prefill_mfma_kernel(PrefillArgs a)
     }
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// the query-sum piece that each of a group's six score-bias slots multiplies
+constexpr int kQPiece[6] = {0, 1, 2, 0, 1, 0};
+
+// v as the sum of three bf16 values (each returned as its 16 bits in the low
+// half), exact to all 24 bits of v: each piece is the truncation of what the
+// pieces before it leave, and those differences are exact
+__device__ __forceinline__ void bf16_split3(float v, uint32_t (&out)[3])
+{
+    const uint32_t b1 = __builtin_bit_cast(uint32_t, v) & 0xFFFF0000u;
+    const float r1 = v - __builtin_bit_cast(float, b1);
+    const uint32_t b2 = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
+    const float r2 = r1 - __builtin_bit_cast(float, b2);
+    out[0] = b1 >> 16;
+    out[1] = b2 >> 16;
+    out[2] = __builtin_bit_cast(uint32_t, r2) >> 16;
+}
+
+// K word as an MFMA operand of centred codes: k_operand_sub's subnormals
+// n 2^-20 less 8 2^-20 (the fp16 subnormal 0x0080), exact
+__device__ __forceinline__ half8 k_operand_centred(uint32_t w, uint32_t m_fine)
+{
+    const half2v c8 = as_h2(0x00800080u);
+    return cat8(as_h2((w << 4) & m_fine) - c8, as_h2(w & m_fine) - c8, as_h2((w >> 4) & m_fine) - c8,
+                as_h2((w >> 8) & m_fine) - c8);
+}
+
+// ---------------------------------------------------------------------------
+// int4 codes: the scale and bias factors enter the matrix core
+//
+// One wavefront per block of 16 NB query columns (NB = 1 at D = 256, where
+// the accumulators of one block take as many registers as two do at
+// D = 128); the D = 128 kernel below shares the operands of a tile across a
+// workgroup. The per-column vector work of a tile is cut to the score's
+// per-group scaling, the exponential and one hi/lo split of each weight;
+// everything else is a matrix instruction whose operands are exact:
+//
+// Scores: e[t][c] = sum_g x_{t,g} (Kcodes' . Q[c])_g + Sb[t][c], with the K
+// codes centred, n - 8, as the subnormals (n - 8) 2^-20, x = s_k c 2^20 (one
+// accumulator per group as before), and Sb = sum_g b'_k c qsum_g + 7 - m,
+// b'_k = b_k + 8 s_k (the value of the centre code), from one bf16 matrix
+// instruction per 16-row block: b'_k and c qsum_g and 7 - m (fp32) as three
+// bf16 pieces each, so every product is exact and the bf16 range takes any
+// bias and any query. The matrix core truncates each instruction's sum at
+// its largest term; with uncentred codes that term would be b_k c qsum_g,
+// which cancels against most of the code products (for the outlier
+// workload's K about 150 in log2 units, against scores of about 10), and
+// the truncation would show in the weights.
+//
+// Weights are carried as p' = 2^7 p = exp2(e) (at most 2^(7 - kHeadroom)), as
+// an fp16 hi half (truncated) and the exact remainder lo; both halves are at
+// the same scale, so lo sinks into the fp16 subnormals only for p' < 2^-4,
+// where its absolute error is at most 2^-25 of p'.
+//
+// Values: the scale goes into the value operand instead of the weights, so
+// one (hi, lo) weight pair serves every scale group. s_v (fp16) is split
+// into s_hi (its top eight significant bits) and s_lo = s_v - s_hi (three
+// bits); a centred code n - 8 times s_hi or s_lo is exact in fp16 (|n - 8|
+// is at most 7, or 8, a power of two). Both are halved (so that 8 s_hi stays
+// below the fp16 maximum for every fp16 scale); halving is exact except for
+// s_lo of scales below 2^-13, where it leaves at most 2^-26 absolute error
+// per element. One accumulator per output takes p'_hi V_hi + p'_hi V_lo +
+// p'_lo V_hi (p'_lo V_lo, at most 2^-18 of the whole, is left out).
+//
+// Bias and normaliser: the weight operands times a table whose columns are
+// the value a group's centre code stands for, w = b_v + 8 s_v (fp32), as an
+// fp16 hi (truncated) and lo pair per group, and ones give sum p' w and
+// sum p' = l' in one more accumulator; the output is (2 acc + sum p' w) / l'.
+// w lies between the group's extreme values, so its hi half never overflows;
+// the pair holds it to 2^-22 relative, or 2^-24 absolute where w is below
+// the fp16 normal range. (b_v and 8 s_v in columns of their own would cancel
+// in the sum and magnify the matrix core's truncation by |b_v| / |output|.)
+template <int PF, int NB, bool Q32, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+void sdpa_prefill_i4_kernel(PrefillArgs a)
+{
+    constexpr int NG = D / 64;        // scale groups of 64
+    constexpr int VS = D / 128;       // sets of 16 value words (two groups each)
+    constexpr int W = D / 8;          // words per row
+    constexpr int KM = D / 32;        // score products per 16-row block
+    constexpr int KPG = KM / NG;      // of them per scale group
+    constexpr int PAIRS = PT * NG;
+    constexpr int MP = PAIRS / 64;    // (row, group) pairs per lane
+    static_assert(PAIRS % 64 == 0, "whole pairs per lane");
+    constexpr int QH = Q32 ? 2 : 1;   // query halves: hi (and lo)
+    // score-bias operand slots: group g at 6g..6g+5, (b1, b1, b1, b2, b2, b3)
+    // against (Q1, Q2, Q3, Q1, Q2, Q1); then three ones against the pieces of
+    // 7 - m; the rest zero
+    constexpr int SBR = 6 * NG;       // first slot of the reference pieces
+    constexpr int SBL = (SBR + 3 + 7) / 8 * 8;  // slots stored per row
+    constexpr int NQ4 = SBL / 8;      // lane groups that hold used slots
+    constexpr int NVB = 2 * NG + 2;   // value-bias table rows: w hi, w lo per group, ones, zeros
+    constexpr float kRef = 7.0f;      // weights are 2^kRef p
+
+    const int lane = threadIdx.x;
+    const int q4 = lane >> 4;
+    const int col = lane & 15;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int nrep = a.n_rep;
+    const int p0 = blockIdx.x * a.pb;
+    const int npos = min(a.pb, a.sq - p0);
+    const int t_end = (int)a.q_start + p0 + npos;
+    const int t_all = (int)a.q_start + p0;
+    const int ntile = (t_end + PT - 1) / PT;
+    const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
+    const bool low8 = (lane & 8) == 0;
+
+    int cpos[NB], chead[NB];
+    bool con[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int cc = 16 * nb + col;
+        cpos[nb] = cc / nrep;
+        chead[nb] = cc % nrep;
+        con[nb] = cc < a.pb * nrep && cpos[nb] < npos;
+    }
+
+    const uint32_t rows_ok = (uint32_t)t_end;
+    const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t mres[4] = {
+        make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
+        make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
+
+    // per-tile tables, two-slot LDS ring
+    __shared__ __align__(16) float xs[2][PT][NG];            // s_k c 2^20
+    __shared__ __align__(16) uint16_t sba[2][PT][SBL];       // score-bias operand rows (bf16)
+    __shared__ __align__(16) uint16_t vbt[2][NVB][PT];       // value-bias table (fp16), by column
+    __shared__ __align__(16) uint16_t svt[2][2 * NG][PT];    // s_hi / 2, then s_lo / 2 (fp16)
+    const Unpacker unpack = Unpacker::make();
+    const float cs = a.score_scale;
+    const float csk = cs * 1048576.0f;
+    const uint32_t m_fine = 0x00F000F0u;
+
+    // the constant parts of the tables, in both slots: ones against the
+    // reference pieces, zero slots, the ones and zeros columns
+    {
+        const int s = lane >> 5, r = lane & 31;
+#pragma unroll
+        for (int k = SBR; k < SBL; ++k)
+            sba[s][r][k] = k < SBR + 3 ? (uint16_t)0x3F80u : (uint16_t)0u;
+        vbt[s][2 * NG][r] = 0x3C00u;
+        vbt[s][2 * NG + 1][r] = 0u;
+    }
+
+    constexpr uint32_t kNoRows = 0x80000000u;
+    uint32_t kbuf[PF][2][KM];
+    uint32_t vbuf[PF][VS][8];
+    uint32_t mbuf[PF][MP][4];
+    auto load_tile = [&](int ti, uint32_t (&kt)[2][KM], uint32_t (&vt)[VS][8], uint32_t (&mt)[MP][4]) {
+        const bool in = ti < ntile;
+#pragma unroll
+        for (int pp = 0; pp < MP; ++pp) {
+            const uint32_t moff = in ? (uint32_t)((PT * ti) * NG + lane + 64 * pp) * 2u : kNoRows;
+#pragma unroll
+            for (int arr = 0; arr < 4; ++arr)
+                mt[pp][arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
+        }
+        const uint32_t base = in ? (uint32_t)(PT * ti) * (uint32_t)(W * 4) : kNoRows;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + q4) * 4);
+#pragma unroll
+            for (int uu = 0; uu < KM; ++uu)
+                kt[blk][uu] = __builtin_amdgcn_raw_buffer_load_b32(kq, off + 16 * uu, 0, 0);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < VS; ++s2) {
+            const uint32_t voff = base + (uint32_t)((4 * q4 * W + 16 * s2 + col) * 4);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
+        }
+    };
+    auto stage_meta = [&](int slot, const uint32_t (&mt)[MP][4]) {
+#pragma unroll
+        for (int pp = 0; pp < MP; ++pp) {
+            const int idx = lane + 64 * pp;
+            const int r = idx / NG, g = idx % NG;
+            const uint16_t ks = (uint16_t)mt[pp][0], kb = (uint16_t)mt[pp][1];
+            const uint16_t vsb = (uint16_t)mt[pp][2], vbb = (uint16_t)mt[pp][3];
+            xs[slot][r][g] = h_val(ks) * csk;
+            uint32_t bp[3];
+            bf16_split3(fmaf(8.0f, h_val(ks), h_val(kb)), bp);
+            uint32_t *srow = reinterpret_cast<uint32_t *>(&sba[slot][r][6 * g]);
+            srow[0] = bp[0] | (bp[0] << 16);
+            srow[1] = bp[0] | (bp[1] << 16);
+            srow[2] = bp[1] | (bp[2] << 16);
+            const float w = fmaf(8.0f, h_val(vsb), h_val(vbb));
+            const float whi = (float)__builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w, 0.0f))[0];
+            // (the halves are copied out before the bit casts: a bit cast of a
+            // vector element in place reads element 0)
+            const half2v wp = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(whi, w - whi));
+            const _Float16 wh = wp[0], wl = wp[1];
+            vbt[slot][2 * g][r] = __builtin_bit_cast(uint16_t, wh);
+            vbt[slot][2 * g + 1][r] = __builtin_bit_cast(uint16_t, wl);
+            const float sh = h_val((uint16_t)(vsb & 0xFFF8u));
+            const float sl = h_val(vsb) - sh;
+            svt[slot][g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * sh));
+            svt[slot][NG + g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * sl));
+        }
+        asm volatile("" ::: "memory");
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(u, kbuf[u], vbuf[u], mbuf[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // query operands (as in the kernel above) and the fp32 group sums of
+    // exactly what the matrix core sees
+    half8 qop[NB][QH][KM];
+    float qsum[NB][NG];
+    __shared__ __align__(16) half8 q_lds[NB][QH][KM][64];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con[nb] ? chead[nb] : 0)) * a.sq + p0 +
+                              (con[nb] ? cpos[nb] : 0)) * D;
+        float gs[NG] = {};
+#pragma unroll
+        for (int uu = 0; uu < KM; ++uu) {
+            float x[8];
+            if constexpr (Q32) {
+                const float *qp = reinterpret_cast<const float *>(a.q) + qrow + 32 * uu + 8 * q4;
+                const float4 x0 = *reinterpret_cast<const float4 *>(qp);
+                const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
+                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+                x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            } else {
+                const half8 h8 = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow +
+                                                                  32 * uu + 8 * q4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[j] = (float)h8[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xv = con[nb] ? x[kPerm[j]] : 0.0f;
+                const _Float16 hi = (_Float16)xv;
+                qop[nb][0][uu][j] = hi;
+                if constexpr (Q32) {
+                    const _Float16 lo = (_Float16)(xv - (float)hi);
+                    qop[nb][QH - 1][uu][j] = lo;
+                    gs[uu / KPG] += (float)hi + (float)lo;
+                } else {
+                    gs[uu / KPG] += (float)hi;
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            qsum[nb][g] = xrow_sum(gs[g]);
+#pragma unroll
+        for (int hl = 0; hl < QH; ++hl)
+#pragma unroll
+            for (int uu = 0; uu < KM; ++uu)
+                q_lds[nb][hl][uu][lane] = qop[nb][hl][uu];
+    }
+    stage_meta(0, mbuf[0]);
+
+    // the score-bias B operand of block nb: this lane's column, slots
+    // 8 q4 .. 8 q4 + 7 (c qsum_g and 7 - m as bf16 pieces)
+    float ref[NB];  // 7 - m, this lane's column
+    bf16x8 sbb[NB];
+    auto build_sbb = [&](int nb) {
+        uint32_t qp[NG][3], rp[3];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            bf16_split3(cs * qsum[nb][g], qp[g]);
+        bf16_split3(ref[nb], rp);
+        auto piece = [&](int k) -> uint32_t {  // k a constant after unrolling
+            if (k < SBR)
+                return qp[k / 6][kQPiece[k % 6]];
+            if (k < SBR + 3)
+                return rp[k - SBR];
+            return 0u;
+        };
+        u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int qq = 0; qq < NQ4; ++qq)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const uint32_t v = piece(8 * qq + 2 * jj) | (piece(8 * qq + 2 * jj + 1) << 16);
+                w[jj] = q4 == qq ? v : w[jj];
+            }
+        sbb[nb] = __builtin_bit_cast(bf16x8, w);
+    };
+
+    float4v acc[NB][8 * VS], bacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        ref[nb] = kRef;
+        build_sbb(nb);
+        bacc[nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 8 * VS; ++m)
+            acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int vrow = min(col, 2 * NG + 1);  // this lane's value-bias table row
+
+#pragma unroll 1
+    for (int kk = 0; kk < ntile; kk += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int ti = kk + u;
+            const int slot = u & 1;
+
+            // ---- exponents of the lane's 8 rows (16 blk + 4 q4 + i) for each block's column
+            float sc[NB][8];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int ar = 16 * blk + col;
+                const u32x4 araw = *reinterpret_cast<const u32x4 *>(&sba[slot][ar][8 * min(q4, NQ4 - 1)]);
+                const bf16x8 sa = __builtin_bit_cast(bf16x8, araw);
+                float4v s[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa, sbb[nb], (float4v){0.0f, 0.0f, 0.0f, 0.0f},
+                                                                   0, 0, 0);
+                float4v sacc[NG][NB];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        sacc[g][nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KPG; ++k) {
+                        const half8 ka = k_operand_centred(kbuf[u][blk][g * KPG + k], m_fine);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int hl = 0; hl < QH; ++hl)
+                                sacc[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q_lds[nb][hl][g * KPG + k][lane],
+                                                                                    sacc[g][nb], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float xg[NG];
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        xg[g] = xs[slot][16 * blk + 4 * q4 + i][g];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        float e = s[nb][i];
+#pragma unroll
+                        for (int g = 0; g < NG; ++g)
+                            e = fmaf(xg[g], sacc[g][nb][i], e);
+                        sc[nb][4 * blk + i] = e;
+                    }
+                }
+            }
+            if (PT * ti + PT - 1 > t_all) {  // uniform: some row is past some column's position
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int lim = t_all + cpos[nb];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = PT * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
+                        sc[nb][i] = r <= lim ? sc[nb][i] : -INFINITY;
+                    }
+                }
+            }
+            half8 phi[NB], plo[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float mx = max3_raw(max3_raw(sc[nb][0], sc[nb][1], sc[nb][2]),
+                                          max3_raw(sc[nb][3], sc[nb][4], sc[nb][5]), max_raw(sc[nb][6], sc[nb][7]));
+                // ---- reference raised only when an exponent exceeds kRef (the first tile sets it)
+                if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > kRef) != 0) {
+                    const float full = xrow_max(mx, -INFINITY);
+                    const bool raise = full > kRef || (ti == 0 && full > -INFINITY);
+                    const float r_new = raise ? ref[nb] - (full - (kRef - kHeadroom)) : ref[nb];
+                    const float delta = ref[nb] - r_new;
+                    ref[nb] = r_new;
+                    build_sbb(nb);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        sc[nb][i] -= delta;
+                    if (ti != 0) {
+                        const float corr = __builtin_amdgcn_exp2f(-delta);
+                        float4v corr_row;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            corr_row[i] = __shfl(corr, 4 * q4 + i);
+                        bacc[nb] *= corr_row;
+#pragma unroll
+                        for (int m = 0; m < 8 * VS; ++m)
+                            acc[nb][m] *= corr_row;
+                    }
+                }
+                // ---- weights 2^7 p as hi (truncated) and lo halves
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const float w0 = __builtin_amdgcn_exp2f(sc[nb][j]);
+                    const float w1 = __builtin_amdgcn_exp2f(sc[nb][j + 1]);
+                    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                    const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0 - (float)h[0],
+                                                                                          w1 - (float)h[1]));
+                    phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
+                    plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
+                }
+            }
+
+            // ---- value products: the lane's rows (2 jp, 2 jp + 1) pair up in
+            // each fp16 pair of the operand, so the scale halves of a pair of
+            // rows multiply one half2
+#pragma unroll
+            for (int s2 = 0; s2 < VS; ++s2) {
+                const uint32_t(&vw)[8] = vbuf[u][s2];
+                uint32_t bx[2][4];
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    const uint32_t xw = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], 0x05040100u);
+                    const uint32_t yw = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], 0x07060302u);
+                    bx[0][jp] = take_half_row<0xC>(xw, yw);
+                    bx[1][jp] = take_half_row<0x3>(xw, yw);
+                }
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int gg = 2 * s2 + g;
+                    const uint2 h0 = *reinterpret_cast<const uint2 *>(&svt[slot][gg][4 * q4]);
+                    const uint2 h1 = *reinterpret_cast<const uint2 *>(&svt[slot][gg][16 + 4 * q4]);
+                    const uint2 l0 = *reinterpret_cast<const uint2 *>(&svt[slot][NG + gg][4 * q4]);
+                    const uint2 l1 = *reinterpret_cast<const uint2 *>(&svt[slot][NG + gg][16 + 4 * q4]);
+                    const half2v shi[4] = {as_h2(h0.x), as_h2(h0.y), as_h2(h1.x), as_h2(h1.y)};
+                    const half2v slo[4] = {as_h2(l0.x), as_h2(l0.y), as_h2(l1.x), as_h2(l1.y)};
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) {
+                        half2v e[4];
+#pragma unroll
+                        for (int jp = 0; jp < 4; ++jp)
+                            e[jp] = unpack.one(bx[g][jp], mm);
+                        const half8 vh = cat8(e[0] * shi[0], e[1] * shi[1], e[2] * shi[2], e[3] * shi[3]);
+                        const half8 vl = cat8(e[0] * slo[0], e[1] * slo[1], e[2] * slo[2], e[3] * slo[3]);
+                        const int m = 8 * s2 + 4 * g + mm;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vh, acc[nb][m], 0, 0, 0);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vl, acc[nb][m], 0, 0, 0);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], vh, acc[nb][m], 0, 0, 0);
+                    }
+                }
+            }
+            // ---- bias sums and the normaliser: rows 4 q4 .. + 3 and 16 + 4 q4 .. + 3 of table row vrow
+            {
+                const uint2 c0 = *reinterpret_cast<const uint2 *>(&vbt[slot][vrow][4 * q4]);
+                const uint2 c1 = *reinterpret_cast<const uint2 *>(&vbt[slot][vrow][16 + 4 * q4]);
+                const half8 bv = __builtin_bit_cast(half8, (u32x4){c0.x, c0.y, c1.x, c1.y});
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    bacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], bv, bacc[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    bacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, bacc[nb], 0, 0, 0);
+            }
+
+            load_tile(ti + PF, kbuf[u], vbuf[u], mbuf[u]);
+            stage_meta(slot ^ 1, mbuf[(u + 1) % PF]);
+        }
+    }
+
+    // ---- normalised outputs: accumulator row 4 q4 + i is column 16 nb + 4 q4 + i;
+    // its bias sums and l' sit in lanes 16 q4 + n of bacc (table column n)
+    const int rowbase = lane & 48;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = 16 * nb + 4 * q4 + i;
+            const float inv_l = 1.0f / __shfl(bacc[nb][i], rowbase + 2 * NG);
+            const int rpos = cc / nrep, rhead = cc % nrep;
+            const bool on = cc < a.pb * nrep && rpos < npos;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                const int s2 = gg >> 1, g = gg & 1;
+                const float bias = __shfl(bacc[nb][i], rowbase + 2 * gg) + __shfl(bacc[nb][i], rowbase + 2 * gg + 1);
+                const int d0 = 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
+                float o[4];
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm)
+                    o[mm] = fmaf(2.0f, acc[nb][8 * s2 + 4 * g + mm][i], bias) * inv_l;
+                if (on) {
+                    float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// int4 codes, D = 128: WG wavefronts share each tile's unpacked operands
+//
+// The arithmetic of sdpa_prefill_i4_kernel, with WG wavefronts per
+// workgroup on consecutive position blocks of one (batch, KV head): they
+// read the same rows, so each unpacks only 1/WG of a tile's K operands
+// (centred codes as subnormals) and of its centred V codes into LDS, one
+// wavefront in turn stages the tile's factor tables, and one barrier per
+// tile separates building tile t + 1 (into the other half of a two-slot
+// ring) from the reads of tile t. Each wavefront then scales the V codes
+// by s_hi / 2 and s_lo / 2 itself (those operands are not shared: sharing
+// them would double the LDS they take and the reads per tile). Two
+// workgroups share a CU (2 wavefronts per SIMD) with fp16 queries; with fp32
+// queries the hi and lo query operands take the LDS of a second one.
+template <int PF, int NB, bool Q32, int WG>
+__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(Q32 ? 1 : 2)))
+void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
+{
+    constexpr int D = 128, NG = 2, W = 16, KM = 4, KPG = 2;
+    constexpr int QH = Q32 ? 2 : 1;
+    constexpr int SBR = 6 * NG;
+    constexpr int SBL = (SBR + 3 + 7) / 8 * 8;
+    constexpr int NQ4 = SBL / 8;
+    constexpr int NVB = 2 * NG + 2;
+    constexpr float kRef = 7.0f;
+    constexpr int NKO = 2 * KM;   // K operands of a tile: (16-row block, 32 dimensions)
+    constexpr int NVO = 4 * NG;   // centred V operands of a tile: (scale group, mm)
+    constexpr int KO = NKO / WG;  // of them built by each wavefront
+    constexpr int VO = NVO / WG;
+    static_assert(NKO % WG == 0 && NVO % WG == 0, "operands split evenly");
+    static_assert(PT * NG == 64, "one (row, group) pair per lane of the staging wavefront");
+
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const int col = lane & 15;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int nrep = a.n_rep;
+    const int p0g = blockIdx.x * WG * a.pb;                // first position of the workgroup
+    const int p0 = p0g + wv * a.pb;                        // of this wavefront
+    const int npos = max(0, min(a.pb, a.sq - p0));         // this wavefront's positions (may be none)
+    const int t_end = (int)a.q_start + min(p0g + WG * a.pb, a.sq);  // rows [0, t_end) are read
+    const int t_all = (int)a.q_start + p0;
+    const int ntile = (t_end + PT - 1) / PT;
+    const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
+    const bool low8 = (lane & 8) == 0;
+
+    int cpos[NB], chead[NB];
+    bool con[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int cc = 16 * nb + col;
+        cpos[nb] = cc / nrep;
+        chead[nb] = cc % nrep;
+        con[nb] = cc < a.pb * nrep && cpos[nb] < npos;
+    }
+
+    const uint32_t rows_ok = (uint32_t)t_end;
+    const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t mres[4] = {
+        make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
+        make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
+
+    __shared__ __align__(16) half8 kop[2][NKO][64];          // K operands
+    __shared__ __align__(16) half8 vop[2][NVO][64];          // centred V codes
+    __shared__ __align__(16) float xs[2][PT][NG];
+    __shared__ __align__(16) uint16_t sba[2][PT][SBL];
+    __shared__ __align__(16) uint16_t vbt[2][NVB][PT];
+    __shared__ __align__(16) uint16_t svt[2][2 * NG][PT];
+    __shared__ __align__(16) half8 q_lds[WG][NB][QH][KM][64];
+    const float cs = a.score_scale;
+    const float csk = cs * 1048576.0f;
+    const uint32_t m_fine = 0x00F000F0u;
+
+    // this wavefront's V operands are (g, mm) = (i, wv) for i < VO (WG = 4)
+    // or (v >> 2, v & 3) with v = wv + WG i in general: the nibble to take
+    // is chosen by wave-uniform shift, mask, magic and offset
+    static_assert(WG == 4 || WG == 2 || WG == 1, "two, four or eight (g, mm) operands per wavefront");
+
+    if (wv == 0) {
+        const int s = lane >> 5, r = lane & 31;
+#pragma unroll
+        for (int k = SBR; k < SBL; ++k)
+            sba[s][r][k] = k < SBR + 3 ? (uint16_t)0x3F80u : (uint16_t)0u;
+        vbt[s][2 * NG][r] = 0x3C00u;
+        vbt[s][2 * NG + 1][r] = 0u;
+    }
+
+    constexpr uint32_t kNoRows = 0x80000000u;
+    uint32_t kbuf[PF][KO];
+    uint32_t vbuf[PF][8];
+    uint32_t mbuf[PF][4];
+    auto load_tile = [&](int ti, uint32_t (&kt)[KO], uint32_t (&vt)[8], uint32_t (&mt)[4]) {
+        const bool in = ti < ntile;
+        const uint32_t base = in ? (uint32_t)(PT * ti) * (uint32_t)(W * 4) : kNoRows;
+#pragma unroll
+        for (int i = 0; i < KO; ++i) {
+            const int o = wv + WG * i;  // blk = o / KM, uu = o % KM
+            kt[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                kq, base + (uint32_t)((((16 * (o / KM) + col) * W + q4) * 4) + 16 * (o % KM)), 0, 0);
+        }
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + col) * 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
+        if (ti % WG == wv) {  // this wavefront stages tile ti's tables
+            const uint32_t moff = in ? (uint32_t)((PT * ti) * NG + lane) * 2u : kNoRows;
+#pragma unroll
+            for (int arr = 0; arr < 4; ++arr)
+                mt[arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
+        }
+    };
+    // wave-uniform selectors of this wavefront's V nibbles (mm = v & 3)
+    auto build = [&](int ti, int slot, const uint32_t (&kt)[KO], const uint32_t (&vt)[8], const uint32_t (&mt)[4]) {
+#pragma unroll
+        for (int i = 0; i < KO; ++i)
+            kop[slot][wv + WG * i][lane] = k_operand_centred(kt[i], m_fine);
+        uint32_t bx[2][4];
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+            const uint32_t xw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x05040100u);
+            const uint32_t yw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x07060302u);
+            bx[0][jp] = take_half_row<0xC>(xw, yw);
+            bx[1][jp] = take_half_row<0x3>(xw, yw);
+        }
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const int v = wv + WG * i;
+            const int g = v >> 2, mm = v & 3;  // g: a constant when WG = 4
+            const uint32_t sh = mm >= 2 ? 8u : 0u;
+            const uint32_t mask = opaque_s((mm & 1) ? 0x00F000F0u : 0x000F000Fu);
+            const uint32_t magic = opaque_v((mm & 1) ? 0x54005400u : 0x64006400u);
+            const half2v off = as_h2((mm & 1) ? 0x54805480u : 0x64086408u);  // 72 or 1032
+            half2v e[4];
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp) {
+                const uint32_t x = g == 0 ? bx[0][jp] : bx[1][jp];
+                e[jp] = as_h2(and_or(x >> sh, mask, magic)) - off;
+            }
+            vop[slot][v][lane] = cat8(e[0], e[1], e[2], e[3]);
+        }
+        if (ti % WG == wv) {
+            const int r = lane / NG, g = lane % NG;
+            const uint16_t ks = (uint16_t)mt[0], kb = (uint16_t)mt[1];
+            const uint16_t vsb = (uint16_t)mt[2], vbb = (uint16_t)mt[3];
+            xs[slot][r][g] = h_val(ks) * csk;
+            uint32_t bp[3];
+            bf16_split3(fmaf(8.0f, h_val(ks), h_val(kb)), bp);
+            uint32_t *srow = reinterpret_cast<uint32_t *>(&sba[slot][r][6 * g]);
+            srow[0] = bp[0] | (bp[0] << 16);
+            srow[1] = bp[0] | (bp[1] << 16);
+            srow[2] = bp[1] | (bp[2] << 16);
+            const float w = fmaf(8.0f, h_val(vsb), h_val(vbb));
+            const float whi = (float)__builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w, 0.0f))[0];
+            const half2v wp = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(whi, w - whi));
+            const _Float16 wh = wp[0], wl = wp[1];
+            vbt[slot][2 * g][r] = __builtin_bit_cast(uint16_t, wh);
+            vbt[slot][2 * g + 1][r] = __builtin_bit_cast(uint16_t, wl);
+            const float shv = h_val((uint16_t)(vsb & 0xFFF8u));
+            const float slv = h_val(vsb) - shv;
+            svt[slot][g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * shv));
+            svt[slot][NG + g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * slv));
+        }
+    };
+
+    // query operands (as in the kernels above)
+    float qsum[NB][NG];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con[nb] ? chead[nb] : 0)) * a.sq +
+                              (con[nb] ? p0 + cpos[nb] : 0)) * D;
+        float gs[NG] = {};
+#pragma unroll
+        for (int uu = 0; uu < KM; ++uu) {
+            float x[8];
+            if constexpr (Q32) {
+                const float *qp = reinterpret_cast<const float *>(a.q) + qrow + 32 * uu + 8 * q4;
+                const float4 x0 = *reinterpret_cast<const float4 *>(qp);
+                const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
+                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+                x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            } else {
+                const half8 h8 = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow +
+                                                                  32 * uu + 8 * q4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[j] = (float)h8[j];
+            }
+            half8 qh, ql;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xv = con[nb] ? x[kPerm[j]] : 0.0f;
+                const _Float16 hi = (_Float16)xv;
+                qh[j] = hi;
+                if constexpr (Q32) {
+                    const _Float16 lo = (_Float16)(xv - (float)hi);
+                    ql[j] = lo;
+                    gs[uu / KPG] += (float)hi + (float)lo;
+                } else {
+                    gs[uu / KPG] += (float)hi;
+                }
+            }
+            q_lds[wv][nb][0][uu][lane] = qh;
+            if constexpr (Q32)
+                q_lds[wv][nb][QH - 1][uu][lane] = ql;
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            qsum[nb][g] = xrow_sum(gs[g]);
+    }
+
+    // prologue: raw words of tiles 0 .. PF - 1, tile 0 built, tile PF loaded
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        load_tile(u, kbuf[u], vbuf[u], mbuf[u]);
+    build(0, 0, kbuf[0], vbuf[0], mbuf[0]);
+    load_tile(PF, kbuf[0], vbuf[0], mbuf[0]);
+    __syncthreads();
+
+    float ref[NB];
+    bf16x8 sbb[NB];
+    auto build_sbb = [&](int nb) {
+        uint32_t qp[NG][3], rp[3];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            bf16_split3(cs * qsum[nb][g], qp[g]);
+        bf16_split3(ref[nb], rp);
+        auto piece = [&](int k) -> uint32_t {
+            if (k < SBR)
+                return qp[k / 6][kQPiece[k % 6]];
+            if (k < SBR + 3)
+                return rp[k - SBR];
+            return 0u;
+        };
+        u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int qq = 0; qq < NQ4; ++qq)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const uint32_t v = piece(8 * qq + 2 * jj) | (piece(8 * qq + 2 * jj + 1) << 16);
+                w[jj] = q4 == qq ? v : w[jj];
+            }
+        sbb[nb] = __builtin_bit_cast(bf16x8, w);
+    };
+
+    float4v acc[NB][8], bacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        ref[nb] = kRef;
+        build_sbb(nb);
+        bacc[nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int vrow = min(col, 2 * NG + 1);
+
+#pragma unroll 1
+    for (int kk = 0; kk < ntile; kk += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int ti = kk + u;
+            const int slot = u & 1;
+
+            float sc[NB][8];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const u32x4 araw =
+                    *reinterpret_cast<const u32x4 *>(&sba[slot][16 * blk + col][8 * min(q4, NQ4 - 1)]);
+                const bf16x8 sa = __builtin_bit_cast(bf16x8, araw);
+                float4v s[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa, sbb[nb], (float4v){0.0f, 0.0f, 0.0f, 0.0f},
+                                                                   0, 0, 0);
+                float4v sacc[NG][NB];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        sacc[g][nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KPG; ++k) {
+                        const half8 ka = kop[slot][blk * KM + g * KPG + k][lane];
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int hl = 0; hl < QH; ++hl)
+                                sacc[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    ka, q_lds[wv][nb][hl][g * KPG + k][lane], sacc[g][nb], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float2 xg = *reinterpret_cast<const float2 *>(&xs[slot][16 * blk + 4 * q4 + i][0]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        sc[nb][4 * blk + i] = fmaf(xg.x, sacc[0][nb][i], fmaf(xg.y, sacc[1][nb][i], s[nb][i]));
+                }
+            }
+            if (PT * ti + PT - 1 > t_all) {
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int lim = t_all + cpos[nb];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = PT * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
+                        sc[nb][i] = r <= lim ? sc[nb][i] : -INFINITY;
+                    }
+                }
+            }
+            half8 phi[NB], plo[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float mx = max3_raw(max3_raw(sc[nb][0], sc[nb][1], sc[nb][2]),
+                                          max3_raw(sc[nb][3], sc[nb][4], sc[nb][5]), max_raw(sc[nb][6], sc[nb][7]));
+                if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > kRef) != 0) {
+                    const float full = xrow_max(mx, -INFINITY);
+                    const bool raise = full > kRef || (ti == 0 && full > -INFINITY);
+                    const float r_new = raise ? ref[nb] - (full - (kRef - kHeadroom)) : ref[nb];
+                    const float delta = ref[nb] - r_new;
+                    ref[nb] = r_new;
+                    build_sbb(nb);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        sc[nb][i] -= delta;
+                    if (ti != 0) {
+                        const float corr = __builtin_amdgcn_exp2f(-delta);
+                        float4v corr_row;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            corr_row[i] = __shfl(corr, 4 * q4 + i);
+                        bacc[nb] *= corr_row;
+#pragma unroll
+                        for (int m = 0; m < 8; ++m)
+                            acc[nb][m] *= corr_row;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const float w0 = __builtin_amdgcn_exp2f(sc[nb][j]);
+                    const float w1 = __builtin_amdgcn_exp2f(sc[nb][j + 1]);
+                    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                    const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0 - (float)h[0],
+                                                                                          w1 - (float)h[1]));
+                    phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
+                    plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
+                }
+            }
+
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const uint2 h0 = *reinterpret_cast<const uint2 *>(&svt[slot][g][4 * q4]);
+                const uint2 h1 = *reinterpret_cast<const uint2 *>(&svt[slot][g][16 + 4 * q4]);
+                const uint2 l0 = *reinterpret_cast<const uint2 *>(&svt[slot][NG + g][4 * q4]);
+                const uint2 l1 = *reinterpret_cast<const uint2 *>(&svt[slot][NG + g][16 + 4 * q4]);
+                const half2v shi[4] = {as_h2(h0.x), as_h2(h0.y), as_h2(h1.x), as_h2(h1.y)};
+                const half2v slo[4] = {as_h2(l0.x), as_h2(l0.y), as_h2(l1.x), as_h2(l1.y)};
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const u32x4 cw = __builtin_bit_cast(u32x4, vop[slot][4 * g + mm][lane]);
+                    const half2v e[4] = {as_h2(cw[0]), as_h2(cw[1]), as_h2(cw[2]), as_h2(cw[3])};
+                    const half8 vh = cat8(e[0] * shi[0], e[1] * shi[1], e[2] * shi[2], e[3] * shi[3]);
+                    const half8 vl = cat8(e[0] * slo[0], e[1] * slo[1], e[2] * slo[2], e[3] * slo[3]);
+                    const int m = 4 * g + mm;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vh, acc[nb][m], 0, 0, 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vl, acc[nb][m], 0, 0, 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], vh, acc[nb][m], 0, 0, 0);
+                }
+            }
+            {
+                const uint2 c0 = *reinterpret_cast<const uint2 *>(&vbt[slot][vrow][4 * q4]);
+                const uint2 c1 = *reinterpret_cast<const uint2 *>(&vbt[slot][vrow][16 + 4 * q4]);
+                const half8 bv = __builtin_bit_cast(half8, (u32x4){c0.x, c0.y, c1.x, c1.y});
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    bacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], bv, bacc[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    bacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, bacc[nb], 0, 0, 0);
+            }
+
+            // tile ti + 1 into the other slot (its words were loaded PF tiles
+            // ago), tile ti + 1 + PF into the freed registers, then the barrier
+            // that ends the reads of slot `slot` and publishes slot `slot ^ 1`
+            const int nu = (u + 1) % PF;
+            build(ti + 1, slot ^ 1, kbuf[nu], vbuf[nu], mbuf[nu]);
+            load_tile(ti + 1 + PF, kbuf[nu], vbuf[nu], mbuf[nu]);
+            __syncthreads();
+        }
+    }
+
+    const int rowbase = lane & 48;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = 16 * nb + 4 * q4 + i;
+            const float inv_l = 1.0f / __shfl(bacc[nb][i], rowbase + 2 * NG);
+            const int rpos = cc / nrep, rhead = cc % nrep;
+            const bool on = cc < a.pb * nrep && rpos < npos;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const float bias = __shfl(bacc[nb][i], rowbase + 2 * g) + __shfl(bacc[nb][i], rowbase + 2 * g + 1);
+                const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
+                float o[4];
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm)
+                    o[mm] = fmaf(2.0f, acc[nb][4 * g + mm][i], bias) * inv_l;
+                if (on) {
+                    float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
@@ -514,33 +1400,45 @@ bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
            (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) && (bits == 4 || bits == 8);
 }
 
-// blocks of 16 query columns per wavefront: two at D = 128 (8-bit codes with
-// one block: 35.8 ms against 28.8 ms on the 4096-position chunk), one at
-// D = 256
+// blocks of 16 query columns per wavefront. 8-bit codes: two at D = 128
+// (one block: 35.8 ms against 28.8 ms on the 4096-position chunk), one at
+// D = 256. int4: four at D = 128, two at D = 256 (one accumulator per output
+// leaves room for twice the columns).
+// blocks of 16 query columns per wavefront: two at D = 128, one at D = 256
 constexpr int prefill_nb(int D) { return D == 256 ? 1 : 2; }
 
 int prefill_positions_per_block(int n_rep, int D) { return 16 * prefill_nb(D) / n_rep; }
+
+// wavefronts per workgroup (consecutive position blocks of one KV head)
+constexpr int prefill_wg(int D, int bits) { return bits == 4 && D == 128 ? 4 : 1; }
 
 template <int D>
 void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
 {
     constexpr int NB = prefill_nb(D);
+    constexpr int WG = prefill_wg(D, 4);
     if (a.bits == 8 && a.q_f32)
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 8, true, D>), grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
     else if (a.bits == 8)
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 8, false, D>), grid, dim3(64), 0, s, a);
-    else if (a.q_f32)
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 4, true, D>), grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
+    else if constexpr (D == 128) {
+        if (a.q_f32)
+            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, true, WG>), grid, dim3(64 * WG), 0, s, a);
+        else
+            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, false, WG>), grid, dim3(64 * WG), 0, s, a);
+    } else if (a.q_f32)
+        hipLaunchKernelGGL((sdpa_prefill_i4_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
     else
-        hipLaunchKernelGGL((sdpa_prefill_mfma_kernel<2, NB, 4, false, D>), grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((sdpa_prefill_i4_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
 {
-    if ((a.D != 128 && a.D != 256) || a.pb < 1 || a.pb * a.n_rep > 16 * prefill_nb(a.D) ||
-        (a.bits != 4 && a.bits != 8))
+    if ((a.D != 128 && a.D != 256) || (a.bits != 4 && a.bits != 8) || a.pb < 1 ||
+        a.pb * a.n_rep > 16 * prefill_nb(a.D))
         return hipErrorInvalidValue;
-    const int64_t blocks = (a.sq + a.pb - 1) / a.pb;
+    const int64_t per_block = (int64_t)a.pb * prefill_wg(a.D, a.bits);
+    const int64_t blocks = (a.sq + per_block - 1) / per_block;
     dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
     if (a.D == 256)
         launch_prefill_d<256>(a, grid, s);

@@ -220,3 +220,42 @@ def test_unsupported_shapes_refused(what):
     with pytest.raises(kvq.KvqError) as e:
         kvq.sdpa_int4_prefill(gc, 10, q, 0.1)
     assert e.value.status == -7
+
+
+def test_prompt_from_row_zero_sampled():
+    """A 1200-position prompt from row 0 on the Llama layer's heads: many
+    workgroups, a ragged last one, and the causal triangle; sampled positions
+    (the first, tile and workgroup edges, the last) against the oracle's
+    decode attention over the rows each position sees."""
+    note("prefill prompt 1200 from row 0")
+    sq, hq, hkv = 1200, 64, 8
+    q = kvq_synth.normal((1, hq, sq, 128), [93, 0]).astype(np.float16)
+    k = kvq_synth.normal((1, hkv, sq, 128), [93, 1]).astype(np.float16)
+    v = kvq_synth.normal((1, hkv, sq, 128), [93, 2]).astype(np.float16)
+    alpha = 1 / np.sqrt(128)
+    oc = oracle.Cache(1, hkv, 128, sq, 64)
+    oc.append(k, v, 0)
+    got = _run(oc, 0, q, alpha)
+    for i in (0, 1, 3, 4, 31, 32, 33, 599, 1023, 1024, 1199):
+        ref = oracle.sdpa(oc, i + 1, np.ascontiguousarray(q[:, :, i]), alpha)
+        check_attention(got[:, :, i], ref, REL_L2, label="prompt pos %d" % i)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_small_value_ranges(bits):
+    """V rows scaled by 2^-7 (int4 value scales near 2^-9, where the split of
+    a scale into its top eight bits and the rest is still exact after
+    halving) and K rows by 2^-4: the matrix-core products stay exact, so the
+    usual gate holds."""
+    note("prefill small value ranges bits=%d" % bits)
+    q_start, sq, hq, hkv = 900, 40, 8, 2
+    S = q_start + sq
+    q = kvq_synth.normal((1, hq, sq, 128), [94, bits, 0]).astype(np.float16)
+    k = (kvq_synth.normal((1, hkv, S, 128), [94, bits, 1]) * 2.0 ** -4).astype(np.float16)
+    v = (kvq_synth.normal((1, hkv, S, 128), [94, bits, 2]) * 2.0 ** -7).astype(np.float16)
+    alpha = 1 / np.sqrt(128)
+    oc = oracle.Cache(1, hkv, 128, S, 64, bits=bits)
+    oc.append(k, v, 0)
+    got = _run(oc, q_start, q, alpha)
+    ref = oracle.sdpa_prefill(oc, q_start, q, alpha)
+    check_attention(got, ref, REL_L2, atol=2e-5, rtol=1e-2, label="prefill small values")
