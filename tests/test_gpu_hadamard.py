@@ -252,7 +252,7 @@ def test_rotated_decode_step_gemma(kernel):
     note("rotated step gemma kernel=%d" % kernel)
     q, k, v, alpha = kvq_synth.gemma_layer(787)
     got, oc = _rot_step_case(q, k.astype(np.float16), v.astype(np.float16), alpha, 786, 800, kernel)
-    check_attention(got, oracle.sdpa_rotated(oc, 787, q, alpha), 2e-4, atol=1e-3, rtol=1e-3, label="rotated gemma")
+    check_attention(got, oracle.sdpa_rotated(oc, 787, q, alpha), 1e-4, atol=1e-3, rtol=1e-3, label="rotated gemma")
 
 
 def test_rotated_decode_step_rejects_fp32_rows():

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 REL_L2 = 2e-5            # the vector-ALU gate of the int4 tests (fp32 throughout)
 MFMA_REL_L2 = 1e-4       # the matrix-core gate of the int4 tests
-REL_L2_UNSCALED = 2e-4   # softmax scale 1: score rounding passes undamped into the weights
+REL_L2_UNSCALED = 1e-4   # softmax scale 1 (test_gpu_sdpa.py): score rounding passes undamped into the weights
 KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_AUTO]
 GATE = {kvq.KERNEL_VALU: REL_L2, kvq.KERNEL_MFMA_WAVE: MFMA_REL_L2, kvq.KERNEL_AUTO: MFMA_REL_L2}
 

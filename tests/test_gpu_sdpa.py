@@ -21,10 +21,12 @@ pytestmark = pytest.mark.gpu
 MFMA_REL_L2 = 1e-4
 REL_L2 = {kvq.KERNEL_VALU: 2e-5, kvq.KERNEL_AUTO: MFMA_REL_L2, kvq.KERNEL_MFMA: MFMA_REL_L2,
           kvq.KERNEL_MFMA_SPLIT: MFMA_REL_L2, kvq.KERNEL_MFMA_WAVE: MFMA_REL_L2}
-# With softmax scale 1 and normalised Q/K the scores reach O(100); their fp32
-# rounding (~sqrt(D) * 2^-24 * sum|q k|) passes undamped into the weights, so
-# the per-head L2 gate there is set one decade wider.
-REL_L2_UNSCALED = 2e-4
+# With softmax scale 1 and normalised Q/K the scores reach O(100) and their
+# fp32 rounding passes undamped into the weights, so the vector-ALU kernel's
+# 2e-5 gate does not hold there: every kernel takes the matrix-core gate.
+# Measured worst per-head errors of these sets: 2.75e-5 (vector-ALU kernel,
+# 8-bit, 4096 rows), at most 1.4e-5 on the matrix-core kernels.
+REL_L2_UNSCALED = 1e-4
 KERNELS = [kvq.KERNEL_VALU, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE, kvq.KERNEL_AUTO]
 MATRIX = (kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_SPLIT, kvq.KERNEL_MFMA_WAVE)
 
