@@ -671,7 +671,7 @@ def main():
         att8 = layer_bytes(s8, 8) / (i8["partial_ms_avg"] * 1e-3) / 1e9
         next_rows["int8"] = {
             "workload": "the headline layer (B1 Hq64 Hkv8 D128 G64, Skv %d) with 8-bit codes: decode step "
-                        "(append inside the one-wavefront matrix-core attention kernel, then the reduce); bulk "
+                        "(append inside the eight-wavefront matrix-core attention kernel, then the reduce); bulk "
                         "append of the outlier-workload shape" % s8,
             "layer_bytes": layer_bytes(s8, 8),
             "step_us": round(i8["ms_per_step"] * 1e3, 3),
@@ -792,8 +792,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("sdpa_partial_mfma1_kernel<128, 2, false, 2, 4, 8> (the decode step's attention launch: "
-                       "eight-wavefront workgroups, appends the row, one merged partial per workgroup)"
+            "kernel": ("sdpa_partial_mfma1_kernel<128, 2, false, 2, %d, 8> (the decode step's attention launch: "
+                       "eight-wavefront workgroups, appends the row, one merged partial per workgroup)" % bits
                        if args.step == "fused" and args.kernel in ("auto", "mfma") else
                        "the attention launch of the step (also appends the row in the fused steps)"),
             "achieved": round(achieved, 2),

@@ -2,16 +2,22 @@
 
 The compiler inserts the wait states that gfx9 matrix instructions need
 around vector instructions, but it cannot see inside inline asm. Every kernel
-is compiled to assembly and checked two ways:
+is compiled to assembly and checked two ways, against the requirements of the
+CDNA3 ISA's table of independent instructions between dependent matrix (XDL)
+and vector instructions (the same numbers LLVM's hazard recognizer encodes
+for gfx940 and gfx950):
  - each v_mfma's A, B and C sources are traced back to the last instruction
    that wrote them: if that was a vector instruction (in or out of inline
    asm), at least two wait states (instructions or s_nop slots) must separate
-   the two;
+   the two (the table's VALU write -> XDL source read);
  - each vector instruction inside inline asm that reads a register a v_mfma
    wrote, or writes a register a v_mfma read as its accumulator, must come at
-   least MFMA_TO_ASM wait states after that v_mfma (more than the 16x16x32
-   and 32x32x16 instructions need), scanning back in layout order across
-   block boundaries.
+   least MFMA_TO_ASM wait states after that v_mfma, scanning back in layout
+   order across block boundaries. The table asks for the instruction's pass
+   count plus 3 (one more on gfx950) between an XDL instruction and a vector
+   read or overwrite of its registers: 12 for the 8-pass 16x16x32 f16 and
+   bf16 instructions, the only matrix instructions the kernels use (a
+   16-pass 32x32 instruction would need 20, more than MFMA_TO_ASM).
 """
 
 import os
@@ -174,3 +180,10 @@ def test_checker_flags_a_close_write():
     assert _min_wait(lines) == 2
     lines = ["v_mul_f32 v2, v2, v9", "v_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[20:23], v[0:3]"]
     assert _min_wait(lines) == 0  # an accumulator source counts too
+
+
+def test_only_eight_pass_matrix_instructions(mfma_asm):
+    """MFMA_TO_ASM covers the 8-pass 16x16x32 instructions only; a longer
+    matrix instruction would need a larger threshold."""
+    ops = set(re.findall(r"^\s*(v_mfma\w+)", mfma_asm, re.M))
+    assert ops and ops <= {"v_mfma_f32_16x16x32_f16", "v_mfma_f32_16x16x32_bf16"}, ops
