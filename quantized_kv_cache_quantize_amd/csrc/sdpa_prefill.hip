@@ -970,17 +970,18 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
 //
 // The arithmetic of sdpa_prefill_i4_kernel, with WG wavefronts per
 // workgroup on consecutive position blocks of one (batch, KV head): they
-// read the same rows, so each unpacks only 1/WG of a tile's K operands
-// (centred codes as subnormals) and of its centred V codes into LDS, one
-// wavefront in turn stages the tile's factor tables, and one barrier per
-// tile separates building tile t + 1 (into the other half of a two-slot
-// ring) from the reads of tile t. Each wavefront then scales the V codes
-// by s_hi / 2 and s_lo / 2 itself (those operands are not shared: sharing
-// them would double the LDS they take and the reads per tile). Two
-// workgroups share a CU (2 wavefronts per SIMD) with fp16 queries; with fp32
-// queries the hi and lo query operands take the LDS of a second one.
+// read the same rows, so each builds only 1/WG of a tile's matrix operands
+// into LDS: the K operands (centred codes as subnormals) and the V operands
+// (centred codes times s_hi / 2 and times s_lo / 2). One wavefront in turn
+// stages a tile's factor tables two tiles ahead (three-slot ring: the
+// builders of tile t + 1 read its value-scale halves while tile t is being
+// computed), and one barrier per tile separates building tile t + 1 (into
+// the other half of a two-slot operand ring) from the reads of tile t.
+// WG = 8 with fp16 queries (one workgroup per CU, two wavefronts per SIMD);
+// WG = 4 with fp32 queries, whose hi and lo query operands take twice the
+// LDS (one wavefront per SIMD).
 template <int PF, int NB, bool Q32, int WG>
-__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(Q32 ? 1 : 2)))
+__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WG / 4)))
 void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
 {
     constexpr int D = 128, NG = 2, W = 16, KM = 4, KPG = 2;
@@ -991,11 +992,12 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     constexpr int NVB = 2 * NG + 2;
     constexpr float kRef = 7.0f;
     constexpr int NKO = 2 * KM;   // K operands of a tile: (16-row block, 32 dimensions)
-    constexpr int NVO = 4 * NG;   // centred V operands of a tile: (scale group, mm)
+    constexpr int NVO = 4 * NG;   // V operands of a tile, hi and lo each: (scale group, mm)
     constexpr int KO = NKO / WG;  // of them built by each wavefront
     constexpr int VO = NVO / WG;
     static_assert(NKO % WG == 0 && NVO % WG == 0, "operands split evenly");
     static_assert(PT * NG == 64, "one (row, group) pair per lane of the staging wavefront");
+    static_assert(PF == 2, "tile j's words in register buffer j % 2");
 
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -1031,23 +1033,25 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
         make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
 
     __shared__ __align__(16) half8 kop[2][NKO][64];          // K operands
-    __shared__ __align__(16) half8 vop[2][NVO][64];          // centred V codes
-    __shared__ __align__(16) float xs[2][PT][NG];
-    __shared__ __align__(16) uint16_t sba[2][PT][SBL];
-    __shared__ __align__(16) uint16_t vbt[2][NVB][PT];
-    __shared__ __align__(16) uint16_t svt[2][2 * NG][PT];
+    __shared__ __align__(16) half8 vhi[2][NVO][64];          // V operands, codes x s_hi / 2
+    __shared__ __align__(16) half8 vlo[2][NVO][64];          // V operands, codes x s_lo / 2
+    __shared__ __align__(16) float xs[3][PT][NG];            // factor tables, three-slot ring
+    __shared__ __align__(16) uint16_t sba[3][PT][SBL];
+    __shared__ __align__(16) uint16_t vbt[3][NVB][PT];
+    __shared__ __align__(16) uint16_t svt[3][2 * NG][PT];
     __shared__ __align__(16) half8 q_lds[WG][NB][QH][KM][64];
     const float cs = a.score_scale;
     const float csk = cs * 1048576.0f;
     const uint32_t m_fine = 0x00F000F0u;
 
-    // this wavefront's V operands are (g, mm) = (i, wv) for i < VO (WG = 4)
-    // or (v >> 2, v & 3) with v = wv + WG i in general: the nibble to take
-    // is chosen by wave-uniform shift, mask, magic and offset
-    static_assert(WG == 4 || WG == 2 || WG == 1, "two, four or eight (g, mm) operands per wavefront");
+    // this wavefront's V operands are (g, mm) = (v >> 2, v & 3) with
+    // v = wv + WG i: the nibble to take is chosen by wave-uniform shift,
+    // mask, magic and offset
+    static_assert(WG == 8 || WG == 4, "one or two (g, mm) operands per wavefront");
 
-    if (wv == 0) {
-        const int s = lane >> 5, r = lane & 31;
+    // the constant parts of the tables, in all three slots
+    if (threadIdx.x < 3 * PT) {
+        const int s = threadIdx.x / PT, r = threadIdx.x % PT;
 #pragma unroll
         for (int k = SBR; k < SBL; ++k)
             sba[s][r][k] = k < SBR + 3 ? (uint16_t)0x3F80u : (uint16_t)0u;
@@ -1079,8 +1083,9 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
                 mt[arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
         }
     };
-    // wave-uniform selectors of this wavefront's V nibbles (mm = v & 3)
-    auto build = [&](int ti, int slot, const uint32_t (&kt)[KO], const uint32_t (&vt)[8], const uint32_t (&mt)[4]) {
+    // tile ti's operands into operand slot `slot`; its value-scale halves
+    // come from table slot `ts` (staged a tile earlier)
+    auto build = [&](int slot, int ts, const uint32_t (&kt)[KO], const uint32_t (&vt)[8]) {
 #pragma unroll
         for (int i = 0; i < KO; ++i)
             kop[slot][wv + WG * i][lane] = k_operand_centred(kt[i], m_fine);
@@ -1095,40 +1100,53 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
 #pragma unroll
         for (int i = 0; i < VO; ++i) {
             const int v = wv + WG * i;
-            const int g = v >> 2, mm = v & 3;  // g: a constant when WG = 4
+            const int g = v >> 2, mm = v & 3;
             const uint32_t sh = mm >= 2 ? 8u : 0u;
             const uint32_t mask = opaque_s((mm & 1) ? 0x00F000F0u : 0x000F000Fu);
             const uint32_t magic = opaque_v((mm & 1) ? 0x54005400u : 0x64006400u);
             const half2v off = as_h2((mm & 1) ? 0x54805480u : 0x64086408u);  // 72 or 1032
+            const uint2 h0 = *reinterpret_cast<const uint2 *>(&svt[ts][g][4 * q4]);
+            const uint2 h1 = *reinterpret_cast<const uint2 *>(&svt[ts][g][16 + 4 * q4]);
+            const uint2 l0 = *reinterpret_cast<const uint2 *>(&svt[ts][NG + g][4 * q4]);
+            const uint2 l1 = *reinterpret_cast<const uint2 *>(&svt[ts][NG + g][16 + 4 * q4]);
+            const half2v shi[4] = {as_h2(h0.x), as_h2(h0.y), as_h2(h1.x), as_h2(h1.y)};
+            const half2v slo[4] = {as_h2(l0.x), as_h2(l0.y), as_h2(l1.x), as_h2(l1.y)};
             half2v e[4];
 #pragma unroll
             for (int jp = 0; jp < 4; ++jp) {
                 const uint32_t x = g == 0 ? bx[0][jp] : bx[1][jp];
                 e[jp] = as_h2(and_or(x >> sh, mask, magic)) - off;
             }
-            vop[slot][v][lane] = cat8(e[0], e[1], e[2], e[3]);
+            vhi[slot][v][lane] = cat8(e[0] * shi[0], e[1] * shi[1], e[2] * shi[2], e[3] * shi[3]);
+            vlo[slot][v][lane] = cat8(e[0] * slo[0], e[1] * slo[1], e[2] * slo[2], e[3] * slo[3]);
         }
-        if (ti % WG == wv) {
+    };
+    // tile tj's factor tables into table slot ts, by the wavefront that
+    // loaded its metadata
+    auto stage = [&](int tj, int ts, const uint32_t (&mt)[4]) {
+        if (tj % WG == wv) {
             const int r = lane / NG, g = lane % NG;
             const uint16_t ks = (uint16_t)mt[0], kb = (uint16_t)mt[1];
             const uint16_t vsb = (uint16_t)mt[2], vbb = (uint16_t)mt[3];
-            xs[slot][r][g] = h_val(ks) * csk;
+            xs[ts][r][g] = h_val(ks) * csk;
             uint32_t bp[3];
             bf16_split3(fmaf(8.0f, h_val(ks), h_val(kb)), bp);
-            uint32_t *srow = reinterpret_cast<uint32_t *>(&sba[slot][r][6 * g]);
+            uint32_t *srow = reinterpret_cast<uint32_t *>(&sba[ts][r][6 * g]);
             srow[0] = bp[0] | (bp[0] << 16);
             srow[1] = bp[0] | (bp[1] << 16);
             srow[2] = bp[1] | (bp[2] << 16);
             const float w = fmaf(8.0f, h_val(vsb), h_val(vbb));
             const float whi = (float)__builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w, 0.0f))[0];
+            // (the halves are copied out before the bit casts: a bit cast of a
+            // vector element in place reads element 0)
             const half2v wp = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(whi, w - whi));
             const _Float16 wh = wp[0], wl = wp[1];
-            vbt[slot][2 * g][r] = __builtin_bit_cast(uint16_t, wh);
-            vbt[slot][2 * g + 1][r] = __builtin_bit_cast(uint16_t, wl);
+            vbt[ts][2 * g][r] = __builtin_bit_cast(uint16_t, wh);
+            vbt[ts][2 * g + 1][r] = __builtin_bit_cast(uint16_t, wl);
             const float shv = h_val((uint16_t)(vsb & 0xFFF8u));
             const float slv = h_val(vsb) - shv;
-            svt[slot][g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * shv));
-            svt[slot][NG + g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * slv));
+            svt[ts][g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * shv));
+            svt[ts][NG + g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * slv));
         }
     };
 
@@ -1178,12 +1196,16 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
             qsum[nb][g] = xrow_sum(gs[g]);
     }
 
-    // prologue: raw words of tiles 0 .. PF - 1, tile 0 built, tile PF loaded
+    // prologue: raw words of tiles 0 and 1; tile 0 staged, then built (its
+    // builders read its value-scale halves); tile 1 staged; tile 2 loaded
 #pragma unroll
     for (int u = 0; u < PF; ++u)
         load_tile(u, kbuf[u], vbuf[u], mbuf[u]);
-    build(0, 0, kbuf[0], vbuf[0], mbuf[0]);
-    load_tile(PF, kbuf[0], vbuf[0], mbuf[0]);
+    stage(0, 0, mbuf[0]);
+    __syncthreads();
+    build(0, 0, kbuf[0], vbuf[0]);
+    stage(1, 1, mbuf[1]);
+    load_tile(2, kbuf[0], vbuf[0], mbuf[0]);
     __syncthreads();
 
     float ref[NB];
@@ -1224,18 +1246,20 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     }
     const int vrow = min(col, 2 * NG + 1);
 
+    int ts = 0;  // table slot of tile ti (ti % 3)
 #pragma unroll 1
     for (int kk = 0; kk < ntile; kk += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             const int ti = kk + u;
             const int slot = u & 1;
+            const int ts1 = ts == 2 ? 0 : ts + 1, ts2 = ts1 == 2 ? 0 : ts1 + 1;
 
             float sc[NB][8];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 const u32x4 araw =
-                    *reinterpret_cast<const u32x4 *>(&sba[slot][16 * blk + col][8 * min(q4, NQ4 - 1)]);
+                    *reinterpret_cast<const u32x4 *>(&sba[ts][16 * blk + col][8 * min(q4, NQ4 - 1)]);
                 const bf16x8 sa = __builtin_bit_cast(bf16x8, araw);
                 float4v s[NB];
 #pragma unroll
@@ -1261,7 +1285,7 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float2 xg = *reinterpret_cast<const float2 *>(&xs[slot][16 * blk + 4 * q4 + i][0]);
+                    const float2 xg = *reinterpret_cast<const float2 *>(&xs[ts][16 * blk + 4 * q4 + i][0]);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         sc[nb][4 * blk + i] = fmaf(xg.x, sacc[0][nb][i], fmaf(xg.y, sacc[1][nb][i], s[nb][i]));
@@ -1319,34 +1343,21 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
             }
 
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const uint2 h0 = *reinterpret_cast<const uint2 *>(&svt[slot][g][4 * q4]);
-                const uint2 h1 = *reinterpret_cast<const uint2 *>(&svt[slot][g][16 + 4 * q4]);
-                const uint2 l0 = *reinterpret_cast<const uint2 *>(&svt[slot][NG + g][4 * q4]);
-                const uint2 l1 = *reinterpret_cast<const uint2 *>(&svt[slot][NG + g][16 + 4 * q4]);
-                const half2v shi[4] = {as_h2(h0.x), as_h2(h0.y), as_h2(h1.x), as_h2(h1.y)};
-                const half2v slo[4] = {as_h2(l0.x), as_h2(l0.y), as_h2(l1.x), as_h2(l1.y)};
+            for (int m = 0; m < NVO; ++m) {
+                const half8 vh = vhi[slot][m][lane], vl = vlo[slot][m][lane];
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const u32x4 cw = __builtin_bit_cast(u32x4, vop[slot][4 * g + mm][lane]);
-                    const half2v e[4] = {as_h2(cw[0]), as_h2(cw[1]), as_h2(cw[2]), as_h2(cw[3])};
-                    const half8 vh = cat8(e[0] * shi[0], e[1] * shi[1], e[2] * shi[2], e[3] * shi[3]);
-                    const half8 vl = cat8(e[0] * slo[0], e[1] * slo[1], e[2] * slo[2], e[3] * slo[3]);
-                    const int m = 4 * g + mm;
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vh, acc[nb][m], 0, 0, 0);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vh, acc[nb][m], 0, 0, 0);
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vl, acc[nb][m], 0, 0, 0);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vl, acc[nb][m], 0, 0, 0);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], vh, acc[nb][m], 0, 0, 0);
-                }
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], vh, acc[nb][m], 0, 0, 0);
             }
             {
-                const uint2 c0 = *reinterpret_cast<const uint2 *>(&vbt[slot][vrow][4 * q4]);
-                const uint2 c1 = *reinterpret_cast<const uint2 *>(&vbt[slot][vrow][16 + 4 * q4]);
+                const uint2 c0 = *reinterpret_cast<const uint2 *>(&vbt[ts][vrow][4 * q4]);
+                const uint2 c1 = *reinterpret_cast<const uint2 *>(&vbt[ts][vrow][16 + 4 * q4]);
                 const half8 bv = __builtin_bit_cast(half8, (u32x4){c0.x, c0.y, c1.x, c1.y});
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
@@ -1356,13 +1367,17 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
                     bacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, bacc[nb], 0, 0, 0);
             }
 
-            // tile ti + 1 into the other slot (its words were loaded PF tiles
-            // ago), tile ti + 1 + PF into the freed registers, then the barrier
-            // that ends the reads of slot `slot` and publishes slot `slot ^ 1`
+            // tile ti + 1's operands into the other operand slot (its words
+            // were loaded two tiles ago, its tables staged one tile ago), tile
+            // ti + 2's tables into the third table slot, tile ti + 3 into the
+            // freed registers, then the barrier that ends the reads of tile
+            // ti and publishes what was written
             const int nu = (u + 1) % PF;
-            build(ti + 1, slot ^ 1, kbuf[nu], vbuf[nu], mbuf[nu]);
-            load_tile(ti + 1 + PF, kbuf[nu], vbuf[nu], mbuf[nu]);
+            build(slot ^ 1, ts1, kbuf[nu], vbuf[nu]);
+            stage(ti + 2, ts2, mbuf[u]);
+            load_tile(ti + 3, kbuf[nu], vbuf[nu], mbuf[nu]);
             __syncthreads();
+            ts = ts1;
         }
     }
 
@@ -1409,23 +1424,25 @@ constexpr int prefill_nb(int D) { return D == 256 ? 1 : 2; }
 
 int prefill_positions_per_block(int n_rep, int D) { return 16 * prefill_nb(D) / n_rep; }
 
-// wavefronts per workgroup (consecutive position blocks of one KV head)
-constexpr int prefill_wg(int D, int bits) { return bits == 4 && D == 128 ? 4 : 1; }
+// wavefronts per workgroup (consecutive position blocks of one KV head):
+// int4 at D = 128 shares each tile's operands across 8 wavefronts with fp16
+// queries, 4 with fp32 queries (LDS)
+constexpr int prefill_wg(int D, int bits, bool q_f32) { return bits == 4 && D == 128 ? (q_f32 ? 4 : 8) : 1; }
 
 template <int D>
 void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
 {
     constexpr int NB = prefill_nb(D);
-    constexpr int WG = prefill_wg(D, 4);
+    constexpr int WG16 = prefill_wg(D, 4, false), WG32 = prefill_wg(D, 4, true);
     if (a.bits == 8 && a.q_f32)
         hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
     else if (a.bits == 8)
         hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
     else if constexpr (D == 128) {
         if (a.q_f32)
-            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, true, WG>), grid, dim3(64 * WG), 0, s, a);
+            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, true, WG32>), grid, dim3(64 * WG32), 0, s, a);
         else
-            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, false, WG>), grid, dim3(64 * WG), 0, s, a);
+            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, false, WG16>), grid, dim3(64 * WG16), 0, s, a);
     } else if (a.q_f32)
         hipLaunchKernelGGL((sdpa_prefill_i4_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
     else
@@ -1437,7 +1454,7 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
     if ((a.D != 128 && a.D != 256) || (a.bits != 4 && a.bits != 8) || a.pb < 1 ||
         a.pb * a.n_rep > 16 * prefill_nb(a.D))
         return hipErrorInvalidValue;
-    const int64_t per_block = (int64_t)a.pb * prefill_wg(a.D, a.bits);
+    const int64_t per_block = (int64_t)a.pb * prefill_wg(a.D, a.bits, a.q_f32 != 0);
     const int64_t blocks = (a.sq + per_block - 1) / per_block;
     dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
     if (a.D == 256)
