@@ -81,8 +81,10 @@ typedef enum kvq_dtype { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
 typedef enum kvq_kernel {
     KVQ_KERNEL_AUTO = 0,        /* fastest variant that supports the shape */
     KVQ_KERNEL_VALU = 1,        /* vector-ALU kernel: any supported shape */
-    KVQ_KERNEL_MFMA = 2,        /* matrix-core kernels, D in {128, 256} and (Hq/Hkv) * (D/G) <= 16;
-                                   the variant below is chosen by grid size */
+    KVQ_KERNEL_MFMA = 2,        /* matrix-core kernels, D in {128, 256}, D/G <= 4 (any Hq/Hkv: the
+                                   query heads of a KV head run in blocks of at most 16 / (D/G)
+                                   heads, each block its own grid row); the variant below is
+                                   chosen by grid size */
     KVQ_KERNEL_MFMA_SPLIT = 3,  /* matrix-core, four wavefronts per chunk (any chunk length) */
     KVQ_KERNEL_MFMA_WAVE = 4    /* matrix-core, one wavefront per chunk: chunk <= 512 and
                                    chunk * (D/G) and capacity * (D/G) multiples of 8 */
@@ -327,9 +329,10 @@ int64_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t Hq, int64_t m
  *                normalised, 16-byte aligned.
  *  workspace:    device memory owned by the caller, 16-byte aligned, at least
  *                kvq_decode_workspace_bytes(cache, Hq, len + 1) bytes
- *                (KVQ_E_SHAPE otherwise). Its first 4 * B * Hkv bytes are
- *                the arrival counters (uint32, one per (batch, KV head)):
- *                zero them once before the first call (e.g. hipMemset);
+ *                (KVQ_E_SHAPE otherwise). Its first 4 * B * Hq bytes hold
+ *                the arrival counters (uint32, one per batch, KV head and
+ *                block of its query heads, at most B * Hq of them): zero
+ *                them once before the first call (e.g. hipMemset);
  *                every call leaves them at zero again. Calls that use one
  *                workspace must not overlap in time (one stream, or ordered
  *                by events); after a call that did not complete (a fault),
@@ -338,8 +341,8 @@ int64_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t Hq, int64_t m
  *                be NULL), recorded in the kernel's own dispatch as in
  *                kvq_sdpa_int4_partial_timed.
  * The matrix-core shapes of the one-wavefront kernel run in one launch
- * (D 128 or 256, (Hq/Hkv) * (D/G) <= 16, capacity * (D/G) a multiple of 8,
- * 4- or 8-bit codes); other shapes run as kvq_decode_step with 512-row
+ * (D 128 or 256, D/G <= 4, capacity * (D/G) a multiple of 8, 4- or 8-bit
+ * codes); other shapes run as kvq_decode_step with 512-row
  * chunks (append, partial and reduce), inside the same workspace. The cache
  * row written is the one kvq_quantize_kv_append writes, bit for bit; out
  * matches kvq_sdpa_int4 within the attention tolerance (the merge order

@@ -257,6 +257,8 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     a.Hq = Hq;
     a.n_rep = n_rep;
     a.G = cache->group;
+    const int split = mfma_head_split(cache->head_dim, cache->group, n_rep);
+    a.head_split = split > 0 ? split : 1;
     a.bits = bits;
     a.score_scale = softmax_scale * kLog2e;
     a.k_new = nullptr;
@@ -531,19 +533,21 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
 }
 
 // Workspace of the single-launch decode step, for steps over at most
-// max_rows rows: per (batch, KV head) an arrival counter (padded to 256
-// bytes), then room for one merged partial per 512 rows and (batch, KV head)
-// (kMergeHeader + n_rep * D floats), which also holds the split-K partials
-// (m, l, acc, fp32) of the paths with a separate reduce.
-int64_t counter_region(const kvq_cache *c) { return ((int64_t)c->batch * c->kv_heads * 4 + 255) / 256 * 256; }
+// max_rows rows: the arrival counters, one per (batch, grid row), B * Hq at
+// most (a grid row is a KV head and a block of its query heads), padded to
+// 256 bytes; then room for one merged partial per 512 rows and grid row
+// (kMergeHeader + block heads * D floats), which also holds the split-K
+// partials (m, l, acc, fp32) of the paths with a separate reduce.
+int64_t counter_region(const kvq_cache *c, int32_t Hq) { return ((int64_t)c->batch * Hq * 4 + 255) / 256 * 256; }
 
 int64_t workspace_bytes(const kvq_cache *c, int32_t Hq, int64_t max_rows)
 {
     const int64_t n_rep = Hq / c->kv_heads, D = c->head_dim;
+    const int split = mfma_head_split(c->head_dim, c->group, (int)n_rep);
     const int64_t blocks = (max_rows + 511) / 512;
-    const int64_t merged = kMergeHeader + n_rep * D, split = n_rep * (D + 2);
-    return counter_region(c) + (int64_t)c->batch * c->kv_heads * blocks * (merged > split ? merged : split) * 4 +
-           64;
+    const int64_t merged = (split > 0 ? split : 1) * kMergeHeader + n_rep * D, partials = n_rep * (D + 2);
+    return counter_region(c, Hq) +
+           (int64_t)c->batch * c->kv_heads * blocks * (merged > partials ? merged : partials) * 4 + 64;
 }
 
 int single_launch_impl(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
@@ -567,7 +571,7 @@ int single_launch_impl(const kvq_cache *cache, int64_t len, const void *k_new, c
     if (ws_bytes < workspace_bytes(cache, Hq, skv))
         return KVQ_E_SHAPE;
     // the split-K workspace of the three-launch path, inside the same bytes
-    char *base = (char *)workspace + counter_region(cache);
+    char *base = (char *)workspace + counter_region(cache, Hq);
     const int64_t C = kvq_num_chunks(skv, 512);
     const int64_t nm = ((int64_t)cache->batch * Hq * C + 3) / 4 * 4;
     float *part_m = (float *)base, *part_l = part_m + nm, *part_acc = part_l + nm;

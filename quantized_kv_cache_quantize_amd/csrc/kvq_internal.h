@@ -65,6 +65,9 @@ struct PartialArgs {
     int32_t Hq;
     int32_t n_rep;
     int32_t G;
+    // matrix-core kernels: the n_rep query heads of a KV head run as head_split
+    // blocks of n_rep / head_split heads, one grid row each (mfma_head_split)
+    int32_t head_split;
     int32_t bits;       // 4 or 8 bits per code (the matrix-core kernels take 4 only)
     float score_scale;  // softmax_scale * log2(e)
     // Fused decode step (one-wavefront kernel only): when append_row >= 0,
@@ -86,9 +89,8 @@ struct PartialArgs {
     // and stores them as partial wg of its (batch, KV head) in merge_ws
     // (kMergeHeader + n_rep * D tagged 64-bit words: (m, l) pairs in log2
     // units, then the value sums) and takes a ticket from
-    // counters[2 (b Hkv + kvh)]; the workgroup with the last ticket merges
-    // all nwg partials into out, sets the counter back to zero and advances
-    // the epoch in counters[2 (b Hkv + kvh) + 1].
+    // counters[b * grid rows + row]; the workgroup with the last ticket
+    // merges all nwg partials into out and sets the counter back to zero.
     float *merge_ws;
     uint32_t *counters;
     float *out;
@@ -152,6 +154,7 @@ struct Launch {
 hipError_t launch_quantize(const QuantizeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_partial_valu(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l);
 bool mfma_supports(int D, int G, int n_rep, int chunk);
+int mfma_head_split(int D, int G, int n_rep);
 hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l);
 bool mfma_one_wave_ok(const PartialArgs &a, int D, int batch);
 // the fused decode step: append (a.append_row) + partial with the one-wavefront kernel

@@ -100,14 +100,16 @@ void sdpa_partial_mfma_kernel(PartialArgs a)
     const int q4 = lane >> 4;
     const int col = lane & 15;
     const int c = blockIdx.x;
-    const int kvh = blockIdx.y;
+    // grid row y = (KV head, block of its query heads): the n_rep query heads
+    // of a KV head come in head_split blocks of nrep columns each
+    const int kvh = blockIdx.y / a.head_split;
     const int b = blockIdx.z;
-    const int nrep = a.n_rep;
+    const int nrep = a.n_rep / a.head_split;
     const int R = nrep * NG;
     const int hl = col / NG, gl = col % NG;
     const bool col_on = col < R;
     const float col_mask = col_on ? 0.0f : -INFINITY;
-    const int h0 = kvh * nrep;
+    const int h0 = kvh * a.n_rep + (blockIdx.y - kvh * a.head_split) * nrep;  // first query head of the block
 
     // Rows are counted inside one (batch, KV head); the host checks that a
     // head's code array stays below 2 GiB, so 32-bit offsets suffice.
@@ -504,16 +506,17 @@ __device__ void append_new_row(const PartialArgs &a, int b, int kvh, int64_t kvr
 //    workgroup's ticket is taken, and every load of the last workgroup is
 //    issued after its own ticket came back, after every other ticket.
 // Elements are handled in pairs of adjacent dimensions (one 64-bit access).
+// bh: the (batch, grid row) index of this workgroup's counter and partials;
+// hq0: the index b * Hq + h of its first query head.
 template <int D, int NG, int WG>
-__device__ __forceinline__ void merge_epilogue(const PartialArgs &a, int b, int kvh, int nrep, const float *ml_s,
-                                               const float *acc_s)
+__device__ __forceinline__ void merge_epilogue(const PartialArgs &a, int64_t bh, int64_t hq0, int nrep,
+                                               const float *ml_s, const float *acc_s)
 {
     constexpr int NT1 = 64 * WG;
     constexpr int MAXH = 16 / NG;
     constexpr int EP = (MAXH * D / 2 + NT1 - 1) / NT1;  // dimension pairs per thread, at most
     constexpr int PB = 32 / EP;                         // partials per batch of loads (128 registers)
     const int tid = threadIdx.x;
-    const int64_t bh = (int64_t)b * a.Hkv + kvh;
     const int nwg = a.nwg;
     const int npair = nrep * D / 2;
     __syncthreads();  // every wavefront's state is in LDS
@@ -552,7 +555,7 @@ __device__ __forceinline__ void merge_epilogue(const PartialArgs &a, int b, int 
 
     if (a.part_acc) {  // split-K partial blockIdx.x of nwg, m in natural-log units
         const int64_t C = nwg;
-        const int64_t o = ((int64_t)b * a.Hq + (int64_t)kvh * nrep) * C + blockIdx.x;
+        const int64_t o = hq0 * C + blockIdx.x;
 #pragma unroll
         for (int k = 0; k < EP; ++k) {
             const int pr = tid + k * NT1;
@@ -649,7 +652,7 @@ __device__ __forceinline__ void merge_epilogue(const PartialArgs &a, int b, int 
         const int pr = tid + k * NT1;
         if (pr < npair) {
             const int h = 2 * pr / D, d = 2 * pr % D;
-            *reinterpret_cast<float2 *>(a.out + ((int64_t)b * a.Hq + (int64_t)kvh * nrep + h) * D + d) =
+            *reinterpret_cast<float2 *>(a.out + (hq0 + h) * D + d) =
                 make_float2(acc[k].x / L[k], acc[k].y / L[k]);
         }
     }
@@ -696,9 +699,10 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     const int q4 = lane >> 4;
     const int col = lane & 15;
     const int c = blockIdx.x * WG + wave;  // this wavefront's chunk of rows
-    const int kvh = blockIdx.y;
+    // grid row y = (KV head, block of its query heads), as in the split kernel
+    const int kvh = blockIdx.y / a.head_split;
     const int b = blockIdx.z;
-    const int nrep = a.n_rep;
+    const int nrep = a.n_rep / a.head_split;
     const int R = nrep * NG;
     // score column col = (head hl, scale group gl): hl * NG + gl, or with GV
     // hl + 8 gl, so that a lane and its partner of the other group are
@@ -707,7 +711,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // columns without a query head compute on zero Q and are never written;
     // every column keeps its own softmax state, so they need no masking
     const bool col_on = hl < nrep;
-    const int h0 = kvh * nrep;
+    const int h0 = kvh * a.n_rep + (blockIdx.y - kvh * a.head_split) * nrep;  // first query head of the block
     const bool low8 = (lane & 8) == 0;  // GV: this lane's V word is in group 0
 
     // Rows of this wavefront: tiles of TILE rows from t0, TS * TILE apart,
@@ -723,7 +727,10 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     const int last = t1 - 1;
     const int ntile = t1 > t0 ? (t1 - t0 + TS * TILE - 1) / (TS * TILE) : 0;
     const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
-    // uniform: the fused decode step's new row is in one of this wavefront's tiles
+    // uniform: the fused decode step's new row is in one of this wavefront's
+    // tiles. Every query-head block of the KV head quantises and stores it:
+    // the stores are the same bytes, and each block reads the row only after
+    // its own stores are complete, so no block can see the old row.
     if (a.append_row >= t0 && a.append_row < t1 && ((a.append_row - t0) / TILE) % TS == 0)
         append_new_row<D, NG, BITS>(a, b, kvh, kvrow0);
     const uint32_t rows_ok = (uint32_t)a.skv;
@@ -1264,7 +1271,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             emit([&](int h) { return &mg_ml[wave][h][0]; }, [&](int h) { return &mg_ml[wave][h][1]; },
                  [&](int h) { return &mg_acc[wave][h][0]; }, 1.0f);
         }
-        merge_epilogue<D, NG, WG>(a, b, kvh, nrep, &mg_ml[0][0][0], &mg_acc[0][0][0]);
+        merge_epilogue<D, NG, WG>(a, (int64_t)b * gridDim.y + blockIdx.y, (int64_t)b * a.Hq + h0, nrep,
+                                  &mg_ml[0][0][0], &mg_acc[0][0][0]);
     }
 }
 
@@ -1298,7 +1306,7 @@ bool one_wave_fits(const PartialArgs &a, int D, int batch)
 template <int D, int NG>
 hipError_t launch_dg8(const PartialArgs &a, int q_dtype, int batch, int variant, const Launch &l)
 {
-    dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
+    dim3 grid((unsigned)a.num_chunks, (unsigned)(a.Hkv * a.head_split), (unsigned)batch);
     if ((variant != KVQ_KERNEL_AUTO && variant != KVQ_KERNEL_MFMA && variant != KVQ_KERNEL_MFMA_WAVE) ||
         !one_wave_fits(a, D, batch))
         return hipErrorInvalidValue;
@@ -1314,8 +1322,8 @@ hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, 
 {
     if (a.bits == 8)
         return launch_dg8<D, NG>(a, q_dtype, batch, variant, l);
-    dim3 grid((unsigned)a.num_chunks, (unsigned)a.Hkv, (unsigned)batch);
-    const int64_t items = (int64_t)a.num_chunks * a.Hkv * batch;
+    dim3 grid((unsigned)a.num_chunks, (unsigned)(a.Hkv * a.head_split), (unsigned)batch);
+    const int64_t items = (int64_t)a.num_chunks * a.Hkv * a.head_split * batch;
     bool one = variant == KVQ_KERNEL_MFMA_WAVE;
     if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO)
         one = one_wave_fits(a, D, batch) && items >= kOneWaveItems;
@@ -1336,15 +1344,28 @@ hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, 
 
 }  // namespace
 
+// Query-head blocks per KV head for the matrix-core kernels: a block is the
+// largest divisor of n_rep whose (head, group) columns fit the 16 columns of
+// one score instruction; 0 when no matrix-core kernel takes the shape.
+int mfma_head_split(int D, int G, int n_rep)
+{
+    if (D != 128 && D != 256)
+        return 0;
+    if (G != 32 && G != 64 && G != 128)
+        return 0;
+    const int NG = D / G;
+    if (NG > 4 || n_rep < 1)
+        return 0;
+    for (int nsub = 16 / NG; nsub >= 1; --nsub)
+        if (n_rep % nsub == 0)
+            return n_rep / nsub;
+    return 0;
+}
+
 bool mfma_supports(int D, int G, int n_rep, int chunk)
 {
     (void)chunk;
-    if (D != 128 && D != 256)
-        return false;
-    if (G != 32 && G != 64 && G != 128)
-        return false;
-    const int NG = D / G;
-    return NG <= 4 && n_rep >= 1 && n_rep * NG <= 16;
+    return mfma_head_split(D, G, n_rep) > 0;
 }
 
 hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int batch, int variant, const Launch &l)
@@ -1388,6 +1409,7 @@ bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t 
 {
     if (!mfma_supports(D, G, n_rep, 512) || (bits != 4 && bits != 8) || skv < 1 || heads < 1)
         return false;
+    heads *= mfma_head_split(D, G, n_rep);  // workgroup rows: (batch, KV head, query-head block)
     const int NG = D / G;
     if ((cap * NG) % 8 != 0)
         return false;
@@ -1414,7 +1436,7 @@ void launch_single(const PartialArgs &a, dim3 grid, const Launch &l)
 template <int D, int NG>
 hipError_t launch_single_dg(const PartialArgs &a, int q_dtype, int batch, const Launch &l)
 {
-    const dim3 grid((unsigned)a.nwg, (unsigned)a.Hkv, (unsigned)batch);
+    const dim3 grid((unsigned)a.nwg, (unsigned)(a.Hkv * a.head_split), (unsigned)batch);
     if (a.bits == 8) {
         if (q_dtype == KVQ_F32)
             launch_single<D, NG, true, 8>(a, grid, l);

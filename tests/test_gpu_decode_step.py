@@ -93,6 +93,20 @@ def test_decode_step_head_dim_256(kernel):
     _step_and_compare(q, k, v, alpha, 785, cap=800, kernel=kernel)
 
 
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE])
+@pytest.mark.parametrize("Hq,Hkv,D,G,length", [(64, 2, 128, 64, 0), (64, 2, 128, 64, 1500), (20, 1, 256, 128, 999),
+                                               (14, 2, 128, 32, 513)])
+def test_decode_step_wide_gqa(kernel, Hq, Hkv, D, G, length):
+    """Query heads of one KV head in several blocks: every block quantises the
+    new row into the same cache bytes and attends over it."""
+    note("decode step wide gqa Hq%d Hkv%d D%d G%d len=%d kernel=%d" % (Hq, Hkv, D, G, length, kernel))
+    S = length + 1
+    q = kvq_synth.normal((1, Hq, D), [88, Hq, D, length, 0]).astype(np.float16)
+    k = kvq_synth.normal((1, Hkv, S, D), [88, Hq, D, length, 1]).astype(np.float16)
+    v = kvq_synth.normal((1, Hkv, S, D), [88, Hq, D, length, 2]).astype(np.float16)
+    _step_and_compare(q, k, v, 1 / np.sqrt(D), length, cap=(S + 15) // 8 * 8, kernel=kernel, G=G)
+
+
 def test_decode_steps_in_sequence():
     """Three tokens decoded one after another into one cache."""
     note("decode steps in sequence")

@@ -255,6 +255,21 @@ def test_rotated_decode_step_gemma(kernel):
     check_attention(got, oracle.sdpa_rotated(oc, 787, q, alpha), 1e-4, atol=1e-3, rtol=1e-3, label="rotated gemma")
 
 
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_rotated_decode_step_wide_gqa(kernel, bits):
+    """32 query heads per KV head run as four blocks of eight: each block
+    rotates its own queries and the new row, and all write the same bytes."""
+    note("rotated step wide gqa bits=%d kernel=%d" % (bits, kernel))
+    length, Hq, Hkv, D = 1500, 64, 2, 128
+    q = kvq_synth.normal((1, Hq, D), [89, bits, 0]).astype(np.float16)
+    k = kvq_synth.to_f16(kvq_synth.normal((1, Hkv, length + 1, D), [89, bits, 1]))
+    v = kvq_synth.to_f16(kvq_synth.normal((1, Hkv, length + 1, D), [89, bits, 2]))
+    alpha = 1 / np.sqrt(D)
+    got, oc = _rot_step_case(q, k, v, alpha, length, 1512, kernel, bits=bits)
+    check_attention(got, oracle.sdpa_rotated(oc, length + 1, q, alpha), 1e-4, label="rotated wide gqa")
+
+
 def test_rotated_decode_step_rejects_fp32_rows():
     note("rotated step fp32 rows")
     g = kvq.QuantKVCache(1, 8, 128, 16, 64, device="cuda")

@@ -134,6 +134,28 @@ def test_shapes(kernel, B, Hq, Hkv, D, G, qdt):
     check_attention(out, oracle.sdpa(oc, S, q, alpha), REL_L2[kernel], label="shape")
 
 
+# More query heads per KV head than the 16 columns of one score instruction
+# hold: the matrix-core kernels run each KV head's query heads in blocks
+# (n_rep 32 at D/G 2 -> 4 blocks of 8; 32 at D/G 1 -> 2 of 16; 12 at D/G 4 ->
+# 3 of 4; 8 at D/G 4 -> 2 of 4; 20 at D/G 2 -> 4 of 5; 7 at D/G 4 -> 7 of 1).
+WIDE_GQA = [(1, 64, 2, 128, 64, np.float16), (2, 32, 1, 128, 128, np.float32), (1, 24, 2, 128, 32, np.float16),
+            (1, 16, 2, 256, 64, np.float16), (1, 20, 1, 256, 128, np.float32), (1, 14, 2, 128, 32, np.float16)]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("B,Hq,Hkv,D,G,qdt", WIDE_GQA)
+@pytest.mark.parametrize("S", [700, 2100])
+def test_wide_gqa(kernel, B, Hq, Hkv, D, G, qdt, S):
+    note("sdpa wide gqa B%d Hq%d Hkv%d D%d G%d S%d kernel=%d" % (B, Hq, Hkv, D, G, S, kernel))
+    q = kvq_synth.normal((B, Hq, D), [87, Hq, D, G, S, 0]).astype(qdt)
+    k = kvq_synth.normal((B, Hkv, S, D), [87, Hq, D, G, S, 1]).astype(np.float16)
+    v = kvq_synth.normal((B, Hkv, S, D), [87, Hq, D, G, S, 2]).astype(np.float16)
+    oc = _oracle_cache(k, v, cap=S + 12, G=G)
+    alpha = 1 / np.sqrt(D)
+    out, *_ = _run(gpu_cache_from_oracle(oc), S, q, alpha, kernel)
+    check_attention(out, oracle.sdpa(oc, S, q, alpha), REL_L2[kernel], label="wide gqa")
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("skv", [33, 423, 786, 950, 8192])
 def test_gemma_unscaled(kernel, skv):

@@ -36,10 +36,10 @@ def _new_row(k, v, length):
     return (np.ascontiguousarray(k[:, :, length:length + 1]), np.ascontiguousarray(v[:, :, length:length + 1]))
 
 
-def _counters_zero(ws, gc):
-    """The arrival counters of the workspace, one uint32 per (batch, KV
-    head), are back at zero."""
-    return not ws[:4 * gc.batch * gc.kv_heads].any().item()
+def _counters_zero(ws, gc, hq):
+    """The arrival counters of the workspace (the first 4 * B * Hq bytes)
+    are back at zero."""
+    return not ws[:4 * gc.batch * hq].any().item()
 
 
 def _step(q, k, v, alpha, length, cap, G=64, bits=4, rel_l2=REL_L2, atol=2e-3, rtol=1e-2, compare_two=True):
@@ -50,7 +50,7 @@ def _step(q, k, v, alpha, length, cap, G=64, bits=4, rel_l2=REL_L2, atol=2e-3, r
     ws = kvq.decode_workspace(g, q.shape[1], length + 1)
     out = kvq.decode_step_single_launch(g, length, knd, vnd, qd, alpha, workspace=ws)
     torch.cuda.synchronize()
-    assert _counters_zero(ws, g), "arrival counters not reset"
+    assert _counters_zero(ws, g, q.shape[1]), "arrival counters not reset"
     oc.append(kn, vn, length)
     assert_cache_equal(g, oc)
     got = out.cpu().numpy()
@@ -95,7 +95,10 @@ def test_fp32_inputs(bits):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,D,G", [(2, 8, 2, 128, 64), (1, 16, 1, 128, 128), (1, 12, 4, 128, 32),
-                                          (1, 8, 8, 128, 64), (2, 16, 4, 256, 64), (1, 4, 1, 256, 32)])
+                                          (1, 8, 8, 128, 64), (2, 16, 4, 256, 64), (1, 4, 1, 256, 32),
+                                          # several query-head blocks per KV head, one arrival counter each
+                                          (1, 64, 2, 128, 64), (2, 32, 1, 128, 128), (1, 20, 1, 256, 128),
+                                          (1, 14, 2, 128, 32)])
 def test_shapes(B, Hq, Hkv, D, G):
     note("single-launch shape B%d Hq%d Hkv%d D%d G%d" % (B, Hq, Hkv, D, G))
     S = 5000
@@ -105,16 +108,16 @@ def test_shapes(B, Hq, Hkv, D, G):
     _step(q, k, v, 1 / np.sqrt(D), S - 1, cap=S + 8, G=G)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 2), (128, 64, 2)])
-def test_three_launch_shapes(D, Hq, Hkv):
-    """Shapes outside the matrix-core kernel (D 64; 32 query heads per KV
-    head) take append + partial + reduce inside the same workspace."""
-    note("single-launch fallback D%d Hq%d Hkv%d" % (D, Hq, Hkv))
+@pytest.mark.parametrize("D,G,Hq,Hkv", [(64, 64, 8, 2), (256, 32, 8, 2)])
+def test_three_launch_shapes(D, G, Hq, Hkv):
+    """Shapes outside the matrix-core kernel (D 64; eight scale groups per
+    row) take append + partial + reduce inside the same workspace."""
+    note("single-launch fallback D%d G%d Hq%d Hkv%d" % (D, G, Hq, Hkv))
     S = 1500
     q = kvq_synth.normal((1, Hq, D), [84, D, Hq, 0]).astype(np.float16)
     k = kvq_synth.normal((1, Hkv, S, D), [84, D, Hq, 1]).astype(np.float16)
     v = kvq_synth.normal((1, Hkv, S, D), [84, D, Hq, 2]).astype(np.float16)
-    _step(q, k, v, 1 / np.sqrt(D), S - 1, cap=S, rel_l2=2e-5)
+    _step(q, k, v, 1 / np.sqrt(D), S - 1, cap=S, G=G, rel_l2=2e-5)
 
 
 def test_steps_in_sequence_one_workspace():
@@ -136,7 +139,7 @@ def test_steps_in_sequence_one_workspace():
         kn, vn = _new_row(k, v, t)
         out = kvq.decode_step_single_launch(g, t, to_dev(kn), to_dev(vn), qd, alpha, workspace=ws)
         torch.cuda.synchronize()
-        assert _counters_zero(ws, g), "counters not reset after step %d" % t
+        assert _counters_zero(ws, g, q.shape[1]), "counters not reset after step %d" % t
         oc.append(kn, vn, t)
         check_attention(out.cpu().numpy(), oracle.sdpa(oc, t + 1, q, alpha), REL_L2, label="step %d" % t)
     assert_cache_equal(g, oc)
@@ -184,7 +187,7 @@ def test_graph_replays():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), "replay %d differs from the eager call" % i
-        assert _counters_zero(ws, g)
+        assert _counters_zero(ws, g, q.shape[1])
         # eager work between replays
         kvq.decode_step_single_launch(g, length, knd, vnd, qd, alpha, workspace=ws)
         torch.cuda.synchronize()
