@@ -40,6 +40,19 @@ namespace {
 
 constexpr int PT = 32;  // rows per tile
 
+// Workgroup order. A launch is one row of (position blocks x Hkv) workgroups
+// per batch entry, dispatched in index order, consecutive workgroups going to
+// the chip's eight XCDs in turn. The KV head varies fastest, so that with
+// Hkv a multiple of 8 all workgroups of a head run on one XCD and share its
+// L2 for the head's K/V rows; the position blocks come last first, so that
+// under the causal mask the workgroups with the most rows start first and the
+// short ones fill the end.
+__device__ __forceinline__ int prefill_head(const PrefillArgs &a) { return (int)(blockIdx.x % (unsigned)a.Hkv); }
+__device__ __forceinline__ int prefill_block(const PrefillArgs &a)
+{
+    return (int)(gridDim.x / (unsigned)a.Hkv) - 1 - (int)(blockIdx.x / (unsigned)a.Hkv);
+}
+
 // 8-bit codes (four per word). NB blocks of 16 query columns per wavefront
 // (every unpacked K and V operand feeds NB matrix instructions), PF tiles in
 // flight; operands are unpacked right before the instruction that reads them
@@ -84,10 +97,10 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
     const int lane = threadIdx.x;
     const int q4 = lane >> 4;
     const int col = lane & 15;
-    const int kvh = blockIdx.y;
+    const int kvh = prefill_head(a);
     const int b = blockIdx.z;
     const int nrep = a.n_rep;
-    const int p0 = blockIdx.x * a.pb;              // first position of the block
+    const int p0 = prefill_block(a) * a.pb;        // first position of the block
     const int npos = min(a.pb, a.sq - p0);         // positions in this block
     const int t_end = (int)a.q_start + p0 + npos;  // rows [0, t_end) are read
     const int t_all = (int)a.q_start + p0;         // rows <= t_all are seen by every column
@@ -564,10 +577,10 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
     const int lane = threadIdx.x;
     const int q4 = lane >> 4;
     const int col = lane & 15;
-    const int kvh = blockIdx.y;
+    const int kvh = prefill_head(a);
     const int b = blockIdx.z;
     const int nrep = a.n_rep;
-    const int p0 = blockIdx.x * a.pb;
+    const int p0 = prefill_block(a) * a.pb;
     const int npos = min(a.pb, a.sq - p0);
     const int t_end = (int)a.q_start + p0 + npos;
     const int t_all = (int)a.q_start + p0;
@@ -1003,10 +1016,10 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     const int lane = threadIdx.x & 63;
     const int q4 = lane >> 4;
     const int col = lane & 15;
-    const int kvh = blockIdx.y;
+    const int kvh = prefill_head(a);
     const int b = blockIdx.z;
     const int nrep = a.n_rep;
-    const int p0g = blockIdx.x * WG * a.pb;                // first position of the workgroup
+    const int p0g = prefill_block(a) * WG * a.pb;          // first position of the workgroup
     const int p0 = p0g + wv * a.pb;                        // of this wavefront
     const int npos = max(0, min(a.pb, a.sq - p0));         // this wavefront's positions (may be none)
     const int t_end = (int)a.q_start + min(p0g + WG * a.pb, a.sq);  // rows [0, t_end) are read
@@ -1456,7 +1469,8 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
         return hipErrorInvalidValue;
     const int64_t per_block = (int64_t)a.pb * prefill_wg(a.D, a.bits, a.q_f32 != 0);
     const int64_t blocks = (a.sq + per_block - 1) / per_block;
-    dim3 grid((unsigned)blocks, (unsigned)a.Hkv, (unsigned)batch);
+    // one row of blocks x Hkv workgroups per batch entry (prefill_head, prefill_block)
+    dim3 grid((unsigned)(blocks * a.Hkv), 1u, (unsigned)batch);
     if (a.D == 256)
         launch_prefill_d<256>(a, grid, s);
     else
