@@ -396,7 +396,9 @@ def time_gemma_decode(kvq, torch, skv: int, steps: int, warmup: int, pool_bytes:
     n_layers = max(2, min(max_layers, math.ceil(pool_bytes / gemma_bytes(skv))))
     pool = []
     for _ in range(n_layers):
-        cache = kvq.QuantKVCache(B, GEMMA_HKV, GEMMA_D, skv, G, device=dev)
+        # capacity rounded up to 8 rows: the tile kernels want each head's
+        # scale/bias rows 16-byte aligned (capacity * D/G a multiple of 8)
+        cache = kvq.QuantKVCache(B, GEMMA_HKV, GEMMA_D, (skv + 7) // 8 * 8, G, device=dev)
         k = rms_gain(torch.randn((B, GEMMA_HKV, skv, GEMMA_D), generator=gen, device=dev), gk).half()
         v = torch.randn((B, GEMMA_HKV, skv, GEMMA_D), generator=gen, device=dev).half()
         kvq.quantize_kv_append(cache, 0, k[:, :, :skv - 1].contiguous(), v[:, :, :skv - 1].contiguous())
@@ -406,23 +408,42 @@ def time_gemma_decode(kvq, torch, skv: int, steps: int, warmup: int, pool_bytes:
         out = torch.empty((B, GEMMA_HQ, GEMMA_D), dtype=torch.float32, device=dev)
         pool.append((cache, q, kn, vn, ws, out))
         del k, v
-    stream = torch.cuda.current_stream()
-
-    def run(n):
+    def run(n, stream):
         for i in range(n):
             cache, q, kn, vn, ws, out = pool[i % len(pool)]
             kvq.decode_step(cache, skv - 1, kn, vn, q, 1.0, 512, out=out, workspace=ws, stream=stream)
 
-    run(warmup)
+    stream = torch.cuda.current_stream()
+    run(warmup, stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    run(steps)
+    run(steps, stream)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    del pool
-    return us, n_layers
+    # the same steps with the host out of the loop: one pass over the pool
+    # (every layer once) captured in a HIP graph, median of 5 replays
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        run(len(pool), side)
+        with torch.cuda.graph(graph, stream=side):
+            run(len(pool), side)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / len(pool))
+    del graph, pool
+    return us, n_layers, sorted(per)[len(per) // 2]
 
 
 def time_outlier_append_decode(kvq, torch, steps: int, warmup: int, reps: int = 40):
@@ -706,10 +727,12 @@ def main():
     if not args.no_workloads:
         gem = []
         for gs in GEMMA_SKVS:
-            us, nl = time_gemma_decode(kvq, torch, gs, max(20, args.steps // 2), args.warmup, pool_bytes)
+            us, nl, gus = time_gemma_decode(kvq, torch, gs, max(20, args.steps // 2), args.warmup, pool_bytes)
             gb = gemma_bytes(gs)
             gem.append({"skv": gs, "us_per_step": round(us, 3), "gbs": round(gb / (us * 1e-6) / 1e9, 2),
-                        "frac_of_hbm_peak": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "pool_layers": nl})
+                        "frac_of_hbm_peak": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "graph_us_per_step": round(gus, 3),
+                        "graph_gbs": round(gb / (gus * 1e-6) / 1e9, 2), "pool_layers": nl})
         app_us, dec_us = time_outlier_append_decode(kvq, torch, max(20, args.steps // 2), args.warmup)
         ab = bulk_append_bytes()
         db = layer_bytes(APPEND_CAP)
@@ -720,9 +743,11 @@ def main():
             "gemma_decode": {
                 "workload": "Gemma-style unscaled decode layer: B1 Hq32 Hkv16 D256, softmax scale 1, Q/K rows at "
                             "unit RMS x per-channel gain U(0.5,2), V N(0,1); kvq_decode_step (AUTO) at each "
-                            "context; bytes = int4 K+V codes + fp16 scale/bias (4608 B per row)",
+                            "context (cache capacity: the context rounded up to 8 rows); bytes = int4 K+V codes "
+                            "+ fp16 scale/bias (4608 B per row)",
                 "timing": "events around max(20, steps/2) steps over a pool of distinct layers (<= 64; the "
-                          "short contexts then sit in the 256 MB last-level cache: latency-bound)",
+                          "short contexts then sit in the 256 MB last-level cache: latency-bound); graph_*: one "
+                          "pass over the pool captured in a HIP graph, median of 5 replays (no host issue time)",
                 "points": gem},
             "outlier_append_decode": {
                 "workload": "append of 4096 fp16 rows per KV head (Llama layout B1 Hkv8 D128 G64; K Student-t(3) "

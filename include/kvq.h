@@ -268,8 +268,10 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
  * step is two launches (attention, reduce) instead of three:
  *  - AUTO / MFMA: workgroups of eight wavefronts (four at D = 256), each
  *    wavefront streaming every eighth 32-row tile of the workgroup's rows
- *    (512 / 256 / 128 rows per wavefront, the most that still gives two
- *    wavefronts per SIMD), merged in LDS into one partial per workgroup, so
+ *    (a power of two from 512 down to 64 rows per wavefront, 128 at
+ *    D = 256: the most that still gives two wavefronts per SIMD, a
+ *    workgroup covering at least 512 rows), merged in LDS into one partial
+ *    per workgroup, so
  *    the reduce reads at most as many partials as there are chunks; out
  *    matches kvq_sdpa_int4 within the attention tolerance (a different
  *    split of the rows);

@@ -462,15 +462,21 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
         if (st)
             return st;
     }
-    // fused when the one-wavefront kernel is the one that runs: forced, or
-    // AUTO / MFMA at one (chunk, KV head) item or more per SIMD (below that
-    // the four-wavefront kernel plus a separate append is faster)
-    const int64_t items = p.a.num_chunks * cache->kv_heads * cache->batch;
-    // (8-bit caches: always, the one-wavefront kernel being their only
-    // matrix-core kernel)
-    const bool fused = p.use_mfma && mfma_one_wave_ok(p.a, cache->head_dim, cache->batch) &&
-                       (kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 || rot_inside ||
-                        ((kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) && items >= kOneWaveItems));
+    // AUTO / MFMA: the multi-wavefront workgroups of the single-launch step,
+    // each writing one split-K partial for its rows (at most the caller's
+    // chunk count of partials per head), the token's row appended inside
+    int32_t rows = 0, nwg = 0;
+    const bool one_ok = p.use_mfma && mfma_one_wave_ok(p.a, cache->head_dim, cache->batch);
+    const bool wide = one_ok && (kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) &&
+                      decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, p.a.bits,
+                                         cache->capacity, len + 1, (int64_t)cache->batch * cache->kv_heads, rows,
+                                         nwg) &&
+                      nwg <= p.a.num_chunks;
+    // fused (append inside the attention launch) whenever a one-wavefront
+    // tile kernel runs: the workgroups above, or the one-wavefront kernel
+    // forced, on 8-bit caches (their only matrix-core kernel) or with the
+    // rotation inside
+    const bool fused = one_ok && (wide || kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 || rot_inside);
     if (fused) {
         p.a.k_new = k_new;
         p.a.v_new = v_new;
@@ -495,15 +501,6 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
                 return st;
             p.a.q = out;
         }
-        // AUTO / MFMA: the multi-wavefront workgroups of the single-launch
-        // step, each writing one split-K partial for its rows (fewer partials
-        // for the reduce: at most the caller's chunk count)
-        int32_t rows = 0, nwg = 0;
-        const bool wide = (kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) &&
-                          decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, p.a.bits,
-                                             cache->capacity, len + 1, (int64_t)cache->batch * cache->kv_heads, rows,
-                                             nwg) &&
-                          nwg <= p.a.num_chunks;
         if (wide) {
             p.a.chunk = rows;
             p.a.nwg = nwg;

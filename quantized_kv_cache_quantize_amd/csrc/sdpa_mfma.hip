@@ -1396,9 +1396,10 @@ hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int bat
 
 // Single-launch decode step. Workgroups of WG wavefronts (two per SIMD of
 // one CU at D = 128, one at D = 256), each wavefront streaming `rows` rows;
-// rows is the largest of 512, 256, 128 that still gives at least two
-// wavefronts per SIMD of the 256-CU chip (at 64K rows of the Llama layer:
-// 256), so short contexts trade longer streams for more of them.
+// rows is the largest power of two from 512 down to 512 / WG that still
+// gives at least two wavefronts per SIMD of the 256-CU chip (at 64K rows of
+// the Llama layer: 256), so short contexts trade longer streams for more of
+// them.
 constexpr int64_t kSingleWaves = 2048;
 
 template <int D>
@@ -1413,10 +1414,14 @@ bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t 
     const int NG = D / G;
     if ((cap * NG) % 8 != 0)
         return false;
-    int r = 512;
-    while (r > 128 && heads * ((skv + r - 1) / r) < kSingleWaves)
-        r /= 2;
+    // rows per wavefront: halved from 512 while the grid has fewer than
+    // kSingleWaves wavefronts, down to 512 / WG (a workgroup then still
+    // covers 512 rows: at most one partial per 512 rows, the workspace's
+    // count)
     const int wg = D == 128 ? single_wg<128>() : single_wg<256>();
+    int r = 512;
+    while (r > 512 / wg && heads * ((skv + r - 1) / r) < kSingleWaves)
+        r /= 2;
     const int64_t n = (skv + (int64_t)wg * r - 1) / ((int64_t)wg * r);
     if (n > kMaxMergeGroups || (r * NG) % 8 != 0)
         return false;
