@@ -107,6 +107,20 @@ def test_decode_step_wide_gqa(kernel, Hq, Hkv, D, G, length):
     _step_and_compare(q, k, v, 1 / np.sqrt(D), length, cap=(S + 15) // 8 * 8, kernel=kernel, G=G)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,G,length", [(3, 24, 3, 128, 64, 2999), (2, 16, 4, 256, 64, 1500),
+                                                 (2, 64, 8, 128, 64, 700), (4, 8, 1, 128, 32, 63)])
+def test_decode_step_batches(B, Hq, Hkv, D, G, length):
+    """Batch entries index their own cache rows, partials and outputs in the
+    eight- (four-) wavefront workgroups, at lengths from two workgroups per
+    head down to one tile."""
+    note("decode step batch B%d Hq%d Hkv%d D%d G%d len=%d" % (B, Hq, Hkv, D, G, length))
+    S = length + 1
+    q = kvq_synth.normal((B, Hq, D), [90, B, Hq, D, 0]).astype(np.float16)
+    k = kvq_synth.normal((B, Hkv, S, D), [90, B, Hq, D, 1]).astype(np.float16)
+    v = kvq_synth.normal((B, Hkv, S, D), [90, B, Hq, D, 2]).astype(np.float16)
+    _step_and_compare(q, k, v, 1 / np.sqrt(D), length, cap=(S + 7) // 8 * 8, G=G)
+
+
 def test_decode_steps_in_sequence():
     """Three tokens decoded one after another into one cache."""
     note("decode steps in sequence")
