@@ -614,6 +614,11 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
     const float cs = a.score_scale;
     const float csk = cs * 1048576.0f;
     const uint32_t m_fine = 0x00F000F0u;
+    // 1.0 the compiler cannot see: the weights' lo halves w - hi below then
+    // stay a multiply-add whose fp16 operand hi is read as it is (one mixed
+    // fp16/fp32 FMA instead of a conversion and a subtraction); the product
+    // w * 1 and the difference are exact either way
+    const float one = __builtin_bit_cast(float, opaque_s(0x3f800000u));
 
     // the constant parts of the tables, in both slots: ones against the
     // reference pieces, zero slots, the ones and zeros columns
@@ -880,8 +885,8 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
                     const float w0 = __builtin_amdgcn_exp2f(sc[nb][j]);
                     const float w1 = __builtin_amdgcn_exp2f(sc[nb][j + 1]);
                     const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-                    const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0 - (float)h[0],
-                                                                                          w1 - (float)h[1]));
+                    const half2v l = __builtin_bit_cast(
+                        half2v, __builtin_amdgcn_cvt_pkrtz(fmaf(w0, one, -(float)h[0]), fmaf(w1, one, -(float)h[1])));
                     phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
                     plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
                 }
@@ -1056,6 +1061,11 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     const float cs = a.score_scale;
     const float csk = cs * 1048576.0f;
     const uint32_t m_fine = 0x00F000F0u;
+    // 1.0 the compiler cannot see: the weights' lo halves w - hi below then
+    // stay a multiply-add whose fp16 operand hi is read as it is (one mixed
+    // fp16/fp32 FMA instead of a conversion and a subtraction); the product
+    // w * 1 and the difference are exact either way
+    const float one = __builtin_bit_cast(float, opaque_s(0x3f800000u));
 
     // this wavefront's V operands are (g, mm) = (v >> 2, v & 3) with
     // v = wv + WG i: the nibble to take is chosen by wave-uniform shift,
@@ -1348,8 +1358,8 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
                     const float w0 = __builtin_amdgcn_exp2f(sc[nb][j]);
                     const float w1 = __builtin_amdgcn_exp2f(sc[nb][j + 1]);
                     const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-                    const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0 - (float)h[0],
-                                                                                          w1 - (float)h[1]));
+                    const half2v l = __builtin_bit_cast(
+                        half2v, __builtin_amdgcn_cvt_pkrtz(fmaf(w0, one, -(float)h[0]), fmaf(w1, one, -(float)h[1])));
                     phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
                     plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
                 }
