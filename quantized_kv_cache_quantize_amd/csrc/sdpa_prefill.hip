@@ -1053,10 +1053,13 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     __shared__ __align__(16) half8 kop[2][NKO][64];          // K operands
     __shared__ __align__(16) half8 vhi[2][NVO][64];          // V operands, codes x s_hi / 2
     __shared__ __align__(16) half8 vlo[2][NVO][64];          // V operands, codes x s_lo / 2
-    __shared__ __align__(16) float xs[3][PT][NG];            // factor tables, three-slot ring
-    __shared__ __align__(16) uint16_t sba[3][PT][SBL];
-    __shared__ __align__(16) uint16_t vbt[3][NVB][PT];
-    __shared__ __align__(16) uint16_t svt[3][2 * NG][PT];
+    // factor tables, a ring of NTS slots (slot of tile t: t % NTS), staged in
+    // batches: every WG tiles each wavefront stages one of the next WG tiles
+    constexpr int NTS = 2 * WG;
+    __shared__ __align__(16) float xs[NTS][PT][NG];
+    __shared__ __align__(16) uint16_t sba[NTS][PT][SBL];
+    __shared__ __align__(16) uint16_t vbt[NTS][NVB][PT];
+    __shared__ __align__(16) uint16_t svt[NTS][2 * NG][PT];
     __shared__ __align__(16) half8 q_lds[WG][NB][QH][KM][64];
     const float cs = a.score_scale;
     const float csk = cs * 1048576.0f;
@@ -1072,8 +1075,9 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     // mask, magic and offset
     static_assert(WG == 8 || WG == 4, "one or two (g, mm) operands per wavefront");
 
-    // the constant parts of the tables, in all three slots
-    if (threadIdx.x < 3 * PT) {
+    // the constant parts of the tables, in every slot
+    static_assert(NTS * PT <= 64 * WG, "one thread per (slot, row)");
+    if (threadIdx.x < NTS * PT) {
         const int s = threadIdx.x / PT, r = threadIdx.x % PT;
 #pragma unroll
         for (int k = SBR; k < SBL; ++k)
@@ -1085,8 +1089,7 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     constexpr uint32_t kNoRows = 0x80000000u;
     uint32_t kbuf[PF][KO];
     uint32_t vbuf[PF][8];
-    uint32_t mbuf[PF][4];
-    auto load_tile = [&](int ti, uint32_t (&kt)[KO], uint32_t (&vt)[8], uint32_t (&mt)[4]) {
+    auto load_tile = [&](int ti, uint32_t (&kt)[KO], uint32_t (&vt)[8]) {
         const bool in = ti < ntile;
         const uint32_t base = in ? (uint32_t)(PT * ti) * (uint32_t)(W * 4) : kNoRows;
 #pragma unroll
@@ -1099,12 +1102,13 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
-        if (ti % WG == wv) {  // this wavefront stages tile ti's tables
-            const uint32_t moff = in ? (uint32_t)((PT * ti) * NG + lane) * 2u : kNoRows;
+    };
+    // the scale/bias words of tile tj, one (row, group) per lane
+    auto load_meta = [&](int tj, uint32_t (&mt)[4]) {
+        const uint32_t moff = tj < ntile ? (uint32_t)((PT * tj) * NG + lane) * 2u : kNoRows;
 #pragma unroll
-            for (int arr = 0; arr < 4; ++arr)
-                mt[arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
-        }
+        for (int arr = 0; arr < 4; ++arr)
+            mt[arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
     };
     // tile ti's operands into operand slot `slot`; its value-scale halves
     // come from table slot `ts` (staged a tile earlier)
@@ -1144,33 +1148,31 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
             vlo[slot][v][lane] = cat8(e[0] * slo[0], e[1] * slo[1], e[2] * slo[2], e[3] * slo[3]);
         }
     };
-    // tile tj's factor tables into table slot ts, by the wavefront that
-    // loaded its metadata
-    auto stage = [&](int tj, int ts, const uint32_t (&mt)[4]) {
-        if (tj % WG == wv) {
-            const int r = lane / NG, g = lane % NG;
-            const uint16_t ks = (uint16_t)mt[0], kb = (uint16_t)mt[1];
-            const uint16_t vsb = (uint16_t)mt[2], vbb = (uint16_t)mt[3];
-            xs[ts][r][g] = h_val(ks) * csk;
-            uint32_t bp[3];
-            bf16_split3(fmaf(8.0f, h_val(ks), h_val(kb)), bp);
-            uint32_t *srow = reinterpret_cast<uint32_t *>(&sba[ts][r][6 * g]);
-            srow[0] = bp[0] | (bp[0] << 16);
-            srow[1] = bp[0] | (bp[1] << 16);
-            srow[2] = bp[1] | (bp[2] << 16);
-            const float w = fmaf(8.0f, h_val(vsb), h_val(vbb));
-            const float whi = (float)__builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w, 0.0f))[0];
-            // (the halves are copied out before the bit casts: a bit cast of a
-            // vector element in place reads element 0)
-            const half2v wp = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(whi, w - whi));
-            const _Float16 wh = wp[0], wl = wp[1];
-            vbt[ts][2 * g][r] = __builtin_bit_cast(uint16_t, wh);
-            vbt[ts][2 * g + 1][r] = __builtin_bit_cast(uint16_t, wl);
-            const float shv = h_val((uint16_t)(vsb & 0xFFF8u));
-            const float slv = h_val(vsb) - shv;
-            svt[ts][g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * shv));
-            svt[ts][NG + g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * slv));
-        }
+    // a tile's factor tables into table slot ts, from its scale/bias words
+    // mt (load_meta)
+    auto stage = [&](int ts, const uint32_t (&mt)[4]) {
+        const int r = lane / NG, g = lane % NG;
+        const uint16_t ks = (uint16_t)mt[0], kb = (uint16_t)mt[1];
+        const uint16_t vsb = (uint16_t)mt[2], vbb = (uint16_t)mt[3];
+        xs[ts][r][g] = h_val(ks) * csk;
+        uint32_t bp[3];
+        bf16_split3(fmaf(8.0f, h_val(ks), h_val(kb)), bp);
+        uint32_t *srow = reinterpret_cast<uint32_t *>(&sba[ts][r][6 * g]);
+        srow[0] = bp[0] | (bp[0] << 16);
+        srow[1] = bp[0] | (bp[1] << 16);
+        srow[2] = bp[1] | (bp[2] << 16);
+        const float w = fmaf(8.0f, h_val(vsb), h_val(vbb));
+        const float whi = (float)__builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w, 0.0f))[0];
+        // (the halves are copied out before the bit casts: a bit cast of a
+        // vector element in place reads element 0)
+        const half2v wp = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(whi, w - whi));
+        const _Float16 wh = wp[0], wl = wp[1];
+        vbt[ts][2 * g][r] = __builtin_bit_cast(uint16_t, wh);
+        vbt[ts][2 * g + 1][r] = __builtin_bit_cast(uint16_t, wl);
+        const float shv = h_val((uint16_t)(vsb & 0xFFF8u));
+        const float slv = h_val(vsb) - shv;
+        svt[ts][g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * shv));
+        svt[ts][NG + g][r] = __builtin_bit_cast(uint16_t, (_Float16)(0.5f * slv));
     };
 
     // query operands (as in the kernels above)
@@ -1219,16 +1221,23 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
             qsum[nb][g] = xrow_sum(gs[g]);
     }
 
-    // prologue: raw words of tiles 0 and 1; tile 0 staged, then built (its
-    // builders read its value-scale halves); tile 1 staged; tile 2 loaded
+    // prologue: raw words of tiles 0 and 1; the tables of tiles 0 and 1
+    // staged by wavefronts 0 and 1, the scale/bias words of the first batch
+    // (tiles 2 .. WG + 1, one per wavefront) loaded; then tile 0 built (its
+    // builders read its value-scale halves) and tile 2 loaded
+    uint32_t mb[4];  // this wavefront's tile of the next batch
 #pragma unroll
     for (int u = 0; u < PF; ++u)
-        load_tile(u, kbuf[u], vbuf[u], mbuf[u]);
-    stage(0, 0, mbuf[0]);
+        load_tile(u, kbuf[u], vbuf[u]);
+    if (wv < 2) {
+        uint32_t m0[4];
+        load_meta(wv, m0);
+        stage(wv, m0);
+    }
+    load_meta(2 + wv, mb);
     __syncthreads();
     build(0, 0, kbuf[0], vbuf[0]);
-    stage(1, 1, mbuf[1]);
-    load_tile(2, kbuf[0], vbuf[0], mbuf[0]);
+    load_tile(2, kbuf[0], vbuf[0]);
     __syncthreads();
 
     float ref[NB];
@@ -1269,14 +1278,13 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     }
     const int vrow = min(col, 2 * NG + 1);
 
-    int ts = 0;  // table slot of tile ti (ti % 3)
 #pragma unroll 1
     for (int kk = 0; kk < ntile; kk += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             const int ti = kk + u;
             const int slot = u & 1;
-            const int ts1 = ts == 2 ? 0 : ts + 1, ts2 = ts1 == 2 ? 0 : ts1 + 1;
+            const int ts = ti & (NTS - 1), ts1 = (ti + 1) & (NTS - 1);  // table slots of tiles ti, ti + 1
 
             float sc[NB][8];
 #pragma unroll
@@ -1391,16 +1399,21 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
             }
 
             // tile ti + 1's operands into the other operand slot (its words
-            // were loaded two tiles ago, its tables staged one tile ago), tile
-            // ti + 2's tables into the third table slot, tile ti + 3 into the
-            // freed registers, then the barrier that ends the reads of tile
-            // ti and publishes what was written
+            // were loaded two tiles ago, its tables staged at least a tile
+            // ago); every WG tiles the batch of tables of tiles ti + 2 ..
+            // ti + WG + 1 (this wavefront's: ti + 2 + wv), whose words were
+            // loaded a tile earlier, so that the wavefronts share that work
+            // evenly; tile ti + 3 into the freed registers; then the barrier
+            // that ends the reads of tile ti and publishes what was written.
+            // The batch's slots are none of tiles ti and ti + 1 (NTS >= WG + 2).
             const int nu = (u + 1) % PF;
             build(slot ^ 1, ts1, kbuf[nu], vbuf[nu]);
-            stage(ti + 2, ts2, mbuf[u]);
-            load_tile(ti + 3, kbuf[nu], vbuf[nu], mbuf[nu]);
+            if (ti % WG == 0)
+                stage((ti + 2 + wv) & (NTS - 1), mb);
+            else if ((ti + 1) % WG == 0)
+                load_meta(ti + 3 + wv, mb);
+            load_tile(ti + 3, kbuf[nu], vbuf[nu]);
             __syncthreads();
-            ts = ts1;
         }
     }
 
