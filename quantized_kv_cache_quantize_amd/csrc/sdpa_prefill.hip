@@ -990,11 +990,13 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
 // workgroup on consecutive position blocks of one (batch, KV head): they
 // read the same rows, so each builds only 1/WG of a tile's matrix operands
 // into LDS: the K operands (centred codes as subnormals) and the V operands
-// (centred codes times s_hi / 2 and times s_lo / 2). One wavefront in turn
-// stages a tile's factor tables two tiles ahead (three-slot ring: the
+// (centred codes times s_hi / 2 and times s_lo / 2). The factor tables
+// are staged in batches into a ring of 2 WG slots: every WG tiles each
+// wavefront stages one of the next WG tiles (tiles t + 2 .. t + WG + 1 at
+// tile t), so the staging falls on all wavefronts in the same tile (the
 // builders of tile t + 1 read its value-scale halves while tile t is being
-// computed), and one barrier per tile separates building tile t + 1 (into
-// the other half of a two-slot operand ring) from the reads of tile t.
+// computed); one barrier per tile separates building tile t + 1 (into the
+// other half of a two-slot operand ring) from the reads of tile t.
 // WG = 8 with fp16 queries (one workgroup per CU, two wavefronts per SIMD);
 // WG = 4 with fp32 queries, whose hi and lo query operands take twice the
 // LDS (one wavefront per SIMD).
