@@ -467,11 +467,16 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
     // chunk count of partials per head), the token's row appended inside
     int32_t rows = 0, nwg = 0;
     const bool one_ok = p.use_mfma && mfma_one_wave_ok(p.a, cache->head_dim, cache->batch);
-    const bool wide = one_ok && (kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) &&
-                      decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, p.a.bits,
-                                         cache->capacity, len + 1, (int64_t)cache->batch * cache->kv_heads, rows,
-                                         nwg) &&
-                      nwg <= p.a.num_chunks;
+    bool wide = one_ok && (kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) &&
+                decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, p.a.bits, cache->capacity,
+                                   len + 1, (int64_t)cache->batch * cache->kv_heads, rows, nwg) &&
+                nwg <= p.a.num_chunks;
+    // With the query rotated inside, every wavefront rotates it in its
+    // prologue: where the workgroups would stream fewer than 512 rows per
+    // wavefront and the one-wavefront kernel already has a chunk per SIMD,
+    // the one-wavefront kernel's 512-row streams amortise that better.
+    if (wide && rot_inside && rows < 512 && p.a.num_chunks * cache->kv_heads * cache->batch >= kOneWaveItems)
+        wide = false;
     // fused (append inside the attention launch) whenever a one-wavefront
     // tile kernel runs: the workgroups above, or the one-wavefront kernel
     // forced, on 8-bit caches (their only matrix-core kernel) or with the
