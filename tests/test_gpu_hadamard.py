@@ -270,6 +270,30 @@ def test_rotated_decode_step_wide_gqa(kernel, bits):
     check_attention(got, oracle.sdpa_rotated(oc, length + 1, q, alpha), 1e-4, label="rotated wide gqa")
 
 
+def test_rotated_decode_step_auto_kernel_choice_64k():
+    """At 64K rows of the Llama layer AUTO runs the rotated step on the
+    one-wavefront kernel (the workgroups would stream 256 rows per wavefront):
+    the same cache bytes and output bits as forcing that kernel, whose
+    arithmetic the oracle tests above check."""
+    note("rotated step auto at 64K")
+    skv = 65536
+    q, k, v, alpha = kvq_synth.llama_layer(skv)
+    outs, caches = [], []
+    for kernel in (kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE):
+        g = kvq.QuantKVCache(1, 8, 128, skv, 64, device="cuda")
+        kvq.quantize_kv_append_rotated(g, 0, to_dev(np.ascontiguousarray(k[:, :, :skv - 1])),
+                                       to_dev(np.ascontiguousarray(v[:, :, :skv - 1])))
+        out = kvq.decode_step_rotated(g, skv - 1, to_dev(np.ascontiguousarray(k[:, :, skv - 1:])),
+                                      to_dev(np.ascontiguousarray(v[:, :, skv - 1:])), to_dev(q), alpha,
+                                      kernel=kernel)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        caches.append(host_arrays(g))
+    assert np.array_equal(outs[0], outs[1]), "AUTO's rotated step differs from the one-wavefront kernel's"
+    for a, b in zip(*caches):
+        assert np.array_equal(a, b)
+
+
 def test_rotated_decode_step_rejects_fp32_rows():
     note("rotated step fp32 rows")
     g = kvq.QuantKVCache(1, 8, 128, 16, 64, device="cuda")
