@@ -1397,9 +1397,11 @@ hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int bat
 // Single-launch decode step. Workgroups of WG wavefronts (two per SIMD of
 // one CU at D = 128, one at D = 256), each wavefront streaming `rows` rows;
 // rows is the largest power of two from 512 down to 512 / WG that still
-// gives at least two wavefronts per SIMD of the 256-CU chip (at 64K rows of
-// the Llama layer: 256), so short contexts trade longer streams for more of
-// them.
+// gives as many wavefronts as the 256-CU chip holds at once (two per SIMD at
+// D = 128: at 64K rows of the Llama layer 256 rows; one per SIMD at D = 256,
+// whose kernel takes more than half a SIMD's registers), so short contexts
+// trade longer streams for more of them, and no context runs in two rounds
+// where one would do.
 constexpr int64_t kSingleWaves = 2048;
 
 template <int D>
@@ -1420,7 +1422,8 @@ bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t 
     // count)
     const int wg = D == 128 ? single_wg<128>() : single_wg<256>();
     int r = 512;
-    while (r > 512 / wg && heads * ((skv + r - 1) / r) < kSingleWaves)
+    const int64_t waves = D == 128 ? kSingleWaves : kSingleWaves / 2;
+    while (r > 512 / wg && heads * ((skv + r - 1) / r) < waves)
         r /= 2;
     const int64_t n = (skv + (int64_t)wg * r - 1) / ((int64_t)wg * r);
     if (n > kMaxMergeGroups || (r * NG) % 8 != 0)
