@@ -1453,11 +1453,9 @@ bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
            (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) && (bits == 4 || bits == 8);
 }
 
-// blocks of 16 query columns per wavefront. 8-bit codes: two at D = 128
-// (one block: 35.8 ms against 28.8 ms on the 4096-position chunk), one at
-// D = 256. int4: four at D = 128, two at D = 256 (one accumulator per output
-// leaves room for twice the columns).
 // blocks of 16 query columns per wavefront: two at D = 128, one at D = 256
+// (8-bit codes with one block at D = 128: 35.8 ms against 28.8 ms on the
+// 4096-position chunk)
 constexpr int prefill_nb(int D) { return D == 256 ? 1 : 2; }
 
 int prefill_positions_per_block(int n_rep, int D) { return 16 * prefill_nb(D) / n_rep; }
