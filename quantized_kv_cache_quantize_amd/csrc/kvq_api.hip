@@ -475,13 +475,16 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
     // prologue: where the workgroups would stream fewer than 512 rows per
     // wavefront and the one-wavefront kernel already has a chunk per SIMD,
     // the one-wavefront kernel's 512-row streams amortise that better.
-    if (wide && rot_inside && rows < 512 && p.a.num_chunks * cache->kv_heads * cache->batch >= kOneWaveItems)
+    if (wide && rot_inside && rows < 512 && p.a.num_chunks * (int64_t)cache->kv_heads * cache->batch >= kOneWaveItems)
         wide = false;
     // fused (append inside the attention launch) whenever a one-wavefront
-    // tile kernel runs: the workgroups above, or the one-wavefront kernel
-    // forced, on 8-bit caches (their only matrix-core kernel) or with the
-    // rotation inside
-    const bool fused = one_ok && (wide || kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 || rot_inside);
+    // tile kernel runs: the workgroups above; or the one-wavefront kernel:
+    // forced, on 8-bit caches (their only matrix-core kernel), with the
+    // rotation inside, or under AUTO / MFMA at a chunk per SIMD or more where
+    // the workgroups do not fit (more merge groups than they take)
+    const int64_t items = p.a.num_chunks * cache->kv_heads * cache->batch;
+    const bool fused = one_ok && (wide || kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 || rot_inside ||
+                                  ((kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) && items >= kOneWaveItems));
     if (fused) {
         p.a.k_new = k_new;
         p.a.v_new = v_new;
