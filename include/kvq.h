@@ -297,12 +297,15 @@ int kvq_decode_step(const kvq_cache *cache, int64_t len, const void *k_new, cons
  * in the original coordinates. Arguments as kvq_decode_step, but k_new and
  * v_new must be fp16 (KVQ_E_DTYPE otherwise), and `out` must not overlap q
  * unless q is fp32 and out == q (KVQ_E_SHAPE).
- * With the one-wavefront kernel and D = 128 the step is two launches: the
- * attention kernel rotates the query (fp32 butterflies, a relative error of
- * a few 2^-24) in its prologue and the appended rows (float64, exact for
- * fp16 rows) in its fused append, and the reduce rotates each head's output
- * (fp32) before storing it. Otherwise the query is first rotated into `out`
- * (four launches).
+ * At D = 128 on the matrix-core tile kernels (the one-wavefront kernel, or
+ * under AUTO / MFMA the eight-wavefront workgroups of kvq_decode_step; AUTO
+ * keeps the one-wavefront kernel where the workgroups would stream fewer
+ * than 512 rows per wavefront and it already has a chunk per SIMD) the step
+ * is two launches: the attention kernel rotates the query (fp32
+ * butterflies, a relative error of a few 2^-24) in its prologue and the
+ * appended rows (float64, exact for fp16 rows) in its fused append, and the
+ * reduce rotates each head's output (fp32) before storing it. Otherwise the
+ * query is first rotated into `out` (four launches).
  */
 int kvq_decode_step_rotated(const kvq_cache *cache, int64_t len, const void *k_new, const void *v_new, int kv_dtype,
                             const void *q, int q_dtype, int32_t Hq, float softmax_scale, int32_t chunk,

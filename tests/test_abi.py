@@ -323,6 +323,10 @@ def test_single_launch_step_validation(L):
     assert ws(c, 64, 1) > 256 and ws(c, 64, 512) == ws(c, 64, 1)
     assert ws(c, 64, 513) > ws(c, 64, 512)
     assert ws(c, 64, 131072) >= 256 + 8 * 256 * (32 + 8 * 128) * 4
+    # 32 query heads per KV head run as 4 blocks of 8: a counter and a merge
+    # header per block, the value sums of all 32 heads
+    c2 = _cache(capacity=131072, kv_heads=2)
+    assert ws(c2, 64, 131072) >= 64 * 4 + 2 * 256 * (4 * 32 + 32 * 128) * 4
     assert ws(c, 63, 100) == 0 and ws(c, 0, 100) == 0 and ws(c, 64, 0) == 0
     assert ws(_cache(head_dim=96), 64, 100) == 0
     assert _single(L, None) == E_NULL
