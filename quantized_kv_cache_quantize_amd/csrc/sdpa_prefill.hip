@@ -1447,9 +1447,12 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
 
 }  // namespace
 
+// n_rep up to the query columns of a wavefront (16 per block: 32 at D =
+// 128, 16 at D = 256), where a wavefront then takes one position of all its
+// KV head's query heads
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
 {
-    return (D == 128 || D == 256) && G == 64 && n_rep >= 1 && n_rep <= 16 &&
+    return (D == 128 || D == 256) && G == 64 && n_rep >= 1 && n_rep <= (D == 256 ? 16 : 32) &&
            (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) && (bits == 4 || bits == 8);
 }
 

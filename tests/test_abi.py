@@ -269,13 +269,14 @@ def test_prefill_validation(L):
     assert _prefill(L, _cache(), q=P + 4) == E_ALIGN
     assert _prefill(L, _cache(), out=P + 8) == E_ALIGN
     # outside the prefill kernel: head sizes other than 128 and 256, other
-    # groups, more than 16 query heads per KV head (4- and 8-bit codes, fp16
-    # and fp32 queries are inside)
+    # groups, more query heads per KV head than a wavefront's columns (32 at
+    # D 128, 16 at D 256; 4- and 8-bit codes, fp16 and fp32 queries are inside)
     assert _prefill(L, _cache(head_dim=64)) == E_UNSUP
     assert _prefill(L, _cache(group=32)) == E_UNSUP
     assert _prefill(L, _cache(head_dim=64), qd=1) == E_UNSUP
     assert _prefill(L, _cache(bits=3)) == E_SHAPE
-    assert _prefill(L, _cache(kv_heads=2), hq=64) == E_UNSUP
+    assert _prefill(L, _cache(kv_heads=1), hq=64) == E_UNSUP
+    assert _prefill(L, _cache(kv_heads=1, head_dim=256), hq=20) == E_UNSUP
 
 
 def _step_rot(L, cache, length=100, k=P, v=P, kvd=0, q=P, qd=0, hq=64, scale=0.1, chunk=512, m=P, l=P, acc=P,

@@ -53,6 +53,20 @@ def test_head_layouts(hq, hkv):
     check_attention(got, oracle.sdpa_prefill(oc, 300, q, alpha), REL_L2, label="prefill heads")
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("hq,hkv,q32", [(64, 2, False), (40, 2, False), (32, 1, True), (24, 1, False)])
+def test_wide_gqa(hq, hkv, q32, bits):
+    """More than 16 query heads per KV head at D 128: each wavefront takes one
+    position of all the KV head's query heads (32 and 20 of its 32 columns,
+    with an fp32 query too)."""
+    note("prefill wide gqa hq=%d hkv=%d q32=%d bits=%d" % (hq, hkv, q32, bits))
+    q, oc, alpha = _case(1, hq, hkv, 700, 37, seed=hq * 10 + hkv + bits, bits=bits)
+    if q32:
+        q = (q.astype(np.float32) + kvq_synth.normal(q.shape, [91, hq]).astype(np.float32) * 1e-3)
+    got = _run(oc, 700, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, 700, q, alpha), REL_L2, label="prefill wide gqa")
+
+
 @pytest.mark.parametrize("bits,D", [(4, 128), (8, 128), (4, 256), (8, 256)])
 def test_batch_two_and_spare_capacity(bits, D):
     note("prefill batch 2 bits=%d D=%d" % (bits, D))
