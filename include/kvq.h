@@ -49,7 +49,8 @@
  *    reads and writes this format. Of the split-K kernels, the vector-ALU
  *    and the one-wavefront matrix-core kernel (KVQ_KERNEL_MFMA_WAVE) read
  *    8-bit codes; AUTO and MFMA run 8-bit caches on the latter when the chunk
- *    layout fits it, else on the vector-ALU kernel.
+ *    layout fits it, else on the vector-ALU kernel. The same holds for
+ *    head_dim 64 at either code width.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -81,11 +82,12 @@ typedef enum kvq_dtype { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
 typedef enum kvq_kernel {
     KVQ_KERNEL_AUTO = 0,        /* fastest variant that supports the shape */
     KVQ_KERNEL_VALU = 1,        /* vector-ALU kernel: any supported shape */
-    KVQ_KERNEL_MFMA = 2,        /* matrix-core kernels, D in {128, 256}, D/G <= 4 (any Hq/Hkv: the
-                                   query heads of a KV head run in blocks of at most 16 / (D/G)
-                                   heads, each block its own grid row); the variant below is
-                                   chosen by grid size */
-    KVQ_KERNEL_MFMA_SPLIT = 3,  /* matrix-core, four wavefronts per chunk (any chunk length) */
+    KVQ_KERNEL_MFMA = 2,        /* matrix-core kernels, D in {64, 128, 256}, D/G <= 4 (any Hq/Hkv: the
+                                   query heads of a KV head run in blocks of at most 8 / (D/G)
+                                   heads, 16 / (D/G) at D = 128 with D/G = 2, each block its own
+                                   grid row); the variant below is chosen by grid size */
+    KVQ_KERNEL_MFMA_SPLIT = 3,  /* matrix-core, four wavefronts per chunk (any chunk length); int4
+                                   codes at D in {128, 256} only */
     KVQ_KERNEL_MFMA_WAVE = 4    /* matrix-core, one wavefront per chunk: chunk <= 512 and
                                    chunk * (D/G) and capacity * (D/G) multiples of 8 */
     /* any other value returns KVQ_E_SHAPE (5 named a two-wavefront variant, since removed) */

@@ -234,8 +234,9 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     const int bits = cache_bits(cache);
     const bool want_mfma = kernel == KVQ_KERNEL_MFMA || kernel == KVQ_KERNEL_MFMA_SPLIT ||
                            kernel == KVQ_KERNEL_MFMA_WAVE;
-    // 8-bit caches have the one-wavefront matrix-core kernel only
-    if (bits == 8 && kernel == KVQ_KERNEL_MFMA_SPLIT)
+    // 8-bit caches and head_dim 64 have the one-wavefront matrix-core kernel only
+    const bool wave_only = bits == 8 || cache->head_dim == 64;
+    if (wave_only && kernel == KVQ_KERNEL_MFMA_SPLIT)
         return KVQ_E_UNSUPPORTED;
 
     PartialArgs &a = p.a;
@@ -273,7 +274,7 @@ int prepare_partial(const kvq_cache *cache, int64_t skv, const void *q, int q_dt
     a.out = nullptr;
     a.nwg = 0;
     const bool mfma_ok = mfma_supports(cache->head_dim, cache->group, n_rep, chunk) &&
-                         (bits == 4 || mfma_one_wave_ok(a, cache->head_dim, cache->batch));
+                         (!wave_only || mfma_one_wave_ok(a, cache->head_dim, cache->batch));
     if (want_mfma && !mfma_ok)
         return KVQ_E_UNSUPPORTED;
     if (kernel == KVQ_KERNEL_MFMA_WAVE && !mfma_one_wave_ok(a, cache->head_dim, cache->batch))
@@ -479,11 +480,13 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
         wide = false;
     // fused (append inside the attention launch) whenever a one-wavefront
     // tile kernel runs: the workgroups above; or the one-wavefront kernel:
-    // forced, on 8-bit caches (their only matrix-core kernel), with the
-    // rotation inside, or under AUTO / MFMA at a chunk per SIMD or more where
-    // the workgroups do not fit (more merge groups than they take)
+    // forced, on 8-bit caches and at head_dim 64 (their only matrix-core
+    // kernel), with the rotation inside, or under AUTO / MFMA at a chunk per
+    // SIMD or more where the workgroups do not fit (more merge groups than
+    // they take)
     const int64_t items = p.a.num_chunks * cache->kv_heads * cache->batch;
-    const bool fused = one_ok && (wide || kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 || rot_inside ||
+    const bool fused = one_ok && (wide || kernel == KVQ_KERNEL_MFMA_WAVE || p.a.bits == 8 || cache->head_dim == 64 ||
+                                  rot_inside ||
                                   ((kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) && items >= kOneWaveItems));
     if (fused) {
         p.a.k_new = k_new;

@@ -666,7 +666,7 @@ __device__ __forceinline__ void merge_epilogue(const PartialArgs &a, int64_t bh,
 // one (KV head, batch) per workgroup, merged in LDS, then across workgroups
 // by the last one to arrive (merge_epilogue).
 template <int D, int NG, bool Q32, int PF, int BITS, int WG = 1>
-__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
+__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void sdpa_partial_mfma1_kernel(PartialArgs a)
 {
     // BITS = 8: byte codes, two words per eight dimensions, both K and V
@@ -678,11 +678,18 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // input range. The value products are multiplied by VU = 1 / WS when the
     // partial state is written.
     constexpr bool B8 = BITS == 8;
+    // D = 64: eight dimension octets per row, so each of the 16 value
+    // columns is half an octet (octet col & 7, dimensions 4 (col >> 3) + m,
+    // m < 4); otherwise a column is a whole octet
+    constexpr bool HV = D == 64;
     constexpr int W = D * BITS / 32;  // words per row
     constexpr int WPL = W / 4;        // K words per lane: a quarter row
+    constexpr int KV4 = (WPL + 3) / 4;  // 16-byte K loads per lane and block (int4 at D = 64: one 8-byte load)
     constexpr int KM = D / 32;        // score products per 16-row block
-    constexpr int VS = D / 128;       // sets of 16 value columns (eight dimensions each)
-    constexpr int VW = BITS / 4;      // value words per row and column
+    constexpr int VS = HV ? 1 : D / 128;  // sets of 16 value columns
+    constexpr int VM = HV ? 4 : 8;        // dimensions per value column
+    constexpr int VW = BITS / 4;      // value words per row and octet
+    constexpr int NV = HV ? 1 : VW;   // value words per row and column
     constexpr int WPG = D / 8 / NG;   // eight-dimension columns per scale group
     constexpr float VC = B8 ? 128.0f : 8.0f;     // centre of the value codes
     constexpr float WS = B8 ? 64.0f : 1.0f;      // scale of the value weights
@@ -690,9 +697,13 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     constexpr int PAIRS = TILE * NG;        // (row, group) pairs of scale/bias per tile
     constexpr int MP = (PAIRS + 63) / 64;   // pairs per lane (NG = 1: lanes 32-63 repeat 0-31)
     // D = 128 with two scale groups: value products group by group, with the
-    // hi and lo weight halves as operand rows (half the matrix instructions)
+    // hi and lo weight halves as operand rows (half the matrix instructions).
+    // Every other layout has at most 8 score columns (the host's head
+    // blocks): the hi halves of columns 0-7 are operand rows 0-7 and their lo
+    // halves rows 8-15, so that one matrix instruction takes both. Either way
+    // the lo halves are stored times kLoScale, above the fp16 subnormals.
     constexpr bool GV = D == 128 && NG == 2;
-    constexpr float LS = GV ? kLoScale : 1.0f;  // scale of the lo weight halves
+    constexpr float LS = kLoScale;  // scale of the lo weight halves
 
     const int lane = threadIdx.x & 63;
     const int wave = WG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
@@ -808,12 +819,12 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // of loads in flight the same on every path, so each wait only covers the
     // data about to be used instead of draining the whole ring.
     constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D * BITS / 8 < 2^31)
-    uint4 kbuf[PF][2][WPL / 4];
-    uint32_t vbuf[PF][VS][8 * VW];
+    uint4 kbuf[PF][2][KV4];
+    uint32_t vbuf[PF][VS][8 * NV];
     uint32_t mbuf[PF][MP][4];
     // scale/bias of a tile first, then its K and V words (a wait for the
     // scale/bias of the next tile then leaves that tile's words in flight)
-    auto load_tile = [&](int ti, uint4 (&kt)[2][WPL / 4], uint32_t (&vt)[VS][8 * VW], uint32_t (&mt)[MP][4]) {
+    auto load_tile = [&](int ti, uint4 (&kt)[2][KV4], uint32_t (&vt)[VS][8 * NV], uint32_t (&mt)[MP][4]) {
         const bool in = ti < ntile;
 #pragma unroll
         for (int p = 0; p < MP; ++p) {
@@ -827,17 +838,29 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const uint32_t off = base + (uint32_t)(((16 * blk + col) * W + WPL * q4) * 4);
+            if constexpr (WPL == 2) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(kq, off, 0, 0);
+                kt[blk][0] = make_uint4(x[0], x[1], 0u, 0u);
+            } else {
 #pragma unroll
-            for (int v4 = 0; v4 < WPL / 4; ++v4)
-                kt[blk][v4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
+                for (int v4 = 0; v4 < KV4; ++v4)
+                    kt[blk][v4] =
+                        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kq, off + 16 * v4, 0, 0));
+            }
         }
-        const uint32_t voff = base + (uint32_t)((4 * q4 * W + VW * col) * 4);
+        // first value word of this lane's column in a row; with HV the word
+        // that holds dimensions 8 (col & 7) + 4 (col >> 3) .. + 3 (int4: the
+        // word of the whole octet)
+        const int vcol = HV ? (B8 ? 2 * (col & 7) + (col >> 3) : (col & 7)) : VW * col;
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + vcol) * 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int s2 = 0; s2 < VS; ++s2) {
                 const uint32_t o = voff + ((16 * (j >> 2) + (j & 3)) * W + 16 * VW * s2) * 4;
-                if constexpr (B8) {
+                if constexpr (HV) {
+                    vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, o, 0, 0);
+                } else if constexpr (B8) {
                     const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
                     vt[s2][2 * j] = x[0];
                     vt[s2][2 * j + 1] = x[1];
@@ -937,11 +960,11 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // largest score so far, relative to m_run (the partial state is written
     // against the true maximum, which lies in [m_run - kHeadroom, m_run]).
     float m_run = 0.0f, m_part = 0.0f, l_run = 0.0f, b_run = 0.0f, m_top = -INFINITY;
-    float4v acc[VS][8];
+    float4v acc[VS][VM];
 #pragma unroll
     for (int s = 0; s < VS; ++s)
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < VM; ++m)
             acc[s][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll 1
@@ -953,8 +976,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             // they add nothing, and the loop has no exit but its own test
             const int ti = kk + u;
             const int slot = u & 1;  // PF is even, so this is ti & 1
-            const uint4 (&kcur)[2][WPL / 4] = kbuf[u];
-            const uint32_t (&vcur)[VS][8 * VW] = vbuf[u];
+            const uint4 (&kcur)[2][KV4] = kbuf[u];
+            const uint32_t (&vcur)[VS][8 * NV] = vbuf[u];
 
             // factors of the tile's 8 rows held by this lane: rows 4*q4 + i
             // (i < 4) and 16 + 4*q4 + i - 4 (i >= 4), column group gl
@@ -1027,12 +1050,12 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                     float4v corr_row;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        corr_row[i] = __shfl(corr, 4 * q4 + i);
+                        corr_row[i] = __shfl(corr, GV ? 4 * q4 + i : (4 * q4 + i) & 7);  // lo row r: column r - 8
                     mfma_result_wait();
 #pragma unroll
                     for (int s2 = 0; s2 < VS; ++s2)
 #pragma unroll
-                        for (int m = 0; m < 8; ++m)
+                        for (int m = 0; m < VM; ++m)
                             scale_in_place(acc[s2][m], corr_row);
                 }
             }
@@ -1047,8 +1070,8 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                 lsum += p0 + p1;
                 bsum = fmaf(p0, fac[j].w, fmaf(p1, fac[j + 1].w, bsum));
                 const float w0 = p0 * fac[j].z, w1 = p1 * fac[j + 1].z;
-                // any rounding of hi works: lo = w - hi is exact in fp32; with
-                // GV the lo halves have rows of their own and are kept as
+                // any rounding of hi works: lo = w - hi is exact in fp32; the
+                // lo halves have operand rows of their own and are kept as
                 // lo * kLoScale, above the fp16 subnormal range
                 const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
                 const half2v l = __builtin_bit_cast(
@@ -1058,6 +1081,18 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             }
             l_run += lsum;
             b_run += bsum;
+            // the operand rows of the other layouts: lanes 8-15 of each row
+            // of 16 (columns without a query head) take the lo halves of
+            // lanes 0-7
+            half8 alr;
+            if constexpr (!GV) {
+                const u32x4 H = __builtin_bit_cast(u32x4, phi), L = __builtin_bit_cast(u32x4, plo);
+                u32x4 A;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    A[r] = take_half_row<0xC>(H[r], L[r]);
+                alr = __builtin_bit_cast(half8, A);
+            }
             if constexpr (GV) {
                 // Group-aligned value products: row h + 8 e of group g's
                 // value operand is the hi (e = 0) or lo (e = 1) half of head
@@ -1125,7 +1160,29 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
             } else {
 #pragma unroll
                 for (int s2 = 0; s2 < VS; ++s2) {
-                    if constexpr (B8) {
+                    if constexpr (HV) {
+                        // dimension m of the column's half octet in rows (2jp,
+                        // 2jp + 1): byte m of their words (8-bit codes), or
+                        // nibble m of the two bytes the lane's half selects
+                        uint32_t xw[4];
+                        const uint32_t hsel = (col >> 3) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+                        for (int jp = 0; jp < 4; ++jp)
+                            xw[jp] = B8 ? 0u : __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], hsel);
+#pragma unroll
+                        for (int m = 0; m < VM; ++m) {
+                            half2v e[4];
+#pragma unroll
+                            for (int jp = 0; jp < 4; ++jp) {
+                                if constexpr (B8)
+                                    e[jp] = v_pair8(vcur[s2][2 * jp], vcur[s2][2 * jp + 1], sel_b[m], magic16);
+                                else
+                                    e[jp] = unpack.one(xw[jp], m);
+                            }
+                            const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                            acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alr, bv, acc[s2][m], 0, 0, 0);
+                        }
+                    } else if constexpr (B8) {
                         // column dimension m of rows (2jp, 2jp + 1): byte m & 3
                         // of their first (m < 4) or second word
 #pragma unroll
@@ -1136,28 +1193,26 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                                 e[jp] = v_pair8(vcur[s2][4 * jp + (m >> 2)], vcur[s2][4 * jp + 2 + (m >> 2)],
                                                 sel_b[m & 3], magic16);
                             const half8 bv = cat8(e[0], e[1], e[2], e[3]);
-                            acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
-                            acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
+                            acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alr, bv, acc[s2][m], 0, 0, 0);
                         }
-                        continue;
-                    }
-                    // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
-                    // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
-                    uint32_t xw[4], yw[4];
+                    } else {
+                        // rows (2jp, 2jp + 1) interleaved nibble-pair by nibble-pair:
+                        // xw holds dimensions 8col + 0..3, yw dimensions 8col + 4..7
+                        uint32_t xw[4], yw[4];
 #pragma unroll
-                    for (int jp = 0; jp < 4; ++jp) {
-                        xw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
-                        yw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
-                    }
+                        for (int jp = 0; jp < 4; ++jp) {
+                            xw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x05040100u);
+                            yw[jp] = __builtin_amdgcn_perm(vcur[s2][2 * jp + 1], vcur[s2][2 * jp], 0x07060302u);
+                        }
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        half2v e[4];
+                        for (int m = 0; m < 8; ++m) {
+                            half2v e[4];
 #pragma unroll
-                        for (int jp = 0; jp < 4; ++jp)
-                            e[jp] = unpack.one(m < 4 ? xw[jp] : yw[jp], m & 3);
-                        const half8 bv = cat8(e[0], e[1], e[2], e[3]);
-                        acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, bv, acc[s2][m], 0, 0, 0);
-                        acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, bv, acc[s2][m], 0, 0, 0);
+                            for (int jp = 0; jp < 4; ++jp)
+                                e[jp] = unpack.one(m < 4 ? xw[jp] : yw[jp], m & 3);
+                            const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+                            acc[s2][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alr, bv, acc[s2][m], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -1223,25 +1278,50 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
                                     fmaf(o[r][3], f, bias));
             }
         } else {
+            // Rows 0-7 of the value products (the hi weight halves of columns
+            // 0-7) sit in lanes q4 < 2, rows 8-15 (their lo halves times
+            // kLoScale) in lanes l + 32: a swap of the upper and lower 32
+            // lanes of a register with itself gives lanes l < 32 both, and
+            // there column rr = 4 q4 + i holds hi + lo / kLoScale.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 4 * q4 + i;
                 const float bias_r = __shfl(b_tot, rr);
                 const float f = __shfl(renorm, rr);
-                if (rr < R) {
+                float o[VS][VM];
+#pragma unroll
+                for (int s = 0; s < VS; ++s)
+#pragma unroll
+                    for (int m = 0; m < VM; ++m) {
+                        const float e = acc[s][m][i];
+                        const uint32_t x = __builtin_bit_cast(uint32_t, e);
+                        const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+                        // (through scalars: a bit cast of a vector element in place reads element 0)
+                        const uint32_t own = sw[0], lo = sw[1];
+                        o[s][m] = fmaf(__builtin_bit_cast(float, lo), 1.0f / kLoScale, __builtin_bit_cast(float, own));
+                    }
+                if (rr < R) {  // R <= 8: lanes q4 < 2
                     const int h = rr / NG, g = rr % NG;
                     float *dst = acc_at(h);
+                    const float fu = f * VU;
+                    if constexpr (HV) {
+                        const int oct = col & 7;  // the column's octet, dimensions 4 (col >> 3) .. + 3 of it
+                        if (oct / WPG == g)
+                            *reinterpret_cast<float4 *>(dst + 8 * oct + 4 * (col >> 3)) =
+                                make_float4(fmaf(o[0][0], fu, bias_r), fmaf(o[0][1], fu, bias_r),
+                                            fmaf(o[0][2], fu, bias_r), fmaf(o[0][3], fu, bias_r));
+                    } else {
 #pragma unroll
-                    for (int s = 0; s < VS; ++s) {
-                        const int word = 16 * s + col;
-                        if (word / WPG == g) {
-                            const float fu = f * VU;
-                            float4 lo = {fmaf(acc[s][0][i], fu, bias_r), fmaf(acc[s][1][i], fu, bias_r),
-                                         fmaf(acc[s][2][i], fu, bias_r), fmaf(acc[s][3][i], fu, bias_r)};
-                            float4 hi = {fmaf(acc[s][4][i], fu, bias_r), fmaf(acc[s][5][i], fu, bias_r),
-                                         fmaf(acc[s][6][i], fu, bias_r), fmaf(acc[s][7][i], fu, bias_r)};
-                            *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
-                            *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
+                        for (int s = 0; s < VS; ++s) {
+                            const int word = 16 * s + col;
+                            if (word / WPG == g) {
+                                float4 lo = {fmaf(o[s][0], fu, bias_r), fmaf(o[s][1], fu, bias_r),
+                                             fmaf(o[s][2], fu, bias_r), fmaf(o[s][3], fu, bias_r)};
+                                float4 hi = {fmaf(o[s][4], fu, bias_r), fmaf(o[s][5], fu, bias_r),
+                                             fmaf(o[s][6], fu, bias_r), fmaf(o[s][7], fu, bias_r)};
+                                *reinterpret_cast<float4 *>(dst + 8 * word) = lo;
+                                *reinterpret_cast<float4 *>(dst + 8 * word + 4) = hi;
+                            }
                         }
                     }
                 }
@@ -1276,6 +1356,16 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     }
 }
 
+// Score columns of one grid row: at most 16, and at most 8 for the
+// one-wavefront kernel's layouts other than D = 128 with two scale groups.
+template <int D, int NG>
+bool block_fits(const PartialArgs &a, bool one_wave)
+{
+    const int R = a.n_rep / a.head_split * NG;
+    return a.head_split >= 1 && a.n_rep % a.head_split == 0 &&
+           R <= ((one_wave && !(D == 128 && NG == 2)) ? 8 : 16);
+}
+
 template <int D, int NG, bool Q32, int BITS>
 void launch_one_wave(const PartialArgs &a, dim3 grid, const Launch &l)
 {
@@ -1302,61 +1392,78 @@ bool one_wave_fits(const PartialArgs &a, int D, int batch)
     return true;
 }
 
-// 8-bit caches: the one-wavefront kernel only
+// 8-bit caches and D = 64: the one-wavefront kernel only
 template <int D, int NG>
-hipError_t launch_dg8(const PartialArgs &a, int q_dtype, int batch, int variant, const Launch &l)
+hipError_t launch_dg_wave(const PartialArgs &a, int q_dtype, int batch, int variant, const Launch &l)
 {
     dim3 grid((unsigned)a.num_chunks, (unsigned)(a.Hkv * a.head_split), (unsigned)batch);
     if ((variant != KVQ_KERNEL_AUTO && variant != KVQ_KERNEL_MFMA && variant != KVQ_KERNEL_MFMA_WAVE) ||
-        !one_wave_fits(a, D, batch))
+        !one_wave_fits(a, D, batch) || !block_fits<D, NG>(a, true))
         return hipErrorInvalidValue;
-    if (q_dtype == KVQ_F32)
-        launch_one_wave<D, NG, true, 8>(a, grid, l);
-    else
-        launch_one_wave<D, NG, false, 8>(a, grid, l);
+    if (a.bits == 8) {
+        if (q_dtype == KVQ_F32)
+            launch_one_wave<D, NG, true, 8>(a, grid, l);
+        else
+            launch_one_wave<D, NG, false, 8>(a, grid, l);
+    } else {
+        if (q_dtype == KVQ_F32)
+            launch_one_wave<D, NG, true, 4>(a, grid, l);
+        else
+            launch_one_wave<D, NG, false, 4>(a, grid, l);
+    }
     return hipGetLastError();
 }
 
 template <int D, int NG>
 hipError_t launch_dg(const PartialArgs &a, int q_dtype, int batch, int variant, const Launch &l)
 {
-    if (a.bits == 8)
-        return launch_dg8<D, NG>(a, q_dtype, batch, variant, l);
-    dim3 grid((unsigned)a.num_chunks, (unsigned)(a.Hkv * a.head_split), (unsigned)batch);
-    const int64_t items = (int64_t)a.num_chunks * a.Hkv * a.head_split * batch;
-    bool one = variant == KVQ_KERNEL_MFMA_WAVE;
-    if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO)
-        one = one_wave_fits(a, D, batch) && items >= kOneWaveItems;
-    if (one && !one_wave_fits(a, D, batch))
-        return hipErrorInvalidValue;
-    if (one) {
-        if (q_dtype == KVQ_F32)
-            launch_one_wave<D, NG, true, 4>(a, grid, l);
-        else
-            launch_one_wave<D, NG, false, 4>(a, grid, l);
-    } else if (q_dtype == KVQ_F32) {
-        hipExtLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, true>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
+    if constexpr (D == 64) {
+        return launch_dg_wave<D, NG>(a, q_dtype, batch, variant, l);
     } else {
-        hipExtLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, false>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0, a);
+        if (a.bits == 8)
+            return launch_dg_wave<D, NG>(a, q_dtype, batch, variant, l);
+        dim3 grid((unsigned)a.num_chunks, (unsigned)(a.Hkv * a.head_split), (unsigned)batch);
+        const int64_t items = (int64_t)a.num_chunks * a.Hkv * a.head_split * batch;
+        bool one = variant == KVQ_KERNEL_MFMA_WAVE;
+        if (variant == KVQ_KERNEL_MFMA || variant == KVQ_KERNEL_AUTO)
+            one = one_wave_fits(a, D, batch) && items >= kOneWaveItems;
+        if ((one && !one_wave_fits(a, D, batch)) || !block_fits<D, NG>(a, one))
+            return hipErrorInvalidValue;
+        if (one) {
+            if (q_dtype == KVQ_F32)
+                launch_one_wave<D, NG, true, 4>(a, grid, l);
+            else
+                launch_one_wave<D, NG, false, 4>(a, grid, l);
+        } else if (q_dtype == KVQ_F32) {
+            hipExtLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, true>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0,
+                                  a);
+        } else {
+            hipExtLaunchKernelGGL((sdpa_partial_mfma_kernel<D, NG, false>), grid, dim3(NT), 0, l.s, l.start, l.stop, 0,
+                                  a);
+        }
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
 // Query-head blocks per KV head for the matrix-core kernels: a block is the
-// largest divisor of n_rep whose (head, group) columns fit the 16 columns of
-// one score instruction; 0 when no matrix-core kernel takes the shape.
+// largest divisor of n_rep whose (head, group) columns fit the score columns
+// of one block: the 16 of one score instruction at D = 128 with two scale
+// groups, 8 elsewhere (the one-wavefront kernel's value products there take
+// the lo weight halves as operand rows 8-15); 0 when no matrix-core kernel
+// takes the shape.
 int mfma_head_split(int D, int G, int n_rep)
 {
-    if (D != 128 && D != 256)
+    if (D != 64 && D != 128 && D != 256)
         return 0;
-    if (G != 32 && G != 64 && G != 128)
+    if ((G != 32 && G != 64 && G != 128) || G > D)
         return 0;
     const int NG = D / G;
     if (NG > 4 || n_rep < 1)
         return 0;
-    for (int nsub = 16 / NG; nsub >= 1; --nsub)
+    const int cols = (D == 128 && NG == 2) ? 16 : 8;
+    for (int nsub = cols / NG; nsub >= 1; --nsub)
         if (n_rep % nsub == 0)
             return n_rep / nsub;
     return 0;
@@ -1373,7 +1480,10 @@ hipError_t launch_partial_mfma(const PartialArgs &a, int D, int q_dtype, int bat
     if (a.bits != 4 && a.bits != 8)
         return hipErrorInvalidValue;
     const int NG = D / a.G;
-    if (D == 128) {
+    if (D == 64) {
+        if (NG == 1) return launch_dg<64, 1>(a, q_dtype, batch, variant, l);
+        if (NG == 2) return launch_dg<64, 2>(a, q_dtype, batch, variant, l);
+    } else if (D == 128) {
         if (NG == 1) return launch_dg<128, 1>(a, q_dtype, batch, variant, l);
         if (NG == 2) return launch_dg<128, 2>(a, q_dtype, batch, variant, l);
         if (NG == 4) return launch_dg<128, 4>(a, q_dtype, batch, variant, l);
@@ -1405,7 +1515,7 @@ hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int bat
 constexpr int64_t kSingleWaves = 2048;
 
 template <int D>
-constexpr int single_wg() { return D == 128 ? 8 : 4; }
+constexpr int single_wg() { return D <= 128 ? 8 : 4; }
 
 bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t skv, int64_t heads, int32_t &rows,
                         int32_t &nwg)
@@ -1420,9 +1530,9 @@ bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t 
     // kSingleWaves wavefronts, down to 512 / WG (a workgroup then still
     // covers 512 rows: at most one partial per 512 rows, the workspace's
     // count)
-    const int wg = D == 128 ? single_wg<128>() : single_wg<256>();
+    const int wg = D <= 128 ? single_wg<128>() : single_wg<256>();
     int r = 512;
-    const int64_t waves = D == 128 ? kSingleWaves : kSingleWaves / 2;
+    const int64_t waves = D <= 128 ? kSingleWaves : kSingleWaves / 2;
     while (r > 512 / wg && heads * ((skv + r - 1) / r) < waves)
         r /= 2;
     const int64_t n = (skv + (int64_t)wg * r - 1) / ((int64_t)wg * r);
@@ -1445,6 +1555,8 @@ template <int D, int NG>
 hipError_t launch_single_dg(const PartialArgs &a, int q_dtype, int batch, const Launch &l)
 {
     const dim3 grid((unsigned)a.nwg, (unsigned)(a.Hkv * a.head_split), (unsigned)batch);
+    if (!block_fits<D, NG>(a, true))
+        return hipErrorInvalidValue;
     if (a.bits == 8) {
         if (q_dtype == KVQ_F32)
             launch_single<D, NG, true, 8>(a, grid, l);
@@ -1466,7 +1578,10 @@ hipError_t launch_decode_single(const PartialArgs &a, int D, int q_dtype, int ba
     if (a.nwg < 1 || a.chunk > CH1 || (!a.part_acc && (!a.merge_ws || !a.counters || !a.out)))
         return hipErrorInvalidValue;
     const int NG = D / a.G;
-    if (D == 128) {
+    if (D == 64) {
+        if (NG == 1) return launch_single_dg<64, 1>(a, q_dtype, batch, l);
+        if (NG == 2) return launch_single_dg<64, 2>(a, q_dtype, batch, l);
+    } else if (D == 128) {
         if (NG == 1) return launch_single_dg<128, 1>(a, q_dtype, batch, l);
         if (NG == 2) return launch_single_dg<128, 2>(a, q_dtype, batch, l);
         if (NG == 4) return launch_single_dg<128, 4>(a, q_dtype, batch, l);

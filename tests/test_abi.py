@@ -154,6 +154,15 @@ def test_bits_validation(L):
     # ... and it needs chunks of at most 512 rows
     assert _partial(L, _cache(bits=8), kernel=4, chunk=1024) == E_UNSUP
     assert _partial(L, _cache(bits=8), kernel=2, chunk=1024) == E_UNSUP
+    # head_dim 64 likewise (int4 and int8): no four-wavefront variant, and
+    # the one-wavefront kernel's chunks of at most 512 rows
+    for bits in (4, 8):
+        assert _partial(L, _cache(head_dim=64, bits=bits), kernel=3) == E_UNSUP
+        assert _step(L, _cache(head_dim=64, bits=bits), kernel=3) == E_UNSUP
+        assert _partial(L, _cache(head_dim=64, bits=bits), kernel=4, chunk=1024) == E_UNSUP
+        assert _partial(L, _cache(head_dim=64, group=32, bits=bits), kernel=2, chunk=1024) == E_UNSUP
+        # scale/bias rows of a head must start on 16 bytes (capacity * D/G a multiple of 8)
+        assert _partial(L, _cache(head_dim=64, capacity=1020, bits=bits), kernel=4) == E_UNSUP
 
 
 def _append_rot(L, cache, length=0, k=P, v=P, dtype=0, n=1):

@@ -257,6 +257,21 @@ def test_rotated_decode_step_gemma(kernel):
 
 @pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE])
 @pytest.mark.parametrize("bits", [4, 8])
+def test_rotated_decode_step_head_dim_64(kernel, bits):
+    """D = 64: the query rotated before the attention kernel, the new rows
+    inside its append (eight lanes per row), half-octet value columns."""
+    note("rotated step d64 bits=%d kernel=%d" % (bits, kernel))
+    length, Hq, Hkv, D = 2500, 32, 8, 64
+    q = kvq_synth.normal((1, Hq, D), [90, bits, 0]).astype(np.float16)
+    k = kvq_synth.to_f16(kvq_synth.normal((1, Hkv, length + 1, D), [90, bits, 1]))
+    v = kvq_synth.to_f16(kvq_synth.normal((1, Hkv, length + 1, D), [90, bits, 2]))
+    alpha = 1 / np.sqrt(D)
+    got, oc = _rot_step_case(q, k, v, alpha, length, 2504, kernel, bits=bits)
+    check_attention(got, oracle.sdpa_rotated(oc, length + 1, q, alpha), 1e-4, label="rotated d64")
+
+
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_WAVE])
+@pytest.mark.parametrize("bits", [4, 8])
 def test_rotated_decode_step_wide_gqa(kernel, bits):
     """32 query heads per KV head run as four blocks of eight: each block
     rotates its own queries and the new row, and all write the same bytes."""

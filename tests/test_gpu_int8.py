@@ -116,7 +116,7 @@ def test_ragged(kernel, skv, chunk):
                                               (1, 16, 1, 128, 64, np.float16), (1, 8, 1, 256, 128, np.float32),
                                               (1, 2, 2, 256, 64, np.float16), (2, 8, 2, 128, 32, np.float32),
                                               (1, 4, 1, 64, 64, np.float16),
-                                              # query heads of a KV head in blocks (32 -> 4 x 8, 20 -> 4 x 5)
+                                              # query heads of a KV head in blocks (32 -> 4 x 8, 20 -> 5 x 4)
                                               (1, 64, 2, 128, 64, np.float16), (1, 20, 1, 256, 128, np.float32)])
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_shapes(kernel, B, Hq, Hkv, D, G, qdt):

@@ -136,8 +136,10 @@ def test_shapes(kernel, B, Hq, Hkv, D, G, qdt):
 
 # More query heads per KV head than the 16 columns of one score instruction
 # hold: the matrix-core kernels run each KV head's query heads in blocks
-# (n_rep 32 at D/G 2 -> 4 blocks of 8; 32 at D/G 1 -> 2 of 16; 12 at D/G 4 ->
-# 3 of 4; 8 at D/G 4 -> 2 of 4; 20 at D/G 2 -> 4 of 5; 7 at D/G 4 -> 7 of 1).
+# (at most 16 (head, group) columns per block at D = 128, D/G = 2, else 8:
+# n_rep 32 at D 128, D/G 2 -> 4 blocks of 8; 32 at D/G 1 -> 4 of 8; 12 at D/G
+# 4 -> 6 of 2; 8 at D/G 4 -> 4 of 2; 20 at D 256, D/G 2 -> 5 of 4; 7 at D/G 4
+# -> 7 of 1).
 WIDE_GQA = [(1, 64, 2, 128, 64, np.float16), (2, 32, 1, 128, 128, np.float32), (1, 24, 2, 128, 32, np.float16),
             (1, 16, 2, 256, 64, np.float16), (1, 20, 1, 256, 128, np.float32), (1, 14, 2, 128, 32, np.float16)]
 
