@@ -677,6 +677,7 @@ void sdpa_partial_mfma1_kernel(PartialArgs a)
     // p * s_v * 2^6 <= 514 * 64 stays below the fp16 maximum for any fp16
     // input range. The value products are multiplied by VU = 1 / WS when the
     // partial state is written.
+    static_assert(PF % 2 == 0, "the scale/bias ring alternates two slots");
     constexpr bool B8 = BITS == 8;
     // D = 64: eight dimension octets per row, so each of the 16 value
     // columns is half an octet (octet col & 7, dimensions 4 (col >> 3) + m,
@@ -1366,14 +1367,19 @@ bool block_fits(const PartialArgs &a, bool one_wave)
            R <= ((one_wave && !(D == 128 && NG == 2)) ? 8 : 16);
 }
 
+// Tiles in flight per wavefront (even: the scale/bias ring has two slots):
+// two. With 2048 wavefronts at 128K that is 19 MB of int4 tiles requested at
+// the start; four (38 MB) measured 6% slower at 128K and 10% at 64K
+// (presumably because each wavefront's first tile then queues behind more of
+// the others' requests). At D = 64, whose tiles are half as many bytes, four
+// and six measured 7% and 19% slower at 128K.
+template <int D>
+constexpr int ring_depth() { return 2; }
+
 template <int D, int NG, bool Q32, int BITS>
 void launch_one_wave(const PartialArgs &a, dim3 grid, const Launch &l)
 {
-    // two tiles in flight per wavefront: with 2048 wavefronts at 128K that is
-    // 19 MB of int4 tiles requested at the start. Four int4 tiles (38 MB)
-    // measured 6% slower at 128K and 10% at 64K (presumably because each
-    // wavefront's first tile then queues behind more of the others' requests).
-    constexpr int PF = 2;
+    constexpr int PF = ring_depth<D>();
     hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, PF, BITS>), grid, dim3(64), 0, l.s, l.start, l.stop,
                           0, a);
 }
@@ -1547,8 +1553,8 @@ template <int D, int NG, bool Q32, int BITS>
 void launch_single(const PartialArgs &a, dim3 grid, const Launch &l)
 {
     constexpr int WG = single_wg<D>();
-    hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, 2, BITS, WG>), grid, dim3(64 * WG), 0, l.s, l.start,
-                          l.stop, 0, a);
+    hipExtLaunchKernelGGL((sdpa_partial_mfma1_kernel<D, NG, Q32, ring_depth<D>(), BITS, WG>), grid, dim3(64 * WG), 0,
+                          l.s, l.start, l.stop, 0, a);
 }
 
 template <int D, int NG>
