@@ -396,9 +396,7 @@ def time_gemma_decode(kvq, torch, skv: int, steps: int, warmup: int, pool_bytes:
     n_layers = max(2, min(max_layers, math.ceil(pool_bytes / gemma_bytes(skv))))
     pool = []
     for _ in range(n_layers):
-        # capacity rounded up to 8 rows: the tile kernels want each head's
-        # scale/bias rows 16-byte aligned (capacity * D/G a multiple of 8)
-        cache = kvq.QuantKVCache(B, GEMMA_HKV, GEMMA_D, (skv + 7) // 8 * 8, G, device=dev)
+        cache = kvq.QuantKVCache(B, GEMMA_HKV, GEMMA_D, skv, G, device=dev)
         k = rms_gain(torch.randn((B, GEMMA_HKV, skv, GEMMA_D), generator=gen, device=dev), gk).half()
         v = torch.randn((B, GEMMA_HKV, skv, GEMMA_D), generator=gen, device=dev).half()
         kvq.quantize_kv_append(cache, 0, k[:, :, :skv - 1].contiguous(), v[:, :, :skv - 1].contiguous())
@@ -743,7 +741,7 @@ def main():
             "gemma_decode": {
                 "workload": "Gemma-style unscaled decode layer: B1 Hq32 Hkv16 D256, softmax scale 1, Q/K rows at "
                             "unit RMS x per-channel gain U(0.5,2), V N(0,1); kvq_decode_step (AUTO) at each "
-                            "context (cache capacity: the context rounded up to 8 rows); bytes = int4 K+V codes "
+                            "context (cache capacity: the context); bytes = int4 K+V codes "
                             "+ fp16 scale/bias (4608 B per row)",
                 "timing": "events around max(20, steps/2) steps over a pool of distinct layers (<= 64; the "
                           "short contexts then sit in the 256 MB last-level cache: latency-bound); graph_*: one "

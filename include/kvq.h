@@ -88,8 +88,7 @@ typedef enum kvq_kernel {
                                    grid row); the variant below is chosen by grid size */
     KVQ_KERNEL_MFMA_SPLIT = 3,  /* matrix-core, four wavefronts per chunk (any chunk length); int4
                                    codes at D in {128, 256} only */
-    KVQ_KERNEL_MFMA_WAVE = 4    /* matrix-core, one wavefront per chunk: chunk <= 512 and
-                                   chunk * (D/G) and capacity * (D/G) multiples of 8 */
+    KVQ_KERNEL_MFMA_WAVE = 4    /* matrix-core, one wavefront per chunk: chunk <= 512 */
     /* any other value returns KVQ_E_SHAPE (5 named a two-wavefront variant, since removed) */
 } kvq_kernel;
 
@@ -349,8 +348,8 @@ int64_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t Hq, int64_t m
  *                be NULL), recorded in the kernel's own dispatch as in
  *                kvq_sdpa_int4_partial_timed.
  * The matrix-core shapes of the one-wavefront kernel run in one launch
- * (D 128 or 256, D/G <= 4, capacity * (D/G) a multiple of 8, 4- or 8-bit
- * codes); other shapes run as kvq_decode_step with 512-row
+ * (D 64, 128 or 256, D/G <= 4, 4- or 8-bit codes); other shapes run as
+ * kvq_decode_step with 512-row
  * chunks (append, partial and reduce), inside the same workspace. The cache
  * row written is the one kvq_quantize_kv_append writes, bit for bit; out
  * matches kvq_sdpa_int4 within the attention tolerance (the merge order

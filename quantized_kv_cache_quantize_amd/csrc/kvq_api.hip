@@ -469,8 +469,8 @@ int decode_step_impl(const kvq_cache *cache, int64_t len, const void *k_new, con
     int32_t rows = 0, nwg = 0;
     const bool one_ok = p.use_mfma && mfma_one_wave_ok(p.a, cache->head_dim, cache->batch);
     bool wide = one_ok && (kernel == KVQ_KERNEL_AUTO || kernel == KVQ_KERNEL_MFMA) &&
-                decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, p.a.bits, cache->capacity,
-                                   len + 1, (int64_t)cache->batch * cache->kv_heads, rows, nwg) &&
+                decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, p.a.bits, len + 1,
+                                   (int64_t)cache->batch * cache->kv_heads, rows, nwg) &&
                 nwg <= p.a.num_chunks;
     // With the query rotated inside, every wavefront rotates it in its
     // prologue: where the workgroups would stream fewer than 512 rows per
@@ -590,10 +590,10 @@ int single_launch_impl(const kvq_cache *cache, int64_t len, const void *k_new, c
         return st;
     int32_t rows = 0, nwg = 0;
     const int64_t heads = (int64_t)cache->batch * cache->kv_heads;
-    if (p.use_mfma && decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, cache_bits(cache),
-                                         cache->capacity, skv, heads, rows, nwg)) {
+    if (p.use_mfma && decode_single_plan(cache->head_dim, cache->group, Hq / cache->kv_heads, cache_bits(cache), skv,
+                                         heads, rows, nwg)) {
         p.a.chunk = rows;
-        p.a.num_chunks = (int64_t)nwg * (cache->head_dim == 128 ? 8 : 4);
+        p.a.num_chunks = (int64_t)nwg * (cache->head_dim <= 128 ? 8 : 4);  // wavefronts: eight per workgroup up to D 128
         p.a.k_new = k_new;
         p.a.v_new = v_new;
         p.a.append_row = len;

@@ -162,8 +162,7 @@ hipError_t launch_decode_fused(const PartialArgs &a, int D, int q_dtype, int bat
 // the single-launch decode step: rows per wavefront and workgroups per
 // (batch, KV head) for a step over skv rows, or false if the shape does not
 // take it
-bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t skv, int64_t heads, int32_t &rows,
-                        int32_t &nwg);
+bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t skv, int64_t heads, int32_t &rows, int32_t &nwg);
 hipError_t launch_decode_single(const PartialArgs &a, int D, int q_dtype, int batch, const Launch &l);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 

@@ -1384,18 +1384,15 @@ void launch_one_wave(const PartialArgs &a, dim3 grid, const Launch &l)
                           0, a);
 }
 
-// The one-wavefront kernel needs chunks of at most 512 rows whose scale/bias
-// segments start on 16-byte boundaries; it pays off once there are enough
-// (chunk, head) items to give every SIMD two wavefronts.
+// The one-wavefront kernel needs chunks of at most 512 rows (its scale and
+// bias arrive as one 2-byte load per (row, group) and array, so any capacity
+// and chunk length will do); it pays off once there are enough (chunk, head)
+// items to give every SIMD two wavefronts.
 bool one_wave_fits(const PartialArgs &a, int D, int batch)
 {
-    const int NG = D / a.G;
-    if (a.chunk > CH1)
-        return false;
-    if (((int64_t)a.chunk * NG) % 8 != 0 || (a.cap * NG) % 8 != 0)
-        return false;
+    (void)D;
     (void)batch;
-    return true;
+    return a.chunk <= CH1;
 }
 
 // 8-bit caches and D = 64: the one-wavefront kernel only
@@ -1523,15 +1520,11 @@ constexpr int64_t kSingleWaves = 2048;
 template <int D>
 constexpr int single_wg() { return D <= 128 ? 8 : 4; }
 
-bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t skv, int64_t heads, int32_t &rows,
-                        int32_t &nwg)
+bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t skv, int64_t heads, int32_t &rows, int32_t &nwg)
 {
     if (!mfma_supports(D, G, n_rep, 512) || (bits != 4 && bits != 8) || skv < 1 || heads < 1)
         return false;
     heads *= mfma_head_split(D, G, n_rep);  // workgroup rows: (batch, KV head, query-head block)
-    const int NG = D / G;
-    if ((cap * NG) % 8 != 0)
-        return false;
     // rows per wavefront: halved from 512 while the grid has fewer than
     // kSingleWaves wavefronts, down to 512 / WG (a workgroup then still
     // covers 512 rows: at most one partial per 512 rows, the workspace's
@@ -1542,7 +1535,7 @@ bool decode_single_plan(int D, int G, int n_rep, int bits, int64_t cap, int64_t 
     while (r > 512 / wg && heads * ((skv + r - 1) / r) < waves)
         r /= 2;
     const int64_t n = (skv + (int64_t)wg * r - 1) / ((int64_t)wg * r);
-    if (n > kMaxMergeGroups || (r * NG) % 8 != 0)
+    if (n > kMaxMergeGroups)
         return false;
     rows = r;
     nwg = (int32_t)n;

@@ -161,8 +161,6 @@ def test_bits_validation(L):
         assert _step(L, _cache(head_dim=64, bits=bits), kernel=3) == E_UNSUP
         assert _partial(L, _cache(head_dim=64, bits=bits), kernel=4, chunk=1024) == E_UNSUP
         assert _partial(L, _cache(head_dim=64, group=32, bits=bits), kernel=2, chunk=1024) == E_UNSUP
-        # scale/bias rows of a head must start on 16 bytes (capacity * D/G a multiple of 8)
-        assert _partial(L, _cache(head_dim=64, capacity=1020, bits=bits), kernel=4) == E_UNSUP
 
 
 def _append_rot(L, cache, length=0, k=P, v=P, dtype=0, n=1):

@@ -125,7 +125,7 @@ def test_shapes(kernel, B, Hq, Hkv, D, G, qdt):
     q = kvq_synth.normal((B, Hq, D), [181, Hq, D, G, 0]).astype(qdt)
     k = kvq_synth.normal((B, Hkv, S, D), [181, Hq, D, G, 1]).astype(np.float16)
     v = kvq_synth.normal((B, Hkv, S, D), [181, Hq, D, G, 2]).astype(np.float16)
-    oc = _oracle_cache(k, v, cap=S + 12, G=G)  # (capacity * D/G a multiple of 8: one-wavefront layout)
+    oc = _oracle_cache(k, v, cap=S + 13, G=G)
     alpha = 1 / np.sqrt(D)
     try:
         out, *_ = run_sdpa(gpu_cache_from_oracle(oc), S, q, alpha, kernel=kernel)
