@@ -128,7 +128,7 @@ int64_t kvq_cache_bytes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32
  * memory once with a plain grid-stride kernel (16-byte loads, 2048
  * workgroups of 256 threads) and discard them. Timing it over a buffer no
  * cache holds (>= 1 GB) gives the HBM read rate this GPU reaches, beside
- * which the attention kernel's algorithmic bytes per second are judged.
+ * which the attention kernel's algorithmic bytes per second are compared.
  *  buf:  device memory, 16-byte aligned; bytes: a multiple of 16, >= 0
  *        (0: no-op returning KVQ_OK).
  *  sink: one device uint32, 4-byte aligned; written only when a thread's XOR
