@@ -45,6 +45,30 @@ def test_noalloc_matches_decode_step(bits):
         check_attention(out1.cpu().numpy(), oracle.sdpa(oc, skv, q, alpha), 1e-4, label="noalloc skv=%d" % skv)
 
 
+def test_noalloc_head_dim_64():
+    """head_dim 64 (32 query heads on 8 KV heads): the same two calls."""
+    for skv in (40000, 9000):
+        note("noalloc decode step d64 skv=%d" % skv)
+        q = kvq_synth.normal((1, 32, 64), [197, skv, 0]).astype(np.float16)
+        k = kvq_synth.to_f16(kvq_synth.normal((1, 8, skv, 64), [197, skv, 1]))
+        v = kvq_synth.to_f16(kvq_synth.normal((1, 8, skv, 64), [197, skv, 2]))
+        alpha, length = 0.125, skv - 1
+        oc = oracle.Cache(1, 8, 64, skv, 64)
+        oc.append(np.ascontiguousarray(k[:, :, :length]), np.ascontiguousarray(v[:, :, :length]), 0)
+        kn = np.ascontiguousarray(k[:, :, length:])
+        vn = np.ascontiguousarray(v[:, :, length:])
+        g1, g2 = gpu_cache_from_oracle(oc), gpu_cache_from_oracle(oc)
+        qd, knd, vnd = to_dev(q), to_dev(kn), to_dev(vn)
+        out1 = torch.full((1, 32, 64), float("nan"), device="cuda")
+        kvq.decode_step_noalloc(g1, length, knd, vnd, qd, alpha, out=out1)
+        out2 = kvq.decode_step(g2, length, knd, vnd, qd, alpha)
+        torch.cuda.synchronize()
+        oc.append(kn, vn, length)
+        assert_cache_equal(g1, oc)
+        assert torch.equal(out1, out2), "no-alloc step differs from kvq_decode_step (d64, skv %d)" % skv
+        check_attention(out1.cpu().numpy(), oracle.sdpa(oc, skv, q, alpha), 1e-4, label="noalloc d64 skv=%d" % skv)
+
+
 def test_noalloc_refuses_beyond_scratch():
     """A request whose partials exceed the static scratch returns
     KVQ_E_SCRATCH before anything is enqueued (the cache is left as it was)."""
