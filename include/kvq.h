@@ -250,8 +250,8 @@ int kvq_sdpa_int4(const kvq_cache *cache, int64_t skv, const void *q, int q_dtyp
  *        hi and lo halves, e.g. a query rotated for a Hadamard-rotated
  *        cache), 16-byte aligned; Hq a multiple of Hkv.
  *  out:  [B][Hq][sq][D] fp32, normalised, 16-byte aligned.
- * One launch, no workspace. Supported: D = 128 or 256, G = 64, 4- or 8-bit
- * codes, Hq / Hkv <= 32 at D = 128 and <= 16 at D = 256
+ * One launch, no workspace. Supported: D = 64, 128 or 256, G = 64, 4- or
+ * 8-bit codes, Hq / Hkv <= 32 at D = 64 and 128 and <= 16 at D = 256
  * (KVQ_E_UNSUPPORTED otherwise). q_start + sq beyond the capacity returns
  * KVQ_E_CAPACITY. On a Hadamard-rotated cache: rotate q with
  * kvq_hadamard_rotate (fp32 out), call this with KVQ_F32, rotate out back.

@@ -28,9 +28,10 @@
 // normalised in the kernel (no split over rows, so no partial state).
 //
 // Three kernels: 8-bit codes (sdpa_prefill_b8_kernel: per-group value
-// weights, the layout the int4 kernels started from), int4 at D = 256
-// (sdpa_prefill_i4_kernel) and int4 at D = 128 (sdpa_prefill_i4_wg_kernel,
-// the same arithmetic with the tile's operands shared by a workgroup).
+// weights, the layout the int4 kernels started from), int4 at D = 64 and
+// 256 (sdpa_prefill_i4_kernel) and int4 at D = 128
+// (sdpa_prefill_i4_wg_kernel, the same arithmetic with the tile's operands
+// shared by a workgroup).
 
 #include "kvq_internal.h"
 #include "mfma_common.h"
@@ -81,7 +82,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
 void sdpa_prefill_b8_kernel(PrefillArgs a)
 {
     constexpr int NG = D / 64;   // scale groups of 64
-    constexpr int VS = D / 128;  // sets of 16 value words (two groups each)
+    // D = 64: one group of 16 words per row; each of the 16 value columns is
+    // one word (octet col & 7, dimensions 4 (col >> 3) + mm, mm < 4);
+    // otherwise a column is an octet (two words), two groups per set
+    constexpr bool HV = D == 64;
+    constexpr int VS = HV ? 1 : D / 128;  // sets of 16 value columns
+    constexpr int VM = HV ? 4 : 8;        // value accumulators per set
     constexpr int W = D / 4;    // words per row
     constexpr int KW = 2;       // words per eight dimensions
     constexpr int KM = D / 32;        // score products per 16-row block
@@ -90,8 +96,8 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
     constexpr float WS = 64.0f;        // scale of the value weights
     constexpr float VU = 1.0f / 64.0f;  // unit of the value products
     constexpr int PAIRS = PT * NG;
-    constexpr int MP = PAIRS / 64;  // (row, group) pairs per lane
-    static_assert(PAIRS % 64 == 0, "whole pairs per lane");
+    constexpr int MP = (PAIRS + 63) / 64;  // (row, group) pairs per lane (D = 64: lanes 0-31)
+    static_assert(PAIRS % 64 == 0 || PAIRS == 32, "whole pairs per lane, or one for half the lanes");
     constexpr bool QLDS = NB > 1 || D > 128;  // query operands in LDS
 
     const int lane = threadIdx.x;
@@ -171,19 +177,27 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
         // V: dimensions 128 s2 + 8 col .. + 7 (KW words) of rows 16 (j >> 2) + 4 q4 + (j & 3)
 #pragma unroll
         for (int s2 = 0; s2 < VS; ++s2) {
-            const uint32_t voff = base + (uint32_t)((4 * q4 * W + KW * (16 * s2 + col)) * 4);
+            // HV: the one word of dimensions 8 (col & 7) + 4 (col >> 3) .. + 3
+            const uint32_t voff =
+                base + (uint32_t)((4 * q4 * W + (HV ? KW * (col & 7) + (col >> 3) : KW * (16 * s2 + col))) * 4);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t o = voff + ((16 * (j >> 2) + (j & 3)) * W) * 4;
-                const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
-                vt[s2][2 * j] = x[0];
-                vt[s2][2 * j + 1] = x[1];
+                if constexpr (HV) {
+                    vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, o, 0, 0);
+                } else {
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(vq, o, 0, 0);
+                    vt[s2][2 * j] = x[0];
+                    vt[s2][2 * j + 1] = x[1];
+                }
             }
         }
     };
     auto stage_meta = [&](int slot, const uint32_t (&mt)[MP][4]) {
 #pragma unroll
         for (int pp = 0; pp < MP; ++pp) {
+            if (PAIRS < 64 && lane + 64 * pp >= PAIRS)  // D = 64: lanes 32-63 loaded the next tile's words
+                break;
             const float ks = h_val((uint16_t)mt[pp][0]);
             const float kb = h_val((uint16_t)mt[pp][1]);
             const float vs = h_val((uint16_t)mt[pp][2]);
@@ -265,7 +279,7 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
     stage_meta(0, mbuf[0]);
 
     float m_run[NB], l_run[NB], b_run[NB][NG];
-    float4v acc[NB][8 * VS], accl[NB][8 * VS];  // [nb][8 s2 + 4 g + mm]: hi and lo (x kLoScale) weight halves
+    float4v acc[NB][VM * VS], accl[NB][VM * VS];  // [nb][8 s2 + 4 g + mm]: hi and lo (x kLoScale) weight halves
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         m_run[nb] = 0.0f;
@@ -274,7 +288,7 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
         for (int g = 0; g < NG; ++g)
             b_run[nb][g] = 0.0f;
 #pragma unroll
-        for (int m = 0; m < 8 * VS; ++m) {
+        for (int m = 0; m < VM * VS; ++m) {
             acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
             accl[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
         }
@@ -367,7 +381,7 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
                         for (int i = 0; i < 4; ++i)
                             corr_row[i] = __shfl(corr, 4 * q4 + i);
 #pragma unroll
-                        for (int m = 0; m < 8 * VS; ++m) {
+                        for (int m = 0; m < VM * VS; ++m) {
                             acc[nb][m] *= corr_row;
                             accl[nb][m] *= corr_row;
                         }
@@ -387,6 +401,42 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
             // give 0..3 in its own group's products and lend 4..7 to lane
             // l ^ 8 (row r's two words hold dimensions 0..3 and 4..7), and
             // every unpacked operand serves all NB blocks
+            if constexpr (HV) {
+                // one scale group; rows (2 jp, 2 jp + 1) of the lane's word
+                const uint32_t(&vw)[8 * KW] = vbuf[u][0];
+                half8 phi[NB], plo[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    float bsum = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2) {
+                        const float2 f0 = fac_zw(slot, 16 * (j >> 2) + 4 * q4 + (j & 3), 0);
+                        const float2 f1 = fac_zw(slot, 16 * ((j + 1) >> 2) + 4 * q4 + ((j + 1) & 3), 0);
+                        bsum = fmaf(p[nb][j], f0.y, fmaf(p[nb][j + 1], f1.y, bsum));
+                        const float w0 = p[nb][j] * f0.x, w1 = p[nb][j + 1] * f1.x;
+                        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                        const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(
+                                                                        (w0 - (float)h[0]) * kLoScale,
+                                                                        (w1 - (float)h[1]) * kLoScale));
+                        phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
+                        plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
+                    }
+                    b_run[nb][0] += bsum;
+                }
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    half2v e[4];
+#pragma unroll
+                    for (int jp = 0; jp < 4; ++jp)
+                        e[jp] = v_pair8(vw[2 * jp], vw[2 * jp + 1], sel_b[mm], magic16);
+                    const half8 bv = cat8(e[0], e[1], e[2], e[3]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        acc[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], bv, acc[nb][mm], 0, 0, 0);
+                        accl[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, accl[nb][mm], 0, 0, 0);
+                    }
+                }
+            } else
 #pragma unroll
             for (int s2 = 0; s2 < VS; ++s2) {
                 const uint32_t(&vw)[8 * KW] = vbuf[u][s2];
@@ -462,7 +512,8 @@ void sdpa_prefill_b8_kernel(PrefillArgs a)
                 // group gg's products of this lane: dimensions 128 s2 + 8 col +
                 // 0..3 when its own word is in the set's group g, else
                 // 128 s2 + 8 (col ^ 8) + 4..7
-                const int d0 = 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
+                const int d0 = HV ? 8 * (col & 7) + 4 * (col >> 3)  // the column's word
+                                  : 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
                 float o[4];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm) {
@@ -557,13 +608,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
 void sdpa_prefill_i4_kernel(PrefillArgs a)
 {
     constexpr int NG = D / 64;        // scale groups of 64
-    constexpr int VS = D / 128;       // sets of 16 value words (two groups each)
+    // D = 64: one group of eight words per row, so each of the 16 value
+    // columns is half a word (word col & 7, dimensions 4 (col >> 3) + mm,
+    // mm < 4); otherwise a column is a whole word, two groups per set
+    constexpr bool HV = D == 64;
+    constexpr int VS = HV ? 1 : D / 128;  // sets of 16 value columns
+    constexpr int VM = HV ? 4 : 8;        // value accumulators per set
     constexpr int W = D / 8;          // words per row
     constexpr int KM = D / 32;        // score products per 16-row block
     constexpr int KPG = KM / NG;      // of them per scale group
     constexpr int PAIRS = PT * NG;
-    constexpr int MP = PAIRS / 64;    // (row, group) pairs per lane
-    static_assert(PAIRS % 64 == 0, "whole pairs per lane");
+    constexpr int MP = (PAIRS + 63) / 64;  // (row, group) pairs per lane (D = 64: lanes 0-31)
+    static_assert(PAIRS % 64 == 0 || PAIRS == 32, "whole pairs per lane, or one for half the lanes");
     constexpr int QH = Q32 ? 2 : 1;   // query halves: hi (and lo)
     // score-bias operand slots: group g at 6g..6g+5, (b1, b1, b1, b2, b2, b3)
     // against (Q1, Q2, Q3, Q1, Q2, Q1); then three ones against the pieces of
@@ -654,7 +710,7 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
         }
 #pragma unroll
         for (int s2 = 0; s2 < VS; ++s2) {
-            const uint32_t voff = base + (uint32_t)((4 * q4 * W + 16 * s2 + col) * 4);
+            const uint32_t voff = base + (uint32_t)((4 * q4 * W + (HV ? (col & 7) : 16 * s2 + col)) * 4);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
@@ -664,6 +720,8 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
 #pragma unroll
         for (int pp = 0; pp < MP; ++pp) {
             const int idx = lane + 64 * pp;
+            if (PAIRS < 64 && idx >= PAIRS)  // D = 64: lanes 32-63 loaded the next tile's words
+                break;
             const int r = idx / NG, g = idx % NG;
             const uint16_t ks = (uint16_t)mt[pp][0], kb = (uint16_t)mt[pp][1];
             const uint16_t vsb = (uint16_t)mt[pp][2], vbb = (uint16_t)mt[pp][3];
@@ -775,14 +833,14 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
         sbb[nb] = __builtin_bit_cast(bf16x8, w);
     };
 
-    float4v acc[NB][8 * VS], bacc[NB];
+    float4v acc[NB][VM * VS], bacc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         ref[nb] = kRef;
         build_sbb(nb);
         bacc[nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int m = 0; m < 8 * VS; ++m)
+        for (int m = 0; m < VM * VS; ++m)
             acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
     }
     const int vrow = min(col, 2 * NG + 1);  // this lane's value-bias table row
@@ -875,7 +933,7 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
                             corr_row[i] = __shfl(corr, 4 * q4 + i);
                         bacc[nb] *= corr_row;
 #pragma unroll
-                        for (int m = 0; m < 8 * VS; ++m)
+                        for (int m = 0; m < VM * VS; ++m)
                             acc[nb][m] *= corr_row;
                     }
                 }
@@ -895,6 +953,40 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
             // ---- value products: the lane's rows (2 jp, 2 jp + 1) pair up in
             // each fp16 pair of the operand, so the scale halves of a pair of
             // rows multiply one half2
+            if constexpr (HV) {
+                // the two bytes (four nibbles) of the lane's half of its word
+                // in rows 2 jp and 2 jp + 1; one scale group
+                const uint32_t(&vw)[8] = vbuf[u][0];
+                const uint32_t hsel = (col >> 3) ? 0x07060302u : 0x05040100u;
+                uint32_t xw[4];
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp)
+                    xw[jp] = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], hsel);
+                const uint2 h0 = *reinterpret_cast<const uint2 *>(&svt[slot][0][4 * q4]);
+                const uint2 h1 = *reinterpret_cast<const uint2 *>(&svt[slot][0][16 + 4 * q4]);
+                const uint2 l0 = *reinterpret_cast<const uint2 *>(&svt[slot][NG][4 * q4]);
+                const uint2 l1 = *reinterpret_cast<const uint2 *>(&svt[slot][NG][16 + 4 * q4]);
+                const half2v shi[4] = {as_h2(h0.x), as_h2(h0.y), as_h2(h1.x), as_h2(h1.y)};
+                const half2v slo[4] = {as_h2(l0.x), as_h2(l0.y), as_h2(l1.x), as_h2(l1.y)};
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    half2v e[4];
+#pragma unroll
+                    for (int jp = 0; jp < 4; ++jp)
+                        e[jp] = unpack.one(xw[jp], mm);
+                    const half8 vh = cat8(e[0] * shi[0], e[1] * shi[1], e[2] * shi[2], e[3] * shi[3]);
+                    const half8 vl = cat8(e[0] * slo[0], e[1] * slo[1], e[2] * slo[2], e[3] * slo[3]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vh, acc[nb][mm], 0, 0, 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vl, acc[nb][mm], 0, 0, 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], vh, acc[nb][mm], 0, 0, 0);
+                }
+            } else
 #pragma unroll
             for (int s2 = 0; s2 < VS; ++s2) {
                 const uint32_t(&vw)[8] = vbuf[u][s2];
@@ -969,7 +1061,8 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
             for (int gg = 0; gg < NG; ++gg) {
                 const int s2 = gg >> 1, g = gg & 1;
                 const float bias = __shfl(bacc[nb][i], rowbase + 2 * gg) + __shfl(bacc[nb][i], rowbase + 2 * gg + 1);
-                const int d0 = 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
+                const int d0 = HV ? 8 * (col & 7) + 4 * (col >> 3)  // the column's half word
+                                  : 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
                 float o[4];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm)
@@ -1447,12 +1540,12 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
 
 }  // namespace
 
-// n_rep up to the query columns of a wavefront (16 per block: 32 at D =
-// 128, 16 at D = 256), where a wavefront then takes one position of all its
-// KV head's query heads
+// n_rep up to the query columns of a wavefront (16 per block: 32 at D = 64
+// and 128, 16 at D = 256), where a wavefront then takes one position of all
+// its KV head's query heads
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
 {
-    return (D == 128 || D == 256) && G == 64 && n_rep >= 1 && n_rep <= (D == 256 ? 16 : 32) &&
+    return (D == 64 || D == 128 || D == 256) && G == 64 && n_rep >= 1 && n_rep <= (D == 256 ? 16 : 32) &&
            (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) && (bits == 4 || bits == 8);
 }
 
@@ -1490,7 +1583,7 @@ void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
 {
-    if ((a.D != 128 && a.D != 256) || (a.bits != 4 && a.bits != 8) || a.pb < 1 ||
+    if ((a.D != 64 && a.D != 128 && a.D != 256) || (a.bits != 4 && a.bits != 8) || a.pb < 1 ||
         a.pb * a.n_rep > 16 * prefill_nb(a.D))
         return hipErrorInvalidValue;
     const int64_t per_block = (int64_t)a.pb * prefill_wg(a.D, a.bits, a.q_f32 != 0);
@@ -1499,6 +1592,8 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
     dim3 grid((unsigned)(blocks * a.Hkv), 1u, (unsigned)batch);
     if (a.D == 256)
         launch_prefill_d<256>(a, grid, s);
+    else if (a.D == 64)
+        launch_prefill_d<64>(a, grid, s);
     else
         launch_prefill_d<128>(a, grid, s);
     return hipGetLastError();

@@ -275,14 +275,14 @@ def test_prefill_validation(L):
     assert _prefill(L, _cache(capacity=1024), q_start=1025, sq=1) == E_CAP
     assert _prefill(L, _cache(), q=P + 4) == E_ALIGN
     assert _prefill(L, _cache(), out=P + 8) == E_ALIGN
-    # outside the prefill kernel: head sizes other than 128 and 256, other
-    # groups, more query heads per KV head than a wavefront's columns (32 at
-    # D 128, 16 at D 256; 4- and 8-bit codes, fp16 and fp32 queries are inside)
-    assert _prefill(L, _cache(head_dim=64)) == E_UNSUP
+    # outside the prefill kernels: groups other than 64, more query heads per
+    # KV head than a wavefront's columns (32 at D 64 and 128, 16 at D 256;
+    # 4- and 8-bit codes, fp16 and fp32 queries are inside)
     assert _prefill(L, _cache(group=32)) == E_UNSUP
-    assert _prefill(L, _cache(head_dim=64), qd=1) == E_UNSUP
+    assert _prefill(L, _cache(head_dim=64, group=32), qd=1) == E_UNSUP
     assert _prefill(L, _cache(bits=3)) == E_SHAPE
     assert _prefill(L, _cache(kv_heads=1), hq=64) == E_UNSUP
+    assert _prefill(L, _cache(kv_heads=1, head_dim=64), hq=40) == E_UNSUP
     assert _prefill(L, _cache(kv_heads=1, head_dim=256), hq=20) == E_UNSUP
 
 

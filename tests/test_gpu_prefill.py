@@ -223,11 +223,43 @@ def test_head_dim_256_fp32_queries_and_gqa8():
     check_attention(got.cpu().numpy(), oracle.sdpa_prefill(oc, 300, q, alpha), REL_L2, label="prefill D256 fp32")
 
 
-@pytest.mark.parametrize("what", ["d64", "g32"])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("q_start,sq", [(0, 1), (0, 33), (300, 45), (1000, 17), (4000, 96)])
+def test_head_dim_64(bits, q_start, sq):
+    """D = 64 (one scale group; each value column half a word): 32 query
+    heads on 8 KV heads."""
+    note("prefill D64 bits=%d q_start=%d sq=%d" % (bits, q_start, sq))
+    q, oc, alpha = _case(1, 32, 8, q_start, sq, seed=9700 + bits * 100 + sq, bits=bits, D=64)
+    got = _run(oc, q_start, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, q_start, q, alpha), REL_L2, label="prefill D64")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("hq,hkv,q32", [(16, 16, False), (64, 2, True), (12, 4, False), (8, 2, True)])
+def test_head_dim_64_layouts(bits, hq, hkv, q32):
+    """D = 64: multi-head, 32 heads per KV head (one position per
+    wavefront), GQA 3, and fp32 queries."""
+    note("prefill D64 hq=%d hkv=%d q32=%d bits=%d" % (hq, hkv, q32, bits))
+    q, oc, alpha = _case(1, hq, hkv, 500, 40, seed=9800 + hq * 10 + hkv + bits, bits=bits, D=64)
+    if q32:
+        q = (q.astype(np.float32) + kvq_synth.normal(q.shape, [92, hq]).astype(np.float32) * 1e-3)
+    got = _run(oc, 500, q, alpha)
+    check_attention(got, oracle.sdpa_prefill(oc, 500, q, alpha), REL_L2, label="prefill D64 layouts")
+
+
+def test_head_dim_64_unscaled_batch_two():
+    note("prefill D64 alpha 1, batch 2")
+    q, oc, _ = _case(2, 8, 2, 250, 30, seed=9900, cap=301, D=64)
+    q = (q.astype(np.float32) * np.float32(0.5)).astype(np.float16)
+    got = _run(oc, 250, q, 1.0)
+    check_attention(got, oracle.sdpa_prefill(oc, 250, q, 1.0), REL_L2, atol=1e-3, rtol=1e-3, label="prefill D64 a1")
+
+
+@pytest.mark.parametrize("what", ["g32", "d64_g32"])
 def test_unsupported_shapes_refused(what):
     note("prefill refuses %s" % what)
-    D = 64 if what == "d64" else 128
-    G = 32 if what == "g32" else 64
+    D = 64 if what == "d64_g32" else 128
+    G = 32
     bits = 4
     gc = kvq.QuantKVCache(1, 2, D, 64, G, device="cuda", bits=bits)
     q = torch.zeros((1, 8, 4, D), dtype=torch.float16, device="cuda")
