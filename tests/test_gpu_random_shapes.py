@@ -5,7 +5,8 @@ entry points (kvq_sdpa_int4 under AUTO and every forced kernel variant,
 kvq_decode_step, kvq_decode_step_single_launch) and checked against the
 float64 oracle, the appended row bit for bit. A forced variant may refuse a
 shape only with KVQ_E_UNSUPPORTED, and only where its documented limits say
-so."""
+so. Prefill likewise over the shapes it takes (prefix, positions, heads,
+head_dim, code width, query dtype, batch, spare capacity)."""
 
 import numpy as np
 import pytest
@@ -117,3 +118,35 @@ def test_draws_are_valid():
     for i in range(N_CASES):
         c = _draw(i)
         assert c["D"] % c["G"] == 0 and c["Hq"] % c["Hkv"] == 0 and c["cap"] > c["skv"]
+
+
+N_PREFILL = 48
+
+
+def _draw_prefill(i):
+    """A prefill case the kernels take: G 64, at most 32 query heads per KV
+    head (16 at D 256)."""
+    rng = np.random.default_rng([20263, i])
+    D = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    n_rep = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16] + ([20, 24, 32] if D < 256 else [])))
+    return dict(D=D, Hkv=Hkv, Hq=Hkv * n_rep, B=int(rng.choice([1, 1, 2])), bits=int(rng.choice([4, 8])),
+                q32=bool(rng.random() < 0.3), q_start=int(rng.choice([0, int(rng.integers(1, 2500))])),
+                sq=int(rng.integers(1, 80)), spare=int(rng.integers(0, 20)))
+
+
+@pytest.mark.parametrize("i", range(N_PREFILL))
+def test_random_prefill(i):
+    c = _draw_prefill(i)
+    note("random prefill %d: %s" % (i, c))
+    B, Hq, Hkv, D, q_start, sq = c["B"], c["Hq"], c["Hkv"], c["D"], c["q_start"], c["sq"]
+    S = q_start + sq
+    q = kvq_synth.normal((B, Hq, sq, D), [20264, i, 0]).astype(np.float32 if c["q32"] else np.float16)
+    k = kvq_synth.to_f16(kvq_synth.normal((B, Hkv, S, D), [20264, i, 1]))
+    v = kvq_synth.to_f16(kvq_synth.normal((B, Hkv, S, D), [20264, i, 2]))
+    oc = oracle.Cache(B, Hkv, D, S + c["spare"], 64, bits=c["bits"])
+    oc.append(k, v, 0)
+    alpha = 1 / np.sqrt(D)
+    out = kvq.sdpa_int4_prefill(gpu_cache_from_oracle(oc), q_start, to_dev(q), alpha)
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy(), oracle.sdpa_prefill(oc, q_start, q, alpha), 1e-4, label="prefill case %d" % i)
