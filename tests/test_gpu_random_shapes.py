@@ -6,7 +6,8 @@ kvq_decode_step, kvq_decode_step_single_launch) and checked against the
 float64 oracle, the appended row bit for bit. A forced variant may refuse a
 shape only with KVQ_E_UNSUPPORTED, and only where its documented limits say
 so. Prefill likewise over the shapes it takes (prefix, positions, heads,
-head_dim, code width, query dtype, batch, spare capacity)."""
+head_dim, code width, query dtype, batch, spare capacity), and the rotated
+decode step over the decode shapes."""
 
 import numpy as np
 import pytest
@@ -150,3 +151,29 @@ def test_random_prefill(i):
     out = kvq.sdpa_int4_prefill(gpu_cache_from_oracle(oc), q_start, to_dev(q), alpha)
     torch.cuda.synchronize()
     check_attention(out.cpu().numpy(), oracle.sdpa_prefill(oc, q_start, q, alpha), 1e-4, label="prefill case %d" % i)
+
+
+N_ROTATED = 24
+
+
+@pytest.mark.parametrize("i", range(N_ROTATED))
+def test_random_rotated_step(i):
+    """The rotated decode step (kvq_decode_step_rotated) on random shapes: the
+    rotated row bit for bit, the output against the oracle's attention over
+    the rotated cache, rotated back."""
+    c = _draw(1000 + i)
+    note("random rotated step %d: %s" % (i, c))
+    q, k, v = _inputs(c, 1000 + i)
+    skv, alpha = c["skv"], c["alpha"]
+    oc = oracle.Cache(c["B"], c["Hkv"], c["D"], c["cap"], c["G"], bits=c["bits"])
+    oc.append_rotated(np.ascontiguousarray(k[:, :, :skv]), np.ascontiguousarray(v[:, :, :skv]), 0)
+    kn = np.ascontiguousarray(k[:, :, skv:skv + 1])
+    vn = np.ascontiguousarray(v[:, :, skv:skv + 1])
+    g = gpu_cache_from_oracle(oc)
+    out = kvq.decode_step_rotated(g, skv, to_dev(kn), to_dev(vn), to_dev(q), alpha, chunk=c["chunk"])
+    torch.cuda.synchronize()
+    oc.append_rotated(kn, vn, skv)
+    assert_cache_equal(g, oc)
+    atol, rtol = _tol(c)
+    check_attention(out.cpu().numpy(), oracle.sdpa_rotated(oc, skv + 1, q, alpha), 1e-4, atol=atol, rtol=rtol,
+                    label="rotated case %d" % i)
