@@ -28,8 +28,8 @@
 // normalised in the kernel (no split over rows, so no partial state).
 //
 // Three kernels: 8-bit codes (sdpa_prefill_b8_kernel: per-group value
-// weights, the layout the int4 kernels started from), int4 at D = 64 and
-// 256 (sdpa_prefill_i4_kernel) and int4 at D = 128
+// weights, the layout the int4 kernels started from), int4 at D = 256
+// (sdpa_prefill_i4_kernel) and int4 at D = 64 and 128
 // (sdpa_prefill_i4_wg_kernel, the same arithmetic with the tile's operands
 // shared by a workgroup).
 
@@ -608,18 +608,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
 void sdpa_prefill_i4_kernel(PrefillArgs a)
 {
     constexpr int NG = D / 64;        // scale groups of 64
-    // D = 64: one group of eight words per row, so each of the 16 value
-    // columns is half a word (word col & 7, dimensions 4 (col >> 3) + mm,
-    // mm < 4); otherwise a column is a whole word, two groups per set
-    constexpr bool HV = D == 64;
-    constexpr int VS = HV ? 1 : D / 128;  // sets of 16 value columns
-    constexpr int VM = HV ? 4 : 8;        // value accumulators per set
+    constexpr int VS = D / 128;       // sets of 16 value words (two groups each)
     constexpr int W = D / 8;          // words per row
     constexpr int KM = D / 32;        // score products per 16-row block
     constexpr int KPG = KM / NG;      // of them per scale group
     constexpr int PAIRS = PT * NG;
-    constexpr int MP = (PAIRS + 63) / 64;  // (row, group) pairs per lane (D = 64: lanes 0-31)
-    static_assert(PAIRS % 64 == 0 || PAIRS == 32, "whole pairs per lane, or one for half the lanes");
+    constexpr int MP = PAIRS / 64;    // (row, group) pairs per lane
+    static_assert(PAIRS % 64 == 0, "whole pairs per lane");
     constexpr int QH = Q32 ? 2 : 1;   // query halves: hi (and lo)
     // score-bias operand slots: group g at 6g..6g+5, (b1, b1, b1, b2, b2, b3)
     // against (Q1, Q2, Q3, Q1, Q2, Q1); then three ones against the pieces of
@@ -710,7 +705,7 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
         }
 #pragma unroll
         for (int s2 = 0; s2 < VS; ++s2) {
-            const uint32_t voff = base + (uint32_t)((4 * q4 * W + (HV ? (col & 7) : 16 * s2 + col)) * 4);
+            const uint32_t voff = base + (uint32_t)((4 * q4 * W + 16 * s2 + col) * 4);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 vt[s2][j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
@@ -720,8 +715,6 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
 #pragma unroll
         for (int pp = 0; pp < MP; ++pp) {
             const int idx = lane + 64 * pp;
-            if (PAIRS < 64 && idx >= PAIRS)  // D = 64: lanes 32-63 loaded the next tile's words
-                break;
             const int r = idx / NG, g = idx % NG;
             const uint16_t ks = (uint16_t)mt[pp][0], kb = (uint16_t)mt[pp][1];
             const uint16_t vsb = (uint16_t)mt[pp][2], vbb = (uint16_t)mt[pp][3];
@@ -833,14 +826,14 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
         sbb[nb] = __builtin_bit_cast(bf16x8, w);
     };
 
-    float4v acc[NB][VM * VS], bacc[NB];
+    float4v acc[NB][8 * VS], bacc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         ref[nb] = kRef;
         build_sbb(nb);
         bacc[nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int m = 0; m < VM * VS; ++m)
+        for (int m = 0; m < 8 * VS; ++m)
             acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
     }
     const int vrow = min(col, 2 * NG + 1);  // this lane's value-bias table row
@@ -933,7 +926,7 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
                             corr_row[i] = __shfl(corr, 4 * q4 + i);
                         bacc[nb] *= corr_row;
 #pragma unroll
-                        for (int m = 0; m < VM * VS; ++m)
+                        for (int m = 0; m < 8 * VS; ++m)
                             acc[nb][m] *= corr_row;
                     }
                 }
@@ -953,40 +946,6 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
             // ---- value products: the lane's rows (2 jp, 2 jp + 1) pair up in
             // each fp16 pair of the operand, so the scale halves of a pair of
             // rows multiply one half2
-            if constexpr (HV) {
-                // the two bytes (four nibbles) of the lane's half of its word
-                // in rows 2 jp and 2 jp + 1; one scale group
-                const uint32_t(&vw)[8] = vbuf[u][0];
-                const uint32_t hsel = (col >> 3) ? 0x07060302u : 0x05040100u;
-                uint32_t xw[4];
-#pragma unroll
-                for (int jp = 0; jp < 4; ++jp)
-                    xw[jp] = __builtin_amdgcn_perm(vw[2 * jp + 1], vw[2 * jp], hsel);
-                const uint2 h0 = *reinterpret_cast<const uint2 *>(&svt[slot][0][4 * q4]);
-                const uint2 h1 = *reinterpret_cast<const uint2 *>(&svt[slot][0][16 + 4 * q4]);
-                const uint2 l0 = *reinterpret_cast<const uint2 *>(&svt[slot][NG][4 * q4]);
-                const uint2 l1 = *reinterpret_cast<const uint2 *>(&svt[slot][NG][16 + 4 * q4]);
-                const half2v shi[4] = {as_h2(h0.x), as_h2(h0.y), as_h2(h1.x), as_h2(h1.y)};
-                const half2v slo[4] = {as_h2(l0.x), as_h2(l0.y), as_h2(l1.x), as_h2(l1.y)};
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    half2v e[4];
-#pragma unroll
-                    for (int jp = 0; jp < 4; ++jp)
-                        e[jp] = unpack.one(xw[jp], mm);
-                    const half8 vh = cat8(e[0] * shi[0], e[1] * shi[1], e[2] * shi[2], e[3] * shi[3]);
-                    const half8 vl = cat8(e[0] * slo[0], e[1] * slo[1], e[2] * slo[2], e[3] * slo[3]);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vh, acc[nb][mm], 0, 0, 0);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], vl, acc[nb][mm], 0, 0, 0);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb][mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], vh, acc[nb][mm], 0, 0, 0);
-                }
-            } else
 #pragma unroll
             for (int s2 = 0; s2 < VS; ++s2) {
                 const uint32_t(&vw)[8] = vbuf[u][s2];
@@ -1061,8 +1020,7 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
             for (int gg = 0; gg < NG; ++gg) {
                 const int s2 = gg >> 1, g = gg & 1;
                 const float bias = __shfl(bacc[nb][i], rowbase + 2 * gg) + __shfl(bacc[nb][i], rowbase + 2 * gg + 1);
-                const int d0 = HV ? 8 * (col & 7) + 4 * (col >> 3)  // the column's half word
-                                  : 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
+                const int d0 = 128 * s2 + ((g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4);
                 float o[4];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm)
@@ -1077,7 +1035,8 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// int4 codes, D = 128: WG wavefronts share each tile's unpacked operands
+// int4 codes, D = 64 and 128: WG wavefronts share each tile's unpacked
+// operands
 //
 // The arithmetic of sdpa_prefill_i4_kernel, with WG wavefronts per
 // workgroup on consecutive position blocks of one (batch, KV head): they
@@ -1090,14 +1049,20 @@ void sdpa_prefill_i4_kernel(PrefillArgs a)
 // builders of tile t + 1 read its value-scale halves while tile t is being
 // computed); one barrier per tile separates building tile t + 1 (into the
 // other half of a two-slot operand ring) from the reads of tile t.
-// WG = 8 with fp16 queries (one workgroup per CU, two wavefronts per SIMD);
-// WG = 4 with fp32 queries, whose hi and lo query operands take twice the
-// LDS (one wavefront per SIMD).
-template <int PF, int NB, bool Q32, int WG>
+// D = 128: WG = 8 with fp16 queries (one workgroup per CU, two wavefronts
+// per SIMD); WG = 4 with fp32 queries, whose hi and lo query operands take
+// twice the LDS (one wavefront per SIMD). D = 64: WG = 4 (a tile has four K
+// and four V operands, one of each per wavefront).
+template <int PF, int NB, bool Q32, int WG, int D>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WG / 4)))
 void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
 {
-    constexpr int D = 128, NG = 2, W = 16, KM = 4, KPG = 2;
+    // D = 64: one scale group of eight words; each of the 16 value columns is
+    // half a word (word col & 7, dimensions 4 (col >> 3) + mm), as in the
+    // one-wavefront kernel
+    static_assert(D == 128 || D == 64, "two scale groups, or one");
+    constexpr bool HV = D == 64;
+    constexpr int NG = D / 64, W = D / 8, KM = D / 32, KPG = 2;
     constexpr int QH = Q32 ? 2 : 1;
     constexpr int SBR = 6 * NG;
     constexpr int SBL = (SBR + 3 + 7) / 8 * 8;
@@ -1109,7 +1074,7 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     constexpr int KO = NKO / WG;  // of them built by each wavefront
     constexpr int VO = NVO / WG;
     static_assert(NKO % WG == 0 && NVO % WG == 0, "operands split evenly");
-    static_assert(PT * NG == 64, "one (row, group) pair per lane of the staging wavefront");
+    static_assert(PT * NG == 64 || PT * NG == 32, "at most one (row, group) pair per lane of the staging wavefront");
     static_assert(PF == 2, "tile j's words in register buffer j % 2");
 
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1151,10 +1116,14 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     // factor tables, a ring of NTS slots (slot of tile t: t % NTS), staged in
     // batches: every WG tiles each wavefront stages one of the next WG tiles
     constexpr int NTS = 2 * WG;
-    __shared__ __align__(16) float xs[NTS][PT][NG];
-    __shared__ __align__(16) uint16_t sba[NTS][PT][SBL];
-    __shared__ __align__(16) uint16_t vbt[NTS][NVB][PT];
-    __shared__ __align__(16) uint16_t svt[NTS][2 * NG][PT];
+    // rows per table slot: PT, and at D = 64 (32 (row, group) pairs per tile)
+    // 8 more that take the stores of the staging lanes 32-63, so that every
+    // lane stores (a branch around the stores does not compile here)
+    constexpr int PTX = PT * NG < 64 ? PT + 8 : PT;
+    __shared__ __align__(16) float xs[NTS][PTX][NG];
+    __shared__ __align__(16) uint16_t sba[NTS][PTX][SBL];
+    __shared__ __align__(16) uint16_t vbt[NTS][NVB][PTX];
+    __shared__ __align__(16) uint16_t svt[NTS][2 * NG][PTX];
     __shared__ __align__(16) half8 q_lds[WG][NB][QH][KM][64];
     const float cs = a.score_scale;
     const float csk = cs * 1048576.0f;
@@ -1193,7 +1162,7 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
             kt[i] = __builtin_amdgcn_raw_buffer_load_b32(
                 kq, base + (uint32_t)((((16 * (o / KM) + col) * W + q4) * 4) + 16 * (o % KM)), 0, 0);
         }
-        const uint32_t voff = base + (uint32_t)((4 * q4 * W + col) * 4);
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + (HV ? (col & 7) : col)) * 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
@@ -1214,10 +1183,17 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
         uint32_t bx[2][4];
 #pragma unroll
         for (int jp = 0; jp < 4; ++jp) {
-            const uint32_t xw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x05040100u);
-            const uint32_t yw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x07060302u);
-            bx[0][jp] = take_half_row<0xC>(xw, yw);
-            bx[1][jp] = take_half_row<0x3>(xw, yw);
+            if constexpr (HV) {  // the two bytes of the lane's half word (one group)
+                const uint32_t xw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x05040100u);
+                const uint32_t yw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x07060302u);
+                bx[0][jp] = (col >> 3) ? yw : xw;
+                bx[1][jp] = bx[0][jp];
+            } else {
+                const uint32_t xw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x05040100u);
+                const uint32_t yw = __builtin_amdgcn_perm(vt[2 * jp + 1], vt[2 * jp], 0x07060302u);
+                bx[0][jp] = take_half_row<0xC>(xw, yw);
+                bx[1][jp] = take_half_row<0x3>(xw, yw);
+            }
         }
 #pragma unroll
         for (int i = 0; i < VO; ++i) {
@@ -1246,7 +1222,8 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     // a tile's factor tables into table slot ts, from its scale/bias words
     // mt (load_meta)
     auto stage = [&](int ts, const uint32_t (&mt)[4]) {
-        const int r = lane / NG, g = lane % NG;
+        // (D = 64: lanes 32-63 loaded the next tile's words; they store into the spare row PT)
+        const int r = PT * NG < 64 && lane >= PT * NG ? PT : lane / NG, g = lane % NG;
         const uint16_t ks = (uint16_t)mt[0], kb = (uint16_t)mt[1];
         const uint16_t vsb = (uint16_t)mt[2], vbb = (uint16_t)mt[3];
         xs[ts][r][g] = h_val(ks) * csk;
@@ -1411,10 +1388,17 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float2 xg = *reinterpret_cast<const float2 *>(&xs[ts][16 * blk + 4 * q4 + i][0]);
+                    if constexpr (NG == 2) {
+                        const float2 xg = *reinterpret_cast<const float2 *>(&xs[ts][16 * blk + 4 * q4 + i][0]);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        sc[nb][4 * blk + i] = fmaf(xg.x, sacc[0][nb][i], fmaf(xg.y, sacc[1][nb][i], s[nb][i]));
+                        for (int nb = 0; nb < NB; ++nb)
+                            sc[nb][4 * blk + i] = fmaf(xg.x, sacc[0][nb][i], fmaf(xg.y, sacc[1][nb][i], s[nb][i]));
+                    } else {
+                        const float xg = xs[ts][16 * blk + 4 * q4 + i][0];
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            sc[nb][4 * blk + i] = fmaf(xg, sacc[0][nb][i], s[nb][i]);
+                    }
                 }
             }
             if (PT * ti + PT - 1 > t_all) {
@@ -1524,7 +1508,8 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const float bias = __shfl(bacc[nb][i], rowbase + 2 * g) + __shfl(bacc[nb][i], rowbase + 2 * g + 1);
-                const int d0 = (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
+                const int d0 = HV ? 8 * (col & 7) + 4 * (col >> 3)  // the column's half word
+                                  : (g == (low8 ? 0 : 1)) ? 8 * col : 8 * (col ^ 8) + 4;
                 float o[4];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm)
@@ -1558,8 +1543,12 @@ int prefill_positions_per_block(int n_rep, int D) { return 16 * prefill_nb(D) / 
 
 // wavefronts per workgroup (consecutive position blocks of one KV head):
 // int4 at D = 128 shares each tile's operands across 8 wavefronts with fp16
-// queries, 4 with fp32 queries (LDS)
-constexpr int prefill_wg(int D, int bits, bool q_f32) { return bits == 4 && D == 128 ? (q_f32 ? 4 : 8) : 1; }
+// queries, 4 with fp32 queries (LDS); int4 at D = 64 across 4 (a tile has
+// four K and four V operands)
+constexpr int prefill_wg(int D, int bits, bool q_f32)
+{
+    return bits != 4 ? 1 : D == 128 ? (q_f32 ? 4 : 8) : D == 64 ? 4 : 1;
+}
 
 template <int D>
 void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
@@ -1570,11 +1559,11 @@ void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
         hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
     else if (a.bits == 8)
         hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
-    else if constexpr (D == 128) {
+    else if constexpr (D == 128 || D == 64) {
         if (a.q_f32)
-            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, true, WG32>), grid, dim3(64 * WG32), 0, s, a);
+            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, true, WG32, D>), grid, dim3(64 * WG32), 0, s, a);
         else
-            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, false, WG16>), grid, dim3(64 * WG16), 0, s, a);
+            hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, false, WG16, D>), grid, dim3(64 * WG16), 0, s, a);
     } else if (a.q_f32)
         hipLaunchKernelGGL((sdpa_prefill_i4_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
     else
