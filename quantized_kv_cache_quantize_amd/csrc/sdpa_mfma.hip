@@ -13,8 +13,10 @@
 //  - codes enter as the exact fp16 integers code - 8 (magic-number unpack and
 //    an exact fp16 subtraction; see Unpacker for why they are centred);
 //  - fp16 Q is exact; fp32 Q is split into hi + lo fp16 halves (two MFMAs);
-//  - the value weights p * scale_v are split into hi + lo fp16 halves (two
-//    MFMAs), so about 22 bits of each weight survive;
+//  - the value weights p * scale_v are split into hi + lo fp16 halves, so
+//    about 22 bits of each weight survive (the four-wavefront kernel takes
+//    them in two MFMAs; the one-wavefront kernel keeps the lo halves times
+//    2^11 in operand rows of their own, above the fp16 subnormals);
 //  - products of these operands are exact before the matrix core sums them.
 // Scale and bias are applied outside the matrix core, per group, as in
 // "What I Built Instead" (Gemma page): q . k^ = sum_g s_g (q . code)_g +
@@ -22,15 +24,19 @@
 //
 // Score GEMM: S[t][(h,g)] = Kcodes[t][:] . Qg[(h,g)][:], where column (h,g)
 // of Qg holds query head h restricted to scale group g (zeros elsewhere), so
-// each group's partial dot product comes out separately. 16 columns cover
-// n_rep * (D/G) <= 16. K rows are the A operand: a lane loads 16 bytes (32
-// nibbles) of one row; the contraction order of dimensions is permuted
-// identically in Qg.
+// each group's partial dot product comes out separately. A grid row takes a
+// block of the KV head's query heads whose (head, group) columns fit the 16
+// columns (8 in the one-wavefront kernel's layouts other than D = 128 with
+// two groups, whose value products use rows 8-15 for the lo halves). K rows
+// are the A operand: a lane loads 16 bytes (32 nibbles) of one row (8 at
+// D = 64); the contraction order of dimensions is permuted identically in
+// Qg.
 //
 // Value GEMM: O[(h,g)][d] += P'_g[(h,g)][t] . Vcodes[t][d]; rows whose group g
 // differs from the group of column d are discarded. A lane holds 8 rows of
 // one output column, so the V words of its 8 rows are transposed nibble-pair
-// by nibble-pair with v_perm while unpacking.
+// by nibble-pair with v_perm while unpacking (at D = 64 a column is half a
+// word, four dimensions).
 //
 // Softmax: each wavefront takes every fourth 32-row tile of the chunk and
 // keeps an online softmax across its tiles (the accumulator is rescaled only
