@@ -374,7 +374,7 @@ int kvq_sdpa_int4_prefill(const kvq_cache *cache, int64_t q_start, int32_t sq, c
     const int n_rep = Hq / cache->kv_heads;
     if (!prefill_supports(cache->head_dim, cache->group, n_rep, q_dtype, cache_bits(cache)))
         return KVQ_E_UNSUPPORTED;
-    const int pb = prefill_positions_per_block(n_rep, cache->head_dim);
+    const int pb = prefill_positions_per_block(n_rep, cache->head_dim, cache_bits(cache));
     if ((int64_t)cache->batch * Hq * sq > ((int64_t)1 << 40) / cache->head_dim || (sq + pb - 1) / pb > 0x7fffffff)
         return KVQ_E_SHAPE;
     PrefillArgs a;

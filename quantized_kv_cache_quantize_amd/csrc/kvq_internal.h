@@ -140,7 +140,7 @@ struct PrefillArgs {
     float score_scale;  // softmax_scale * log2(e)
 };
 bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits);
-int prefill_positions_per_block(int n_rep, int D);
+int prefill_positions_per_block(int n_rep, int D, int bits);
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
 
 // Where a partial-phase launch goes: the stream and, optionally, two events

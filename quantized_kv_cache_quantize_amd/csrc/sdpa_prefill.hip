@@ -27,11 +27,12 @@
 // only when a score exceeds it, as in the decode kernel; the output is
 // normalised in the kernel (no split over rows, so no partial state).
 //
-// Three kernels: 8-bit codes (sdpa_prefill_b8_kernel: per-group value
-// weights, the layout the int4 kernels started from), int4 at D = 256
-// (sdpa_prefill_i4_kernel) and int4 at D = 64 and 128
-// (sdpa_prefill_i4_wg_kernel, the same arithmetic with the tile's operands
-// shared by a workgroup).
+// Four kernels: 8-bit codes (sdpa_prefill_b8_kernel: per-group value
+// weights, the layout the int4 kernels started from; sdpa_prefill_b8_wg_kernel
+// at D = 128 with n_rep <= 16, the same arithmetic with one block of query
+// columns per wavefront and the tile's operands shared by a workgroup), int4
+// at D = 256 (sdpa_prefill_i4_kernel) and int4 at D = 64 and 128
+// (sdpa_prefill_i4_wg_kernel, the tile's operands shared by a workgroup).
 
 #include "kvq_internal.h"
 #include "mfma_common.h"
@@ -1523,6 +1524,410 @@ void sdpa_prefill_i4_wg_kernel(PrefillArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit codes, one block of 16 query columns per wavefront: WG wavefronts
+// share each tile's unpacked operands (launched at D = 128 with n_rep <= 16;
+// the code also takes D = 64, where the one-wavefront kernel is faster)
+//
+// The arithmetic of sdpa_prefill_b8_kernel (the codes enter the matrix core
+// as exact centred integers; the key scale and bias apply in fp32 after the
+// score products, the value scale inside the per-group weights, the value
+// bias as a running sum), with WG wavefronts per workgroup on consecutive
+// position blocks of one (batch, KV head). They read the same rows, so each
+// unpacks 1/WG of a tile's K operands (16-row block x 32 dimensions) and V
+// operands (scale group g, dimension mm of the column's four) into a
+// two-slot LDS ring, and one wavefront per tile, in turn, stages the tile's
+// fp32 factors. One barrier per tile separates building tile t + 1 from the
+// reads of tile t.
+//
+// V operand (g, mm) takes one word per row and lane: lane col reads the word
+// of dimensions 64 g + 8 (col & 7) + 4 (col >> 3) .. + 3 (the D = 64 layout
+// of the one-wavefront kernel, once per group), so that its builder loads
+// only its group's words and needs no lane exchange; value column col of
+// the operand is dimension 64 g + 8 (col & 7) + 4 (col >> 3) + mm.
+template <int PF, int NB, bool Q32, int WG, int D>
+__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(2)))
+void sdpa_prefill_b8_wg_kernel(PrefillArgs a)
+{
+    static_assert(D == 128 || D == 64, "two scale groups, or one");
+    static_assert(PF == 2, "tile j's words in register buffer j % 2");
+    constexpr int NG = D / 64;   // scale groups of 64
+    constexpr int W = D / 4;     // words per row
+    constexpr int KM = D / 32;   // score products per 16-row block
+    constexpr int KPG = 2;       // of them per scale group
+    constexpr float VC = 128.0f;        // centre of the value codes
+    constexpr float WS = 64.0f;         // scale of the value weights
+    constexpr float VU = 1.0f / 64.0f;  // unit of the value products
+    constexpr int PAIRS = PT * NG;      // (row, group) pairs of a tile
+    constexpr int NKO = 2 * KM;         // K operands of a tile: (16-row block, 32 dimensions)
+    constexpr int NVO = 4 * NG;         // V operands of a tile: (scale group, mm)
+    constexpr int KO = NKO / WG;        // of them built by each wavefront
+    constexpr int VO = NVO / WG;
+    static_assert(NKO % WG == 0 && NVO % WG == 0 && 4 % VO == 0, "operands split evenly, one group per builder");
+    static_assert(PAIRS == 64 || PAIRS == 32, "at most one (row, group) pair per lane of the staging wavefront");
+    constexpr int QH = Q32 ? 2 : 1;     // query halves: hi (and lo)
+
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const int col = lane & 15;
+    const int kvh = prefill_head(a);
+    const int b = blockIdx.z;
+    const int nrep = a.n_rep;
+    const int p0g = prefill_block(a) * WG * a.pb;                   // first position of the workgroup
+    const int p0 = p0g + wv * a.pb;                                 // of this wavefront
+    const int npos = max(0, min(a.pb, a.sq - p0));                  // this wavefront's positions (may be none)
+    const int t_end = (int)a.q_start + min(p0g + WG * a.pb, a.sq);  // rows [0, t_end) are read
+    const int t_all = (int)a.q_start + p0;                          // rows <= t_all are seen by every column
+    const int ntile = (t_end + PT - 1) / PT;
+    const int64_t kvrow0 = ((int64_t)b * a.Hkv + kvh) * a.cap;
+
+    int cpos[NB], chead[NB];
+    bool con[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int cc = 16 * nb + col;
+        cpos[nb] = cc / nrep;
+        chead[nb] = cc % nrep;
+        con[nb] = cc < a.pb * nrep && cpos[nb] < npos;
+    }
+
+    const uint32_t rows_ok = (uint32_t)t_end;
+    const __amdgpu_buffer_rsrc_t kq = make_rsrc(a.k_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t vq = make_rsrc(a.v_q + kvrow0 * W, rows_ok * W * 4u);
+    const __amdgpu_buffer_rsrc_t mres[4] = {
+        make_rsrc(a.k_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.k_bias + kvrow0 * NG, rows_ok * NG * 2u),
+        make_rsrc(a.v_scale + kvrow0 * NG, rows_ok * NG * 2u), make_rsrc(a.v_bias + kvrow0 * NG, rows_ok * NG * 2u)};
+
+    __shared__ __align__(16) half8 kop[2][NKO][64];  // K operands
+    __shared__ __align__(16) half8 vop[2][NVO][64];  // V operands
+    // fp32 factors per (row, group) of a tile (c = softmax scale * log2 e):
+    // x = s_k c, y = (b_k + 128 s_k) c, z = s_v WS, w = b_v + VC s_v
+    __shared__ __align__(16) float4 mring[2][PAIRS];
+    __shared__ __align__(16) half8 q_lds[WG][NB][QH][KM][64];
+    const float cs = a.score_scale;
+    const uint32_t magic8 = opaque_s(kMagic1024x4), magic16 = opaque_s(0x64006400u);
+    const uint32_t sel_even = opaque_s(0x04020400u), sel_odd = opaque_s(0x04030401u);
+    const uint32_t sel_b[4] = {opaque_s(0x0C040C00u), opaque_s(0x0C050C01u), opaque_s(0x0C060C02u),
+                               opaque_s(0x0C070C03u)};
+
+    // this wavefront's operands: K (blk, uu) = (o / KM, o % KM) and V (g, mm)
+    // = (v >> 2, v & 3) for o = KO wv + i, v = VO wv + i (one group gv)
+    const int gv = (VO * wv) >> 2;
+    constexpr uint32_t kNoRows = 0x80000000u;  // > any records size (capacity * D < 2^31 bytes)
+    uint32_t kbuf[PF][KO][2];
+    uint32_t vbuf[PF][8];
+    uint32_t mbuf[PF][4];
+    auto load_tile = [&](int ti, uint32_t (&kt)[KO][2], uint32_t (&vt)[8], uint32_t (&mt)[4]) {
+        const bool in = ti < ntile;
+        const uint32_t moff = in ? (uint32_t)((PT * ti) * NG + lane) * 2u : kNoRows;
+#pragma unroll
+        for (int arr = 0; arr < 4; ++arr)
+            mt[arr] = __builtin_amdgcn_raw_buffer_load_b16(mres[arr], moff, 0, 0);
+        const uint32_t base = in ? (uint32_t)(PT * ti) * (uint32_t)(W * 4) : kNoRows;
+        // K: row 16 blk + col, dimensions 32 uu + 8 q4 .. + 7 (two words)
+#pragma unroll
+        for (int i = 0; i < KO; ++i) {
+            const int o = KO * wv + i;
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(
+                kq, base + (uint32_t)(((16 * (o / KM) + col) * W + 8 * (o % KM) + 2 * q4) * 4), 0, 0);
+            kt[i][0] = x[0];
+            kt[i][1] = x[1];
+        }
+        // V: the group-gv word of rows 16 (j >> 2) + 4 q4 + (j & 3)
+        const uint32_t voff = base + (uint32_t)((4 * q4 * W + 16 * gv + 2 * (col & 7) + (col >> 3)) * 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            vt[j] = __builtin_amdgcn_raw_buffer_load_b32(vq, voff + ((16 * (j >> 2) + (j & 3)) * W) * 4, 0, 0);
+    };
+    // tile's operands into operand slot `slot`
+    auto build = [&](int slot, const uint32_t (&kt)[KO][2], const uint32_t (&vt)[8]) {
+#pragma unroll
+        for (int i = 0; i < KO; ++i)
+            kop[slot][KO * wv + i][lane] = k_operand8(kt[i][0], kt[i][1], magic8, sel_even, sel_odd);
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const int mm = (VO * wv + i) & 3;
+            half2v e[4];
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp)
+                e[jp] = v_pair8(vt[2 * jp], vt[2 * jp + 1], sel_b[mm], magic16);
+            vop[slot][VO * wv + i][lane] = cat8(e[0], e[1], e[2], e[3]);
+        }
+    };
+    // a tile's factors into slot `slot`, from its scale/bias words
+    auto stage_meta = [&](int slot, const uint32_t (&mt)[4]) {
+        if (PAIRS < 64 && lane >= PAIRS)  // D = 64: lanes 32-63 loaded the next tile's words
+            return;
+        const float ks = h_val((uint16_t)mt[0]);
+        const float kb = h_val((uint16_t)mt[1]);
+        const float vs = h_val((uint16_t)mt[2]);
+        const float vb = h_val((uint16_t)mt[3]);
+        mring[slot][lane] = make_float4(ks * cs, fmaf(128.0f, ks, kb) * cs, vs * WS, fmaf(VC, vs, vb));
+    };
+    auto fac_xy = [&](int slot, int r, int g) {
+        return *reinterpret_cast<const float2 *>(&mring[slot][r * NG + g]);
+    };
+    auto fac_zw = [&](int slot, int r, int g) {
+        return *(reinterpret_cast<const float2 *>(&mring[slot][r * NG + g]) + 1);
+    };
+
+    // prologue: tiles 0 and 1 loaded, tile 0 built and staged, tile 2 loaded
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        load_tile(u, kbuf[u], vbuf[u], mbuf[u]);
+    build(0, kbuf[0], vbuf[0]);
+    if (wv == 0)
+        stage_meta(0, mbuf[0]);
+    load_tile(2, kbuf[0], vbuf[0], mbuf[0]);
+
+    // each block's column query as B operands (kPerm8 order, as in the
+    // one-wavefront kernel); qsum: group sums of what the matrix core sees
+    float qsum[NB][NG];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t qrow = (((int64_t)b * a.Hq + kvh * nrep + (con[nb] ? chead[nb] : 0)) * a.sq +
+                              (con[nb] ? p0 + cpos[nb] : 0)) * D;
+        float gs[NG] = {};
+#pragma unroll
+        for (int uu = 0; uu < KM; ++uu) {
+            float x[8];
+            if constexpr (Q32) {
+                const float *qp = reinterpret_cast<const float *>(a.q) + qrow + 32 * uu + 8 * q4;
+                const float4 x0 = *reinterpret_cast<const float4 *>(qp);
+                const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
+                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+                x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            } else {
+                const half8 h8 = *reinterpret_cast<const half8 *>(reinterpret_cast<const _Float16 *>(a.q) + qrow +
+                                                                  32 * uu + 8 * q4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[j] = (float)h8[j];
+            }
+            half8 qh, ql;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xv = con[nb] ? x[kPerm8[j]] : 0.0f;
+                const _Float16 hi = (_Float16)xv;
+                qh[j] = hi;
+                if constexpr (Q32) {
+                    const _Float16 lo = (_Float16)(xv - (float)hi);
+                    ql[j] = lo;
+                    gs[uu / KPG] += (float)hi + (float)lo;
+                } else {
+                    gs[uu / KPG] += (float)hi;
+                }
+            }
+            q_lds[wv][nb][0][uu][lane] = qh;
+            if constexpr (Q32)
+                q_lds[wv][nb][QH - 1][uu][lane] = ql;
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            qsum[nb][g] = xrow_sum(gs[g]);
+    }
+    __syncthreads();
+
+    float m_run[NB], l_run[NB], b_run[NB][NG];
+    float4v acc[NB][NVO], accl[NB][NVO];  // [nb][4 g + mm]: hi and lo (x kLoScale) weight halves
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = 0.0f;
+        l_run[nb] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            b_run[nb][g] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NVO; ++m) {
+            acc[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+            accl[nb][m] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+
+#pragma unroll 1
+    for (int kk = 0; kk < ntile; kk += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int ti = kk + u;
+            const int slot = u;
+            const int nu = u ^ 1;
+
+            // tile ti + 1 into the other slot (its words loaded two tiles
+            // ago; its factors staged by wavefront (ti + 1) % WG), tile ti + 3
+            // into the freed registers
+            build(nu, kbuf[nu], vbuf[nu]);
+            if (wv == ((ti + 1) & (WG - 1)))
+                stage_meta(nu, mbuf[nu]);
+            load_tile(ti + 3, kbuf[nu], vbuf[nu], mbuf[nu]);
+
+            // ---- scores of the lane's 8 rows (4 q4 + i, 16 + 4 q4 + i - 4), log2 units
+            float sc[NB][8];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                float s[NB][4];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[nb][i] = -m_run[nb];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    float4v sacc[NB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        sacc[nb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KPG; ++k) {
+                        const half8 ka = kop[slot][blk * KM + g * KPG + k][lane];
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int hl = 0; hl < QH; ++hl)
+                                sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    ka, q_lds[wv][nb][hl][g * KPG + k][lane], sacc[nb], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float2 f = fac_xy(slot, 16 * blk + 4 * q4 + i, g);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            s[nb][i] = fmaf(f.x, sacc[nb][i], fmaf(f.y, qsum[nb][g], s[nb][i]));
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sc[nb][4 * blk + i] = s[nb][i];
+            }
+            if (PT * ti + PT - 1 > t_all) {  // uniform: some row is past some column's position
+                asm volatile("" ::: "memory");  // keep this a branch
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int lim = t_all + cpos[nb];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = PT * ti + 16 * (i >> 2) + 4 * q4 + (i & 3);
+                        sc[nb][i] = r <= lim ? sc[nb][i] : -INFINITY;
+                    }
+                }
+            }
+            float p[NB][8];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float mx = max3_raw(max3_raw(sc[nb][0], sc[nb][1], sc[nb][2]),
+                                          max3_raw(sc[nb][3], sc[nb][4], sc[nb][5]), max_raw(sc[nb][6], sc[nb][7]));
+                // ---- reference raised only when a score exceeds it (the first tile sets it)
+                if (ti == 0 || __builtin_amdgcn_ballot_w64(mx > 0.0f) != 0) {
+                    const float full = xrow_max(mx, -INFINITY);
+                    const bool raise = full > 0.0f || (ti == 0 && full > -INFINITY);
+                    const float delta = raise ? full + kHeadroom : 0.0f;
+                    m_run[nb] += delta;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        sc[nb][i] -= delta;
+                    if (ti != 0) {
+                        const float corr = __builtin_amdgcn_exp2f(-delta);
+                        l_run[nb] *= corr;
+#pragma unroll
+                        for (int g = 0; g < NG; ++g)
+                            b_run[nb][g] *= corr;
+                        float4v corr_row;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            corr_row[i] = __shfl(corr, 4 * q4 + i);
+#pragma unroll
+                        for (int m = 0; m < NVO; ++m) {
+                            acc[nb][m] *= corr_row;
+                            accl[nb][m] *= corr_row;
+                        }
+                    }
+                }
+                float lsum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    p[nb][i] = __builtin_amdgcn_exp2f(sc[nb][i]);
+                    lsum += p[nb][i];
+                }
+                l_run[nb] += lsum;
+            }
+
+            // ---- value products, group by group: the weights p s_v WS as hi
+            // and lo (x kLoScale) fp16 halves, each V operand serving all NB
+            // blocks
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                half8 phi[NB], plo[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    float bsum = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2) {
+                        const float2 f0 = fac_zw(slot, 16 * (j >> 2) + 4 * q4 + (j & 3), g);
+                        const float2 f1 = fac_zw(slot, 16 * ((j + 1) >> 2) + 4 * q4 + ((j + 1) & 3), g);
+                        bsum = fmaf(p[nb][j], f0.y, fmaf(p[nb][j + 1], f1.y, bsum));
+                        const float w0 = p[nb][j] * f0.x, w1 = p[nb][j + 1] * f1.x;
+                        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+                        const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(
+                                                                        (w0 - (float)h[0]) * kLoScale,
+                                                                        (w1 - (float)h[1]) * kLoScale));
+                        phi[nb][j] = h[0]; phi[nb][j + 1] = h[1];
+                        plo[nb][j] = l[0]; plo[nb][j + 1] = l[1];
+                    }
+                    b_run[nb][g] += bsum;
+                }
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const half8 bv = vop[slot][4 * g + mm][lane];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        acc[nb][4 * g + mm] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(phi[nb], bv, acc[nb][4 * g + mm], 0, 0, 0);
+                        accl[nb][4 * g + mm] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(plo[nb], bv, accl[nb][4 * g + mm], 0, 0, 0);
+                    }
+                }
+            }
+            __syncthreads();  // reads of tile ti done, tile ti + 1 published
+        }
+    }
+
+    // ---- normalised outputs: row r = 4 q4 + i is column 16 nb + r
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const float l_tot = xrow_sum(l_run[nb]);
+        float b_tot[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            b_tot[g] = xrow_sum(b_run[nb][g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q4 + i;
+            const int cc = 16 * nb + r;
+            const float inv_l = 1.0f / __shfl(l_tot, r);
+            const int rpos = cc / nrep, rhead = cc % nrep;
+            const bool on = cc < a.pb * nrep && rpos < npos;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const float bias = __shfl(b_tot[g], r);
+                const int d0 = 64 * g + 8 * (col & 7) + 4 * (col >> 3);
+                float o[4];
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const float hi = acc[nb][4 * g + mm][i];
+                    const float lo = accl[nb][4 * g + mm][i];
+                    o[mm] = (fmaf(lo, VU / kLoScale, hi * VU) + bias) * inv_l;
+                }
+                if (on) {
+                    float *dst = a.out + (((int64_t)b * a.Hq + kvh * nrep + rhead) * a.sq + p0 + rpos) * D + d0;
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // n_rep up to the query columns of a wavefront (16 per block: 32 at D = 64
@@ -1534,37 +1939,62 @@ bool prefill_supports(int D, int G, int n_rep, int q_dtype, int bits)
            (q_dtype == KVQ_F16 || q_dtype == KVQ_F32) && (bits == 4 || bits == 8);
 }
 
-// blocks of 16 query columns per wavefront: two at D = 128, one at D = 256
-// (8-bit codes with one block at D = 128: 35.8 ms against 28.8 ms on the
-// 4096-position chunk)
-constexpr int prefill_nb(int D) { return D == 256 ? 1 : 2; }
+// blocks of 16 query columns per wavefront: two at D = 64 and 128, one at
+// D = 256 (8-bit codes in one wavefront with one block at D = 128: 35.8 ms
+// against 28.8 ms on the 4096-position chunk); one for 8-bit codes at
+// D = 128 with n_rep <= 16, whose workgroups share the tile operands and run
+// two wavefronts per SIMD (22.0 ms against 27.9 ms for the chunk; at D = 64
+// 6.22 ms against 5.84 ms, so D = 64 keeps the one-wavefront kernel)
+constexpr int prefill_nb(int D, int bits, int n_rep)
+{
+    return D == 256 || (bits == 8 && D == 128 && n_rep <= 16) ? 1 : 2;
+}
 
-int prefill_positions_per_block(int n_rep, int D) { return 16 * prefill_nb(D) / n_rep; }
+int prefill_positions_per_block(int n_rep, int D, int bits) { return 16 * prefill_nb(D, bits, n_rep) / n_rep; }
 
 // wavefronts per workgroup (consecutive position blocks of one KV head):
 // int4 at D = 128 shares each tile's operands across 8 wavefronts with fp16
-// queries, 4 with fp32 queries (LDS); int4 at D = 64 across 4 (a tile has
-// four K and four V operands)
-constexpr int prefill_wg(int D, int bits, bool q_f32)
+// queries, 4 with fp32 queries (whose hi and lo query operands take twice
+// the LDS); int4 at D = 64 across 4 (a tile has four K and four V operands);
+// 8-bit codes at D = 128 with one block per wavefront across 4 (at most 256
+// registers, so that two workgroups share a CU: 22.0 ms on the chunk against
+// 23.6 ms in workgroups of 8); one wavefront otherwise
+constexpr int prefill_wg(int D, int bits, bool q_f32, int nb)
 {
-    return bits != 4 ? 1 : D == 128 ? (q_f32 ? 4 : 8) : D == 64 ? 4 : 1;
+    if (bits == 8)
+        return D == 128 && nb == 1 ? 4 : 1;
+    return D == 128 ? (q_f32 ? 4 : 8) : D == 64 ? 4 : 1;
 }
 
 template <int D>
 void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
 {
-    constexpr int NB = prefill_nb(D);
-    constexpr int WG16 = prefill_wg(D, 4, false), WG32 = prefill_wg(D, 4, true);
-    if (a.bits == 8 && a.q_f32)
-        hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
-    else if (a.bits == 8)
-        hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
-    else if constexpr (D == 128 || D == 64) {
-        if (a.q_f32)
+    constexpr int NB = D == 256 ? 1 : 2;
+    constexpr int WG16 = prefill_wg(D, 4, false, NB), WG32 = prefill_wg(D, 4, true, NB);
+    constexpr int WB = prefill_wg(D, 8, false, 1);
+    if constexpr (D == 128) {
+        if (a.bits == 8 && a.pb * a.n_rep <= 16) {
+            if (a.q_f32)
+                hipLaunchKernelGGL((sdpa_prefill_b8_wg_kernel<2, 1, true, WB, D>), grid, dim3(64 * WB), 0, s, a);
+            else
+                hipLaunchKernelGGL((sdpa_prefill_b8_wg_kernel<2, 1, false, WB, D>), grid, dim3(64 * WB), 0, s, a);
+            return;
+        }
+    }
+    if constexpr (D == 128 || D == 64) {
+        if (a.bits == 8 && a.q_f32)
+            hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
+        else if (a.bits == 8)
+            hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
+        else if (a.q_f32)
             hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, true, WG32, D>), grid, dim3(64 * WG32), 0, s, a);
         else
             hipLaunchKernelGGL((sdpa_prefill_i4_wg_kernel<2, NB, false, WG16, D>), grid, dim3(64 * WG16), 0, s, a);
-    } else if (a.q_f32)
+    } else if (a.bits == 8 && a.q_f32)
+        hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
+    else if (a.bits == 8)
+        hipLaunchKernelGGL((sdpa_prefill_b8_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
+    else if (a.q_f32)
         hipLaunchKernelGGL((sdpa_prefill_i4_kernel<2, NB, true, D>), grid, dim3(64), 0, s, a);
     else
         hipLaunchKernelGGL((sdpa_prefill_i4_kernel<2, NB, false, D>), grid, dim3(64), 0, s, a);
@@ -1572,10 +2002,11 @@ void launch_prefill_d(const PrefillArgs &a, dim3 grid, hipStream_t s)
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s)
 {
+    const int nb = prefill_nb(a.D, a.bits, a.n_rep);
     if ((a.D != 64 && a.D != 128 && a.D != 256) || (a.bits != 4 && a.bits != 8) || a.pb < 1 ||
-        a.pb * a.n_rep > 16 * prefill_nb(a.D))
+        a.pb != 16 * nb / a.n_rep)
         return hipErrorInvalidValue;
-    const int64_t per_block = (int64_t)a.pb * prefill_wg(a.D, a.bits, a.q_f32 != 0);
+    const int64_t per_block = (int64_t)a.pb * prefill_wg(a.D, a.bits, a.q_f32 != 0, nb);
     const int64_t blocks = (a.sq + per_block - 1) / per_block;
     // one row of blocks x Hkv workgroups per batch entry (prefill_head, prefill_block)
     dim3 grid((unsigned)(blocks * a.Hkv), 1u, (unsigned)batch);
