@@ -305,3 +305,22 @@ def test_small_value_ranges(bits):
     got = _run(oc, q_start, q, alpha)
     ref = oracle.sdpa_prefill(oc, q_start, q, alpha)
     check_attention(got, ref, REL_L2, atol=2e-5, rtol=1e-2, label="prefill small values")
+
+
+# 8-bit codes at D 128 with at most 16 query heads per KV head run in
+# workgroups of four wavefronts of 16 query columns each (16 / n_rep
+# positions per wavefront); above 16 heads, one wavefront of 32 columns.
+# Cases: the boundary n_rep 16 / 20, and a last workgroup whose later
+# wavefronts have no positions (n_rep 1: 64 positions per workgroup, sq 65
+# and 130; n_rep 8: 8 positions per workgroup, sq 9), with fp32 queries.
+@pytest.mark.parametrize("hq,hkv,q_start,sq,q32", [(16, 1, 0, 40, False), (20, 1, 0, 40, False),
+                                                   (16, 1, 700, 9, True), (20, 1, 700, 9, True),
+                                                   (2, 2, 0, 65, False), (4, 4, 300, 130, True),
+                                                   (64, 8, 100, 9, False), (64, 8, 3000, 23, True)])
+def test_int8_workgroup_edges(hq, hkv, q_start, sq, q32):
+    note("prefill int8 workgroup edges hq=%d hkv=%d q_start=%d sq=%d q32=%d" % (hq, hkv, q_start, sq, q32))
+    q, oc, alpha = _case(1, hq, hkv, q_start, sq, seed=77000 + hq * 100 + sq, bits=8)
+    if q32:
+        q = (q.astype(np.float32) * np.float32(1.0001)).astype(np.float32)
+    check_attention(_run(oc, q_start, q, alpha), oracle.sdpa_prefill(oc, q_start, q, alpha), REL_L2,
+                    label="int8 workgroup edges")
