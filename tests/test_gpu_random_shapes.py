@@ -121,7 +121,7 @@ def test_draws_are_valid():
         assert c["D"] % c["G"] == 0 and c["Hq"] % c["Hkv"] == 0 and c["cap"] > c["skv"]
 
 
-N_PREFILL = 48
+N_PREFILL = 96
 
 
 def _draw_prefill(i):
